@@ -1,0 +1,327 @@
+"""Oracle forward and backward of one decoder-only GPT training step (numpy).
+
+Test infrastructure only (see the package docstring).  Plain definitions, in
+the order the pages describe the model, with hand-written backward formulas.
+
+What the pages fix (dev.to "¿Cómo Entrenar Tu Propio ChatGPT por $50?",
+section "Cómo Funciona nanochat" -> "1. Modelo GPT (nanochat/gpt.py)", and the
+same list in apidog.com/pt "Modelo GPT"):
+  * rotary position embeddings (RoPE), no learned positions;
+  * QK normalisation of queries and keys;
+  * token embedding and output matrix not tied;
+  * ReLU squared in the MLP;
+  * causal attention through ``flash_attn_func(q, k, v, causal=True, ...)``
+    (section "5. Unificación Flash Attention");
+  * vocabulary of 32,768 tokens (section "Lo que nanochat cubre").
+Readings taken where the pages are silent (each listed in the design doc):
+  * pre-norm RMSNorm without gain, eps 1e-6 inside the square root, also
+    used for the 128-wide QK normalisation; a final norm before the head;
+  * RoPE base 10000, rotate-half pairing (i, i + hd/2), angle t * base^(-2i/hd),
+    applied before the QK normalisation (the two commute: rotation keeps the
+    per-head RMS);
+  * full causal window, scale 1/sqrt(hd), multi-head (one KV head per head);
+  * inputs ids[:, :T], targets ids[:, 1:], loss = mean over all B*T rows;
+  * no biases, no logit soft-capping.
+
+fp8 mode (``fp8=True``): the four block projections (qkv, out, fc, proj) use
+per-tensor scaled fake quantisation as the precision passage describes
+(apidog.com/pt "Gerenciamento de Precisão", apidog.com/de
+"Präzisionsverwaltung": Float8Linear with tensorwise scaling): E4M3 for
+activations and weights, E5M2 for output gradients, scale = fmax / amax of the
+current tensor.  The fused q/k/v weight counts as one tensor.
+
+Pinned by (tests/test_oracle_model.py): central finite differences in float64
+of every parameter tensor on a tiny shape; a brute-force double-loop causal
+attention; torch CPU autograd (float64) with torch's own RMS norm and
+scaled-dot-product attention as an independent second implementation; the
+closed form loss = ln V for a zero output matrix; softmax rows summing to 1;
+RoPE identity at position 0, norm preservation and relative-position
+invariance; RMSNorm output mean square = ms / (ms + eps).
+"""
+
+from dataclasses import dataclass
+
+import numpy as np
+
+from . import fp8 as _fp8
+
+
+@dataclass(frozen=True)
+class Config:
+    n_layer: int
+    d_model: int
+    n_head: int
+    head_dim: int
+    hidden: int
+    vocab: int
+    eps: float = 1e-6
+    rope_base: float = 10000.0
+
+    @staticmethod
+    def from_depth(depth, vocab=32768):
+        """Shapes from the single depth dial: width 64*depth, 128-wide heads,
+        MLP 4x (dev.to page, "La Filosofía: Un Solo Selector")."""
+        d = 64 * depth
+        return Config(n_layer=depth, d_model=d, n_head=d // 128, head_dim=128,
+                      hidden=4 * d, vocab=vocab)
+
+
+# ----------------------------------------------------------------------------
+# building blocks
+# ----------------------------------------------------------------------------
+
+def rms_norm(x, eps):
+    """y = x / sqrt(mean(x^2) + eps) over the last axis; returns (y, r) with
+    r = 1/sqrt(mean(x^2) + eps)."""
+    ms = np.mean(x * x, axis=-1, keepdims=True)
+    r = 1.0 / np.sqrt(ms + eps)
+    return x * r, r
+
+
+def rms_norm_bwd(dy, y, r):
+    """Gradient of rms_norm: dx = r * (dy - y * mean(dy * y)), y the output."""
+    return r * (dy - y * np.mean(dy * y, axis=-1, keepdims=True))
+
+
+def rope_tables(T, head_dim, base, dtype=np.float64):
+    """cos/sin of angle t * base^(-2i/head_dim), t < T, i < head_dim/2
+    (computed in float64)."""
+    half = head_dim // 2
+    inv_freq = base ** (-(2.0 * np.arange(half, dtype=np.float64)) / head_dim)
+    ang = np.arange(T, dtype=np.float64)[:, None] * inv_freq[None, :]
+    return np.cos(ang).astype(dtype), np.sin(ang).astype(dtype)
+
+
+def rope(x, cos, sin):
+    """Rotate pairs (i, i + hd/2) of the last axis by the position angle.
+    x: [..., T, hd]; cos/sin: [T, hd/2]."""
+    half = x.shape[-1] // 2
+    x1, x2 = x[..., :half], x[..., half:]
+    return np.concatenate([x1 * cos - x2 * sin, x1 * sin + x2 * cos], axis=-1)
+
+
+def rope_bwd(dy, cos, sin):
+    """Transpose of the rotation (the inverse rotation)."""
+    half = dy.shape[-1] // 2
+    d1, d2 = dy[..., :half], dy[..., half:]
+    return np.concatenate([d1 * cos + d2 * sin, -d1 * sin + d2 * cos], axis=-1)
+
+
+def causal_attention(q, k, v):
+    """softmax(q k^T / sqrt(hd) with key j > query i masked) v.
+    q, k, v: [..., T, hd].  Returns (y, lse) with lse the row log-sum-exp of
+    the scaled, masked scores."""
+    T, hd = q.shape[-2], q.shape[-1]
+    s = (q @ np.swapaxes(k, -1, -2)) / np.sqrt(hd)
+    mask = np.triu(np.ones((T, T), dtype=bool), k=1)
+    s = np.where(mask, -np.inf, s)
+    m = np.max(s, axis=-1, keepdims=True)
+    e = np.exp(s - m)
+    den = np.sum(e, axis=-1, keepdims=True)
+    p = e / den
+    lse = (m + np.log(den))[..., 0]
+    return p @ v, lse
+
+
+def causal_attention_bwd(q, k, v, y, dy, lse):
+    """Backward of causal_attention with P recomputed from lse:
+    dV = P^T dY; dP = dY V^T; dS = P * (dP - rowsum(dY * Y)); dQ = dS K / sqrt(hd);
+    dK = dS^T Q / sqrt(hd)."""
+    T, hd = q.shape[-2], q.shape[-1]
+    scale = 1.0 / np.sqrt(hd)
+    s = (q @ np.swapaxes(k, -1, -2)) * scale
+    mask = np.triu(np.ones((T, T), dtype=bool), k=1)
+    p = np.where(mask, 0.0, np.exp(s - lse[..., None]))
+    dv = np.swapaxes(p, -1, -2) @ dy
+    dp = dy @ np.swapaxes(v, -1, -2)
+    dsum = np.sum(dy * y, axis=-1, keepdims=True)
+    ds = p * (dp - dsum)
+    dq = (ds @ k) * scale
+    dk = (np.swapaxes(ds, -1, -2) @ q) * scale
+    return dq, dk, dv
+
+
+def cross_entropy(z, tgt):
+    """Per-row loss lse(z) - z[tgt] with max-subtracted log-sum-exp.
+    z: [R, V]; tgt: [R] int.  Returns (row_loss, lse)."""
+    m = np.max(z, axis=-1, keepdims=True)
+    lse = (m + np.log(np.sum(np.exp(z - m), axis=-1, keepdims=True)))[:, 0]
+    picked = z[np.arange(z.shape[0]), tgt]
+    return lse - picked, lse
+
+
+def cross_entropy_bwd(z, tgt, lse, scale):
+    """d(scale * sum row_loss)/dz = scale * (softmax(z) - onehot(tgt))."""
+    dz = np.exp(z - lse[:, None])
+    dz[np.arange(z.shape[0]), tgt] -= 1.0
+    return dz * scale
+
+
+# ----------------------------------------------------------------------------
+# linear layers (bf16-valued weights; optional fp8 fake quantisation)
+# ----------------------------------------------------------------------------
+
+def _lin_fwd(x2, w, fp8):
+    """y = x w^T for x [R, K], w [N, K]."""
+    if fp8:
+        x2 = _fp8.fake_quant(x2, "e4m3")
+        w = _fp8.fake_quant(w, "e4m3")
+    return x2 @ w.T
+
+
+def _lin_bwd(x2, w, dy2, fp8):
+    """dX = dY w, dW = dY^T x."""
+    if fp8:
+        dy2 = _fp8.fake_quant(dy2, "e5m2")
+        w = _fp8.fake_quant(w, "e4m3")
+        x2 = _fp8.fake_quant(x2, "e4m3")
+    return dy2 @ w, dy2.T @ x2
+
+
+# ----------------------------------------------------------------------------
+# parameters
+# ----------------------------------------------------------------------------
+
+def param_names(cfg):
+    """Parameter tensors in packed order: wte, per layer (wq, wk, wv, wo),
+    per layer wfc, per layer wproj, lm_head."""
+    names = ["wte"]
+    for i in range(cfg.n_layer):
+        names += [f"wq.{i}", f"wk.{i}", f"wv.{i}", f"wo.{i}"]
+    names += [f"wfc.{i}" for i in range(cfg.n_layer)]
+    names += [f"wproj.{i}" for i in range(cfg.n_layer)]
+    names.append("lm_head")
+    return names
+
+
+def param_shapes(cfg):
+    d, h, V = cfg.d_model, cfg.hidden, cfg.vocab
+    shapes = {}
+    for n in param_names(cfg):
+        base = n.split(".")[0]
+        shapes[n] = {"wte": (V, d), "lm_head": (V, d), "wq": (d, d), "wk": (d, d),
+                     "wv": (d, d), "wo": (d, d), "wfc": (h, d), "wproj": (d, h)}[base]
+    return shapes
+
+
+# ----------------------------------------------------------------------------
+# the step
+# ----------------------------------------------------------------------------
+
+def _forward_backward_chunk(P, ids, cfg, loss_scale, dtype, want_grads, want_logits, fp8, cos, sin):
+    B, T1 = ids.shape
+    T = T1 - 1
+    d, H, hd = cfg.d_model, cfg.n_head, cfg.head_dim
+    R = B * T
+    inp = ids[:, :T].reshape(-1)
+    tgt = ids[:, 1:].reshape(-1)
+    eps = cfg.eps
+
+    x = P["wte"][inp].astype(dtype)  # [R, d]
+    caches = []
+    for i in range(cfg.n_layer):
+        wqkv = np.concatenate([P[f"wq.{i}"], P[f"wk.{i}"], P[f"wv.{i}"]], axis=0)
+        h1, r1 = rms_norm(x, eps)
+        qkv = _lin_fwd(h1, wqkv, fp8)
+        q_raw = qkv[:, :d].reshape(B, T, H, hd).transpose(0, 2, 1, 3)
+        k_raw = qkv[:, d:2 * d].reshape(B, T, H, hd).transpose(0, 2, 1, 3)
+        v = qkv[:, 2 * d:].reshape(B, T, H, hd).transpose(0, 2, 1, 3)
+        qn, rq = rms_norm(rope(q_raw, cos, sin), eps)
+        kn, rk = rms_norm(rope(k_raw, cos, sin), eps)
+        y, lse_att = causal_attention(qn, kn, v)
+        y2 = y.transpose(0, 2, 1, 3).reshape(R, d)
+        x = x + _lin_fwd(y2, P[f"wo.{i}"], fp8)
+        h2, r2 = rms_norm(x, eps)
+        u = _lin_fwd(h2, P[f"wfc.{i}"], fp8)
+        a = np.maximum(u, 0.0) ** 2
+        x = x + _lin_fwd(a, P[f"wproj.{i}"], fp8)
+        caches.append((h1, r1, wqkv, qn, rq, kn, rk, v, y, y2, lse_att, h2, r2, u, a))
+
+    hf, rf = rms_norm(x, eps)
+    z = hf @ P["lm_head"].T
+    row_loss, lse = cross_entropy(z, tgt)
+    out = {"row_loss": row_loss.reshape(B, T), "lse": lse.reshape(B, T),
+           "loss_sum": float(np.sum(row_loss, dtype=np.float64))}
+    if want_logits:
+        out["logits"] = z
+    if not want_grads:
+        return out
+
+    G = {}
+    dz = cross_entropy_bwd(z, tgt, lse, loss_scale)
+    del z
+    G["lm_head"] = dz.T @ hf
+    g = rms_norm_bwd(dz @ P["lm_head"], hf, rf)
+    del dz
+    for i in reversed(range(cfg.n_layer)):
+        (h1, r1, wqkv, qn, rq, kn, rk, v, y, y2, lse_att, h2, r2, u, a) = caches[i]
+        # MLP
+        da, G[f"wproj.{i}"] = _lin_bwd(a, P[f"wproj.{i}"], g, fp8)
+        du = da * 2.0 * np.maximum(u, 0.0)
+        dh2, G[f"wfc.{i}"] = _lin_bwd(h2, P[f"wfc.{i}"], du, fp8)
+        g = g + rms_norm_bwd(dh2, h2, r2)
+        # attention
+        dy2, G[f"wo.{i}"] = _lin_bwd(y2, P[f"wo.{i}"], g, fp8)
+        dy = dy2.reshape(B, T, H, hd).transpose(0, 2, 1, 3)
+        dqn, dkn, dv = causal_attention_bwd(qn, kn, v, y, dy, lse_att)
+        dq = rope_bwd(rms_norm_bwd(dqn, qn, rq), cos, sin)
+        dk = rope_bwd(rms_norm_bwd(dkn, kn, rk), cos, sin)
+        dqkv = np.concatenate([t.transpose(0, 2, 1, 3).reshape(R, d) for t in (dq, dk, dv)], axis=1)
+        dh1, dwqkv = _lin_bwd(h1, wqkv, dqkv, fp8)
+        G[f"wq.{i}"], G[f"wk.{i}"], G[f"wv.{i}"] = dwqkv[:d], dwqkv[d:2 * d], dwqkv[2 * d:]
+        g = g + rms_norm_bwd(dh1, h1, r1)
+        caches[i] = None
+    dwte = np.zeros(P["wte"].shape, dtype=dtype)
+    np.add.at(dwte, inp, g)
+    G["wte"] = dwte
+    out["grads"] = G
+    return out
+
+
+def forward_backward(P, ids, cfg, dtype=np.float64, want_grads=True, want_logits=False,
+                     fp8=False, seq_chunk=None):
+    """One training step's forward and backward.
+
+    P: dict name -> array (the bf16-rounded weight values, see precision.py);
+    ids: int array [B, T+1].  Returns dict with ``loss`` (mean over B*T rows),
+    ``row_loss`` and ``lse`` [B, T], optional ``logits`` [B*T, V] and ``grads``
+    (dict name -> gradient of ``loss``).
+
+    seq_chunk: process that many sequences at a time (the sequences of a batch
+    are independent up to the loss mean); not allowed with fp8, whose
+    per-tensor scales span the whole batch."""
+    ids = np.asarray(ids)
+    B, T1 = ids.shape
+    T = T1 - 1
+    P = {k: np.asarray(v, dtype=dtype) for k, v in P.items()}
+    cos, sin = rope_tables(T, cfg.head_dim, cfg.rope_base, dtype)
+    loss_scale = 1.0 / (B * T)
+    if seq_chunk is None or seq_chunk >= B:
+        chunks = [(0, B)]
+    else:
+        if fp8:
+            raise ValueError("fp8 per-tensor scales need the whole batch at once")
+        chunks = [(s, min(B, s + seq_chunk)) for s in range(0, B, seq_chunk)]
+    total, grads, row_loss, lse, logits = 0.0, None, [], [], []
+    for s, e in chunks:
+        o = _forward_backward_chunk(P, ids[s:e], cfg, loss_scale, dtype, want_grads,
+                                    want_logits, fp8, cos, sin)
+        total += o["loss_sum"]
+        row_loss.append(o["row_loss"])
+        lse.append(o["lse"])
+        if want_logits:
+            logits.append(o["logits"])
+        if want_grads:
+            if grads is None:
+                grads = o["grads"]
+            else:
+                for k in grads:
+                    grads[k] += o["grads"][k]
+    out = {"loss": total / (B * T), "row_loss": np.concatenate(row_loss),
+           "lse": np.concatenate(lse)}
+    if want_logits:
+        out["logits"] = np.concatenate(logits)
+    if want_grads:
+        out["grads"] = grads
+    return out
+
