@@ -1,0 +1,84 @@
+// Internal helpers shared by the HIP sources of libgptstep (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <string>
+
+namespace gs {
+
+typedef __attribute__((__vector_size__(8 * sizeof(short)))) short bf16x8_t;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16_t;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
+typedef __attribute__((__vector_size__(8 * sizeof(int)))) int i32x8_t;
+
+// ---------------------------------------------------------------------------
+// bf16 <-> fp32 (bit patterns in uint16_t)
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float bf2f(uint16_t b) { return __uint_as_float(((uint32_t)b) << 16); }
+
+// round to nearest, ties to even (NaN stays NaN)
+__device__ __forceinline__ uint16_t f2bf(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+__device__ __forceinline__ uint32_t pack_bf2(float a, float b) {
+  return (uint32_t)f2bf(a) | ((uint32_t)f2bf(b) << 16);
+}
+
+__device__ __forceinline__ float lo_bf(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float hi_bf(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// ---------------------------------------------------------------------------
+// wave64 reductions
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+// XCD-aware remap of a linear workgroup id.  The dispatcher places workgroup
+// i on XCD i % 8; this returns an id such that each XCD sees one contiguous
+// range of logical ids (so neighbouring tiles share that XCD's L2).
+__device__ __forceinline__ int xcd_remap(int bid, int nblk) {
+  const int q = nblk / 8, r = nblk % 8;
+  const int xcd = bid % 8, loc = bid / 8;
+  return (xcd < r) ? xcd * (q + 1) + loc : r * (q + 1) + (xcd - r) * q + loc;
+}
+
+}  // namespace gs
+
+// ---------------------------------------------------------------------------
+// host-side error plumbing (api.cpp owns the thread-local message)
+// ---------------------------------------------------------------------------
+namespace gs {
+void set_error(const std::string& msg);
+}
+
+#define GS_HIP_CHECK(expr)                                                       \
+  do {                                                                           \
+    hipError_t e_ = (expr);                                                      \
+    if (e_ != hipSuccess) {                                                      \
+      gs::set_error(std::string(#expr) + ": " + hipGetErrorString(e_));          \
+      return -4;                                                                 \
+    }                                                                            \
+  } while (0)
+
+#define GS_LAUNCH_CHECK(name)                                                    \
+  do {                                                                           \
+    hipError_t e_ = hipGetLastError();                                           \
+    if (e_ != hipSuccess) {                                                      \
+      gs::set_error(std::string("launch of ") + name + ": " + hipGetErrorString(e_)); \
+      return -4;                                                                 \
+    }                                                                            \
+  } while (0)

@@ -1,0 +1,506 @@
+// Bandwidth-bound kernels of the step: embedding gather/scatter, RMSNorm,
+// rotary embedding with QK normalisation, cross-entropy row reduction, loss
+// mean, and the elementwise parts of the Muon update.
+//
+// Model passage (dev.to "¿Cómo Entrenar Tu Propio ChatGPT por $50?",
+// "1. Modelo GPT"): rotary embeddings, QK normalisation, untied token
+// embedding.  Muon passage ("2. Optimizador Muon"): momentum, normalised start
+// of the Newton-Schulz iteration, apply.  Readings used here: gainless RMS
+// norm with eps = 1e-6 inside the root; rotation of pairs (i, i + 64) by
+// angle t * 10000^(-i/64); QK norm over each 128-wide head after rotation.
+//
+// Every kernel here streams its rows once: one wave64 per row (vectorised
+// 16-byte accesses) so the row statistics reduce with wave shuffles only.
+
+#include "common.h"
+#include "kernels.h"
+
+namespace gs {
+
+namespace {
+
+constexpr float kEps = 1e-6f;
+constexpr int kMaxD = 4096;              // 64 * 64 (largest supported depth)
+constexpr int kMaxChunks = kMaxD / 4 / 64;  // float4 chunks per lane at d = 4096
+
+inline int nblocks(long long n, int per) { return (int)((n + per - 1) / per); }
+
+// ----------------------------------------------------------------------------
+__global__ void fill_f32_kernel(float* p, long long n, float v) {
+  long long i = ((long long)blockIdx.x * blockDim.x + threadIdx.x) * 4;
+  const long long stride = (long long)gridDim.x * blockDim.x * 4;
+  for (; i < n; i += stride) {
+    if (i + 3 < n && (((uintptr_t)(p + i)) & 15) == 0) {
+      *reinterpret_cast<float4*>(p + i) = make_float4(v, v, v, v);
+    } else {
+      for (int j = 0; j < 4 && i + j < n; ++j) p[i + j] = v;
+    }
+  }
+}
+
+__global__ void cast_bf16_kernel(const float* __restrict__ src, uint16_t* __restrict__ dst, long long n) {
+  long long i = ((long long)blockIdx.x * blockDim.x + threadIdx.x) * 4;
+  const long long stride = (long long)gridDim.x * blockDim.x * 4;
+  for (; i < n; i += stride) {
+    if (i + 3 < n) {
+      const float4 v = *reinterpret_cast<const float4*>(src + i);
+      *reinterpret_cast<uint2*>(dst + i) = make_uint2(pack_bf2(v.x, v.y), pack_bf2(v.z, v.w));
+    } else {
+      for (int j = 0; i + j < n; ++j) dst[i + j] = f2bf(src[i + j]);
+    }
+  }
+}
+
+// cos/sin of t * 10000^(-2i/128), computed in double precision
+__global__ void rope_table_kernel(float* cs, int T) {
+  const int idx = blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= T * 64) return;
+  const int t = idx / 64, i = idx % 64;
+  const double inv_freq = pow(10000.0, -(2.0 * i) / 128.0);
+  const double ang = (double)t * inv_freq;
+  cs[idx] = (float)cos(ang);
+  cs[T * 64 + idx] = (float)sin(ang);
+}
+
+// x[n, :] = wte[ids[b, t], :] for n = b*T + t (bf16 -> fp32, exact)
+__global__ void embed_fwd_kernel(const int* __restrict__ ids, const uint16_t* __restrict__ wte,
+                                 float* __restrict__ x, int B, int T, int d) {
+  const int lane = threadIdx.x & 63;
+  const long long n = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (n >= (long long)B * T) return;
+  const int b = (int)(n / T), t = (int)(n % T);
+  const long long id = ids[(long long)b * (T + 1) + t];
+  const uint16_t* src = wte + id * d;
+  float* dst = x + n * d;
+  for (int c = lane; c < d / 8; c += 64) {
+    const uint4 w = *reinterpret_cast<const uint4*>(src + c * 8);
+    *reinterpret_cast<float4*>(dst + c * 8) = make_float4(lo_bf(w.x), hi_bf(w.x), lo_bf(w.y), hi_bf(w.y));
+    *reinterpret_cast<float4*>(dst + c * 8 + 4) = make_float4(lo_bf(w.z), hi_bf(w.z), lo_bf(w.w), hi_bf(w.w));
+  }
+}
+
+// dwte[ids[b, t], :] += g[n, :]
+__global__ void embed_bwd_kernel(const int* __restrict__ ids, const float* __restrict__ g,
+                                 float* __restrict__ dwte, int B, int T, int d) {
+  const int lane = threadIdx.x & 63;
+  const long long n = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (n >= (long long)B * T) return;
+  const int b = (int)(n / T), t = (int)(n % T);
+  const long long id = ids[(long long)b * (T + 1) + t];
+  float* dst = dwte + id * d;
+  const float* src = g + n * d;
+  for (int c = lane; c < d / 4; c += 64) {
+    const float4 v = *reinterpret_cast<const float4*>(src + c * 4);
+    unsafeAtomicAdd(dst + c * 4 + 0, v.x);
+    unsafeAtomicAdd(dst + c * 4 + 1, v.y);
+    unsafeAtomicAdd(dst + c * 4 + 2, v.z);
+    unsafeAtomicAdd(dst + c * 4 + 3, v.w);
+  }
+}
+
+// h = x * r, r = 1/sqrt(mean(x^2) + eps); one wave per row
+__global__ void rmsnorm_fwd_kernel(const float* __restrict__ x, uint16_t* __restrict__ h,
+                                   float* __restrict__ r, long long N, int d) {
+  const int lane = threadIdx.x & 63;
+  const long long n = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (n >= N) return;
+  const int nc = d / 4;
+  const float* xr = x + n * d;
+  float4 v[kMaxChunks];
+  float ss = 0.f;
+#pragma unroll
+  for (int i = 0; i < kMaxChunks; ++i) {
+    const int c = i * 64 + lane;
+    if (c < nc) {
+      v[i] = *reinterpret_cast<const float4*>(xr + c * 4);
+      ss += v[i].x * v[i].x + v[i].y * v[i].y + v[i].z * v[i].z + v[i].w * v[i].w;
+    }
+  }
+  ss = wave_sum(ss);
+  const float rr = 1.0f / sqrtf(ss / (float)d + kEps);
+  uint16_t* hr = h + n * d;
+#pragma unroll
+  for (int i = 0; i < kMaxChunks; ++i) {
+    const int c = i * 64 + lane;
+    if (c < nc) {
+      *reinterpret_cast<uint2*>(hr + c * 4) =
+          make_uint2(pack_bf2(v[i].x * rr, v[i].y * rr), pack_bf2(v[i].z * rr, v[i].w * rr));
+    }
+  }
+  if (lane == 0) r[n] = rr;
+}
+
+// g += r * (dh - h * mean(dh * h)); g_bf = bf16(g); one wave per row
+__global__ void rmsnorm_bwd_kernel(const float* __restrict__ dh, const uint16_t* __restrict__ h,
+                                   const float* __restrict__ r, float* __restrict__ g,
+                                   uint16_t* __restrict__ g_bf, long long N, int d) {
+  const int lane = threadIdx.x & 63;
+  const long long n = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (n >= N) return;
+  const int nc = d / 4;
+  float4 dv[kMaxChunks], hv[kMaxChunks];
+  float dot = 0.f;
+#pragma unroll
+  for (int i = 0; i < kMaxChunks; ++i) {
+    const int c = i * 64 + lane;
+    if (c < nc) {
+      dv[i] = *reinterpret_cast<const float4*>(dh + n * d + c * 4);
+      const uint2 w = *reinterpret_cast<const uint2*>(h + n * d + c * 4);
+      hv[i] = make_float4(lo_bf(w.x), hi_bf(w.x), lo_bf(w.y), hi_bf(w.y));
+      dot += dv[i].x * hv[i].x + dv[i].y * hv[i].y + dv[i].z * hv[i].z + dv[i].w * hv[i].w;
+    }
+  }
+  dot = wave_sum(dot) / (float)d;
+  const float rr = r[n];
+#pragma unroll
+  for (int i = 0; i < kMaxChunks; ++i) {
+    const int c = i * 64 + lane;
+    if (c < nc) {
+      float4 gv = *reinterpret_cast<const float4*>(g + n * d + c * 4);
+      gv.x += rr * (dv[i].x - hv[i].x * dot);
+      gv.y += rr * (dv[i].y - hv[i].y * dot);
+      gv.z += rr * (dv[i].z - hv[i].z * dot);
+      gv.w += rr * (dv[i].w - hv[i].w * dot);
+      *reinterpret_cast<float4*>(g + n * d + c * 4) = gv;
+      *reinterpret_cast<uint2*>(g_bf + n * d + c * 4) = make_uint2(pack_bf2(gv.x, gv.y), pack_bf2(gv.z, gv.w));
+    }
+  }
+}
+
+// In place on one 128-wide head: rotate (e, e+64) by the position angle, then
+// RMS-normalise over the head.  Lane e holds elements e and e + 64.
+__device__ __forceinline__ float rope_norm_head(uint16_t* p, const float* cs, int T, int t, int lane) {
+  const float c = cs[t * 64 + lane], sn = cs[T * 64 + t * 64 + lane];
+  const float x1 = bf2f(p[lane]), x2 = bf2f(p[lane + 64]);
+  const float y1 = x1 * c - x2 * sn, y2 = x1 * sn + x2 * c;
+  const float ss = wave_sum(y1 * y1 + y2 * y2);
+  const float rr = 1.0f / sqrtf(ss / 128.f + kEps);
+  p[lane] = f2bf(y1 * rr);
+  p[lane + 64] = f2bf(y2 * rr);
+  return rr;
+}
+
+// one wave per (token, head): q and k of that head
+__global__ void rope_qknorm_fwd_kernel(uint16_t* __restrict__ qkv, float* __restrict__ rq,
+                                       float* __restrict__ rk, const float* __restrict__ cs,
+                                       long long N, int T, int H) {
+  const int lane = threadIdx.x & 63;
+  const long long w = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (w >= N * H) return;
+  const long long n = w / H;
+  const int hh = (int)(w % H), t = (int)(n % T);
+  const int d = H * 128;
+  uint16_t* row = qkv + n * 3 * d;
+  const float a = rope_norm_head(row + hh * 128, cs, T, t, lane);
+  const float b = rope_norm_head(row + d + hh * 128, cs, T, t, lane);
+  if (lane == 0) {
+    rq[w] = a;
+    rk[w] = b;
+  }
+}
+
+// dx for one head: d_rot = r (dy - y mean(dy y)); dx = R^T d_rot
+__device__ __forceinline__ void rope_norm_head_bwd(float dy1, float dy2, const uint16_t* y, float rr,
+                                                   const float* cs, int T, int t, int lane,
+                                                   uint16_t* out) {
+  const float y1 = bf2f(y[lane]), y2 = bf2f(y[lane + 64]);
+  const float dot = wave_sum(dy1 * y1 + dy2 * y2) / 128.f;
+  const float d1 = rr * (dy1 - y1 * dot), d2 = rr * (dy2 - y2 * dot);
+  const float c = cs[t * 64 + lane], sn = cs[T * 64 + t * 64 + lane];
+  out[lane] = f2bf(d1 * c + d2 * sn);
+  out[lane + 64] = f2bf(-d1 * sn + d2 * c);
+}
+
+__global__ void rope_qknorm_bwd_kernel(const float* __restrict__ dq_acc, uint16_t* __restrict__ dqkv,
+                                       const uint16_t* __restrict__ qkv, const float* __restrict__ rq,
+                                       const float* __restrict__ rk, const float* __restrict__ cs,
+                                       long long N, int T, int H) {
+  const int lane = threadIdx.x & 63;
+  const long long w = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (w >= N * H) return;
+  const long long n = w / H;
+  const int hh = (int)(w % H), t = (int)(n % T);
+  const int d = H * 128;
+  const float* dq = dq_acc + n * d + hh * 128;
+  rope_norm_head_bwd(dq[lane], dq[lane + 64], qkv + n * 3 * d + hh * 128, rq[w], cs, T, t, lane,
+                     dqkv + n * 3 * d + hh * 128);
+  uint16_t* dk = dqkv + n * 3 * d + d + hh * 128;
+  const float k1 = bf2f(dk[lane]), k2 = bf2f(dk[lane + 64]);
+  rope_norm_head_bwd(k1, k2, qkv + n * 3 * d + d + hh * 128, rk[w], cs, T, t, lane, dk);
+}
+
+// lse = log-sum-exp over the per-tile (max, sum exp) partials; loss = lse - z[target]
+__global__ void ce_reduce_kernel(const float2* __restrict__ part, int nparts, const float* __restrict__ zt,
+                                 float* __restrict__ lse, float* __restrict__ row_loss,
+                                 float* __restrict__ lse_out, long long N) {
+  const int lane = threadIdx.x & 63;
+  const long long n = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (n >= N) return;
+  const float2* p = part + n * nparts;
+  float m = -INFINITY;
+  for (int i = lane; i < nparts; i += 64) m = fmaxf(m, p[i].x);
+  m = wave_max(m);
+  float s = 0.f;
+  for (int i = lane; i < nparts; i += 64) s += p[i].y * __expf(p[i].x - m);
+  s = wave_sum(s);
+  if (lane == 0) {
+    const float l = m + logf(s);
+    lse[n] = l;
+    row_loss[n] = l - zt[n];
+    if (lse_out) lse_out[n] = l;
+  }
+}
+
+// loss = mean(row_loss), one block, double accumulation (deterministic)
+__global__ void loss_mean_kernel(const float* __restrict__ row_loss, float* __restrict__ loss, long long N) {
+  __shared__ double red[1024 / 64];
+  double s = 0.0;
+  for (long long i = threadIdx.x; i < N; i += blockDim.x) s += (double)row_loss[i];
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o, 64);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = s;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    double t = 0.0;
+    for (int i = 0; i < (int)(blockDim.x / 64); ++i) t += red[i];
+    loss[0] = (float)(t / (double)N);
+  }
+}
+
+// ---------------------------- Muon elementwise ------------------------------
+__global__ void muon_momentum_kernel(float* __restrict__ M, const float* __restrict__ G, long long n, float mu) {
+  long long i = ((long long)blockIdx.x * blockDim.x + threadIdx.x) * 4;
+  const long long stride = (long long)gridDim.x * blockDim.x * 4;
+  for (; i < n; i += stride) {
+    if (i + 3 < n) {
+      float4 m = *reinterpret_cast<const float4*>(M + i);
+      const float4 g = *reinterpret_cast<const float4*>(G + i);
+      m.x = mu * m.x + g.x; m.y = mu * m.y + g.y; m.z = mu * m.z + g.z; m.w = mu * m.w + g.w;
+      *reinterpret_cast<float4*>(M + i) = m;
+    } else {
+      for (int j = 0; i + j < n; ++j) M[i + j] = mu * M[i + j] + G[i + j];
+    }
+  }
+}
+
+// partial[b * nblk + blk] = sum of squares of chunk blk of matrix b
+__global__ void frob_partial_kernel(const float* __restrict__ X, float* __restrict__ partial,
+                                    long long per, int nblk) {
+  const int b = blockIdx.y, blk = blockIdx.x;
+  const long long chunk = (per + nblk - 1) / nblk;
+  const long long beg = blk * chunk, end = min(per, beg + chunk);
+  const float* x = X + (long long)b * per;
+  float s = 0.f;
+  for (long long i = beg + threadIdx.x; i < end; i += blockDim.x) s += x[i] * x[i];
+  __shared__ float red[4];
+  s = wave_sum(s);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = s;
+  __syncthreads();
+  if (threadIdx.x == 0) partial[(long long)b * nblk + blk] = red[0] + red[1] + red[2] + red[3];
+}
+
+__device__ __forceinline__ float frob_norm(const float* partial, int b, int nblk) {
+  double s = 0.0;
+  for (int i = 0; i < nblk; ++i) s += (double)partial[(long long)b * nblk + i];
+  return (float)sqrt(s);
+}
+
+// 64x64 output tiles, 256 threads; TR: out[i][j] = in[j][i]
+template <bool TR>
+__global__ void ns_init_kernel(const float* __restrict__ src, const float* __restrict__ partial, int nblk,
+                               float* __restrict__ X, uint16_t* __restrict__ Xb, int rows, int cols,
+                               float eps) {
+  // output oriented [l, s]: l = max(rows, cols), s = min
+  const int b = blockIdx.z;
+  const int lr = TR ? cols : rows, ls = TR ? rows : cols;
+  const float inv = 1.0f / (frob_norm(partial, b, nblk) + eps);
+  const float* in = src + (long long)b * rows * cols;
+  float* out = X + (long long)b * rows * cols;
+  uint16_t* outb = Xb + (long long)b * rows * cols;
+  const int i0 = blockIdx.y * 64, j0 = blockIdx.x * 64;
+  __shared__ float tile[64][65];
+  if (TR) {
+    // in is [ls rows? no: in is [rows, cols] = [ls, lr]; out[i][j] = in[j][i]
+    for (int e = threadIdx.x; e < 64 * 64; e += 256) {
+      const int jj = e / 64, ii = e % 64;  // read in[j0+jj][i0+ii] coalesced along ii
+      const int gj = j0 + jj, gi = i0 + ii;
+      tile[jj][ii] = (gj < ls && gi < lr) ? in[(long long)gj * lr + gi] : 0.f;
+    }
+    __syncthreads();
+    for (int e = threadIdx.x; e < 64 * 64; e += 256) {
+      const int ii = e / 64, jj = e % 64;
+      const int gi = i0 + ii, gj = j0 + jj;
+      if (gi < lr && gj < ls) {
+        const float v = tile[jj][ii] * inv;
+        out[(long long)gi * ls + gj] = v;
+        outb[(long long)gi * ls + gj] = f2bf(v);
+      }
+    }
+  } else {
+    for (int e = threadIdx.x; e < 64 * 64; e += 256) {
+      const int ii = e / 64, jj = e % 64;
+      const int gi = i0 + ii, gj = j0 + jj;
+      if (gi < lr && gj < ls) {
+        const float v = in[(long long)gi * ls + gj] * inv;
+        out[(long long)gi * ls + gj] = v;
+        outb[(long long)gi * ls + gj] = f2bf(v);
+      }
+    }
+  }
+}
+
+// output tiles over W [rows, cols]; X oriented [l, s] (transposed when TR)
+template <bool TR>
+__global__ void muon_apply_kernel(const float* __restrict__ X, float* __restrict__ W, uint16_t* __restrict__ Wb,
+                                  float* __restrict__ O_out, int rows, int cols, float lr, float wd) {
+  const int b = blockIdx.z;
+  const float* x = X + (long long)b * rows * cols;
+  const long long base = (long long)b * rows * cols;
+  const int r0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
+  __shared__ float tile[64][65];
+  if (TR) {
+    // X is [cols, rows]; O[r][c] = X[c][r]
+    for (int e = threadIdx.x; e < 64 * 64; e += 256) {
+      const int cc = e / 64, rr = e % 64;
+      const int gc = c0 + cc, gr = r0 + rr;
+      tile[cc][rr] = (gc < cols && gr < rows) ? x[(long long)gc * rows + gr] : 0.f;
+    }
+    __syncthreads();
+  }
+  const float decay = 1.f - lr * wd;
+  for (int e = threadIdx.x; e < 64 * 64; e += 256) {
+    const int rr = e / 64, cc = e % 64;
+    const int gr = r0 + rr, gc = c0 + cc;
+    if (gr < rows && gc < cols) {
+      const long long idx = (long long)gr * cols + gc;
+      const float o = TR ? tile[cc][rr] : x[idx];
+      if (O_out) O_out[base + idx] = o;
+      if (W) {
+        const float w = W[base + idx] * decay - lr * o;
+        W[base + idx] = w;
+        if (Wb) Wb[base + idx] = f2bf(w);
+      }
+    }
+  }
+}
+
+}  // namespace
+
+// ----------------------------------------------------------------------------
+// launchers
+// ----------------------------------------------------------------------------
+int launch_fill_f32(float* p, long long n, float v, hipStream_t s) {
+  if (n <= 0) return 0;
+  const int blocks = (int)min<long long>(nblocks(n, 1024), 8192);
+  hipLaunchKernelGGL(fill_f32_kernel, dim3(blocks), dim3(256), 0, s, p, n, v);
+  GS_LAUNCH_CHECK("fill_f32");
+  return 0;
+}
+
+int launch_cast_bf16(const float* src, uint16_t* dst, long long n, hipStream_t s) {
+  if (n <= 0) return 0;
+  const int blocks = (int)min<long long>(nblocks(n, 1024), 16384);
+  hipLaunchKernelGGL(cast_bf16_kernel, dim3(blocks), dim3(256), 0, s, src, dst, n);
+  GS_LAUNCH_CHECK("cast_bf16");
+  return 0;
+}
+
+int launch_rope_table(float* cs, int T, hipStream_t s) {
+  hipLaunchKernelGGL(rope_table_kernel, dim3(nblocks((long long)T * 64, 256)), dim3(256), 0, s, cs, T);
+  GS_LAUNCH_CHECK("rope_table");
+  return 0;
+}
+
+int launch_embed_fwd(const int* ids, const uint16_t* wte, float* x, int B, int T, int d, hipStream_t s) {
+  hipLaunchKernelGGL(embed_fwd_kernel, dim3(nblocks((long long)B * T, 4)), dim3(256), 0, s, ids, wte, x, B, T, d);
+  GS_LAUNCH_CHECK("embed_fwd");
+  return 0;
+}
+
+int launch_embed_bwd(const int* ids, const float* g, float* dwte, int B, int T, int d, hipStream_t s) {
+  hipLaunchKernelGGL(embed_bwd_kernel, dim3(nblocks((long long)B * T, 4)), dim3(256), 0, s, ids, g, dwte, B, T, d);
+  GS_LAUNCH_CHECK("embed_bwd");
+  return 0;
+}
+
+int launch_rmsnorm_fwd(const float* x, uint16_t* h, float* r, long long N, int d, hipStream_t s) {
+  hipLaunchKernelGGL(rmsnorm_fwd_kernel, dim3(nblocks(N, 4)), dim3(256), 0, s, x, h, r, N, d);
+  GS_LAUNCH_CHECK("rmsnorm_fwd");
+  return 0;
+}
+
+int launch_rmsnorm_bwd(const float* dh, const uint16_t* h, const float* r, float* g, uint16_t* g_bf,
+                       long long N, int d, hipStream_t s) {
+  hipLaunchKernelGGL(rmsnorm_bwd_kernel, dim3(nblocks(N, 4)), dim3(256), 0, s, dh, h, r, g, g_bf, N, d);
+  GS_LAUNCH_CHECK("rmsnorm_bwd");
+  return 0;
+}
+
+int launch_rope_qknorm_fwd(uint16_t* qkv, float* rq, float* rk, const float* cs, long long N, int T, int H,
+                           hipStream_t s) {
+  hipLaunchKernelGGL(rope_qknorm_fwd_kernel, dim3(nblocks(N * H, 4)), dim3(256), 0, s, qkv, rq, rk, cs, N, T, H);
+  GS_LAUNCH_CHECK("rope_qknorm_fwd");
+  return 0;
+}
+
+int launch_rope_qknorm_bwd(const float* dq_acc, uint16_t* dqkv, const uint16_t* qkv, const float* rq,
+                           const float* rk, const float* cs, long long N, int T, int H, hipStream_t s) {
+  hipLaunchKernelGGL(rope_qknorm_bwd_kernel, dim3(nblocks(N * H, 4)), dim3(256), 0, s, dq_acc, dqkv, qkv, rq,
+                     rk, cs, N, T, H);
+  GS_LAUNCH_CHECK("rope_qknorm_bwd");
+  return 0;
+}
+
+int launch_ce_reduce(const float* part, int nparts, const float* zt, float* lse, float* row_loss,
+                     float* lse_out, long long N, hipStream_t s) {
+  hipLaunchKernelGGL(ce_reduce_kernel, dim3(nblocks(N, 4)), dim3(256), 0, s,
+                     reinterpret_cast<const float2*>(part), nparts, zt, lse, row_loss, lse_out, N);
+  GS_LAUNCH_CHECK("ce_reduce");
+  return 0;
+}
+
+int launch_loss_mean(const float* row_loss, float* loss, long long N, hipStream_t s) {
+  hipLaunchKernelGGL(loss_mean_kernel, dim3(1), dim3(1024), 0, s, row_loss, loss, N);
+  GS_LAUNCH_CHECK("loss_mean");
+  return 0;
+}
+
+int launch_muon_momentum(float* M, const float* G, long long n, float mu, hipStream_t s) {
+  const int blocks = (int)min<long long>(nblocks(n, 1024), 16384);
+  hipLaunchKernelGGL(muon_momentum_kernel, dim3(blocks), dim3(256), 0, s, M, G, n, mu);
+  GS_LAUNCH_CHECK("muon_momentum");
+  return 0;
+}
+
+int launch_frob_partial(const float* X, float* partial, int count, long long per, int nblk, hipStream_t s) {
+  hipLaunchKernelGGL(frob_partial_kernel, dim3(nblk, count), dim3(256), 0, s, X, partial, per, nblk);
+  GS_LAUNCH_CHECK("frob_partial");
+  return 0;
+}
+
+int launch_ns_init(const float* src, const float* partial, int nblk, float* X, uint16_t* Xb, int count,
+                   int rows, int cols, float eps, hipStream_t s) {
+  const bool tr = rows < cols;
+  const int lr = tr ? cols : rows, ls = tr ? rows : cols;
+  dim3 grid((ls + 63) / 64, (lr + 63) / 64, count);
+  if (tr)
+    hipLaunchKernelGGL(ns_init_kernel<true>, grid, dim3(256), 0, s, src, partial, nblk, X, Xb, rows, cols, eps);
+  else
+    hipLaunchKernelGGL(ns_init_kernel<false>, grid, dim3(256), 0, s, src, partial, nblk, X, Xb, rows, cols, eps);
+  GS_LAUNCH_CHECK("ns_init");
+  return 0;
+}
+
+int launch_muon_apply(const float* X, float* W, uint16_t* Wb, float* O_out, int count, int rows, int cols,
+                      float lr, float wd, hipStream_t s) {
+  const bool tr = rows < cols;
+  dim3 grid((cols + 63) / 64, (rows + 63) / 64, count);
+  if (tr)
+    hipLaunchKernelGGL(muon_apply_kernel<true>, grid, dim3(256), 0, s, X, W, Wb, O_out, rows, cols, lr, wd);
+  else
+    hipLaunchKernelGGL(muon_apply_kernel<false>, grid, dim3(256), 0, s, X, W, Wb, O_out, rows, cols, lr, wd);
+  GS_LAUNCH_CHECK("muon_apply");
+  return 0;
+}
+
+}  // namespace gs

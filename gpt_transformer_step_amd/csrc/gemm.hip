@@ -1,0 +1,21 @@
+// Dispatch of the bf16 GEMM family by operand layout (kernel in gemm_kernel.h).
+#include "gemm_kernel.h"
+
+namespace gs {
+
+int gemm_bf16_kk(const GemmArgs& a, int epi, hipStream_t s);
+int gemm_bf16_km(const GemmArgs& a, int epi, hipStream_t s);
+int gemm_bf16_mm(const GemmArgs& a, int epi, hipStream_t s);
+int gemm_bf16_mk(const GemmArgs& a, int epi, hipStream_t s);
+
+int gemm_tile_n(const GemmArgs& a) { return use_big_tile(a) ? 256 : 128; }
+
+int gemm_bf16(const GemmArgs& a, int epi, hipStream_t s) {
+  if (a.M <= 0 || a.N <= 0 || a.batch <= 0) return 0;
+  if (a.a_kcontig && a.b_kcontig) return gemm_bf16_kk(a, epi, s);
+  if (a.a_kcontig) return gemm_bf16_km(a, epi, s);
+  if (a.b_kcontig) return gemm_bf16_mk(a, epi, s);
+  return gemm_bf16_mm(a, epi, s);
+}
+
+}  // namespace gs

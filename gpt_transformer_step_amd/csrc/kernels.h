@@ -1,0 +1,48 @@
+// Internal launchers of the non-GEMM kernels of libgptstep.  All take device
+// pointers, enqueue on `s` and return 0 or a gpt_status error code.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gs {
+
+// --- elementwise / bandwidth-bound (elementwise.hip) -----------------------
+int launch_fill_f32(float* p, long long n, float v, hipStream_t s);
+int launch_cast_bf16(const float* src, uint16_t* dst, long long n, hipStream_t s);
+int launch_rope_table(float* cos_sin /* [T, 64] cos then [T, 64] sin */, int T, hipStream_t s);
+int launch_embed_fwd(const int* ids, const uint16_t* wte, float* x, int B, int T, int d, hipStream_t s);
+int launch_embed_bwd(const int* ids, const float* g, float* dwte, int B, int T, int d, hipStream_t s);
+int launch_rmsnorm_fwd(const float* x, uint16_t* h, float* r, long long N, int d, hipStream_t s);
+int launch_rmsnorm_bwd(const float* dh, const uint16_t* h, const float* r, float* g, uint16_t* g_bf,
+                       long long N, int d, hipStream_t s);
+int launch_rope_qknorm_fwd(uint16_t* qkv, float* rq, float* rk, const float* cos_sin, long long N,
+                           int T, int H, hipStream_t s);
+int launch_rope_qknorm_bwd(const float* dq_acc, uint16_t* dqkv, const uint16_t* qkv, const float* rq,
+                           const float* rk, const float* cos_sin, long long N, int T, int H,
+                           hipStream_t s);
+int launch_ce_reduce(const float* part, int nparts, const float* zt, float* lse, float* row_loss,
+                     float* lse_out, long long N, hipStream_t s);
+int launch_loss_mean(const float* row_loss, float* loss, long long N, hipStream_t s);
+int launch_logits_copy(const float* part_unused, hipStream_t s);
+
+// --- Muon elementwise (elementwise.hip) ------------------------------------
+int launch_muon_momentum(float* M, const float* G, long long n, float mu, hipStream_t s);
+int launch_frob_partial(const float* X, float* partial, int count, long long per, int nblk,
+                        hipStream_t s);
+// X[b] (oriented [l, s]) = src[b] / (||src[b]|| + eps); transposed when rows < cols
+int launch_ns_init(const float* src, const float* partial, int nblk, float* X, uint16_t* Xb,
+                   int count, int rows, int cols, float eps, hipStream_t s);
+// O = X oriented back; W = W (1 - lr wd) - lr O; W_bf16 = bf16(W); O_out = O
+int launch_muon_apply(const float* X, float* W, uint16_t* Wb, float* O_out, int count, int rows,
+                      int cols, float lr, float wd, hipStream_t s);
+
+// --- attention (attention.hip) ---------------------------------------------
+int launch_attn_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, long long ld_qkv,
+                    uint16_t* out, long long ld_out, float* lse, int B, int H, int T, hipStream_t s);
+int launch_attn_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, long long ld_qkv,
+                    const uint16_t* out, const uint16_t* dout, long long ld_out, const float* lse,
+                    float* delta, float* dq_acc, uint16_t* dk, uint16_t* dv, long long ld_dkv, int B,
+                    int H, int T, hipStream_t s);
+
+}  // namespace gs

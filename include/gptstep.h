@@ -1,0 +1,156 @@
+/*
+ * gptstep.h -- C ABI of libgptstep.so: one pretraining step of a depth-
+ * parameterised decoder-only GPT (forward, backward, Muon update) on AMD
+ * MI355X (gfx950).
+ *
+ * What is computed follows the nanochat pages:
+ *   dev.to, "¿Cómo Entrenar Tu Propio ChatGPT por $50?":
+ *     "La Filosofía: Un Solo Selector" -- one dial, the depth;
+ *     "1. Modelo GPT (nanochat/gpt.py)" -- RoPE, QK normalisation, untied
+ *        embedding and head, ReLU^2 MLP, causal flash attention;
+ *     "2. Optimizador Muon (nanochat/optim.py)" -- Newton-Schulz iteration
+ *        A = X^T X, B = b A + c A A, X = a X + X B over a coefficient table;
+ *     "3. Gestión de Precisión (nanochat/common.py)" -- fp32 master weights,
+ *        weights cast to the bf16 compute dtype for each matmul;
+ *   apidog.com/pt and apidog.com/de, the precision sections -- the fp8 option
+ *     with one scale per tensor ("escalonamento por tensor", "tensorweise").
+ *
+ * Shapes come from the depth alone: d_model = 64 * depth, heads of width 128
+ * (so n_head = d_model / 128 and depth must be even), MLP hidden = 4 * d_model.
+ *
+ * Conventions for every entry point:
+ *   - Pointers are DEVICE pointers unless the comment says "host".
+ *   - The caller owns all memory.  The library never allocates or frees
+ *     device memory; scratch space comes from a caller-provided workspace
+ *     whose size is queried first.
+ *   - Every call validates its arguments on the host first and returns a
+ *     status; no argument error ever reaches the device.  Kernel launch
+ *     failures return GPT_ERR_HIP with details in gpt_last_error().
+ *   - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL = the
+ *     default stream).  No call synchronises the device; results (including
+ *     the loss) are in device memory when the stream reaches them.
+ *   - Preconditions that are not checked (they would need a device sync):
+ *     0 <= id < vocab for every token id; device buffers of the stated sizes;
+ *     gpt_step_bwd follows gpt_step_fwd on the same stream with the same
+ *     shape, parameters, ids and workspace, with no other use of that
+ *     workspace in between.
+ *   - Not thread-safe across calls that share a workspace or outputs.
+ */
+#ifndef GPTSTEP_H
+#define GPTSTEP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef void* gpt_stream_t; /* hipStream_t */
+
+typedef enum {
+  GPT_OK = 0,
+  GPT_ERR_INVALID_ARG = -1, /* null required pointer, bad count/size/flag */
+  GPT_ERR_SHAPE = -2,       /* depth odd or < 2, vocab/seq_len/batch < 1, too large */
+  GPT_ERR_WORKSPACE = -3,   /* workspace smaller than the queried size */
+  GPT_ERR_HIP = -4,         /* a HIP runtime call or kernel launch failed */
+  GPT_ERR_UNSUPPORTED = -5  /* unknown precision or layout */
+} gpt_status;
+
+typedef enum {
+  GPT_PREC_BF16 = 0, /* bf16 operands, fp32 accumulation */
+  GPT_PREC_FP8 = 1   /* the four block GEMMs in fp8 (E4M3 activations and
+                        weights, E5M2 output gradients, one fp32 scale per
+                        tensor); head, attention and Muon stay bf16 */
+} gpt_precision;
+
+/* The model and batch.  d_model = 64*depth, n_head = d_model/128,
+ * hidden = 4*d_model.  Limits: 2 <= depth <= 64 and even; 1 <= vocab <= 2^24;
+ * 1 <= seq_len <= 16384; 1 <= batch; batch*seq_len <= 2^24. */
+typedef struct {
+  int32_t depth;
+  int32_t vocab;
+  int32_t seq_len;   /* T: tokens per sequence (ids carry T+1 per row) */
+  int32_t batch;     /* B: sequences per step */
+  int32_t precision; /* gpt_precision */
+} gpt_shape;
+
+/* Packed parameter buffers, all with gpt_param_count() elements in the packed
+ * order: wte [V,d] | for each layer: wq, wk, wv, wo [d,d] | for each layer
+ * wfc [4d,d] | for each layer wproj [d,4d] | lm_head [V,d], each row-major
+ * [out, in].  wq, wk, wv of one layer are adjacent, so they form one [3d,d]
+ * operand.  The S group is the 4*depth [d,d] matrices, the F group the depth
+ * wfc matrices, the P group the depth wproj matrices. */
+typedef struct {
+  const float* master;  /* fp32 master weights (read by nothing in fwd/bwd) */
+  const uint16_t* bf16; /* bf16 working copy (bit patterns) used by fwd/bwd */
+  float* grad;          /* fp32 gradients, written by gpt_step_bwd */
+} gpt_params;
+
+/* Number of parameters (elements) of the packed buffers. */
+gpt_status gpt_param_count(const gpt_shape* shape, size_t* n_params /* host */);
+
+/* Element offsets of the 2 + 6*depth tensors in packed order (wte, then per
+ * layer wq wk wv wo, then each wfc, then each wproj, then lm_head).
+ * `offsets` (host) must hold `capacity` entries; *n_tensors (host) receives
+ * the count.  GPT_ERR_INVALID_ARG when capacity is too small. */
+gpt_status gpt_param_layout(const gpt_shape* shape, size_t* offsets, int32_t capacity,
+                            int32_t* n_tensors);
+
+/* Bytes of workspace that gpt_step_fwd / gpt_step_bwd need for this shape
+ * (activations saved by the forward pass plus backward scratch). */
+gpt_status gpt_workspace_size(const gpt_shape* shape, size_t* bytes /* host */);
+
+/* dst[i] = bf16(src[i]), round to nearest even; n elements. */
+gpt_status gpt_cast_bf16(const float* src, uint16_t* dst, size_t n, gpt_stream_t stream);
+
+/* Forward pass and loss (dev.to page, "1. Modelo GPT"; the loss is the mean
+ * cross-entropy of next-token prediction over all batch*seq_len positions).
+ *   ids     int32 [batch, seq_len+1]; inputs ids[:, :T], targets ids[:, 1:].
+ *   loss    fp32 [1]: mean loss.
+ *   row_lse nullable fp32 [batch*seq_len]: log-sum-exp of each row's logits.
+ *   logits  nullable fp32 [batch*seq_len, vocab]: full logits, meant for
+ *           tiny shapes only (the normal path never forms them).
+ *   ws      workspace of at least gpt_workspace_size() bytes, 256-aligned.
+ * The workspace keeps the activations gpt_step_bwd needs. */
+gpt_status gpt_step_fwd(const gpt_shape* shape, const gpt_params* params, const int32_t* ids,
+                        float* loss, float* row_lse, float* logits, void* ws, size_t ws_bytes,
+                        gpt_stream_t stream);
+
+/* Backward pass of the mean loss: writes (accumulate = 0) or adds
+ * (accumulate = 1) the gradient of every parameter into params->grad. */
+gpt_status gpt_step_bwd(const gpt_shape* shape, const gpt_params* params, const int32_t* ids,
+                        int32_t accumulate, void* ws, size_t ws_bytes, gpt_stream_t stream);
+
+/* Workspace bytes for muon_update on `count` matrices of [rows, cols]. */
+gpt_status muon_workspace_size(int32_t count, int32_t rows, int32_t cols, size_t* bytes /* host */);
+
+/* Muon update of `count` same-shape fp32 matrices [rows, cols], contiguous
+ * (dev.to page, "2. Optimizador Muon"):
+ *   M <- momentum * M + G                      (skipped when M is NULL: M := G)
+ *   X <- M / (||M||_F + 1e-7), oriented so that rows >= cols
+ *   for each (a, b, c) of coeffs[0 .. ns_steps-1]:
+ *       A = X^T X;  B = b A + c A A;  X = a X + X B   (bf16 MFMA, fp32 accumulate,
+ *                                                      X kept in fp32)
+ *   O = X oriented back to [rows, cols]
+ *   W <- W * (1 - lr * weight_decay) - lr * O;  W_bf16 <- bf16(W)
+ * W, W_bf16 and O_out are each nullable (W NULL: no apply; O_out: copy of O).
+ * coeffs: HOST array of 3*ns_steps floats (a, b, c per iteration);
+ * 1 <= ns_steps <= 16.  G may alias M only when M is NULL. */
+gpt_status muon_update(float* W, uint16_t* W_bf16, const float* G, float* M, float* O_out,
+                       int32_t count, int32_t rows, int32_t cols, const float* coeffs,
+                       int32_t ns_steps, float lr, float momentum, float weight_decay, void* ws,
+                       size_t ws_bytes, gpt_stream_t stream);
+
+/* Text of a status, and the message of the last failing call on this thread
+ * (empty when none).  Both return static or thread-local storage. */
+const char* gpt_status_string(gpt_status status);
+const char* gpt_last_error(void);
+
+/* Library ABI version (bumped on any signature change). */
+int32_t gpt_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* GPTSTEP_H */

@@ -1,0 +1,72 @@
+/*
+ * gptstep_ops.h -- component entry points of libgptstep.so.
+ *
+ * These expose the individual steps that gpt_step_fwd / gpt_step_bwd /
+ * muon_update chain together, so each can be checked on its own.  They use
+ * the same kernels as the step entry points and follow the conventions of
+ * gptstep.h (device pointers unless marked host; caller-owned memory; host
+ * validation first; asynchronous on `stream`; status return).
+ */
+#ifndef GPTSTEP_OPS_H
+#define GPTSTEP_OPS_H
+
+#include "gptstep.h"
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Operand layouts of gpt_op_gemm.  An operand is a logical [rows, K] matrix:
+ *   GPT_LAYOUT_K_CONTIG : element (r, k) at X[r * ld + k]   (row-major [rows, K])
+ *   GPT_LAYOUT_MN_CONTIG: element (r, k) at X[k * ld + r]   (row-major [K, rows]) */
+enum { GPT_LAYOUT_K_CONTIG = 0, GPT_LAYOUT_MN_CONTIG = 1 };
+enum { GPT_DTYPE_F32 = 0, GPT_DTYPE_BF16 = 1 };
+
+/* Batched bf16 matrix product with fp32 accumulation (the linear layers of
+ * dev.to "¿Cómo Entrenar Tu Propio ChatGPT por $50?", "3. Gestión de
+ * Precisión": F.linear with the weight cast to bf16):
+ *   C[b][m, n] = alpha * sum_k A[b][m, k] * B[b][n, k]  (+ beta * C[b][m, n] for f32 C)
+ * for b < batch, m < M, n < N, k < K.  A, B: bf16 bit patterns; strides
+ * stride_* in elements between batch items; ld* in elements, multiples of 8;
+ * A, B, C 16-byte aligned.  c_dtype: GPT_DTYPE_F32 or GPT_DTYPE_BF16 (beta
+ * must be 0 for bf16).  M, N, K, batch >= 0 (0 is a no-op). */
+gpt_status gpt_op_gemm(int32_t M, int32_t N, int32_t K, int32_t batch, const uint16_t* A,
+                       int32_t a_layout, int64_t lda, int64_t stride_a, const uint16_t* B,
+                       int32_t b_layout, int64_t ldb, int64_t stride_b, void* C, int32_t c_dtype,
+                       int64_t ldc, int64_t stride_c, float alpha, float beta, gpt_stream_t stream);
+
+/* Causal multi-head attention forward with head width 128 (dev.to page,
+ * "5. Unificación Flash Attention": flash_attn_func(q, k, v, causal=True)):
+ *   out[b,t,h,:] = sum_{j<=t} softmax_j(q[b,t,h,:] . k[b,j,h,:] / sqrt(128)) v[b,j,h,:]
+ * q, k, v, out: bf16, element (b, t, h, e) at ptr[(b*T + t) * ld + h*128 + e]
+ * (ld in elements, multiple of 8).  lse: fp32 [B, H, T], the natural-log
+ * log-sum-exp of each row of scaled scores (needed by the backward). */
+gpt_status gpt_op_attention_fwd(int32_t batch, int32_t n_head, int32_t seq_len, const uint16_t* q,
+                                const uint16_t* k, const uint16_t* v, int64_t ld_qkv,
+                                uint16_t* out, int64_t ld_out, float* lse, gpt_stream_t stream);
+
+/* Backward of gpt_op_attention_fwd given dout (same layout as out):
+ *   dq_acc fp32, element (b,t,h,e) at dq_acc[(b*T+t) * H*128 + h*128 + e] (overwritten);
+ *   dk, dv bf16 in the q/k/v layout with leading dimension ld_dkv;
+ *   delta: fp32 scratch [B, H, T] (receives rowsum(dout * out)). */
+gpt_status gpt_op_attention_bwd(int32_t batch, int32_t n_head, int32_t seq_len, const uint16_t* q,
+                                const uint16_t* k, const uint16_t* v, int64_t ld_qkv,
+                                const uint16_t* out, const uint16_t* dout, int64_t ld_out,
+                                const float* lse, float* delta, float* dq_acc, uint16_t* dk,
+                                uint16_t* dv, int64_t ld_dkv, gpt_stream_t stream);
+
+/* Size in bytes and offset of a named activation inside the step workspace
+ * after gpt_step_fwd, for inspection.  which: 0 residual x after the last
+ * layer (fp32 [N,d]); 1 h1 of `layer` (bf16 [N,d], normed input of the
+ * attention); 2 qkv of `layer` (bf16 [N,3d], q and k after rotation and
+ * normalisation); 3 attention output of `layer` (bf16 [N,d]); 4 h2 of
+ * `layer` (bf16 [N,d]); 5 relu^2 activation of `layer` (bf16 [N,4d]);
+ * 6 final normed hidden state (bf16 [N,d]); 7 per-row lse (fp32 [N]);
+ * 8 per-row loss (fp32 [N]).  N = batch*seq_len. */
+gpt_status gpt_workspace_tensor(const gpt_shape* shape, int32_t which, int32_t layer,
+                                size_t* offset /* host */, size_t* bytes /* host */);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* GPTSTEP_OPS_H */
