@@ -44,6 +44,7 @@ from dataclasses import dataclass
 import numpy as np
 
 from . import fp8 as _fp8
+from . import precision as _precision
 
 
 @dataclass(frozen=True)
@@ -208,7 +209,7 @@ def param_shapes(cfg):
 # the step
 # ----------------------------------------------------------------------------
 
-def _forward_backward_chunk(P, ids, cfg, loss_scale, dtype, want_grads, want_logits, fp8, cos, sin):
+def _forward_backward_chunk(P, ids, cfg, loss_scale, dtype, want_grads, want_logits, fp8, cos, sin, op):
     B, T1 = ids.shape
     T = T1 - 1
     d, H, hd = cfg.d_model, cfg.n_head, cfg.head_dim
@@ -222,23 +223,27 @@ def _forward_backward_chunk(P, ids, cfg, loss_scale, dtype, want_grads, want_log
     for i in range(cfg.n_layer):
         wqkv = np.concatenate([P[f"wq.{i}"], P[f"wk.{i}"], P[f"wv.{i}"]], axis=0)
         h1, r1 = rms_norm(x, eps)
-        qkv = _lin_fwd(h1, wqkv, fp8)
+        h1o = op(h1)
+        qkv = _lin_fwd(h1o, wqkv, fp8)
         q_raw = qkv[:, :d].reshape(B, T, H, hd).transpose(0, 2, 1, 3)
         k_raw = qkv[:, d:2 * d].reshape(B, T, H, hd).transpose(0, 2, 1, 3)
-        v = qkv[:, 2 * d:].reshape(B, T, H, hd).transpose(0, 2, 1, 3)
+        v = op(qkv[:, 2 * d:].reshape(B, T, H, hd).transpose(0, 2, 1, 3))
         qn, rq = rms_norm(rope(q_raw, cos, sin), eps)
         kn, rk = rms_norm(rope(k_raw, cos, sin), eps)
-        y, lse_att = causal_attention(qn, kn, v)
-        y2 = y.transpose(0, 2, 1, 3).reshape(R, d)
+        qs, ks = op(qn), op(kn)
+        y, lse_att = causal_attention(qs, ks, v)
+        y2 = op(y.transpose(0, 2, 1, 3).reshape(R, d))
         x = x + _lin_fwd(y2, P[f"wo.{i}"], fp8)
         h2, r2 = rms_norm(x, eps)
-        u = _lin_fwd(h2, P[f"wfc.{i}"], fp8)
-        a = np.maximum(u, 0.0) ** 2
+        h2o = op(h2)
+        u = _lin_fwd(h2o, P[f"wfc.{i}"], fp8)
+        a = op(np.maximum(u, 0.0) ** 2)
         x = x + _lin_fwd(a, P[f"wproj.{i}"], fp8)
-        caches.append((h1, r1, wqkv, qn, rq, kn, rk, v, y, y2, lse_att, h2, r2, u, a))
+        caches.append((h1, h1o, r1, wqkv, qn, qs, rq, kn, ks, rk, v, y2, lse_att, h2, h2o, r2, u, a))
 
     hf, rf = rms_norm(x, eps)
-    z = hf @ P["lm_head"].T
+    hfo = op(hf)
+    z = hfo @ P["lm_head"].T
     row_loss, lse = cross_entropy(z, tgt)
     out = {"row_loss": row_loss.reshape(B, T), "lse": lse.reshape(B, T),
            "loss_sum": float(np.sum(row_loss, dtype=np.float64))}
@@ -248,26 +253,29 @@ def _forward_backward_chunk(P, ids, cfg, loss_scale, dtype, want_grads, want_log
         return out
 
     G = {}
-    dz = cross_entropy_bwd(z, tgt, lse, loss_scale)
+    dz = op(cross_entropy_bwd(z, tgt, lse, loss_scale))
     del z
-    G["lm_head"] = dz.T @ hf
+    G["lm_head"] = dz.T @ hfo
     g = rms_norm_bwd(dz @ P["lm_head"], hf, rf)
     del dz
     for i in reversed(range(cfg.n_layer)):
-        (h1, r1, wqkv, qn, rq, kn, rk, v, y, y2, lse_att, h2, r2, u, a) = caches[i]
+        (h1, h1o, r1, wqkv, qn, qs, rq, kn, ks, rk, v, y2, lse_att, h2, h2o, r2, u, a) = caches[i]
         # MLP
-        da, G[f"wproj.{i}"] = _lin_bwd(a, P[f"wproj.{i}"], g, fp8)
-        du = da * 2.0 * np.maximum(u, 0.0)
-        dh2, G[f"wfc.{i}"] = _lin_bwd(h2, P[f"wfc.{i}"], du, fp8)
+        gb = op(g)
+        da, G[f"wproj.{i}"] = _lin_bwd(a, P[f"wproj.{i}"], gb, fp8)
+        du = op(da * 2.0 * np.maximum(u, 0.0))
+        dh2, G[f"wfc.{i}"] = _lin_bwd(h2o, P[f"wfc.{i}"], du, fp8)
         g = g + rms_norm_bwd(dh2, h2, r2)
         # attention
-        dy2, G[f"wo.{i}"] = _lin_bwd(y2, P[f"wo.{i}"], g, fp8)
-        dy = dy2.reshape(B, T, H, hd).transpose(0, 2, 1, 3)
-        dqn, dkn, dv = causal_attention_bwd(qn, kn, v, y, dy, lse_att)
+        gb = op(g)
+        dy2, G[f"wo.{i}"] = _lin_bwd(y2, P[f"wo.{i}"], gb, fp8)
+        dy = op(dy2).reshape(B, T, H, hd).transpose(0, 2, 1, 3)
+        y = y2.reshape(B, T, H, hd).transpose(0, 2, 1, 3)
+        dqn, dkn, dv = causal_attention_bwd(qs, ks, v, y, dy, lse_att)
         dq = rope_bwd(rms_norm_bwd(dqn, qn, rq), cos, sin)
         dk = rope_bwd(rms_norm_bwd(dkn, kn, rk), cos, sin)
-        dqkv = np.concatenate([t.transpose(0, 2, 1, 3).reshape(R, d) for t in (dq, dk, dv)], axis=1)
-        dh1, dwqkv = _lin_bwd(h1, wqkv, dqkv, fp8)
+        dqkv = op(np.concatenate([t.transpose(0, 2, 1, 3).reshape(R, d) for t in (dq, dk, dv)], axis=1))
+        dh1, dwqkv = _lin_bwd(h1o, wqkv, dqkv, fp8)
         G[f"wq.{i}"], G[f"wk.{i}"], G[f"wv.{i}"] = dwqkv[:d], dwqkv[d:2 * d], dwqkv[2 * d:]
         g = g + rms_norm_bwd(dh1, h1, r1)
         caches[i] = None
@@ -279,7 +287,7 @@ def _forward_backward_chunk(P, ids, cfg, loss_scale, dtype, want_grads, want_log
 
 
 def forward_backward(P, ids, cfg, dtype=np.float64, want_grads=True, want_logits=False,
-                     fp8=False, seq_chunk=None):
+                     fp8=False, seq_chunk=None, bf16_operands=False):
     """One training step's forward and backward.
 
     P: dict name -> array (the bf16-rounded weight values, see precision.py);
@@ -289,12 +297,30 @@ def forward_backward(P, ids, cfg, dtype=np.float64, want_grads=True, want_logits
 
     seq_chunk: process that many sequences at a time (the sequences of a batch
     are independent up to the loss mean); not allowed with fp8, whose
-    per-tensor scales span the whole batch."""
+    per-tensor scales span the whole batch.
+
+    bf16_operands: every operand of a matrix product holds bf16 values -- the
+    precision passage's compute dtype (dev.to "3. Gestión de Precisión":
+    F.linear(x, W.to(x.dtype)) with x in bf16 on bf16-capable GPUs; the
+    attention call receives bf16 q, k, v).  The activations entering a
+    product (normed inputs, q/k/v, attention output, ReLU^2 output, head
+    input) and the gradients entering a product (dlogits, residual gradient,
+    MLP hidden gradient, attention output gradient, q/k/v gradient) are
+    rounded to bf16 (nearest even); products accumulate in `dtype`; norms,
+    rotary, softmax and the residual stream stay in `dtype`.  With False
+    (default) nothing is rounded and the result is the exact function of the
+    bf16 weights."""
     ids = np.asarray(ids)
     B, T1 = ids.shape
     T = T1 - 1
     P = {k: np.asarray(v, dtype=dtype) for k, v in P.items()}
     cos, sin = rope_tables(T, cfg.head_dim, cfg.rope_base, dtype)
+    if bf16_operands:
+        def op(t):
+            return _precision.round_bf16(t).astype(dtype)
+    else:
+        def op(t):
+            return t
     loss_scale = 1.0 / (B * T)
     if seq_chunk is None or seq_chunk >= B:
         chunks = [(0, B)]
@@ -305,7 +331,7 @@ def forward_backward(P, ids, cfg, dtype=np.float64, want_grads=True, want_logits
     total, grads, row_loss, lse, logits = 0.0, None, [], [], []
     for s, e in chunks:
         o = _forward_backward_chunk(P, ids[s:e], cfg, loss_scale, dtype, want_grads,
-                                    want_logits, fp8, cos, sin)
+                                    want_logits, fp8, cos, sin, op)
         total += o["loss_sum"]
         row_loss.append(o["row_loss"])
         lse.append(o["lse"])

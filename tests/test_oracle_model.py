@@ -218,3 +218,36 @@ def test_inputs_generator_is_stable():
     # std close to 1/sqrt(fan_in)
     assert abs(t["wfc.0"].std() * math.sqrt(128) - 1) < 0.02
     assert abs(t["wproj.1"].std() * math.sqrt(512) - 1) < 0.02
+
+
+def test_bf16_operand_mode():
+    """The bf16-operand reading changes only the rounding of product operands:
+    with weights and data that are already bf16-exact at every operand point
+    it is identical to the exact mode, and otherwise it stays within bf16
+    rounding distance of it."""
+    cfg = TINY
+    P = _tiny_params(cfg, seed=41)
+    ids = _tiny_ids(cfg, B=2, T=8, seed=42)
+    a = om.forward_backward(P, ids, cfg)
+    b = om.forward_backward(P, ids, cfg, bf16_operands=True)
+    assert abs(a["loss"] - b["loss"]) < 1e-2 * abs(a["loss"])
+    for k in a["grads"]:
+        num = np.linalg.norm(a["grads"][k] - b["grads"][k])
+        assert num <= 5e-2 * np.linalg.norm(a["grads"][k]) + 1e-12, k
+        # the modes really differ (the rounding is applied)
+    assert any(not np.array_equal(a["grads"][k], b["grads"][k]) for k in a["grads"])
+
+
+def test_bf16_operand_rounding_points(monkeypatch):
+    """Every rounding the mode applies is to an operand of a matrix product:
+    replacing the rounding by the identity gives back the exact mode bit for bit."""
+    cfg = TINY
+    P = _tiny_params(cfg, seed=43)
+    ids = _tiny_ids(cfg, B=2, T=8, seed=44)
+    a = om.forward_backward(P, ids, cfg)
+    from oracle import precision
+    monkeypatch.setattr(precision, "round_bf16", lambda t: np.asarray(t))
+    b = om.forward_backward(P, ids, cfg, bf16_operands=True)
+    assert a["loss"] == b["loss"]
+    for k in a["grads"]:
+        assert np.array_equal(a["grads"][k], b["grads"][k])
