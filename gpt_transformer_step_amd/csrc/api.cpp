@@ -2,6 +2,7 @@
 // the launch sequence of the training step.  Kernels live in the .hip files.
 
 #include <math.h>
+#include <algorithm>
 #include <string.h>
 
 #include <string>
@@ -178,3 +179,518 @@ extern "C" gpt_status gpt_op_gemm(int32_t M, int32_t N, int32_t K, int32_t batch
 }
 
 
+// ---------------------------------------------------------------------------
+// workspace layout of the step
+// ---------------------------------------------------------------------------
+namespace {
+
+constexpr size_t kAlign = 256;
+inline size_t al(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+// vocabulary chunk of the fused head backward (columns of dlogits held at once)
+inline int vocab_chunk(const Dims& D) { return D.V < 8192 ? D.V : 8192; }
+
+inline int ce_nparts(const Dims& D) {
+  GemmArgs a;
+  a.M = (int)D.N; a.N = D.V; a.K = D.d; a.batch = 1; a.k_split = 1;
+  const int bn = gemm_tile_n(a);
+  return ((D.V + bn - 1) / bn) * 2;
+}
+
+struct Layer {
+  size_t h1, r1, qkv, rq, rk, att, lse, h2, r2, act;
+};
+
+struct WS {
+  size_t cs, x, hf, rf, part, zt, lse, row_loss;
+  std::vector<Layer> layer;
+  // backward scratch
+  size_t g, g_bf, dh, du, dout, delta, dq_acc, dqkv, dz;
+  size_t total;
+};
+
+WS ws_layout(const Dims& D) {
+  WS w;
+  size_t o = 0;
+  auto take = [&](size_t bytes) { size_t r = o; o = al(o + bytes); return r; };
+  const size_t N = (size_t)D.N, d = D.d, H = D.H;
+  w.cs = take(2 * (size_t)D.T * 64 * 4);
+  w.x = take(N * d * 4);
+  w.layer.resize(D.L);
+  for (int l = 0; l < D.L; ++l) {
+    Layer& L = w.layer[l];
+    L.h1 = take(N * d * 2);
+    L.r1 = take(N * 4);
+    L.qkv = take(N * 3 * d * 2);
+    L.rq = take(N * H * 4);
+    L.rk = take(N * H * 4);
+    L.att = take(N * d * 2);
+    L.lse = take(N * H * 4);
+    L.h2 = take(N * d * 2);
+    L.r2 = take(N * 4);
+    L.act = take(N * D.hidden * 2);
+  }
+  w.hf = take(N * d * 2);
+  w.rf = take(N * 4);
+  w.part = take(N * (size_t)ce_nparts(D) * 8);
+  w.zt = take(N * 4);
+  w.lse = take(N * 4);
+  w.row_loss = take(N * 4);
+  w.g = take(N * d * 4);
+  w.g_bf = take(N * d * 2);
+  w.dh = take(N * d * 4);
+  w.du = take(N * D.hidden * 2);
+  w.dout = take(N * d * 2);
+  w.delta = take(N * H * 4);
+  w.dq_acc = take(N * d * 4);
+  w.dqkv = take(N * 3 * d * 2);
+  w.dz = take(N * (size_t)vocab_chunk(D) * 2);
+  w.total = o;
+  return w;
+}
+
+template <class T>
+inline T* at(void* ws, size_t off) { return reinterpret_cast<T*>(reinterpret_cast<char*>(ws) + off); }
+
+// k-splits for a weight-gradient product with a small output and long K
+inline int wgrad_splits(int M, int N, int K) {
+  const long long t256 = (long long)((M + 255) / 256) * ((N + 255) / 256);
+  if (t256 >= 512) return 1;
+  long long ks = (512 + t256 - 1) / t256;
+  ks = std::min<long long>(ks, std::max(1, K / 1024));
+  ks = std::min<long long>(ks, 32);
+  return (int)std::max<long long>(ks, 1);
+}
+
+// C[M,N] (f32, ld ldc) (+)= A^T B with A stored [K][M], B stored [K][N] (bf16)
+int wgrad(const void* A, long long lda, const void* B, long long ldb, float* C, long long ldc, int M, int N,
+          int K, bool accumulate, hipStream_t s) {
+  GemmArgs a;
+  a.M = M; a.N = N; a.K = K;
+  a.A = A; a.lda = lda; a.a_kcontig = 0;
+  a.B = B; a.ldb = ldb; a.b_kcontig = 0;
+  a.C = C; a.ldc = ldc;
+  const int ks = wgrad_splits(M, N, K);
+  if (ks == 1) {
+    a.beta = accumulate ? 1.f : 0.f;
+    return gemm_bf16(a, EPI_F32, s);
+  }
+  if (!accumulate) {
+    if (ldc == N) {
+      int rc = launch_fill_f32(C, (long long)M * N, 0.f, s);
+      if (rc) return rc;
+    } else {
+      set_error("wgrad: split-K needs a dense output");
+      return -1;
+    }
+  }
+  a.k_split = ks;
+  return gemm_bf16(a, EPI_F32_ATOMIC, s);
+}
+
+}  // namespace
+
+extern "C" gpt_status gpt_workspace_size(const gpt_shape* shape, size_t* bytes) {
+  Dims D;
+  TRY(check_shape(shape, &D));
+  if (!bytes) FAIL(GPT_ERR_INVALID_ARG, "bytes is NULL");
+  *bytes = ws_layout(D).total;
+  return GPT_OK;
+}
+
+extern "C" gpt_status gpt_workspace_tensor(const gpt_shape* shape, int32_t which, int32_t layer, size_t* offset,
+                                           size_t* bytes) {
+  Dims D;
+  TRY(check_shape(shape, &D));
+  if (!offset || !bytes) FAIL(GPT_ERR_INVALID_ARG, "NULL output");
+  const WS w = ws_layout(D);
+  const size_t N = (size_t)D.N, d = D.d;
+  if (which >= 1 && which <= 5 && (layer < 0 || layer >= D.L)) FAIL(GPT_ERR_INVALID_ARG, "layer out of range");
+  switch (which) {
+    case 0: *offset = w.x; *bytes = N * d * 4; break;
+    case 1: *offset = w.layer[layer].h1; *bytes = N * d * 2; break;
+    case 2: *offset = w.layer[layer].qkv; *bytes = N * 3 * d * 2; break;
+    case 3: *offset = w.layer[layer].att; *bytes = N * d * 2; break;
+    case 4: *offset = w.layer[layer].h2; *bytes = N * d * 2; break;
+    case 5: *offset = w.layer[layer].act; *bytes = N * D.hidden * 2; break;
+    case 6: *offset = w.hf; *bytes = N * d * 2; break;
+    case 7: *offset = w.lse; *bytes = N * 4; break;
+    case 8: *offset = w.row_loss; *bytes = N * 4; break;
+    case 9: *offset = w.zt; *bytes = N * 4; break;
+    default: FAIL(GPT_ERR_INVALID_ARG, "unknown workspace tensor");
+  }
+  return GPT_OK;
+}
+
+extern "C" gpt_status gpt_cast_bf16(const float* src, uint16_t* dst, size_t n, gpt_stream_t stream) {
+  if (n == 0) return GPT_OK;
+  if (!src || !dst) FAIL(GPT_ERR_INVALID_ARG, "NULL pointer");
+  if (((uintptr_t)src & 15) || ((uintptr_t)dst & 7)) FAIL(GPT_ERR_INVALID_ARG, "src must be 16-byte and dst 8-byte aligned");
+  TRY(launch_cast_bf16(src, dst, (long long)n, S(stream)));
+  return GPT_OK;
+}
+
+namespace {
+
+int check_step_args(const gpt_shape* shape, const gpt_params* params, const int32_t* ids, void* ws,
+                    size_t ws_bytes, Dims* D, WS* w) {
+  int rc = check_shape(shape, D);
+  if (rc) return rc;
+  if (!params || !params->bf16) FAIL(GPT_ERR_INVALID_ARG, "params or params->bf16 is NULL");
+  if (!ids) FAIL(GPT_ERR_INVALID_ARG, "ids is NULL");
+  if (!ws) FAIL(GPT_ERR_INVALID_ARG, "workspace is NULL");
+  if ((uintptr_t)ws % kAlign) FAIL(GPT_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  if (((uintptr_t)params->bf16 & 15)) FAIL(GPT_ERR_INVALID_ARG, "params->bf16 must be 16-byte aligned");
+  *w = ws_layout(*D);
+  if (ws_bytes < w->total) FAIL(GPT_ERR_WORKSPACE, "workspace smaller than gpt_workspace_size()");
+  if (D->prec == GPT_PREC_FP8) FAIL(GPT_ERR_UNSUPPORTED, "fp8 precision is not available in this build");
+  return 0;
+}
+
+}  // namespace
+
+extern "C" gpt_status gpt_step_fwd(const gpt_shape* shape, const gpt_params* params, const int32_t* ids,
+                                   float* loss, float* row_lse, float* logits, void* ws, size_t ws_bytes,
+                                   gpt_stream_t stream) {
+  Dims D;
+  WS w;
+  TRY(check_step_args(shape, params, ids, ws, ws_bytes, &D, &w));
+  if (!loss) FAIL(GPT_ERR_INVALID_ARG, "loss is NULL");
+  if (logits && (D.V % 4)) FAIL(GPT_ERR_INVALID_ARG, "logits output needs vocab % 4 == 0");
+  hipStream_t s = S(stream);
+  const ParamLayout P = param_layout(D);
+  const uint16_t* W = params->bf16;
+  const int N = (int)D.N, d = D.d;
+  float* x = at<float>(ws, w.x);
+  float* cs = at<float>(ws, w.cs);
+
+  TRY(launch_rope_table(cs, D.T, s));
+  TRY(launch_embed_fwd(ids, W + P.wte, x, D.B, D.T, d, s));
+  for (int l = 0; l < D.L; ++l) {
+    const Layer& L = w.layer[l];
+    uint16_t* h1 = at<uint16_t>(ws, L.h1);
+    uint16_t* qkv = at<uint16_t>(ws, L.qkv);
+    uint16_t* att = at<uint16_t>(ws, L.att);
+    uint16_t* h2 = at<uint16_t>(ws, L.h2);
+    uint16_t* act = at<uint16_t>(ws, L.act);
+    TRY(launch_rmsnorm_fwd(x, h1, at<float>(ws, L.r1), N, d, s));
+    {
+      GemmArgs a;  // [q | k | v] = h1 [Wq; Wk; Wv]^T, q and k rotated and RMS-normalised per head
+      a.M = N; a.N = 3 * d; a.K = d;
+      a.A = h1; a.lda = d; a.B = W + P.qkv(D, l); a.ldb = d;
+      a.C = qkv; a.ldc = 3 * d;
+      a.rope = cs; a.row_T = D.T; a.n_head = D.H;
+      a.part = at<float>(ws, L.rq); a.zt = at<float>(ws, L.rk);
+      TRY(gemm_bf16(a, EPI_QKV, s));
+    }
+    TRY(launch_attn_fwd(qkv, qkv + d, qkv + 2 * d, 3 * d, att, d, at<float>(ws, L.lse), D.B, D.H, D.T, s));
+    {
+      GemmArgs a;  // x += att Wo^T
+      a.M = N; a.N = d; a.K = d;
+      a.A = att; a.lda = d; a.B = W + P.wo(D, l); a.ldb = d;
+      a.C = x; a.ldc = d;
+      TRY(gemm_bf16(a, EPI_RESID, s));
+    }
+    TRY(launch_rmsnorm_fwd(x, h2, at<float>(ws, L.r2), N, d, s));
+    {
+      GemmArgs a;  // act = relu(h2 Wfc^T)^2
+      a.M = N; a.N = D.hidden; a.K = d;
+      a.A = h2; a.lda = d; a.B = W + P.fc(D, l); a.ldb = d;
+      a.C = act; a.ldc = D.hidden;
+      TRY(gemm_bf16(a, EPI_RELU2, s));
+    }
+    {
+      GemmArgs a;  // x += act Wproj^T
+      a.M = N; a.N = d; a.K = D.hidden;
+      a.A = act; a.lda = D.hidden; a.B = W + P.proj(D, l); a.ldb = D.hidden;
+      a.C = x; a.ldc = d;
+      TRY(gemm_bf16(a, EPI_RESID, s));
+    }
+  }
+  uint16_t* hf = at<uint16_t>(ws, w.hf);
+  TRY(launch_rmsnorm_fwd(x, hf, at<float>(ws, w.rf), N, d, s));
+  {
+    GemmArgs a;  // per-tile (max, sum exp) of the logits hf W_lm^T, never stored
+    a.M = N; a.N = D.V; a.K = d;
+    a.A = hf; a.lda = d; a.B = W + P.lm_head; a.ldb = d;
+    a.row_i = ids; a.row_T = D.T; a.col_offset = 0;
+    a.part = at<float>(ws, w.part); a.nparts = ce_nparts(D); a.zt = at<float>(ws, w.zt);
+    TRY(gemm_bf16(a, EPI_CE_FWD, s));
+  }
+  TRY(launch_ce_reduce(at<float>(ws, w.part), ce_nparts(D), at<float>(ws, w.zt), at<float>(ws, w.lse),
+                       at<float>(ws, w.row_loss), row_lse, N, s));
+  TRY(launch_loss_mean(at<float>(ws, w.row_loss), loss, N, s));
+  if (logits) {
+    GemmArgs a;
+    a.M = N; a.N = D.V; a.K = d;
+    a.A = hf; a.lda = d; a.B = W + P.lm_head; a.ldb = d;
+    a.C = logits; a.ldc = D.V;
+    TRY(gemm_bf16(a, EPI_F32, s));
+  }
+  return GPT_OK;
+}
+
+extern "C" gpt_status gpt_step_bwd(const gpt_shape* shape, const gpt_params* params, const int32_t* ids,
+                                   int32_t accumulate, void* ws, size_t ws_bytes, gpt_stream_t stream) {
+  Dims D;
+  WS w;
+  TRY(check_step_args(shape, params, ids, ws, ws_bytes, &D, &w));
+  if (!params->grad) FAIL(GPT_ERR_INVALID_ARG, "params->grad is NULL");
+  if ((uintptr_t)params->grad & 15) FAIL(GPT_ERR_INVALID_ARG, "params->grad must be 16-byte aligned");
+  if (accumulate != 0 && accumulate != 1) FAIL(GPT_ERR_INVALID_ARG, "accumulate must be 0 or 1");
+  hipStream_t s = S(stream);
+  const ParamLayout P = param_layout(D);
+  const uint16_t* W = params->bf16;
+  float* G = params->grad;
+  const bool acc = accumulate != 0;
+  const int N = (int)D.N, d = D.d, hid = D.hidden;
+  uint16_t* hf = at<uint16_t>(ws, w.hf);
+  float* g = at<float>(ws, w.g);
+  uint16_t* g_bf = at<uint16_t>(ws, w.g_bf);
+  float* dh = at<float>(ws, w.dh);
+  uint16_t* du = at<uint16_t>(ws, w.du);
+  uint16_t* dout = at<uint16_t>(ws, w.dout);
+  uint16_t* dqkv = at<uint16_t>(ws, w.dqkv);
+  float* dq_acc = at<float>(ws, w.dq_acc);
+  uint16_t* dz = at<uint16_t>(ws, w.dz);
+  const float* cs = at<float>(ws, w.cs);
+
+  // fused head + cross-entropy backward, one vocabulary chunk at a time
+  const int vc = vocab_chunk(D);
+  for (int c0 = 0; c0 < D.V; c0 += vc) {
+    const int nv = std::min(vc, D.V - c0);
+    {
+      GemmArgs a;  // dz = (softmax(hf W_lm^T) - onehot(target)) / N, this chunk's columns
+      a.M = N; a.N = nv; a.K = d;
+      a.A = hf; a.lda = d; a.B = W + P.lm_head + (size_t)c0 * d; a.ldb = d;
+      a.C = dz; a.ldc = vc;
+      a.row_f = at<float>(ws, w.lse); a.row_i = ids; a.row_T = D.T; a.col_offset = c0;
+      a.beta = 1.0f / (float)N;
+      TRY(gemm_bf16(a, EPI_CE_BWD, s));
+    }
+    {
+      GemmArgs a;  // dh (+)= dz W_lm[chunk]
+      a.M = N; a.N = d; a.K = nv;
+      a.A = dz; a.lda = vc; a.B = W + P.lm_head + (size_t)c0 * d; a.ldb = d; a.b_kcontig = 0;
+      a.C = dh; a.ldc = d; a.beta = c0 > 0 ? 1.f : 0.f;
+      TRY(gemm_bf16(a, EPI_F32, s));
+    }
+    // dW_lm[chunk] (+)= dz^T hf
+    TRY(wgrad(dz, vc, hf, d, G + P.lm_head + (size_t)c0 * d, d, nv, d, N, acc, s));
+  }
+  TRY(launch_fill_f32(g, (long long)N * d, 0.f, s));
+  TRY(launch_rmsnorm_bwd(dh, hf, at<float>(ws, w.rf), g, g_bf, N, d, s));
+
+  for (int l = D.L - 1; l >= 0; --l) {
+    const Layer& L = w.layer[l];
+    const uint16_t* h1 = at<uint16_t>(ws, L.h1);
+    const uint16_t* qkv = at<uint16_t>(ws, L.qkv);
+    const uint16_t* att = at<uint16_t>(ws, L.att);
+    const uint16_t* h2 = at<uint16_t>(ws, L.h2);
+    const uint16_t* act = at<uint16_t>(ws, L.act);
+    // ---- MLP ----
+    {
+      GemmArgs a;  // du = (g Wproj) * 2 relu(u)  with relu(u) = sqrt(act)
+      a.M = N; a.N = hid; a.K = d;
+      a.A = g_bf; a.lda = d; a.B = W + P.proj(D, l); a.ldb = hid; a.b_kcontig = 0;
+      a.C = du; a.ldc = hid; a.aux = act; a.ldaux = hid;
+      TRY(gemm_bf16(a, EPI_DRELU2, s));
+    }
+    TRY(wgrad(g_bf, d, act, hid, G + P.proj(D, l), hid, d, hid, N, acc, s));  // dWproj = g^T act
+    {
+      GemmArgs a;  // dh = du Wfc
+      a.M = N; a.N = d; a.K = hid;
+      a.A = du; a.lda = hid; a.B = W + P.fc(D, l); a.ldb = d; a.b_kcontig = 0;
+      a.C = dh; a.ldc = d;
+      TRY(gemm_bf16(a, EPI_F32, s));
+    }
+    TRY(wgrad(du, hid, h2, d, G + P.fc(D, l), d, hid, d, N, acc, s));  // dWfc = du^T h2
+    TRY(launch_rmsnorm_bwd(dh, h2, at<float>(ws, L.r2), g, g_bf, N, d, s));
+    // ---- attention ----
+    {
+      GemmArgs a;  // dO = g Wo
+      a.M = N; a.N = d; a.K = d;
+      a.A = g_bf; a.lda = d; a.B = W + P.wo(D, l); a.ldb = d; a.b_kcontig = 0;
+      a.C = dout; a.ldc = d;
+      TRY(gemm_bf16(a, EPI_BF16, s));
+    }
+    TRY(wgrad(g_bf, d, att, d, G + P.wo(D, l), d, d, d, N, acc, s));  // dWo = g^T att
+    TRY(launch_attn_bwd(qkv, qkv + d, qkv + 2 * d, 3 * d, att, dout, d, at<float>(ws, L.lse),
+                        at<float>(ws, w.delta), dq_acc, dqkv + d, dqkv + 2 * d, 3 * d, D.B, D.H, D.T, s));
+    TRY(launch_rope_qknorm_bwd(dq_acc, dqkv, qkv, at<float>(ws, L.rq), at<float>(ws, L.rk), cs, N, D.T, D.H, s));
+    {
+      GemmArgs a;  // dh = dqkv [Wq; Wk; Wv]
+      a.M = N; a.N = d; a.K = 3 * d;
+      a.A = dqkv; a.lda = 3 * d; a.B = W + P.qkv(D, l); a.ldb = d; a.b_kcontig = 0;
+      a.C = dh; a.ldc = d;
+      TRY(gemm_bf16(a, EPI_F32, s));
+    }
+    TRY(wgrad(dqkv, 3 * d, h1, d, G + P.qkv(D, l), d, 3 * d, d, N, acc, s));  // dWqkv = dqkv^T h1
+    TRY(launch_rmsnorm_bwd(dh, h1, at<float>(ws, L.r1), g, g_bf, N, d, s));
+  }
+  if (!acc) TRY(launch_fill_f32(G + P.wte, (long long)D.V * d, 0.f, s));
+  TRY(launch_embed_bwd(ids, g, G + P.wte, D.B, D.T, d, s));
+  return GPT_OK;
+}
+
+// ---------------------------------------------------------------------------
+// Muon
+// ---------------------------------------------------------------------------
+namespace {
+
+constexpr int kFrobBlocks = 64;
+
+struct MuonWS {
+  size_t partial, X, Xb0, Xb1, A, Ab, Bb, total;
+};
+
+MuonWS muon_layout(int count, int rows, int cols) {
+  MuonWS m;
+  size_t o = 0;
+  auto take = [&](size_t bytes) { size_t r = o; o = al(o + bytes); return r; };
+  const size_t n = (size_t)count * rows * cols;
+  const size_t sm = (size_t)std::min(rows, cols);
+  m.partial = take((size_t)count * kFrobBlocks * 4);
+  m.X = take(n * 4);
+  m.Xb0 = take(n * 2);
+  m.Xb1 = take(n * 2);
+  m.A = take((size_t)count * sm * sm * 4);
+  m.Ab = take((size_t)count * sm * sm * 2);
+  m.Bb = take((size_t)count * sm * sm * 2);
+  m.total = o;
+  return m;
+}
+
+int check_muon_shape(int32_t count, int32_t rows, int32_t cols) {
+  if (count < 1 || rows < 1 || cols < 1) FAIL(GPT_ERR_INVALID_ARG, "count, rows and cols must be >= 1");
+  if ((rows % 8) || (cols % 8)) FAIL(GPT_ERR_INVALID_ARG, "rows and cols must be multiples of 8");
+  if ((long long)rows * cols > (1LL << 30) || (long long)count * rows * cols > (1LL << 34))
+    FAIL(GPT_ERR_INVALID_ARG, "matrices too large");
+  return 0;
+}
+
+}  // namespace
+
+extern "C" gpt_status muon_workspace_size(int32_t count, int32_t rows, int32_t cols, size_t* bytes) {
+  TRY(check_muon_shape(count, rows, cols));
+  if (!bytes) FAIL(GPT_ERR_INVALID_ARG, "bytes is NULL");
+  *bytes = muon_layout(count, rows, cols).total;
+  return GPT_OK;
+}
+
+extern "C" gpt_status muon_update(float* Wt, uint16_t* W_bf16, const float* Gm, float* M, float* O_out,
+                                  int32_t count, int32_t rows, int32_t cols, const float* coeffs,
+                                  int32_t ns_steps, float lr, float momentum, float weight_decay, void* ws,
+                                  size_t ws_bytes, gpt_stream_t stream) {
+  TRY(check_muon_shape(count, rows, cols));
+  if (!Gm) FAIL(GPT_ERR_INVALID_ARG, "G is NULL");
+  if (!coeffs) FAIL(GPT_ERR_INVALID_ARG, "coeffs is NULL");
+  if (ns_steps < 1 || ns_steps > 16) FAIL(GPT_ERR_INVALID_ARG, "ns_steps must be in [1, 16]");
+  if (W_bf16 && !Wt) FAIL(GPT_ERR_INVALID_ARG, "W_bf16 given without W");
+  if (!ws || ((uintptr_t)ws % kAlign)) FAIL(GPT_ERR_INVALID_ARG, "workspace NULL or not 256-byte aligned");
+  if (((uintptr_t)Gm | (uintptr_t)M) & 15) FAIL(GPT_ERR_INVALID_ARG, "G and M must be 16-byte aligned");
+  for (int i = 0; i < 3 * ns_steps; ++i)
+    if (!isfinite(coeffs[i])) FAIL(GPT_ERR_INVALID_ARG, "non-finite coefficient");
+  const MuonWS m = muon_layout(count, rows, cols);
+  if (ws_bytes < m.total) FAIL(GPT_ERR_WORKSPACE, "workspace smaller than muon_workspace_size()");
+  hipStream_t s = S(stream);
+  const long long per = (long long)rows * cols;
+  const int lrow = std::max(rows, cols), sm = std::min(rows, cols);
+
+  const float* src = Gm;
+  if (M) {
+    TRY(launch_muon_momentum(M, Gm, per * count, momentum, s));
+    src = M;
+  }
+  float* partial = at<float>(ws, m.partial);
+  float* X = at<float>(ws, m.X);
+  uint16_t* Xb[2] = {at<uint16_t>(ws, m.Xb0), at<uint16_t>(ws, m.Xb1)};
+  float* A = at<float>(ws, m.A);
+  uint16_t* Ab = at<uint16_t>(ws, m.Ab);
+  uint16_t* Bb = at<uint16_t>(ws, m.Bb);
+  TRY(launch_frob_partial(src, partial, count, per, kFrobBlocks, s));
+  TRY(launch_ns_init(src, partial, kFrobBlocks, X, Xb[0], count, rows, cols, 1e-7f, s));
+
+  const long long sX = (long long)lrow * sm, sA = (long long)sm * sm;
+  // Gram products need split-K when the batch has few output tiles
+  const long long gram_tiles = (long long)count * ((sm + 127) / 128) * ((sm + 127) / 128);
+  const int gram_split = gram_tiles >= 512 ? 1 : (int)std::min<long long>(std::max(1, lrow / 1024),
+                                                                            (512 + gram_tiles - 1) / gram_tiles);
+  int cur = 0;
+  for (int it = 0; it < ns_steps; ++it) {
+    const float ca = coeffs[3 * it], cb = coeffs[3 * it + 1], cc = coeffs[3 * it + 2];
+    {
+      GemmArgs a;  // A = X^T X (fp32 and bf16)
+      a.M = sm; a.N = sm; a.K = lrow; a.batch = count;
+      a.A = Xb[cur]; a.lda = sm; a.sA = sX; a.a_kcontig = 0;
+      a.B = Xb[cur]; a.ldb = sm; a.sB = sX; a.b_kcontig = 0;
+      a.C = A; a.ldc = sm; a.sC = sA; a.C2 = Ab; a.ldc2 = sm; a.sC2 = sA;
+      if (gram_split <= 1) {
+        TRY(gemm_bf16(a, EPI_F32_BF16, s));
+      } else {
+        TRY(launch_fill_f32(A, sA * count, 0.f, s));
+        a.k_split = gram_split;
+        TRY(gemm_bf16(a, EPI_F32_ATOMIC, s));
+        TRY(launch_cast_bf16(A, Ab, sA * count, s));
+      }
+    }
+    {
+      GemmArgs a;  // B = b A + c A A
+      a.M = sm; a.N = sm; a.K = sm; a.batch = count;
+      a.A = Ab; a.lda = sm; a.sA = sA;
+      a.B = Ab; a.ldb = sm; a.sB = sA; a.b_kcontig = 0;
+      a.C = Bb; a.ldc = sm; a.sC = sA;
+      a.aux = A; a.ldaux = sm; a.sAux = sA;
+      a.alpha = cc; a.beta = cb;
+      TRY(gemm_bf16(a, EPI_NS_POLY, s));
+    }
+    {
+      GemmArgs a;  // X = a X + X B
+      a.M = lrow; a.N = sm; a.K = sm; a.batch = count;
+      a.A = Xb[cur]; a.lda = sm; a.sA = sX;
+      a.B = Bb; a.ldb = sm; a.sB = sA; a.b_kcontig = 0;
+      a.C = X; a.ldc = sm; a.sC = sX; a.C2 = Xb[cur ^ 1]; a.ldc2 = sm; a.sC2 = sX;
+      a.beta = ca;
+      TRY(gemm_bf16(a, EPI_NS_UPD, s));
+    }
+    cur ^= 1;
+  }
+  TRY(launch_muon_apply(X, Wt, W_bf16, O_out, count, rows, cols, lr, weight_decay, s));
+  return GPT_OK;
+}
+
+// ---------------------------------------------------------------------------
+// component: attention
+// ---------------------------------------------------------------------------
+extern "C" gpt_status gpt_op_attention_fwd(int32_t batch, int32_t n_head, int32_t seq_len, const uint16_t* q,
+                                           const uint16_t* k, const uint16_t* v, int64_t ld_qkv, uint16_t* out,
+                                           int64_t ld_out, float* lse, gpt_stream_t stream) {
+  if (batch < 0 || n_head < 1 || seq_len < 0) FAIL(GPT_ERR_INVALID_ARG, "bad batch/n_head/seq_len");
+  if (batch == 0 || seq_len == 0) return GPT_OK;
+  if (!q || !k || !v || !out || !lse) FAIL(GPT_ERR_INVALID_ARG, "NULL pointer");
+  if (ld_qkv < (int64_t)n_head * 128 || ld_out < (int64_t)n_head * 128 || (ld_qkv % 8) || (ld_out % 8))
+    FAIL(GPT_ERR_INVALID_ARG, "leading dimensions must be >= 128*n_head and multiples of 8");
+  if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)out) & 15) FAIL(GPT_ERR_INVALID_ARG, "misaligned");
+  TRY(launch_attn_fwd(q, k, v, ld_qkv, out, ld_out, lse, batch, n_head, seq_len, S(stream)));
+  return GPT_OK;
+}
+
+extern "C" gpt_status gpt_op_attention_bwd(int32_t batch, int32_t n_head, int32_t seq_len, const uint16_t* q,
+                                           const uint16_t* k, const uint16_t* v, int64_t ld_qkv, const uint16_t* out,
+                                           const uint16_t* dout, int64_t ld_out, const float* lse, float* delta,
+                                           float* dq_acc, uint16_t* dk, uint16_t* dv, int64_t ld_dkv,
+                                           gpt_stream_t stream) {
+  if (batch < 0 || n_head < 1 || seq_len < 0) FAIL(GPT_ERR_INVALID_ARG, "bad batch/n_head/seq_len");
+  if (batch == 0 || seq_len == 0) return GPT_OK;
+  if (!q || !k || !v || !out || !dout || !lse || !delta || !dq_acc || !dk || !dv)
+    FAIL(GPT_ERR_INVALID_ARG, "NULL pointer");
+  if (ld_qkv < (int64_t)n_head * 128 || ld_out < (int64_t)n_head * 128 || ld_dkv < (int64_t)n_head * 128 ||
+      (ld_qkv % 8) || (ld_out % 8) || (ld_dkv % 8))
+    FAIL(GPT_ERR_INVALID_ARG, "leading dimensions must be >= 128*n_head and multiples of 8");
+  if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)out | (uintptr_t)dout | (uintptr_t)dk |
+       (uintptr_t)dv | (uintptr_t)dq_acc) & 15)
+    FAIL(GPT_ERR_INVALID_ARG, "misaligned");
+  TRY(launch_attn_bwd(q, k, v, ld_qkv, out, dout, ld_out, lse, delta, dq_acc, dk, dv, ld_dkv, batch, n_head,
+                      seq_len, S(stream)));
+  return GPT_OK;
+}

@@ -12,6 +12,8 @@
 // Every kernel here streams its rows once: one wave64 per row (vectorised
 // 16-byte accesses) so the row statistics reduce with wave shuffles only.
 
+#include <algorithm>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -63,7 +65,7 @@ __global__ void rope_table_kernel(float* cs, int T) {
 }
 
 // x[n, :] = wte[ids[b, t], :] for n = b*T + t (bf16 -> fp32, exact)
-__global__ void embed_fwd_kernel(const int* __restrict__ ids, const uint16_t* __restrict__ wte,
+__global__ void __launch_bounds__(256) embed_fwd_kernel(const int* __restrict__ ids, const uint16_t* __restrict__ wte,
                                  float* __restrict__ x, int B, int T, int d) {
   const int lane = threadIdx.x & 63;
   const long long n = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -80,7 +82,7 @@ __global__ void embed_fwd_kernel(const int* __restrict__ ids, const uint16_t* __
 }
 
 // dwte[ids[b, t], :] += g[n, :]
-__global__ void embed_bwd_kernel(const int* __restrict__ ids, const float* __restrict__ g,
+__global__ void __launch_bounds__(256) embed_bwd_kernel(const int* __restrict__ ids, const float* __restrict__ g,
                                  float* __restrict__ dwte, int B, int T, int d) {
   const int lane = threadIdx.x & 63;
   const long long n = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -99,7 +101,7 @@ __global__ void embed_bwd_kernel(const int* __restrict__ ids, const float* __res
 }
 
 // h = x * r, r = 1/sqrt(mean(x^2) + eps); one wave per row
-__global__ void rmsnorm_fwd_kernel(const float* __restrict__ x, uint16_t* __restrict__ h,
+__global__ void __launch_bounds__(256) rmsnorm_fwd_kernel(const float* __restrict__ x, uint16_t* __restrict__ h,
                                    float* __restrict__ r, long long N, int d) {
   const int lane = threadIdx.x & 63;
   const long long n = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -131,7 +133,7 @@ __global__ void rmsnorm_fwd_kernel(const float* __restrict__ x, uint16_t* __rest
 }
 
 // g += r * (dh - h * mean(dh * h)); g_bf = bf16(g); one wave per row
-__global__ void rmsnorm_bwd_kernel(const float* __restrict__ dh, const uint16_t* __restrict__ h,
+__global__ void __launch_bounds__(256) rmsnorm_bwd_kernel(const float* __restrict__ dh, const uint16_t* __restrict__ h,
                                    const float* __restrict__ r, float* __restrict__ g,
                                    uint16_t* __restrict__ g_bf, long long N, int d) {
   const int lane = threadIdx.x & 63;
@@ -167,38 +169,6 @@ __global__ void rmsnorm_bwd_kernel(const float* __restrict__ dh, const uint16_t*
   }
 }
 
-// In place on one 128-wide head: rotate (e, e+64) by the position angle, then
-// RMS-normalise over the head.  Lane e holds elements e and e + 64.
-__device__ __forceinline__ float rope_norm_head(uint16_t* p, const float* cs, int T, int t, int lane) {
-  const float c = cs[t * 64 + lane], sn = cs[T * 64 + t * 64 + lane];
-  const float x1 = bf2f(p[lane]), x2 = bf2f(p[lane + 64]);
-  const float y1 = x1 * c - x2 * sn, y2 = x1 * sn + x2 * c;
-  const float ss = wave_sum(y1 * y1 + y2 * y2);
-  const float rr = 1.0f / sqrtf(ss / 128.f + kEps);
-  p[lane] = f2bf(y1 * rr);
-  p[lane + 64] = f2bf(y2 * rr);
-  return rr;
-}
-
-// one wave per (token, head): q and k of that head
-__global__ void rope_qknorm_fwd_kernel(uint16_t* __restrict__ qkv, float* __restrict__ rq,
-                                       float* __restrict__ rk, const float* __restrict__ cs,
-                                       long long N, int T, int H) {
-  const int lane = threadIdx.x & 63;
-  const long long w = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (w >= N * H) return;
-  const long long n = w / H;
-  const int hh = (int)(w % H), t = (int)(n % T);
-  const int d = H * 128;
-  uint16_t* row = qkv + n * 3 * d;
-  const float a = rope_norm_head(row + hh * 128, cs, T, t, lane);
-  const float b = rope_norm_head(row + d + hh * 128, cs, T, t, lane);
-  if (lane == 0) {
-    rq[w] = a;
-    rk[w] = b;
-  }
-}
-
 // dx for one head: d_rot = r (dy - y mean(dy y)); dx = R^T d_rot
 __device__ __forceinline__ void rope_norm_head_bwd(float dy1, float dy2, const uint16_t* y, float rr,
                                                    const float* cs, int T, int t, int lane,
@@ -211,7 +181,7 @@ __device__ __forceinline__ void rope_norm_head_bwd(float dy1, float dy2, const u
   out[lane + 64] = f2bf(-d1 * sn + d2 * c);
 }
 
-__global__ void rope_qknorm_bwd_kernel(const float* __restrict__ dq_acc, uint16_t* __restrict__ dqkv,
+__global__ void __launch_bounds__(256) rope_qknorm_bwd_kernel(const float* __restrict__ dq_acc, uint16_t* __restrict__ dqkv,
                                        const uint16_t* __restrict__ qkv, const float* __restrict__ rq,
                                        const float* __restrict__ rk, const float* __restrict__ cs,
                                        long long N, int T, int H) {
@@ -230,7 +200,7 @@ __global__ void rope_qknorm_bwd_kernel(const float* __restrict__ dq_acc, uint16_
 }
 
 // lse = log-sum-exp over the per-tile (max, sum exp) partials; loss = lse - z[target]
-__global__ void ce_reduce_kernel(const float2* __restrict__ part, int nparts, const float* __restrict__ zt,
+__global__ void __launch_bounds__(256) ce_reduce_kernel(const float2* __restrict__ part, int nparts, const float* __restrict__ zt,
                                  float* __restrict__ lse, float* __restrict__ row_loss,
                                  float* __restrict__ lse_out, long long N) {
   const int lane = threadIdx.x & 63;
@@ -391,7 +361,7 @@ __global__ void muon_apply_kernel(const float* __restrict__ X, float* __restrict
 // ----------------------------------------------------------------------------
 int launch_fill_f32(float* p, long long n, float v, hipStream_t s) {
   if (n <= 0) return 0;
-  const int blocks = (int)min<long long>(nblocks(n, 1024), 8192);
+  const int blocks = (int)std::min<long long>(nblocks(n, 1024), 8192);
   hipLaunchKernelGGL(fill_f32_kernel, dim3(blocks), dim3(256), 0, s, p, n, v);
   GS_LAUNCH_CHECK("fill_f32");
   return 0;
@@ -399,7 +369,7 @@ int launch_fill_f32(float* p, long long n, float v, hipStream_t s) {
 
 int launch_cast_bf16(const float* src, uint16_t* dst, long long n, hipStream_t s) {
   if (n <= 0) return 0;
-  const int blocks = (int)min<long long>(nblocks(n, 1024), 16384);
+  const int blocks = (int)std::min<long long>(nblocks(n, 1024), 16384);
   hipLaunchKernelGGL(cast_bf16_kernel, dim3(blocks), dim3(256), 0, s, src, dst, n);
   GS_LAUNCH_CHECK("cast_bf16");
   return 0;
@@ -436,13 +406,6 @@ int launch_rmsnorm_bwd(const float* dh, const uint16_t* h, const float* r, float
   return 0;
 }
 
-int launch_rope_qknorm_fwd(uint16_t* qkv, float* rq, float* rk, const float* cs, long long N, int T, int H,
-                           hipStream_t s) {
-  hipLaunchKernelGGL(rope_qknorm_fwd_kernel, dim3(nblocks(N * H, 4)), dim3(256), 0, s, qkv, rq, rk, cs, N, T, H);
-  GS_LAUNCH_CHECK("rope_qknorm_fwd");
-  return 0;
-}
-
 int launch_rope_qknorm_bwd(const float* dq_acc, uint16_t* dqkv, const uint16_t* qkv, const float* rq,
                            const float* rk, const float* cs, long long N, int T, int H, hipStream_t s) {
   hipLaunchKernelGGL(rope_qknorm_bwd_kernel, dim3(nblocks(N * H, 4)), dim3(256), 0, s, dq_acc, dqkv, qkv, rq,
@@ -466,7 +429,7 @@ int launch_loss_mean(const float* row_loss, float* loss, long long N, hipStream_
 }
 
 int launch_muon_momentum(float* M, const float* G, long long n, float mu, hipStream_t s) {
-  const int blocks = (int)min<long long>(nblocks(n, 1024), 16384);
+  const int blocks = (int)std::min<long long>(nblocks(n, 1024), 16384);
   hipLaunchKernelGGL(muon_momentum_kernel, dim3(blocks), dim3(256), 0, s, M, G, n, mu);
   GS_LAUNCH_CHECK("muon_momentum");
   return 0;

@@ -19,6 +19,8 @@ enum Epi {
   EPI_NS_UPD,      // x = beta * C_f32 + v; C f32 = x; C2 bf16 = x  (X = a X + X B)
   EPI_CE_FWD,      // per-row partial (max, sum exp) over the tile's columns + target logit
   EPI_CE_BWD,      // C bf16 = alpha * (exp(raw - lse[m]) - [col == tgt[m]])
+  EPI_QKV,         // [q | k | v] projection: rotate + RMS-normalise each 128-wide q/k head,
+                   // C bf16; per (row, head) 1/rms to rq / rk (part, zt); needs 256-wide tiles
   EPI_COUNT
 };
 
@@ -41,6 +43,8 @@ struct GemmArgs {
   int nparts = 0;
   float* zt = nullptr;           // CE target logit [M]
   int k_split = 1;               // > 1 only with EPI_F32_ATOMIC
+  const float* rope = nullptr;    // EPI_QKV: cos [row_T, 64] then sin [row_T, 64]
+  int n_head = 0;                 // EPI_QKV: heads per q (and k) block
   const float* scale_a = nullptr;  // fp8: device scalars; v *= 1 / (scale_a * scale_b)
   const float* scale_b = nullptr;
 };

@@ -311,7 +311,68 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_bf16_kernel(GemmArgs p) {
   }
 
   // ----------------------------- epilogue ---------------------------------
-  if constexpr (EPI == EPI_CE_FWD) {
+  if constexpr (EPI == EPI_QKV) {
+    // Each wave owns 128 columns = one head (tiles are 256 wide).  Lane row m
+    // holds head features e = j*32 + 8g + 4lh + r; the rotation partner
+    // e + 64 sits in the same lane at j + 2, the other half of the head in
+    // lane ^ 32.
+    static_assert(WN == 128, "EPI_QKV needs 128 columns per wave");
+    const int nb = n0 + wn * WN;        // first column of this wave's head
+    const int dmodel = p.n_head * 128;
+    const bool is_qk = nb < 2 * dmodel;
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      const int m = m0 + wm * WM + i * 32 + lr;
+      float y[TN][16];
+      float ss = 0.f;
+      const int t = (m < p.M) ? m % p.row_T : 0;
+      if (is_qk) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const int e = j * 32 + 8 * g + 4 * lh;
+            const float4 c4 = *reinterpret_cast<const float4*>(p.rope + (long long)t * 64 + e);
+            const float4 s4 = *reinterpret_cast<const float4*>(p.rope + (long long)p.row_T * 64 + (long long)t * 64 + e);
+            const float cc[4] = {c4.x, c4.y, c4.z, c4.w}, sn[4] = {s4.x, s4.y, s4.z, s4.w};
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const float x1 = acc[i][j][4 * g + r] * p.alpha, x2 = acc[i][j + 2][4 * g + r] * p.alpha;
+              const float y1 = x1 * cc[r] - x2 * sn[r], y2 = x1 * sn[r] + x2 * cc[r];
+              y[j][4 * g + r] = y1;
+              y[j + 2][4 * g + r] = y2;
+              ss += y1 * y1 + y2 * y2;
+            }
+          }
+        ss += __shfl_xor(ss, 32, 64);
+        const float rr = 1.0f / sqrtf(ss / 128.f + 1e-6f);
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) y[j][e] *= rr;
+        if (lh == 0 && m < p.M) {
+          const int head = (nb % dmodel) / 128;
+          float* rdst = (nb < dmodel) ? p.part : p.zt;
+          rdst[(long long)m * p.n_head + head] = rr;
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) y[j][e] = acc[i][j][e] * p.alpha;
+      }
+      if (m >= p.M || nb >= p.N) continue;
+      uint16_t* crow = reinterpret_cast<uint16_t*>(p.C) + (long long)m * p.ldc + nb;
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int e = j * 32 + 8 * g + 4 * lh;
+          *reinterpret_cast<uint2*>(crow + e) = make_uint2(pack_bf2(y[j][4 * g], y[j][4 * g + 1]),
+                                                           pack_bf2(y[j][4 * g + 2], y[j][4 * g + 3]));
+        }
+    }
+  } else if constexpr (EPI == EPI_CE_FWD) {
     // Per row: max and sum of exp over this wave's WN columns, merged with
     // the partner lane (lane ^ 32) that holds the other half of the columns.
 #pragma unroll
@@ -382,8 +443,12 @@ inline bool use_big_tile(const GemmArgs& a) {
 
 template <bool AK, bool BKC, int EPI>
 int launch_tiles(const GemmArgs& a, hipStream_t s) {
-  if (use_big_tile(a)) return launch_t<256, 256, AK, BKC, EPI>(a, s);
-  return launch_t<128, 128, AK, BKC, EPI>(a, s);
+  if constexpr (EPI == EPI_QKV) {
+    return launch_t<256, 256, AK, BKC, EPI>(a, s);
+  } else {
+    if (use_big_tile(a)) return launch_t<256, 256, AK, BKC, EPI>(a, s);
+    return launch_t<128, 128, AK, BKC, EPI>(a, s);
+  }
 }
 
 }  // namespace

@@ -12,6 +12,7 @@ int gemm_bf16_kk(const GemmArgs& a, int epi, hipStream_t s) {
     case EPI_RELU2: return launch_tiles<true, true, EPI_RELU2>(a, s);
     case EPI_CE_FWD: return launch_tiles<true, true, EPI_CE_FWD>(a, s);
     case EPI_CE_BWD: return launch_tiles<true, true, EPI_CE_BWD>(a, s);
+    case EPI_QKV: return launch_tiles<true, true, EPI_QKV>(a, s);
     default:
       set_error("gemm_bf16: epilogue not built for this operand layout");
       return -5;

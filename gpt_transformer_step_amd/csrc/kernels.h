@@ -16,15 +16,12 @@ int launch_embed_bwd(const int* ids, const float* g, float* dwte, int B, int T, 
 int launch_rmsnorm_fwd(const float* x, uint16_t* h, float* r, long long N, int d, hipStream_t s);
 int launch_rmsnorm_bwd(const float* dh, const uint16_t* h, const float* r, float* g, uint16_t* g_bf,
                        long long N, int d, hipStream_t s);
-int launch_rope_qknorm_fwd(uint16_t* qkv, float* rq, float* rk, const float* cos_sin, long long N,
-                           int T, int H, hipStream_t s);
 int launch_rope_qknorm_bwd(const float* dq_acc, uint16_t* dqkv, const uint16_t* qkv, const float* rq,
                            const float* rk, const float* cos_sin, long long N, int T, int H,
                            hipStream_t s);
 int launch_ce_reduce(const float* part, int nparts, const float* zt, float* lse, float* row_loss,
                      float* lse_out, long long N, hipStream_t s);
 int launch_loss_mean(const float* row_loss, float* loss, long long N, hipStream_t s);
-int launch_logits_copy(const float* part_unused, hipStream_t s);
 
 // --- Muon elementwise (elementwise.hip) ------------------------------------
 int launch_muon_momentum(float* M, const float* G, long long n, float mu, hipStream_t s);

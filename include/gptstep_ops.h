@@ -62,7 +62,8 @@ gpt_status gpt_op_attention_bwd(int32_t batch, int32_t n_head, int32_t seq_len, 
  * normalisation); 3 attention output of `layer` (bf16 [N,d]); 4 h2 of
  * `layer` (bf16 [N,d]); 5 relu^2 activation of `layer` (bf16 [N,4d]);
  * 6 final normed hidden state (bf16 [N,d]); 7 per-row lse (fp32 [N]);
- * 8 per-row loss (fp32 [N]).  N = batch*seq_len. */
+ * 8 per-row loss (fp32 [N]); 9 per-row logit of the target token (fp32 [N]).
+ * N = batch*seq_len. */
 gpt_status gpt_workspace_tensor(const gpt_shape* shape, int32_t which, int32_t layer,
                                 size_t* offset /* host */, size_t* bytes /* host */);
 
