@@ -1,0 +1,251 @@
+"""Training-step throughput of libgptstep on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload d20]
+                    [--precision bf16|fp8] [--no-cpu-baseline]
+
+One step = gpt_step_fwd + gpt_step_bwd + muon_update on the three groups of
+block matrices (the q/k/v/o matrices, the MLP input matrices, the MLP output
+matrices) on synthetic inputs already resident in HBM: uniform token ids and
+N(0, 1/fan_in) weights from the seeded generators.  W untimed warm-up steps,
+then K timed steps between two synchronised events on the launch stream.
+Prints one JSON line.
+
+MFU counts algorithmic FLOPs only: 6 (12 L d^2 + V d) per token for the
+matrix products, 6 L d T per token for the causal half of attention, plus
+5 Newton-Schulz iterations of (4 l s^2 + 2 s^3) per block matrix; recomputed
+scores and logits are not counted.  Peak: MI355X dense bf16 MFMA,
+2.5166 PFLOP/s.
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16 = 2516.6e12   # dense MFMA FLOP/s
+PEAK_FP8 = 5033.2e12
+NS5 = [(15.0 / 8.0, -10.0 / 8.0, 3.0 / 8.0)] * 5
+METRIC = "training tokens/sec + MFU (% of MFMA peak), depth-20 GPT, 1 MI355X"
+
+
+def shapes(depth):
+    d = 64 * depth
+    return d, d // 128, 4 * d
+
+
+def alg_flops(depth, V, T, B):
+    L = depth
+    d, _, _ = shapes(depth)
+    N = B * T
+    f_model = 6 * (12 * L * d * d + V * d) * N + 6 * L * d * T * N
+    groups = muon_groups(depth)
+    f_ns = 0
+    for count, rows, cols in groups:
+        l, s = max(rows, cols), min(rows, cols)
+        f_ns += count * 5 * (4 * l * s * s + 2 * s ** 3)
+    return f_model, f_ns
+
+
+def muon_groups(depth):
+    d, _, hid = shapes(depth)
+    return [(4 * depth, d, d), (depth, hid, d), (depth, d, hid)]
+
+
+def kernel_flops(name, depth, V, T, B):
+    """Algorithmic FLOPs of one launch of a kernel category (None: not a
+    contraction)."""
+    d, H, hid = shapes(depth)
+    N = B * T
+    attn = 2.0 * B * H * T * (T + 1) / 2 * 128 * 2  # QK^T and PV over the causal half
+    table = {
+        "gemm_qkv_rope_fwd": 2.0 * N * 3 * d * d, "gemm_o_fwd": 2.0 * N * d * d,
+        "gemm_fc_relu2_fwd": 2.0 * N * hid * d, "gemm_proj_fwd": 2.0 * N * d * hid,
+        "gemm_ce_fwd": 2.0 * N * V * d, "attn_fwd": attn, "attn_bwd": 2 * attn,
+        "gemm_proj_dgrad": 2.0 * N * d * hid, "gemm_proj_wgrad": 2.0 * N * d * hid,
+        "gemm_fc_dgrad": 2.0 * N * d * hid, "gemm_fc_wgrad": 2.0 * N * d * hid,
+        "gemm_o_dgrad": 2.0 * N * d * d, "gemm_o_wgrad": 2.0 * N * d * d,
+        "gemm_qkv_dgrad": 2.0 * N * 3 * d * d, "gemm_qkv_wgrad": 2.0 * N * 3 * d * d,
+    }
+    return table.get(name)
+
+
+def cpu_baseline(wl, depth, V, T, B, seed_ids, seed_w):
+    """The oracle (numpy, as it stands) on a bounded sample of the workload:
+    one sequence's forward+backward in float32 and one Newton-Schulz per block
+    matrix shape (float64), scaled to a full step."""
+    from gpt_transformer_step_amd import inputs
+    from oracle import model as om
+    from oracle import muon as omu
+    from oracle import precision
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+    except Exception:  # pragma: no cover
+        cores = len(os.sched_getaffinity(0))
+    dims = inputs.Dims.from_depth(depth, V)
+    cfg = om.Config.from_depth(depth, V)
+    master = inputs.master_weights(dims, seed_w)
+    P = {k: v for k, v in inputs.unpack(dims, precision.round_bf16(master)).items()}
+    ids = inputs.token_ids(B, T, V, seed_ids)[:1]
+    t0 = time.perf_counter()
+    om.forward_backward(P, ids, cfg, dtype=np.float32)
+    t_seq = time.perf_counter() - t0
+    t_ns = 0.0
+    g = np.random.default_rng(0)
+    for count, rows, cols in muon_groups(depth):
+        G = g.standard_normal((rows, cols)).astype(np.float32)
+        t0 = time.perf_counter()
+        omu.newton_schulz(G, NS5)
+        t_ns += count * (time.perf_counter() - t0)
+    step_s = B * t_seq + t_ns
+    return {"value": B * T / step_s, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+            "sample": (f"{wl}: forward+backward of 1 of {B} sequences (float32, {t_seq:.1f} s) and one "
+                       f"Newton-Schulz per block-matrix shape (float64); scaled to a full step "
+                       f"({step_s:.0f} s)")}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="d20", choices=["d2", "d12", "d20", "d26"])
+    ap.add_argument("--precision", default="bf16", choices=["bf16", "fp8"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--breakdown", action="store_true", help="print per-kernel times to stderr")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the step runs on a "
+              f"single MI355X with no collectives)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from gpt_transformer_step_amd import binding as Bd
+    from gpt_transformer_step_amd import inputs
+
+    wl = inputs.WORKLOADS[args.workload]
+    depth, T, B = wl["depth"], wl["seq_len"], wl["batch"]
+    V = 32768
+    d, H, hid = shapes(depth)
+    prec = Bd.PREC_FP8 if args.precision == "fp8" else Bd.PREC_BF16
+    dev = torch.device("cuda:0")
+    sh = Bd.shape(depth, V, T, B, prec)
+    n = Bd.param_count(sh)
+    dims = inputs.Dims.from_depth(depth, V)
+    master_np = inputs.master_weights(dims, inputs.SEED_W)
+    master = torch.from_numpy(master_np).to(dev)
+    del master_np
+    bf16 = torch.empty(n, dtype=torch.bfloat16, device=dev)
+    Bd.cast_bf16(master, bf16)
+    grad = torch.zeros(n, dtype=torch.float32, device=dev)
+    ids = torch.from_numpy(inputs.token_ids(B, T, V, inputs.SEED_IDS)).to(dev)
+    ws = torch.empty(Bd.workspace_size(sh), dtype=torch.uint8, device=dev)
+    params = Bd.make_params(master, bf16, grad)
+    loss = torch.zeros(1, dtype=torch.float32, device=dev)
+    offs = Bd.param_layout(sh)
+    # the three Muon groups are contiguous ranges of the packed buffers
+    starts = [offs[1], offs[1 + 4 * depth], offs[1 + 5 * depth]]
+    groups = []
+    for (count, rows, cols), st in zip(muon_groups(depth), starts):
+        size = count * rows * cols
+        groups.append(dict(count=count, rows=rows, cols=cols, start=st,
+                           M=torch.zeros(size, dtype=torch.float32, device=dev),
+                           ws=torch.empty(Bd.muon_workspace_size(count, rows, cols), dtype=torch.uint8,
+                                          device=dev)))
+
+    def step():
+        Bd.step_fwd(sh, params, ids, loss, ws)
+        Bd.step_bwd(sh, params, ids, ws)
+        for gr in groups:
+            st, size = gr["start"], gr["count"] * gr["rows"] * gr["cols"]
+            view = (gr["count"], gr["rows"], gr["cols"])
+            Bd.muon_update(grad[st:st + size].view(view), NS5, gr["ws"], W=master[st:st + size].view(view),
+                           W_bf16=bf16[st:st + size].view(view), M=gr["M"], lr=0.02, momentum=0.95,
+                           weight_decay=0.0)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    first_loss = float(loss.item())
+
+    # per-kernel-category pass (untimed) to find the dominant kernel
+    cats = Bd.profile_categories()
+    Bd.profile_reset()
+    Bd.profile_enable((1 << len(cats)) - 1)
+    step()
+    torch.cuda.synchronize()
+    breakdown = {}
+    for i, c in enumerate(cats):
+        t, cnt = Bd.profile_read(i)
+        if cnt:
+            breakdown[c] = (t, cnt)
+    Bd.profile_enable(0)
+    Bd.profile_reset()
+    contractions = {c: v for c, v in breakdown.items() if kernel_flops(c, depth, V, T, B)}
+    dom = max(contractions, key=lambda c: contractions[c][0])
+    dom_idx = cats.index(dom)
+
+    # timed region: K steps; the dominant kernel bracketed by HIP events on its launch stream
+    Bd.profile_enable(1 << dom_idx)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(args.steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    dom_ms, dom_cnt = Bd.profile_read(dom_idx)
+    Bd.profile_enable(0)
+    Bd.profile_reset()
+    last_loss = float(loss.item())
+
+    f_model, f_ns = alg_flops(depth, V, T, B)
+    tok = B * T
+    step_s = ms / 1e3
+    fwd_bwd_ms = sum(v[0] for k, v in breakdown.items()
+                     if not k.startswith("ns_") and k != "muon_elementwise")
+    kf = kernel_flops(dom, depth, V, T, B)
+    avg_launch_s = dom_ms / dom_cnt / 1e3
+    achieved = kf / avg_launch_s / 1e12
+    peak = PEAK_BF16 / 1e12
+    out = {
+        "metric": METRIC,
+        "value": tok / step_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if prec == Bd.PREC_BF16 else "fp8-e4m3/e5m2 block GEMMs, bf16 rest",
+        "data": "synthetic: uniform token ids, N(0,1/fan_in) weights (seeded PCG64)",
+        "config": {"workload": args.workload, "depth": depth, "d_model": d, "n_head": H, "seq_len": T,
+                   "micro_batch": B, "vocab": V, "tokens_per_step": tok, "parallelism": "single GPU",
+                   "optimizer": "Muon (5 Newton-Schulz iterations) on all block matrices"},
+        "mfu": (f_model + f_ns) / step_s / PEAK_BF16,
+        "mfu_model": f_model / (fwd_bwd_ms / 1e3) / PEAK_BF16 if fwd_bwd_ms else None,
+        "tflops": (f_model + f_ns) / step_s / 1e12,
+        "loss": [first_loss, last_loss],
+        "roofline": {"bound": "mfma", "kernel": dom, "achieved": achieved, "peak": peak,
+                     "unit": "TFLOP/s", "frac": achieved / peak, "traffic": None,
+                     "flops_per_launch": kf, "avg_launch_ms": avg_launch_s * 1e3,
+                     "launches": dom_cnt},
+        "breakdown_ms_per_step": {k: round(v[0], 3) for k, v in sorted(breakdown.items(), key=lambda kv: -kv[1][0])},
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(args.workload, depth, V, T, B, inputs.SEED_IDS, inputs.SEED_W)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

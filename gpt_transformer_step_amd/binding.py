@@ -61,9 +61,13 @@ _SIGS = {
     "gpt_op_attention_bwd": [_i32, _i32, _i32, _vp, _vp, _vp, _i64, _vp, _vp, _i64, _vp, _vp, _vp,
                              _vp, _vp, _i64, _vp],
     "gpt_workspace_tensor": [_P(Shape), _i32, _i32, _P(_sz), _P(_sz)],
+    "gpt_profile_enable": [ctypes.c_uint64],
+    "gpt_profile_reset": [],
+    "gpt_profile_read": [_i32, _P(ctypes.c_double), _P(_i32)],
 }
 
-EXPORTED = ["gpt_status_string", "gpt_last_error", "gpt_abi_version"] + list(_SIGS)
+EXPORTED = ["gpt_status_string", "gpt_last_error", "gpt_abi_version", "gpt_profile_num_categories",
+            "gpt_profile_category_name"] + list(_SIGS)
 
 for _name, _args in _SIGS.items():
     _f = getattr(_lib, _name, None)
@@ -76,6 +80,9 @@ _lib.gpt_last_error.argtypes = []
 _lib.gpt_status_string.restype = ctypes.c_char_p
 _lib.gpt_status_string.argtypes = [ctypes.c_int]
 _lib.gpt_abi_version.restype = ctypes.c_int32
+_lib.gpt_profile_num_categories.restype = ctypes.c_int32
+_lib.gpt_profile_category_name.restype = ctypes.c_char_p
+_lib.gpt_profile_category_name.argtypes = [ctypes.c_int32]
 
 
 def lib():
@@ -199,3 +206,21 @@ def attention_bwd(q, k, v, out, dout, lse, delta, dq_acc, dk, dv, batch, n_head,
     _call("gpt_op_attention_bwd", batch, n_head, seq_len, _ptr(q), _ptr(k), _ptr(v), ld_qkv,
           _ptr(out), _ptr(dout), ld_out, _ptr(lse), _ptr(delta), _ptr(dq_acc), _ptr(dk), _ptr(dv),
           ld_dkv, _stream(stream))
+
+
+def profile_categories():
+    return [_lib.gpt_profile_category_name(i).decode() for i in range(_lib.gpt_profile_num_categories())]
+
+
+def profile_enable(mask):
+    _call("gpt_profile_enable", int(mask))
+
+
+def profile_reset():
+    _call("gpt_profile_reset")
+
+
+def profile_read(cat):
+    t, n = ctypes.c_double(), _i32()
+    _call("gpt_profile_read", cat, ctypes.byref(t), ctypes.byref(n))
+    return t.value, n.value

