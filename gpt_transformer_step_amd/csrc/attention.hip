@@ -17,11 +17,16 @@
 //     read from LDS in that same order (it is stored transposed, keys
 //     contiguous, by an 8x8 register transpose at load time);
 //   * K / V tiles of 64 keys are double buffered in LDS.
-// Backward (one workgroup = 128 keys, 4 waves x 32 keys, looping over query
-// tiles of 64): recompute S = Q K^T and P = exp(S - lse), dV^T += dO^T P,
-// dP = dO V^T, dS = P (dP - D), dK^T += Q^T dS; dS goes through LDS for
-// dQ = dS K, which is accumulated in fp32 with atomics (dQ receives a
-// contribution from every key block).
+// Backward, two kernels and no atomics:
+//   * dK/dV: one workgroup = 128 keys (4 waves x 32 keys) looping over query
+//     tiles of 32: recompute S = Q K^T and P = exp(S - lse), dP = dO V^T,
+//     dS = P (dP - delta), then dV^T += dO^T P and dK^T += Q^T dS with P and
+//     dS taken straight from the accumulators;
+//   * dQ: one workgroup = 128 queries looping over key tiles of 64, shaped
+//     like the forward: S^T and dP^T recomputed, dQ^T += K^T dS^T.
+// The second kernel recomputes two of the four products of the first; in
+// exchange dQ needs neither fp32 atomics nor a pass through LDS for dS, and
+// the result is deterministic.
 
 #include "common.h"
 #include "kernels.h"
@@ -32,6 +37,7 @@ namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kRescale = 8.0f;  // log2 of the largest unnormalised P
 
 __device__ __forceinline__ int sw(int r) { return r & 7; }
 // rows of 256 bytes (16 chunks of 16 B)
@@ -41,20 +47,30 @@ __device__ __forceinline__ int off128(int r, int c) { return r * 128 + ((c ^ sw(
 
 __device__ __forceinline__ uint4 ld16(const uint16_t* p) { return *reinterpret_cast<const uint4*>(p); }
 
-// transpose an 8x8 bf16 block held as 8 rows of 16 B: out[c] = column c
-__device__ __forceinline__ void transpose8x8(const uint4* in, uint4* out) {
+// column c of an 8x8 bf16 block held as 8 rows of 16 B
+__device__ __forceinline__ uint4 column8x8(const uint4* in, int c) {
+  const int d = c >> 1;
+  uint32_t w[4];
 #pragma unroll
-  for (int c = 0; c < 8; ++c) {
-    const int d = c >> 1;
-    uint32_t w[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const uint32_t a = reinterpret_cast<const uint32_t*>(&in[2 * q])[d];
-      const uint32_t b = reinterpret_cast<const uint32_t*>(&in[2 * q + 1])[d];
-      w[q] = (c & 1) ? ((a >> 16) | (b & 0xffff0000u)) : ((a & 0xffffu) | (b << 16));
-    }
-    out[c] = make_uint4(w[0], w[1], w[2], w[3]);
+  for (int q = 0; q < 4; ++q) {
+    const uint32_t a = reinterpret_cast<const uint32_t*>(&in[2 * q])[d];
+    const uint32_t b = reinterpret_cast<const uint32_t*>(&in[2 * q + 1])[d];
+    w[q] = (c & 1) ? ((a >> 16) | (b & 0xffff0000u)) : ((a & 0xffffu) | (b << 16));
   }
+  return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+// column c of an 8x4 bf16 block held as 8 rows of 8 B
+__device__ __forceinline__ uint4 column8x4(const uint2* in, int c) {
+  const int d = c >> 1;
+  uint32_t w[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const uint32_t a = reinterpret_cast<const uint32_t*>(&in[2 * q])[d];
+    const uint32_t b = reinterpret_cast<const uint32_t*>(&in[2 * q + 1])[d];
+    w[q] = (c & 1) ? ((a >> 16) | (b & 0xffff0000u)) : ((a & 0xffffu) | (b << 16));
+  }
+  return make_uint4(w[0], w[1], w[2], w[3]);
 }
 
 // B/A fragment of 8 keys in accumulator order from a transposed tile
@@ -119,10 +135,8 @@ __device__ __forceinline__ void fwd_store_kv(const KVLoad& L, char* sk, char* sv
   }
   if (tid < 128) {
     const int kb = tid & 7, eb = tid >> 3;
-    uint4 t[8];
-    transpose8x8(L.v, t);
 #pragma unroll
-    for (int c = 0; c < 8; ++c) *reinterpret_cast<uint4*>(svt + off128(eb * 8 + c, kb)) = t[c];
+    for (int c = 0; c < 8; ++c) *reinterpret_cast<uint4*>(svt + off128(eb * 8 + c, kb)) = column8x8(L.v, c);
   }
 }
 
@@ -193,34 +207,43 @@ attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, 
           s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fk, fq[ks], s[kt], 0, 0, 0);
         }
       }
-      // scale, mask, tile max
+      // scale, mask (diagonal / ragged tiles only), tile max
+      const bool diag = (key0 + FK - 1 > wq0) || (key0 + FK > T);  // wave-uniform
       float x[32];
       float tmax = -INFINITY;
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
-          const int key = key0 + kt * 32 + 8 * (e >> 2) + 4 * lh + (e & 3);
-          const float val = (key <= myq && key < T) ? s[kt][e] * c : -INFINITY;
+          float val = s[kt][e] * c;
+          if (diag) {
+            const int key = key0 + kt * 32 + 8 * (e >> 2) + 4 * lh + (e & 3);
+            val = (key <= myq && key < T) ? val : -INFINITY;
+          }
           x[kt * 16 + e] = val;
           tmax = fmaxf(tmax, val);
         }
       tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-      const float mnew = fmaxf(m, tmax);
-      const float mref = (mnew == -INFINITY) ? 0.f : mnew;
-      const float alpha = exp2f(m - mref);
+      // lazy rescale: the reference max moves only when a row max exceeds it
+      // by more than 2^8, so P stays <= 256 and most tiles skip the O rescale
+      const bool need = tmax > m + kRescale;
+      if (__any(need)) {
+        const float mn = need ? tmax : m;
+        const float alpha = __builtin_amdgcn_exp2f(m - mn);
+        l *= alpha;
+        m = mn;
+#pragma unroll
+        for (int et = 0; et < 4; ++et)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) o[et][e] *= alpha;
+      }
       float psum = 0.f;
 #pragma unroll
       for (int i = 0; i < 32; ++i) {
-        x[i] = exp2f(x[i] - mref);
+        x[i] = __builtin_amdgcn_exp2f(x[i] - m);
         psum += x[i];
       }
-      l = l * alpha + psum;
-      m = mnew;
-#pragma unroll
-      for (int et = 0; et < 4; ++et)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) o[et][e] *= alpha;
+      l += psum;
       // O^T += V^T P^T over the 64 keys (4 k-steps of 16)
 #pragma unroll
       for (int st = 0; st < 4; ++st) {
@@ -259,52 +282,61 @@ attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, 
 // ============================================================================
 // backward
 // ============================================================================
-constexpr int BKEYS = 128;  // keys per workgroup
-constexpr int BQT = 64;     // queries per tile
-
-// delta[b,h,t] = sum_e dout * out; also zero dq_acc. One wave per (token, head).
-__global__ void attn_bwd_pre_kernel(const uint16_t* __restrict__ out, const uint16_t* __restrict__ dout,
-                                    long long ld_out, float* __restrict__ delta, float* __restrict__ dq_acc,
-                                    int H, int T, long long NH) {
+// delta[b,h,t] = sum_e dout * out.  One wave per (token, head).
+__global__ void __launch_bounds__(256) attn_bwd_pre_kernel(const uint16_t* __restrict__ out,
+                                                           const uint16_t* __restrict__ dout, long long ld_out,
+                                                           float* __restrict__ delta, int H, int T, long long NH) {
   const int lane = threadIdx.x & 63;
   const long long w = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (w >= NH) return;
   const long long n = w / H;
   const int h = (int)(w % H);
-  const uint16_t* o = out + n * ld_out + h * 128;
-  const uint16_t* d = dout + n * ld_out + h * 128;
-  const uint32_t ow = reinterpret_cast<const uint32_t*>(o)[lane];
-  const uint32_t dw = reinterpret_cast<const uint32_t*>(d)[lane];
-  float s = lo_bf(ow) * lo_bf(dw) + hi_bf(ow) * hi_bf(dw);
-  s = wave_sum(s);
+  const uint32_t ow = reinterpret_cast<const uint32_t*>(out + n * ld_out + h * 128)[lane];
+  const uint32_t dw = reinterpret_cast<const uint32_t*>(dout + n * ld_out + h * 128)[lane];
+  const float s = wave_sum(lo_bf(ow) * lo_bf(dw) + hi_bf(ow) * hi_bf(dw));
   const long long b = n / T, t = n % T;
   if (lane == 0) delta[(b * H + h) * T + t] = s;
-  float2* dq = reinterpret_cast<float2*>(dq_acc + n * (long long)H * 128 + h * 128);
-  dq[lane] = make_float2(0.f, 0.f);
 }
 
-constexpr int B_QN = 0;                      // Q natural   [64][256 B]
-constexpr int B_QT = B_QN + BQT * 256;       // Q^T         [128][128 B]
-constexpr int B_DN = B_QT + 128 * 128;       // dO natural  [64][256 B]
-constexpr int B_DT = B_DN + BQT * 256;       // dO^T        [128][128 B]
-constexpr int B_DS = B_DT + 128 * 128;       // dS          [64 q][256 B = 128 keys]
-constexpr int B_KT = B_DS + BQT * 256;       // K^T         [128 e][256 B = 128 keys]
-constexpr int B_LSE = B_KT + 128 * 256;      // lse * log2e [64] fp32
-constexpr int B_DEL = B_LSE + BQT * 4;       // delta       [64] fp32
-constexpr int B_TOTAL = B_DEL + BQT * 4;
+// rows of 64 bytes (4 chunks of 16 B)
+__device__ __forceinline__ int off64(int r, int c) { return r * 64 + ((c ^ (r & 3)) << 4); }
 
-__global__ void __launch_bounds__(256, 1)
-attn_bwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
-                long long ld, const uint16_t* __restrict__ dout, long long ld_out, const float* __restrict__ lse,
-                const float* __restrict__ delta, float* __restrict__ dq_acc, uint16_t* __restrict__ dk,
-                uint16_t* __restrict__ dv, long long ld_dkv, int H, int T) {
-  __shared__ __attribute__((aligned(16))) char smem[B_TOTAL];
+__device__ __forceinline__ bf16x8_t read_perm_frag64(const char* lds, int row, int s, int h) {
+  const uint2 a = *reinterpret_cast<const uint2*>(lds + off64(row, 2 * s) + 8 * h);
+  const uint2 b = *reinterpret_cast<const uint2*>(lds + off64(row, 2 * s + 1) + 8 * h);
+  bf16x8_t f;
+  uint32_t* w = reinterpret_cast<uint32_t*>(&f);
+  w[0] = a.x; w[1] = a.y; w[2] = b.x; w[3] = b.y;
+  return f;
+}
+
+// ---------------------------------------------------------------------------
+// dK, dV: one workgroup = 128 keys (4 waves x 32), query tiles of 32.
+//   S = Q K^T, dP = dO V^T (accumulator: column = key, rows = queries)
+//   P = exp(S - lse), dS = P (dP - delta)
+//   dV^T += dO^T P, dK^T += Q^T dS  (P, dS as B operands in accumulator order)
+// ---------------------------------------------------------------------------
+constexpr int KV_KEYS = 128;
+constexpr int KV_Q = 32;
+constexpr int KV_SK = 0;                          // K natural [128 keys][256 B]
+constexpr int KV_QN = KV_SK + KV_KEYS * 256;      // Q natural [32][256 B]
+constexpr int KV_QT = KV_QN + KV_Q * 256;         // Q^T [128 e][64 B]
+constexpr int KV_DN = KV_QT + 128 * 64;           // dO natural
+constexpr int KV_DT = KV_DN + KV_Q * 256;         // dO^T
+constexpr int KV_LSE = KV_DT + 128 * 64;          // lse * log2e [32]
+constexpr int KV_DEL = KV_LSE + KV_Q * 4;         // delta [32]
+constexpr int KV_TOTAL = KV_DEL + KV_Q * 4;
+
+__global__ void __launch_bounds__(256, 2)
+attn_bwd_kv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+                   long long ld, const uint16_t* __restrict__ dout, long long ld_out, const float* __restrict__ lse,
+                   const float* __restrict__ delta, uint16_t* __restrict__ dk, uint16_t* __restrict__ dv,
+                   long long ld_dkv, int H, int T) {
+  __shared__ __attribute__((aligned(16))) char smem[KV_TOTAL];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, lr = lane & 31, lh = lane >> 5;
-  const int nkb = (T + BKEYS - 1) / BKEYS;
-  const int kb = blockIdx.x;  // key block; the early blocks (most query tiles) come first
+  const int kb = blockIdx.x;
   const int bh = blockIdx.y, b = bh / H, h = bh % H;
   const long long rowbase = (long long)b * T;
-  const int d = H * 128;
   const uint16_t* qh = q + rowbase * ld + h * 128;
   const uint16_t* kh = k + rowbase * ld + h * 128;
   const uint16_t* vh = v + rowbase * ld + h * 128;
@@ -313,38 +345,31 @@ attn_bwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, 
   const float* delh = delta + (long long)bh * T;
   const float scale = 0.08838834764831845f;
   const float c = scale * kLog2e;
-  (void)nkb;
 
-  const int k0 = kb * BKEYS;
+  const int k0 = kb * KV_KEYS;
   const int wk0 = k0 + wave * 32;
-  const int mykey = wk0 + lr;  // this lane's key (column of S, P, dS)
+  const int mykey = wk0 + lr;
 
-  // K and V fragments of the wave's 32 keys (B operand: column = key)
-  bf16x8_t fk[8], fv[8];
+  // V fragments of the wave's keys (B operand: column = key, 8 features per k-step)
+  bf16x8_t fv[8];
 #pragma unroll
   for (int ks = 0; ks < 8; ++ks) {
     if (mykey < T) {
-      const uint4 a = ld16(kh + (long long)mykey * ld + ks * 16 + lh * 8);
-      const uint4 bq = ld16(vh + (long long)mykey * ld + ks * 16 + lh * 8);
-      fk[ks] = *reinterpret_cast<const bf16x8_t*>(&a);
-      fv[ks] = *reinterpret_cast<const bf16x8_t*>(&bq);
+      const uint4 a = ld16(vh + (long long)mykey * ld + ks * 16 + lh * 8);
+      fv[ks] = *reinterpret_cast<const bf16x8_t*>(&a);
     } else {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) { fk[ks][e] = 0; fv[ks][e] = 0; }
+      for (int e = 0; e < 8; ++e) fv[ks][e] = 0;
     }
   }
-  // K^T of the whole key block in LDS (for dQ = dS K)
-  {
-    const int kbk = tid & 15, eb = tid >> 4;  // keys kbk*8.., features eb*8..
-    uint4 blk[8], t8[8];
+  // K of the whole block in LDS
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int key = k0 + kbk * 8 + j;
-      blk[j] = key < T ? ld16(kh + (long long)key * ld + eb * 8) : make_uint4(0, 0, 0, 0);
-    }
-    transpose8x8(blk, t8);
-#pragma unroll
-    for (int cc = 0; cc < 8; ++cc) *reinterpret_cast<uint4*>(smem + B_KT + off256(eb * 8 + cc, kbk)) = t8[cc];
+  for (int i = 0; i < 8; ++i) {
+    const int cidx = tid + 256 * i;
+    const int r = cidx >> 4, ch = cidx & 15;
+    const int key = k0 + r;
+    *reinterpret_cast<uint4*>(smem + KV_SK + off256(r, ch)) =
+        key < T ? ld16(kh + (long long)key * ld + ch * 8) : make_uint4(0, 0, 0, 0);
   }
 
   f32x16_t dvt[4], dkt[4];
@@ -353,138 +378,89 @@ attn_bwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, 
 #pragma unroll
     for (int e = 0; e < 16; ++e) { dvt[et][e] = 0.f; dkt[et][e] = 0.f; }
 
-  const int qt_first = k0 / BQT;
-  const int nqt = (T + BQT - 1) / BQT;
-
-  // loader: threads 0..127 an 8x8 block of Q, 128..255 of dO
-  auto load_tile = [&](int qt, uint4* blk) {
-    const int t = tid & 127;
-    const int qb8 = t & 7, eb = t >> 3;  // queries qb8*8.., features eb*8..
-    const uint16_t* base = (tid < 128) ? qh : doh;
-    const long long ldx = (tid < 128) ? ld : ld_out;
+  const int nqt = (T + KV_Q - 1) / KV_Q;
+  for (int qt = k0 / KV_Q; qt < nqt; ++qt) {
+    const int q0 = qt * KV_Q;
+    __syncthreads();
+    {
+      // an 8x4 block of Q (tid < 128) or dO: queries qb*8 .. +7, features eb*4 .. +3
+      const int blk = tid & 127, qb = blk & 3, eb = blk >> 2;
+      const bool isq = tid < 128;
+      const uint16_t* base = isq ? qh : doh;
+      const long long ldx = isq ? ld : ld_out;
+      uint2 r8[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int qq = qt * BQT + qb8 * 8 + j;
-      blk[j] = qq < T ? ld16(base + (long long)qq * ldx + eb * 8) : make_uint4(0, 0, 0, 0);
-    }
-  };
-  auto store_tile = [&](int qt, const uint4* blk) {
-    const int t = tid & 127;
-    const int qb8 = t & 7, eb = t >> 3;
-    char* nat = smem + ((tid < 128) ? B_QN : B_DN);
-    char* tr = smem + ((tid < 128) ? B_QT : B_DT);
+      for (int j = 0; j < 8; ++j) {
+        const int qq = q0 + qb * 8 + j;
+        r8[j] = qq < T ? *reinterpret_cast<const uint2*>(base + (long long)qq * ldx + eb * 4) : make_uint2(0, 0);
+      }
+      char* nat = smem + (isq ? KV_QN : KV_DN);
+      char* tr = smem + (isq ? KV_QT : KV_DT);
 #pragma unroll
-    for (int j = 0; j < 8; ++j) *reinterpret_cast<uint4*>(nat + off256(qb8 * 8 + j, eb)) = blk[j];
-    uint4 t8[8];
-    transpose8x8(blk, t8);
+      for (int j = 0; j < 8; ++j)
+        *reinterpret_cast<uint2*>(nat + off256(qb * 8 + j, eb >> 1) + 8 * (eb & 1)) = r8[j];
 #pragma unroll
-    for (int cc = 0; cc < 8; ++cc) *reinterpret_cast<uint4*>(tr + off128(eb * 8 + cc, qb8)) = t8[cc];
-    if (tid < BQT) {
-      const int qq = qt * BQT + tid;
-      reinterpret_cast<float*>(smem + B_LSE)[tid] = qq < T ? lseh[qq] * kLog2e : INFINITY;
-      reinterpret_cast<float*>(smem + B_DEL)[tid] = qq < T ? delh[qq] : 0.f;
-    }
-  };
-
-  uint4 pre[8];
-  if (qt_first < nqt) {
-    load_tile(qt_first, pre);
-    store_tile(qt_first, pre);
-  }
-  __syncthreads();
-
-  const float* slse = reinterpret_cast<const float*>(smem + B_LSE);
-  const float* sdel = reinterpret_cast<const float*>(smem + B_DEL);
-
-  for (int qt = qt_first; qt < nqt; ++qt) {
-    const bool more = qt + 1 < nqt;
-    if (more) load_tile(qt + 1, pre);
-    const int q0 = qt * BQT;
-
-    // S = Q K^T and dP = dO V^T for the two 32-query halves
-    f32x16_t s[2], dp[2];
-#pragma unroll
-    for (int h2 = 0; h2 < 2; ++h2) {
-#pragma unroll
-      for (int e = 0; e < 16; ++e) { s[h2][e] = 0.f; dp[h2][e] = 0.f; }
-#pragma unroll
-      for (int ks = 0; ks < 8; ++ks) {
-        const bf16x8_t aq = *reinterpret_cast<const bf16x8_t*>(smem + B_QN + off256(h2 * 32 + lr, ks * 2 + lh));
-        const bf16x8_t ad = *reinterpret_cast<const bf16x8_t*>(smem + B_DN + off256(h2 * 32 + lr, ks * 2 + lh));
-        s[h2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, fk[ks], s[h2], 0, 0, 0);
-        dp[h2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ad, fv[ks], dp[h2], 0, 0, 0);
+      for (int cc = 0; cc < 4; ++cc) *reinterpret_cast<uint4*>(tr + off64(eb * 4 + cc, qb)) = column8x4(r8, cc);
+      if (tid < KV_Q) {
+        const int qq = q0 + tid;
+        reinterpret_cast<float*>(smem + KV_LSE)[tid] = qq < T ? lseh[qq] * kLog2e : INFINITY;
+      } else if (tid < 2 * KV_Q) {
+        const int i = tid - KV_Q, qq = q0 + i;
+        reinterpret_cast<float*>(smem + KV_DEL)[i] = qq < T ? delh[qq] : 0.f;
       }
     }
-    // P and dS; element (h2, e) is query q0 + 32 h2 + 8 (e/4) + 4 lh + e%4, key mykey
-    float p[32], ds[32];
+    __syncthreads();
+    if (q0 + KV_Q - 1 < wk0) continue;  // every query of the tile precedes every key of the wave
+
+    f32x16_t sacc, dpacc;
 #pragma unroll
-    for (int h2 = 0; h2 < 2; ++h2)
+    for (int e = 0; e < 16; ++e) { sacc[e] = 0.f; dpacc[e] = 0.f; }
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int ql = h2 * 32 + 8 * (e >> 2) + 4 * lh + (e & 3);
-        const int qq = q0 + ql;
-        float pv = exp2f(s[h2][e] * c - slse[ql]);
-        pv = (mykey <= qq && mykey < T) ? pv : 0.f;
-        p[h2 * 16 + e] = pv;
-        ds[h2 * 16 + e] = pv * (dp[h2][e] - sdel[ql]);
+    for (int ks = 0; ks < 8; ++ks) {
+      const bf16x8_t aq = *reinterpret_cast<const bf16x8_t*>(smem + KV_QN + off256(lr, ks * 2 + lh));
+      const bf16x8_t bk = *reinterpret_cast<const bf16x8_t*>(smem + KV_SK + off256(wave * 32 + lr, ks * 2 + lh));
+      const bf16x8_t ad = *reinterpret_cast<const bf16x8_t*>(smem + KV_DN + off256(lr, ks * 2 + lh));
+      sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, bk, sacc, 0, 0, 0);
+      dpacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ad, fv[ks], dpacc, 0, 0, 0);
+    }
+    const float* slse = reinterpret_cast<const float*>(smem + KV_LSE);
+    const float* sdel = reinterpret_cast<const float*>(smem + KV_DEL);
+    const bool diag = (q0 < wk0 + 31) || (q0 + KV_Q > T) || (wk0 + 32 > T);
+    // P and dS packed to bf16 straight away, in accumulator order (k-step st
+    // holds values 8 st .. 8 st + 7)
+    bf16x8_t fp[2], fs[2];
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+      uint32_t* wp = reinterpret_cast<uint32_t*>(&fp[st]);
+      uint32_t* wd = reinterpret_cast<uint32_t*>(&fs[st]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float pv[2], dv2[2];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const int e = 8 * st + 2 * i + u;
+          const int ql = 8 * (e >> 2) + 4 * lh + (e & 3);
+          float pe = __builtin_amdgcn_exp2f(sacc[e] * c - slse[ql]);
+          if (diag) pe = (mykey <= q0 + ql && mykey < T) ? pe : 0.f;
+          pv[u] = pe;
+          dv2[u] = pe * (dpacc[e] - sdel[ql]);
+        }
+        wp[i] = pack_bf2(pv[0], pv[1]);
+        wd[i] = pack_bf2(dv2[0], dv2[1]);
       }
-    // dV^T += dO^T P ; dK^T += Q^T dS  (k-steps of 16 queries, accumulator order)
+    }
 #pragma unroll
-    for (int st = 0; st < 4; ++st) {
-      const bf16x8_t fp = pack_perm(p + (st >> 1) * 16, st & 1);
-      const bf16x8_t fs = pack_perm(ds + (st >> 1) * 16, st & 1);
+    for (int st = 0; st < 2; ++st) {
 #pragma unroll
       for (int et = 0; et < 4; ++et) {
-        const bf16x8_t ad = read_perm_frag(smem + B_DT, et * 32 + lr, st, lh);
-        const bf16x8_t aq = read_perm_frag(smem + B_QT, et * 32 + lr, st, lh);
-        dvt[et] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ad, fp, dvt[et], 0, 0, 0);
-        dkt[et] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, fs, dkt[et], 0, 0, 0);
+        const bf16x8_t ad = read_perm_frag64(smem + KV_DT, et * 32 + lr, st, lh);
+        const bf16x8_t aq = read_perm_frag64(smem + KV_QT, et * 32 + lr, st, lh);
+        dvt[et] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ad, fp[st], dvt[et], 0, 0, 0);
+        dkt[et] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, fs[st], dkt[et], 0, 0, 0);
       }
     }
-    // dS to LDS as [query][key] (keys of the whole block)
-    {
-      uint16_t* sds = reinterpret_cast<uint16_t*>(smem + B_DS);
-      const int key_local = wave * 32 + lr;
-      const int kc = key_local >> 3, kw = key_local & 7;
-#pragma unroll
-      for (int h2 = 0; h2 < 2; ++h2)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int ql = h2 * 32 + 8 * (e >> 2) + 4 * lh + (e & 3);
-          sds[(off256(ql, kc) >> 1) + kw] = f2bf(ds[h2 * 16 + e]);
-        }
-    }
-    __syncthreads();
-    // dQ[q, e] += scale * sum_key dS[q, key] K[key, e]; wave owns features wave*32..+31
-    {
-      f32x16_t acc[2];
-#pragma unroll
-      for (int h2 = 0; h2 < 2; ++h2) {
-#pragma unroll
-        for (int e = 0; e < 16; ++e) acc[h2][e] = 0.f;
-#pragma unroll
-        for (int ks = 0; ks < 8; ++ks) {
-          const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(smem + B_DS + off256(h2 * 32 + lr, ks * 2 + lh));
-          const bf16x8_t bk = *reinterpret_cast<const bf16x8_t*>(smem + B_KT + off256(wave * 32 + lr, ks * 2 + lh));
-          acc[h2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bk, acc[h2], 0, 0, 0);
-        }
-      }
-      // accumulator: column = feature wave*32 + lr, rows = queries 8g + 4lh + r
-#pragma unroll
-      for (int h2 = 0; h2 < 2; ++h2)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int qq = q0 + h2 * 32 + 8 * (e >> 2) + 4 * lh + (e & 3);
-          if (qq < T)
-            unsafeAtomicAdd(dq_acc + (rowbase + qq) * d + h * 128 + wave * 32 + lr, acc[h2][e] * scale);
-        }
-    }
-    __syncthreads();
-    if (more) store_tile(qt + 1, pre);
-    __syncthreads();
   }
 
-  // dK = scale * dK^T^T, dV: lane owns key mykey, features et*32 + 8g + 4lh + r
   if (mykey < T) {
     uint16_t* dkr = dk + (rowbase + mykey) * ld_dkv + h * 128;
     uint16_t* dvr = dv + (rowbase + mykey) * ld_dkv + h * 128;
@@ -502,6 +478,139 @@ attn_bwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, 
   }
 }
 
+// ---------------------------------------------------------------------------
+// dQ: one workgroup = 128 queries (4 waves x 32), key tiles of 64.
+//   S^T = K Q^T, dP^T = V dO^T (accumulator: column = query, rows = keys)
+//   dS^T = P^T (dP^T - delta);  dQ^T += K^T dS^T  (dS^T as B operand)
+// ---------------------------------------------------------------------------
+constexpr int DQ_Q = 128;
+constexpr int DQ_K = 64;
+constexpr int DQ_KN = 0;                       // K natural [64][256 B]
+constexpr int DQ_VN = DQ_KN + DQ_K * 256;      // V natural [64][256 B]
+constexpr int DQ_KT = DQ_VN + DQ_K * 256;      // K^T [128 e][128 B]
+constexpr int DQ_TOTAL = DQ_KT + 128 * 128;
+
+__global__ void __launch_bounds__(256, 2)
+attn_bwd_q_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+                  long long ld, const uint16_t* __restrict__ dout, long long ld_out, const float* __restrict__ lse,
+                  const float* __restrict__ delta, float* __restrict__ dq_out, int H, int T) {
+  __shared__ __attribute__((aligned(16))) char smem[DQ_TOTAL];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, lr = lane & 31, lh = lane >> 5;
+  const int nqb = (T + DQ_Q - 1) / DQ_Q;
+  const int qb = nqb - 1 - blockIdx.x;  // longest rows first
+  const int bh = blockIdx.y, b = bh / H, h = bh % H;
+  const long long rowbase = (long long)b * T;
+  const int d = H * 128;
+  const uint16_t* qh = q + rowbase * ld + h * 128;
+  const uint16_t* kh = k + rowbase * ld + h * 128;
+  const uint16_t* vh = v + rowbase * ld + h * 128;
+  const uint16_t* doh = dout + rowbase * ld_out + h * 128;
+  const float scale = 0.08838834764831845f;
+  const float c = scale * kLog2e;
+
+  const int q0 = qb * DQ_Q;
+  const int wq0 = q0 + wave * 32;
+  const int myq = wq0 + lr;
+  bf16x8_t fq[8], fd[8];
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) {
+    if (myq < T) {
+      const uint4 a = ld16(qh + (long long)myq * ld + ks * 16 + lh * 8);
+      const uint4 bq = ld16(doh + (long long)myq * ld_out + ks * 16 + lh * 8);
+      fq[ks] = *reinterpret_cast<const bf16x8_t*>(&a);
+      fd[ks] = *reinterpret_cast<const bf16x8_t*>(&bq);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) { fq[ks][e] = 0; fd[ks][e] = 0; }
+    }
+  }
+  const float lse2 = myq < T ? lse[(long long)bh * T + myq] * kLog2e : INFINITY;
+  const float del = myq < T ? delta[(long long)bh * T + myq] : 0.f;
+
+  f32x16_t dqt[4];
+#pragma unroll
+  for (int et = 0; et < 4; ++et)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) dqt[et][e] = 0.f;
+
+  const int last_key = min(T - 1, q0 + DQ_Q - 1);
+  const int ntiles = last_key / DQ_K + 1;
+  for (int j = 0; j < ntiles; ++j) {
+    const int key0 = j * DQ_K;
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int cidx = tid + 256 * i;
+      const int r = cidx >> 4, ch = cidx & 15;
+      const int key = key0 + r;
+      const bool ok = key < T;
+      *reinterpret_cast<uint4*>(smem + DQ_KN + off256(r, ch)) =
+          ok ? ld16(kh + (long long)key * ld + ch * 8) : make_uint4(0, 0, 0, 0);
+      *reinterpret_cast<uint4*>(smem + DQ_VN + off256(r, ch)) =
+          ok ? ld16(vh + (long long)key * ld + ch * 8) : make_uint4(0, 0, 0, 0);
+    }
+    if (tid < 128) {
+      const int kb8 = tid & 7, eb = tid >> 3;
+      uint4 r8[8];
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj) {
+        const int key = key0 + kb8 * 8 + jj;
+        r8[jj] = key < T ? ld16(kh + (long long)key * ld + eb * 8) : make_uint4(0, 0, 0, 0);
+      }
+#pragma unroll
+      for (int cc = 0; cc < 8; ++cc)
+        *reinterpret_cast<uint4*>(smem + DQ_KT + off128(eb * 8 + cc, kb8)) = column8x8(r8, cc);
+    }
+    __syncthreads();
+    if (key0 > wq0 + 31) continue;  // wave-uniform: every key follows every query of the wave
+
+    f32x16_t st[2], dpt[2];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) { st[kt][e] = 0.f; dpt[kt][e] = 0.f; }
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) {
+        const bf16x8_t ak = *reinterpret_cast<const bf16x8_t*>(smem + DQ_KN + off256(kt * 32 + lr, ks * 2 + lh));
+        const bf16x8_t av = *reinterpret_cast<const bf16x8_t*>(smem + DQ_VN + off256(kt * 32 + lr, ks * 2 + lh));
+        st[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak, fq[ks], st[kt], 0, 0, 0);
+        dpt[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, fd[ks], dpt[kt], 0, 0, 0);
+      }
+    }
+    const bool diag = (key0 + DQ_K - 1 > wq0) || (key0 + DQ_K > T);
+    float ds[32];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int key = key0 + kt * 32 + 8 * (e >> 2) + 4 * lh + (e & 3);
+        float pv = __builtin_amdgcn_exp2f(st[kt][e] * c - lse2);
+        if (diag) pv = (key <= myq && key < T) ? pv : 0.f;
+        ds[kt * 16 + e] = pv * (dpt[kt][e] - del);
+      }
+#pragma unroll
+    for (int s4 = 0; s4 < 4; ++s4) {
+      const bf16x8_t fs = pack_perm(ds + (s4 >> 1) * 16, s4 & 1);
+#pragma unroll
+      for (int et = 0; et < 4; ++et) {
+        const bf16x8_t ak = read_perm_frag(smem + DQ_KT, et * 32 + lr, s4, lh);
+        dqt[et] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak, fs, dqt[et], 0, 0, 0);
+      }
+    }
+  }
+  if (myq < T) {
+    float* dqr = dq_out + (rowbase + myq) * d + h * 128;
+#pragma unroll
+    for (int et = 0; et < 4; ++et)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int e = et * 32 + 8 * g + 4 * lh;
+        *reinterpret_cast<float4*>(dqr + e) = make_float4(dqt[et][4 * g] * scale, dqt[et][4 * g + 1] * scale,
+                                                          dqt[et][4 * g + 2] * scale, dqt[et][4 * g + 3] * scale);
+      }
+  }
+}
+
 }  // namespace
 
 int launch_attn_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, long long ld_qkv, uint16_t* out,
@@ -515,17 +624,19 @@ int launch_attn_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, lon
 
 int launch_attn_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, long long ld_qkv,
                     const uint16_t* out, const uint16_t* dout, long long ld_out, const float* lse, float* delta,
-                    float* dq_acc, uint16_t* dk, uint16_t* dv, long long ld_dkv, int B, int H, int T,
+                    float* dq, uint16_t* dk, uint16_t* dv, long long ld_dkv, int B, int H, int T,
                     hipStream_t s) {
   if (B <= 0 || T <= 0) return 0;
   const long long NH = (long long)B * T * H;
   hipLaunchKernelGGL(attn_bwd_pre_kernel, dim3((unsigned)((NH + 3) / 4)), dim3(256), 0, s, out, dout, ld_out,
-                     delta, dq_acc, H, T, NH);
+                     delta, H, T, NH);
   GS_LAUNCH_CHECK("attn_bwd_pre");
-  dim3 grid((T + BKEYS - 1) / BKEYS, B * H);
-  hipLaunchKernelGGL(attn_bwd_kernel, grid, dim3(256), 0, s, q, k, v, ld_qkv, dout, ld_out, lse, delta, dq_acc,
-                     dk, dv, ld_dkv, H, T);
-  GS_LAUNCH_CHECK("attn_bwd");
+  hipLaunchKernelGGL(attn_bwd_kv_kernel, dim3((T + KV_KEYS - 1) / KV_KEYS, B * H), dim3(256), 0, s, q, k, v,
+                     ld_qkv, dout, ld_out, lse, delta, dk, dv, ld_dkv, H, T);
+  GS_LAUNCH_CHECK("attn_bwd_kv");
+  hipLaunchKernelGGL(attn_bwd_q_kernel, dim3((T + DQ_Q - 1) / DQ_Q, B * H), dim3(256), 0, s, q, k, v, ld_qkv,
+                     dout, ld_out, lse, delta, dq, H, T);
+  GS_LAUNCH_CHECK("attn_bwd_q");
   return 0;
 }
 

@@ -18,16 +18,18 @@ typedef __attribute__((__vector_size__(8 * sizeof(int)))) int i32x8_t;
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ float bf2f(uint16_t b) { return __uint_as_float(((uint32_t)b) << 16); }
 
-// round to nearest, ties to even (NaN stays NaN)
+// fp32 -> bf16 with the hardware converter (v_cvt_pk_bf16_f32: round to
+// nearest, ties to even; NaN stays NaN)
+typedef __bf16 bf16x2_hw __attribute__((ext_vector_type(2)));
+
 __device__ __forceinline__ uint16_t f2bf(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
+  const __bf16 h = (__bf16)f;
+  return __builtin_bit_cast(uint16_t, h);
 }
 
 __device__ __forceinline__ uint32_t pack_bf2(float a, float b) {
-  return (uint32_t)f2bf(a) | ((uint32_t)f2bf(b) << 16);
+  const bf16x2_hw v = {(__bf16)a, (__bf16)b};
+  return __builtin_bit_cast(uint32_t, v);
 }
 
 __device__ __forceinline__ float lo_bf(uint32_t w) { return __uint_as_float(w << 16); }

@@ -12,11 +12,13 @@
 //   * Operands are staged global -> registers -> LDS, double buffered, one
 //     barrier per K step; the next step's global loads are in flight while the
 //     current step's MFMAs run.
-//   * LDS holds every operand tile k-contiguous (128 B per row, 16 B chunks
-//     XOR-swizzled by row), which is the order MFMA fragments are read in.  An
-//     operand that is contiguous along M/N in memory (the weight-gradient and
-//     Gram products) is loaded as 8x8 blocks and transposed in registers
-//     before the LDS write, so no product needs a transposed copy in HBM.
+//   * Each operand tile sits in LDS in its memory layout.  A k-contiguous tile
+//     is read as MFMA fragments with 16-byte loads; an m/n-contiguous tile
+//     (the weight-gradient, data-gradient and Gram operands) is read with the
+//     gfx950 transpose load ds_read_b64_tr_b16, two per fragment, so no
+//     product needs a transposed copy in HBM or a transpose in registers.
+//     Both layouts are XOR-swizzled so fragment reads are bank-conflict free
+//     (64 banks of 4 bytes, 16-lane groups per 16-byte read).
 //   * The MFMA is issued with the operands swapped (B tile as src0), so each
 //     lane's accumulators hold one output row and groups of 4 consecutive
 //     columns: stores are 8/16-byte vectors and row reductions (the
@@ -33,103 +35,140 @@ namespace gs {
 namespace {
 
 constexpr int kBK = 64;        // K elements per stage (128 bytes of bf16)
-constexpr int kThreads = 256;
+// Workgroup shape per tile size: 256x256 tiles use 8 waves (two per SIMD, so
+// one wave's LDS waits overlap the other's MFMAs), 128x128 tiles use 4.  The
+// waves form a (NT/128) x 2 grid; each wave owns 64 rows and BN/2 columns.
+template <int BM, int BN>
+struct Cfg {
+  static constexpr int NT = BM == 256 ? 512 : 256;
+  static constexpr int WAVES_M = NT / 128;
+  static constexpr int WM = BM / WAVES_M, WN = BN / 2;
+  static constexpr int TM = WM / 32, TN = WN / 32;
+};
 
-__device__ __forceinline__ int swz(int r) { return r & 7; }
+// k-contiguous LDS tile: R rows of 64 k (128 B); 16-byte chunks XOR-swizzled
+// by (r >> 1) & 7 so that 16 consecutive rows at one logical chunk (a
+// fragment read by 16 lanes) hit 16 distinct bank groups (64 banks x 4 B).
+__device__ __forceinline__ int lds_off_k(int r, int kc) { return r * 128 + ((kc ^ ((r >> 1) & 7)) << 4); }
 
-// byte offset of 16-byte chunk kc of row r in a k-contiguous LDS tile
-__device__ __forceinline__ int lds_off(int r, int kc) { return r * 128 + ((kc ^ swz(r)) << 4); }
+// mn-contiguous LDS tile: 64 rows (k) of R elements (2R bytes) stored as in
+// memory; 64-byte units XOR-swizzled by k & 3, so the 4 consecutive k rows of
+// a transpose read land in 4 distinct bank groups.
+template <int R>
+__device__ __forceinline__ int lds_off_mn(int k, int i) {
+  return k * (2 * R) + ((((i >> 5) ^ (k & 3))) << 6) + ((i & 31) << 1);
+}
+
+typedef short v4s_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4s_t lds_v4s_t;
+
+// transpose read: within each 16-lane group, lane j receives element j % 4 of
+// the 8 bytes loaded by lanes 4t + j / 4 (t = 0..3)
+__device__ __forceinline__ v4s_t ds_read_tr(const char* lds_generic, int byte_off) {
+  const __attribute__((address_space(3))) char* base =
+      (const __attribute__((address_space(3))) char*)(lds_generic);
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s_t*)(base + byte_off));
+}
 
 // ---------------------------------------------------------------------------
-// global -> register staging of one operand tile (R rows x 64 k)
+// global -> register staging of one operand tile (R rows x 64 k): R*8 chunks
+// of 16 B, R/32 per thread, for either layout.
 // ---------------------------------------------------------------------------
-template <int R, bool KC>
+template <int R, bool KC, int NT>
 struct TileLoader {
-  // k-contiguous: R*8 chunks of 16 B, R/32 per thread.
-  // mn-contiguous: R*64/64 = R blocks of 8x8, one per thread (threads < R).
-  static constexpr int kRegs = KC ? R / 32 : 8;
+  static constexpr int kRegs = R * 8 / NT;
   uint4 v[kRegs];
 
+  template <bool GUARD>
   __device__ __forceinline__ void load(const uint16_t* __restrict__ X, long long ld, int row0, int rows,
                                        int k0, int K, int tid) {
-    const bool full = (row0 + R <= rows) && (k0 + kBK <= K);
-    if constexpr (KC) {
+    const bool full = !GUARD || ((row0 + R <= rows) && (k0 + kBK <= K));
 #pragma unroll
-      for (int i = 0; i < kRegs; ++i) {
-        const int c = tid + kThreads * i;
-        const int r = c >> 3, kc = c & 7;
-        const int gr = row0 + r, gk = k0 + kc * 8;
-        if (full) {
-          v[i] = *reinterpret_cast<const uint4*>(X + (long long)gr * ld + gk);
-        } else {
-          uint32_t w[4];
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            uint32_t lo = 0, hi = 0;
-            if (gr < rows && gk + 2 * j < K) lo = X[(long long)gr * ld + gk + 2 * j];
-            if (gr < rows && gk + 2 * j + 1 < K) hi = X[(long long)gr * ld + gk + 2 * j + 1];
-            w[j] = lo | (hi << 16);
-          }
-          v[i] = make_uint4(w[0], w[1], w[2], w[3]);
-        }
+    for (int i = 0; i < kRegs; ++i) {
+      const int c = tid + NT * i;
+      int gr, gk;
+      if constexpr (KC) {
+        gr = row0 + (c >> 3);
+        gk = k0 + (c & 7) * 8;
+      } else {
+        gk = k0 + c / (R / 8);
+        gr = row0 + (c % (R / 8)) * 8;
       }
-    } else {
-      if (tid < R) {
-        const int rb = tid % (R / 8), kb = tid / (R / 8);
-        const int gr = row0 + rb * 8;
+      const long long base = KC ? (long long)gr * ld + gk : (long long)gk * ld + gr;
+      if (full) {
+        v[i] = *reinterpret_cast<const uint4*>(X + base);
+      } else {
+        uint32_t w[4];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const int gk = k0 + kb * 8 + j;
-          if (full) {
-            v[j] = *reinterpret_cast<const uint4*>(X + (long long)gk * ld + gr);
+        for (int j = 0; j < 4; ++j) {
+          uint32_t lo = 0, hi = 0;
+          if constexpr (KC) {
+            if (gr < rows && gk + 2 * j < K) lo = X[base + 2 * j];
+            if (gr < rows && gk + 2 * j + 1 < K) hi = X[base + 2 * j + 1];
           } else {
-            uint32_t w[4];
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-              uint32_t lo = 0, hi = 0;
-              if (gk < K && gr + 2 * q < rows) lo = X[(long long)gk * ld + gr + 2 * q];
-              if (gk < K && gr + 2 * q + 1 < rows) hi = X[(long long)gk * ld + gr + 2 * q + 1];
-              w[q] = lo | (hi << 16);
-            }
-            v[j] = make_uint4(w[0], w[1], w[2], w[3]);
+            if (gk < K && gr + 2 * j < rows) lo = X[base + 2 * j];
+            if (gk < K && gr + 2 * j + 1 < rows) hi = X[base + 2 * j + 1];
           }
+          w[j] = lo | (hi << 16);
         }
+        v[i] = make_uint4(w[0], w[1], w[2], w[3]);
       }
+    }
+  }
+
+  // Direct global -> LDS copy of a whole interior tile (global_load_lds_dwordx4):
+  // lane l of wave w in round i fills the 16-byte LDS slot 256 i + 64 w + l of
+  // the tile, so each lane fetches the global chunk that the swizzled layout
+  // places in that slot.
+  __device__ __forceinline__ static void load_direct(const uint16_t* __restrict__ X, long long ld, int row0,
+                                                     int k0, char* lds, int tid) {
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+#pragma unroll
+    for (int i = 0; i < kRegs; ++i) {
+      const int slot = tid + NT * i;
+      long long src;
+      if constexpr (KC) {
+        const int r = slot >> 3, kc = (slot & 7) ^ ((r >> 1) & 7);
+        src = (long long)(row0 + r) * ld + k0 + kc * 8;
+      } else {
+        const int b = slot * 16;
+        const int k = b / (2 * R), rb = b % (2 * R);
+        const int i_el = (((rb >> 6) ^ (k & 3)) << 5) + ((rb & 63) >> 1);
+        src = (long long)(k0 + k) * ld + row0 + i_el;
+      }
+      __attribute__((address_space(3))) char* dst =
+          (__attribute__((address_space(3))) char*)(lds) + (NT * i + 64 * wave) * 16;
+      __builtin_amdgcn_global_load_lds((const void*)(X + src), (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
     }
   }
 
   __device__ __forceinline__ void store(char* lds, int tid) const {
+#pragma unroll
+    for (int i = 0; i < kRegs; ++i) {
+      const int c = tid + NT * i;
+      const int off = KC ? lds_off_k(c >> 3, c & 7) : lds_off_mn<R>(c / (R / 8), (c % (R / 8)) * 8);
+      *reinterpret_cast<uint4*>(lds + off) = v[i];
+    }
+  }
+
+  // MFMA fragment of rows r0 .. r0+31 (r0 a multiple of 32), k-step ks: lane
+  // l holds row r0 + l % 32 and k = 16 ks + 8 (l / 32) + 0..7
+  __device__ __forceinline__ static bf16x8_t frag(const char* lds, int r0, int ks, int lane) {
     if constexpr (KC) {
-#pragma unroll
-      for (int i = 0; i < kRegs; ++i) {
-        const int c = tid + kThreads * i;
-        const int r = c >> 3, kc = c & 7;
-        *reinterpret_cast<uint4*>(lds + lds_off(r, kc)) = v[i];
-      }
+      return *reinterpret_cast<const bf16x8_t*>(lds + lds_off_k(r0 + (lane & 31), ks * 2 + (lane >> 5)));
     } else {
-      if (tid < R) {
-        const int rb = tid % (R / 8), kb = tid / (R / 8);
-        // v[j] holds k = kb*8 + j for rows rb*8 .. rb*8+7 (two rows per dword)
-#pragma unroll
-        for (int rr = 0; rr < 8; ++rr) {
-          const int d = rr >> 1;
-          uint32_t w[4];
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const uint32_t a = reinterpret_cast<const uint32_t*>(&v[2 * q])[d];
-            const uint32_t b = reinterpret_cast<const uint32_t*>(&v[2 * q + 1])[d];
-            w[q] = (rr & 1) ? ((a >> 16) | (b & 0xffff0000u)) : ((a & 0xffffu) | (b << 16));
-          }
-          *reinterpret_cast<uint4*>(lds + lds_off(rb * 8 + rr, kb)) = make_uint4(w[0], w[1], w[2], w[3]);
-        }
-      }
+      const int g = lane >> 4, m = lane & 15;
+      const int i = r0 + 16 * (g & 1) + 4 * (m & 3);
+      const int k = ks * 16 + 8 * (g >> 1) + (m >> 2);
+      const v4s_t a = ds_read_tr(lds, lds_off_mn<R>(k, i));
+      const v4s_t b = ds_read_tr(lds, lds_off_mn<R>(k + 4, i));
+      bf16x8_t f;
+      f[0] = a[0]; f[1] = a[1]; f[2] = a[2]; f[3] = a[3];
+      f[4] = b[0]; f[5] = b[1]; f[6] = b[2]; f[7] = b[3];
+      return f;
     }
   }
 };
-
-__device__ __forceinline__ bf16x8_t read_frag(const char* lds, int r, int kc) {
-  return *reinterpret_cast<const bf16x8_t*>(lds + lds_off(r, kc));
-}
 
 // ---------------------------------------------------------------------------
 // epilogues on 4 consecutive columns n .. n+3 of row m
@@ -230,12 +269,114 @@ __device__ __forceinline__ void epi4(const GemmArgs& p, int bi, int m, int n, co
   }
 }
 
+
+// ---------------------------------------------------------------------------
+// K loop: double-buffered LDS stages, fragments double-buffered in registers,
+// and (for interior tiles, GUARD = false) an explicit interleave of MFMAs with
+// the global loads, LDS fragment reads and LDS stores of the same iteration.
+// ---------------------------------------------------------------------------
+template <int BM, int BN, bool AK, bool BKC, bool GUARD>
+__device__ __forceinline__ void mainloop(const GemmArgs& p, const uint16_t* A, const uint16_t* B, int m0, int n0,
+                                         int kt0, int nk, char* smem, int tid,
+                                         f32x16_t (&acc)[Cfg<BM, BN>::TM][Cfg<BM, BN>::TN]) {
+  constexpr int NT = Cfg<BM, BN>::NT;
+  constexpr int WM = Cfg<BM, BN>::WM, WN = Cfg<BM, BN>::WN, TM = Cfg<BM, BN>::TM, TN = Cfg<BM, BN>::TN;
+  using LA = TileLoader<BM, AK, NT>;
+  using LB = TileLoader<BN, BKC, NT>;
+  constexpr int A_BYTES = BM * 128, STAGE = (BM + BN) * 128;
+  constexpr int KS = kBK / 16;
+  constexpr int NM = TM * TN;                                    // MFMAs per k-step
+  constexpr int NV = LA::kRegs + LB::kRegs;  // global loads per tile
+  constexpr int ND = (AK ? 1 : 2) * TM + (BKC ? 1 : 2) * TN;     // LDS reads per k-step
+  const int lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  if (nk <= 0) return;
+
+  LA la;
+  LB lb;
+  if constexpr (GUARD) {
+    la.template load<true>(A, p.lda, m0, p.M, kt0 * kBK, p.K, tid);
+    lb.template load<true>(B, p.ldb, n0, p.N, kt0 * kBK, p.K, tid);
+    la.store(smem, tid);
+    lb.store(smem + A_BYTES, tid);
+  } else {
+    LA::load_direct(A, p.lda, m0, kt0 * kBK, smem, tid);
+    LB::load_direct(B, p.ldb, n0, kt0 * kBK, smem + A_BYTES, tid);
+  }
+  __syncthreads();
+
+  bf16x8_t fa[2][TM], fb[2][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i) fa[0][i] = LA::frag(smem, wm * WM + i * 32, 0, lane);
+#pragma unroll
+  for (int j = 0; j < TN; ++j) fb[0][j] = LB::frag(smem + A_BYTES, wn * WN + j * 32, 0, lane);
+
+  for (int kt = 0; kt < nk; ++kt) {
+    const char* sa = smem + (kt & 1) * STAGE;
+    const char* sb = sa + A_BYTES;
+    char* so = smem + ((kt + 1) & 1) * STAGE;
+    // next tile (the last iteration reloads its own tile: harmless, no branch)
+    const int kn = (kt0 + (kt + 1 < nk ? kt + 1 : kt)) * kBK;
+    if constexpr (GUARD) {
+      la.template load<true>(A, p.lda, m0, p.M, kn, p.K, tid);
+      lb.template load<true>(B, p.ldb, n0, p.N, kn, p.K, tid);
+    } else {
+      // the other stage was last read before the previous barrier
+      LA::load_direct(A, p.lda, m0, kn, so, tid);
+      LB::load_direct(B, p.ldb, n0, kn, so + A_BYTES, tid);
+    }
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const int cur = ks & 1, nxt = cur ^ 1;
+      if (ks + 1 < KS) {
+#pragma unroll
+        for (int i = 0; i < TM; ++i) fa[nxt][i] = LA::frag(sa, wm * WM + i * 32, ks + 1, lane);
+#pragma unroll
+        for (int j = 0; j < TN; ++j) fb[nxt][j] = LB::frag(sb, wn * WN + j * 32, ks + 1, lane);
+      }
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[cur][j], fa[cur][i], acc[i][j], 0, 0, 0);
+      if constexpr (GUARD) {
+        if (ks + 1 == KS) {
+          la.store(so, tid);
+          lb.store(so + A_BYTES, tid);
+        }
+      }
+    }
+    if constexpr (!GUARD) {
+      // k-step 0: MFMAs with the direct loads and the fragment reads of k-step 1;
+      // later k-steps: MFMAs with the next fragment reads
+#pragma unroll
+      for (int x = 0; x < NM; ++x) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if (x < NV) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+        if (x < ND) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+#pragma unroll
+      for (int ks = 1; ks < KS; ++ks)
+#pragma unroll
+        for (int x = 0; x < NM; ++x) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          if (ks + 1 < KS && x < ND) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < TM; ++i) fa[0][i] = LA::frag(so, wm * WM + i * 32, 0, lane);
+#pragma unroll
+    for (int j = 0; j < TN; ++j) fb[0][j] = LB::frag(so + A_BYTES, wn * WN + j * 32, 0, lane);
+  }
+}
+
 // ---------------------------------------------------------------------------
 // the kernel
 // ---------------------------------------------------------------------------
 template <int BM, int BN, bool AK, bool BKC, int EPI>
-__global__ void __launch_bounds__(kThreads, 1) gemm_bf16_kernel(GemmArgs p) {
-  constexpr int WM = BM / 2, WN = BN / 2, TM = WM / 32, TN = WN / 32;
+__global__ void __launch_bounds__((Cfg<BM, BN>::NT), 1) gemm_bf16_kernel(GemmArgs p) {
+  constexpr int WM = Cfg<BM, BN>::WM, WN = Cfg<BM, BN>::WN, TM = Cfg<BM, BN>::TM, TN = Cfg<BM, BN>::TN;
   constexpr int A_BYTES = BM * 128, B_BYTES = BN * 128, STAGE = A_BYTES + B_BYTES;
   __shared__ __attribute__((aligned(16))) char smem[2 * STAGE];
 
@@ -270,45 +411,12 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_bf16_kernel(GemmArgs p) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
-  TileLoader<BM, AK> la;
-  TileLoader<BN, BKC> lb;
-  if (nk > 0) {
-    la.load(A, p.lda, m0, p.M, kt0 * kBK, p.K, tid);
-    lb.load(B, p.ldb, n0, p.N, kt0 * kBK, p.K, tid);
-    la.store(smem, tid);
-    lb.store(smem + A_BYTES, tid);
-  }
-  __syncthreads();
-
+  const bool fast = (m0 + BM <= p.M) && (n0 + BN <= p.N) && (p.K % kBK == 0);
+  if (fast)
+    mainloop<BM, BN, AK, BKC, false>(p, A, B, m0, n0, kt0, nk, smem, tid, acc);
+  else
+    mainloop<BM, BN, AK, BKC, true>(p, A, B, m0, n0, kt0, nk, smem, tid, acc);
   const int lr = lane & 31, lh = lane >> 5;
-  for (int kt = 0; kt < nk; ++kt) {
-    const char* sa = smem + (kt & 1) * STAGE;
-    const char* sb = sa + A_BYTES;
-    const bool more = kt + 1 < nk;
-    if (more) {
-      la.load(A, p.lda, m0, p.M, (kt0 + kt + 1) * kBK, p.K, tid);
-      lb.load(B, p.ldb, n0, p.N, (kt0 + kt + 1) * kBK, p.K, tid);
-    }
-#pragma unroll
-    for (int ks = 0; ks < kBK / 16; ++ks) {
-      bf16x8_t fa[TM], fb[TN];
-#pragma unroll
-      for (int i = 0; i < TM; ++i) fa[i] = read_frag(sa, wm * WM + i * 32 + lr, ks * 2 + lh);
-#pragma unroll
-      for (int j = 0; j < TN; ++j) fb[j] = read_frag(sb, wn * WN + j * 32 + lr, ks * 2 + lh);
-#pragma unroll
-      for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[j], fa[i], acc[i][j], 0, 0, 0);
-    }
-    if (more) {
-      char* nxt = smem + ((kt + 1) & 1) * STAGE;
-      la.store(nxt, tid);
-      lb.store(nxt + A_BYTES, tid);
-    }
-    __syncthreads();
-  }
 
   // ----------------------------- epilogue ---------------------------------
   if constexpr (EPI == EPI_QKV) {
@@ -431,7 +539,7 @@ template <int BM, int BN, bool AK, bool BKC, int EPI>
 int launch_t(const GemmArgs& a, hipStream_t s) {
   const int tiles = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
   dim3 grid(tiles, a.batch * a.k_split);
-  hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, AK, BKC, EPI>), grid, dim3(kThreads), 0, s, a);
+  hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, AK, BKC, EPI>), grid, dim3(Cfg<BM, BN>::NT), 0, s, a);
   GS_LAUNCH_CHECK("gemm_bf16");
   return 0;
 }

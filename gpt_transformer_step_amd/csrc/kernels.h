@@ -39,7 +39,7 @@ int launch_attn_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, lon
                     uint16_t* out, long long ld_out, float* lse, int B, int H, int T, hipStream_t s);
 int launch_attn_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, long long ld_qkv,
                     const uint16_t* out, const uint16_t* dout, long long ld_out, const float* lse,
-                    float* delta, float* dq_acc, uint16_t* dk, uint16_t* dv, long long ld_dkv, int B,
+                    float* delta, float* dq, uint16_t* dk, uint16_t* dv, long long ld_dkv, int B,
                     int H, int T, hipStream_t s);
 
 }  // namespace gs
