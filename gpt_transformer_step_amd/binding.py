@@ -64,6 +64,7 @@ _SIGS = {
     "gpt_profile_enable": [ctypes.c_uint64],
     "gpt_profile_reset": [],
     "gpt_profile_read": [_i32, _P(ctypes.c_double), _P(_i32)],
+    "gpt_probe_mfma": [_i32, _i32, _i32, _vp, _P(ctypes.c_double), _vp],
 }
 
 EXPORTED = ["gpt_status_string", "gpt_last_error", "gpt_abi_version", "gpt_profile_num_categories",
@@ -224,3 +225,10 @@ def profile_read(cat):
     t, n = ctypes.c_double(), _i32()
     _call("gpt_profile_read", cat, ctypes.byref(t), ctypes.byref(n))
     return t.value, n.value
+
+
+def probe_mfma(fp8, blocks, iters, out, stream=None):
+    """Launch the matrix-core-only probe; returns the FLOPs of the launch."""
+    f = ctypes.c_double()
+    _call("gpt_probe_mfma", int(fp8), blocks, iters, _ptr(out), ctypes.byref(f), _stream(stream))
+    return f.value

@@ -291,6 +291,8 @@ inline int ce_nparts(const Dims& D) {
   return ((D.V + bn - 1) / bn) * 2;
 }
 
+inline size_t wgrad_part_elems(int M, int N, int K);
+
 struct Layer {
   size_t h1, r1, qkv, rq, rk, att, lse, h2, r2, act;
 };
@@ -299,7 +301,7 @@ struct WS {
   size_t cs, x, hf, rf, part, zt, lse, row_loss;
   std::vector<Layer> layer;
   // backward scratch
-  size_t g, g_bf, dh, du, dout, delta, dq_acc, dqkv, dz;
+  size_t g, g_bf, dh, du, dout, delta, dq_acc, dqkv, dz, wpart;
   size_t total;
 };
 
@@ -339,6 +341,16 @@ WS ws_layout(const Dims& D) {
   w.dq_acc = take(N * d * 4);
   w.dqkv = take(N * 3 * d * 2);
   w.dz = take(N * (size_t)vocab_chunk(D) * 2);
+  {
+    const int Nt = (int)D.N, dd = D.d, hd = D.hidden;
+    size_t mx = 0;
+    mx = std::max(mx, wgrad_part_elems(3 * dd, dd, Nt));
+    mx = std::max(mx, wgrad_part_elems(dd, dd, Nt));
+    mx = std::max(mx, wgrad_part_elems(hd, dd, Nt));
+    mx = std::max(mx, wgrad_part_elems(dd, hd, Nt));
+    mx = std::max(mx, wgrad_part_elems(vocab_chunk(D), dd, Nt));
+    w.wpart = take(std::max<size_t>(mx, 1) * 4);
+  }
   w.total = o;
   return w;
 }
@@ -346,40 +358,40 @@ WS ws_layout(const Dims& D) {
 template <class T>
 inline T* at(void* ws, size_t off) { return reinterpret_cast<T*>(reinterpret_cast<char*>(ws) + off); }
 
-// k-splits for a weight-gradient product with a small output and long K
+// k-splits for a weight-gradient product (small output, long K): enough
+// workgroups to fill the chip; each split writes a partial that a small
+// reduction adds up (no atomics, deterministic)
 inline int wgrad_splits(int M, int N, int K) {
   const long long t256 = (long long)((M + 255) / 256) * ((N + 255) / 256);
-  if (t256 >= 512) return 1;
+  if (t256 >= 256) return 1;
   long long ks = (512 + t256 - 1) / t256;
-  ks = std::min<long long>(ks, std::max(1, K / 1024));
-  ks = std::min<long long>(ks, 32);
+  ks = std::min<long long>(ks, std::max(1, K / 2048));
+  ks = std::min<long long>(ks, 16);
   return (int)std::max<long long>(ks, 1);
 }
 
-// C[M,N] (f32, ld ldc) (+)= A^T B with A stored [K][M], B stored [K][N] (bf16)
-int wgrad(const void* A, long long lda, const void* B, long long ldb, float* C, long long ldc, int M, int N,
-          int K, bool accumulate, hipStream_t s) {
+inline size_t wgrad_part_elems(int M, int N, int K) {
+  const int ks = wgrad_splits(M, N, K);
+  return ks > 1 ? (size_t)ks * M * N : 0;
+}
+
+// C[M,N] (f32, dense, ld N) (+)= A^T B with A stored [K][M], B stored [K][N] (bf16)
+int wgrad(const void* A, long long lda, const void* B, long long ldb, float* C, int M, int N, int K,
+          bool accumulate, float* part, hipStream_t s) {
   GemmArgs a;
   a.M = M; a.N = N; a.K = K;
   a.A = A; a.lda = lda; a.a_kcontig = 0;
   a.B = B; a.ldb = ldb; a.b_kcontig = 0;
-  a.C = C; a.ldc = ldc;
   const int ks = wgrad_splits(M, N, K);
   if (ks == 1) {
+    a.C = C; a.ldc = N;
     a.beta = accumulate ? 1.f : 0.f;
     return gemm_bf16(a, EPI_F32, s);
   }
-  if (!accumulate) {
-    if (ldc == N) {
-      int rc = launch_fill_f32(C, (long long)M * N, 0.f, s);
-      if (rc) return rc;
-    } else {
-      set_error("wgrad: split-K needs a dense output");
-      return -1;
-    }
-  }
-  a.k_split = ks;
-  return gemm_bf16(a, EPI_F32_ATOMIC, s);
+  a.C = part; a.ldc = N; a.k_split = ks; a.split_stride = (long long)M * N; a.beta = 0.f;
+  int rc = gemm_bf16(a, EPI_F32, s);
+  if (rc) return rc;
+  return launch_splitk_reduce(part, ks, (long long)M * N, C, nullptr, (long long)M * N, accumulate ? 1.f : 0.f, s);
 }
 
 }  // namespace
@@ -552,6 +564,7 @@ extern "C" gpt_status gpt_step_bwd(const gpt_shape* shape, const gpt_params* par
   uint16_t* dqkv = at<uint16_t>(ws, w.dqkv);
   float* dq_acc = at<float>(ws, w.dq_acc);
   uint16_t* dz = at<uint16_t>(ws, w.dz);
+  float* wpart = at<float>(ws, w.wpart);
   const float* cs = at<float>(ws, w.cs);
 
   // fused head + cross-entropy backward, one vocabulary chunk at a time
@@ -577,7 +590,7 @@ extern "C" gpt_status gpt_step_bwd(const gpt_shape* shape, const gpt_params* par
       TRY(gemm_bf16(a, EPI_F32, s));
     }
     // dW_lm[chunk] (+)= dz^T hf
-    { ProfScope ps_(P_CE_DW, s); TRY(wgrad(dz, vc, hf, d, G + P.lm_head + (size_t)c0 * d, d, nv, d, N, acc, s)); }
+    { ProfScope ps_(P_CE_DW, s); TRY(wgrad(dz, vc, hf, d, G + P.lm_head + (size_t)c0 * d, nv, d, N, acc, wpart, s)); }
   }
   { ProfScope ps_(P_FILL, s); TRY(launch_fill_f32(g, (long long)N * d, 0.f, s)); }
   { ProfScope ps_(P_RMSNORM_BWD, s); TRY(launch_rmsnorm_bwd(dh, hf, at<float>(ws, w.rf), g, g_bf, N, d, s)); }
@@ -598,7 +611,7 @@ extern "C" gpt_status gpt_step_bwd(const gpt_shape* shape, const gpt_params* par
       a.C = du; a.ldc = hid; a.aux = act; a.ldaux = hid;
       TRY(gemm_bf16(a, EPI_DRELU2, s));
     }
-    { ProfScope ps_(P_PROJ_WGRAD, s); TRY(wgrad(g_bf, d, act, hid, G + P.proj(D, l), hid, d, hid, N, acc, s)); }  // dWproj = g^T act
+    { ProfScope ps_(P_PROJ_WGRAD, s); TRY(wgrad(g_bf, d, act, hid, G + P.proj(D, l), d, hid, N, acc, wpart, s)); }  // dWproj = g^T act
     {
       GemmArgs a;  // dh = du Wfc
       ProfScope ps_(P_FC_DGRAD, s);
@@ -607,7 +620,7 @@ extern "C" gpt_status gpt_step_bwd(const gpt_shape* shape, const gpt_params* par
       a.C = dh; a.ldc = d;
       TRY(gemm_bf16(a, EPI_F32, s));
     }
-    { ProfScope ps_(P_FC_WGRAD, s); TRY(wgrad(du, hid, h2, d, G + P.fc(D, l), d, hid, d, N, acc, s)); }  // dWfc = du^T h2
+    { ProfScope ps_(P_FC_WGRAD, s); TRY(wgrad(du, hid, h2, d, G + P.fc(D, l), hid, d, N, acc, wpart, s)); }  // dWfc = du^T h2
     { ProfScope ps_(P_RMSNORM_BWD, s); TRY(launch_rmsnorm_bwd(dh, h2, at<float>(ws, L.r2), g, g_bf, N, d, s)); }
     // ---- attention ----
     {
@@ -618,7 +631,7 @@ extern "C" gpt_status gpt_step_bwd(const gpt_shape* shape, const gpt_params* par
       a.C = dout; a.ldc = d;
       TRY(gemm_bf16(a, EPI_BF16, s));
     }
-    { ProfScope ps_(P_O_WGRAD, s); TRY(wgrad(g_bf, d, att, d, G + P.wo(D, l), d, d, d, N, acc, s)); }  // dWo = g^T att
+    { ProfScope ps_(P_O_WGRAD, s); TRY(wgrad(g_bf, d, att, d, G + P.wo(D, l), d, d, N, acc, wpart, s)); }  // dWo = g^T att
     { ProfScope ps_(P_ATTN_BWD, s); TRY(launch_attn_bwd(qkv, qkv + d, qkv + 2 * d, 3 * d, att, dout, d, at<float>(ws, L.lse),
                         at<float>(ws, w.delta), dq_acc, dqkv + d, dqkv + 2 * d, 3 * d, D.B, D.H, D.T, s)); }
     { ProfScope ps_(P_ROPE_BWD, s); TRY(launch_rope_qknorm_bwd(dq_acc, dqkv, qkv, at<float>(ws, L.rq), at<float>(ws, L.rk), cs, N, D.T, D.H, s)); }
@@ -630,7 +643,7 @@ extern "C" gpt_status gpt_step_bwd(const gpt_shape* shape, const gpt_params* par
       a.C = dh; a.ldc = d;
       TRY(gemm_bf16(a, EPI_F32, s));
     }
-    { ProfScope ps_(P_QKV_WGRAD, s); TRY(wgrad(dqkv, 3 * d, h1, d, G + P.qkv(D, l), d, 3 * d, d, N, acc, s)); }  // dWqkv = dqkv^T h1
+    { ProfScope ps_(P_QKV_WGRAD, s); TRY(wgrad(dqkv, 3 * d, h1, d, G + P.qkv(D, l), 3 * d, d, N, acc, wpart, s)); }  // dWqkv = dqkv^T h1
     { ProfScope ps_(P_RMSNORM_BWD, s); TRY(launch_rmsnorm_bwd(dh, h1, at<float>(ws, L.r1), g, g_bf, N, d, s)); }
   }
   if (!acc) { ProfScope ps_(P_FILL, s); TRY(launch_fill_f32(G + P.wte, (long long)D.V * d, 0.f, s)); }
@@ -646,8 +659,16 @@ namespace {
 constexpr int kFrobBlocks = 64;
 
 struct MuonWS {
-  size_t partial, X, Xb0, Xb1, A, Ab, Bb, total;
+  size_t partial, X, Xb0, Xb1, A, Ab, Bb, gpart, total;
 };
+
+// k-splits of the Gram products X^T X (a few output tiles, long K)
+inline int gram_splits(int count, int rows, int cols) {
+  const int lrow = std::max(rows, cols), sm = std::min(rows, cols);
+  const long long tiles = (long long)count * ((sm + 127) / 128) * ((sm + 127) / 128);
+  if (tiles >= 512) return 1;
+  return (int)std::max<long long>(1, std::min<long long>(std::max(1, lrow / 1024), (512 + tiles - 1) / tiles));
+}
 
 MuonWS muon_layout(int count, int rows, int cols) {
   MuonWS m;
@@ -662,6 +683,8 @@ MuonWS muon_layout(int count, int rows, int cols) {
   m.A = take((size_t)count * sm * sm * 4);
   m.Ab = take((size_t)count * sm * sm * 2);
   m.Bb = take((size_t)count * sm * sm * 2);
+  const int gs_ = gram_splits(count, rows, cols);
+  m.gpart = take(gs_ > 1 ? (size_t)gs_ * count * sm * sm * 4 : 4);
   m.total = o;
   return m;
 }
@@ -717,10 +740,8 @@ extern "C" gpt_status muon_update(float* Wt, uint16_t* W_bf16, const float* Gm, 
   { ProfScope ps_(P_MUON_ELEMWISE, s); TRY(launch_ns_init(src, partial, kFrobBlocks, X, Xb[0], count, rows, cols, 1e-7f, s)); }
 
   const long long sX = (long long)lrow * sm, sA = (long long)sm * sm;
-  // Gram products need split-K when the batch has few output tiles
-  const long long gram_tiles = (long long)count * ((sm + 127) / 128) * ((sm + 127) / 128);
-  const int gram_split = gram_tiles >= 512 ? 1 : (int)std::min<long long>(std::max(1, lrow / 1024),
-                                                                            (512 + gram_tiles - 1) / gram_tiles);
+  const int gram_split = gram_splits(count, rows, cols);
+  float* gpart = at<float>(ws, m.gpart);
   int cur = 0;
   for (int it = 0; it < ns_steps; ++it) {
     const float ca = coeffs[3 * it], cb = coeffs[3 * it + 1], cc = coeffs[3 * it + 2];
@@ -734,10 +755,10 @@ extern "C" gpt_status muon_update(float* Wt, uint16_t* W_bf16, const float* Gm, 
       if (gram_split <= 1) {
         TRY(gemm_bf16(a, EPI_F32_BF16, s));
       } else {
-        TRY(launch_fill_f32(A, sA * count, 0.f, s));
-        a.k_split = gram_split;
-        TRY(gemm_bf16(a, EPI_F32_ATOMIC, s));
-        TRY(launch_cast_bf16(A, Ab, sA * count, s));
+        // split-K partials [split][count][sm][sm], then A = sum, Ab = bf16(A)
+        a.C = gpart; a.sC = sA; a.k_split = gram_split; a.split_stride = sA * count;
+        TRY(gemm_bf16(a, EPI_F32, s));
+        TRY(launch_splitk_reduce(gpart, gram_split, sA * count, A, Ab, sA * count, 0.f, s));
       }
     }
     {
@@ -800,5 +821,15 @@ extern "C" gpt_status gpt_op_attention_bwd(int32_t batch, int32_t n_head, int32_
     FAIL(GPT_ERR_INVALID_ARG, "misaligned");
   TRY(launch_attn_bwd(q, k, v, ld_qkv, out, dout, ld_out, lse, delta, dq_acc, dk, dv, ld_dkv, batch, n_head,
                       seq_len, S(stream)));
+  return GPT_OK;
+}
+
+// ---------------------------------------------------------------------------
+// roofline probe
+// ---------------------------------------------------------------------------
+extern "C" gpt_status gpt_probe_mfma(int32_t fp8, int32_t blocks, int32_t iters, float* out, double* flops,
+                                     gpt_stream_t stream) {
+  if (blocks < 1 || iters < 1 || !out || !flops) FAIL(GPT_ERR_INVALID_ARG, "bad probe arguments");
+  TRY(launch_mfma_peak(fp8 ? 1 : 0, blocks, iters, out, flops, S(stream)));
   return GPT_OK;
 }

@@ -237,6 +237,32 @@ __global__ void loss_mean_kernel(const float* __restrict__ row_loss, float* __re
   }
 }
 
+// out = beta * out + sum of nsplit partials (stride elements apart); optional bf16 copy
+__global__ void splitk_reduce_kernel(const float* __restrict__ part, int nsplit, long long stride,
+                                     float* __restrict__ out, uint16_t* __restrict__ out_bf, long long n, float beta) {
+  long long i = ((long long)blockIdx.x * blockDim.x + threadIdx.x) * 4;
+  const long long step = (long long)gridDim.x * blockDim.x * 4;
+  for (; i < n; i += step) {
+    if (i + 3 < n) {
+      float4 acc = beta != 0.f ? *reinterpret_cast<const float4*>(out + i) : make_float4(0.f, 0.f, 0.f, 0.f);
+      if (beta != 0.f && beta != 1.f) { acc.x *= beta; acc.y *= beta; acc.z *= beta; acc.w *= beta; }
+      for (int sp = 0; sp < nsplit; ++sp) {
+        const float4 v = *reinterpret_cast<const float4*>(part + sp * stride + i);
+        acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
+      }
+      *reinterpret_cast<float4*>(out + i) = acc;
+      if (out_bf) *reinterpret_cast<uint2*>(out_bf + i) = make_uint2(pack_bf2(acc.x, acc.y), pack_bf2(acc.z, acc.w));
+    } else {
+      for (long long j = i; j < n; ++j) {
+        float a = beta != 0.f ? beta * out[j] : 0.f;
+        for (int sp = 0; sp < nsplit; ++sp) a += part[sp * stride + j];
+        out[j] = a;
+        if (out_bf) out_bf[j] = f2bf(a);
+      }
+    }
+  }
+}
+
 // ---------------------------- Muon elementwise ------------------------------
 __global__ void muon_momentum_kernel(float* __restrict__ M, const float* __restrict__ G, long long n, float mu) {
   long long i = ((long long)blockIdx.x * blockDim.x + threadIdx.x) * 4;
@@ -425,6 +451,15 @@ int launch_ce_reduce(const float* part, int nparts, const float* zt, float* lse,
 int launch_loss_mean(const float* row_loss, float* loss, long long N, hipStream_t s) {
   hipLaunchKernelGGL(loss_mean_kernel, dim3(1), dim3(1024), 0, s, row_loss, loss, N);
   GS_LAUNCH_CHECK("loss_mean");
+  return 0;
+}
+
+int launch_splitk_reduce(const float* part, int nsplit, long long stride, float* out, uint16_t* out_bf, long long n,
+                         float beta, hipStream_t s) {
+  if (n <= 0) return 0;
+  const int blocks = (int)std::min<long long>(nblocks(n, 1024), 8192);
+  hipLaunchKernelGGL(splitk_reduce_kernel, dim3(blocks), dim3(256), 0, s, part, nsplit, stride, out, out_bf, n, beta);
+  GS_LAUNCH_CHECK("splitk_reduce");
   return 0;
 }
 

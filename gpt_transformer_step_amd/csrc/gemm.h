@@ -42,7 +42,8 @@ struct GemmArgs {
   float* part = nullptr;         // CE partials: float2 [M, nparts]
   int nparts = 0;
   float* zt = nullptr;           // CE target logit [M]
-  int k_split = 1;               // > 1 only with EPI_F32_ATOMIC
+  int k_split = 1;               // > 1: EPI_F32_ATOMIC, or EPI_F32 writing one partial per split
+  long long split_stride = 0;    // EPI_F32 with k_split > 1: split s writes C + s * split_stride
   const float* rope = nullptr;    // EPI_QKV: cos [row_T, 64] then sin [row_T, 64]
   int n_head = 0;                 // EPI_QKV: heads per q (and k) block
   const float* scale_a = nullptr;  // fp8: device scalars; v *= 1 / (scale_a * scale_b)

@@ -174,10 +174,10 @@ struct TileLoader {
 // epilogues on 4 consecutive columns n .. n+3 of row m
 // ---------------------------------------------------------------------------
 template <int EPI>
-__device__ __forceinline__ void epi4(const GemmArgs& p, int bi, int m, int n, const float* v) {
+__device__ __forceinline__ void epi4(const GemmArgs& p, int bi, int m, int n, const float* v, long long coff) {
   const bool full = (n + 3 < p.N);
   if constexpr (EPI == EPI_F32 || EPI == EPI_RESID || EPI == EPI_F32_ATOMIC) {
-    float* C = reinterpret_cast<float*>(p.C) + (long long)bi * p.sC + (long long)m * p.ldc + n;
+    float* C = reinterpret_cast<float*>(p.C) + (long long)bi * p.sC + coff + (long long)m * p.ldc + n;
     if (EPI == EPI_F32_ATOMIC) {
 #pragma unroll
       for (int j = 0; j < 4; ++j)
@@ -516,6 +516,8 @@ __global__ void __launch_bounds__((Cfg<BM, BN>::NT), 1) gemm_bf16_kernel(GemmArg
       }
     }
   } else {
+    // split-K partials: split s writes its own slice of C (reduced afterwards)
+    const long long coff = (EPI == EPI_F32 && p.k_split > 1) ? (long long)split * p.split_stride : 0;
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
       const int m = m0 + wm * WM + i * 32 + lr;
@@ -529,7 +531,7 @@ __global__ void __launch_bounds__((Cfg<BM, BN>::NT), 1) gemm_bf16_kernel(GemmArg
           float v[4];
 #pragma unroll
           for (int r = 0; r < 4; ++r) v[r] = acc[i][j][4 * g + r] * p.alpha;
-          epi4<EPI>(p, bi, m, n, v);
+          epi4<EPI>(p, bi, m, n, v, coff);
         }
     }
   }

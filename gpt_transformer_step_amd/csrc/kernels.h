@@ -22,6 +22,9 @@ int launch_rope_qknorm_bwd(const float* dq_acc, uint16_t* dqkv, const uint16_t* 
 int launch_ce_reduce(const float* part, int nparts, const float* zt, float* lse, float* row_loss,
                      float* lse_out, long long N, hipStream_t s);
 int launch_loss_mean(const float* row_loss, float* loss, long long N, hipStream_t s);
+// out[0..n) = beta * out + sum_{s < nsplit} part[s * stride + i]; optional bf16 copy out_bf
+int launch_splitk_reduce(const float* part, int nsplit, long long stride, float* out, uint16_t* out_bf, long long n,
+                         float beta, hipStream_t s);
 
 // --- Muon elementwise (elementwise.hip) ------------------------------------
 int launch_muon_momentum(float* M, const float* G, long long n, float mu, hipStream_t s);
@@ -41,5 +44,8 @@ int launch_attn_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, lon
                     const uint16_t* out, const uint16_t* dout, long long ld_out, const float* lse,
                     float* delta, float* dq, uint16_t* dk, uint16_t* dv, long long ld_dkv, int B,
                     int H, int T, hipStream_t s);
+
+// --- roofline probes (probe.hip) -------------------------------------------
+int launch_mfma_peak(int fp8, int blocks, int iters, float* out, double* flops, hipStream_t s);
 
 }  // namespace gs

@@ -46,7 +46,7 @@ gpt_status gpt_op_attention_fwd(int32_t batch, int32_t n_head, int32_t seq_len, 
                                 uint16_t* out, int64_t ld_out, float* lse, gpt_stream_t stream);
 
 /* Backward of gpt_op_attention_fwd given dout (same layout as out):
- *   dq_acc fp32, element (b,t,h,e) at dq_acc[(b*T+t) * H*128 + h*128 + e] (overwritten);
+ *   dq_acc fp32, element (b,t,h,e) at dq_acc[(b*T+t) * H*128 + h*128 + e] (written);
  *   dk, dv bf16 in the q/k/v layout with leading dimension ld_dkv;
  *   delta: fp32 scratch [B, H, T] (receives rowsum(dout * out)). */
 gpt_status gpt_op_attention_bwd(int32_t batch, int32_t n_head, int32_t seq_len, const uint16_t* q,
@@ -79,6 +79,14 @@ const char* gpt_profile_category_name(int32_t category);
 gpt_status gpt_profile_enable(uint64_t mask);
 gpt_status gpt_profile_reset(void);
 gpt_status gpt_profile_read(int32_t category, double* total_ms /* host */, int32_t* launches /* host */);
+
+/* Roofline probe: a matrix-core-only kernel (no memory traffic) with
+ * `blocks` workgroups of 4 waves, each issuing iters x 8 independent MFMAs
+ * (fp8 = 0: v_mfma_f32_32x32x16_bf16; fp8 = 1: the 32x32x64 E4M3 MFMA).
+ * `out` (device, fp32 [blocks*256]) receives a checksum; *flops (host) the
+ * FLOPs the launch performs.  Time it with events to get the sustained rate. */
+gpt_status gpt_probe_mfma(int32_t fp8, int32_t blocks, int32_t iters, float* out, double* flops /* host */,
+                          gpt_stream_t stream);
 
 #ifdef __cplusplus
 }
