@@ -423,18 +423,17 @@ __global__ void __launch_bounds__((Cfg<BM, BN>::NT), 1) gemm_bf16_kernel(GemmArg
     // Each wave owns 128 columns = one head (tiles are 256 wide).  Lane row m
     // holds head features e = j*32 + 8g + 4lh + r; the rotation partner
     // e + 64 sits in the same lane at j + 2, the other half of the head in
-    // lane ^ 32.
+    // lane ^ 32.  The rotated, normalised values replace the accumulators and
+    // are stored by the coalesced path below.
     static_assert(WN == 128, "EPI_QKV needs 128 columns per wave");
-    const int nb = n0 + wn * WN;        // first column of this wave's head
+    const int nb = n0 + wn * WN;  // first column of this wave's head
     const int dmodel = p.n_head * 128;
-    const bool is_qk = nb < 2 * dmodel;
+    if (nb < 2 * dmodel) {        // q or k head (wave-uniform)
 #pragma unroll
-    for (int i = 0; i < TM; ++i) {
-      const int m = m0 + wm * WM + i * 32 + lr;
-      float y[TN][16];
-      float ss = 0.f;
-      const int t = (m < p.M) ? m % p.row_T : 0;
-      if (is_qk) {
+      for (int i = 0; i < TM; ++i) {
+        const int m = m0 + wm * WM + i * 32 + lr;
+        const int t = (m < p.M) ? m % p.row_T : 0;
+        float ss = 0.f;
 #pragma unroll
         for (int j = 0; j < 2; ++j)
 #pragma unroll
@@ -445,10 +444,10 @@ __global__ void __launch_bounds__((Cfg<BM, BN>::NT), 1) gemm_bf16_kernel(GemmArg
             const float cc[4] = {c4.x, c4.y, c4.z, c4.w}, sn[4] = {s4.x, s4.y, s4.z, s4.w};
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-              const float x1 = acc[i][j][4 * g + r] * p.alpha, x2 = acc[i][j + 2][4 * g + r] * p.alpha;
+              const float x1 = acc[i][j][4 * g + r], x2 = acc[i][j + 2][4 * g + r];
               const float y1 = x1 * cc[r] - x2 * sn[r], y2 = x1 * sn[r] + x2 * cc[r];
-              y[j][4 * g + r] = y1;
-              y[j + 2][4 * g + r] = y2;
+              acc[i][j][4 * g + r] = y1;
+              acc[i][j + 2][4 * g + r] = y2;
               ss += y1 * y1 + y2 * y2;
             }
           }
@@ -457,30 +456,16 @@ __global__ void __launch_bounds__((Cfg<BM, BN>::NT), 1) gemm_bf16_kernel(GemmArg
 #pragma unroll
         for (int j = 0; j < TN; ++j)
 #pragma unroll
-          for (int e = 0; e < 16; ++e) y[j][e] *= rr;
+          for (int e = 0; e < 16; ++e) acc[i][j][e] *= rr;
         if (lh == 0 && m < p.M) {
           const int head = (nb % dmodel) / 128;
           float* rdst = (nb < dmodel) ? p.part : p.zt;
           rdst[(long long)m * p.n_head + head] = rr;
         }
-      } else {
-#pragma unroll
-        for (int j = 0; j < TN; ++j)
-#pragma unroll
-          for (int e = 0; e < 16; ++e) y[j][e] = acc[i][j][e] * p.alpha;
       }
-      if (m >= p.M || nb >= p.N) continue;
-      uint16_t* crow = reinterpret_cast<uint16_t*>(p.C) + (long long)m * p.ldc + nb;
-#pragma unroll
-      for (int j = 0; j < TN; ++j)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int e = j * 32 + 8 * g + 4 * lh;
-          *reinterpret_cast<uint2*>(crow + e) = make_uint2(pack_bf2(y[j][4 * g], y[j][4 * g + 1]),
-                                                           pack_bf2(y[j][4 * g + 2], y[j][4 * g + 3]));
-        }
     }
-  } else if constexpr (EPI == EPI_CE_FWD) {
+  }
+  if constexpr (EPI == EPI_CE_FWD) {
     // Per row: max and sum of exp over this wave's WN columns, merged with
     // the partner lane (lane ^ 32) that holds the other half of the columns.
 #pragma unroll
@@ -518,21 +503,45 @@ __global__ void __launch_bounds__((Cfg<BM, BN>::NT), 1) gemm_bf16_kernel(GemmArg
   } else {
     // split-K partials: split s writes its own slice of C (reduced afterwards)
     const long long coff = (EPI == EPI_F32 && p.k_split > 1) ? (long long)split * p.split_stride : 0;
+    // Coalesced epilogue: each wave stages its accumulators, 32 rows at a
+    // time, in its own LDS region (16-byte chunks XOR-swizzled by row, so
+    // both the row-per-lane writes and the row-contiguous reads are
+    // conflict free), then applies the epilogue on 4-column chunks laid out
+    // along rows: consecutive lanes touch consecutive 16-byte pieces of a row.
+    constexpr int ROWB = WN * 4;                 // bytes per staged row
+    constexpr int CH = WN / 4;                   // 16-byte chunks per row
+    static_assert(32 * ROWB * (Cfg<BM, BN>::NT / 64) <= 2 * STAGE, "epilogue staging exceeds LDS");
+    char* wbuf = smem + wave * 32 * ROWB;
+    __syncthreads();  // every wave is done with the operand tiles
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
-      const int m = m0 + wm * WM + i * 32 + lr;
-      if (m >= p.M) continue;
 #pragma unroll
       for (int j = 0; j < TN; ++j)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-          const int n = n0 + wn * WN + j * 32 + 8 * g + 4 * lh;
-          if (n >= p.N) continue;
-          float v[4];
-#pragma unroll
-          for (int r = 0; r < 4; ++r) v[r] = acc[i][j][4 * g + r] * p.alpha;
-          epi4<EPI>(p, bi, m, n, v, coff);
+          const int cc = (j * 32 + 8 * g + 4 * lh) >> 2;
+          *reinterpret_cast<float4*>(wbuf + lr * ROWB + ((cc ^ (lr & 15)) << 4)) =
+              make_float4(acc[i][j][4 * g] * p.alpha, acc[i][j][4 * g + 1] * p.alpha,
+                          acc[i][j][4 * g + 2] * p.alpha, acc[i][j][4 * g + 3] * p.alpha);
         }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll 4
+      for (int it = 0; it < 32 * CH / 64; ++it) {
+        const int q = it * 64 + lane;
+        const int rr = q / CH, cc = q % CH;
+        const float4 v4 = *reinterpret_cast<const float4*>(wbuf + rr * ROWB + ((cc ^ (rr & 15)) << 4));
+        const int m = m0 + wm * WM + i * 32 + rr;
+        const int n = n0 + wn * WN + cc * 4;
+        if (m < p.M && n < p.N) {
+          const float v[4] = {v4.x, v4.y, v4.z, v4.w};
+          epi4<(EPI == EPI_QKV ? (int)EPI_BF16 : EPI)>(p, bi, m, n, v, coff);
+        }
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     }
   }
 }
