@@ -4,7 +4,7 @@ Test infrastructure only.  The precision passage of the pages (apidog.com/pt
 "Gerenciamento de Precisão"; apidog.com/de "Präzisionsverwaltung"; dev.to
 "3. Gestión de Precisión") turns most linear layers into fp8 layers with one
 scale per tensor; the habrGPT news page (news.hamidun.com, "Fp8 frente a
-bf16") compares that format with bf16.  Readings (the design doc lists them):
+bf16") compares that format with bf16.  Readings:
   * formats are the OCP ones: E4M3 (bias 7, no infinities, largest finite 448)
     for activations and weights, E5M2 (bias 15, largest finite 57344) for
     output gradients;

@@ -13,7 +13,7 @@ same list in apidog.com/pt "Modelo GPT"):
   * causal attention through ``flash_attn_func(q, k, v, causal=True, ...)``
     (section "5. Unificación Flash Attention");
   * vocabulary of 32,768 tokens (section "Lo que nanochat cubre").
-Readings taken where the pages are silent (each listed in the design doc):
+Readings taken where the pages are silent:
   * pre-norm RMSNorm without gain, eps 1e-6 inside the square root, also
     used for the 128-wide QK normalisation; a final norm before the head;
   * RoPE base 10000, rotate-half pairing (i, i + hd/2), angle t * base^(-2i/hd),

@@ -8,7 +8,7 @@ orthogonalisation by a Newton-Schulz iteration with Polar-Express
 coefficients, five iterations); each iteration takes a coefficient triple
 (a, b, c) and computes A = X^T X, B = b A + c A A, X = a X + X B.
 
-Readings taken (the design doc lists them):
+Readings taken:
   * momentum M <- mu M + G with M = 0 before the first step, no Nesterov term;
   * X0 = M / (||M||_F + 1e-7); the loop runs on the orientation with
     rows >= cols (X^T X is the small Gram matrix) and the result is
