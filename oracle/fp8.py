@@ -69,8 +69,9 @@ def encode(x, fmt):
     dhi = table[hi] - ax
     pick_hi = (dhi < dlo) | ((dhi == dlo) & (hi % 2 == 0))
     idx = np.where(pick_hi, hi, lo)
-    neg = np.signbit(x) & (idx > 0)
-    return (idx | np.where(neg, 0x80, 0)).astype(np.uint8)
+    # the sign bit is kept, also when the magnitude rounds to zero (IEEE-754
+    # rounding gives -0 for a negative value below half the smallest step)
+    return (idx | np.where(np.signbit(x), 0x80, 0)).astype(np.uint8)
 
 
 def tensor_scale(t, fmt):

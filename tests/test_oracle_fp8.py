@@ -12,10 +12,8 @@ def test_every_finite_code_roundtrips(fmt):
     vals = fp8.decode(codes, fmt)
     fin = np.isfinite(vals)
     back = fp8.encode(vals[fin], fmt)
-    # -0.0 encodes to +0 (code 0); every other finite code is its own image
-    same = back == codes[fin]
-    zero_neg = (codes[fin] == 0x80)
-    assert np.all(same | zero_neg)
+    # every finite code is its own image (-0.0 included)
+    assert np.array_equal(back, codes[fin])
 
 
 def test_format_constants():
@@ -51,6 +49,12 @@ def test_against_torch_casts(fmt, tdt):
     ours = fp8.decode(fp8.encode(x, fmt), fmt)
     ref = torch.tensor(x).to(getattr(torch, tdt)).to(torch.float64).numpy()
     assert np.array_equal(ours, ref)
+    # the codes themselves, including the sign of values that round to zero
+    tiny = np.array([-1e-6, 1e-6, -0.0, 0.0, -fp8.decode(np.uint8(1), fmt) * 0.49], np.float32)
+    codes = fp8.encode(np.concatenate([x, tiny]), fmt)
+    ref_codes = torch.tensor(np.concatenate([x, tiny])).to(getattr(torch, tdt)).view(torch.uint8).numpy()
+    assert np.array_equal(codes, ref_codes)
+    assert list(codes[-5:]) == [0x80, 0, 0x80, 0, 0x80]
 
 
 def test_fake_quant_scale():
