@@ -22,6 +22,7 @@ _lib = ctypes.CDLL(LIB_PATH)
 PREC_BF16, PREC_FP8 = 0, 1
 LAYOUT_K, LAYOUT_MN = 0, 1
 DTYPE_F32, DTYPE_BF16 = 0, 1
+FP8_E4M3, FP8_E5M2 = 0, 1
 
 STATUS = {0: "ok", -1: "invalid argument", -2: "invalid shape", -3: "workspace too small",
           -4: "HIP runtime error", -5: "unsupported"}
@@ -65,10 +66,12 @@ _SIGS = {
     "gpt_profile_reset": [],
     "gpt_profile_read": [_i32, _P(ctypes.c_double), _P(_i32)],
     "gpt_probe_mfma": [_i32, _i32, _i32, _vp, _P(ctypes.c_double), _vp],
+    "gpt_op_quantize_fp8": [_vp, _i32, _i64, _i32, _i32, _i32, _vp, _vp, _i64, _vp, _i64, _vp, _vp],
+    "gpt_op_gemm_fp8": [_i32, _i32, _i32, _vp, _i32, _i64, _vp, _i32, _i64, _vp, _i64, _vp, _vp, _f32, _vp],
 }
 
 EXPORTED = ["gpt_status_string", "gpt_last_error", "gpt_abi_version", "gpt_profile_num_categories",
-            "gpt_profile_category_name"] + list(_SIGS)
+            "gpt_profile_category_name", "gpt_fp8_partials"] + list(_SIGS)
 
 for _name, _args in _SIGS.items():
     _f = getattr(_lib, _name, None)
@@ -84,6 +87,8 @@ _lib.gpt_abi_version.restype = ctypes.c_int32
 _lib.gpt_profile_num_categories.restype = ctypes.c_int32
 _lib.gpt_profile_category_name.restype = ctypes.c_char_p
 _lib.gpt_profile_category_name.argtypes = [ctypes.c_int32]
+_lib.gpt_fp8_partials.restype = ctypes.c_int32
+_lib.gpt_fp8_partials.argtypes = [ctypes.c_int32, ctypes.c_int32]
 
 
 def lib():
@@ -232,3 +237,26 @@ def probe_mfma(fp8, blocks, iters, out, stream=None):
     f = ctypes.c_double()
     _call("gpt_probe_mfma", int(fp8), blocks, iters, _ptr(out), ctypes.byref(f), _stream(stream))
     return f.value
+
+
+def fp8_partials(rows, cols):
+    return int(_lib.gpt_fp8_partials(rows, cols))
+
+
+def quantize_fp8(x, fmt, scale, partial, q=None, qt=None, rows=None, cols=None, ldx=None, ldq=None, ldqt=None,
+                 stream=None):
+    """Per-tensor fp8 codes of x [rows, cols] (bf16 or fp32): q [rows, cols]
+    and / or qt [cols, rows] (uint8 tensors), scale (fp32 [1]) = fmax / amax."""
+    if rows is None:
+        rows, cols = x.shape
+    x_dtype = DTYPE_F32 if x.dtype == torch.float32 else DTYPE_BF16
+    _call("gpt_op_quantize_fp8", _ptr(x), x_dtype, ldx or cols, rows, cols, fmt, _ptr(scale), _ptr(q),
+          ldq or cols, _ptr(qt), ldqt or rows, _ptr(partial), _stream(stream))
+
+
+def gemm_fp8(A, fmt_a, B, fmt_b, C, M, N, K, scale_a, scale_b, lda=None, ldb=None, ldc=None, beta=0.0,
+             stream=None):
+    """C fp32 [M, N] = dec(A) dec(B)^T / (scale_a scale_b) (+ beta C); A [M, K]
+    and B [N, K] uint8 codes."""
+    _call("gpt_op_gemm_fp8", M, N, K, _ptr(A), fmt_a, lda or K, _ptr(B), fmt_b, ldb or K, _ptr(C), ldc or N,
+          _ptr(scale_a), _ptr(scale_b), beta, _stream(stream))

@@ -181,6 +181,54 @@ extern "C" gpt_status gpt_op_gemm(int32_t M, int32_t N, int32_t K, int32_t batch
 
 
 // ---------------------------------------------------------------------------
+// component: fp8 quantisation and fp8 GEMM
+// ---------------------------------------------------------------------------
+extern "C" int32_t gpt_fp8_partials(int32_t rows, int32_t cols) {
+  if (rows < 1 || cols < 1) return 1;
+  return fp8_partials(rows, cols);
+}
+
+extern "C" gpt_status gpt_op_quantize_fp8(const void* x, int32_t x_dtype, int64_t ldx, int32_t rows, int32_t cols,
+                                          int32_t fmt, float* scale, uint8_t* q, int64_t ldq, uint8_t* qt,
+                                          int64_t ldqt, float* partial, gpt_stream_t stream) {
+  if (rows < 0 || cols < 0) FAIL(GPT_ERR_INVALID_ARG, "negative size");
+  if (rows == 0 || cols == 0) return GPT_OK;
+  if (!x || !scale || !partial) FAIL(GPT_ERR_INVALID_ARG, "NULL pointer");
+  if (x_dtype != GPT_DTYPE_F32 && x_dtype != GPT_DTYPE_BF16) FAIL(GPT_ERR_UNSUPPORTED, "unknown x dtype");
+  if (fmt != GPT_FP8_E4M3 && fmt != GPT_FP8_E5M2) FAIL(GPT_ERR_UNSUPPORTED, "unknown fp8 format");
+  if ((rows % 16) || (cols % 16)) FAIL(GPT_ERR_INVALID_ARG, "rows and cols must be multiples of 16");
+  if ((long long)rows * cols / 4 >= (1LL << 31)) FAIL(GPT_ERR_INVALID_ARG, "tensor too large");
+  if (ldx < cols || (ldx % 4)) FAIL(GPT_ERR_INVALID_ARG, "ldx must be >= cols and a multiple of 4");
+  if (q && (ldq < cols || (ldq % 4))) FAIL(GPT_ERR_INVALID_ARG, "ldq must be >= cols and a multiple of 4");
+  if (qt && (ldqt < rows || (ldqt % 16))) FAIL(GPT_ERR_INVALID_ARG, "ldqt must be >= rows and a multiple of 16");
+  if (((uintptr_t)x & (x_dtype == GPT_DTYPE_F32 ? 15 : 7)) || ((uintptr_t)q & 3) || ((uintptr_t)qt & 15))
+    FAIL(GPT_ERR_INVALID_ARG, "misaligned pointer");
+  TRY(quantize_fp8(x, x_dtype == GPT_DTYPE_F32, ldx, rows, cols, fmt, partial, scale, q, ldq, qt, ldqt, S(stream)));
+  return GPT_OK;
+}
+
+extern "C" gpt_status gpt_op_gemm_fp8(int32_t M, int32_t N, int32_t K, const uint8_t* A, int32_t fmt_a, int64_t lda,
+                                      const uint8_t* B, int32_t fmt_b, int64_t ldb, float* C, int64_t ldc,
+                                      const float* scale_a, const float* scale_b, float beta, gpt_stream_t stream) {
+  if (M < 0 || N < 0 || K < 0) FAIL(GPT_ERR_INVALID_ARG, "negative size");
+  if (M == 0 || N == 0) return GPT_OK;
+  if (!A || !B || !C || !scale_a || !scale_b) FAIL(GPT_ERR_INVALID_ARG, "NULL pointer");
+  if ((fmt_a != GPT_FP8_E4M3 && fmt_a != GPT_FP8_E5M2) || (fmt_b != GPT_FP8_E4M3 && fmt_b != GPT_FP8_E5M2))
+    FAIL(GPT_ERR_UNSUPPORTED, "unknown fp8 format");
+  if (K % 16) FAIL(GPT_ERR_INVALID_ARG, "K must be a multiple of 16");
+  if (lda < K || ldb < K || ldc < N || (lda % 16) || (ldb % 16) || (ldc % 4))
+    FAIL(GPT_ERR_INVALID_ARG, "lda, ldb must be >= K and multiples of 16; ldc >= N and a multiple of 4");
+  if (((uintptr_t)A | (uintptr_t)B | (uintptr_t)C) & 15) FAIL(GPT_ERR_INVALID_ARG, "pointers must be 16-byte aligned");
+  GemmArgs a;
+  a.M = M; a.N = N; a.K = K;
+  a.A = A; a.lda = lda; a.B = B; a.ldb = ldb;
+  a.C = C; a.ldc = ldc; a.beta = beta;
+  a.scale_a = scale_a; a.scale_b = scale_b;
+  TRY(gemm_fp8(a, EPI_F32, fmt_a, fmt_b, S(stream)));
+  return GPT_OK;
+}
+
+// ---------------------------------------------------------------------------
 // per-category kernel timing with HIP events (off unless enabled)
 // ---------------------------------------------------------------------------
 namespace {
@@ -189,14 +237,14 @@ enum ProfCat {
   P_EMBED_FWD, P_RMSNORM_FWD, P_GEMM_QKV, P_ATTN_FWD, P_GEMM_O, P_GEMM_FC, P_GEMM_PROJ, P_CE_FWD,
   P_CE_REDUCE, P_CE_DZ, P_CE_DH, P_CE_DW, P_RMSNORM_BWD, P_PROJ_DGRAD, P_PROJ_WGRAD, P_FC_DGRAD,
   P_FC_WGRAD, P_O_DGRAD, P_O_WGRAD, P_ATTN_BWD, P_ROPE_BWD, P_QKV_DGRAD, P_QKV_WGRAD, P_EMBED_BWD,
-  P_FILL, P_MUON_ELEMWISE, P_NS_GRAM, P_NS_POLY, P_NS_UPDATE, P_COUNT
+  P_FILL, P_MUON_ELEMWISE, P_NS_GRAM, P_NS_POLY, P_NS_UPDATE, P_FP8_QUANT, P_COUNT
 };
 const char* kProfNames[P_COUNT] = {
     "embed_fwd", "rmsnorm_fwd", "gemm_qkv_rope_fwd", "attn_fwd", "gemm_o_fwd", "gemm_fc_relu2_fwd",
     "gemm_proj_fwd", "gemm_ce_fwd", "ce_reduce", "gemm_ce_dlogits", "gemm_ce_dh", "gemm_ce_dw",
     "rmsnorm_bwd", "gemm_proj_dgrad", "gemm_proj_wgrad", "gemm_fc_dgrad", "gemm_fc_wgrad",
     "gemm_o_dgrad", "gemm_o_wgrad", "attn_bwd", "rope_qknorm_bwd", "gemm_qkv_dgrad", "gemm_qkv_wgrad",
-    "embed_bwd", "fill", "muon_elementwise", "ns_gram", "ns_poly", "ns_update"};
+    "embed_bwd", "fill", "muon_elementwise", "ns_gram", "ns_poly", "ns_update", "fp8_quant"};
 
 struct Profiler {
   uint64_t mask = 0;
@@ -295,13 +343,24 @@ inline size_t wgrad_part_elems(int M, int N, int K);
 
 struct Layer {
   size_t h1, r1, qkv, rq, rk, att, lse, h2, r2, act;
+  // fp8 precision only: transposed E4M3 codes of the block-product inputs
+  // (for the weight gradients) and the weights' codes, plain and transposed
+  size_t h1t, attt, h2t, actt;
+  size_t wqkv8, wqkv8t, wo8, wo8t, wfc8, wfc8t, wproj8, wproj8t;
 };
+
+// per-layer fp8 scales (fmax / amax of the tensor)
+enum Fp8Scale { SC_H1, SC_ATT, SC_H2, SC_ACT, SC_WQKV, SC_WO, SC_WFC, SC_WPROJ, SC_G_MLP, SC_DU, SC_G_ATT,
+                SC_DQKV, SC_COUNT = 16 };
 
 struct WS {
   size_t cs, x, hf, rf, part, zt, lse, row_loss;
   std::vector<Layer> layer;
   // backward scratch
   size_t g, g_bf, dh, du, dout, delta, dq_acc, dqkv, dz, wpart;
+  // fp8 precision only: codes of the current product input (forward) and of
+  // the current output gradient, plain and transposed (backward); scales
+  size_t xq, dyq, dyqt, scales, qpart;
   size_t total;
 };
 
@@ -351,6 +410,30 @@ WS ws_layout(const Dims& D) {
     mx = std::max(mx, wgrad_part_elems(vocab_chunk(D), dd, Nt));
     w.wpart = take(std::max<size_t>(mx, 1) * 4);
   }
+  w.xq = w.dyq = w.dyqt = w.scales = w.qpart = 0;
+  if (D.prec == GPT_PREC_FP8) {
+    const size_t dd = (size_t)d * d, hd = (size_t)D.hidden;
+    for (int l = 0; l < D.L; ++l) {
+      Layer& L = w.layer[l];
+      L.h1t = take(N * d);
+      L.attt = take(N * d);
+      L.h2t = take(N * d);
+      L.actt = take(N * hd);
+      L.wqkv8 = take(3 * dd);
+      L.wqkv8t = take(3 * dd);
+      L.wo8 = take(dd);
+      L.wo8t = take(dd);
+      L.wfc8 = take(hd * d);
+      L.wfc8t = take(hd * d);
+      L.wproj8 = take(hd * d);
+      L.wproj8t = take(hd * d);
+    }
+    w.xq = take(N * hd);
+    w.dyq = take(N * hd);
+    w.dyqt = take(N * hd);
+    w.scales = take((size_t)D.L * SC_COUNT * 4);
+    w.qpart = take((size_t)kFp8Partials * 4);
+  }
   w.total = o;
   return w;
 }
@@ -390,6 +473,26 @@ int wgrad(const void* A, long long lda, const void* B, long long ldb, float* C, 
   }
   a.C = part; a.ldc = N; a.k_split = ks; a.split_stride = (long long)M * N; a.beta = 0.f;
   int rc = gemm_bf16(a, EPI_F32, s);
+  if (rc) return rc;
+  return launch_splitk_reduce(part, ks, (long long)M * N, C, nullptr, (long long)M * N, accumulate ? 1.f : 0.f, s);
+}
+
+// fp8 weight gradient: C[M,N] (+)= A B^T / (sa sb) with A = dY^T codes
+// [M][K] (E5M2) and B = X^T codes [N][K] (E4M3), both k-contiguous
+int wgrad_fp8(const uint8_t* A, const uint8_t* B, const float* sa, const float* sb, float* C, int M, int N, int K,
+              bool accumulate, float* part, hipStream_t s) {
+  GemmArgs a;
+  a.M = M; a.N = N; a.K = K;
+  a.A = A; a.lda = K; a.B = B; a.ldb = K;
+  a.scale_a = sa; a.scale_b = sb;
+  const int ks = wgrad_splits(M, N, K);
+  if (ks == 1) {
+    a.C = C; a.ldc = N;
+    a.beta = accumulate ? 1.f : 0.f;
+    return gemm_fp8(a, EPI_F32, 1, 0, s);
+  }
+  a.C = part; a.ldc = N; a.k_split = ks; a.split_stride = (long long)M * N; a.beta = 0.f;
+  int rc = gemm_fp8(a, EPI_F32, 1, 0, s);
   if (rc) return rc;
   return launch_splitk_reduce(part, ks, (long long)M * N, C, nullptr, (long long)M * N, accumulate ? 1.f : 0.f, s);
 }
@@ -449,7 +552,8 @@ int check_step_args(const gpt_shape* shape, const gpt_params* params, const int3
   if (((uintptr_t)params->bf16 & 15)) FAIL(GPT_ERR_INVALID_ARG, "params->bf16 must be 16-byte aligned");
   *w = ws_layout(*D);
   if (ws_bytes < w->total) FAIL(GPT_ERR_WORKSPACE, "workspace smaller than gpt_workspace_size()");
-  if (D->prec == GPT_PREC_FP8) FAIL(GPT_ERR_UNSUPPORTED, "fp8 precision is not available in this build");
+  if (D->prec == GPT_PREC_FP8 && (D->N % 16))
+    FAIL(GPT_ERR_UNSUPPORTED, "fp8 precision needs batch*seq_len to be a multiple of 16");
   return 0;
 }
 
@@ -471,15 +575,51 @@ extern "C" gpt_status gpt_step_fwd(const gpt_shape* shape, const gpt_params* par
   float* cs = at<float>(ws, w.cs);
 
   TRY(launch_rope_table(cs, D.T, s));
+  const bool f8 = D.prec == GPT_PREC_FP8;
+  const int hid = D.hidden;
+  float* qpart = f8 ? at<float>(ws, w.qpart) : nullptr;
+  uint8_t* xq = f8 ? at<uint8_t>(ws, w.xq) : nullptr;
+  if (f8) {
+    // E4M3 codes of every block weight, plain (forward) and transposed (data gradient)
+    ProfScope ps_(P_FP8_QUANT, s);
+    for (int l = 0; l < D.L; ++l) {
+      const Layer& L = w.layer[l];
+      float* sc = at<float>(ws, w.scales) + (size_t)l * SC_COUNT;
+      TRY(quantize_fp8(W + P.qkv(D, l), 0, d, 3 * d, d, 0, qpart, sc + SC_WQKV, at<uint8_t>(ws, L.wqkv8), d,
+                       at<uint8_t>(ws, L.wqkv8t), 3 * d, s));
+      TRY(quantize_fp8(W + P.wo(D, l), 0, d, d, d, 0, qpart, sc + SC_WO, at<uint8_t>(ws, L.wo8), d,
+                       at<uint8_t>(ws, L.wo8t), d, s));
+      TRY(quantize_fp8(W + P.fc(D, l), 0, d, hid, d, 0, qpart, sc + SC_WFC, at<uint8_t>(ws, L.wfc8), d,
+                       at<uint8_t>(ws, L.wfc8t), hid, s));
+      TRY(quantize_fp8(W + P.proj(D, l), 0, hid, d, hid, 0, qpart, sc + SC_WPROJ, at<uint8_t>(ws, L.wproj8), hid,
+                       at<uint8_t>(ws, L.wproj8t), d, s));
+    }
+  }
+  // y (op)= X W^T for one block product: bf16 operands, or (fp8) the E4M3 codes
+  // of X (quantised here; the transposed codes are kept for the weight
+  // gradient) and of W
+  auto quant_x = [&](const uint16_t* X, int K, size_t xt_off, float* sx) -> int {
+    if (!f8) return 0;
+    ProfScope ps_(P_FP8_QUANT, s);
+    return quantize_fp8(X, 0, K, N, K, 0, qpart, sx, xq, K, at<uint8_t>(ws, xt_off), N, s);
+  };
+  auto block_fwd = [&](GemmArgs& a, int epi, int K, const uint8_t* w8, const float* sx, const float* sw) -> int {
+    if (!f8) return gemm_bf16(a, epi, s);
+    a.A = xq; a.lda = K; a.B = w8; a.ldb = K;
+    a.scale_a = sx; a.scale_b = sw;
+    return gemm_fp8(a, epi, 0, 0, s);
+  };
   { ProfScope ps_(P_EMBED_FWD, s); TRY(launch_embed_fwd(ids, W + P.wte, x, D.B, D.T, d, s)); }
   for (int l = 0; l < D.L; ++l) {
     const Layer& L = w.layer[l];
+    float* sc = f8 ? at<float>(ws, w.scales) + (size_t)l * SC_COUNT : nullptr;
     uint16_t* h1 = at<uint16_t>(ws, L.h1);
     uint16_t* qkv = at<uint16_t>(ws, L.qkv);
     uint16_t* att = at<uint16_t>(ws, L.att);
     uint16_t* h2 = at<uint16_t>(ws, L.h2);
     uint16_t* act = at<uint16_t>(ws, L.act);
     { ProfScope ps_(P_RMSNORM_FWD, s); TRY(launch_rmsnorm_fwd(x, h1, at<float>(ws, L.r1), N, d, s)); }
+    TRY(quant_x(h1, d, L.h1t, sc ? sc + SC_H1 : nullptr));
     {
       GemmArgs a;  // [q | k | v] = h1 [Wq; Wk; Wv]^T, q and k rotated and RMS-normalised per head
       ProfScope ps_(P_GEMM_QKV, s);
@@ -488,33 +628,40 @@ extern "C" gpt_status gpt_step_fwd(const gpt_shape* shape, const gpt_params* par
       a.C = qkv; a.ldc = 3 * d;
       a.rope = cs; a.row_T = D.T; a.n_head = D.H;
       a.part = at<float>(ws, L.rq); a.zt = at<float>(ws, L.rk);
-      TRY(gemm_bf16(a, EPI_QKV, s));
+      TRY(block_fwd(a, EPI_QKV, d, f8 ? at<uint8_t>(ws, L.wqkv8) : nullptr, sc ? sc + SC_H1 : nullptr,
+                    sc ? sc + SC_WQKV : nullptr));
     }
     { ProfScope ps_(P_ATTN_FWD, s); TRY(launch_attn_fwd(qkv, qkv + d, qkv + 2 * d, 3 * d, att, d, at<float>(ws, L.lse), D.B, D.H, D.T, s)); }
+    TRY(quant_x(att, d, L.attt, sc ? sc + SC_ATT : nullptr));
     {
       GemmArgs a;  // x += att Wo^T
       ProfScope ps_(P_GEMM_O, s);
       a.M = N; a.N = d; a.K = d;
       a.A = att; a.lda = d; a.B = W + P.wo(D, l); a.ldb = d;
       a.C = x; a.ldc = d;
-      TRY(gemm_bf16(a, EPI_RESID, s));
+      TRY(block_fwd(a, EPI_RESID, d, f8 ? at<uint8_t>(ws, L.wo8) : nullptr, sc ? sc + SC_ATT : nullptr,
+                    sc ? sc + SC_WO : nullptr));
     }
     { ProfScope ps_(P_RMSNORM_FWD, s); TRY(launch_rmsnorm_fwd(x, h2, at<float>(ws, L.r2), N, d, s)); }
+    TRY(quant_x(h2, d, L.h2t, sc ? sc + SC_H2 : nullptr));
     {
       GemmArgs a;  // act = relu(h2 Wfc^T)^2
       ProfScope ps_(P_GEMM_FC, s);
-      a.M = N; a.N = D.hidden; a.K = d;
+      a.M = N; a.N = hid; a.K = d;
       a.A = h2; a.lda = d; a.B = W + P.fc(D, l); a.ldb = d;
-      a.C = act; a.ldc = D.hidden;
-      TRY(gemm_bf16(a, EPI_RELU2, s));
+      a.C = act; a.ldc = hid;
+      TRY(block_fwd(a, EPI_RELU2, d, f8 ? at<uint8_t>(ws, L.wfc8) : nullptr, sc ? sc + SC_H2 : nullptr,
+                    sc ? sc + SC_WFC : nullptr));
     }
+    TRY(quant_x(act, hid, L.actt, sc ? sc + SC_ACT : nullptr));
     {
       GemmArgs a;  // x += act Wproj^T
       ProfScope ps_(P_GEMM_PROJ, s);
-      a.M = N; a.N = d; a.K = D.hidden;
-      a.A = act; a.lda = D.hidden; a.B = W + P.proj(D, l); a.ldb = D.hidden;
+      a.M = N; a.N = d; a.K = hid;
+      a.A = act; a.lda = hid; a.B = W + P.proj(D, l); a.ldb = hid;
       a.C = x; a.ldc = d;
-      TRY(gemm_bf16(a, EPI_RESID, s));
+      TRY(block_fwd(a, EPI_RESID, hid, f8 ? at<uint8_t>(ws, L.wproj8) : nullptr,
+                    sc ? sc + SC_ACT : nullptr, sc ? sc + SC_WPROJ : nullptr));
     }
   }
   uint16_t* hf = at<uint16_t>(ws, w.hf);
@@ -595,55 +742,99 @@ extern "C" gpt_status gpt_step_bwd(const gpt_shape* shape, const gpt_params* par
   { ProfScope ps_(P_FILL, s); TRY(launch_fill_f32(g, (long long)N * d, 0.f, s)); }
   { ProfScope ps_(P_RMSNORM_BWD, s); TRY(launch_rmsnorm_bwd(dh, hf, at<float>(ws, w.rf), g, g_bf, N, d, s)); }
 
+  const bool f8 = D.prec == GPT_PREC_FP8;
+  float* qpart = f8 ? at<float>(ws, w.qpart) : nullptr;
+  uint8_t* dyq = f8 ? at<uint8_t>(ws, w.dyq) : nullptr;
+  uint8_t* dyqt = f8 ? at<uint8_t>(ws, w.dyqt) : nullptr;
+  // E5M2 codes of an output gradient dY [N, cols], plain and transposed
+  auto quant_dy = [&](const uint16_t* dy, int cols, float* sdy) -> int {
+    ProfScope ps_(P_FP8_QUANT, s);
+    return quantize_fp8(dy, 0, cols, N, cols, 1, qpart, sdy, dyq, cols, dyqt, N, s);
+  };
+  // data gradient dX [N, cols_x] = dY W for a weight W [cols_dy, cols_x]: fp8
+  // operands are the dY codes and the transposed weight codes W^T [cols_x, cols_dy]
+  auto dgrad_fp8 = [&](GemmArgs& a, int epi, int cols_dy, const uint8_t* wt8, const float* sdy,
+                       const float* sw) -> int {
+    a.A = dyq; a.lda = cols_dy; a.a_kcontig = 1;
+    a.B = wt8; a.ldb = cols_dy; a.b_kcontig = 1;
+    a.scale_a = sdy; a.scale_b = sw;
+    return gemm_fp8(a, epi, 1, 0, s);
+  };
+
   for (int l = D.L - 1; l >= 0; --l) {
     const Layer& L = w.layer[l];
+    float* sc = f8 ? at<float>(ws, w.scales) + (size_t)l * SC_COUNT : nullptr;
     const uint16_t* h1 = at<uint16_t>(ws, L.h1);
     const uint16_t* qkv = at<uint16_t>(ws, L.qkv);
     const uint16_t* att = at<uint16_t>(ws, L.att);
     const uint16_t* h2 = at<uint16_t>(ws, L.h2);
     const uint16_t* act = at<uint16_t>(ws, L.act);
     // ---- MLP ----
+    if (f8) TRY(quant_dy(g_bf, d, sc + SC_G_MLP));
     {
       GemmArgs a;  // du = (g Wproj) * 2 relu(u)  with relu(u) = sqrt(act)
       ProfScope ps_(P_PROJ_DGRAD, s);
       a.M = N; a.N = hid; a.K = d;
       a.A = g_bf; a.lda = d; a.B = W + P.proj(D, l); a.ldb = hid; a.b_kcontig = 0;
       a.C = du; a.ldc = hid; a.aux = act; a.ldaux = hid;
-      TRY(gemm_bf16(a, EPI_DRELU2, s));
+      if (f8) TRY(dgrad_fp8(a, EPI_DRELU2, d, at<uint8_t>(ws, L.wproj8t), sc + SC_G_MLP, sc + SC_WPROJ));
+      else TRY(gemm_bf16(a, EPI_DRELU2, s));
     }
-    { ProfScope ps_(P_PROJ_WGRAD, s); TRY(wgrad(g_bf, d, act, hid, G + P.proj(D, l), d, hid, N, acc, wpart, s)); }  // dWproj = g^T act
+    {
+      ProfScope ps_(P_PROJ_WGRAD, s);  // dWproj = g^T act
+      if (f8) TRY(wgrad_fp8(dyqt, at<uint8_t>(ws, L.actt), sc + SC_G_MLP, sc + SC_ACT, G + P.proj(D, l), d, hid, N, acc, wpart, s));
+      else TRY(wgrad(g_bf, d, act, hid, G + P.proj(D, l), d, hid, N, acc, wpart, s));
+    }
+    if (f8) TRY(quant_dy(du, hid, sc + SC_DU));
     {
       GemmArgs a;  // dh = du Wfc
       ProfScope ps_(P_FC_DGRAD, s);
       a.M = N; a.N = d; a.K = hid;
       a.A = du; a.lda = hid; a.B = W + P.fc(D, l); a.ldb = d; a.b_kcontig = 0;
       a.C = dh; a.ldc = d;
-      TRY(gemm_bf16(a, EPI_F32, s));
+      if (f8) TRY(dgrad_fp8(a, EPI_F32, hid, at<uint8_t>(ws, L.wfc8t), sc + SC_DU, sc + SC_WFC));
+      else TRY(gemm_bf16(a, EPI_F32, s));
     }
-    { ProfScope ps_(P_FC_WGRAD, s); TRY(wgrad(du, hid, h2, d, G + P.fc(D, l), hid, d, N, acc, wpart, s)); }  // dWfc = du^T h2
+    {
+      ProfScope ps_(P_FC_WGRAD, s);  // dWfc = du^T h2
+      if (f8) TRY(wgrad_fp8(dyqt, at<uint8_t>(ws, L.h2t), sc + SC_DU, sc + SC_H2, G + P.fc(D, l), hid, d, N, acc, wpart, s));
+      else TRY(wgrad(du, hid, h2, d, G + P.fc(D, l), hid, d, N, acc, wpart, s));
+    }
     { ProfScope ps_(P_RMSNORM_BWD, s); TRY(launch_rmsnorm_bwd(dh, h2, at<float>(ws, L.r2), g, g_bf, N, d, s)); }
     // ---- attention ----
+    if (f8) TRY(quant_dy(g_bf, d, sc + SC_G_ATT));
     {
       GemmArgs a;  // dO = g Wo
       ProfScope ps_(P_O_DGRAD, s);
       a.M = N; a.N = d; a.K = d;
       a.A = g_bf; a.lda = d; a.B = W + P.wo(D, l); a.ldb = d; a.b_kcontig = 0;
       a.C = dout; a.ldc = d;
-      TRY(gemm_bf16(a, EPI_BF16, s));
+      if (f8) TRY(dgrad_fp8(a, EPI_BF16, d, at<uint8_t>(ws, L.wo8t), sc + SC_G_ATT, sc + SC_WO));
+      else TRY(gemm_bf16(a, EPI_BF16, s));
     }
-    { ProfScope ps_(P_O_WGRAD, s); TRY(wgrad(g_bf, d, att, d, G + P.wo(D, l), d, d, N, acc, wpart, s)); }  // dWo = g^T att
+    {
+      ProfScope ps_(P_O_WGRAD, s);  // dWo = g^T att
+      if (f8) TRY(wgrad_fp8(dyqt, at<uint8_t>(ws, L.attt), sc + SC_G_ATT, sc + SC_ATT, G + P.wo(D, l), d, d, N, acc, wpart, s));
+      else TRY(wgrad(g_bf, d, att, d, G + P.wo(D, l), d, d, N, acc, wpart, s));
+    }
     { ProfScope ps_(P_ATTN_BWD, s); TRY(launch_attn_bwd(qkv, qkv + d, qkv + 2 * d, 3 * d, att, dout, d, at<float>(ws, L.lse),
                         at<float>(ws, w.delta), dq_acc, dqkv + d, dqkv + 2 * d, 3 * d, D.B, D.H, D.T, s)); }
     { ProfScope ps_(P_ROPE_BWD, s); TRY(launch_rope_qknorm_bwd(dq_acc, dqkv, qkv, at<float>(ws, L.rq), at<float>(ws, L.rk), cs, N, D.T, D.H, s)); }
+    if (f8) TRY(quant_dy(dqkv, 3 * d, sc + SC_DQKV));
     {
       GemmArgs a;  // dh = dqkv [Wq; Wk; Wv]
       ProfScope ps_(P_QKV_DGRAD, s);
       a.M = N; a.N = d; a.K = 3 * d;
       a.A = dqkv; a.lda = 3 * d; a.B = W + P.qkv(D, l); a.ldb = d; a.b_kcontig = 0;
       a.C = dh; a.ldc = d;
-      TRY(gemm_bf16(a, EPI_F32, s));
+      if (f8) TRY(dgrad_fp8(a, EPI_F32, 3 * d, at<uint8_t>(ws, L.wqkv8t), sc + SC_DQKV, sc + SC_WQKV));
+      else TRY(gemm_bf16(a, EPI_F32, s));
     }
-    { ProfScope ps_(P_QKV_WGRAD, s); TRY(wgrad(dqkv, 3 * d, h1, d, G + P.qkv(D, l), 3 * d, d, N, acc, wpart, s)); }  // dWqkv = dqkv^T h1
+    {
+      ProfScope ps_(P_QKV_WGRAD, s);  // dWqkv = dqkv^T h1
+      if (f8) TRY(wgrad_fp8(dyqt, at<uint8_t>(ws, L.h1t), sc + SC_DQKV, sc + SC_H1, G + P.qkv(D, l), 3 * d, d, N, acc, wpart, s));
+      else TRY(wgrad(dqkv, 3 * d, h1, d, G + P.qkv(D, l), 3 * d, d, N, acc, wpart, s));
+    }
     { ProfScope ps_(P_RMSNORM_BWD, s); TRY(launch_rmsnorm_bwd(dh, h1, at<float>(ws, L.r1), g, g_bf, N, d, s)); }
   }
   if (!acc) { ProfScope ps_(P_FILL, s); TRY(launch_fill_f32(G + P.wte, (long long)D.V * d, 0.f, s)); }

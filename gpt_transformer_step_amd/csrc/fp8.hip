@@ -1,0 +1,170 @@
+// Per-tensor fp8 quantisation for the fp8 block products (apidog.com/pt
+// "Gerenciamento de Precisão" and apidog.com/de "Präzisionsverwaltung": most
+// linear layers in fp8 with one scale per tensor).
+//
+//   amax  = max |x| over the whole tensor          (amax_partial + fp8_scale)
+//   s     = fmax / amax in fp32 (1 when amax == 0)  fmax: 448 (E4M3), 57344 (E5M2)
+//   code  = RNE(clamp(x * s, -fmax, fmax))          (fp8_quant)
+//
+// The hardware converter (v_cvt_pk_fp8_f32 / v_cvt_pk_bf8_f32, OCP formats on
+// gfx950) rounds to nearest even but does not saturate, so values are clamped
+// to +-fmax first.  The quantiser writes the codes in the tensor's layout,
+// transposed, or both: fp8 products take both operands k-contiguous, so the
+// data-gradient product needs W^T and the weight-gradient product needs
+// dY^T and X^T.
+
+#include <algorithm>
+
+#include "common.h"
+#include "kernels.h"
+
+namespace gs {
+
+namespace {
+
+constexpr int kQT = 64;        // quantiser tile: 64 x 64 elements, 256 threads of 4 x 4
+constexpr int kLDT = kQT + 4;  // LDS row (bytes) of the transposed tile, padded against bank conflicts
+
+__device__ __forceinline__ float fmax_of(int fmt) { return fmt ? 57344.f : 448.f; }
+
+template <bool F32>
+__device__ __forceinline__ void load4(const void* x, long long idx, float* v) {
+  if constexpr (F32) {
+    const float4 f = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(x) + idx);
+    v[0] = f.x; v[1] = f.y; v[2] = f.z; v[3] = f.w;
+  } else {
+    const uint2 w = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(x) + idx);
+    v[0] = lo_bf(w.x); v[1] = hi_bf(w.x); v[2] = lo_bf(w.y); v[3] = hi_bf(w.y);
+  }
+}
+
+// max |x| over rows x cols (cols % 4 == 0), one partial per block
+template <bool F32>
+__global__ void __launch_bounds__(256) amax_partial_kernel(const void* __restrict__ x, long long ldx, int rows,
+                                                          int cols, float* __restrict__ partial) {
+  // rows * cols / 4 < 2^31 (checked on the host): 32-bit index arithmetic
+  const unsigned c4 = (unsigned)cols / 4u;
+  const unsigned n4 = (unsigned)rows * c4;
+  float m = 0.f;
+  for (unsigned i = blockIdx.x * 256u + threadIdx.x; i < n4; i += gridDim.x * 256u) {
+    const unsigned r = i / c4, c = (i - r * c4) * 4u;
+    float v[4];
+    load4<F32>(x, (long long)r * ldx + c, v);
+    m = fmaxf(m, fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3]))));
+  }
+  m = wave_max(m);
+  __shared__ float red[4];
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) partial[blockIdx.x] = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+}
+
+__global__ void __launch_bounds__(256) fp8_scale_kernel(const float* __restrict__ partial, int np, int fmt,
+                                                       float* __restrict__ scale) {
+  float m = 0.f;
+  for (int i = threadIdx.x; i < np; i += 256) m = fmaxf(m, partial[i]);
+  m = wave_max(m);
+  __shared__ float red[4];
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const float amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    scale[0] = amax > 0.f ? fmax_of(fmt) / amax : 1.f;
+  }
+}
+
+// two fp8 codes (low 16 bits of the result)
+template <int FMT>
+__device__ __forceinline__ uint32_t cvt2(float a, float b) {
+  if constexpr (FMT == 0) return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false) & 0xffffu;
+  else return (uint32_t)__builtin_amdgcn_cvt_pk_bf8_f32(a, b, 0, false) & 0xffffu;
+}
+
+// One 64 x 64 tile per block; thread t owns the 4 x 4 block at rows
+// 4 (t / 16), columns 4 (t % 16).  rows % 16 == 0 and cols % 16 == 0.
+template <bool F32, int FMT>
+__global__ void __launch_bounds__(256) fp8_quant_kernel(const void* __restrict__ x, long long ldx, int rows, int cols,
+                                                       const float* __restrict__ scale, uint8_t* __restrict__ q,
+                                                       long long ldq, uint8_t* __restrict__ qt, long long ldqt) {
+  __shared__ __attribute__((aligned(16))) uint8_t tile[kQT * kLDT];
+  const int t = threadIdx.x;
+  const int r0 = blockIdx.y * kQT, c0 = blockIdx.x * kQT;
+  const int rb = 4 * (t >> 4), cb = 4 * (t & 15);
+  const float s = scale[0];
+  const float fm = fmax_of(FMT);
+  const bool in = (r0 + rb < rows) && (c0 + cb < cols);
+  uint32_t rw[4] = {0u, 0u, 0u, 0u};  // row words: codes of row i, columns 0..3
+  if (in) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float v[4];
+      load4<F32>(x, (long long)(r0 + rb + i) * ldx + c0 + cb, v);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) v[j] = fminf(fmaxf(v[j] * s, -fm), fm);
+      rw[i] = cvt2<FMT>(v[0], v[1]) | (cvt2<FMT>(v[2], v[3]) << 16);
+    }
+    if (q) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) *reinterpret_cast<uint32_t*>(q + (long long)(r0 + rb + i) * ldq + c0 + cb) = rw[i];
+    }
+  }
+  if (!qt) return;
+  // column words: codes of column j, rows 0..3, into the transposed tile
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint32_t cw = ((rw[0] >> (8 * j)) & 0xffu) | (((rw[1] >> (8 * j)) & 0xffu) << 8) |
+                        (((rw[2] >> (8 * j)) & 0xffu) << 16) | (((rw[3] >> (8 * j)) & 0xffu) << 24);
+    *reinterpret_cast<uint32_t*>(tile + (cb + j) * kLDT + rb) = cw;
+  }
+  __syncthreads();
+  // row c of the transposed tile = column c0 + c of x: 64 codes, 16 per thread
+  const int c = t >> 2, seg = 16 * (t & 3);
+  if (c0 + c < cols && r0 + seg < rows) {
+    const uint32_t* src = reinterpret_cast<const uint32_t*>(tile + c * kLDT + seg);
+    *reinterpret_cast<uint4*>(qt + (long long)(c0 + c) * ldqt + r0 + seg) = make_uint4(src[0], src[1], src[2], src[3]);
+  }
+}
+
+}  // namespace
+
+int fp8_partials(long long rows, long long cols) {
+  const long long n4 = rows * cols / 4;
+  return (int)std::max<long long>(1, std::min<long long>(kFp8Partials, (n4 + 255) / 256));
+}
+
+int launch_fp8_amax_scale(const void* x, int is_f32, long long ldx, int rows, int cols, int fmt, float* partial,
+                          float* scale, hipStream_t s) {
+  const int np = fp8_partials(rows, cols);
+  if (is_f32)
+    hipLaunchKernelGGL(amax_partial_kernel<true>, dim3(np), dim3(256), 0, s, x, ldx, rows, cols, partial);
+  else
+    hipLaunchKernelGGL(amax_partial_kernel<false>, dim3(np), dim3(256), 0, s, x, ldx, rows, cols, partial);
+  GS_LAUNCH_CHECK("amax_partial");
+  hipLaunchKernelGGL(fp8_scale_kernel, dim3(1), dim3(256), 0, s, partial, np, fmt, scale);
+  GS_LAUNCH_CHECK("fp8_scale");
+  return 0;
+}
+
+int launch_fp8_quant(const void* x, int is_f32, long long ldx, int rows, int cols, int fmt, const float* scale,
+                     uint8_t* q, long long ldq, uint8_t* qt, long long ldqt, hipStream_t s) {
+  if (rows <= 0 || cols <= 0) return 0;
+  dim3 grid((cols + kQT - 1) / kQT, (rows + kQT - 1) / kQT);
+#define GS_Q(F, M) hipLaunchKernelGGL((fp8_quant_kernel<F, M>), grid, dim3(256), 0, s, x, ldx, rows, cols, scale, q, ldq, qt, ldqt)
+  if (is_f32) {
+    if (fmt) GS_Q(true, 1); else GS_Q(true, 0);
+  } else {
+    if (fmt) GS_Q(false, 1); else GS_Q(false, 0);
+  }
+#undef GS_Q
+  GS_LAUNCH_CHECK("fp8_quant");
+  return 0;
+}
+
+int quantize_fp8(const void* x, int is_f32, long long ldx, int rows, int cols, int fmt, float* partial, float* scale,
+                 uint8_t* q, long long ldq, uint8_t* qt, long long ldqt, hipStream_t s) {
+  int rc = launch_fp8_amax_scale(x, is_f32, ldx, rows, cols, fmt, partial, scale, s);
+  if (rc) return rc;
+  return launch_fp8_quant(x, is_f32, ldx, rows, cols, fmt, scale, q, ldq, qt, ldqt, s);
+}
+
+}  // namespace gs

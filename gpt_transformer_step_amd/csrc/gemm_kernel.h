@@ -1,22 +1,28 @@
-// bf16 GEMM family on CDNA4 matrix cores (v_mfma_f32_32x32x16_bf16).
+// GEMM family on CDNA4 matrix cores: bf16 (v_mfma_f32_32x32x16_bf16) and
+// fp8 (v_mfma_scale_f32_32x32x64_f8f6f4, OCP E4M3 / E5M2 codes).
 //
 // Every dense contraction of the step runs here: the q/k/v, output, MLP and
 // head projections of the model passage (dev.to "¿Cómo Entrenar Tu Propio
 // ChatGPT por $50?", "1. Modelo GPT"; the bf16 cast of weights in
 // "3. Gestión de Precisión"), their data and weight gradients, the chunked
-// head/cross-entropy products, and the three products of each Newton-Schulz
-// iteration ("2. Optimizador Muon": A = X^T X, B = b A + c A A, X = a X + X B).
+// head/cross-entropy products, the three products of each Newton-Schulz
+// iteration ("2. Optimizador Muon": A = X^T X, B = b A + c A A, X = a X + X B),
+// and the fp8 block products with one scale per tensor (apidog.com/pt
+// "Gerenciamento de Precisão").
 //
 // Design (gfx950):
-//   * 256 threads = 4 waves in a 2x2 grid; workgroup tile BM x BN, K step 64.
-//   * Operands are staged global -> registers -> LDS, double buffered, one
-//     barrier per K step; the next step's global loads are in flight while the
-//     current step's MFMAs run.
+//   * 256x256 tiles with 8 waves (two per SIMD), or 128x128 tiles with 4; the
+//     waves form a (waves/2) x 2 grid, each owning 64 rows and BN/2 columns.
+//     One LDS stage holds 128 bytes of k per row (64 bf16 or 128 fp8 codes).
+//   * Operands are staged in LDS, double buffered, one barrier per stage;
+//     interior tiles are copied global -> LDS directly (global_load_lds), so
+//     the next stage's loads are in flight while this stage's MFMAs run.
 //   * Each operand tile sits in LDS in its memory layout.  A k-contiguous tile
-//     is read as MFMA fragments with 16-byte loads; an m/n-contiguous tile
+//     is read as MFMA fragments with 16-byte loads; an m/n-contiguous bf16 tile
 //     (the weight-gradient, data-gradient and Gram operands) is read with the
-//     gfx950 transpose load ds_read_b64_tr_b16, two per fragment, so no
-//     product needs a transposed copy in HBM or a transpose in registers.
+//     gfx950 transpose load ds_read_b64_tr_b16, two per fragment, so no bf16
+//     product needs a transposed copy in HBM.  fp8 operands are always
+//     k-contiguous (the quantiser writes transposed copies where needed).
 //     Both layouts are XOR-swizzled so fragment reads are bank-conflict free
 //     (64 banks of 4 bytes, 16-lane groups per 16-byte read).
 //   * The MFMA is issued with the operands swapped (B tile as src0), so each
@@ -28,13 +34,20 @@
 
 #pragma once
 
+#include <type_traits>
+
 #include "common.h"
 #include "gemm.h"
 
 namespace gs {
 namespace {
 
-constexpr int kBK = 64;        // K elements per stage (128 bytes of bf16)
+// F8 template parameter: 0 = bf16 operands; 1 + fa + 2 fb = fp8 operands with
+// A in format fa and B in format fb (0 = E4M3, 1 = E5M2).
+constexpr int f8_fmt_a(int f8) { return (f8 - 1) & 1; }
+constexpr int f8_fmt_b(int f8) { return (f8 - 1) >> 1; }
+// K elements per LDS stage (128 bytes per row)
+constexpr int stage_k(int f8) { return f8 ? 128 : 64; }
 // Workgroup shape per tile size: 256x256 tiles use 8 waves (two per SIMD, so
 // one wave's LDS waits overlap the other's MFMAs), 128x128 tiles use 4.  The
 // waves form a (NT/128) x 2 grid; each wave owns 64 rows and BN/2 columns.
@@ -71,32 +84,42 @@ __device__ __forceinline__ v4s_t ds_read_tr(const char* lds_generic, int byte_of
 }
 
 // ---------------------------------------------------------------------------
-// global -> register staging of one operand tile (R rows x 64 k): R*8 chunks
-// of 16 B, R/32 per thread, for either layout.
+// global -> register staging of one operand tile (R rows x 128 bytes of k):
+// R*8 chunks of 16 B, R*8/NT per thread, for either layout.  ES = bytes per
+// element (2: bf16, 1: fp8 codes; fp8 tiles are k-contiguous only).
 // ---------------------------------------------------------------------------
-template <int R, bool KC, int NT>
+template <int R, bool KC, int NT, int ES = 2>
 struct TileLoader {
   static constexpr int kRegs = R * 8 / NT;
+  static constexpr int EPC = 16 / ES;   // elements per 16-byte chunk
+  static constexpr int KBK = 128 / ES;  // k elements per stage
+  static_assert(ES == 2 || KC, "fp8 operands must be k-contiguous");
   uint4 v[kRegs];
 
   template <bool GUARD>
-  __device__ __forceinline__ void load(const uint16_t* __restrict__ X, long long ld, int row0, int rows,
+  __device__ __forceinline__ void load(const void* __restrict__ Xv, long long ld, int row0, int rows,
                                        int k0, int K, int tid) {
-    const bool full = !GUARD || ((row0 + R <= rows) && (k0 + kBK <= K));
+    const char* __restrict__ Xb = reinterpret_cast<const char*>(Xv);
+    const uint16_t* __restrict__ X = reinterpret_cast<const uint16_t*>(Xv);
+    const bool full = !GUARD || ((row0 + R <= rows) && (k0 + KBK <= K));
 #pragma unroll
     for (int i = 0; i < kRegs; ++i) {
       const int c = tid + NT * i;
       int gr, gk;
       if constexpr (KC) {
         gr = row0 + (c >> 3);
-        gk = k0 + (c & 7) * 8;
+        gk = k0 + (c & 7) * EPC;
       } else {
         gk = k0 + c / (R / 8);
         gr = row0 + (c % (R / 8)) * 8;
       }
       const long long base = KC ? (long long)gr * ld + gk : (long long)gk * ld + gr;
       if (full) {
-        v[i] = *reinterpret_cast<const uint4*>(X + base);
+        v[i] = *reinterpret_cast<const uint4*>(Xb + base * ES);
+      } else if constexpr (ES == 1) {
+        // fp8: K is a multiple of 16 (checked on the host), so a chunk is
+        // either wholly inside the operand or wholly outside
+        v[i] = (gr < rows && gk < K) ? *reinterpret_cast<const uint4*>(Xb + base) : make_uint4(0, 0, 0, 0);
       } else {
         uint32_t w[4];
 #pragma unroll
@@ -120,8 +143,9 @@ struct TileLoader {
   // lane l of wave w in round i fills the 16-byte LDS slot 256 i + 64 w + l of
   // the tile, so each lane fetches the global chunk that the swizzled layout
   // places in that slot.
-  __device__ __forceinline__ static void load_direct(const uint16_t* __restrict__ X, long long ld, int row0,
+  __device__ __forceinline__ static void load_direct(const void* __restrict__ Xv, long long ld, int row0,
                                                      int k0, char* lds, int tid) {
+    const char* __restrict__ X = reinterpret_cast<const char*>(Xv);
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 #pragma unroll
     for (int i = 0; i < kRegs; ++i) {
@@ -129,7 +153,7 @@ struct TileLoader {
       long long src;
       if constexpr (KC) {
         const int r = slot >> 3, kc = (slot & 7) ^ ((r >> 1) & 7);
-        src = (long long)(row0 + r) * ld + k0 + kc * 8;
+        src = (long long)(row0 + r) * ld + k0 + kc * EPC;
       } else {
         const int b = slot * 16;
         const int k = b / (2 * R), rb = b % (2 * R);
@@ -138,7 +162,7 @@ struct TileLoader {
       }
       __attribute__((address_space(3))) char* dst =
           (__attribute__((address_space(3))) char*)(lds) + (NT * i + 64 * wave) * 16;
-      __builtin_amdgcn_global_load_lds((const void*)(X + src), (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void*)(X + src * ES), (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
     }
   }
 
@@ -167,6 +191,20 @@ struct TileLoader {
       f[4] = b[0]; f[5] = b[1]; f[6] = b[2]; f[7] = b[3];
       return f;
     }
+  }
+
+  // fp8 fragment of rows r0 .. r0+31, k-step ks (64 codes): lane l holds row
+  // r0 + l % 32 and the 32 codes of 16-byte chunks 4 ks + 2 (l / 32) + {0, 1}.
+  // (Any assignment of the 64 k values to (lane half, byte) works as long as
+  // both operands use the same one: the MFMA pairs equal positions.)
+  __device__ __forceinline__ static i32x8_t frag8(const char* lds, int r0, int ks, int lane) {
+    const int r = r0 + (lane & 31), c = ks * 4 + (lane >> 5) * 2;
+    const uint4 a = *reinterpret_cast<const uint4*>(lds + lds_off_k(r, c));
+    const uint4 b = *reinterpret_cast<const uint4*>(lds + lds_off_k(r, c + 1));
+    i32x8_t f;
+    f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w;
+    f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
+    return f;
   }
 };
 
@@ -275,48 +313,60 @@ __device__ __forceinline__ void epi4(const GemmArgs& p, int bi, int m, int n, co
 // and (for interior tiles, GUARD = false) an explicit interleave of MFMAs with
 // the global loads, LDS fragment reads and LDS stores of the same iteration.
 // ---------------------------------------------------------------------------
-template <int BM, int BN, bool AK, bool BKC, bool GUARD>
-__device__ __forceinline__ void mainloop(const GemmArgs& p, const uint16_t* A, const uint16_t* B, int m0, int n0,
+template <int BM, int BN, bool AK, bool BKC, bool GUARD, int F8>
+__device__ __forceinline__ void mainloop(const GemmArgs& p, const void* A, const void* B, int m0, int n0,
                                          int kt0, int nk, char* smem, int tid,
                                          f32x16_t (&acc)[Cfg<BM, BN>::TM][Cfg<BM, BN>::TN]) {
   constexpr int NT = Cfg<BM, BN>::NT;
   constexpr int WM = Cfg<BM, BN>::WM, WN = Cfg<BM, BN>::WN, TM = Cfg<BM, BN>::TM, TN = Cfg<BM, BN>::TN;
-  using LA = TileLoader<BM, AK, NT>;
-  using LB = TileLoader<BN, BKC, NT>;
+  constexpr int ES = F8 ? 1 : 2;
+  constexpr int KBK = stage_k(F8);
+  using LA = TileLoader<BM, AK, NT, ES>;
+  using LB = TileLoader<BN, BKC, NT, ES>;
+  using FragT = typename std::conditional<F8 != 0, i32x8_t, bf16x8_t>::type;
   constexpr int A_BYTES = BM * 128, STAGE = (BM + BN) * 128;
-  constexpr int KS = kBK / 16;
+  constexpr int KS = F8 ? 2 : 4;                                 // MFMA k-steps per stage
   constexpr int NM = TM * TN;                                    // MFMAs per k-step
-  constexpr int NV = LA::kRegs + LB::kRegs;  // global loads per tile
-  constexpr int ND = (AK ? 1 : 2) * TM + (BKC ? 1 : 2) * TN;     // LDS reads per k-step
+  constexpr int NV = LA::kRegs + LB::kRegs;                      // global loads per tile
+  constexpr int ND = F8 ? 2 * (TM + TN) : (AK ? 1 : 2) * TM + (BKC ? 1 : 2) * TN;  // LDS reads per k-step
   const int lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   if (nk <= 0) return;
 
+  auto frag_a = [&](const char* base, int r0, int ks) -> FragT {
+    if constexpr (F8) return LA::frag8(base, r0, ks, lane);
+    else return LA::frag(base, r0, ks, lane);
+  };
+  auto frag_b = [&](const char* base, int r0, int ks) -> FragT {
+    if constexpr (F8) return LB::frag8(base, r0, ks, lane);
+    else return LB::frag(base, r0, ks, lane);
+  };
+
   LA la;
   LB lb;
   if constexpr (GUARD) {
-    la.template load<true>(A, p.lda, m0, p.M, kt0 * kBK, p.K, tid);
-    lb.template load<true>(B, p.ldb, n0, p.N, kt0 * kBK, p.K, tid);
+    la.template load<true>(A, p.lda, m0, p.M, kt0 * KBK, p.K, tid);
+    lb.template load<true>(B, p.ldb, n0, p.N, kt0 * KBK, p.K, tid);
     la.store(smem, tid);
     lb.store(smem + A_BYTES, tid);
   } else {
-    LA::load_direct(A, p.lda, m0, kt0 * kBK, smem, tid);
-    LB::load_direct(B, p.ldb, n0, kt0 * kBK, smem + A_BYTES, tid);
+    LA::load_direct(A, p.lda, m0, kt0 * KBK, smem, tid);
+    LB::load_direct(B, p.ldb, n0, kt0 * KBK, smem + A_BYTES, tid);
   }
   __syncthreads();
 
-  bf16x8_t fa[2][TM], fb[2][TN];
+  FragT fa[2][TM], fb[2][TN];
 #pragma unroll
-  for (int i = 0; i < TM; ++i) fa[0][i] = LA::frag(smem, wm * WM + i * 32, 0, lane);
+  for (int i = 0; i < TM; ++i) fa[0][i] = frag_a(smem, wm * WM + i * 32, 0);
 #pragma unroll
-  for (int j = 0; j < TN; ++j) fb[0][j] = LB::frag(smem + A_BYTES, wn * WN + j * 32, 0, lane);
+  for (int j = 0; j < TN; ++j) fb[0][j] = frag_b(smem + A_BYTES, wn * WN + j * 32, 0);
 
   for (int kt = 0; kt < nk; ++kt) {
     const char* sa = smem + (kt & 1) * STAGE;
     const char* sb = sa + A_BYTES;
     char* so = smem + ((kt + 1) & 1) * STAGE;
     // next tile (the last iteration reloads its own tile: harmless, no branch)
-    const int kn = (kt0 + (kt + 1 < nk ? kt + 1 : kt)) * kBK;
+    const int kn = (kt0 + (kt + 1 < nk ? kt + 1 : kt)) * KBK;
     if constexpr (GUARD) {
       la.template load<true>(A, p.lda, m0, p.M, kn, p.K, tid);
       lb.template load<true>(B, p.ldb, n0, p.N, kn, p.K, tid);
@@ -330,15 +380,20 @@ __device__ __forceinline__ void mainloop(const GemmArgs& p, const uint16_t* A, c
       const int cur = ks & 1, nxt = cur ^ 1;
       if (ks + 1 < KS) {
 #pragma unroll
-        for (int i = 0; i < TM; ++i) fa[nxt][i] = LA::frag(sa, wm * WM + i * 32, ks + 1, lane);
+        for (int i = 0; i < TM; ++i) fa[nxt][i] = frag_a(sa, wm * WM + i * 32, ks + 1);
 #pragma unroll
-        for (int j = 0; j < TN; ++j) fb[nxt][j] = LB::frag(sb, wn * WN + j * 32, ks + 1, lane);
+        for (int j = 0; j < TN; ++j) fb[nxt][j] = frag_b(sb, wn * WN + j * 32, ks + 1);
       }
 #pragma unroll
       for (int i = 0; i < TM; ++i)
 #pragma unroll
-        for (int j = 0; j < TN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[cur][j], fa[cur][i], acc[i][j], 0, 0, 0);
+        for (int j = 0; j < TN; ++j) {
+          if constexpr (F8)
+            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                fb[cur][j], fa[cur][i], acc[i][j], f8_fmt_b(F8), f8_fmt_a(F8), 0, 127, 0, 127);
+          else
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[cur][j], fa[cur][i], acc[i][j], 0, 0, 0);
+        }
       if constexpr (GUARD) {
         if (ks + 1 == KS) {
           la.store(so, tid);
@@ -365,17 +420,17 @@ __device__ __forceinline__ void mainloop(const GemmArgs& p, const uint16_t* A, c
     }
     __syncthreads();
 #pragma unroll
-    for (int i = 0; i < TM; ++i) fa[0][i] = LA::frag(so, wm * WM + i * 32, 0, lane);
+    for (int i = 0; i < TM; ++i) fa[0][i] = frag_a(so, wm * WM + i * 32, 0);
 #pragma unroll
-    for (int j = 0; j < TN; ++j) fb[0][j] = LB::frag(so + A_BYTES, wn * WN + j * 32, 0, lane);
+    for (int j = 0; j < TN; ++j) fb[0][j] = frag_b(so + A_BYTES, wn * WN + j * 32, 0);
   }
 }
 
 // ---------------------------------------------------------------------------
 // the kernel
 // ---------------------------------------------------------------------------
-template <int BM, int BN, bool AK, bool BKC, int EPI>
-__global__ void __launch_bounds__((Cfg<BM, BN>::NT), 1) gemm_bf16_kernel(GemmArgs p) {
+template <int BM, int BN, bool AK, bool BKC, int EPI, int F8>
+__global__ void __launch_bounds__((Cfg<BM, BN>::NT), 1) gemm_kernel(GemmArgs p) {
   constexpr int WM = Cfg<BM, BN>::WM, WN = Cfg<BM, BN>::WN, TM = Cfg<BM, BN>::TM, TN = Cfg<BM, BN>::TN;
   constexpr int A_BYTES = BM * 128, B_BYTES = BN * 128, STAGE = A_BYTES + B_BYTES;
   __shared__ __attribute__((aligned(16))) char smem[2 * STAGE];
@@ -395,13 +450,15 @@ __global__ void __launch_bounds__((Cfg<BM, BN>::NT), 1) gemm_bf16_kernel(GemmArg
   const int m0 = tile_m * BM, n0 = tile_n * BN;
 
   const int bi = blockIdx.y / p.k_split, split = blockIdx.y % p.k_split;
-  const int nk_all = (p.K + kBK - 1) / kBK;
+  constexpr int KBK = stage_k(F8);
+  const int nk_all = (p.K + KBK - 1) / KBK;
   const int nk_per = (nk_all + p.k_split - 1) / p.k_split;
   const int kt0 = split * nk_per;
   const int nk = max(0, min(nk_all, kt0 + nk_per) - kt0);
 
-  const uint16_t* A = reinterpret_cast<const uint16_t*>(p.A) + (long long)bi * p.sA;
-  const uint16_t* B = reinterpret_cast<const uint16_t*>(p.B) + (long long)bi * p.sB;
+  constexpr int ES = F8 ? 1 : 2;
+  const char* A = reinterpret_cast<const char*>(p.A) + (long long)bi * p.sA * ES;
+  const char* B = reinterpret_cast<const char*>(p.B) + (long long)bi * p.sB * ES;
 
   f32x16_t acc[TM][TN];
 #pragma unroll
@@ -411,12 +468,22 @@ __global__ void __launch_bounds__((Cfg<BM, BN>::NT), 1) gemm_bf16_kernel(GemmArg
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
-  const bool fast = (m0 + BM <= p.M) && (n0 + BN <= p.N) && (p.K % kBK == 0);
+  const bool fast = (m0 + BM <= p.M) && (n0 + BN <= p.N) && (p.K % KBK == 0);
   if (fast)
-    mainloop<BM, BN, AK, BKC, false>(p, A, B, m0, n0, kt0, nk, smem, tid, acc);
+    mainloop<BM, BN, AK, BKC, false, F8>(p, A, B, m0, n0, kt0, nk, smem, tid, acc);
   else
-    mainloop<BM, BN, AK, BKC, true>(p, A, B, m0, n0, kt0, nk, smem, tid, acc);
+    mainloop<BM, BN, AK, BKC, true, F8>(p, A, B, m0, n0, kt0, nk, smem, tid, acc);
   const int lr = lane & 31, lh = lane >> 5;
+  if constexpr (F8 != 0) {
+    // dequantise: the codes carry x * s_x, so the product carries s_a * s_b
+    const float inv = 1.0f / (p.scale_a[0] * p.scale_b[0]);
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[i][j][e] *= inv;
+  }
 
   // ----------------------------- epilogue ---------------------------------
   if constexpr (EPI == EPI_QKV) {
@@ -546,12 +613,12 @@ __global__ void __launch_bounds__((Cfg<BM, BN>::NT), 1) gemm_bf16_kernel(GemmArg
   }
 }
 
-template <int BM, int BN, bool AK, bool BKC, int EPI>
+template <int BM, int BN, bool AK, bool BKC, int EPI, int F8 = 0>
 int launch_t(const GemmArgs& a, hipStream_t s) {
   const int tiles = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
   dim3 grid(tiles, a.batch * a.k_split);
-  hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, AK, BKC, EPI>), grid, dim3(Cfg<BM, BN>::NT), 0, s, a);
-  GS_LAUNCH_CHECK("gemm_bf16");
+  hipLaunchKernelGGL((gemm_kernel<BM, BN, AK, BKC, EPI, F8>), grid, dim3(Cfg<BM, BN>::NT), 0, s, a);
+  GS_LAUNCH_CHECK(std::string(F8 ? "gemm_fp8" : "gemm_bf16"));
   return 0;
 }
 
@@ -560,13 +627,13 @@ inline bool use_big_tile(const GemmArgs& a) {
   return a.M >= 256 && a.N >= 256 && big >= 512;
 }
 
-template <bool AK, bool BKC, int EPI>
+template <bool AK, bool BKC, int EPI, int F8 = 0>
 int launch_tiles(const GemmArgs& a, hipStream_t s) {
   if constexpr (EPI == EPI_QKV) {
-    return launch_t<256, 256, AK, BKC, EPI>(a, s);
+    return launch_t<256, 256, AK, BKC, EPI, F8>(a, s);
   } else {
-    if (use_big_tile(a)) return launch_t<256, 256, AK, BKC, EPI>(a, s);
-    return launch_t<128, 128, AK, BKC, EPI>(a, s);
+    if (use_big_tile(a)) return launch_t<256, 256, AK, BKC, EPI, F8>(a, s);
+    return launch_t<128, 128, AK, BKC, EPI, F8>(a, s);
   }
 }
 

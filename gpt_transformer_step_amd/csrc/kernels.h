@@ -45,6 +45,20 @@ int launch_attn_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, lon
                     float* delta, float* dq, uint16_t* dk, uint16_t* dv, long long ld_dkv, int B,
                     int H, int T, hipStream_t s);
 
+// --- fp8 quantisation (fp8.hip) --------------------------------------------
+// Tensors are [rows, cols] with row stride ld (elements); rows % 16 == 0,
+// cols % 16 == 0, rows * cols / 4 < 2^31.  fmt 0 = E4M3, 1 = E5M2.
+constexpr int kFp8Partials = 1024;  // floats of `partial` scratch per tensor
+int fp8_partials(long long rows, long long cols);
+// scale[0] = fmax / max|x| (1 when x == 0)
+int launch_fp8_amax_scale(const void* x, int is_f32, long long ldx, int rows, int cols, int fmt, float* partial,
+                          float* scale, hipStream_t s);
+// q[r, c] = code(x[r, c] * scale) and / or qt[c, r] = the same code (each nullable)
+int launch_fp8_quant(const void* x, int is_f32, long long ldx, int rows, int cols, int fmt, const float* scale,
+                     uint8_t* q, long long ldq, uint8_t* qt, long long ldqt, hipStream_t s);
+int quantize_fp8(const void* x, int is_f32, long long ldx, int rows, int cols, int fmt, float* partial, float* scale,
+                 uint8_t* q, long long ldq, uint8_t* qt, long long ldqt, hipStream_t s);
+
 // --- roofline probes (probe.hip) -------------------------------------------
 int launch_mfma_peak(int fp8, int blocks, int iters, float* out, double* flops, hipStream_t s);
 

@@ -35,6 +35,36 @@ gpt_status gpt_op_gemm(int32_t M, int32_t N, int32_t K, int32_t batch, const uin
                        int32_t b_layout, int64_t ldb, int64_t stride_b, void* C, int32_t c_dtype,
                        int64_t ldc, int64_t stride_c, float alpha, float beta, gpt_stream_t stream);
 
+/* fp8 formats (OCP): E4M3 (largest finite 448, no infinities) and E5M2
+ * (largest finite 57344). */
+enum { GPT_FP8_E4M3 = 0, GPT_FP8_E5M2 = 1 };
+
+/* Per-tensor fp8 quantisation (apidog.com/pt "Gerenciamento de Precisão",
+ * apidog.com/de "Präzisionsverwaltung": fp8 linear layers with one scale per
+ * tensor).  x: [rows, cols] row-major with leading dimension ldx (elements),
+ * bf16 (x_dtype = GPT_DTYPE_BF16) or fp32 (GPT_DTYPE_F32).
+ *   scale[0] = fmax / max|x|  (fp32 division; 1 when x is all zero)
+ *   code     = round-to-nearest-even(clamp(x * scale, -fmax, fmax))
+ * q (nullable): codes [rows, cols] with leading dimension ldq;
+ * qt (nullable): the same codes transposed, [cols, rows], leading dimension ldqt.
+ * partial: device fp32 scratch of gpt_fp8_partials(rows, cols) floats.
+ * Needs rows % 16 == 0, cols % 16 == 0, rows*cols < 2^33, ldx % 4 == 0,
+ * ldq % 4 == 0, ldqt % 16 == 0; x 16-byte aligned (fp32) or 8-byte (bf16). */
+int32_t gpt_fp8_partials(int32_t rows, int32_t cols);
+gpt_status gpt_op_quantize_fp8(const void* x, int32_t x_dtype, int64_t ldx, int32_t rows, int32_t cols,
+                               int32_t fmt, float* scale, uint8_t* q, int64_t ldq, uint8_t* qt,
+                               int64_t ldqt, float* partial, gpt_stream_t stream);
+
+/* fp8 matrix product with fp32 accumulation, both operands k-contiguous:
+ *   C[m, n] = sum_k dec(A[m, k]) dec(B[n, k]) / (scale_a[0] * scale_b[0])  (+ beta * C[m, n])
+ * A: codes [M, K] (format fmt_a, leading dimension lda); B: codes [N, K]
+ * (format fmt_b, ldb); C fp32 [M, N] (ldc); scale_a, scale_b: device fp32
+ * scalars (the quantisation scales of the two operands).  K % 16 == 0, lda
+ * and ldb multiples of 16, ldc of 4; pointers 16-byte aligned. */
+gpt_status gpt_op_gemm_fp8(int32_t M, int32_t N, int32_t K, const uint8_t* A, int32_t fmt_a, int64_t lda,
+                           const uint8_t* B, int32_t fmt_b, int64_t ldb, float* C, int64_t ldc,
+                           const float* scale_a, const float* scale_b, float beta, gpt_stream_t stream);
+
 /* Causal multi-head attention forward with head width 128 (dev.to page,
  * "5. Unificación Flash Attention": flash_attn_func(q, k, v, causal=True)):
  *   out[b,t,h,:] = sum_{j<=t} softmax_j(q[b,t,h,:] . k[b,j,h,:] / sqrt(128)) v[b,j,h,:]

@@ -132,3 +132,27 @@ def test_gemm_rejects_on_host(B):
 def test_profile_categories(B):
     cats = B.profile_categories()
     assert "attn_fwd" in cats and "gemm_fc_relu2_fwd" in cats and len(set(cats)) == len(cats)
+
+
+def test_fp8_ops_reject_on_host(B):
+    lib = B.lib()
+    fake = ctypes.c_void_p(4096)
+    # rows not a multiple of 16
+    rc = lib.gpt_op_quantize_fp8(fake, 1, 64, 8, 64, 0, fake, fake, 64, None, 0, fake, None)
+    assert rc == -1
+    rc = lib.gpt_op_quantize_fp8(fake, 1, 64, 16, 64, 2, fake, fake, 64, None, 0, fake, None)
+    assert rc == -5   # unknown format
+    rc = lib.gpt_op_quantize_fp8(fake, 1, 64, 16, 64, 0, None, fake, 64, None, 0, fake, None)
+    assert rc == -1   # scale is NULL
+    rc = lib.gpt_op_gemm_fp8(64, 64, 24, fake, 0, 32, fake, 0, 32, fake, 64, fake, fake, 0.0, None)
+    assert rc == -1   # K not a multiple of 16
+    rc = lib.gpt_op_gemm_fp8(64, 64, 32, fake, 0, 32, fake, 0, 32, fake, 64, None, fake, 0.0, None)
+    assert rc == -1   # scale_a NULL
+    assert lib.gpt_op_gemm_fp8(0, 64, 32, None, 0, 32, None, 0, 32, None, 64, None, None, 0.0, None) == 0
+    assert B.fp8_partials(65536, 1280) == 1024 and B.fp8_partials(16, 16) == 1
+
+
+def test_fp8_workspace_is_larger(B):
+    bf = B.workspace_size(B.shape(4, 4096, 256, 2, B.PREC_BF16))
+    f8 = B.workspace_size(B.shape(4, 4096, 256, 2, B.PREC_FP8))
+    assert f8 > bf

@@ -1,0 +1,203 @@
+"""fp8 path on the GPU: per-tensor quantiser, fp8 GEMM, and the whole step at
+GPT_PREC_FP8 against the oracle's fp8 fake-quant mode.
+
+* Quantiser: codes and scale bit-exact against oracle/fp8.py on the same
+  values (amax, the fp32 scale fmax / amax, the fp32 product x * s, then
+  saturate + round to nearest even), plain and transposed layouts.
+* GEMM: against the float64 product of the decoded codes divided by the two
+  scales: rel L2 <= 2e-4.  The fp8 x fp8 products are exact, but the gfx950
+  fp8 MFMA sums each 64-wide block of products with a narrower internal
+  alignment than fp32: on random codes spanning the whole fp8 range the
+  result moves by 2e-5 .. 5e-5 relative, the same for K = 16 and K = 512
+  (so it is per block, not accumulated), and it is not subnormal flushing
+  (the diagnostic below compares both).  That is far below fp8's own
+  quantisation step (2^-4 relative for E4M3).
+* Step: the GPU computes with bf16 activations feeding the fp8 quantiser, so
+  its closest definition is the oracle with fp8=True and bf16_operands=True.
+  Bars per quantity: loss relative error and lse / gradient rel L2 <=
+  max(1e-2, 1.5 F8), where F8 is the distance between that oracle and the
+  fp8 oracle without bf16 rounding (the code flips that bf16 rounding alone
+  causes), and gradient cosine >= min(0.999, 1 - 1.5 (1 - c8)) with c8 the
+  cosine between those two oracles.  Against the exact oracle (no fp8) the
+  bar is max(5e-2, 1.5 Q), Q being the fp8 oracle's own distance from the
+  exact one.  Per-tensor E5M2 gradients are coarse (2 mantissa bits): at
+  depth 2 the fp8 oracle is 10-20 % (rel L2) from the exact gradients, and
+  rounding the activations to bf16 before quantising moves them by a similar
+  amount, so a fixed 0.999 cosine would reject the method itself.  A wrong
+  scale, transpose or format would still move them by O(1).
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from gpu_util import cosine, rel_l2, say, to_dev_bf16
+from oracle import fp8 as ofp8
+from step_util import StepRun, oracle_run
+
+pytestmark = pytest.mark.gpu
+
+FMTS = {0: "e4m3", 1: "e5m2"}
+
+
+def _B():
+    from gpt_transformer_step_amd import binding
+    return binding
+
+
+def _values(rows, cols, seed, dtype):
+    g = np.random.default_rng(seed)
+    x = g.standard_normal((rows, cols)) * np.exp(g.uniform(-6, 3, (rows, 1)))
+    x[0, :3] = 0.0
+    if dtype == "bf16":
+        from oracle import precision
+        return precision.round_bf16(x.astype(np.float32)).astype(np.float64)
+    return x.astype(np.float32).astype(np.float64)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("fmt", [0, 1])
+@pytest.mark.parametrize("rows,cols", [(64, 128), (208, 272), (1024, 1280)])
+def test_quantize_bitexact(dtype, fmt, rows, cols):
+    B = _B()
+    say(f"quantize {dtype} {FMTS[fmt]} {rows}x{cols}")
+    x = _values(rows, cols, rows * 7 + cols + fmt, dtype)
+    dx = to_dev_bf16(x) if dtype == "bf16" else torch.from_numpy(x.astype(np.float32)).cuda()
+    q = torch.zeros((rows, cols), dtype=torch.uint8, device="cuda")
+    qt = torch.zeros((cols, rows), dtype=torch.uint8, device="cuda")
+    scale = torch.zeros(1, dtype=torch.float32, device="cuda")
+    part = torch.empty(B.fp8_partials(rows, cols), dtype=torch.float32, device="cuda")
+    B.quantize_fp8(dx, fmt, scale, part, q=q, qt=qt)
+    torch.cuda.synchronize()
+    s = ofp8.tensor_scale(x, FMTS[fmt])
+    codes = ofp8.encode((x.astype(np.float32) * s).astype(np.float64), FMTS[fmt])
+    assert float(scale.item()) == float(s)
+    got = q.cpu().numpy()
+    assert np.array_equal(got, codes), f"{np.sum(got != codes)} codes differ"
+    assert np.array_equal(qt.cpu().numpy(), codes.T)
+
+
+def test_quantize_zero_tensor():
+    B = _B()
+    x = torch.zeros((32, 64), dtype=torch.bfloat16, device="cuda")
+    q = torch.full((32, 64), 7, dtype=torch.uint8, device="cuda")
+    scale = torch.zeros(1, dtype=torch.float32, device="cuda")
+    part = torch.empty(B.fp8_partials(32, 64), dtype=torch.float32, device="cuda")
+    B.quantize_fp8(x, 0, scale, part, q=q)
+    torch.cuda.synchronize()
+    assert float(scale.item()) == 1.0
+    assert int(q.max().item()) == 0
+
+
+def _random_codes(g, shape, fmt):
+    c = g.integers(0, 256, size=shape, dtype=np.int64)
+    # no NaN / infinity codes
+    if fmt == 0:
+        c = np.where((c & 0x7f) == 0x7f, c - 1, c)
+    else:
+        c = np.where((c & 0x7c) == 0x7c, c & 0xbb, c)
+    return c.astype(np.uint8)
+
+
+@pytest.mark.parametrize("fa,fb", [(0, 0), (1, 0), (0, 1), (1, 1)])
+@pytest.mark.parametrize("M,N,K", [(256, 256, 512), (300, 200, 144), (130, 72, 16), (8192, 4096, 256)])
+def test_gemm_fp8(fa, fb, M, N, K):
+    B = _B()
+    say(f"gemm_fp8 {FMTS[fa]} x {FMTS[fb]} M={M} N={N} K={K}")
+    g = np.random.default_rng(M + N + K + 10 * fa + 20 * fb)
+    A = _random_codes(g, (M, K), fa)
+    Bm = _random_codes(g, (N, K), fb)
+    sa, sb = np.float32(3.0), np.float32(0.375)
+    dA = torch.from_numpy(A).cuda()
+    dB = torch.from_numpy(Bm).cuda()
+    C = torch.full((M, N), 0.5, dtype=torch.float32, device="cuda")
+    dsa = torch.tensor([sa], dtype=torch.float32, device="cuda")
+    dsb = torch.tensor([sb], dtype=torch.float32, device="cuda")
+    beta = 0.25 if M < 1000 else 0.0
+    B.gemm_fp8(dA, fa, dB, fb, C, M, N, K, dsa, dsb, beta=beta)
+    torch.cuda.synchronize()
+    da, db = ofp8.decode(A, FMTS[fa]), ofp8.decode(Bm, FMTS[fb])
+    ref = da @ db.T / (float(sa) * float(sb)) + beta * 0.5
+    got = C.cpu().numpy().astype(np.float64)
+    e = rel_l2(got, ref)
+    # diagnostics: the same product with subnormal codes flushed to zero
+    sub_a = (A & (0x78 if fa == 0 else 0x7c)) == 0
+    sub_b = (Bm & (0x78 if fb == 0 else 0x7c)) == 0
+    ref_ftz = np.where(sub_a, 0.0, da) @ np.where(sub_b, 0.0, db).T / (float(sa) * float(sb)) + beta * 0.5
+    say(f"  rel_l2 {e:.2e} (vs subnormals flushed: {rel_l2(got, ref_ftz):.2e}; flush itself moves "
+        f"{rel_l2(ref_ftz, ref):.2e})")
+    assert e <= 2e-4
+
+
+CONFIGS = [
+    # depth, vocab, seq_len, batch
+    (2, 32768, 128, 2),
+    (2, 1000, 100, 4),    # ragged T and V; B*T = 400 is a multiple of 16
+    (4, 4096, 256, 2),
+]
+
+
+def _bar(e, floor, base):
+    return e <= max(base, 1.5 * floor)
+
+
+@pytest.mark.parametrize("depth,vocab,T,Bn", CONFIGS)
+def test_step_fp8_parity(depth, vocab, T, Bn):
+    B = _B()
+    say(f"fp8 step parity depth={depth} V={vocab} T={T} B={Bn}")
+    run = StepRun(depth, vocab, T, Bn, precision_flag=B.PREC_FP8)
+    run.fwd()
+    run.bwd()
+    torch.cuda.synchronize()
+    loss = float(run.loss.item())
+    lse = run.row_lse.cpu().numpy().astype(np.float64)
+    grads = run.grads()
+
+    ref = oracle_run(run, fp8=True, bf16_operands=True)     # closest definition
+    f8x = oracle_run(run, fp8=True)                         # fp8 without bf16 rounding
+    exact = oracle_run(run)                                 # no fp8, no rounding
+    say(f"  loss gpu {loss:.6f}  fp8+bf16 oracle {ref['loss']:.6f}  fp8 oracle {f8x['loss']:.6f}  "
+        f"exact {exact['loss']:.6f}")
+    fl = abs(ref["loss"] - f8x["loss"]) / abs(ref["loss"])
+    assert _bar(abs(loss - ref["loss"]) / abs(ref["loss"]), fl, 1e-2)
+    q_l = abs(ref["loss"] - exact["loss"]) / abs(exact["loss"])
+    assert _bar(abs(loss - exact["loss"]) / abs(exact["loss"]), q_l, 5e-2)
+    e_lse = rel_l2(lse, ref["lse"])
+    say(f"  lse rel_l2 vs fp8 oracle {e_lse:.2e}")
+    assert _bar(e_lse, rel_l2(ref["lse"], f8x["lse"]), 1e-2)
+
+    bad, worst = [], (0.0, "")
+    for name, r in ref["grads"].items():
+        g = np.asarray(grads[name], dtype=np.float64)
+        assert np.all(np.isfinite(g)), name
+        e, c = rel_l2(g, r), cosine(g, r)
+        floor = rel_l2(r, f8x["grads"][name])
+        tol = max(1e-2, 1.5 * floor)
+        cos_min = min(0.999, 1.0 - 1.5 * (1.0 - cosine(r, f8x["grads"][name])))
+        ex = exact["grads"][name]
+        e_x = rel_l2(g, ex)
+        q = rel_l2(r, ex)
+        tol_x = max(5e-2, 1.5 * q)
+        if e / tol > worst[0]:
+            worst = (e / tol, f"{name}: rel_l2 {e:.2e} (floor {floor:.2e}) cos {c:.6f}; vs exact {e_x:.2e} "
+                              f"(fp8 oracle {q:.2e})")
+        if not (e <= tol and c >= cos_min and e_x <= tol_x):
+            bad.append(f"{name}: rel_l2 {e:.2e} (floor {floor:.2e}) cos {c:.6f}; vs exact {e_x:.2e} "
+                       f"(fp8 oracle {q:.2e})")
+    say(f"  worst gradient vs its bar: {worst[1]}")
+    assert not bad, bad
+
+
+def test_fp8_rejects_ragged_token_count():
+    B = _B()
+    sh = B.shape(2, 1000, 100, 3, B.PREC_FP8)   # 300 tokens, not a multiple of 16
+    ws = torch.empty(B.workspace_size(sh), dtype=torch.uint8, device="cuda")
+    n = B.param_count(sh)
+    master = torch.zeros(n, dtype=torch.float32, device="cuda")
+    bf = torch.zeros(n, dtype=torch.bfloat16, device="cuda")
+    params = B.make_params(master, bf, master)
+    ids = torch.zeros((3, 101), dtype=torch.int32, device="cuda")
+    loss = torch.zeros(1, dtype=torch.float32, device="cuda")
+    with pytest.raises(B.GptError) as e:
+        B.step_fwd(sh, params, ids, loss, ws)
+    assert e.value.code == -5
