@@ -66,7 +66,10 @@ def kernel_flops(name, depth, V, T, B):
     table = {
         "gemm_qkv_rope_fwd": 2.0 * N * 3 * d * d, "gemm_o_fwd": 2.0 * N * d * d,
         "gemm_fc_relu2_fwd": 2.0 * N * hid * d, "gemm_proj_fwd": 2.0 * N * d * hid,
-        "gemm_ce_fwd": 2.0 * N * V * d, "attn_fwd": attn, "attn_bwd": 2 * attn,
+        "gemm_ce_fwd": 2.0 * N * V * d, "attn_fwd": attn,
+        # backward: dV, dP, dK in the dK/dV kernel, dQ in the dQ kernel (recomputed
+        # scores and the dQ kernel's second dP are not counted)
+        "attn_bwd_dkdv": 1.5 * attn, "attn_bwd_dq": 0.5 * attn,
         "gemm_proj_dgrad": 2.0 * N * d * hid, "gemm_proj_wgrad": 2.0 * N * d * hid,
         "gemm_fc_dgrad": 2.0 * N * d * hid, "gemm_fc_wgrad": 2.0 * N * d * hid,
         "gemm_o_dgrad": 2.0 * N * d * d, "gemm_o_wgrad": 2.0 * N * d * d,
@@ -84,6 +87,22 @@ def block_gemm_flops(depth, T, B):
     """FLOPs of the four block products per layer, forward and backward."""
     d, _, _ = shapes(depth)
     return 6 * 12 * depth * d * d * B * T
+
+
+def measured_traffic(category):
+    """HBM bytes per launch of a kernel category from the committed rocprofv3
+    counter summary (profiles/traffic.json), or None when there is none or the
+    kernel's source changed since the counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        rec = json.load(open(path)).get(category)
+        if rec is None:
+            return None
+        sha = hashlib.sha256(open(os.path.join(ROOT, rec["source"]), "rb").read()).hexdigest()
+        return rec["hbm_bytes_per_launch"] if sha == rec["source_sha256"] else None
+    except (OSError, ValueError, KeyError):
+        return None
 
 
 def cpu_baseline(wl, depth, V, T, B, seed_ids, seed_w):
@@ -130,7 +149,20 @@ def main():
     ap.add_argument("--precision", default="bf16", choices=["bf16", "fp8"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--breakdown", action="store_true", help="print per-kernel times to stderr")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                    help="only run a plain device-to-device copy of BYTES three times and exit (the reference "
+                         "for scaling the HBM byte counters of a profiler)")
     args = ap.parse_args()
+    if args.copy_calibration:
+        import torch
+        n = args.copy_calibration // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read": 4 * n, "copy_bytes_written": 4 * n, "copies": 3}), flush=True)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the step runs on a "
               f"single MI355X with no collectives)", file=sys.stderr)
@@ -180,10 +212,12 @@ def main():
                            W_bf16=bf16[st:st + size].view(view), M=gr["M"], lr=0.02, momentum=0.95,
                            weight_decay=0.0)
 
+    print(f"bench: inputs resident ({args.workload}, {args.precision}); warm-up", file=sys.stderr, flush=True)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
     first_loss = float(loss.item())
+    print("bench: warm-up done; per-category pass", file=sys.stderr, flush=True)
 
     # per-kernel-category pass (untimed) to find the dominant kernel
     cats = Bd.profile_categories()
@@ -202,6 +236,7 @@ def main():
     dom = max(contractions, key=lambda c: contractions[c][0])
     dom_idx = cats.index(dom)
 
+    print(f"bench: dominant contraction {dom}; timed steps", file=sys.stderr, flush=True)
     # timed region: K steps; the dominant kernel bracketed by HIP events on its launch stream
     Bd.profile_enable(1 << dom_idx)
     e0 = torch.cuda.Event(enable_timing=True)
@@ -253,7 +288,7 @@ def main():
         "tflops": (f_model + f_ns) / step_s / 1e12,
         "loss": [first_loss, last_loss],
         "roofline": {"bound": "mfma", "kernel": dom, "achieved": achieved, "peak": peak,
-                     "unit": "TFLOP/s", "frac": achieved / peak, "traffic": None,
+                     "unit": "TFLOP/s", "frac": achieved / peak, "traffic": measured_traffic(dom),
                      "flops_per_launch": kf, "avg_launch_ms": avg_launch_s * 1e3,
                      "launches": dom_cnt},
         "breakdown_ms_per_step": {k: round(v[0], 3) for k, v in sorted(breakdown.items(), key=lambda kv: -kv[1][0])},

@@ -540,21 +540,37 @@ int launch_attn_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, lon
   return 0;
 }
 
+int launch_attn_bwd_part(int part, const uint16_t* q, const uint16_t* k, const uint16_t* v, long long ld_qkv,
+                         const uint16_t* out, const uint16_t* dout, long long ld_out, const float* lse, float* delta,
+                         float* dq, uint16_t* dk, uint16_t* dv, long long ld_dkv, int B, int H, int T,
+                         hipStream_t s) {
+  if (B <= 0 || T <= 0) return 0;
+  if (part == 0) {
+    const long long NH = (long long)B * T * H;
+    hipLaunchKernelGGL(attn_bwd_pre_kernel, dim3((unsigned)((NH + 3) / 4)), dim3(256), 0, s, out, dout, ld_out,
+                       delta, H, T, NH);
+    GS_LAUNCH_CHECK("attn_bwd_pre");
+  } else if (part == 1) {
+    hipLaunchKernelGGL(attn_bwd_kv_kernel, dim3((T + KV_KEYS - 1) / KV_KEYS, B * H), dim3(256), 0, s, q, k, v,
+                       ld_qkv, dout, ld_out, lse, delta, dk, dv, ld_dkv, H, T);
+    GS_LAUNCH_CHECK("attn_bwd_kv");
+  } else {
+    hipLaunchKernelGGL(attn_bwd_q_kernel, dim3((T + DQ_Q - 1) / DQ_Q, B * H), dim3(256), 0, s, q, k, v, ld_qkv,
+                       dout, ld_out, lse, delta, dq, H, T);
+    GS_LAUNCH_CHECK("attn_bwd_q");
+  }
+  return 0;
+}
+
 int launch_attn_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, long long ld_qkv,
                     const uint16_t* out, const uint16_t* dout, long long ld_out, const float* lse, float* delta,
                     float* dq, uint16_t* dk, uint16_t* dv, long long ld_dkv, int B, int H, int T,
                     hipStream_t s) {
-  if (B <= 0 || T <= 0) return 0;
-  const long long NH = (long long)B * T * H;
-  hipLaunchKernelGGL(attn_bwd_pre_kernel, dim3((unsigned)((NH + 3) / 4)), dim3(256), 0, s, out, dout, ld_out,
-                     delta, H, T, NH);
-  GS_LAUNCH_CHECK("attn_bwd_pre");
-  hipLaunchKernelGGL(attn_bwd_kv_kernel, dim3((T + KV_KEYS - 1) / KV_KEYS, B * H), dim3(256), 0, s, q, k, v,
-                     ld_qkv, dout, ld_out, lse, delta, dk, dv, ld_dkv, H, T);
-  GS_LAUNCH_CHECK("attn_bwd_kv");
-  hipLaunchKernelGGL(attn_bwd_q_kernel, dim3((T + DQ_Q - 1) / DQ_Q, B * H), dim3(256), 0, s, q, k, v, ld_qkv,
-                     dout, ld_out, lse, delta, dq, H, T);
-  GS_LAUNCH_CHECK("attn_bwd_q");
+  for (int part = 0; part < 3; ++part) {
+    const int rc = launch_attn_bwd_part(part, q, k, v, ld_qkv, out, dout, ld_out, lse, delta, dq, dk, dv, ld_dkv, B,
+                                        H, T, s);
+    if (rc) return rc;
+  }
   return 0;
 }
 

@@ -44,6 +44,11 @@ int launch_attn_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, lon
                     const uint16_t* out, const uint16_t* dout, long long ld_out, const float* lse,
                     float* delta, float* dq, uint16_t* dk, uint16_t* dv, long long ld_dkv, int B,
                     int H, int T, hipStream_t s);
+// one of the three backward kernels: 0 = delta = rowsum(dout * out), 1 = dK/dV, 2 = dQ
+int launch_attn_bwd_part(int part, const uint16_t* q, const uint16_t* k, const uint16_t* v, long long ld_qkv,
+                         const uint16_t* out, const uint16_t* dout, long long ld_out, const float* lse, float* delta,
+                         float* dq, uint16_t* dk, uint16_t* dv, long long ld_dkv, int B, int H, int T,
+                         hipStream_t s);
 
 // --- fp8 quantisation (fp8.hip) --------------------------------------------
 // Tensors are [rows, cols] with row stride ld (elements); rows % 16 == 0,
