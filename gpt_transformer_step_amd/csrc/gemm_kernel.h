@@ -198,12 +198,15 @@ struct TileLoader {
   // (Any assignment of the 64 k values to (lane half, byte) works as long as
   // both operands use the same one: the MFMA pairs equal positions.)
   __device__ __forceinline__ static i32x8_t frag8(const char* lds, int r0, int ks, int lane) {
+    // native vector loads (a struct-typed load here makes the compiler wait
+    // for every direct global -> LDS load in flight before the read)
+    typedef int i32x4_t __attribute__((ext_vector_type(4)));
     const int r = r0 + (lane & 31), c = ks * 4 + (lane >> 5) * 2;
-    const uint4 a = *reinterpret_cast<const uint4*>(lds + lds_off_k(r, c));
-    const uint4 b = *reinterpret_cast<const uint4*>(lds + lds_off_k(r, c + 1));
+    const i32x4_t a = *reinterpret_cast<const i32x4_t*>(lds + lds_off_k(r, c));
+    const i32x4_t b = *reinterpret_cast<const i32x4_t*>(lds + lds_off_k(r, c + 1));
     i32x8_t f;
-    f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w;
-    f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
+    f[0] = a[0]; f[1] = a[1]; f[2] = a[2]; f[3] = a[3];
+    f[4] = b[0]; f[5] = b[1]; f[6] = b[2]; f[7] = b[3];
     return f;
   }
 };
