@@ -432,7 +432,12 @@ WS ws_layout(const Dims& D) {
     w.dyq = take(N * hd);
     w.dyqt = take(N * hd);
     w.scales = take((size_t)D.L * SC_COUNT * 4);
-    w.qpart = take((size_t)kFp8Partials * 4);
+    // amax partials: the standalone reduction, one per row (norm kernels), or
+    // one per wave of the [N, 4d] bf16 products
+    GemmArgs ga;
+    ga.M = (int)D.N; ga.N = D.hidden; ga.K = d;
+    const long long slots = std::max<long long>(std::max<long long>(kFp8Partials, (long long)D.N), gemm_amax_slots(ga));
+    w.qpart = take((size_t)slots * 4);
   }
   w.total = o;
   return w;
@@ -598,9 +603,11 @@ extern "C" gpt_status gpt_step_fwd(const gpt_shape* shape, const gpt_params* par
   // y (op)= X W^T for one block product: bf16 operands, or (fp8) the E4M3 codes
   // of X (quantised here; the transposed codes are kept for the weight
   // gradient) and of W
-  auto quant_x = [&](const uint16_t* X, int K, size_t xt_off, float* sx) -> int {
+  // np > 0: the producer already wrote np amax partials into qpart
+  auto quant_x = [&](const uint16_t* X, int K, size_t xt_off, float* sx, long long np) -> int {
     if (!f8) return 0;
     ProfScope ps_(P_FP8_QUANT, s);
+    if (np > 0) return quantize_fp8_partials(X, 0, K, N, K, 0, qpart, np, sx, xq, K, at<uint8_t>(ws, xt_off), N, s);
     return quantize_fp8(X, 0, K, N, K, 0, qpart, sx, xq, K, at<uint8_t>(ws, xt_off), N, s);
   };
   auto block_fwd = [&](GemmArgs& a, int epi, int K, const uint8_t* w8, const float* sx, const float* sw) -> int {
@@ -610,6 +617,7 @@ extern "C" gpt_status gpt_step_fwd(const gpt_shape* shape, const gpt_params* par
     return gemm_fp8(a, epi, 0, 0, s);
   };
   { ProfScope ps_(P_EMBED_FWD, s); TRY(launch_embed_fwd(ids, W + P.wte, x, D.B, D.T, d, s)); }
+  long long act_slots = 0;
   for (int l = 0; l < D.L; ++l) {
     const Layer& L = w.layer[l];
     float* sc = f8 ? at<float>(ws, w.scales) + (size_t)l * SC_COUNT : nullptr;
@@ -618,8 +626,8 @@ extern "C" gpt_status gpt_step_fwd(const gpt_shape* shape, const gpt_params* par
     uint16_t* att = at<uint16_t>(ws, L.att);
     uint16_t* h2 = at<uint16_t>(ws, L.h2);
     uint16_t* act = at<uint16_t>(ws, L.act);
-    { ProfScope ps_(P_RMSNORM_FWD, s); TRY(launch_rmsnorm_fwd(x, h1, at<float>(ws, L.r1), N, d, s)); }
-    TRY(quant_x(h1, d, L.h1t, sc ? sc + SC_H1 : nullptr));
+    { ProfScope ps_(P_RMSNORM_FWD, s); TRY(launch_rmsnorm_fwd(x, h1, at<float>(ws, L.r1), N, d, s, qpart)); }
+    TRY(quant_x(h1, d, L.h1t, sc ? sc + SC_H1 : nullptr, N));
     {
       GemmArgs a;  // [q | k | v] = h1 [Wq; Wk; Wv]^T, q and k rotated and RMS-normalised per head
       ProfScope ps_(P_GEMM_QKV, s);
@@ -632,7 +640,7 @@ extern "C" gpt_status gpt_step_fwd(const gpt_shape* shape, const gpt_params* par
                     sc ? sc + SC_WQKV : nullptr));
     }
     { ProfScope ps_(P_ATTN_FWD, s); TRY(launch_attn_fwd(qkv, qkv + d, qkv + 2 * d, 3 * d, att, d, at<float>(ws, L.lse), D.B, D.H, D.T, s)); }
-    TRY(quant_x(att, d, L.attt, sc ? sc + SC_ATT : nullptr));
+    TRY(quant_x(att, d, L.attt, sc ? sc + SC_ATT : nullptr, 0));
     {
       GemmArgs a;  // x += att Wo^T
       ProfScope ps_(P_GEMM_O, s);
@@ -642,18 +650,20 @@ extern "C" gpt_status gpt_step_fwd(const gpt_shape* shape, const gpt_params* par
       TRY(block_fwd(a, EPI_RESID, d, f8 ? at<uint8_t>(ws, L.wo8) : nullptr, sc ? sc + SC_ATT : nullptr,
                     sc ? sc + SC_WO : nullptr));
     }
-    { ProfScope ps_(P_RMSNORM_FWD, s); TRY(launch_rmsnorm_fwd(x, h2, at<float>(ws, L.r2), N, d, s)); }
-    TRY(quant_x(h2, d, L.h2t, sc ? sc + SC_H2 : nullptr));
+    { ProfScope ps_(P_RMSNORM_FWD, s); TRY(launch_rmsnorm_fwd(x, h2, at<float>(ws, L.r2), N, d, s, qpart)); }
+    TRY(quant_x(h2, d, L.h2t, sc ? sc + SC_H2 : nullptr, N));
     {
       GemmArgs a;  // act = relu(h2 Wfc^T)^2
       ProfScope ps_(P_GEMM_FC, s);
       a.M = N; a.N = hid; a.K = d;
       a.A = h2; a.lda = d; a.B = W + P.fc(D, l); a.ldb = d;
       a.C = act; a.ldc = hid;
+      a.amax = qpart;  // NULL for bf16
+      act_slots = f8 ? gemm_amax_slots(a) : 0;
       TRY(block_fwd(a, EPI_RELU2, d, f8 ? at<uint8_t>(ws, L.wfc8) : nullptr, sc ? sc + SC_H2 : nullptr,
                     sc ? sc + SC_WFC : nullptr));
     }
-    TRY(quant_x(act, hid, L.actt, sc ? sc + SC_ACT : nullptr));
+    TRY(quant_x(act, hid, L.actt, sc ? sc + SC_ACT : nullptr, act_slots));
     {
       GemmArgs a;  // x += act Wproj^T
       ProfScope ps_(P_GEMM_PROJ, s);
@@ -740,15 +750,17 @@ extern "C" gpt_status gpt_step_bwd(const gpt_shape* shape, const gpt_params* par
     { ProfScope ps_(P_CE_DW, s); TRY(wgrad(dz, vc, hf, d, G + P.lm_head + (size_t)c0 * d, nv, d, N, acc, wpart, s)); }
   }
   { ProfScope ps_(P_FILL, s); TRY(launch_fill_f32(g, (long long)N * d, 0.f, s)); }
-  { ProfScope ps_(P_RMSNORM_BWD, s); TRY(launch_rmsnorm_bwd(dh, hf, at<float>(ws, w.rf), g, g_bf, N, d, s)); }
-
   const bool f8 = D.prec == GPT_PREC_FP8;
   float* qpart = f8 ? at<float>(ws, w.qpart) : nullptr;
+  { ProfScope ps_(P_RMSNORM_BWD, s); TRY(launch_rmsnorm_bwd(dh, hf, at<float>(ws, w.rf), g, g_bf, N, d, s, qpart)); }
+
   uint8_t* dyq = f8 ? at<uint8_t>(ws, w.dyq) : nullptr;
   uint8_t* dyqt = f8 ? at<uint8_t>(ws, w.dyqt) : nullptr;
   // E5M2 codes of an output gradient dY [N, cols], plain and transposed
-  auto quant_dy = [&](const uint16_t* dy, int cols, float* sdy) -> int {
+  // np > 0: the producer already wrote np amax partials into qpart
+  auto quant_dy = [&](const uint16_t* dy, int cols, float* sdy, long long np) -> int {
     ProfScope ps_(P_FP8_QUANT, s);
+    if (np > 0) return quantize_fp8_partials(dy, 0, cols, N, cols, 1, qpart, np, sdy, dyq, cols, dyqt, N, s);
     return quantize_fp8(dy, 0, cols, N, cols, 1, qpart, sdy, dyq, cols, dyqt, N, s);
   };
   // data gradient dX [N, cols_x] = dY W for a weight W [cols_dy, cols_x]: fp8
@@ -761,6 +773,7 @@ extern "C" gpt_status gpt_step_bwd(const gpt_shape* shape, const gpt_params* par
     return gemm_fp8(a, epi, 1, 0, s);
   };
 
+  long long du_slots = 0;
   for (int l = D.L - 1; l >= 0; --l) {
     const Layer& L = w.layer[l];
     float* sc = f8 ? at<float>(ws, w.scales) + (size_t)l * SC_COUNT : nullptr;
@@ -770,13 +783,15 @@ extern "C" gpt_status gpt_step_bwd(const gpt_shape* shape, const gpt_params* par
     const uint16_t* h2 = at<uint16_t>(ws, L.h2);
     const uint16_t* act = at<uint16_t>(ws, L.act);
     // ---- MLP ----
-    if (f8) TRY(quant_dy(g_bf, d, sc + SC_G_MLP));
+    if (f8) TRY(quant_dy(g_bf, d, sc + SC_G_MLP, N));
     {
       GemmArgs a;  // du = (g Wproj) * 2 relu(u)  with relu(u) = sqrt(act)
       ProfScope ps_(P_PROJ_DGRAD, s);
       a.M = N; a.N = hid; a.K = d;
       a.A = g_bf; a.lda = d; a.B = W + P.proj(D, l); a.ldb = hid; a.b_kcontig = 0;
       a.C = du; a.ldc = hid; a.aux = act; a.ldaux = hid;
+      a.amax = qpart;  // NULL for bf16
+      du_slots = f8 ? gemm_amax_slots(a) : 0;
       if (f8) TRY(dgrad_fp8(a, EPI_DRELU2, d, at<uint8_t>(ws, L.wproj8t), sc + SC_G_MLP, sc + SC_WPROJ));
       else TRY(gemm_bf16(a, EPI_DRELU2, s));
     }
@@ -785,7 +800,7 @@ extern "C" gpt_status gpt_step_bwd(const gpt_shape* shape, const gpt_params* par
       if (f8) TRY(wgrad_fp8(dyqt, at<uint8_t>(ws, L.actt), sc + SC_G_MLP, sc + SC_ACT, G + P.proj(D, l), d, hid, N, acc, wpart, s));
       else TRY(wgrad(g_bf, d, act, hid, G + P.proj(D, l), d, hid, N, acc, wpart, s));
     }
-    if (f8) TRY(quant_dy(du, hid, sc + SC_DU));
+    if (f8) TRY(quant_dy(du, hid, sc + SC_DU, du_slots));
     {
       GemmArgs a;  // dh = du Wfc
       ProfScope ps_(P_FC_DGRAD, s);
@@ -800,9 +815,9 @@ extern "C" gpt_status gpt_step_bwd(const gpt_shape* shape, const gpt_params* par
       if (f8) TRY(wgrad_fp8(dyqt, at<uint8_t>(ws, L.h2t), sc + SC_DU, sc + SC_H2, G + P.fc(D, l), hid, d, N, acc, wpart, s));
       else TRY(wgrad(du, hid, h2, d, G + P.fc(D, l), hid, d, N, acc, wpart, s));
     }
-    { ProfScope ps_(P_RMSNORM_BWD, s); TRY(launch_rmsnorm_bwd(dh, h2, at<float>(ws, L.r2), g, g_bf, N, d, s)); }
+    { ProfScope ps_(P_RMSNORM_BWD, s); TRY(launch_rmsnorm_bwd(dh, h2, at<float>(ws, L.r2), g, g_bf, N, d, s, qpart)); }
     // ---- attention ----
-    if (f8) TRY(quant_dy(g_bf, d, sc + SC_G_ATT));
+    if (f8) TRY(quant_dy(g_bf, d, sc + SC_G_ATT, N));
     {
       GemmArgs a;  // dO = g Wo
       ProfScope ps_(P_O_DGRAD, s);
@@ -823,7 +838,7 @@ extern "C" gpt_status gpt_step_bwd(const gpt_shape* shape, const gpt_params* par
                                at<float>(ws, w.delta), dq_acc, dqkv + d, dqkv + 2 * d, 3 * d, D.B, D.H, D.T, s));
     }
     { ProfScope ps_(P_ROPE_BWD, s); TRY(launch_rope_qknorm_bwd(dq_acc, dqkv, qkv, at<float>(ws, L.rq), at<float>(ws, L.rk), cs, N, D.T, D.H, s)); }
-    if (f8) TRY(quant_dy(dqkv, 3 * d, sc + SC_DQKV));
+    if (f8) TRY(quant_dy(dqkv, 3 * d, sc + SC_DQKV, 0));
     {
       GemmArgs a;  // dh = dqkv [Wq; Wk; Wv]
       ProfScope ps_(P_QKV_DGRAD, s);
@@ -838,7 +853,7 @@ extern "C" gpt_status gpt_step_bwd(const gpt_shape* shape, const gpt_params* par
       if (f8) TRY(wgrad_fp8(dyqt, at<uint8_t>(ws, L.h1t), sc + SC_DQKV, sc + SC_H1, G + P.qkv(D, l), 3 * d, d, N, acc, wpart, s));
       else TRY(wgrad(dqkv, 3 * d, h1, d, G + P.qkv(D, l), 3 * d, d, N, acc, wpart, s));
     }
-    { ProfScope ps_(P_RMSNORM_BWD, s); TRY(launch_rmsnorm_bwd(dh, h1, at<float>(ws, L.r1), g, g_bf, N, d, s)); }
+    { ProfScope ps_(P_RMSNORM_BWD, s); TRY(launch_rmsnorm_bwd(dh, h1, at<float>(ws, L.r1), g, g_bf, N, d, s, qpart)); }
   }
   if (!acc) { ProfScope ps_(P_FILL, s); TRY(launch_fill_f32(G + P.wte, (long long)D.V * d, 0.f, s)); }
   { ProfScope ps_(P_EMBED_BWD, s); TRY(launch_embed_bwd(ids, g, G + P.wte, D.B, D.T, d, s)); }

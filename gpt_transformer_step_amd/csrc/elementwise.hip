@@ -102,7 +102,7 @@ __global__ void __launch_bounds__(256) embed_bwd_kernel(const int* __restrict__ 
 
 // h = x * r, r = 1/sqrt(mean(x^2) + eps); one wave per row
 __global__ void __launch_bounds__(256) rmsnorm_fwd_kernel(const float* __restrict__ x, uint16_t* __restrict__ h,
-                                   float* __restrict__ r, long long N, int d) {
+                                   float* __restrict__ r, long long N, int d, float* __restrict__ amax_part) {
   const int lane = threadIdx.x & 63;
   const long long n = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (n >= N) return;
@@ -121,13 +121,20 @@ __global__ void __launch_bounds__(256) rmsnorm_fwd_kernel(const float* __restric
   ss = wave_sum(ss);
   const float rr = 1.0f / sqrtf(ss / (float)d + kEps);
   uint16_t* hr = h + n * d;
+  float amx = 0.f;
 #pragma unroll
   for (int i = 0; i < kMaxChunks; ++i) {
     const int c = i * 64 + lane;
     if (c < nc) {
-      *reinterpret_cast<uint2*>(hr + c * 4) =
-          make_uint2(pack_bf2(v[i].x * rr, v[i].y * rr), pack_bf2(v[i].z * rr, v[i].w * rr));
+      const uint2 w = make_uint2(pack_bf2(v[i].x * rr, v[i].y * rr), pack_bf2(v[i].z * rr, v[i].w * rr));
+      *reinterpret_cast<uint2*>(hr + c * 4) = w;
+      if (amax_part)
+        amx = fmaxf(amx, fmaxf(fmaxf(fabsf(lo_bf(w.x)), fabsf(hi_bf(w.x))), fmaxf(fabsf(lo_bf(w.y)), fabsf(hi_bf(w.y)))));
     }
+  }
+  if (amax_part) {  // launch-uniform: max |h| of this row (fp8 quantisation scale)
+    amx = wave_max(amx);
+    if (lane == 0) amax_part[n] = amx;
   }
   if (lane == 0) r[n] = rr;
 }
@@ -135,7 +142,7 @@ __global__ void __launch_bounds__(256) rmsnorm_fwd_kernel(const float* __restric
 // g += r * (dh - h * mean(dh * h)); g_bf = bf16(g); one wave per row
 __global__ void __launch_bounds__(256) rmsnorm_bwd_kernel(const float* __restrict__ dh, const uint16_t* __restrict__ h,
                                    const float* __restrict__ r, float* __restrict__ g,
-                                   uint16_t* __restrict__ g_bf, long long N, int d) {
+                                   uint16_t* __restrict__ g_bf, long long N, int d, float* __restrict__ amax_part) {
   const int lane = threadIdx.x & 63;
   const long long n = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (n >= N) return;
@@ -154,6 +161,7 @@ __global__ void __launch_bounds__(256) rmsnorm_bwd_kernel(const float* __restric
   }
   dot = wave_sum(dot) / (float)d;
   const float rr = r[n];
+  float amx = 0.f;
 #pragma unroll
   for (int i = 0; i < kMaxChunks; ++i) {
     const int c = i * 64 + lane;
@@ -164,8 +172,15 @@ __global__ void __launch_bounds__(256) rmsnorm_bwd_kernel(const float* __restric
       gv.z += rr * (dv[i].z - hv[i].z * dot);
       gv.w += rr * (dv[i].w - hv[i].w * dot);
       *reinterpret_cast<float4*>(g + n * d + c * 4) = gv;
-      *reinterpret_cast<uint2*>(g_bf + n * d + c * 4) = make_uint2(pack_bf2(gv.x, gv.y), pack_bf2(gv.z, gv.w));
+      const uint2 w = make_uint2(pack_bf2(gv.x, gv.y), pack_bf2(gv.z, gv.w));
+      *reinterpret_cast<uint2*>(g_bf + n * d + c * 4) = w;
+      if (amax_part)
+        amx = fmaxf(amx, fmaxf(fmaxf(fabsf(lo_bf(w.x)), fabsf(hi_bf(w.x))), fmaxf(fabsf(lo_bf(w.y)), fabsf(hi_bf(w.y)))));
     }
+  }
+  if (amax_part) {  // launch-uniform: max |g_bf| of this row (fp8 quantisation scale)
+    amx = wave_max(amx);
+    if (lane == 0) amax_part[n] = amx;
   }
 }
 
@@ -419,15 +434,15 @@ int launch_embed_bwd(const int* ids, const float* g, float* dwte, int B, int T, 
   return 0;
 }
 
-int launch_rmsnorm_fwd(const float* x, uint16_t* h, float* r, long long N, int d, hipStream_t s) {
-  hipLaunchKernelGGL(rmsnorm_fwd_kernel, dim3(nblocks(N, 4)), dim3(256), 0, s, x, h, r, N, d);
+int launch_rmsnorm_fwd(const float* x, uint16_t* h, float* r, long long N, int d, hipStream_t s, float* amax_part) {
+  hipLaunchKernelGGL(rmsnorm_fwd_kernel, dim3(nblocks(N, 4)), dim3(256), 0, s, x, h, r, N, d, amax_part);
   GS_LAUNCH_CHECK("rmsnorm_fwd");
   return 0;
 }
 
 int launch_rmsnorm_bwd(const float* dh, const uint16_t* h, const float* r, float* g, uint16_t* g_bf,
-                       long long N, int d, hipStream_t s) {
-  hipLaunchKernelGGL(rmsnorm_bwd_kernel, dim3(nblocks(N, 4)), dim3(256), 0, s, dh, h, r, g, g_bf, N, d);
+                       long long N, int d, hipStream_t s, float* amax_part) {
+  hipLaunchKernelGGL(rmsnorm_bwd_kernel, dim3(nblocks(N, 4)), dim3(256), 0, s, dh, h, r, g, g_bf, N, d, amax_part);
   GS_LAUNCH_CHECK("rmsnorm_bwd");
   return 0;
 }

@@ -38,19 +38,50 @@ __device__ __forceinline__ void load4(const void* x, long long idx, float* v) {
   }
 }
 
-// max |x| over rows x cols (cols % 4 == 0), one partial per block
+// max |x| over rows x cols, one partial per block.  Contiguous tensors
+// (ld == cols; cols % 16 == 0) are read as a flat array, 64 bytes per thread
+// per round (four independent 16-byte loads in flight); others row by row.
+template <bool F32>
+__device__ __forceinline__ float amax16(const void* x, long long idx) {
+  // 16 bytes at element idx: 8 bf16 or 4 fp32
+  if constexpr (F32) {
+    const float4 f = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(x) + idx);
+    return fmaxf(fmaxf(fabsf(f.x), fabsf(f.y)), fmaxf(fabsf(f.z), fabsf(f.w)));
+  } else {
+    const uint4 w = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(x) + idx);
+    // |bf16| compares like its bit pattern with the sign cleared
+    const uint32_t m = 0x7fff7fffu;
+    const uint32_t a = max(max((w.x & m) & 0xffffu, (w.x & m) >> 16), max((w.y & m) & 0xffffu, (w.y & m) >> 16));
+    const uint32_t b = max(max((w.z & m) & 0xffffu, (w.z & m) >> 16), max((w.w & m) & 0xffffu, (w.w & m) >> 16));
+    return bf2f((uint16_t)max(a, b));
+  }
+}
+
 template <bool F32>
 __global__ void __launch_bounds__(256) amax_partial_kernel(const void* __restrict__ x, long long ldx, int rows,
                                                           int cols, float* __restrict__ partial) {
-  // rows * cols / 4 < 2^31 (checked on the host): 32-bit index arithmetic
-  const unsigned c4 = (unsigned)cols / 4u;
-  const unsigned n4 = (unsigned)rows * c4;
+  constexpr int EPC = F32 ? 4 : 8;  // elements per 16 bytes
   float m = 0.f;
-  for (unsigned i = blockIdx.x * 256u + threadIdx.x; i < n4; i += gridDim.x * 256u) {
-    const unsigned r = i / c4, c = (i - r * c4) * 4u;
-    float v[4];
-    load4<F32>(x, (long long)r * ldx + c, v);
-    m = fmaxf(m, fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3]))));
+  if (ldx == cols) {
+    const long long n16 = (long long)rows * cols / EPC;
+    const long long stride = (long long)gridDim.x * 256;
+    long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+    for (; i + 3 * stride < n16; i += 4 * stride) {
+      const float a0 = amax16<F32>(x, i * EPC), a1 = amax16<F32>(x, (i + stride) * EPC);
+      const float a2 = amax16<F32>(x, (i + 2 * stride) * EPC), a3 = amax16<F32>(x, (i + 3 * stride) * EPC);
+      m = fmaxf(m, fmaxf(fmaxf(a0, a1), fmaxf(a2, a3)));
+    }
+    for (; i < n16; i += stride) m = fmaxf(m, amax16<F32>(x, i * EPC));
+  } else {
+    // rows * cols / 4 < 2^31 (checked on the host): 32-bit index arithmetic
+    const unsigned c4 = (unsigned)cols / 4u;
+    const unsigned n4 = (unsigned)rows * c4;
+    for (unsigned i = blockIdx.x * 256u + threadIdx.x; i < n4; i += gridDim.x * 256u) {
+      const unsigned r = i / c4, c = (i - r * c4) * 4u;
+      float v[4];
+      load4<F32>(x, (long long)r * ldx + c, v);
+      m = fmaxf(m, fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3]))));
+    }
   }
   m = wave_max(m);
   __shared__ float red[4];
@@ -59,10 +90,10 @@ __global__ void __launch_bounds__(256) amax_partial_kernel(const void* __restric
   if (threadIdx.x == 0) partial[blockIdx.x] = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
 }
 
-__global__ void __launch_bounds__(256) fp8_scale_kernel(const float* __restrict__ partial, int np, int fmt,
+__global__ void __launch_bounds__(256) fp8_scale_kernel(const float* __restrict__ partial, long long np, int fmt,
                                                        float* __restrict__ scale) {
   float m = 0.f;
-  for (int i = threadIdx.x; i < np; i += 256) m = fmaxf(m, partial[i]);
+  for (long long i = threadIdx.x; i < np; i += 256) m = fmaxf(m, partial[i]);
   m = wave_max(m);
   __shared__ float red[4];
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
@@ -140,7 +171,7 @@ int launch_fp8_amax_scale(const void* x, int is_f32, long long ldx, int rows, in
   else
     hipLaunchKernelGGL(amax_partial_kernel<false>, dim3(np), dim3(256), 0, s, x, ldx, rows, cols, partial);
   GS_LAUNCH_CHECK("amax_partial");
-  hipLaunchKernelGGL(fp8_scale_kernel, dim3(1), dim3(256), 0, s, partial, np, fmt, scale);
+  hipLaunchKernelGGL(fp8_scale_kernel, dim3(1), dim3(256), 0, s, partial, (long long)np, fmt, scale);
   GS_LAUNCH_CHECK("fp8_scale");
   return 0;
 }
@@ -164,6 +195,14 @@ int quantize_fp8(const void* x, int is_f32, long long ldx, int rows, int cols, i
                  uint8_t* q, long long ldq, uint8_t* qt, long long ldqt, hipStream_t s) {
   int rc = launch_fp8_amax_scale(x, is_f32, ldx, rows, cols, fmt, partial, scale, s);
   if (rc) return rc;
+  return launch_fp8_quant(x, is_f32, ldx, rows, cols, fmt, scale, q, ldq, qt, ldqt, s);
+}
+
+int quantize_fp8_partials(const void* x, int is_f32, long long ldx, int rows, int cols, int fmt,
+                          const float* partial, long long np, float* scale, uint8_t* q, long long ldq, uint8_t* qt,
+                          long long ldqt, hipStream_t s) {
+  hipLaunchKernelGGL(fp8_scale_kernel, dim3(1), dim3(256), 0, s, partial, np, fmt, scale);
+  GS_LAUNCH_CHECK("fp8_scale");
   return launch_fp8_quant(x, is_f32, ldx, rows, cols, fmt, scale, q, ldq, qt, ldqt, s);
 }
 

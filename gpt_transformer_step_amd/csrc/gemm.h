@@ -48,10 +48,14 @@ struct GemmArgs {
   int n_head = 0;                 // EPI_QKV: heads per q (and k) block
   const float* scale_a = nullptr;  // fp8: device scalars; v *= 1 / (scale_a * scale_b)
   const float* scale_b = nullptr;
+  float* amax = nullptr;           // bf16 epilogues: per-wave max |stored value| at
+                                   // amax[block * waves + wave] (block = x + gridDim.x * y)
 };
 
 // Tile selection visible to callers that size partial buffers.
 int gemm_tile_n(const GemmArgs& a);
+// Number of per-wave amax partials a launch with these arguments writes.
+long long gemm_amax_slots(const GemmArgs& a);
 
 // Launch; returns 0 or the gpt_status error code.
 int gemm_bf16(const GemmArgs& a, int epi, hipStream_t s);

@@ -10,6 +10,13 @@ int gemm_bf16_mk(const GemmArgs& a, int epi, hipStream_t s);
 
 int gemm_tile_n(const GemmArgs& a) { return use_big_tile(a) ? 256 : 128; }
 
+long long gemm_amax_slots(const GemmArgs& a) {
+  const bool big = use_big_tile(a);
+  const int t = big ? 256 : 128;
+  const long long tiles = (long long)((a.M + t - 1) / t) * ((a.N + t - 1) / t);
+  return tiles * a.batch * a.k_split * (big ? Cfg<256, 256>::NT : Cfg<128, 128>::NT) / 64;
+}
+
 int gemm_bf16(const GemmArgs& a, int epi, hipStream_t s) {
   if (a.M <= 0 || a.N <= 0 || a.batch <= 0) return 0;
   if (a.a_kcontig && a.b_kcontig) return gemm_bf16_kk(a, epi, s);

@@ -215,7 +215,8 @@ struct TileLoader {
 // epilogues on 4 consecutive columns n .. n+3 of row m
 // ---------------------------------------------------------------------------
 template <int EPI>
-__device__ __forceinline__ void epi4(const GemmArgs& p, int bi, int m, int n, const float* v, long long coff) {
+__device__ __forceinline__ void epi4(const GemmArgs& p, int bi, int m, int n, const float* v, long long coff,
+                                     float& amx) {
   const bool full = (n + 3 < p.N);
   if constexpr (EPI == EPI_F32 || EPI == EPI_RESID || EPI == EPI_F32_ATOMIC) {
     float* C = reinterpret_cast<float*>(p.C) + (long long)bi * p.sC + coff + (long long)m * p.ldc + n;
@@ -264,10 +265,17 @@ __device__ __forceinline__ void epi4(const GemmArgs& p, int bi, int m, int n, co
       for (int j = 0; j < 4; ++j) o[j] = (n + j < p.N) ? o[j] + p.beta * a[j] : 0.f;
     }
     if (full) {
-      *reinterpret_cast<uint2*>(C) = make_uint2(pack_bf2(o[0], o[1]), pack_bf2(o[2], o[3]));
+      const uint2 w = make_uint2(pack_bf2(o[0], o[1]), pack_bf2(o[2], o[3]));
+      *reinterpret_cast<uint2*>(C) = w;
+      if (p.amax)
+        amx = fmaxf(amx, fmaxf(fmaxf(fabsf(lo_bf(w.x)), fabsf(hi_bf(w.x))), fmaxf(fabsf(lo_bf(w.y)), fabsf(hi_bf(w.y)))));
     } else {
       for (int j = 0; j < 4; ++j)
-        if (n + j < p.N) C[j] = f2bf(o[j]);
+        if (n + j < p.N) {
+          const uint16_t b = f2bf(o[j]);
+          C[j] = b;
+          if (p.amax) amx = fmaxf(amx, fabsf(bf2f(b)));
+        }
     }
   } else if constexpr (EPI == EPI_F32_BF16 || EPI == EPI_NS_UPD) {
     float* C = reinterpret_cast<float*>(p.C) + (long long)bi * p.sC + (long long)m * p.ldc + n;
@@ -583,6 +591,7 @@ __global__ void __launch_bounds__((Cfg<BM, BN>::NT), 1) gemm_kernel(GemmArgs p) 
     static_assert(32 * ROWB * (Cfg<BM, BN>::NT / 64) <= 2 * STAGE, "epilogue staging exceeds LDS");
     char* wbuf = smem + wave * 32 * ROWB;
     __syncthreads();  // every wave is done with the operand tiles
+    float amx = 0.f;  // max |stored value| of this lane (bf16 epilogues with p.amax)
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
 #pragma unroll
@@ -606,12 +615,19 @@ __global__ void __launch_bounds__((Cfg<BM, BN>::NT), 1) gemm_kernel(GemmArgs p) 
         const int n = n0 + wn * WN + cc * 4;
         if (m < p.M && n < p.N) {
           const float v[4] = {v4.x, v4.y, v4.z, v4.w};
-          epi4<(EPI == EPI_QKV ? (int)EPI_BF16 : EPI)>(p, bi, m, n, v, coff);
+          epi4<(EPI == EPI_QKV ? (int)EPI_BF16 : EPI)>(p, bi, m, n, v, coff, amx);
         }
       }
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    }
+    if constexpr (EPI == EPI_BF16 || EPI == EPI_RELU2 || EPI == EPI_DRELU2) {
+      if (p.amax) {  // launch-uniform
+        const float wm_ = wave_max(amx);
+        if (lane == 0)
+          p.amax[((long long)blockIdx.x + (long long)gridDim.x * blockIdx.y) * (Cfg<BM, BN>::NT / 64) + wave] = wm_;
+      }
     }
   }
 }

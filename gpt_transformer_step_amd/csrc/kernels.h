@@ -13,9 +13,11 @@ int launch_cast_bf16(const float* src, uint16_t* dst, long long n, hipStream_t s
 int launch_rope_table(float* cos_sin /* [T, 64] cos then [T, 64] sin */, int T, hipStream_t s);
 int launch_embed_fwd(const int* ids, const uint16_t* wte, float* x, int B, int T, int d, hipStream_t s);
 int launch_embed_bwd(const int* ids, const float* g, float* dwte, int B, int T, int d, hipStream_t s);
-int launch_rmsnorm_fwd(const float* x, uint16_t* h, float* r, long long N, int d, hipStream_t s);
+// amax_part (nullable): per-row max |stored bf16 value| at amax_part[row]
+int launch_rmsnorm_fwd(const float* x, uint16_t* h, float* r, long long N, int d, hipStream_t s,
+                       float* amax_part = nullptr);
 int launch_rmsnorm_bwd(const float* dh, const uint16_t* h, const float* r, float* g, uint16_t* g_bf,
-                       long long N, int d, hipStream_t s);
+                       long long N, int d, hipStream_t s, float* amax_part = nullptr);
 int launch_rope_qknorm_bwd(const float* dq_acc, uint16_t* dqkv, const uint16_t* qkv, const float* rq,
                            const float* rk, const float* cos_sin, long long N, int T, int H,
                            hipStream_t s);
@@ -63,6 +65,10 @@ int launch_fp8_quant(const void* x, int is_f32, long long ldx, int rows, int col
                      uint8_t* q, long long ldq, uint8_t* qt, long long ldqt, hipStream_t s);
 int quantize_fp8(const void* x, int is_f32, long long ldx, int rows, int cols, int fmt, float* partial, float* scale,
                  uint8_t* q, long long ldq, uint8_t* qt, long long ldqt, hipStream_t s);
+// the same with the amax already reduced by the producer into np partials
+int quantize_fp8_partials(const void* x, int is_f32, long long ldx, int rows, int cols, int fmt,
+                          const float* partial, long long np, float* scale, uint8_t* q, long long ldq, uint8_t* qt,
+                          long long ldqt, hipStream_t s);
 
 // --- roofline probes (probe.hip) -------------------------------------------
 int launch_mfma_peak(int fp8, int blocks, int iters, float* out, double* flops, hipStream_t s);
