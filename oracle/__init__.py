@@ -20,6 +20,7 @@ Sources (the pages this implements; all describe nanochat):
 Modules:
   model   -- forward/backward of the decoder-only transformer step.
   muon    -- Muon momentum, Newton-Schulz orthogonalisation, apply.
+  adamw   -- AdamW (decoupled weight decay) for the embedding and head.
   fp8     -- software OCP E4M3 / E5M2 codec and per-tensor fake quantisation.
   precision -- round-to-nearest-even fp32 -> bf16.
 
@@ -30,4 +31,4 @@ whole-model result at the full configuration sizes, for which the pages print
 no worked example (its parts are pinned individually).
 """
 
-from . import precision, model, muon, fp8  # noqa: F401
+from . import precision, model, muon, fp8, adamw  # noqa: F401
