@@ -5,7 +5,8 @@
 
 One step = gpt_step_fwd + gpt_step_bwd + muon_update on the three groups of
 block matrices (the q/k/v/o matrices, the MLP input matrices, the MLP output
-matrices) on synthetic inputs already resident in HBM: uniform token ids and
+matrices) + adamw_update on the embedding and the head, on synthetic inputs
+already resident in HBM: uniform token ids and
 N(0, 1/fan_in) weights from the seeded generators.  W untimed warm-up steps,
 then K timed steps between two synchronised events on the launch stream.
 Prints one JSON line.
@@ -202,9 +203,22 @@ def main():
                            ws=torch.empty(Bd.muon_workspace_size(count, rows, cols), dtype=torch.uint8,
                                           device=dev)))
 
+    # AdamW for the embedding and the head (the two [V, d] tables)
+    adam = []
+    for start in (offs[0], offs[-1]):
+        size = V * d
+        adam.append(dict(start=start, size=size, M=torch.zeros(size, dtype=torch.float32, device=dev),
+                         V=torch.zeros(size, dtype=torch.float32, device=dev)))
+    step_count = [0]
+
     def step():
         Bd.step_fwd(sh, params, ids, loss, ws)
         Bd.step_bwd(sh, params, ids, ws)
+        step_count[0] += 1
+        for ad in adam:
+            st, size = ad["start"], ad["size"]
+            Bd.adamw_update(master[st:st + size], grad[st:st + size], ad["M"], ad["V"], step_count[0], lr=0.004,
+                            beta1=0.8, beta2=0.95, eps=1e-10, weight_decay=0.0, W_bf16=bf16[st:st + size])
         for gr in groups:
             st, size = gr["start"], gr["count"] * gr["rows"] * gr["cols"]
             view = (gr["count"], gr["rows"], gr["cols"])
@@ -257,7 +271,7 @@ def main():
     tok = B * T
     step_s = ms / 1e3
     fwd_bwd_ms = sum(v[0] for k, v in breakdown.items()
-                     if not k.startswith("ns_") and k != "muon_elementwise")
+                     if not k.startswith("ns_") and k not in ("muon_elementwise", "adamw"))
     kf = kernel_flops(dom, depth, V, T, B)
     avg_launch_s = dom_ms / dom_cnt / 1e3
     achieved = kf / avg_launch_s / 1e12
@@ -281,7 +295,8 @@ def main():
         "data": "synthetic: uniform token ids, N(0,1/fan_in) weights (seeded PCG64)",
         "config": {"workload": args.workload, "depth": depth, "d_model": d, "n_head": H, "seq_len": T,
                    "micro_batch": B, "vocab": V, "tokens_per_step": tok, "parallelism": "single GPU",
-                   "optimizer": "Muon (5 Newton-Schulz iterations) on all block matrices"},
+                   "optimizer": "Muon (5 Newton-Schulz iterations) on all block matrices, AdamW on embedding "
+                                "and head"},
         "mfu": (f_model + f_ns) / step_s / PEAK_BF16,
         "mfu_vs_mixed_peak": t_ideal / step_s if fp8 else None,
         "mfu_model": f_model / (fwd_bwd_ms / 1e3) / PEAK_BF16 if fwd_bwd_ms else None,

@@ -53,6 +53,8 @@ _SIGS = {
     "gpt_cast_bf16": [_vp, _vp, _sz, _vp],
     "gpt_step_fwd": [_P(Shape), _P(Params), _vp, _vp, _vp, _vp, _vp, _sz, _vp],
     "gpt_step_bwd": [_P(Shape), _P(Params), _vp, _i32, _vp, _sz, _vp],
+    "gpt_step_bwd_scaled": [_P(Shape), _P(Params), _vp, _i32, _f32, _vp, _sz, _vp],
+    "adamw_update": [_vp, _vp, _vp, _vp, _vp, _sz, _i32, _f32, _f32, _f32, _f32, _f32, _f32, _vp],
     "muon_workspace_size": [_i32, _i32, _i32, _P(_sz)],
     "muon_update": [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _P(_f32), _i32, _f32, _f32, _f32,
                     _vp, _sz, _vp],
@@ -167,6 +169,20 @@ def step_fwd(sh, params, ids, loss, ws, row_lse=None, logits=None, stream=None):
 def step_bwd(sh, params, ids, ws, accumulate=False, stream=None):
     _call("gpt_step_bwd", ctypes.byref(sh), ctypes.byref(params), _ptr(ids), int(accumulate),
           _ptr(ws), ws.numel() * ws.element_size(), _stream(stream))
+
+
+def step_bwd_scaled(sh, params, ids, ws, loss_scale, accumulate=False, stream=None):
+    _call("gpt_step_bwd_scaled", ctypes.byref(sh), ctypes.byref(params), _ptr(ids), int(accumulate),
+          float(loss_scale), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream))
+
+
+def adamw_update(W, G, M, V, step, lr, beta1=0.9, beta2=0.95, eps=1e-8, weight_decay=0.0, grad_scale=1.0,
+                 W_bf16=None, stream=None):
+    """W, G, M, V: fp32 tensors of the same number of elements."""
+    n = W.numel()
+    assert G.numel() == n and M.numel() == n and V.numel() == n
+    _call("adamw_update", _ptr(W), _ptr(W_bf16), _ptr(G), _ptr(M), _ptr(V), n, int(step), lr, beta1, beta2, eps,
+          weight_decay, grad_scale, _stream(stream))
 
 
 def muon_workspace_size(count, rows, cols):

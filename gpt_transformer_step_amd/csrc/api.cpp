@@ -237,14 +237,14 @@ enum ProfCat {
   P_EMBED_FWD, P_RMSNORM_FWD, P_GEMM_QKV, P_ATTN_FWD, P_GEMM_O, P_GEMM_FC, P_GEMM_PROJ, P_CE_FWD,
   P_CE_REDUCE, P_CE_DZ, P_CE_DH, P_CE_DW, P_RMSNORM_BWD, P_PROJ_DGRAD, P_PROJ_WGRAD, P_FC_DGRAD,
   P_FC_WGRAD, P_O_DGRAD, P_O_WGRAD, P_ATTN_BWD_PRE, P_ATTN_BWD_KV, P_ATTN_BWD_Q, P_ROPE_BWD, P_QKV_DGRAD, P_QKV_WGRAD, P_EMBED_BWD,
-  P_FILL, P_MUON_ELEMWISE, P_NS_GRAM, P_NS_POLY, P_NS_UPDATE, P_FP8_QUANT, P_COUNT
+  P_FILL, P_MUON_ELEMWISE, P_NS_GRAM, P_NS_POLY, P_NS_UPDATE, P_FP8_QUANT, P_ADAMW, P_COUNT
 };
 const char* kProfNames[P_COUNT] = {
     "embed_fwd", "rmsnorm_fwd", "gemm_qkv_rope_fwd", "attn_fwd", "gemm_o_fwd", "gemm_fc_relu2_fwd",
     "gemm_proj_fwd", "gemm_ce_fwd", "ce_reduce", "gemm_ce_dlogits", "gemm_ce_dh", "gemm_ce_dw",
     "rmsnorm_bwd", "gemm_proj_dgrad", "gemm_proj_wgrad", "gemm_fc_dgrad", "gemm_fc_wgrad",
     "gemm_o_dgrad", "gemm_o_wgrad", "attn_bwd_delta", "attn_bwd_dkdv", "attn_bwd_dq", "rope_qknorm_bwd", "gemm_qkv_dgrad", "gemm_qkv_wgrad",
-    "embed_bwd", "fill", "muon_elementwise", "ns_gram", "ns_poly", "ns_update", "fp8_quant"};
+    "embed_bwd", "fill", "muon_elementwise", "ns_gram", "ns_poly", "ns_update", "fp8_quant", "adamw"};
 
 struct Profiler {
   uint64_t mask = 0;
@@ -700,9 +700,18 @@ extern "C" gpt_status gpt_step_fwd(const gpt_shape* shape, const gpt_params* par
 
 extern "C" gpt_status gpt_step_bwd(const gpt_shape* shape, const gpt_params* params, const int32_t* ids,
                                    int32_t accumulate, void* ws, size_t ws_bytes, gpt_stream_t stream) {
+  if (!shape) FAIL(GPT_ERR_INVALID_ARG, "shape is NULL");
+  const double n = (double)shape->batch * (double)shape->seq_len;
+  return gpt_step_bwd_scaled(shape, params, ids, accumulate, n > 0 ? (float)(1.0 / n) : 1.f, ws, ws_bytes, stream);
+}
+
+extern "C" gpt_status gpt_step_bwd_scaled(const gpt_shape* shape, const gpt_params* params, const int32_t* ids,
+                                          int32_t accumulate, float loss_scale, void* ws, size_t ws_bytes,
+                                          gpt_stream_t stream) {
   Dims D;
   WS w;
   TRY(check_step_args(shape, params, ids, ws, ws_bytes, &D, &w));
+  if (!(loss_scale > 0.f) || !isfinite(loss_scale)) FAIL(GPT_ERR_INVALID_ARG, "loss_scale must be positive and finite");
   if (!params->grad) FAIL(GPT_ERR_INVALID_ARG, "params->grad is NULL");
   if ((uintptr_t)params->grad & 15) FAIL(GPT_ERR_INVALID_ARG, "params->grad must be 16-byte aligned");
   if (accumulate != 0 && accumulate != 1) FAIL(GPT_ERR_INVALID_ARG, "accumulate must be 0 or 1");
@@ -735,7 +744,7 @@ extern "C" gpt_status gpt_step_bwd(const gpt_shape* shape, const gpt_params* par
       a.A = hf; a.lda = d; a.B = W + P.lm_head + (size_t)c0 * d; a.ldb = d;
       a.C = dz; a.ldc = vc;
       a.row_f = at<float>(ws, w.lse); a.row_i = ids; a.row_T = D.T; a.col_offset = c0;
-      a.beta = 1.0f / (float)N;
+      a.beta = loss_scale;
       TRY(gemm_bf16(a, EPI_CE_BWD, s));
     }
     {
@@ -857,6 +866,27 @@ extern "C" gpt_status gpt_step_bwd(const gpt_shape* shape, const gpt_params* par
   }
   if (!acc) { ProfScope ps_(P_FILL, s); TRY(launch_fill_f32(G + P.wte, (long long)D.V * d, 0.f, s)); }
   { ProfScope ps_(P_EMBED_BWD, s); TRY(launch_embed_bwd(ids, g, G + P.wte, D.B, D.T, d, s)); }
+  return GPT_OK;
+}
+
+// ---------------------------------------------------------------------------
+// AdamW
+// ---------------------------------------------------------------------------
+extern "C" gpt_status adamw_update(float* W, uint16_t* W_bf16, const float* G, float* M, float* V, size_t n,
+                                   int32_t step, float lr, float beta1, float beta2, float eps, float weight_decay,
+                                   float grad_scale, gpt_stream_t stream) {
+  if (n == 0) return GPT_OK;
+  if (!W || !G || !M || !V) FAIL(GPT_ERR_INVALID_ARG, "W, G, M and V must not be NULL");
+  if (n % 4) FAIL(GPT_ERR_INVALID_ARG, "n must be a multiple of 4");
+  if (((uintptr_t)W | (uintptr_t)G | (uintptr_t)M | (uintptr_t)V) & 15) FAIL(GPT_ERR_INVALID_ARG, "fp32 arrays must be 16-byte aligned");
+  if ((uintptr_t)W_bf16 & 7) FAIL(GPT_ERR_INVALID_ARG, "W_bf16 must be 8-byte aligned");
+  if (step < 1) FAIL(GPT_ERR_INVALID_ARG, "step is 1-based");
+  if (!(beta1 >= 0.f && beta1 < 1.f) || !(beta2 >= 0.f && beta2 < 1.f) || !(eps > 0.f))
+    FAIL(GPT_ERR_INVALID_ARG, "need 0 <= beta1, beta2 < 1 and eps > 0");
+  const double bc1 = 1.0 - pow((double)beta1, (double)step), bc2 = 1.0 - pow((double)beta2, (double)step);
+  ProfScope ps_(P_ADAMW, S(stream));
+  TRY(launch_adamw(W, W_bf16, G, M, V, (long long)n, lr, beta1, beta2, eps, weight_decay, (float)(1.0 / bc1),
+                   (float)(1.0 / bc2), grad_scale, S(stream)));
   return GPT_OK;
 }
 

@@ -395,6 +395,36 @@ __global__ void muon_apply_kernel(const float* __restrict__ X, float* __restrict
   }
 }
 
+// AdamW with decoupled weight decay on 4 parameters per thread (n % 4 == 0,
+// 16-byte aligned arrays): g = gs G; m = b1 m + (1-b1) g; v = b2 v + (1-b2) g^2;
+// W = W (1 - lr wd) - lr (m / bc1) / (sqrt(v / bc2) + eps); Wb = bf16(W)
+__global__ void __launch_bounds__(256) adamw_kernel(float* __restrict__ W, uint16_t* __restrict__ Wb,
+                                                    const float* __restrict__ G, float* __restrict__ M,
+                                                    float* __restrict__ V, long long n4, float lr, float b1,
+                                                    float b2, float eps, float wd, float inv_bc1, float inv_bc2,
+                                                    float gs) {
+  const float decay = 1.f - lr * wd;
+  for (long long i = (long long)blockIdx.x * 256 + threadIdx.x; i < n4; i += (long long)gridDim.x * 256) {
+    const float4 g4 = reinterpret_cast<const float4*>(G)[i];
+    float4 m4 = reinterpret_cast<float4*>(M)[i];
+    float4 v4 = reinterpret_cast<float4*>(V)[i];
+    float4 w4 = reinterpret_cast<float4*>(W)[i];
+    float g[4] = {g4.x, g4.y, g4.z, g4.w}, m[4] = {m4.x, m4.y, m4.z, m4.w};
+    float v[4] = {v4.x, v4.y, v4.z, v4.w}, w[4] = {w4.x, w4.y, w4.z, w4.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float gj = g[j] * gs;
+      m[j] = b1 * m[j] + (1.f - b1) * gj;
+      v[j] = b2 * v[j] + (1.f - b2) * gj * gj;
+      w[j] = w[j] * decay - lr * (m[j] * inv_bc1) / (sqrtf(v[j] * inv_bc2) + eps);
+    }
+    reinterpret_cast<float4*>(M)[i] = make_float4(m[0], m[1], m[2], m[3]);
+    reinterpret_cast<float4*>(V)[i] = make_float4(v[0], v[1], v[2], v[3]);
+    reinterpret_cast<float4*>(W)[i] = make_float4(w[0], w[1], w[2], w[3]);
+    if (Wb) reinterpret_cast<uint2*>(Wb)[i] = make_uint2(pack_bf2(w[0], w[1]), pack_bf2(w[2], w[3]));
+  }
+}
+
 }  // namespace
 
 // ----------------------------------------------------------------------------
@@ -501,6 +531,17 @@ int launch_ns_init(const float* src, const float* partial, int nblk, float* X, u
   else
     hipLaunchKernelGGL(ns_init_kernel<false>, grid, dim3(256), 0, s, src, partial, nblk, X, Xb, rows, cols, eps);
   GS_LAUNCH_CHECK("ns_init");
+  return 0;
+}
+
+int launch_adamw(float* W, uint16_t* Wb, const float* G, float* M, float* V, long long n, float lr, float b1,
+                 float b2, float eps, float wd, float inv_bc1, float inv_bc2, float gs, hipStream_t s) {
+  if (n <= 0) return 0;
+  const long long n4 = n / 4;
+  const int blocks = (int)std::min<long long>((n4 + 255) / 256, 4096);
+  hipLaunchKernelGGL(adamw_kernel, dim3(blocks), dim3(256), 0, s, W, Wb, G, M, V, n4, lr, b1, b2, eps, wd, inv_bc1,
+                     inv_bc2, gs);
+  GS_LAUNCH_CHECK("adamw");
   return 0;
 }
 

@@ -39,6 +39,10 @@ int launch_ns_init(const float* src, const float* partial, int nblk, float* X, u
 int launch_muon_apply(const float* X, float* W, uint16_t* Wb, float* O_out, int count, int rows,
                       int cols, float lr, float wd, hipStream_t s);
 
+// AdamW on n fp32 parameters (n % 4 == 0, 16-byte aligned; Wb nullable)
+int launch_adamw(float* W, uint16_t* Wb, const float* G, float* M, float* V, long long n, float lr, float b1,
+                 float b2, float eps, float wd, float inv_bc1, float inv_bc2, float gs, hipStream_t s);
+
 // --- attention (attention.hip) ---------------------------------------------
 int launch_attn_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, long long ld_qkv,
                     uint16_t* out, long long ld_out, float* lse, int B, int H, int T, hipStream_t s);

@@ -122,6 +122,30 @@ gpt_status gpt_step_fwd(const gpt_shape* shape, const gpt_params* params, const 
 gpt_status gpt_step_bwd(const gpt_shape* shape, const gpt_params* params, const int32_t* ids,
                         int32_t accumulate, void* ws, size_t ws_bytes, gpt_stream_t stream);
 
+/* Backward of loss_scale * (sum of the B*T row losses) instead of the mean:
+ * gpt_step_bwd is this call with loss_scale = 1/(batch*seq_len).  For a
+ * batch split into n_micro micro-batches of the same shape, calling it on each
+ * with loss_scale = 1/(n_micro*batch*seq_len), accumulate = 0 for the first
+ * and 1 after, leaves the gradient of the mean loss over all of them (the
+ * pages' gradient accumulation when one GPU stands in for several: dev.to
+ * page, FAQ "¿Qué GPU necesito?").  loss_scale > 0 and finite. */
+gpt_status gpt_step_bwd_scaled(const gpt_shape* shape, const gpt_params* params, const int32_t* ids,
+                               int32_t accumulate, float loss_scale, void* ws, size_t ws_bytes,
+                               gpt_stream_t stream);
+
+/* AdamW with decoupled weight decay on n fp32 parameters, for the matrices
+ * the pages give to AdamW (dev.to page, "2. Optimizador Muon": embeddings and
+ * lm_head):
+ *   g = grad_scale * G;  M <- beta1 M + (1-beta1) g;  V <- beta2 V + (1-beta2) g^2
+ *   W <- W (1 - lr weight_decay) - lr (M / (1-beta1^step)) / (sqrt(V / (1-beta2^step)) + eps)
+ *   W_bf16 <- bf16(W) (nullable)
+ * step: 1-based count of this update (bias correction).  M and V start at 0.
+ * n % 4 == 0; W, G, M, V 16-byte aligned, W_bf16 8-byte aligned.
+ * GPT_ERR_INVALID_ARG for NULL arrays, step < 1, betas outside [0, 1), eps <= 0. */
+gpt_status adamw_update(float* W, uint16_t* W_bf16, const float* G, float* M, float* V, size_t n, int32_t step,
+                        float lr, float beta1, float beta2, float eps, float weight_decay, float grad_scale,
+                        gpt_stream_t stream);
+
 /* Workspace bytes for muon_update on `count` matrices of [rows, cols]. */
 gpt_status muon_workspace_size(int32_t count, int32_t rows, int32_t cols, size_t* bytes /* host */);
 

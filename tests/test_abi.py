@@ -156,3 +156,19 @@ def test_fp8_workspace_is_larger(B):
     bf = B.workspace_size(B.shape(4, 4096, 256, 2, B.PREC_BF16))
     f8 = B.workspace_size(B.shape(4, 4096, 256, 2, B.PREC_FP8))
     assert f8 > bf
+
+
+def test_adamw_and_scaled_bwd_reject_on_host(B):
+    lib = B.lib()
+    fake = ctypes.c_void_p(4096)
+    assert lib.adamw_update(None, None, None, None, None, 0, 1, 1e-3, 0.9, 0.95, 1e-8, 0.0, 1.0, None) == 0
+    rc = lib.adamw_update(fake, None, fake, fake, fake, 6, 1, 1e-3, 0.9, 0.95, 1e-8, 0.0, 1.0, None)
+    assert rc == -1   # n not a multiple of 4
+    rc = lib.adamw_update(fake, None, fake, fake, fake, 8, 0, 1e-3, 0.9, 0.95, 1e-8, 0.0, 1.0, None)
+    assert rc == -1   # step is 1-based
+    rc = lib.adamw_update(fake, None, None, fake, fake, 8, 1, 1e-3, 0.9, 0.95, 1e-8, 0.0, 1.0, None)
+    assert rc == -1   # G NULL
+    sh = B.shape(2, 1024, 64, 2)
+    params = B.Params(fake, fake, fake)
+    rc = lib.gpt_step_bwd_scaled(ctypes.byref(sh), ctypes.byref(params), fake, 0, -1.0, fake, 1 << 40, None)
+    assert rc == -1   # loss_scale must be positive
