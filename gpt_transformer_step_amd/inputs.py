@@ -20,25 +20,29 @@ import numpy as np
 
 @dataclass(frozen=True)
 class Dims:
-    """Tensor shapes of one model: n_layer blocks of width d_model."""
+    """Tensor shapes of one model: n_layer blocks of width d_model; key/value
+    projections of width d_kv = 128 * n_kv_head (d_model without grouping)."""
     n_layer: int
     d_model: int
     hidden: int
     vocab: int
+    d_kv: int = 0
 
     @staticmethod
-    def from_depth(depth, vocab=32768):
+    def from_depth(depth, vocab=32768, n_kv_head=0):
         d = 64 * depth
-        return Dims(n_layer=depth, d_model=d, hidden=4 * d, vocab=vocab)
+        return Dims(n_layer=depth, d_model=d, hidden=4 * d, vocab=vocab,
+                    d_kv=128 * n_kv_head if n_kv_head else d)
 
 
 def packed_tensors(dims):
     """(name, shape) in packed parameter order: wte | per layer wq, wk, wv, wo |
     per layer wfc | per layer wproj | lm_head."""
     d, h, V, L = dims.d_model, dims.hidden, dims.vocab, dims.n_layer
+    dkv = dims.d_kv or d
     out = [("wte", (V, d))]
     for i in range(L):
-        out += [(f"wq.{i}", (d, d)), (f"wk.{i}", (d, d)), (f"wv.{i}", (d, d)), (f"wo.{i}", (d, d))]
+        out += [(f"wq.{i}", (d, d)), (f"wk.{i}", (dkv, d)), (f"wv.{i}", (dkv, d)), (f"wo.{i}", (d, d))]
     out += [(f"wfc.{i}", (h, d)) for i in range(L)]
     out += [(f"wproj.{i}", (d, h)) for i in range(L)]
     out.append(("lm_head", (V, d)))

@@ -23,6 +23,17 @@ Readings taken where the pages are silent:
   * inputs ids[:, :T], targets ids[:, 1:], loss = mean over all B*T rows;
   * no biases, no logit soft-capping.
 
+Attention variants (the same feature list: grouped-query attention with fewer
+key/value heads, and sliding-window layers in a pattern such as "SSSL" that
+alternates short and long context; the flash-attention call takes a
+``window_size``):
+  * n_kv_head key/value heads of width 128; query head h reads key/value head
+    h // (n_head / n_kv_head), and a key/value head's gradient is the sum
+    over its query heads;
+  * window w (the left size of the flash-attention window): in an 'S' layer
+    query i sees keys i - w .. i; 'L' layers are full causal; the pattern
+    string repeats over the layers (layer i takes pattern[i % len]).
+
 fp8 mode (``fp8=True``): the four block projections (qkv, out, fc, proj) use
 per-tensor scaled fake quantisation as the precision passage describes
 (apidog.com/pt "Gerenciamento de Precisão", apidog.com/de
@@ -31,9 +42,10 @@ activations and weights, E5M2 for output gradients, scale = fmax / amax of the
 current tensor.  The fused q/k/v weight counts as one tensor.
 
 Pinned by (tests/test_oracle_model.py): central finite differences in float64
-of every parameter tensor on a tiny shape; a brute-force double-loop causal
-attention; torch CPU autograd (float64) with torch's own RMS norm and
-scaled-dot-product attention as an independent second implementation; the
+of every parameter tensor on a tiny shape (also with grouped key/value heads
+and windowed layers); brute-force double-loop causal and windowed attention; torch CPU autograd (float64) with torch's own RMS norm and
+scaled-dot-product attention (with repeated key/value heads and an explicit
+window mask for the variants) as an independent second implementation; the
 closed form loss = ln V for a zero output matrix; softmax rows summing to 1;
 RoPE identity at position 0, norm preservation and relative-position
 invariance; RMSNorm output mean square = ms / (ms + eps).
@@ -57,14 +69,27 @@ class Config:
     vocab: int
     eps: float = 1e-6
     rope_base: float = 10000.0
+    n_kv_head: int = 0     # key/value heads (GQA); 0 = n_head
+    window: int = 0        # 'S' layers: query i sees keys i - window .. i; 0 = every layer full
+    pattern: str = "L"     # per-layer pattern, repeated over the layers ('S' short, 'L' long)
 
     @staticmethod
-    def from_depth(depth, vocab=32768):
+    def from_depth(depth, vocab=32768, n_kv_head=0, window=0, pattern="L"):
         """Shapes from the single depth dial: width 64*depth, 128-wide heads,
         MLP 4x (dev.to page, "La Filosofía: Un Solo Selector")."""
         d = 64 * depth
         return Config(n_layer=depth, d_model=d, n_head=d // 128, head_dim=128,
-                      hidden=4 * d, vocab=vocab)
+                      hidden=4 * d, vocab=vocab, n_kv_head=n_kv_head, window=window, pattern=pattern)
+
+    @property
+    def kv_heads(self):
+        return self.n_kv_head or self.n_head
+
+    def layer_window(self, i):
+        """Left window of layer i (None: full causal)."""
+        if self.window <= 0 or not self.pattern:
+            return None
+        return self.window if self.pattern[i % len(self.pattern)] == "S" else None
 
 
 # ----------------------------------------------------------------------------
@@ -108,13 +133,24 @@ def rope_bwd(dy, cos, sin):
     return np.concatenate([d1 * cos + d2 * sin, -d1 * sin + d2 * cos], axis=-1)
 
 
-def causal_attention(q, k, v):
-    """softmax(q k^T / sqrt(hd) with key j > query i masked) v.
+def attention_mask(T, window=None):
+    """True where key j is hidden from query i: j > i, and with a window w
+    also j < i - w (the query sees keys i - w .. i)."""
+    i = np.arange(T)[:, None]
+    j = np.arange(T)[None, :]
+    m = j > i
+    if window is not None:
+        m = m | (j < i - window)
+    return m
+
+
+def causal_attention(q, k, v, window=None):
+    """softmax(q k^T / sqrt(hd) with masked keys removed) v (attention_mask).
     q, k, v: [..., T, hd].  Returns (y, lse) with lse the row log-sum-exp of
     the scaled, masked scores."""
     T, hd = q.shape[-2], q.shape[-1]
     s = (q @ np.swapaxes(k, -1, -2)) / np.sqrt(hd)
-    mask = np.triu(np.ones((T, T), dtype=bool), k=1)
+    mask = attention_mask(T, window)
     s = np.where(mask, -np.inf, s)
     m = np.max(s, axis=-1, keepdims=True)
     e = np.exp(s - m)
@@ -124,14 +160,14 @@ def causal_attention(q, k, v):
     return p @ v, lse
 
 
-def causal_attention_bwd(q, k, v, y, dy, lse):
+def causal_attention_bwd(q, k, v, y, dy, lse, window=None):
     """Backward of causal_attention with P recomputed from lse:
     dV = P^T dY; dP = dY V^T; dS = P * (dP - rowsum(dY * Y)); dQ = dS K / sqrt(hd);
     dK = dS^T Q / sqrt(hd)."""
     T, hd = q.shape[-2], q.shape[-1]
     scale = 1.0 / np.sqrt(hd)
     s = (q @ np.swapaxes(k, -1, -2)) * scale
-    mask = np.triu(np.ones((T, T), dtype=bool), k=1)
+    mask = attention_mask(T, window)
     p = np.where(mask, 0.0, np.exp(s - lse[..., None]))
     dv = np.swapaxes(p, -1, -2) @ dy
     dp = dy @ np.swapaxes(v, -1, -2)
@@ -197,11 +233,12 @@ def param_names(cfg):
 
 def param_shapes(cfg):
     d, h, V = cfg.d_model, cfg.hidden, cfg.vocab
+    dkv = cfg.kv_heads * cfg.head_dim
     shapes = {}
     for n in param_names(cfg):
         base = n.split(".")[0]
-        shapes[n] = {"wte": (V, d), "lm_head": (V, d), "wq": (d, d), "wk": (d, d),
-                     "wv": (d, d), "wo": (d, d), "wfc": (h, d), "wproj": (d, h)}[base]
+        shapes[n] = {"wte": (V, d), "lm_head": (V, d), "wq": (d, d), "wk": (dkv, d),
+                     "wv": (dkv, d), "wo": (d, d), "wfc": (h, d), "wproj": (d, h)}[base]
     return shapes
 
 
@@ -213,6 +250,9 @@ def _forward_backward_chunk(P, ids, cfg, loss_scale, dtype, want_grads, want_log
     B, T1 = ids.shape
     T = T1 - 1
     d, H, hd = cfg.d_model, cfg.n_head, cfg.head_dim
+    Hkv = cfg.kv_heads
+    G = H // Hkv         # query heads per key/value head
+    dkv = Hkv * hd
     R = B * T
     inp = ids[:, :T].reshape(-1)
     tgt = ids[:, 1:].reshape(-1)
@@ -226,12 +266,14 @@ def _forward_backward_chunk(P, ids, cfg, loss_scale, dtype, want_grads, want_log
         h1o = op(h1)
         qkv = _lin_fwd(h1o, wqkv, fp8)
         q_raw = qkv[:, :d].reshape(B, T, H, hd).transpose(0, 2, 1, 3)
-        k_raw = qkv[:, d:2 * d].reshape(B, T, H, hd).transpose(0, 2, 1, 3)
-        v = op(qkv[:, 2 * d:].reshape(B, T, H, hd).transpose(0, 2, 1, 3))
+        k_raw = qkv[:, d:d + dkv].reshape(B, T, Hkv, hd).transpose(0, 2, 1, 3)
+        v = op(qkv[:, d + dkv:].reshape(B, T, Hkv, hd).transpose(0, 2, 1, 3))
         qn, rq = rms_norm(rope(q_raw, cos, sin), eps)
         kn, rk = rms_norm(rope(k_raw, cos, sin), eps)
         qs, ks = op(qn), op(kn)
-        y, lse_att = causal_attention(qs, ks, v)
+        # query head h reads key/value head h // G
+        win = cfg.layer_window(i)
+        y, lse_att = causal_attention(qs, np.repeat(ks, G, axis=1), np.repeat(v, G, axis=1), win)
         y2 = op(y.transpose(0, 2, 1, 3).reshape(R, d))
         x = x + _lin_fwd(y2, P[f"wo.{i}"], fp8)
         h2, r2 = rms_norm(x, eps)
@@ -252,37 +294,41 @@ def _forward_backward_chunk(P, ids, cfg, loss_scale, dtype, want_grads, want_log
     if not want_grads:
         return out
 
-    G = {}
+    Gr = {}
     dz = op(cross_entropy_bwd(z, tgt, lse, loss_scale))
     del z
-    G["lm_head"] = dz.T @ hfo
+    Gr["lm_head"] = dz.T @ hfo
     g = rms_norm_bwd(dz @ P["lm_head"], hf, rf)
     del dz
     for i in reversed(range(cfg.n_layer)):
         (h1, h1o, r1, wqkv, qn, qs, rq, kn, ks, rk, v, y2, lse_att, h2, h2o, r2, u, a) = caches[i]
         # MLP
         gb = op(g)
-        da, G[f"wproj.{i}"] = _lin_bwd(a, P[f"wproj.{i}"], gb, fp8)
+        da, Gr[f"wproj.{i}"] = _lin_bwd(a, P[f"wproj.{i}"], gb, fp8)
         du = op(da * 2.0 * np.maximum(u, 0.0))
-        dh2, G[f"wfc.{i}"] = _lin_bwd(h2o, P[f"wfc.{i}"], du, fp8)
+        dh2, Gr[f"wfc.{i}"] = _lin_bwd(h2o, P[f"wfc.{i}"], du, fp8)
         g = g + rms_norm_bwd(dh2, h2, r2)
         # attention
         gb = op(g)
-        dy2, G[f"wo.{i}"] = _lin_bwd(y2, P[f"wo.{i}"], gb, fp8)
+        dy2, Gr[f"wo.{i}"] = _lin_bwd(y2, P[f"wo.{i}"], gb, fp8)
         dy = op(dy2).reshape(B, T, H, hd).transpose(0, 2, 1, 3)
         y = y2.reshape(B, T, H, hd).transpose(0, 2, 1, 3)
-        dqn, dkn, dv = causal_attention_bwd(qs, ks, v, y, dy, lse_att)
+        dqn, dkf, dvf = causal_attention_bwd(qs, np.repeat(ks, G, axis=1), np.repeat(v, G, axis=1), y, dy,
+                                             lse_att, cfg.layer_window(i))
+        # a key/value head collects the gradients of its G query heads
+        dkn = dkf.reshape(B, Hkv, G, T, hd).sum(axis=2)
+        dv = dvf.reshape(B, Hkv, G, T, hd).sum(axis=2)
         dq = rope_bwd(rms_norm_bwd(dqn, qn, rq), cos, sin)
         dk = rope_bwd(rms_norm_bwd(dkn, kn, rk), cos, sin)
-        dqkv = op(np.concatenate([t.transpose(0, 2, 1, 3).reshape(R, d) for t in (dq, dk, dv)], axis=1))
+        dqkv = op(np.concatenate([t.transpose(0, 2, 1, 3).reshape(R, -1) for t in (dq, dk, dv)], axis=1))
         dh1, dwqkv = _lin_bwd(h1o, wqkv, dqkv, fp8)
-        G[f"wq.{i}"], G[f"wk.{i}"], G[f"wv.{i}"] = dwqkv[:d], dwqkv[d:2 * d], dwqkv[2 * d:]
+        Gr[f"wq.{i}"], Gr[f"wk.{i}"], Gr[f"wv.{i}"] = dwqkv[:d], dwqkv[d:d + dkv], dwqkv[d + dkv:]
         g = g + rms_norm_bwd(dh1, h1, r1)
         caches[i] = None
     dwte = np.zeros(P["wte"].shape, dtype=dtype)
     np.add.at(dwte, inp, g)
-    G["wte"] = dwte
-    out["grads"] = G
+    Gr["wte"] = dwte
+    out["grads"] = Gr
     return out
 
 

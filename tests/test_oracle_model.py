@@ -251,3 +251,119 @@ def test_bf16_operand_rounding_points(monkeypatch):
     assert a["loss"] == b["loss"]
     for k in a["grads"]:
         assert np.array_equal(a["grads"][k], b["grads"][k])
+
+
+# ---------------------------------------------------------------------------
+# grouped key/value heads (GQA) and sliding-window layers
+# ---------------------------------------------------------------------------
+TINY_GQA = om.Config(n_layer=3, d_model=32, n_head=4, head_dim=8, hidden=64, vocab=29,
+                     n_kv_head=2, window=3, pattern="SL")
+
+
+def test_window_attention_bruteforce():
+    g = np.random.default_rng(13)
+    H, T, hd, w = 2, 11, 8, 3
+    q, k, v = (g.standard_normal((H, T, hd)) for _ in range(3))
+    y, lse = om.causal_attention(q, k, v, window=w)
+    for h in range(H):
+        for i in range(T):
+            js = [j for j in range(T) if i - w <= j <= i]
+            s = [float(np.dot(q[h, i], k[h, j])) / math.sqrt(hd) for j in js]
+            m = max(s)
+            e = [math.exp(x - m) for x in s]
+            den = sum(e)
+            ref = sum(e[n] / den * v[h, j] for n, j in enumerate(js))
+            assert np.allclose(y[h, i], ref, atol=1e-13)
+            assert lse[h, i] == pytest.approx(m + math.log(den), abs=1e-13)
+    # a window as long as the sequence is the full causal mask
+    y_full, _ = om.causal_attention(q, k, v)
+    y_wide, _ = om.causal_attention(q, k, v, window=T)
+    assert np.array_equal(y_full, y_wide)
+
+
+def test_layer_window_pattern():
+    cfg = TINY_GQA
+    assert [cfg.layer_window(i) for i in range(4)] == [3, None, 3, None]
+    assert om.Config.from_depth(4, 100, window=64, pattern="SSSL").layer_window(3) is None
+    assert om.Config.from_depth(4, 100, window=64, pattern="SSSL").layer_window(5) == 64
+    assert om.Config.from_depth(4, 100).layer_window(0) is None
+    shapes = om.param_shapes(cfg)
+    assert shapes["wk.0"] == (16, 32) and shapes["wv.2"] == (16, 32) and shapes["wq.1"] == (32, 32)
+
+
+def test_finite_differences_gqa_window():
+    cfg = TINY_GQA
+    P = _tiny_params(cfg, seed=51, scale=2.0)
+    ids = _tiny_ids(cfg, B=2, T=9, seed=52)
+    out = om.forward_backward(P, ids, cfg)
+    rng = np.random.default_rng(53)
+    h = 1e-5
+    for name in om.param_names(cfg):
+        W = P[name]
+        for _ in range(3):
+            idx = tuple(int(rng.integers(0, s)) for s in W.shape)
+            if name == "wte":
+                idx = (int(ids[0, int(rng.integers(0, ids.shape[1] - 1))]), idx[1])
+            old = W[idx]
+            W[idx] = old + h
+            lp = om.forward_backward(P, ids, cfg, want_grads=False)["loss"]
+            W[idx] = old - h
+            lm = om.forward_backward(P, ids, cfg, want_grads=False)["loss"]
+            W[idx] = old
+            fd = (lp - lm) / (2 * h)
+            an = out["grads"][name][idx]
+            assert abs(fd - an) / (abs(an) + 1e-4) < 1e-6, (name, idx, fd, an)
+
+
+def test_gqa_window_against_torch_autograd():
+    torch = pytest.importorskip("torch")
+    F = torch.nn.functional
+    cfg = TINY_GQA
+    P = _tiny_params(cfg, seed=61, scale=1.5)
+    ids = _tiny_ids(cfg, B=2, T=10, seed=62)
+    out = om.forward_backward(P, ids, cfg)
+    tp = {k: torch.tensor(v, dtype=torch.float64, requires_grad=True) for k, v in P.items()}
+    B, T = ids.shape[0], ids.shape[1] - 1
+    d, H, Hkv, hd = cfg.d_model, cfg.n_head, cfg.n_kv_head, cfg.head_dim
+    inp, tgt = torch.tensor(ids[:, :T]), torch.tensor(ids[:, 1:])
+    freq = cfg.rope_base ** (-torch.arange(0, hd, 2, dtype=torch.float64) / hd)
+    rot = torch.polar(torch.ones(T, hd // 2, dtype=torch.float64),
+                      torch.arange(T, dtype=torch.float64)[:, None] * freq[None, :])
+
+    def rope_t(x):
+        xc = torch.complex(x[..., : hd // 2], x[..., hd // 2:]) * rot
+        return torch.cat([xc.real, xc.imag], dim=-1)
+
+    def rms(x, n):
+        return F.rms_norm(x, (n,), eps=cfg.eps)
+
+    ii = torch.arange(T)[:, None]
+    jj = torch.arange(T)[None, :]
+    x = tp["wte"][inp]
+    for i in range(cfg.n_layer):
+        h = rms(x, d)
+        q = (h @ tp[f"wq.{i}"].T).view(B, T, H, hd).transpose(1, 2)
+        k = (h @ tp[f"wk.{i}"].T).view(B, T, Hkv, hd).transpose(1, 2)
+        v = (h @ tp[f"wv.{i}"].T).view(B, T, Hkv, hd).transpose(1, 2)
+        q, k = rms(rope_t(q), hd), rms(rope_t(k), hd)
+        w = cfg.layer_window(i)
+        allowed = jj <= ii if w is None else (jj <= ii) & (jj >= ii - w)
+        y = F.scaled_dot_product_attention(q, k.repeat_interleave(H // Hkv, dim=1),
+                                           v.repeat_interleave(H // Hkv, dim=1), attn_mask=allowed)
+        x = x + y.transpose(1, 2).reshape(B, T, d) @ tp[f"wo.{i}"].T
+        h = rms(x, d)
+        x = x + F.relu(h @ tp[f"wfc.{i}"].T).square() @ tp[f"wproj.{i}"].T
+    z = rms(x, d) @ tp["lm_head"].T
+    loss = F.cross_entropy(z.reshape(-1, cfg.vocab), tgt.reshape(-1))
+    loss.backward()
+    assert out["loss"] == pytest.approx(loss.item(), rel=1e-12)
+    for name in om.param_names(cfg):
+        ref = tp[name].grad.numpy()
+        assert np.abs(out["grads"][name] - ref).max() <= 1e-11 * max(1.0, np.abs(ref).max()), name
+
+
+def test_inputs_gqa_shapes():
+    dims = inputs.Dims.from_depth(4, 1000, n_kv_head=1)
+    shp = dict(inputs.packed_tensors(dims))
+    assert shp["wk.0"] == (128, 256) and shp["wv.3"] == (128, 256) and shp["wq.0"] == (256, 256)
+    assert inputs.Dims.from_depth(4).d_kv == 256
