@@ -36,7 +36,8 @@ class GptError(RuntimeError):
 
 class Shape(ctypes.Structure):
     _fields_ = [("depth", ctypes.c_int32), ("vocab", ctypes.c_int32), ("seq_len", ctypes.c_int32),
-                ("batch", ctypes.c_int32), ("precision", ctypes.c_int32)]
+                ("batch", ctypes.c_int32), ("precision", ctypes.c_int32), ("n_kv_head", ctypes.c_int32),
+                ("window", ctypes.c_int32), ("pattern_len", ctypes.c_int32), ("pattern_long", ctypes.c_uint32)]
 
 
 class Params(ctypes.Structure):
@@ -60,8 +61,8 @@ _SIGS = {
                     _vp, _sz, _vp],
     "gpt_op_gemm": [_i32, _i32, _i32, _i32, _vp, _i32, _i64, _i64, _vp, _i32, _i64, _i64, _vp, _i32,
                     _i64, _i64, _f32, _f32, _vp],
-    "gpt_op_attention_fwd": [_i32, _i32, _i32, _vp, _vp, _vp, _i64, _vp, _i64, _vp, _vp],
-    "gpt_op_attention_bwd": [_i32, _i32, _i32, _vp, _vp, _vp, _i64, _vp, _vp, _i64, _vp, _vp, _vp,
+    "gpt_op_attention_fwd": [_i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _i64, _vp, _i64, _vp, _vp],
+    "gpt_op_attention_bwd": [_i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _i64, _vp, _vp, _i64, _vp, _vp, _vp,
                              _vp, _vp, _i64, _vp],
     "gpt_workspace_tensor": [_P(Shape), _i32, _i32, _P(_sz), _P(_sz)],
     "gpt_profile_enable": [ctypes.c_uint64],
@@ -121,8 +122,16 @@ def _stream(stream=None):
     return stream.cuda_stream if hasattr(stream, "cuda_stream") else stream
 
 
-def shape(depth, vocab, seq_len, batch, precision=PREC_BF16):
-    return Shape(depth, vocab, seq_len, batch, precision)
+def shape(depth, vocab, seq_len, batch, precision=PREC_BF16, n_kv_head=0, window=0, pattern=""):
+    """pattern: string of 'S' (windowed) / 'L' (full causal) layers, repeated
+    over the depth (e.g. "SSSL"); empty = every layer full."""
+    bits = 0
+    for i, ch in enumerate(pattern):
+        if ch not in "SL":
+            raise ValueError("pattern letters are S and L")
+        if ch == "L":
+            bits |= 1 << i
+    return Shape(depth, vocab, seq_len, batch, precision, n_kv_head, window, len(pattern), bits)
 
 
 def param_count(sh):
@@ -218,15 +227,16 @@ def gemm(A, B, C, M, N, K, a_layout=LAYOUT_K, b_layout=LAYOUT_K, lda=None, ldb=N
           stride_b, _ptr(C), c_dtype, ldc, stride_c, alpha, beta, _stream(stream))
 
 
-def attention_fwd(q, k, v, out, lse, batch, n_head, seq_len, ld_qkv, ld_out, stream=None):
-    _call("gpt_op_attention_fwd", batch, n_head, seq_len, _ptr(q), _ptr(k), _ptr(v), ld_qkv,
-          _ptr(out), ld_out, _ptr(lse), _stream(stream))
+def attention_fwd(q, k, v, out, lse, batch, n_head, seq_len, ld_qkv, ld_out, n_kv_head=None, window=-1,
+                  stream=None):
+    _call("gpt_op_attention_fwd", batch, n_head, n_kv_head or n_head, seq_len, window, _ptr(q), _ptr(k), _ptr(v),
+          ld_qkv, _ptr(out), ld_out, _ptr(lse), _stream(stream))
 
 
 def attention_bwd(q, k, v, out, dout, lse, delta, dq_acc, dk, dv, batch, n_head, seq_len, ld_qkv,
-                  ld_out, ld_dkv, stream=None):
-    _call("gpt_op_attention_bwd", batch, n_head, seq_len, _ptr(q), _ptr(k), _ptr(v), ld_qkv,
-          _ptr(out), _ptr(dout), ld_out, _ptr(lse), _ptr(delta), _ptr(dq_acc), _ptr(dk), _ptr(dv),
+                  ld_out, ld_dkv, n_kv_head=None, window=-1, stream=None):
+    _call("gpt_op_attention_bwd", batch, n_head, n_kv_head or n_head, seq_len, window, _ptr(q), _ptr(k), _ptr(v),
+          ld_qkv, _ptr(out), _ptr(dout), ld_out, _ptr(lse), _ptr(delta), _ptr(dq_acc), _ptr(dk), _ptr(dv),
           ld_dkv, _stream(stream))
 
 

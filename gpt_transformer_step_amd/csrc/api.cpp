@@ -54,7 +54,7 @@ extern "C" const char* gpt_status_string(gpt_status s) {
 
 extern "C" const char* gpt_last_error(void) { return gs::g_err.c_str(); }
 
-extern "C" int32_t gpt_abi_version(void) { return 1; }
+extern "C" int32_t gpt_abi_version(void) { return 2; }
 
 // ---------------------------------------------------------------------------
 // shapes and layouts
@@ -63,7 +63,15 @@ namespace {
 
 struct Dims {
   int L, d, H, hidden, V, T, B, prec;
+  int Hkv, dkv, dqkv;  // key/value heads, their width 128 Hkv, and the [q | k | v] width d + 2 dkv
+  int window, pat_len;
+  uint32_t pat_long;
   long long N;  // tokens per step
+  // left attention window of layer l (-1: full causal)
+  int layer_window(int l) const {
+    if (window <= 0 || pat_len <= 0) return -1;
+    return ((pat_long >> (l % pat_len)) & 1u) ? -1 : window;
+  }
 };
 
 int check_shape(const gpt_shape* s, Dims* o) {
@@ -79,6 +87,16 @@ int check_shape(const gpt_shape* s, Dims* o) {
   o->L = s->depth;
   o->d = 64 * s->depth;
   o->H = o->d / 128;
+  if (s->n_kv_head < 0 || (s->n_kv_head > 0 && o->H % s->n_kv_head))
+    FAIL(GPT_ERR_SHAPE, "n_kv_head must divide n_head = 32*depth/64");
+  if (s->window < 0) FAIL(GPT_ERR_SHAPE, "window must be >= 0");
+  if (s->pattern_len < 0 || s->pattern_len > 32) FAIL(GPT_ERR_SHAPE, "pattern_len must be in [0, 32]");
+  o->Hkv = s->n_kv_head > 0 ? s->n_kv_head : o->H;
+  o->dkv = 128 * o->Hkv;
+  o->dqkv = o->d + 2 * o->dkv;
+  o->window = s->window;
+  o->pat_len = s->pattern_len;
+  o->pat_long = s->pattern_long;
   o->hidden = 4 * o->d;
   o->V = s->vocab;
   o->T = s->seq_len;
@@ -91,8 +109,10 @@ int check_shape(const gpt_shape* s, Dims* o) {
 // element offsets of the packed parameter tensors
 struct ParamLayout {
   size_t wte, lm_head, total;
-  size_t qkv(const Dims& D, int l) const { return wte_end + (size_t)l * 4 * D.d * D.d; }
-  size_t wo(const Dims& D, int l) const { return qkv(D, l) + (size_t)3 * D.d * D.d; }
+  size_t qkv(const Dims& D, int l) const { return wte_end + (size_t)l * (2 * (size_t)D.d + 2 * (size_t)D.dkv) * D.d; }
+  size_t wk(const Dims& D, int l) const { return qkv(D, l) + (size_t)D.d * D.d; }
+  size_t wv(const Dims& D, int l) const { return wk(D, l) + (size_t)D.dkv * D.d; }
+  size_t wo(const Dims& D, int l) const { return qkv(D, l) + (size_t)D.dqkv * D.d; }
   size_t fc(const Dims& D, int l) const { return s_end + (size_t)l * D.hidden * D.d; }
   size_t proj(const Dims& D, int l) const { return f_end + (size_t)l * D.d * D.hidden; }
   size_t wte_end, s_end, f_end, p_end;
@@ -102,7 +122,7 @@ ParamLayout param_layout(const Dims& D) {
   ParamLayout p;
   p.wte = 0;
   p.wte_end = (size_t)D.V * D.d;
-  p.s_end = p.wte_end + (size_t)D.L * 4 * D.d * D.d;
+  p.s_end = p.wte_end + (size_t)D.L * (2 * (size_t)D.d + 2 * (size_t)D.dkv) * D.d;
   p.f_end = p.s_end + (size_t)D.L * D.hidden * D.d;
   p.p_end = p.f_end + (size_t)D.L * D.d * D.hidden;
   p.lm_head = p.p_end;
@@ -132,8 +152,10 @@ extern "C" gpt_status gpt_param_layout(const gpt_shape* shape, size_t* offsets, 
   int i = 0;
   offsets[i++] = P.wte;
   for (int l = 0; l < D.L; ++l) {
-    const size_t b = P.qkv(D, l);
-    for (int j = 0; j < 4; ++j) offsets[i++] = b + (size_t)j * D.d * D.d;
+    offsets[i++] = P.qkv(D, l);
+    offsets[i++] = P.wk(D, l);
+    offsets[i++] = P.wv(D, l);
+    offsets[i++] = P.wo(D, l);
   }
   for (int l = 0; l < D.L; ++l) offsets[i++] = P.fc(D, l);
   for (int l = 0; l < D.L; ++l) offsets[i++] = P.proj(D, l);
@@ -368,7 +390,7 @@ WS ws_layout(const Dims& D) {
   WS w;
   size_t o = 0;
   auto take = [&](size_t bytes) { size_t r = o; o = al(o + bytes); return r; };
-  const size_t N = (size_t)D.N, d = D.d, H = D.H;
+  const size_t N = (size_t)D.N, d = D.d, H = D.H, Hkv = D.Hkv, dq3 = D.dqkv;
   w.cs = take(2 * (size_t)D.T * 64 * 4);
   w.x = take(N * d * 4);
   w.layer.resize(D.L);
@@ -376,9 +398,9 @@ WS ws_layout(const Dims& D) {
     Layer& L = w.layer[l];
     L.h1 = take(N * d * 2);
     L.r1 = take(N * 4);
-    L.qkv = take(N * 3 * d * 2);
+    L.qkv = take(N * dq3 * 2);
     L.rq = take(N * H * 4);
-    L.rk = take(N * H * 4);
+    L.rk = take(N * Hkv * 4);
     L.att = take(N * d * 2);
     L.lse = take(N * H * 4);
     L.h2 = take(N * d * 2);
@@ -398,12 +420,12 @@ WS ws_layout(const Dims& D) {
   w.dout = take(N * d * 2);
   w.delta = take(N * H * 4);
   w.dq_acc = take(N * d * 4);
-  w.dqkv = take(N * 3 * d * 2);
+  w.dqkv = take(N * dq3 * 2);
   w.dz = take(N * (size_t)vocab_chunk(D) * 2);
   {
     const int Nt = (int)D.N, dd = D.d, hd = D.hidden;
     size_t mx = 0;
-    mx = std::max(mx, wgrad_part_elems(3 * dd, dd, Nt));
+    mx = std::max(mx, wgrad_part_elems(D.dqkv, dd, Nt));
     mx = std::max(mx, wgrad_part_elems(dd, dd, Nt));
     mx = std::max(mx, wgrad_part_elems(hd, dd, Nt));
     mx = std::max(mx, wgrad_part_elems(dd, hd, Nt));
@@ -419,8 +441,8 @@ WS ws_layout(const Dims& D) {
       L.attt = take(N * d);
       L.h2t = take(N * d);
       L.actt = take(N * hd);
-      L.wqkv8 = take(3 * dd);
-      L.wqkv8t = take(3 * dd);
+      L.wqkv8 = take((size_t)D.dqkv * d);
+      L.wqkv8t = take((size_t)D.dqkv * d);
       L.wo8 = take(dd);
       L.wo8t = take(dd);
       L.wfc8 = take(hd * d);
@@ -523,7 +545,7 @@ extern "C" gpt_status gpt_workspace_tensor(const gpt_shape* shape, int32_t which
   switch (which) {
     case 0: *offset = w.x; *bytes = N * d * 4; break;
     case 1: *offset = w.layer[layer].h1; *bytes = N * d * 2; break;
-    case 2: *offset = w.layer[layer].qkv; *bytes = N * 3 * d * 2; break;
+    case 2: *offset = w.layer[layer].qkv; *bytes = N * (size_t)D.dqkv * 2; break;
     case 3: *offset = w.layer[layer].att; *bytes = N * d * 2; break;
     case 4: *offset = w.layer[layer].h2; *bytes = N * d * 2; break;
     case 5: *offset = w.layer[layer].act; *bytes = N * D.hidden * 2; break;
@@ -590,8 +612,8 @@ extern "C" gpt_status gpt_step_fwd(const gpt_shape* shape, const gpt_params* par
     for (int l = 0; l < D.L; ++l) {
       const Layer& L = w.layer[l];
       float* sc = at<float>(ws, w.scales) + (size_t)l * SC_COUNT;
-      TRY(quantize_fp8(W + P.qkv(D, l), 0, d, 3 * d, d, 0, qpart, sc + SC_WQKV, at<uint8_t>(ws, L.wqkv8), d,
-                       at<uint8_t>(ws, L.wqkv8t), 3 * d, s));
+      TRY(quantize_fp8(W + P.qkv(D, l), 0, d, D.dqkv, d, 0, qpart, sc + SC_WQKV, at<uint8_t>(ws, L.wqkv8), d,
+                       at<uint8_t>(ws, L.wqkv8t), D.dqkv, s));
       TRY(quantize_fp8(W + P.wo(D, l), 0, d, d, d, 0, qpart, sc + SC_WO, at<uint8_t>(ws, L.wo8), d,
                        at<uint8_t>(ws, L.wo8t), d, s));
       TRY(quantize_fp8(W + P.fc(D, l), 0, d, hid, d, 0, qpart, sc + SC_WFC, at<uint8_t>(ws, L.wfc8), d,
@@ -631,15 +653,15 @@ extern "C" gpt_status gpt_step_fwd(const gpt_shape* shape, const gpt_params* par
     {
       GemmArgs a;  // [q | k | v] = h1 [Wq; Wk; Wv]^T, q and k rotated and RMS-normalised per head
       ProfScope ps_(P_GEMM_QKV, s);
-      a.M = N; a.N = 3 * d; a.K = d;
+      a.M = N; a.N = D.dqkv; a.K = d;
       a.A = h1; a.lda = d; a.B = W + P.qkv(D, l); a.ldb = d;
-      a.C = qkv; a.ldc = 3 * d;
-      a.rope = cs; a.row_T = D.T; a.n_head = D.H;
+      a.C = qkv; a.ldc = D.dqkv;
+      a.rope = cs; a.row_T = D.T; a.n_head = D.H; a.n_kv_head = D.Hkv;
       a.part = at<float>(ws, L.rq); a.zt = at<float>(ws, L.rk);
       TRY(block_fwd(a, EPI_QKV, d, f8 ? at<uint8_t>(ws, L.wqkv8) : nullptr, sc ? sc + SC_H1 : nullptr,
                     sc ? sc + SC_WQKV : nullptr));
     }
-    { ProfScope ps_(P_ATTN_FWD, s); TRY(launch_attn_fwd(qkv, qkv + d, qkv + 2 * d, 3 * d, att, d, at<float>(ws, L.lse), D.B, D.H, D.T, s)); }
+    { ProfScope ps_(P_ATTN_FWD, s); TRY(launch_attn_fwd(qkv, qkv + d, qkv + d + D.dkv, D.dqkv, att, d, at<float>(ws, L.lse), D.B, D.H, D.Hkv, D.T, D.layer_window(l), s)); }
     TRY(quant_x(att, d, L.attt, sc ? sc + SC_ATT : nullptr, 0));
     {
       GemmArgs a;  // x += att Wo^T
@@ -843,24 +865,25 @@ extern "C" gpt_status gpt_step_bwd_scaled(const gpt_shape* shape, const gpt_para
     }
     for (int part = 0; part < 3; ++part) {
       ProfScope ps_(part == 0 ? P_ATTN_BWD_PRE : part == 1 ? P_ATTN_BWD_KV : P_ATTN_BWD_Q, s);
-      TRY(launch_attn_bwd_part(part, qkv, qkv + d, qkv + 2 * d, 3 * d, att, dout, d, at<float>(ws, L.lse),
-                               at<float>(ws, w.delta), dq_acc, dqkv + d, dqkv + 2 * d, 3 * d, D.B, D.H, D.T, s));
+      TRY(launch_attn_bwd_part(part, qkv, qkv + d, qkv + d + D.dkv, D.dqkv, att, dout, d, at<float>(ws, L.lse),
+                               at<float>(ws, w.delta), dq_acc, dqkv + d, dqkv + d + D.dkv, D.dqkv, D.B, D.H, D.Hkv,
+                               D.T, D.layer_window(l), s));
     }
-    { ProfScope ps_(P_ROPE_BWD, s); TRY(launch_rope_qknorm_bwd(dq_acc, dqkv, qkv, at<float>(ws, L.rq), at<float>(ws, L.rk), cs, N, D.T, D.H, s)); }
-    if (f8) TRY(quant_dy(dqkv, 3 * d, sc + SC_DQKV, 0));
+    { ProfScope ps_(P_ROPE_BWD, s); TRY(launch_rope_qknorm_bwd(dq_acc, dqkv, qkv, at<float>(ws, L.rq), at<float>(ws, L.rk), cs, N, D.T, D.H, D.Hkv, s)); }
+    if (f8) TRY(quant_dy(dqkv, D.dqkv, sc + SC_DQKV, 0));
     {
       GemmArgs a;  // dh = dqkv [Wq; Wk; Wv]
       ProfScope ps_(P_QKV_DGRAD, s);
-      a.M = N; a.N = d; a.K = 3 * d;
-      a.A = dqkv; a.lda = 3 * d; a.B = W + P.qkv(D, l); a.ldb = d; a.b_kcontig = 0;
+      a.M = N; a.N = d; a.K = D.dqkv;
+      a.A = dqkv; a.lda = D.dqkv; a.B = W + P.qkv(D, l); a.ldb = d; a.b_kcontig = 0;
       a.C = dh; a.ldc = d;
-      if (f8) TRY(dgrad_fp8(a, EPI_F32, 3 * d, at<uint8_t>(ws, L.wqkv8t), sc + SC_DQKV, sc + SC_WQKV));
+      if (f8) TRY(dgrad_fp8(a, EPI_F32, D.dqkv, at<uint8_t>(ws, L.wqkv8t), sc + SC_DQKV, sc + SC_WQKV));
       else TRY(gemm_bf16(a, EPI_F32, s));
     }
     {
       ProfScope ps_(P_QKV_WGRAD, s);  // dWqkv = dqkv^T h1
-      if (f8) TRY(wgrad_fp8(dyqt, at<uint8_t>(ws, L.h1t), sc + SC_DQKV, sc + SC_H1, G + P.qkv(D, l), 3 * d, d, N, acc, wpart, s));
-      else TRY(wgrad(dqkv, 3 * d, h1, d, G + P.qkv(D, l), 3 * d, d, N, acc, wpart, s));
+      if (f8) TRY(wgrad_fp8(dyqt, at<uint8_t>(ws, L.h1t), sc + SC_DQKV, sc + SC_H1, G + P.qkv(D, l), D.dqkv, d, N, acc, wpart, s));
+      else TRY(wgrad(dqkv, D.dqkv, h1, d, G + P.qkv(D, l), D.dqkv, d, N, acc, wpart, s));
     }
     { ProfScope ps_(P_RMSNORM_BWD, s); TRY(launch_rmsnorm_bwd(dh, h1, at<float>(ws, L.r1), g, g_bf, N, d, s, qpart)); }
   }
@@ -1030,36 +1053,46 @@ extern "C" gpt_status muon_update(float* Wt, uint16_t* W_bf16, const float* Gm, 
 // ---------------------------------------------------------------------------
 // component: attention
 // ---------------------------------------------------------------------------
-extern "C" gpt_status gpt_op_attention_fwd(int32_t batch, int32_t n_head, int32_t seq_len, const uint16_t* q,
-                                           const uint16_t* k, const uint16_t* v, int64_t ld_qkv, uint16_t* out,
-                                           int64_t ld_out, float* lse, gpt_stream_t stream) {
+namespace {
+int check_attn(int32_t batch, int32_t n_head, int32_t n_kv_head, int32_t seq_len) {
   if (batch < 0 || n_head < 1 || seq_len < 0) FAIL(GPT_ERR_INVALID_ARG, "bad batch/n_head/seq_len");
+  if (n_kv_head < 1 || n_head % n_kv_head) FAIL(GPT_ERR_INVALID_ARG, "n_kv_head must divide n_head");
+  return 0;
+}
+}  // namespace
+
+extern "C" gpt_status gpt_op_attention_fwd(int32_t batch, int32_t n_head, int32_t n_kv_head, int32_t seq_len,
+                                           int32_t window, const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                                           int64_t ld_qkv, uint16_t* out, int64_t ld_out, float* lse,
+                                           gpt_stream_t stream) {
+  TRY(check_attn(batch, n_head, n_kv_head, seq_len));
   if (batch == 0 || seq_len == 0) return GPT_OK;
   if (!q || !k || !v || !out || !lse) FAIL(GPT_ERR_INVALID_ARG, "NULL pointer");
   if (ld_qkv < (int64_t)n_head * 128 || ld_out < (int64_t)n_head * 128 || (ld_qkv % 8) || (ld_out % 8))
     FAIL(GPT_ERR_INVALID_ARG, "leading dimensions must be >= 128*n_head and multiples of 8");
   if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)out) & 15) FAIL(GPT_ERR_INVALID_ARG, "misaligned");
-  TRY(launch_attn_fwd(q, k, v, ld_qkv, out, ld_out, lse, batch, n_head, seq_len, S(stream)));
+  TRY(launch_attn_fwd(q, k, v, ld_qkv, out, ld_out, lse, batch, n_head, n_kv_head, seq_len, window < 0 ? -1 : window,
+                      S(stream)));
   return GPT_OK;
 }
 
-extern "C" gpt_status gpt_op_attention_bwd(int32_t batch, int32_t n_head, int32_t seq_len, const uint16_t* q,
-                                           const uint16_t* k, const uint16_t* v, int64_t ld_qkv, const uint16_t* out,
-                                           const uint16_t* dout, int64_t ld_out, const float* lse, float* delta,
-                                           float* dq_acc, uint16_t* dk, uint16_t* dv, int64_t ld_dkv,
-                                           gpt_stream_t stream) {
-  if (batch < 0 || n_head < 1 || seq_len < 0) FAIL(GPT_ERR_INVALID_ARG, "bad batch/n_head/seq_len");
+extern "C" gpt_status gpt_op_attention_bwd(int32_t batch, int32_t n_head, int32_t n_kv_head, int32_t seq_len,
+                                           int32_t window, const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                                           int64_t ld_qkv, const uint16_t* out, const uint16_t* dout, int64_t ld_out,
+                                           const float* lse, float* delta, float* dq_acc, uint16_t* dk, uint16_t* dv,
+                                           int64_t ld_dkv, gpt_stream_t stream) {
+  TRY(check_attn(batch, n_head, n_kv_head, seq_len));
   if (batch == 0 || seq_len == 0) return GPT_OK;
   if (!q || !k || !v || !out || !dout || !lse || !delta || !dq_acc || !dk || !dv)
     FAIL(GPT_ERR_INVALID_ARG, "NULL pointer");
-  if (ld_qkv < (int64_t)n_head * 128 || ld_out < (int64_t)n_head * 128 || ld_dkv < (int64_t)n_head * 128 ||
+  if (ld_qkv < (int64_t)n_kv_head * 128 || ld_out < (int64_t)n_head * 128 || ld_dkv < (int64_t)n_kv_head * 128 ||
       (ld_qkv % 8) || (ld_out % 8) || (ld_dkv % 8))
-    FAIL(GPT_ERR_INVALID_ARG, "leading dimensions must be >= 128*n_head and multiples of 8");
+    FAIL(GPT_ERR_INVALID_ARG, "leading dimensions too small or not multiples of 8");
   if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)out | (uintptr_t)dout | (uintptr_t)dk |
        (uintptr_t)dv | (uintptr_t)dq_acc) & 15)
     FAIL(GPT_ERR_INVALID_ARG, "misaligned");
-  TRY(launch_attn_bwd(q, k, v, ld_qkv, out, dout, ld_out, lse, delta, dq_acc, dk, dv, ld_dkv, batch, n_head,
-                      seq_len, S(stream)));
+  TRY(launch_attn_bwd(q, k, v, ld_qkv, out, dout, ld_out, lse, delta, dq_acc, dk, dv, ld_dkv, batch, n_head, n_kv_head,
+                      seq_len, window < 0 ? -1 : window, S(stream)));
   return GPT_OK;
 }
 

@@ -119,18 +119,24 @@ constexpr int FQ = 128;                // queries per workgroup
 constexpr int FK = 64;                 // keys per tile
 constexpr int F_STAGE = 2 * FK * 256;  // K tile + V tile
 
+// GEN = false compiles the plain case (every head its own key/value head, no
+// window) without the index arithmetic of the general one.
+template <bool GEN>
 __global__ void __launch_bounds__(256, 2)
 attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
-                long long ld, uint16_t* __restrict__ out, long long ld_out, float* __restrict__ lse, int H, int T) {
+                long long ld, uint16_t* __restrict__ out, long long ld_out, float* __restrict__ lse, int H, int Hkv,
+                int T, int window_arg) {
   __shared__ __attribute__((aligned(16))) char smem[2 * F_STAGE];
+  const int window = GEN ? window_arg : -1;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, lr = lane & 31, lh = lane >> 5;
   const int nqb = (T + FQ - 1) / FQ;
   const int qb = nqb - 1 - blockIdx.x;  // longest rows first
   const int bh = blockIdx.y, b = bh / H, h = bh % H;
+  const int hk = GEN ? h / (H / Hkv) : h;  // key/value head of this query head
   const long long rowbase = (long long)b * T;
   const uint16_t* qh = q + rowbase * ld + h * 128;
-  const uint16_t* kh = k + rowbase * ld + h * 128;
-  const uint16_t* vh = v + rowbase * ld + h * 128;
+  const uint16_t* kh = k + rowbase * ld + hk * 128;
+  const uint16_t* vh = v + rowbase * ld + hk * 128;
 
   const int q0 = qb * FQ;
   const int wq0 = q0 + wave * 32;   // first query of this wave
@@ -157,21 +163,23 @@ attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, 
 
   const int last_key = min(T - 1, q0 + FQ - 1);
   const int ntiles = last_key / FK + 1;
+  const int j0 = window >= 0 ? max(0, q0 - window) / FK : 0;  // first key tile any query of the block sees
 
-  tile_load<FK>(kh, ld, 0, T, smem, tid);
-  tile_load<FK>(vh, ld, 0, T, smem + FK * 256, tid);
+  tile_load<FK>(kh, ld, j0 * FK, T, smem, tid);
+  tile_load<FK>(vh, ld, j0 * FK, T, smem + FK * 256, tid);
   __syncthreads();
 
-  for (int j = 0; j < ntiles; ++j) {
-    const char* sk = smem + (j & 1) * F_STAGE;
+  for (int j = j0; j < ntiles; ++j) {
+    const char* sk = smem + ((j - j0) & 1) * F_STAGE;
     const char* sv = sk + FK * 256;
     if (j + 1 < ntiles) {  // block-uniform; the other stage was last read before the previous barrier
-      char* nk = smem + ((j + 1) & 1) * F_STAGE;
+      char* nk = smem + ((j + 1 - j0) & 1) * F_STAGE;
       tile_load<FK>(kh, ld, (j + 1) * FK, T, nk, tid);
       tile_load<FK>(vh, ld, (j + 1) * FK, T, nk + FK * 256, tid);
     }
     const int key0 = j * FK;
-    if (key0 <= wq0 + 31) {  // wave-uniform: some key precedes some query of the wave
+    // wave-uniform: some key of the tile is visible to some query of the wave
+    if (key0 <= wq0 + 31 && (window < 0 || key0 + FK - 1 >= wq0 - window)) {
       f32x16_t s[2];
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt) {
@@ -182,7 +190,7 @@ attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, 
           s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag16(sk, kt * 32 + lr, ks * 2 + lh), fq[ks], s[kt], 0,
                                                           0, 0);
       }
-      const bool diag = (key0 + FK - 1 > wq0) || (key0 + FK > T);
+      const bool diag = (key0 + FK - 1 > wq0) || (key0 + FK > T) || (window >= 0 && key0 < wq0 + 31 - window);
       // raw scores; the max is taken on raw scores (c > 0) and the scale is
       // folded into the exponent: p = exp2(s c - m)
       float x[32];
@@ -192,7 +200,8 @@ attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, 
 #pragma unroll
           for (int e = 0; e < 16; ++e) {
             const int key = key0 + kt * 32 + 8 * (e >> 2) + 4 * lh + (e & 3);
-            x[kt * 16 + e] = (key <= myq && key < T) ? s[kt][e] : -INFINITY;
+            const bool vis = key <= myq && key < T && (window < 0 || key >= myq - window);
+            x[kt * 16 + e] = vis ? s[kt][e] : -INFINITY;
           }
       } else {
 #pragma unroll
@@ -207,8 +216,10 @@ attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, 
       tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64)) * c;
       const bool need = tmax > m + kRescale;
       if (__any(need)) {
+        // lanes that keep their max scale by 1; with a window a lane may still
+        // be at m = -inf here while another lane of the wave sees its first key
         const float mn = need ? tmax : m;
-        const float alpha = __builtin_amdgcn_exp2f(m - mn);
+        const float alpha = need ? __builtin_amdgcn_exp2f(m - mn) : 1.f;
         l *= alpha;
         m = mn;
 #pragma unroll
@@ -216,10 +227,12 @@ attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, 
 #pragma unroll
           for (int e = 0; e < 16; ++e) o[et][e] *= alpha;
       }
+      // a row that has seen no visible key yet keeps m = -inf; its p are 0
+      const float msafe = m == -INFINITY ? 0.f : m;
       float psum = 0.f;
 #pragma unroll
       for (int i = 0; i < 32; ++i) {
-        x[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(x[i], c, -m));
+        x[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(x[i], c, -msafe));
         psum += x[i];
       }
       l += psum;
@@ -284,22 +297,22 @@ constexpr int KV_LSE = KV_DN + KV_Q * 256;        //   lse * log2e [32], then de
 constexpr int KV_STAGE = KV_LSE + 2 * KV_Q * 4;
 constexpr int KV_TOTAL = KV_STAGE0 + 2 * KV_STAGE;
 
+template <bool GEN>
 __global__ void __launch_bounds__(256, 2)
 attn_bwd_kv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
                    long long ld, const uint16_t* __restrict__ dout, long long ld_out, const float* __restrict__ lse,
                    const float* __restrict__ delta, uint16_t* __restrict__ dk, uint16_t* __restrict__ dv,
-                   long long ld_dkv, int H, int T) {
+                   long long ld_dkv, int H, int Hkv, int T, int window_arg) {
   __shared__ __attribute__((aligned(16))) char smem[KV_TOTAL];
+  const int window = GEN ? window_arg : -1;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, lr = lane & 31, lh = lane >> 5;
   const int kb = blockIdx.x;
-  const int bh = blockIdx.y, b = bh / H, h = bh % H;
+  // one key/value head; its G query heads are processed one after the other
+  const int bhk = blockIdx.y, b = bhk / Hkv, hk = bhk % Hkv;
+  const int G = GEN ? H / Hkv : 1;
   const long long rowbase = (long long)b * T;
-  const uint16_t* qh = q + rowbase * ld + h * 128;
-  const uint16_t* kh = k + rowbase * ld + h * 128;
-  const uint16_t* vh = v + rowbase * ld + h * 128;
-  const uint16_t* doh = dout + rowbase * ld_out + h * 128;
-  const float* lseh = lse + (long long)bh * T;
-  const float* delh = delta + (long long)bh * T;
+  const uint16_t* kh = k + rowbase * ld + hk * 128;
+  const uint16_t* vh = v + rowbase * ld + hk * 128;
   const float c = kScale * kLog2e;
 
   const int k0 = kb * KV_KEYS;
@@ -326,34 +339,45 @@ attn_bwd_kv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
 
   const int nqt = (T + KV_Q - 1) / KV_Q;
   const int qt_first = k0 / KV_Q;
+  // last query tile that sees a key of the block (+1)
+  const int qt_end = window >= 0 ? min(nqt, (k0 + KV_KEYS - 1 + window) / KV_Q + 1) : nqt;
+  const int nq = max(0, qt_end - qt_first);
+  const int n_it = G * nq;  // (query head, query tile) pairs
   char* stages = smem + KV_STAGE0;
 
+  // iteration it: query head hk G + it / nq, query tile qt_first + it % nq
+  auto hq_of = [&](int it) { return GEN ? hk * G + it / nq : hk; };
+  auto q_of = [&](int it) { return q + rowbase * ld + hq_of(it) * 128; };
+  auto do_of = [&](int it) { return dout + rowbase * ld_out + hq_of(it) * 128; };
+  auto qt_of = [&](int it) { return GEN ? qt_first + it % nq : qt_first + it; };
   // threads < 64 hold the per-query statistics of a tile: lse (first 32), delta (next 32)
-  auto stat_of = [&](int qt) -> float {
-    const int i = tid & 31, qq = qt * KV_Q + i;
-    if (tid < KV_Q) return qq < T ? lseh[qq] * kLog2e : INFINITY;
-    return qq < T ? delh[qq] : 0.f;
+  auto stat_of = [&](int it) -> float {
+    const long long row = ((long long)b * H + hq_of(it)) * T;
+    const int i = tid & 31, qq = qt_of(it) * KV_Q + i;
+    if (tid < KV_Q) return qq < T ? lse[row + qq] * kLog2e : INFINITY;
+    return qq < T ? delta[row + qq] : 0.f;
   };
 
   float stat = 0.f;
-  if (qt_first < nqt) {
-    tile_load<KV_Q>(qh, ld, qt_first * KV_Q, T, stages + KV_QN, tid);
-    tile_load<KV_Q>(doh, ld_out, qt_first * KV_Q, T, stages + KV_DN, tid);
-    if (tid < 2 * KV_Q) reinterpret_cast<float*>(stages + KV_LSE)[tid] = stat_of(qt_first);
+  if (n_it > 0) {
+    tile_load<KV_Q>(q_of(0), ld, qt_of(0) * KV_Q, T, stages + KV_QN, tid);
+    tile_load<KV_Q>(do_of(0), ld_out, qt_of(0) * KV_Q, T, stages + KV_DN, tid);
+    if (tid < 2 * KV_Q) reinterpret_cast<float*>(stages + KV_LSE)[tid] = stat_of(0);
   }
   __syncthreads();
 
-  for (int qt = qt_first; qt < nqt; ++qt) {
-    const char* st = stages + ((qt - qt_first) & 1) * KV_STAGE;
-    char* so = stages + ((qt - qt_first + 1) & 1) * KV_STAGE;
-    const bool more = qt + 1 < nqt;  // block-uniform
+  for (int it = 0; it < n_it; ++it) {
+    const char* st = stages + (it & 1) * KV_STAGE;
+    char* so = stages + ((it + 1) & 1) * KV_STAGE;
+    const bool more = it + 1 < n_it;  // block-uniform
     if (more) {
-      tile_load<KV_Q>(qh, ld, (qt + 1) * KV_Q, T, so + KV_QN, tid);
-      tile_load<KV_Q>(doh, ld_out, (qt + 1) * KV_Q, T, so + KV_DN, tid);
-      if (tid < 2 * KV_Q) stat = stat_of(qt + 1);
+      tile_load<KV_Q>(q_of(it + 1), ld, qt_of(it + 1) * KV_Q, T, so + KV_QN, tid);
+      tile_load<KV_Q>(do_of(it + 1), ld_out, qt_of(it + 1) * KV_Q, T, so + KV_DN, tid);
+      if (tid < 2 * KV_Q) stat = stat_of(it + 1);
     }
-    const int q0 = qt * KV_Q;
-    if (q0 + KV_Q - 1 >= wk0) {  // wave-uniform: some query of the tile sees some key of the wave
+    const int q0 = qt_of(it) * KV_Q;
+    // wave-uniform: some query of the tile sees some key of the wave
+    if (q0 + KV_Q - 1 >= wk0 && (window < 0 || q0 <= wk0 + 31 + window)) {
       f32x16_t sacc, dpacc;
 #pragma unroll
       for (int e = 0; e < 16; ++e) { sacc[e] = 0.f; dpacc[e] = 0.f; }
@@ -365,7 +389,8 @@ attn_bwd_kv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
       }
       const float* slse = reinterpret_cast<const float*>(st + KV_LSE);
       const float* sdel = slse + KV_Q;
-      const bool diag = (q0 < wk0 + 31) || (q0 + KV_Q > T) || (wk0 + 32 > T);
+      const bool diag = (q0 < wk0 + 31) || (q0 + KV_Q > T) || (wk0 + 32 > T) ||
+                        (window >= 0 && q0 + KV_Q - 1 > wk0 + window);
       // P and dS packed to bf16 in accumulator order (k-step s: values 8s .. 8s+7)
       bf16x8_t fp[2], fs[2];
 #pragma unroll
@@ -380,7 +405,8 @@ attn_bwd_kv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
             const int e = 8 * s2 + 2 * i + u;
             const int ql = 8 * (e >> 2) + 4 * lh + (e & 3);
             float pe = __builtin_amdgcn_exp2f(sacc[e] * c - slse[ql]);
-            if (diag) pe = (mykey <= q0 + ql && mykey < T) ? pe : 0.f;
+            if (diag)
+              pe = (mykey <= q0 + ql && mykey < T && (window < 0 || mykey >= q0 + ql - window)) ? pe : 0.f;
             pv[u] = pe;
             dv2[u] = pe * (dpacc[e] - sdel[ql]);
           }
@@ -401,8 +427,8 @@ attn_bwd_kv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
   }
 
   if (mykey < T) {
-    uint16_t* dkr = dk + (rowbase + mykey) * ld_dkv + h * 128;
-    uint16_t* dvr = dv + (rowbase + mykey) * ld_dkv + h * 128;
+    uint16_t* dkr = dk + (rowbase + mykey) * ld_dkv + hk * 128;
+    uint16_t* dvr = dv + (rowbase + mykey) * ld_dkv + hk * 128;
 #pragma unroll
     for (int et = 0; et < 4; ++et)
 #pragma unroll
@@ -424,20 +450,24 @@ constexpr int DQ_Q = 128;
 constexpr int DQ_K = 64;
 constexpr int DQ_STAGE = 2 * DQ_K * 256;  // K tile + V tile
 
+template <bool GEN>
 __global__ void __launch_bounds__(256, 2)
 attn_bwd_q_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
                   long long ld, const uint16_t* __restrict__ dout, long long ld_out, const float* __restrict__ lse,
-                  const float* __restrict__ delta, float* __restrict__ dq_out, int H, int T) {
+                  const float* __restrict__ delta, float* __restrict__ dq_out, int H, int Hkv, int T,
+                  int window_arg) {
   __shared__ __attribute__((aligned(16))) char smem[2 * DQ_STAGE];
+  const int window = GEN ? window_arg : -1;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, lr = lane & 31, lh = lane >> 5;
   const int nqb = (T + DQ_Q - 1) / DQ_Q;
   const int qb = nqb - 1 - blockIdx.x;  // longest rows first
   const int bh = blockIdx.y, b = bh / H, h = bh % H;
+  const int hk = GEN ? h / (H / Hkv) : h;
   const long long rowbase = (long long)b * T;
   const int d = H * 128;
   const uint16_t* qh = q + rowbase * ld + h * 128;
-  const uint16_t* kh = k + rowbase * ld + h * 128;
-  const uint16_t* vh = v + rowbase * ld + h * 128;
+  const uint16_t* kh = k + rowbase * ld + hk * 128;
+  const uint16_t* vh = v + rowbase * ld + hk * 128;
   const uint16_t* doh = dout + rowbase * ld_out + h * 128;
   const float c = kScale * kLog2e;
 
@@ -466,20 +496,21 @@ attn_bwd_q_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k
 
   const int last_key = min(T - 1, q0 + DQ_Q - 1);
   const int ntiles = last_key / DQ_K + 1;
-  tile_load<DQ_K>(kh, ld, 0, T, smem, tid);
-  tile_load<DQ_K>(vh, ld, 0, T, smem + DQ_K * 256, tid);
+  const int j0 = window >= 0 ? max(0, q0 - window) / DQ_K : 0;
+  tile_load<DQ_K>(kh, ld, j0 * DQ_K, T, smem, tid);
+  tile_load<DQ_K>(vh, ld, j0 * DQ_K, T, smem + DQ_K * 256, tid);
   __syncthreads();
 
-  for (int j = 0; j < ntiles; ++j) {
-    const char* sk = smem + (j & 1) * DQ_STAGE;
+  for (int j = j0; j < ntiles; ++j) {
+    const char* sk = smem + ((j - j0) & 1) * DQ_STAGE;
     const char* sv = sk + DQ_K * 256;
     if (j + 1 < ntiles) {
-      char* nk = smem + ((j + 1) & 1) * DQ_STAGE;
+      char* nk = smem + ((j + 1 - j0) & 1) * DQ_STAGE;
       tile_load<DQ_K>(kh, ld, (j + 1) * DQ_K, T, nk, tid);
       tile_load<DQ_K>(vh, ld, (j + 1) * DQ_K, T, nk + DQ_K * 256, tid);
     }
     const int key0 = j * DQ_K;
-    if (key0 <= wq0 + 31) {  // wave-uniform
+    if (key0 <= wq0 + 31 && (window < 0 || key0 + DQ_K - 1 >= wq0 - window)) {  // wave-uniform
       f32x16_t st2[2], dpt[2];
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt) {
@@ -493,7 +524,7 @@ attn_bwd_q_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k
                                                             0, 0, 0);
         }
       }
-      const bool diag = (key0 + DQ_K - 1 > wq0) || (key0 + DQ_K > T);
+      const bool diag = (key0 + DQ_K - 1 > wq0) || (key0 + DQ_K > T) || (window >= 0 && key0 < wq0 + 31 - window);
       float ds[32];
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
@@ -502,7 +533,7 @@ attn_bwd_q_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k
           float pv = __builtin_amdgcn_exp2f(st2[kt][e] * c - lse2);
           if (diag) {
             const int key = key0 + kt * 32 + 8 * (e >> 2) + 4 * lh + (e & 3);
-            pv = (key <= myq && key < T) ? pv : 0.f;
+            pv = (key <= myq && key < T && (window < 0 || key >= myq - window)) ? pv : 0.f;
           }
           ds[kt * 16 + e] = pv * (dpt[kt][e] - del);
         }
@@ -532,31 +563,34 @@ attn_bwd_q_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k
 }  // namespace
 
 int launch_attn_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, long long ld_qkv, uint16_t* out,
-                    long long ld_out, float* lse, int B, int H, int T, hipStream_t s) {
+                    long long ld_out, float* lse, int B, int H, int Hkv, int T, int window, hipStream_t s) {
   if (B <= 0 || T <= 0) return 0;
   dim3 grid((T + FQ - 1) / FQ, B * H);
-  hipLaunchKernelGGL(attn_fwd_kernel, grid, dim3(256), 0, s, q, k, v, ld_qkv, out, ld_out, lse, H, T);
+  const bool gen = Hkv != H || window >= 0;
+  hipLaunchKernelGGL(gen ? attn_fwd_kernel<true> : attn_fwd_kernel<false>, grid, dim3(256), 0, s, q, k, v, ld_qkv, out,
+                     ld_out, lse, H, Hkv, T, window);
   GS_LAUNCH_CHECK("attn_fwd");
   return 0;
 }
 
 int launch_attn_bwd_part(int part, const uint16_t* q, const uint16_t* k, const uint16_t* v, long long ld_qkv,
                          const uint16_t* out, const uint16_t* dout, long long ld_out, const float* lse, float* delta,
-                         float* dq, uint16_t* dk, uint16_t* dv, long long ld_dkv, int B, int H, int T,
-                         hipStream_t s) {
+                         float* dq, uint16_t* dk, uint16_t* dv, long long ld_dkv, int B, int H, int Hkv, int T,
+                         int window, hipStream_t s) {
   if (B <= 0 || T <= 0) return 0;
+  const bool gen = Hkv != H || window >= 0;
   if (part == 0) {
     const long long NH = (long long)B * T * H;
     hipLaunchKernelGGL(attn_bwd_pre_kernel, dim3((unsigned)((NH + 3) / 4)), dim3(256), 0, s, out, dout, ld_out,
                        delta, H, T, NH);
     GS_LAUNCH_CHECK("attn_bwd_pre");
   } else if (part == 1) {
-    hipLaunchKernelGGL(attn_bwd_kv_kernel, dim3((T + KV_KEYS - 1) / KV_KEYS, B * H), dim3(256), 0, s, q, k, v,
-                       ld_qkv, dout, ld_out, lse, delta, dk, dv, ld_dkv, H, T);
+    hipLaunchKernelGGL(gen ? attn_bwd_kv_kernel<true> : attn_bwd_kv_kernel<false>, dim3((T + KV_KEYS - 1) / KV_KEYS, B * Hkv), dim3(256), 0, s, q, k, v,
+                       ld_qkv, dout, ld_out, lse, delta, dk, dv, ld_dkv, H, Hkv, T, window);
     GS_LAUNCH_CHECK("attn_bwd_kv");
   } else {
-    hipLaunchKernelGGL(attn_bwd_q_kernel, dim3((T + DQ_Q - 1) / DQ_Q, B * H), dim3(256), 0, s, q, k, v, ld_qkv,
-                       dout, ld_out, lse, delta, dq, H, T);
+    hipLaunchKernelGGL(gen ? attn_bwd_q_kernel<true> : attn_bwd_q_kernel<false>, dim3((T + DQ_Q - 1) / DQ_Q, B * H), dim3(256), 0, s, q, k, v, ld_qkv,
+                       dout, ld_out, lse, delta, dq, H, Hkv, T, window);
     GS_LAUNCH_CHECK("attn_bwd_q");
   }
   return 0;
@@ -564,11 +598,11 @@ int launch_attn_bwd_part(int part, const uint16_t* q, const uint16_t* k, const u
 
 int launch_attn_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, long long ld_qkv,
                     const uint16_t* out, const uint16_t* dout, long long ld_out, const float* lse, float* delta,
-                    float* dq, uint16_t* dk, uint16_t* dv, long long ld_dkv, int B, int H, int T,
-                    hipStream_t s) {
+                    float* dq, uint16_t* dk, uint16_t* dv, long long ld_dkv, int B, int H, int Hkv, int T,
+                    int window, hipStream_t s) {
   for (int part = 0; part < 3; ++part) {
     const int rc = launch_attn_bwd_part(part, q, k, v, ld_qkv, out, dout, ld_out, lse, delta, dq, dk, dv, ld_dkv, B,
-                                        H, T, s);
+                                        H, Hkv, T, window, s);
     if (rc) return rc;
   }
   return 0;

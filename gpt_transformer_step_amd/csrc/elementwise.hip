@@ -196,22 +196,30 @@ __device__ __forceinline__ void rope_norm_head_bwd(float dy1, float dy2, const u
   out[lane + 64] = f2bf(-d1 * sn + d2 * c);
 }
 
+// one wave per (token, head slot): slots 0 .. H-1 are the query heads (gradient
+// from dq_acc, fp32 [N, 128 H]), slots H .. H+Hkv-1 the key heads (gradient in
+// place in dqkv); rows of qkv / dqkv are d + 2 dkv wide
 __global__ void __launch_bounds__(256) rope_qknorm_bwd_kernel(const float* __restrict__ dq_acc, uint16_t* __restrict__ dqkv,
                                        const uint16_t* __restrict__ qkv, const float* __restrict__ rq,
                                        const float* __restrict__ rk, const float* __restrict__ cs,
-                                       long long N, int T, int H) {
+                                       long long N, int T, int H, int Hkv) {
   const int lane = threadIdx.x & 63;
+  const int HS = H + Hkv;
   const long long w = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (w >= N * H) return;
-  const long long n = w / H;
-  const int hh = (int)(w % H), t = (int)(n % T);
-  const int d = H * 128;
-  const float* dq = dq_acc + n * d + hh * 128;
-  rope_norm_head_bwd(dq[lane], dq[lane + 64], qkv + n * 3 * d + hh * 128, rq[w], cs, T, t, lane,
-                     dqkv + n * 3 * d + hh * 128);
-  uint16_t* dk = dqkv + n * 3 * d + d + hh * 128;
-  const float k1 = bf2f(dk[lane]), k2 = bf2f(dk[lane + 64]);
-  rope_norm_head_bwd(k1, k2, qkv + n * 3 * d + d + hh * 128, rk[w], cs, T, t, lane, dk);
+  if (w >= N * HS) return;
+  const long long n = w / HS;
+  const int hh = (int)(w % HS), t = (int)(n % T);
+  const int d = H * 128, ldq = d + 2 * Hkv * 128;
+  if (hh < H) {
+    const float* dq = dq_acc + n * d + hh * 128;
+    rope_norm_head_bwd(dq[lane], dq[lane + 64], qkv + n * ldq + hh * 128, rq[n * H + hh], cs, T, t, lane,
+                       dqkv + n * ldq + hh * 128);
+  } else {
+    const int hk = hh - H;
+    uint16_t* dk = dqkv + n * ldq + d + hk * 128;
+    const float k1 = bf2f(dk[lane]), k2 = bf2f(dk[lane + 64]);
+    rope_norm_head_bwd(k1, k2, qkv + n * ldq + d + hk * 128, rk[n * Hkv + hk], cs, T, t, lane, dk);
+  }
 }
 
 // lse = log-sum-exp over the per-tile (max, sum exp) partials; loss = lse - z[target]
@@ -478,9 +486,9 @@ int launch_rmsnorm_bwd(const float* dh, const uint16_t* h, const float* r, float
 }
 
 int launch_rope_qknorm_bwd(const float* dq_acc, uint16_t* dqkv, const uint16_t* qkv, const float* rq,
-                           const float* rk, const float* cs, long long N, int T, int H, hipStream_t s) {
-  hipLaunchKernelGGL(rope_qknorm_bwd_kernel, dim3(nblocks(N * H, 4)), dim3(256), 0, s, dq_acc, dqkv, qkv, rq,
-                     rk, cs, N, T, H);
+                           const float* rk, const float* cs, long long N, int T, int H, int Hkv, hipStream_t s) {
+  hipLaunchKernelGGL(rope_qknorm_bwd_kernel, dim3(nblocks(N * (H + Hkv), 4)), dim3(256), 0, s, dq_acc, dqkv, qkv,
+                     rq, rk, cs, N, T, H, Hkv);
   GS_LAUNCH_CHECK("rope_qknorm_bwd");
   return 0;
 }

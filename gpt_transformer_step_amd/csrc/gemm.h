@@ -45,7 +45,8 @@ struct GemmArgs {
   int k_split = 1;               // > 1: EPI_F32_ATOMIC, or EPI_F32 writing one partial per split
   long long split_stride = 0;    // EPI_F32 with k_split > 1: split s writes C + s * split_stride
   const float* rope = nullptr;    // EPI_QKV: cos [row_T, 64] then sin [row_T, 64]
-  int n_head = 0;                 // EPI_QKV: heads per q (and k) block
+  int n_head = 0;                 // EPI_QKV: query heads
+  int n_kv_head = 0;              // EPI_QKV: key/value heads (0 = n_head); columns [q | k | v]
   const float* scale_a = nullptr;  // fp8: device scalars; v *= 1 / (scale_a * scale_b)
   const float* scale_b = nullptr;
   float* amax = nullptr;           // bf16 epilogues: per-wave max |stored value| at

@@ -506,7 +506,8 @@ __global__ void __launch_bounds__((Cfg<BM, BN>::NT), 1) gemm_kernel(GemmArgs p) 
     static_assert(WN == 128, "EPI_QKV needs 128 columns per wave");
     const int nb = n0 + wn * WN;  // first column of this wave's head
     const int dmodel = p.n_head * 128;
-    if (nb < 2 * dmodel) {        // q or k head (wave-uniform)
+    const int nkv = p.n_kv_head ? p.n_kv_head : p.n_head;
+    if (nb < dmodel + nkv * 128) {  // q or k head (wave-uniform)
 #pragma unroll
       for (int i = 0; i < TM; ++i) {
         const int m = m0 + wm * WM + i * 32 + lr;
@@ -536,9 +537,8 @@ __global__ void __launch_bounds__((Cfg<BM, BN>::NT), 1) gemm_kernel(GemmArgs p) 
 #pragma unroll
           for (int e = 0; e < 16; ++e) acc[i][j][e] *= rr;
         if (lh == 0 && m < p.M) {
-          const int head = (nb % dmodel) / 128;
-          float* rdst = (nb < dmodel) ? p.part : p.zt;
-          rdst[(long long)m * p.n_head + head] = rr;
+          if (nb < dmodel) p.part[(long long)m * p.n_head + nb / 128] = rr;
+          else p.zt[(long long)m * nkv + (nb - dmodel) / 128] = rr;
         }
       }
     }

@@ -18,8 +18,9 @@ int launch_rmsnorm_fwd(const float* x, uint16_t* h, float* r, long long N, int d
                        float* amax_part = nullptr);
 int launch_rmsnorm_bwd(const float* dh, const uint16_t* h, const float* r, float* g, uint16_t* g_bf,
                        long long N, int d, hipStream_t s, float* amax_part = nullptr);
+// one wave per (token, head) over the n_head query heads and n_kv_head key heads
 int launch_rope_qknorm_bwd(const float* dq_acc, uint16_t* dqkv, const uint16_t* qkv, const float* rq,
-                           const float* rk, const float* cos_sin, long long N, int T, int H,
+                           const float* rk, const float* cos_sin, long long N, int T, int H, int Hkv,
                            hipStream_t s);
 int launch_ce_reduce(const float* part, int nparts, const float* zt, float* lse, float* row_loss,
                      float* lse_out, long long N, hipStream_t s);
@@ -44,17 +45,20 @@ int launch_adamw(float* W, uint16_t* Wb, const float* G, float* M, float* V, lon
                  float b2, float eps, float wd, float inv_bc1, float inv_bc2, float gs, hipStream_t s);
 
 // --- attention (attention.hip) ---------------------------------------------
+// H query heads, Hkv key/value heads (query head h reads head h / (H / Hkv));
+// window: left window (query i sees keys i - window .. i), -1 = full causal
 int launch_attn_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, long long ld_qkv,
-                    uint16_t* out, long long ld_out, float* lse, int B, int H, int T, hipStream_t s);
+                    uint16_t* out, long long ld_out, float* lse, int B, int H, int Hkv, int T, int window,
+                    hipStream_t s);
 int launch_attn_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, long long ld_qkv,
                     const uint16_t* out, const uint16_t* dout, long long ld_out, const float* lse,
                     float* delta, float* dq, uint16_t* dk, uint16_t* dv, long long ld_dkv, int B,
-                    int H, int T, hipStream_t s);
+                    int H, int Hkv, int T, int window, hipStream_t s);
 // one of the three backward kernels: 0 = delta = rowsum(dout * out), 1 = dK/dV, 2 = dQ
 int launch_attn_bwd_part(int part, const uint16_t* q, const uint16_t* k, const uint16_t* v, long long ld_qkv,
                          const uint16_t* out, const uint16_t* dout, long long ld_out, const float* lse, float* delta,
-                         float* dq, uint16_t* dk, uint16_t* dv, long long ld_dkv, int B, int H, int T,
-                         hipStream_t s);
+                         float* dq, uint16_t* dk, uint16_t* dv, long long ld_dkv, int B, int H, int Hkv, int T,
+                         int window, hipStream_t s);
 
 // --- fp8 quantisation (fp8.hip) --------------------------------------------
 // Tensors are [rows, cols] with row stride ld (elements); rows % 16 == 0,

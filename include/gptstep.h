@@ -66,21 +66,39 @@ typedef enum {
 
 /* The model and batch.  d_model = 64*depth, n_head = d_model/128,
  * hidden = 4*d_model.  Limits: 2 <= depth <= 64 and even; 1 <= vocab <= 2^24;
- * 1 <= seq_len <= 16384; 1 <= batch; batch*seq_len <= 2^24. */
+ * 1 <= seq_len <= 16384; 1 <= batch; batch*seq_len <= 2^24.
+ *
+ * Attention variants (dev.to page, "1. Modelo GPT": grouped-query attention
+ * and sliding-window layers in a pattern such as "SSSL"; "5. Unificación Flash
+ * Attention": the window_size argument).  Zero-initialised fields give plain
+ * multi-head, full causal attention in every layer:
+ *   n_kv_head       key/value heads (0 = n_head); must divide n_head.  Query
+ *                   head h reads key/value head h / (n_head / n_kv_head).
+ *   window          left window of the short layers: query i sees keys
+ *                   i - window .. i (0 = no short layers).
+ *   pattern_len     length of the layer pattern, 1 .. 32 (0 = all long);
+ *   pattern_long    bit i set = pattern position i is 'L' (full causal),
+ *                   clear = 'S' (windowed); layer l takes position l % len.
+ *                   "SSSL" is pattern_len 4, pattern_long 0x8. */
 typedef struct {
   int32_t depth;
   int32_t vocab;
   int32_t seq_len;   /* T: tokens per sequence (ids carry T+1 per row) */
   int32_t batch;     /* B: sequences per step */
   int32_t precision; /* gpt_precision */
+  int32_t n_kv_head;
+  int32_t window;
+  int32_t pattern_len;
+  uint32_t pattern_long;
 } gpt_shape;
 
 /* Packed parameter buffers, all with gpt_param_count() elements in the packed
- * order: wte [V,d] | for each layer: wq, wk, wv, wo [d,d] | for each layer
- * wfc [4d,d] | for each layer wproj [d,4d] | lm_head [V,d], each row-major
- * [out, in].  wq, wk, wv of one layer are adjacent, so they form one [3d,d]
- * operand.  The S group is the 4*depth [d,d] matrices, the F group the depth
- * wfc matrices, the P group the depth wproj matrices. */
+ * order: wte [V,d] | for each layer: wq [d,d], wk [dkv,d], wv [dkv,d], wo [d,d]
+ * (dkv = 128 n_kv_head; d without grouped heads) | for each layer wfc [4d,d] |
+ * for each layer wproj [d,4d] | lm_head [V,d], each row-major [out, in].  wq,
+ * wk, wv of one layer are adjacent, so they form one [d+2dkv, d] operand.
+ * Without grouped heads the S group is the 4*depth [d,d] matrices; the F group
+ * is the depth wfc matrices, the P group the depth wproj matrices. */
 typedef struct {
   const float* master;  /* fp32 master weights (read by nothing in fwd/bwd) */
   const uint16_t* bf16; /* bf16 working copy (bit patterns) used by fwd/bwd */
@@ -171,7 +189,8 @@ gpt_status muon_update(float* W, uint16_t* W_bf16, const float* G, float* M, flo
 const char* gpt_status_string(gpt_status status);
 const char* gpt_last_error(void);
 
-/* Library ABI version (bumped on any signature change). */
+/* Library ABI version (bumped on any signature change; 2: gpt_shape carries
+ * the attention variants). */
 int32_t gpt_abi_version(void);
 
 #ifdef __cplusplus

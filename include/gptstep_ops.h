@@ -66,21 +66,26 @@ gpt_status gpt_op_gemm_fp8(int32_t M, int32_t N, int32_t K, const uint8_t* A, in
                            const float* scale_a, const float* scale_b, float beta, gpt_stream_t stream);
 
 /* Causal multi-head attention forward with head width 128 (dev.to page,
- * "5. Unificación Flash Attention": flash_attn_func(q, k, v, causal=True)):
- *   out[b,t,h,:] = sum_{j<=t} softmax_j(q[b,t,h,:] . k[b,j,h,:] / sqrt(128)) v[b,j,h,:]
- * q, k, v, out: bf16, element (b, t, h, e) at ptr[(b*T + t) * ld + h*128 + e]
- * (ld in elements, multiple of 8).  lse: fp32 [B, H, T], the natural-log
- * log-sum-exp of each row of scaled scores (needed by the backward). */
-gpt_status gpt_op_attention_fwd(int32_t batch, int32_t n_head, int32_t seq_len, const uint16_t* q,
-                                const uint16_t* k, const uint16_t* v, int64_t ld_qkv,
+ * "5. Unificación Flash Attention": flash_attn_func(q, k, v, causal=True,
+ * window_size=...)):
+ *   out[b,t,h,:] = sum_{j in W(t)} softmax_j(q[b,t,h,:] . k[b,j,g(h),:] / sqrt(128)) v[b,j,g(h),:]
+ * with W(t) = {j : j <= t, and j >= t - window when window >= 0} (window < 0:
+ * full causal) and g(h) = h / (n_head / n_kv_head) (n_kv_head divides
+ * n_head).  q, out: bf16, element (b, t, h, e) at ptr[(b*T + t) * ld + h*128 + e];
+ * k, v: the same with n_kv_head heads (ld in elements, multiple of 8).
+ * lse: fp32 [B, H, T], the natural-log log-sum-exp of each row of scaled
+ * scores (needed by the backward). */
+gpt_status gpt_op_attention_fwd(int32_t batch, int32_t n_head, int32_t n_kv_head, int32_t seq_len, int32_t window,
+                                const uint16_t* q, const uint16_t* k, const uint16_t* v, int64_t ld_qkv,
                                 uint16_t* out, int64_t ld_out, float* lse, gpt_stream_t stream);
 
 /* Backward of gpt_op_attention_fwd given dout (same layout as out):
  *   dq_acc fp32, element (b,t,h,e) at dq_acc[(b*T+t) * H*128 + h*128 + e] (written);
- *   dk, dv bf16 in the q/k/v layout with leading dimension ld_dkv;
+ *   dk, dv bf16 in the k/v layout with leading dimension ld_dkv (written; a
+ *   key/value head receives the sum over its query heads);
  *   delta: fp32 scratch [B, H, T] (receives rowsum(dout * out)). */
-gpt_status gpt_op_attention_bwd(int32_t batch, int32_t n_head, int32_t seq_len, const uint16_t* q,
-                                const uint16_t* k, const uint16_t* v, int64_t ld_qkv,
+gpt_status gpt_op_attention_bwd(int32_t batch, int32_t n_head, int32_t n_kv_head, int32_t seq_len, int32_t window,
+                                const uint16_t* q, const uint16_t* k, const uint16_t* v, int64_t ld_qkv,
                                 const uint16_t* out, const uint16_t* dout, int64_t ld_out,
                                 const float* lse, float* delta, float* dq_acc, uint16_t* dk,
                                 uint16_t* dv, int64_t ld_dkv, gpt_stream_t stream);

@@ -42,7 +42,7 @@ def test_every_declared_symbol_is_exported(B):
 
 def test_abi_version_and_status_strings(B):
     lib = B.lib()
-    assert lib.gpt_abi_version() == 1
+    assert lib.gpt_abi_version() == 2
     for code, text in [(0, b"ok"), (-1, b"invalid argument"), (-2, b"invalid shape"),
                        (-3, b"workspace too small"), (-4, b"HIP runtime error"), (-5, b"unsupported")]:
         assert lib.gpt_status_string(code) == text

@@ -102,3 +102,74 @@ def test_attention_full_size_sampled(B):
         say(f"  (b={b}, h={h}) out rel_l2 {e:.3e}")
         assert e <= 1e-2
         assert np.abs(lse[b, h].cpu().numpy() - l).max() < 1e-3
+
+
+@pytest.mark.parametrize("Bn,H,Hkv,T,window", [
+    (2, 4, 2, 200, 37),      # grouped heads, window shorter than a tile, ragged T
+    (1, 4, 1, 333, 64),      # one shared key/value head, window = one key tile
+    (1, 2, 2, 640, 200),     # plain heads, window spanning several tiles
+    (2, 2, 1, 150, -1),      # grouped heads, full causal
+    (1, 1, 1, 70, 0),        # window 0: every query sees only its own key
+])
+def test_attention_gqa_window(B, Bn, H, Hkv, T, window):
+    """Query head h reads key/value head h / (H / Hkv); with window w >= 0,
+    query i sees keys i - w .. i.  The oracle repeats each key/value head over
+    its group and applies the window mask; dK and dV of a shared head are the
+    sums over the query heads of its group."""
+    say(f"attention GQA/window B={Bn} H={H} Hkv={Hkv} T={T} window={window}")
+    d, dkv = H * 128, Hkv * 128
+    ld = d + 2 * dkv
+    g = np.random.default_rng(Bn * 1000 + H * 100 + Hkv * 10 + T + window)
+    qkv = g.standard_normal((Bn * T, ld)).astype(np.float32)
+    dq = to_dev_bf16(qkv)
+    qv = dq.view(torch.int16)
+    out = torch.empty((Bn * T, d), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((Bn, H, T), dtype=torch.float32, device="cuda")
+    B.attention_fwd(qv, qv[:, d:], qv[:, d + dkv:], out, lse, Bn, H, T, ld, d, n_kv_head=Hkv, window=window)
+    torch.cuda.synchronize()
+    grp = H // Hkv
+    w = None if window < 0 else window
+    x64 = bf16_values(qkv).astype(np.float64)
+    q = _heads(x64, Bn, T, H, 0, ld)
+    k = np.repeat(_heads(x64, Bn, T, Hkv, d, ld), grp, axis=1)
+    v = np.repeat(_heads(x64, Bn, T, Hkv, d + dkv, ld), grp, axis=1)
+    y, lse_ref = om.causal_attention(q, k, v, window=w)
+    y_got = out.float().cpu().numpy().reshape(Bn, T, H, 128).transpose(0, 2, 1, 3)
+    e = rel_l2(y_got, y)
+    say(f"  out rel_l2 {e:.3e}  lse max err {np.abs(lse.cpu().numpy() - lse_ref).max():.3e}")
+    assert e <= 1e-2
+    assert np.abs(lse.cpu().numpy() - lse_ref).max() < 1e-3
+    if window == 0:
+        # softmax over a single key: the output is v_i itself (bf16)
+        assert np.array_equal(y_got, v)
+
+    dout_np = g.standard_normal((Bn * T, d)).astype(np.float32)
+    dout = to_dev_bf16(dout_np)
+    delta = torch.empty((Bn, H, T), dtype=torch.float32, device="cuda")
+    dq_acc = torch.empty((Bn * T, d), dtype=torch.float32, device="cuda")
+    dkv_t = torch.zeros((Bn * T, ld), dtype=torch.bfloat16, device="cuda")
+    dkvv = dkv_t.view(torch.int16)
+    B.attention_bwd(qv, qv[:, d:], qv[:, d + dkv:], out, dout, lse, delta, dq_acc, dkvv[:, d:],
+                    dkvv[:, d + dkv:], Bn, H, T, ld, d, ld, n_kv_head=Hkv, window=window)
+    torch.cuda.synchronize()
+    y_dev = out.float().cpu().numpy().astype(np.float64).reshape(Bn, T, H, 128).transpose(0, 2, 1, 3)
+    dy = bf16_values(dout_np).astype(np.float64).reshape(Bn, T, H, 128).transpose(0, 2, 1, 3)
+    dq_r, dk_r, dv_r = om.causal_attention_bwd(q, k, v, y_dev, dy, lse_ref, window=w)
+    dk_r = dk_r.reshape(Bn, Hkv, grp, T, 128).sum(axis=2)
+    dv_r = dv_r.reshape(Bn, Hkv, grp, T, 128).sum(axis=2)
+    dq_g = dq_acc.cpu().numpy().reshape(Bn, T, H, 128).transpose(0, 2, 1, 3)
+    dkv_np = dkv_t.float().cpu().numpy()
+    dk_g = _heads(dkv_np, Bn, T, Hkv, d, ld)
+    dv_g = _heads(dkv_np, Bn, T, Hkv, d + dkv, ld)
+    checks = (("dq", dq_g, dq_r), ("dk", dk_g, dk_r), ("dv", dv_g, dv_r))
+    if window == 0:
+        # P = 1 on the diagonal: dS = dP - rowsum(dY * Y) = 0 exactly, so dQ and
+        # dK are rounding noise on both sides; only dV = dY has a definite value
+        for name, got in (("dq", dq_g), ("dk", dk_g)):
+            say(f"  {name} max |.| {np.abs(got).max():.3e}")
+            assert np.abs(got).max() <= 1e-3
+        checks = checks[2:]
+    for name, got, ref in checks:
+        e, c = rel_l2(got, ref), cosine(got, ref)
+        say(f"  {name} rel_l2 {e:.3e} cos {c:.6f}")
+        assert e <= 1e-2 and c >= 0.999

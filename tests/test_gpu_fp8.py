@@ -130,10 +130,11 @@ def test_gemm_fp8(fa, fb, M, N, K):
 
 
 CONFIGS = [
-    # depth, vocab, seq_len, batch
-    (2, 32768, 128, 2),
-    (2, 1000, 100, 4),    # ragged T and V; B*T = 400 is a multiple of 16
-    (4, 4096, 256, 2),
+    # depth, vocab, seq_len, batch, (n_kv_head, window, pattern)
+    (2, 32768, 128, 2, (0, 0, "")),
+    (2, 1000, 100, 4, (0, 0, "")),    # ragged T and V; B*T = 400 is a multiple of 16
+    (4, 4096, 256, 2, (0, 0, "")),
+    (4, 4096, 256, 2, (1, 64, "SSSL")),   # grouped key/value heads, window layers
 ]
 
 
@@ -141,11 +142,12 @@ def _bar(e, floor, base):
     return e <= max(base, 1.5 * floor)
 
 
-@pytest.mark.parametrize("depth,vocab,T,Bn", CONFIGS)
-def test_step_fp8_parity(depth, vocab, T, Bn):
+@pytest.mark.parametrize("depth,vocab,T,Bn,attn", CONFIGS)
+def test_step_fp8_parity(depth, vocab, T, Bn, attn):
     B = _B()
-    say(f"fp8 step parity depth={depth} V={vocab} T={T} B={Bn}")
-    run = StepRun(depth, vocab, T, Bn, precision_flag=B.PREC_FP8)
+    kv, window, pattern = attn
+    say(f"fp8 step parity depth={depth} V={vocab} T={T} B={Bn} n_kv_head={kv} window={window} pattern={pattern}")
+    run = StepRun(depth, vocab, T, Bn, precision_flag=B.PREC_FP8, n_kv_head=kv, window=window, pattern=pattern)
     run.fwd()
     run.bwd()
     torch.cuda.synchronize()

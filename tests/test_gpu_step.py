@@ -81,6 +81,35 @@ def test_step_parity(depth, vocab, T, B):
     check_grads(run.grads(), ref["grads"], floor["grads"])
 
 
+GQA_WINDOW_CONFIGS = [
+    # depth, vocab, seq_len, batch, n_kv_head, window, pattern
+    (4, 4096, 256, 2, 1, 64, "SSSL"),    # two query heads share one key/value head
+    (6, 2048, 200, 2, 3, 50, "SL"),      # plain heads, alternating window layers, ragged T
+    (6, 1000, 130, 2, 1, 200, "S"),      # every layer windowed, window longer than T
+]
+
+
+@pytest.mark.parametrize("depth,vocab,T,B,n_kv_head,window,pattern", GQA_WINDOW_CONFIGS)
+def test_step_parity_gqa_window(depth, vocab, T, B, n_kv_head, window, pattern):
+    """Grouped key/value heads and sliding-window layers through the whole
+    step, against the oracle configured the same way."""
+    say(f"step parity depth={depth} V={vocab} T={T} B={B} n_kv_head={n_kv_head} window={window} "
+        f"pattern={pattern}")
+    run = StepRun(depth, vocab, T, B, n_kv_head=n_kv_head, window=window, pattern=pattern)
+    run.fwd()
+    run.bwd()
+    torch.cuda.synchronize()
+    ref = oracle_run(run)
+    loss = float(run.loss.item())
+    say(f"  loss gpu {loss:.6f} oracle {ref['loss']:.6f}")
+    assert abs(loss - ref["loss"]) <= 1e-2 * abs(ref["loss"])
+    e = rel_l2(from_dev(run.row_lse), ref["lse"].reshape(-1))
+    say(f"  row lse rel_l2 {e:.3e}")
+    assert e <= 1e-2
+    floor = oracle_run(run, bf16_operands=True)
+    check_grads(run.grads(), ref["grads"], floor["grads"])
+
+
 def test_bwd_accumulate_adds():
     run = StepRun(2, 1024, 64, 2)
     run.fwd()
