@@ -16,12 +16,38 @@ Readings taken:
   * the coefficient table is an input (the pages print only its first two
     triples); the update is W <- W (1 - lr wd) - lr X.
 
+NorMuon variance reduction (normuon_scale; dev.to section "2. Optimizador
+Muon", "Reducción de varianza NorMuon"; apidog.com/pt "Redução de Variância
+NorMuon"): after the orthogonalisation the update is rescaled per neuron so
+that no neuron's scale collapses, keeping the overall size of the update.
+The pages show only the first and last lines (per-neuron mean squares, their
+summed norm, the final scale = step size x norm before / norm after); the
+middle is completed with the published NorMuon algorithm (Li et al., 2025,
+"NorMuon: Making Muon more efficient and scalable"):
+  * a neuron is a row of the [out, in] matrix (statistic over the inputs);
+    axis=0 takes columns instead (the pages leave the reduced dimension a
+    variable);
+  * vm_i = mean of O_i^2 over the neuron's weights; V <- beta2 V + (1-beta2) vm
+    with V = 0 before the first step and no bias correction;
+  * step_i = 1 / (sqrt(V_i) + eps);
+  * norm_before = sqrt(sum_i vm_i), norm_after = sqrt(sum_i vm_i step_i^2)
+    (the same measure of O scaled by step);
+  * O'_i = O_i * step_i * norm_before / max(norm_after, 1e-10).
+A bias correction of V would multiply every step_i by one factor, which the
+norm ratio cancels (up to eps).
+
 Pinned by (tests/test_oracle_muon.py): for any table, the result equals
 U diag(p_k(...p_1(sigma / (||G|| + eps)))) V^T computed from a float64 LAPACK
 SVD (each iteration applies the odd polynomial p(s) = a s + b s^3 + c s^5 to
 the singular values); the textbook quintic iterated many times converges to
 the polar factor U V^T; at the first step the update does not depend on mu
-or on the scale of the gradient.
+or on the scale of the gradient.  NorMuon: the rescale keeps the Frobenius
+norm; from V = 0 (eps -> 0) it gives every neuron the same RMS, so an update
+whose neurons already share one RMS (rows of a semi-orthogonal matrix) comes
+back unchanged; V after several steps equals the closed-form weighted sum
+(1 - beta2) sum_s beta2^(t-s) vm_s; scaling O by c (and V by c^2) scales O'
+by c; permuting neurons permutes the result; axis=0 equals axis=1 on the
+transpose.
 """
 
 import numpy as np
@@ -47,6 +73,31 @@ def muon_update(W, G, M, coeffs, lr, momentum, weight_decay, eps=1e-7):
     orthogonalised update."""
     M_new = momentum * np.asarray(M, dtype=np.float64) + np.asarray(G, dtype=np.float64)
     O = newton_schulz(M_new, coeffs, eps)
+    W_new = np.asarray(W, dtype=np.float64) * (1.0 - lr * weight_decay) - lr * O
+    return W_new, M_new, O
+
+
+def normuon_scale(O, V, beta2=0.95, eps=1e-8, axis=1):
+    """NorMuon rescale of an orthogonalised update O [rows, cols].  V holds one
+    second moment per neuron (rows when axis=1, columns when axis=0) and is
+    updated in place.  Returns the rescaled update."""
+    O = np.asarray(O, dtype=np.float64)
+    vm = np.mean(O * O, axis=axis)                 # per-neuron mean square
+    norm_before = np.sqrt(np.sum(vm))
+    V *= beta2
+    V += (1.0 - beta2) * vm
+    step = 1.0 / (np.sqrt(V) + eps)
+    norm_after = np.sqrt(np.sum(vm * step * step))
+    scale = step * (norm_before / max(norm_after, 1e-10))
+    return O * (scale[:, None] if axis == 1 else scale[None, :])
+
+
+def normuon_update(W, G, M, V, coeffs, lr, momentum, weight_decay, beta2=0.95, eps_v=1e-8, axis=1, eps=1e-7):
+    """One Muon step with the NorMuon rescale between the orthogonalisation and
+    the update.  V is updated in place.  Returns (W_new, M_new, O') with O' the
+    rescaled update."""
+    M_new = momentum * np.asarray(M, dtype=np.float64) + np.asarray(G, dtype=np.float64)
+    O = normuon_scale(newton_schulz(M_new, coeffs, eps), V, beta2, eps_v, axis)
     W_new = np.asarray(W, dtype=np.float64) * (1.0 - lr * weight_decay) - lr * O
     return W_new, M_new, O
 
