@@ -1,7 +1,7 @@
 """Training-step throughput of libgptstep on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload d20]
-                    [--precision bf16|fp8] [--no-cpu-baseline]
+                    [--precision bf16|fp8] [--normuon] [--no-cpu-baseline]
 
 One step = gpt_step_fwd + gpt_step_bwd + muon_update on the three groups of
 block matrices (the q/k/v/o matrices, the MLP input matrices, the MLP output
@@ -149,6 +149,8 @@ def main():
     ap.add_argument("--workload", default="d20", choices=["d2", "d12", "d20", "d26"])
     ap.add_argument("--precision", default="bf16", choices=["bf16", "fp8"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--normuon", action="store_true",
+                    help="NorMuon per-neuron rescale after Newton-Schulz (normuon_update)")
     ap.add_argument("--breakdown", action="store_true", help="print per-kernel times to stderr")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device-to-device copy of BYTES three times and exit (the reference "
@@ -200,6 +202,7 @@ def main():
         size = count * rows * cols
         groups.append(dict(count=count, rows=rows, cols=cols, start=st,
                            M=torch.zeros(size, dtype=torch.float32, device=dev),
+                           V=torch.zeros(count * rows, dtype=torch.float32, device=dev) if args.normuon else None,
                            ws=torch.empty(Bd.muon_workspace_size(count, rows, cols), dtype=torch.uint8,
                                           device=dev)))
 
@@ -222,9 +225,14 @@ def main():
         for gr in groups:
             st, size = gr["start"], gr["count"] * gr["rows"] * gr["cols"]
             view = (gr["count"], gr["rows"], gr["cols"])
-            Bd.muon_update(grad[st:st + size].view(view), NS5, gr["ws"], W=master[st:st + size].view(view),
-                           W_bf16=bf16[st:st + size].view(view), M=gr["M"], lr=0.02, momentum=0.95,
-                           weight_decay=0.0)
+            if args.normuon:
+                Bd.normuon_update(grad[st:st + size].view(view), NS5, gr["ws"], gr["V"],
+                                  W=master[st:st + size].view(view), W_bf16=bf16[st:st + size].view(view),
+                                  M=gr["M"], lr=0.02, momentum=0.95, weight_decay=0.0, beta2=0.95, eps=1e-8)
+            else:
+                Bd.muon_update(grad[st:st + size].view(view), NS5, gr["ws"], W=master[st:st + size].view(view),
+                               W_bf16=bf16[st:st + size].view(view), M=gr["M"], lr=0.02, momentum=0.95,
+                               weight_decay=0.0)
 
     print(f"bench: inputs resident ({args.workload}, {args.precision}); warm-up", file=sys.stderr, flush=True)
     for _ in range(args.warmup):
@@ -295,8 +303,8 @@ def main():
         "data": "synthetic: uniform token ids, N(0,1/fan_in) weights (seeded PCG64)",
         "config": {"workload": args.workload, "depth": depth, "d_model": d, "n_head": H, "seq_len": T,
                    "micro_batch": B, "vocab": V, "tokens_per_step": tok, "parallelism": "single GPU",
-                   "optimizer": "Muon (5 Newton-Schulz iterations) on all block matrices, AdamW on embedding "
-                                "and head"},
+                   "optimizer": ("NorMuon" if args.normuon else "Muon") +
+                                " (5 Newton-Schulz iterations) on all block matrices, AdamW on embedding and head"},
         "mfu": (f_model + f_ns) / step_s / PEAK_BF16,
         "mfu_vs_mixed_peak": t_ideal / step_s if fp8 else None,
         "mfu_model": f_model / (fwd_bwd_ms / 1e3) / PEAK_BF16 if fwd_bwd_ms else None,

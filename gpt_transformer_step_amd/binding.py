@@ -59,6 +59,8 @@ _SIGS = {
     "muon_workspace_size": [_i32, _i32, _i32, _P(_sz)],
     "muon_update": [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _P(_f32), _i32, _f32, _f32, _f32,
                     _vp, _sz, _vp],
+    "normuon_update": [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _P(_f32), _i32, _f32, _f32, _f32,
+                       _f32, _f32, _vp, _sz, _vp],
     "gpt_op_gemm": [_i32, _i32, _i32, _i32, _vp, _i32, _i64, _i64, _vp, _i32, _i64, _i64, _vp, _i32,
                     _i64, _i64, _f32, _f32, _vp],
     "gpt_op_attention_fwd": [_i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _i64, _vp, _i64, _vp, _vp],
@@ -212,6 +214,21 @@ def muon_update(G, coeffs, ws, W=None, W_bf16=None, M=None, O_out=None, lr=0.02,
     _call("muon_update", _ptr(W), _ptr(W_bf16), _ptr(G), _ptr(M), _ptr(O_out), count, rows, cols,
           carr, len(coeffs), lr, momentum, weight_decay, _ptr(ws), ws.numel() * ws.element_size(),
           _stream(stream))
+
+
+def normuon_update(G, coeffs, ws, V, W=None, W_bf16=None, M=None, O_out=None, lr=0.02, momentum=0.95,
+                   weight_decay=0.0, beta2=0.95, eps=1e-8, per_row=True, stream=None):
+    """Muon with the NorMuon per-neuron rescale; V: fp32 second moments, one
+    per row (per_row) or column of each matrix, updated in place."""
+    if G.dim() == 2:
+        count, rows, cols = 1, G.shape[0], G.shape[1]
+    else:
+        count, rows, cols = G.shape
+    flat = [float(x) for t in coeffs for x in t]
+    carr = (_f32 * len(flat))(*flat)
+    _call("normuon_update", _ptr(W), _ptr(W_bf16), _ptr(G), _ptr(M), _ptr(V), _ptr(O_out), count, rows, cols,
+          int(bool(per_row)), carr, len(coeffs), lr, momentum, weight_decay, beta2, eps, _ptr(ws),
+          ws.numel() * ws.element_size(), _stream(stream))
 
 
 def gemm(A, B, C, M, N, K, a_layout=LAYOUT_K, b_layout=LAYOUT_K, lda=None, ldb=None, ldc=None,

@@ -921,7 +921,7 @@ namespace {
 constexpr int kFrobBlocks = 64;
 
 struct MuonWS {
-  size_t partial, X, Xb0, Xb1, A, Ab, Bb, gpart, total;
+  size_t partial, X, Xb0, Xb1, A, Ab, Bb, gpart, nm_part, nm_scale, total;
 };
 
 // k-splits of the Gram products X^T X (a few output tiles, long K)
@@ -947,6 +947,8 @@ MuonWS muon_layout(int count, int rows, int cols) {
   m.Bb = take((size_t)count * sm * sm * 2);
   const int gs_ = gram_splits(count, rows, cols);
   m.gpart = take(gs_ > 1 ? (size_t)gs_ * count * sm * sm * 4 : 4);
+  m.nm_part = take((size_t)normuon_part_floats(count, rows, cols) * 4);
+  m.nm_scale = take((size_t)count * std::max(rows, cols) * 4);
   m.total = o;
   return m;
 }
@@ -968,10 +970,16 @@ extern "C" gpt_status muon_workspace_size(int32_t count, int32_t rows, int32_t c
   return GPT_OK;
 }
 
-extern "C" gpt_status muon_update(float* Wt, uint16_t* W_bf16, const float* Gm, float* M, float* O_out,
-                                  int32_t count, int32_t rows, int32_t cols, const float* coeffs,
-                                  int32_t ns_steps, float lr, float momentum, float weight_decay, void* ws,
-                                  size_t ws_bytes, gpt_stream_t stream) {
+namespace {
+struct NorMuonArgs {
+  float* V;
+  int per_row;
+  float beta2, eps;
+};
+
+int muon_impl(float* Wt, uint16_t* W_bf16, const float* Gm, float* M, float* O_out, int32_t count, int32_t rows,
+              int32_t cols, const float* coeffs, int32_t ns_steps, float lr, float momentum, float weight_decay,
+              const NorMuonArgs* nm, void* ws, size_t ws_bytes, gpt_stream_t stream) {
   TRY(check_muon_shape(count, rows, cols));
   if (!Gm) FAIL(GPT_ERR_INVALID_ARG, "G is NULL");
   if (!coeffs) FAIL(GPT_ERR_INVALID_ARG, "coeffs is NULL");
@@ -1046,8 +1054,42 @@ extern "C" gpt_status muon_update(float* Wt, uint16_t* W_bf16, const float* Gm, 
     }
     cur ^= 1;
   }
-  { ProfScope ps_(P_MUON_ELEMWISE, s); TRY(launch_muon_apply(X, Wt, W_bf16, O_out, count, rows, cols, lr, weight_decay, s)); }
+  const float* nsc = nullptr;
+  if (nm) {
+    ProfScope ps_(P_MUON_ELEMWISE, s);
+    float* scale = at<float>(ws, m.nm_scale);
+    TRY(launch_normuon_scale(X, at<float>(ws, m.nm_part), nm->V, scale, count, rows, cols, nm->per_row, nm->beta2,
+                             nm->eps, s));
+    nsc = scale;
+  }
+  {
+    ProfScope ps_(P_MUON_ELEMWISE, s);
+    TRY(launch_muon_apply(X, Wt, W_bf16, O_out, count, rows, cols, lr, weight_decay, nsc, nm ? nm->per_row : 0, s));
+  }
   return GPT_OK;
+}
+}  // namespace
+
+extern "C" gpt_status muon_update(float* Wt, uint16_t* W_bf16, const float* Gm, float* M, float* O_out,
+                                  int32_t count, int32_t rows, int32_t cols, const float* coeffs,
+                                  int32_t ns_steps, float lr, float momentum, float weight_decay, void* ws,
+                                  size_t ws_bytes, gpt_stream_t stream) {
+  return (gpt_status)muon_impl(Wt, W_bf16, Gm, M, O_out, count, rows, cols, coeffs, ns_steps, lr, momentum, weight_decay,
+                   nullptr, ws, ws_bytes, stream);
+}
+
+extern "C" gpt_status normuon_update(float* Wt, uint16_t* W_bf16, const float* Gm, float* M, float* V,
+                                     float* O_out, int32_t count, int32_t rows, int32_t cols, int32_t per_row,
+                                     const float* coeffs, int32_t ns_steps, float lr, float momentum,
+                                     float weight_decay, float beta2, float eps, void* ws, size_t ws_bytes,
+                                     gpt_stream_t stream) {
+  if (!V) FAIL(GPT_ERR_INVALID_ARG, "V (the per-neuron second moments) is NULL");
+  if (per_row != 0 && per_row != 1) FAIL(GPT_ERR_INVALID_ARG, "per_row must be 0 or 1");
+  if (!(beta2 >= 0.f && beta2 < 1.f)) FAIL(GPT_ERR_INVALID_ARG, "beta2 must be in [0, 1)");
+  if (!(eps >= 0.f) || !isfinite(eps)) FAIL(GPT_ERR_INVALID_ARG, "eps must be finite and >= 0");
+  const NorMuonArgs nm{V, per_row, beta2, eps};
+  return (gpt_status)muon_impl(Wt, W_bf16, Gm, M, O_out, count, rows, cols, coeffs, ns_steps, lr, momentum, weight_decay, &nm,
+                   ws, ws_bytes, stream);
 }
 
 // ---------------------------------------------------------------------------

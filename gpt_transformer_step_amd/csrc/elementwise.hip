@@ -368,10 +368,95 @@ __global__ void ns_init_kernel(const float* __restrict__ src, const float* __res
   }
 }
 
-// output tiles over W [rows, cols]; X oriented [l, s] (transposed when TR)
+// ---------------------------------------------------------------------------
+// NorMuon: per-neuron sums of squares of the orthogonalised update X (stored
+// [l, s] per matrix), then per matrix the second-moment EMA, the step sizes
+// and the norm ratio folded into one scale per neuron
+// ---------------------------------------------------------------------------
+constexpr int kNmRows = 256;  // stored rows per workgroup of the column statistic
+
+// part[w] = sum of squares of stored row w (all matrices' rows in sequence);
+// one wave per row, 16-byte loads (s % 4 == 0)
+__global__ void __launch_bounds__(256) nm_rowsq_kernel(const float* __restrict__ X, float* __restrict__ part, int sm,
+                                                       long long nrows) {
+  const int lane = threadIdx.x & 63;
+  const long long w = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (w >= nrows) return;
+  const float* x = X + w * sm;
+  float acc = 0.f;
+  for (int c = lane * 4; c < sm; c += 256) {
+    const float4 v = *reinterpret_cast<const float4*>(x + c);
+    acc += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+  }
+  acc = wave_sum(acc);
+  if (lane == 0) part[w] = acc;
+}
+
+// part[(b nch + ch) s + c] = sum over stored rows ch*kNmRows .. of X[b][r][c]^2;
+// a workgroup covers 64 columns (one per lane) and 4 interleaved row groups
+__global__ void __launch_bounds__(256) nm_colsq_kernel(const float* __restrict__ X, float* __restrict__ part, int l,
+                                                       int sm, int nch) {
+  const int b = blockIdx.z, ch = blockIdx.y;
+  const int lane = threadIdx.x & 63, g = threadIdx.x >> 6;
+  const int c = blockIdx.x * 64 + lane;
+  const int r0 = ch * kNmRows, r1 = min(l, r0 + kNmRows);
+  float acc = 0.f;
+  if (c < sm) {
+    const float* x = X + (long long)b * l * sm + c;
+    for (int r = r0 + g; r < r1; r += 4) {
+      const float v = x[(long long)r * sm];
+      acc += v * v;
+    }
+  }
+  __shared__ float red[4][64];
+  red[g][lane] = acc;
+  __syncthreads();
+  if (g == 0 && c < sm) part[((long long)b * nch + ch) * sm + c] = red[0][lane] + red[1][lane] + red[2][lane] + red[3][lane];
+}
+
+// one workgroup per matrix: vm_i = (sum over chunks) / n; V_i <- beta2 V_i +
+// (1 - beta2) vm_i; step_i = 1 / (sqrt(V_i) + eps);
+// scale_i = step_i sqrt(sum vm) / max(sqrt(sum vm step^2), 1e-10)
+__global__ void __launch_bounds__(256) nm_finalize_kernel(const float* __restrict__ part, int nch, int nneur,
+                                                          float inv_n, float* __restrict__ V,
+                                                          float* __restrict__ scale, float beta2, float eps) {
+  const int b = blockIdx.x;
+  const float* p = part + (long long)b * nch * nneur;
+  float* v = V + (long long)b * nneur;
+  float* sc = scale + (long long)b * nneur;
+  double s0 = 0.0, s1 = 0.0;
+  for (int i = threadIdx.x; i < nneur; i += 256) {
+    float ss = 0.f;
+    for (int ch = 0; ch < nch; ++ch) ss += p[(long long)ch * nneur + i];
+    const float vm = ss * inv_n;
+    const float vn = beta2 * v[i] + (1.f - beta2) * vm;
+    v[i] = vn;
+    const float st = 1.f / (sqrtf(vn) + eps);
+    sc[i] = st;
+    s0 += vm;
+    s1 += (double)vm * st * st;
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    s0 += __shfl_xor(s0, o, 64);
+    s1 += __shfl_xor(s1, o, 64);
+  }
+  __shared__ double red[2][4];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (lane == 0) { red[0][wave] = s0; red[1][wave] = s1; }
+  __syncthreads();
+  const double t0 = red[0][0] + red[0][1] + red[0][2] + red[0][3];
+  const double t1 = red[1][0] + red[1][1] + red[1][2] + red[1][3];
+  const float ratio = (float)(sqrt(t0) / fmax(sqrt(t1), 1e-10));
+  for (int i = threadIdx.x; i < nneur; i += 256) sc[i] *= ratio;  // entries this thread wrote
+}
+
+// output tiles over W [rows, cols]; X oriented [l, s] (transposed when TR);
+// nsc (nullable): NorMuon scale per row (nm_rows) or per column of W
 template <bool TR>
 __global__ void muon_apply_kernel(const float* __restrict__ X, float* __restrict__ W, uint16_t* __restrict__ Wb,
-                                  float* __restrict__ O_out, int rows, int cols, float lr, float wd) {
+                                  float* __restrict__ O_out, int rows, int cols, float lr, float wd,
+                                  const float* __restrict__ nsc, int nm_rows) {
   const int b = blockIdx.z;
   const float* x = X + (long long)b * rows * cols;
   const long long base = (long long)b * rows * cols;
@@ -392,7 +477,8 @@ __global__ void muon_apply_kernel(const float* __restrict__ X, float* __restrict
     const int gr = r0 + rr, gc = c0 + cc;
     if (gr < rows && gc < cols) {
       const long long idx = (long long)gr * cols + gc;
-      const float o = TR ? tile[cc][rr] : x[idx];
+      float o = TR ? tile[cc][rr] : x[idx];
+      if (nsc) o *= nm_rows ? nsc[(long long)b * rows + gr] : nsc[(long long)b * cols + gc];
       if (O_out) O_out[base + idx] = o;
       if (W) {
         const float w = W[base + idx] * decay - lr * o;
@@ -553,14 +639,42 @@ int launch_adamw(float* W, uint16_t* Wb, const float* G, float* M, float* V, lon
   return 0;
 }
 
+int launch_normuon_scale(const float* X, float* part, float* V, float* scale, int count, int rows, int cols,
+                         int per_row, float beta2, float eps, hipStream_t s) {
+  const bool tr = rows < cols;
+  const int l = tr ? cols : rows, sm = tr ? rows : cols;
+  const int nneur = per_row ? rows : cols;
+  const float inv_n = 1.f / (float)(per_row ? cols : rows);
+  int nch = 1;
+  if ((per_row != 0) != tr) {  // neurons are the stored rows
+    const long long nr = (long long)count * l;
+    hipLaunchKernelGGL(nm_rowsq_kernel, dim3((unsigned)((nr + 3) / 4)), dim3(256), 0, s, X, part, sm, nr);
+    GS_LAUNCH_CHECK("nm_rowsq");
+  } else {                     // neurons are the stored columns
+    nch = (l + kNmRows - 1) / kNmRows;
+    hipLaunchKernelGGL(nm_colsq_kernel, dim3((sm + 63) / 64, nch, count), dim3(256), 0, s, X, part, l, sm, nch);
+    GS_LAUNCH_CHECK("nm_colsq");
+  }
+  hipLaunchKernelGGL(nm_finalize_kernel, dim3(count), dim3(256), 0, s, part, nch, nneur, inv_n, V, scale, beta2, eps);
+  GS_LAUNCH_CHECK("nm_finalize");
+  return 0;
+}
+
+long long normuon_part_floats(int count, int rows, int cols) {
+  const int l = std::max(rows, cols), sm = std::min(rows, cols);
+  return (long long)count * std::max<long long>(l, (long long)sm * ((l + kNmRows - 1) / kNmRows));
+}
+
 int launch_muon_apply(const float* X, float* W, uint16_t* Wb, float* O_out, int count, int rows, int cols,
-                      float lr, float wd, hipStream_t s) {
+                      float lr, float wd, const float* nsc, int nm_rows, hipStream_t s) {
   const bool tr = rows < cols;
   dim3 grid((cols + 63) / 64, (rows + 63) / 64, count);
   if (tr)
-    hipLaunchKernelGGL(muon_apply_kernel<true>, grid, dim3(256), 0, s, X, W, Wb, O_out, rows, cols, lr, wd);
+    hipLaunchKernelGGL(muon_apply_kernel<true>, grid, dim3(256), 0, s, X, W, Wb, O_out, rows, cols, lr, wd, nsc,
+                       nm_rows);
   else
-    hipLaunchKernelGGL(muon_apply_kernel<false>, grid, dim3(256), 0, s, X, W, Wb, O_out, rows, cols, lr, wd);
+    hipLaunchKernelGGL(muon_apply_kernel<false>, grid, dim3(256), 0, s, X, W, Wb, O_out, rows, cols, lr, wd, nsc,
+                       nm_rows);
   GS_LAUNCH_CHECK("muon_apply");
   return 0;
 }

@@ -36,9 +36,17 @@ int launch_frob_partial(const float* X, float* partial, int count, long long per
 // X[b] (oriented [l, s]) = src[b] / (||src[b]|| + eps); transposed when rows < cols
 int launch_ns_init(const float* src, const float* partial, int nblk, float* X, uint16_t* Xb,
                    int count, int rows, int cols, float eps, hipStream_t s);
-// O = X oriented back; W = W (1 - lr wd) - lr O; W_bf16 = bf16(W); O_out = O
+// O = X oriented back (times the NorMuon scale nsc of its row (nm_rows) or
+// column when nsc is given); W = W (1 - lr wd) - lr O; W_bf16 = bf16(W); O_out = O
 int launch_muon_apply(const float* X, float* W, uint16_t* Wb, float* O_out, int count, int rows,
-                      int cols, float lr, float wd, hipStream_t s);
+                      int cols, float lr, float wd, const float* nsc, int nm_rows, hipStream_t s);
+// NorMuon: from the orthogonalised X (oriented as for launch_muon_apply),
+// update the per-neuron second moments V and write the per-neuron scale
+// (neurons = rows of W when per_row, else columns); part: scratch of
+// normuon_part_floats floats
+int launch_normuon_scale(const float* X, float* part, float* V, float* scale, int count, int rows, int cols,
+                         int per_row, float beta2, float eps, hipStream_t s);
+long long normuon_part_floats(int count, int rows, int cols);
 
 // AdamW on n fp32 parameters (n % 4 == 0, 16-byte aligned; Wb nullable)
 int launch_adamw(float* W, uint16_t* Wb, const float* G, float* M, float* V, long long n, float lr, float b1,

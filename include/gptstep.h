@@ -164,7 +164,8 @@ gpt_status adamw_update(float* W, uint16_t* W_bf16, const float* G, float* M, fl
                         float lr, float beta1, float beta2, float eps, float weight_decay, float grad_scale,
                         gpt_stream_t stream);
 
-/* Workspace bytes for muon_update on `count` matrices of [rows, cols]. */
+/* Workspace bytes for muon_update / normuon_update on `count` matrices of
+ * [rows, cols]. */
 gpt_status muon_workspace_size(int32_t count, int32_t rows, int32_t cols, size_t* bytes /* host */);
 
 /* Muon update of `count` same-shape fp32 matrices [rows, cols], contiguous
@@ -183,6 +184,24 @@ gpt_status muon_update(float* W, uint16_t* W_bf16, const float* G, float* M, flo
                        int32_t count, int32_t rows, int32_t cols, const float* coeffs,
                        int32_t ns_steps, float lr, float momentum, float weight_decay, void* ws,
                        size_t ws_bytes, gpt_stream_t stream);
+
+/* Muon with the NorMuon per-neuron rescale (dev.to page, "2. Optimizador
+ * Muon", NorMuon variance reduction; apidog.com/pt "Redução de Variância
+ * NorMuon"): as muon_update, with O replaced before the apply by
+ *   vm_i   = mean of O_i^2 over neuron i's weights
+ *   V_i   <- beta2 * V_i + (1 - beta2) * vm_i        (V = 0 before step 1)
+ *   step_i = 1 / (sqrt(V_i) + eps)
+ *   O_i   <- O_i * step_i * sqrt(sum vm) / max(sqrt(sum vm step^2), 1e-10)
+ * (sums over the neurons of one matrix).  A neuron is a row of W when
+ * per_row = 1 (the statistic runs over the inputs), a column when 0.
+ * V: device fp32 [count, rows] (per_row) or [count, cols], updated in place.
+ * O_out receives the rescaled O.  Workspace: muon_workspace_size.
+ * GPT_ERR_INVALID_ARG for V NULL, per_row not 0/1, beta2 outside [0, 1),
+ * eps negative or not finite, and everything muon_update rejects. */
+gpt_status normuon_update(float* W, uint16_t* W_bf16, const float* G, float* M, float* V, float* O_out,
+                          int32_t count, int32_t rows, int32_t cols, int32_t per_row, const float* coeffs,
+                          int32_t ns_steps, float lr, float momentum, float weight_decay, float beta2, float eps,
+                          void* ws, size_t ws_bytes, gpt_stream_t stream);
 
 /* Text of a status, and the message of the last failing call on this thread
  * (empty when none).  Both return static or thread-local storage. */

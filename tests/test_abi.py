@@ -26,14 +26,15 @@ def _declared():
     for h in ("gptstep.h", "gptstep_ops.h"):
         src = open(os.path.join(ROOT, "include", h)).read()
         src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-        for m in re.finditer(r"^\s*(?:const\s+)?[\w]+\*?\s+\*?((?:gpt|muon)_\w+)\s*\(", src, flags=re.M):
+        for m in re.finditer(r"^\s*(?:const\s+)?[\w]+\*?\s+\*?((?:gpt|muon|normuon|adamw)_\w+)\s*\(", src, flags=re.M):
             names.add(m.group(1))
     return names
 
 
 def test_every_declared_symbol_is_exported(B):
     names = _declared()
-    assert {"gpt_step_fwd", "gpt_step_bwd", "muon_update", "gpt_workspace_size", "gpt_op_gemm"} <= names
+    assert {"gpt_step_fwd", "gpt_step_bwd", "muon_update", "normuon_update", "adamw_update", "gpt_workspace_size",
+            "gpt_op_gemm", "gpt_step_bwd_scaled"} <= names
     lib = B.lib()
     missing = [n for n in sorted(names) if not hasattr(lib, n)]
     assert not missing, missing
@@ -117,6 +118,24 @@ def test_muon_rejects_on_host(B):
     assert rc == -3   # workspace too small
     rc = lib.muon_update(None, None, None, None, None, 1, 64, 64, c, 1, 0.1, 0.9, 0.0, fake, 1 << 30, None)
     assert rc == -1   # G is NULL
+
+
+def test_normuon_rejects_on_host(B):
+    lib = B.lib()
+    c = (ctypes.c_float * 3)(1.0, 0.0, 0.0)
+    fake = ctypes.c_void_p(4096)
+
+    def call(V=fake, per_row=1, beta2=0.95, eps=1e-8, ws_bytes=1 << 30, steps=1):
+        return lib.normuon_update(None, None, fake, None, V, None, 1, 64, 64, per_row, c, steps, 0.1, 0.9, 0.0,
+                                  beta2, eps, fake, ws_bytes, None)
+
+    assert call(V=None) == -1
+    assert b"V" in lib.gpt_last_error()
+    assert call(per_row=2) == -1
+    assert call(beta2=1.0) == -1
+    assert call(eps=-1.0) == -1
+    assert call(steps=0) == -1
+    assert call(ws_bytes=10) == -3
 
 
 def test_gemm_rejects_on_host(B):
