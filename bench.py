@@ -35,46 +35,97 @@ NS5 = [(15.0 / 8.0, -10.0 / 8.0, 3.0 / 8.0)] * 5
 METRIC = "training tokens/sec + MFU (% of MFMA peak), depth-20 GPT, 1 MI355X"
 
 
-def shapes(depth):
-    d = 64 * depth
-    return d, d // 128, 4 * d
+class Model:
+    """Shapes of one configuration: depth-derived widths, the key/value head
+    count and the per-layer attention windows."""
+
+    def __init__(self, depth, V, T, B, n_kv_head=0, window=0, pattern=""):
+        self.L, self.V, self.T, self.B = depth, V, T, B
+        self.d = 64 * depth
+        self.H = self.d // 128
+        self.Hkv = n_kv_head or self.H
+        self.dkv = 128 * self.Hkv
+        self.hid = 4 * self.d
+        self.N = B * T
+        self.n_kv_head, self.window, self.pattern = n_kv_head, window, pattern
+        # left window of each layer (None: full causal); pattern letters repeat over the depth
+        self.windows = [window if (window > 0 and pattern and pattern[l % len(pattern)] == "S") else None
+                        for l in range(depth)]
+
+    def pairs(self, w):
+        """Query-key pairs of one sequence and head, the diagonal counted half
+        (T^2/2 for a full causal layer)."""
+        T = self.T
+        if w is None or w >= T - 1:
+            return T * T / 2.0
+        i = np.arange(T)
+        return float(np.minimum(i + 1, w + 1).sum()) - T / 2.0
+
+    def block_mats(self, offs):
+        """(offset, rows, cols) of every block matrix in packed order."""
+        L, d, dkv, hid = self.L, self.d, self.dkv, self.hid
+        mats = []
+        for l in range(L):
+            q, k, v, o = offs[1 + 4 * l: 5 + 4 * l]
+            mats += [(q, d, d), (k, dkv, d), (v, dkv, d), (o, d, d)]
+        mats += [(offs[1 + 4 * L + l], hid, d) for l in range(L)]
+        mats += [(offs[1 + 5 * L + l], d, hid) for l in range(L)]
+        return mats
+
+    def block_shapes(self):
+        """(rows, cols) of every block matrix (offsets not needed)."""
+        d, dkv, hid = self.d, self.dkv, self.hid
+        return [(d, d), (dkv, d), (dkv, d), (d, d)] * self.L + [(hid, d)] * self.L + [(d, hid)] * self.L
+
+    def attn_flops(self):
+        """Algorithmic attention FLOPs of one forward over all layers (QK^T and
+        PV over the visible pairs)."""
+        return sum(2.0 * self.B * self.H * self.pairs(w) * 128 * 2 for w in self.windows)
 
 
-def alg_flops(depth, V, T, B):
-    L = depth
-    d, _, _ = shapes(depth)
-    N = B * T
-    f_model = 6 * (12 * L * d * d + V * d) * N + 6 * L * d * T * N
-    groups = muon_groups(depth)
+def alg_flops(m):
+    """(model FLOPs of one forward+backward, Newton-Schulz FLOPs of one
+    optimizer step)."""
+    d, dkv, N = m.d, m.dkv, m.N
+    per_layer = d * (d + 2 * dkv) + d * d + 8 * d * d
+    f_model = 6 * (m.L * per_layer + m.V * d) * N + 3 * m.attn_flops()
     f_ns = 0
-    for count, rows, cols in groups:
-        l, s = max(rows, cols), min(rows, cols)
-        f_ns += count * 5 * (4 * l * s * s + 2 * s ** 3)
+    for rows, cols in m.block_shapes():
+        l, s_ = max(rows, cols), min(rows, cols)
+        f_ns += 5 * (4 * l * s_ * s_ + 2 * s_ ** 3)
     return f_model, f_ns
 
 
-def muon_groups(depth):
-    d, _, hid = shapes(depth)
-    return [(4 * depth, d, d), (depth, hid, d), (depth, d, hid)]
+def muon_runs(mats):
+    """Runs of adjacent same-shape matrices, each one muon_update call:
+    (start, count, rows, cols)."""
+    runs = []
+    for off, rows, cols in mats:
+        if runs:
+            st, cnt, r, c = runs[-1]
+            if (r, c) == (rows, cols) and st + cnt * r * c == off:
+                runs[-1] = (st, cnt + 1, r, c)
+                continue
+        runs.append((off, 1, rows, cols))
+    return runs
 
 
-def kernel_flops(name, depth, V, T, B):
-    """Algorithmic FLOPs of one launch of a kernel category (None: not a
-    contraction)."""
-    d, H, hid = shapes(depth)
-    N = B * T
-    attn = 2.0 * B * H * T * (T + 1) / 2 * 128 * 2  # QK^T and PV over the causal half
+def kernel_flops(name, m):
+    """Algorithmic FLOPs of one launch of a kernel category, averaged over the
+    layers (None: not a contraction)."""
+    d, dkv, hid, N = m.d, m.dkv, m.hid, m.N
+    attn = m.attn_flops() / m.L
     table = {
-        "gemm_qkv_rope_fwd": 2.0 * N * 3 * d * d, "gemm_o_fwd": 2.0 * N * d * d,
+        "gemm_qkv_rope_fwd": 2.0 * N * (d + 2 * dkv) * d, "gemm_o_fwd": 2.0 * N * d * d,
         "gemm_fc_relu2_fwd": 2.0 * N * hid * d, "gemm_proj_fwd": 2.0 * N * d * hid,
-        "gemm_ce_fwd": 2.0 * N * V * d, "attn_fwd": attn,
+        "gemm_ce_fwd": 2.0 * N * m.V * d, "attn_fwd": attn,
         # backward: dV, dP, dK in the dK/dV kernel, dQ in the dQ kernel (recomputed
         # scores and the dQ kernel's second dP are not counted)
         "attn_bwd_dkdv": 1.5 * attn, "attn_bwd_dq": 0.5 * attn,
         "gemm_proj_dgrad": 2.0 * N * d * hid, "gemm_proj_wgrad": 2.0 * N * d * hid,
         "gemm_fc_dgrad": 2.0 * N * d * hid, "gemm_fc_wgrad": 2.0 * N * d * hid,
         "gemm_o_dgrad": 2.0 * N * d * d, "gemm_o_wgrad": 2.0 * N * d * d,
-        "gemm_qkv_dgrad": 2.0 * N * 3 * d * d, "gemm_qkv_wgrad": 2.0 * N * 3 * d * d,
+        "gemm_qkv_dgrad": 2.0 * N * (d + 2 * dkv) * d, "gemm_qkv_wgrad": 2.0 * N * (d + 2 * dkv) * d,
     }
     return table.get(name)
 
@@ -84,10 +135,10 @@ BLOCK_GEMMS = {"gemm_qkv_rope_fwd", "gemm_o_fwd", "gemm_fc_relu2_fwd", "gemm_pro
                "gemm_qkv_dgrad", "gemm_qkv_wgrad"}
 
 
-def block_gemm_flops(depth, T, B):
+def block_gemm_flops(m):
     """FLOPs of the four block products per layer, forward and backward."""
-    d, _, _ = shapes(depth)
-    return 6 * 12 * depth * d * d * B * T
+    d, dkv = m.d, m.dkv
+    return 6.0 * m.L * (d * (d + 2 * dkv) + 9 * d * d) * m.N
 
 
 def measured_traffic(category):
@@ -106,7 +157,7 @@ def measured_traffic(category):
         return None
 
 
-def cpu_baseline(wl, depth, V, T, B, seed_ids, seed_w):
+def cpu_baseline(wl, m, seed_ids, seed_w):
     """The oracle (numpy, as it stands) on a bounded sample of the workload:
     one sequence's forward+backward in float32 and one Newton-Schulz per block
     matrix shape (float64), scaled to a full step."""
@@ -119,24 +170,27 @@ def cpu_baseline(wl, depth, V, T, B, seed_ids, seed_w):
         cores = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
     except Exception:  # pragma: no cover
         cores = len(os.sched_getaffinity(0))
-    dims = inputs.Dims.from_depth(depth, V)
-    cfg = om.Config.from_depth(depth, V)
+    dims = inputs.Dims.from_depth(m.L, m.V, m.n_kv_head)
+    cfg = om.Config.from_depth(m.L, m.V, m.n_kv_head, m.window, m.pattern or "L")
     master = inputs.master_weights(dims, seed_w)
     P = {k: v for k, v in inputs.unpack(dims, precision.round_bf16(master)).items()}
-    ids = inputs.token_ids(B, T, V, seed_ids)[:1]
+    ids = inputs.token_ids(m.B, m.T, m.V, seed_ids)[:1]
     t0 = time.perf_counter()
     om.forward_backward(P, ids, cfg, dtype=np.float32)
     t_seq = time.perf_counter() - t0
     t_ns = 0.0
     g = np.random.default_rng(0)
-    for count, rows, cols in muon_groups(depth):
+    counts = {}
+    for shp in m.block_shapes():
+        counts[shp] = counts.get(shp, 0) + 1
+    for (rows, cols), count in counts.items():
         G = g.standard_normal((rows, cols)).astype(np.float32)
         t0 = time.perf_counter()
         omu.newton_schulz(G, NS5)
         t_ns += count * (time.perf_counter() - t0)
-    step_s = B * t_seq + t_ns
-    return {"value": B * T / step_s, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
-            "sample": (f"{wl}: forward+backward of 1 of {B} sequences (float32, {t_seq:.1f} s) and one "
+    step_s = m.B * t_seq + t_ns
+    return {"value": m.B * m.T / step_s, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+            "sample": (f"{wl}: forward+backward of 1 of {m.B} sequences (float32, {t_seq:.1f} s) and one "
                        f"Newton-Schulz per block-matrix shape (float64); scaled to a full step "
                        f"({step_s:.0f} s)")}
 
@@ -151,6 +205,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--normuon", action="store_true",
                     help="NorMuon per-neuron rescale after Newton-Schulz (normuon_update)")
+    ap.add_argument("--n-kv-head", type=int, default=0, help="key/value heads (0: one per query head)")
+    ap.add_argument("--window", type=int, default=0, help="left window of the short ('S') layers")
+    ap.add_argument("--pattern", default="", help="layer pattern of S (windowed) / L (full) letters, e.g. SSSL")
     ap.add_argument("--breakdown", action="store_true", help="print per-kernel times to stderr")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device-to-device copy of BYTES three times and exit (the reference "
@@ -178,12 +235,14 @@ def main():
     wl = inputs.WORKLOADS[args.workload]
     depth, T, B = wl["depth"], wl["seq_len"], wl["batch"]
     V = 32768
-    d, H, hid = shapes(depth)
+    m = Model(depth, V, T, B, args.n_kv_head, args.window, args.pattern)
+    d, H = m.d, m.H
     prec = Bd.PREC_FP8 if args.precision == "fp8" else Bd.PREC_BF16
     dev = torch.device("cuda:0")
-    sh = Bd.shape(depth, V, T, B, prec)
+    sh = Bd.shape(depth, V, T, B, prec, n_kv_head=args.n_kv_head, window=args.window, pattern=args.pattern)
     n = Bd.param_count(sh)
-    dims = inputs.Dims.from_depth(depth, V)
+    dims = inputs.Dims.from_depth(depth, V, args.n_kv_head)
+    assert n == inputs.n_params(dims)
     master_np = inputs.master_weights(dims, inputs.SEED_W)
     master = torch.from_numpy(master_np).to(dev)
     del master_np
@@ -195,10 +254,11 @@ def main():
     params = Bd.make_params(master, bf16, grad)
     loss = torch.zeros(1, dtype=torch.float32, device=dev)
     offs = Bd.param_layout(sh)
-    # the three Muon groups are contiguous ranges of the packed buffers
-    starts = [offs[1], offs[1 + 4 * depth], offs[1 + 5 * depth]]
+    # one muon_update per run of adjacent same-shape block matrices: the three
+    # groups (q/k/v/o, MLP in, MLP out) when every head has its own key/value
+    # head; with grouped heads wq/wo and wk/wv pairs differ in shape
     groups = []
-    for (count, rows, cols), st in zip(muon_groups(depth), starts):
+    for st, count, rows, cols in muon_runs(m.block_mats(offs)):
         size = count * rows * cols
         groups.append(dict(count=count, rows=rows, cols=cols, start=st,
                            M=torch.zeros(size, dtype=torch.float32, device=dev),
@@ -254,7 +314,7 @@ def main():
             breakdown[c] = (t, cnt)
     Bd.profile_enable(0)
     Bd.profile_reset()
-    contractions = {c: v for c, v in breakdown.items() if kernel_flops(c, depth, V, T, B)}
+    contractions = {c: v for c, v in breakdown.items() if kernel_flops(c, m)}
     dom = max(contractions, key=lambda c: contractions[c][0])
     dom_idx = cats.index(dom)
 
@@ -275,18 +335,18 @@ def main():
     Bd.profile_reset()
     last_loss = float(loss.item())
 
-    f_model, f_ns = alg_flops(depth, V, T, B)
+    f_model, f_ns = alg_flops(m)
     tok = B * T
     step_s = ms / 1e3
     fwd_bwd_ms = sum(v[0] for k, v in breakdown.items()
                      if not k.startswith("ns_") and k not in ("muon_elementwise", "adamw"))
-    kf = kernel_flops(dom, depth, V, T, B)
+    kf = kernel_flops(dom, m)
     avg_launch_s = dom_ms / dom_cnt / 1e3
     achieved = kf / avg_launch_s / 1e12
     fp8 = prec == Bd.PREC_FP8
     peak = (PEAK_FP8 if (fp8 and dom in BLOCK_GEMMS) else PEAK_BF16) / 1e12
     # fp8: the block products run against the fp8 peak, everything else against bf16
-    f_block = block_gemm_flops(depth, T, B) if fp8 else 0.0
+    f_block = block_gemm_flops(m) if fp8 else 0.0
     t_ideal = f_block / PEAK_FP8 + (f_model + f_ns - f_block) / PEAK_BF16
     out = {
         "metric": METRIC,
@@ -301,7 +361,8 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16" if prec == Bd.PREC_BF16 else "fp8-e4m3/e5m2 block GEMMs, bf16 rest",
         "data": "synthetic: uniform token ids, N(0,1/fan_in) weights (seeded PCG64)",
-        "config": {"workload": args.workload, "depth": depth, "d_model": d, "n_head": H, "seq_len": T,
+        "config": {"workload": args.workload, "depth": depth, "d_model": d, "n_head": H,
+                   "n_kv_head": m.Hkv, "window": args.window, "pattern": args.pattern or "L", "seq_len": T,
                    "micro_batch": B, "vocab": V, "tokens_per_step": tok, "parallelism": "single GPU",
                    "optimizer": ("NorMuon" if args.normuon else "Muon") +
                                 " (5 Newton-Schulz iterations) on all block matrices, AdamW on embedding and head"},
@@ -317,7 +378,7 @@ def main():
         "breakdown_ms_per_step": {k: round(v[0], 3) for k, v in sorted(breakdown.items(), key=lambda kv: -kv[1][0])},
     }
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(args.workload, depth, V, T, B, inputs.SEED_IDS, inputs.SEED_W)
+        out["cpu_baseline"] = cpu_baseline(args.workload, m, inputs.SEED_IDS, inputs.SEED_W)
     print(json.dumps(out), flush=True)
 
 
