@@ -9,7 +9,10 @@ $50?": ClimbMix tokens, vocabulary 32,768, sequence length 2048; per-GPU batch
 16 or 32): token ids are uniform over the vocabulary (real text is Zipfian,
 which changes only embedding-gradient collisions and the loss value, not the
 work), weights are N(0, 1/fan_in) with fan_in the number of columns of the
-stored [out, in] matrix, drawn from one PCG64 stream in packed order.
+stored [out, in] matrix, drawn from one PCG64 stream in packed order.  The
+record-model scalars are drawn near their neutral values (residual scale
+1 + 0.1 z, x0 scale 0.1 z, smear scale 0.5 + 0.1 z, backout scale
+0.2 + 0.05 z) so that every term of the step is exercised.
 """
 
 import hashlib
@@ -27,12 +30,18 @@ class Dims:
     hidden: int
     vocab: int
     d_kv: int = 0
+    features: str = ""     # record-model features: any of "v", "s", "r", "b"
 
     @staticmethod
-    def from_depth(depth, vocab=32768, n_kv_head=0):
+    def from_depth(depth, vocab=32768, n_kv_head=0, features=""):
         d = 64 * depth
         return Dims(n_layer=depth, d_model=d, hidden=4 * d, vocab=vocab,
-                    d_kv=128 * n_kv_head if n_kv_head else d)
+                    d_kv=128 * n_kv_head if n_kv_head else d, features=features)
+
+
+SMEAR_CH = 24      # width of the smear gate's input
+VE_GATE_CH = 32    # width of the value-embedding gate's input
+SCALAR_PAD = 6     # unused tail of the scalar block (keeps the packed total a multiple of 4)
 
 
 def packed_tensors(dims):
@@ -46,7 +55,18 @@ def packed_tensors(dims):
     out += [(f"wfc.{i}", (h, d)) for i in range(L)]
     out += [(f"wproj.{i}", (d, h)) for i in range(L)]
     out.append(("lm_head", (V, d)))
+    if dims.features:
+        ve_layers = range(0, L, 2)
+        out += [(f"ve.{i}", (V, dkv)) for i in ve_layers]
+        out += [(f"ve_gate.{i}", (dkv // 128, VE_GATE_CH)) for i in ve_layers]
+        out += [("resid_lambda", (L,)), ("x0_lambda", (L,)), ("smear_w", (SMEAR_CH,)), ("smear_lambda", (1,)),
+                ("backout_lambda", (1,)), ("pad", (SCALAR_PAD,))]
     return out
+
+
+# (offset, scale) of the scalar parameters: value = offset + scale * z
+_SCALARS = {"resid_lambda": (1.0, 0.1), "x0_lambda": (0.0, 0.1), "smear_lambda": (0.5, 0.1),
+            "backout_lambda": (0.2, 0.05), "pad": (0.0, 0.0)}
 
 
 def n_params(dims):
@@ -67,9 +87,14 @@ def master_weights(dims, seed, packed=None):
     total = n_params(dims)
     out = np.empty(total, dtype=np.float32) if packed is None else packed
     off = 0
-    for _, shape in packed_tensors(dims):
+    for name, shape in packed_tensors(dims):
         n = int(np.prod(shape))
-        fan_in = shape[1]
+        if name in _SCALARS:
+            base, sc = _SCALARS[name]
+            out[off: off + n] = (base + sc * g.standard_normal(n)).astype(np.float32)
+            off += n
+            continue
+        fan_in = shape[-1]
         # draw in slabs to bound the float64 temporary
         done = 0
         while done < n:

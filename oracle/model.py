@@ -34,6 +34,28 @@ alternates short and long context; the flash-attention call takes a
     query i sees keys i - w .. i; 'L' layers are full causal; the pattern
     string repeats over the layers (layer i takes pattern[i % len]).
 
+Record-model features (the same model section: value embeddings in the
+ResFormer style, and the efficiency tricks -- per-layer residual scaling,
+smear, backout; each a flag of Config).  The pages show one line or two of
+each; the readings taken:
+  * value embeddings (``value_embeds``): layers 0, 2, 4, ... ("alternating
+    layers") own a table VE_i [V, n_kv_head * hd] gathered by the input
+    token; gate = 3 sigmoid(h[:, :VE_GATE_CH] Wg_i^T) per key/value head, h
+    being the attention's input (the normed stream) and Wg_i [n_kv_head,
+    VE_GATE_CH] with VE_GATE_CH = 32 (the pages name the width, not its
+    value); v <- v + gate * VE_i[ids] after the projection;
+  * smear (``smear``): right after the embedding gather, token t >= 1 of a
+    sequence adds gate_t times the previous token's embedding, gate_t =
+    smear_lambda * sigmoid(e_t[:24] . smear_w) with e_t the token's own
+    embedding (24 channels as printed); token 0 is unchanged;
+  * per-layer residual scaling (``resid_lambdas``): layer i starts with
+    x <- resid_lambda[i] x + x0_lambda[i] x0, x0 the stream after the
+    embedding (and smear);
+  * backout (``backout``): x_mid is the stream after layer L/2 - 1 (the
+    middle); before the final norm x <- x - backout_lambda x_mid.
+  The scalars and gates are parameters (the optimizer passage gives scalar
+  parameters to AdamW); the extra tensors follow lm_head in packed order.
+
 fp8 mode (``fp8=True``): the four block projections (qkv, out, fc, proj) use
 per-tensor scaled fake quantisation as the precision passage describes
 (apidog.com/pt "Gerenciamento de Precisão", apidog.com/de
@@ -72,14 +94,30 @@ class Config:
     n_kv_head: int = 0     # key/value heads (GQA); 0 = n_head
     window: int = 0        # 'S' layers: query i sees keys i - window .. i; 0 = every layer full
     pattern: str = "L"     # per-layer pattern, repeated over the layers ('S' short, 'L' long)
+    value_embeds: bool = False
+    smear: bool = False
+    resid_lambdas: bool = False
+    backout: bool = False
 
     @staticmethod
-    def from_depth(depth, vocab=32768, n_kv_head=0, window=0, pattern="L"):
+    def from_depth(depth, vocab=32768, n_kv_head=0, window=0, pattern="L", features=""):
         """Shapes from the single depth dial: width 64*depth, 128-wide heads,
-        MLP 4x (dev.to page, "La Filosofía: Un Solo Selector")."""
+        MLP 4x (dev.to page, "La Filosofía: Un Solo Selector").  features: any
+        of "v" (value embeddings), "s" (smear), "r" (residual scaling), "b"
+        (backout)."""
         d = 64 * depth
         return Config(n_layer=depth, d_model=d, n_head=d // 128, head_dim=128,
-                      hidden=4 * d, vocab=vocab, n_kv_head=n_kv_head, window=window, pattern=pattern)
+                      hidden=4 * d, vocab=vocab, n_kv_head=n_kv_head, window=window, pattern=pattern,
+                      value_embeds="v" in features, smear="s" in features, resid_lambdas="r" in features,
+                      backout="b" in features)
+
+    @property
+    def has_features(self):
+        return self.value_embeds or self.smear or self.resid_lambdas or self.backout
+
+    def ve_layers(self):
+        """Layers with a value embedding (every other layer from the first)."""
+        return list(range(0, self.n_layer, 2))
 
     @property
     def kv_heads(self):
@@ -95,6 +133,14 @@ class Config:
 # ----------------------------------------------------------------------------
 # building blocks
 # ----------------------------------------------------------------------------
+
+SMEAR_CH = 24      # embedding channels feeding the smear gate (as printed)
+VE_GATE_CH = 32    # channels of the attention input feeding the value-embedding gate
+
+
+def sigmoid(z):
+    return 1.0 / (1.0 + np.exp(-z))
+
 
 def rms_norm(x, eps):
     """y = x / sqrt(mean(x^2) + eps) over the last axis; returns (y, r) with
@@ -221,24 +267,33 @@ def _lin_bwd(x2, w, dy2, fp8):
 
 def param_names(cfg):
     """Parameter tensors in packed order: wte, per layer (wq, wk, wv, wo),
-    per layer wfc, per layer wproj, lm_head."""
+    per layer wfc, per layer wproj, lm_head; with any record-model feature
+    then every value-embedding table, every value-embedding gate and the
+    scalars (resid_lambda, x0_lambda, smear_w, smear_lambda, backout_lambda)."""
     names = ["wte"]
     for i in range(cfg.n_layer):
         names += [f"wq.{i}", f"wk.{i}", f"wv.{i}", f"wo.{i}"]
     names += [f"wfc.{i}" for i in range(cfg.n_layer)]
     names += [f"wproj.{i}" for i in range(cfg.n_layer)]
     names.append("lm_head")
+    if cfg.has_features:
+        names += [f"ve.{i}" for i in cfg.ve_layers()]
+        names += [f"ve_gate.{i}" for i in cfg.ve_layers()]
+        names += ["resid_lambda", "x0_lambda", "smear_w", "smear_lambda", "backout_lambda"]
     return names
 
 
 def param_shapes(cfg):
-    d, h, V = cfg.d_model, cfg.hidden, cfg.vocab
+    d, h, V, L = cfg.d_model, cfg.hidden, cfg.vocab, cfg.n_layer
     dkv = cfg.kv_heads * cfg.head_dim
     shapes = {}
     for n in param_names(cfg):
         base = n.split(".")[0]
         shapes[n] = {"wte": (V, d), "lm_head": (V, d), "wq": (d, d), "wk": (dkv, d),
-                     "wv": (dkv, d), "wo": (d, d), "wfc": (h, d), "wproj": (d, h)}[base]
+                     "wv": (dkv, d), "wo": (d, d), "wfc": (h, d), "wproj": (d, h),
+                     "ve": (V, dkv), "ve_gate": (cfg.kv_heads, VE_GATE_CH), "resid_lambda": (L,),
+                     "x0_lambda": (L,), "smear_w": (SMEAR_CH,), "smear_lambda": (1,),
+                     "backout_lambda": (1,)}[base]
     return shapes
 
 
@@ -258,16 +313,40 @@ def _forward_backward_chunk(P, ids, cfg, loss_scale, dtype, want_grads, want_log
     tgt = ids[:, 1:].reshape(-1)
     eps = cfg.eps
 
-    x = P["wte"][inp].astype(dtype)  # [R, d]
+    L = cfg.n_layer
+    ve_set = set(cfg.ve_layers()) if cfg.value_embeds else set()
+    e = P["wte"][inp].astype(dtype)  # [R, d] token embeddings
+    x = e
+    if cfg.smear:
+        # token t >= 1 adds gate_t * (embedding of token t-1) within its sequence
+        e3 = e.reshape(B, T, d)
+        prev = np.zeros_like(e3)
+        prev[:, 1:] = e3[:, :-1]
+        s_sig = sigmoid(e3[..., :SMEAR_CH] @ P["smear_w"])         # [B, T]
+        s_gate = P["smear_lambda"][0] * s_sig
+        s_gate[:, 0] = 0.0
+        x = (e3 + s_gate[..., None] * prev).reshape(R, d)
+    x0 = x
+    x_mid = None
     caches = []
-    for i in range(cfg.n_layer):
+    for i in range(L):
+        x_in = x
+        if cfg.resid_lambdas:
+            x = P["resid_lambda"][i] * x + P["x0_lambda"][i] * x0
         wqkv = np.concatenate([P[f"wq.{i}"], P[f"wk.{i}"], P[f"wv.{i}"]], axis=0)
         h1, r1 = rms_norm(x, eps)
         h1o = op(h1)
         qkv = _lin_fwd(h1o, wqkv, fp8)
         q_raw = qkv[:, :d].reshape(B, T, H, hd).transpose(0, 2, 1, 3)
         k_raw = qkv[:, d:d + dkv].reshape(B, T, Hkv, hd).transpose(0, 2, 1, 3)
-        v = op(qkv[:, d + dkv:].reshape(B, T, Hkv, hd).transpose(0, 2, 1, 3))
+        v_lin = qkv[:, d + dkv:]
+        ve = v_gate = None
+        if i in ve_set:
+            # value embedding of the input token, gated per key/value head
+            ve = P[f"ve.{i}"][inp].reshape(R, Hkv, hd)
+            v_gate = 3.0 * sigmoid(h1o[:, :VE_GATE_CH] @ P[f"ve_gate.{i}"].T)   # [R, Hkv]
+            v_lin = v_lin + (v_gate[:, :, None] * ve).reshape(R, dkv)
+        v = op(v_lin.reshape(B, T, Hkv, hd).transpose(0, 2, 1, 3))
         qn, rq = rms_norm(rope(q_raw, cos, sin), eps)
         kn, rk = rms_norm(rope(k_raw, cos, sin), eps)
         qs, ks = op(qn), op(kn)
@@ -281,8 +360,13 @@ def _forward_backward_chunk(P, ids, cfg, loss_scale, dtype, want_grads, want_log
         u = _lin_fwd(h2o, P[f"wfc.{i}"], fp8)
         a = op(np.maximum(u, 0.0) ** 2)
         x = x + _lin_fwd(a, P[f"wproj.{i}"], fp8)
-        caches.append((h1, h1o, r1, wqkv, qn, qs, rq, kn, ks, rk, v, y2, lse_att, h2, h2o, r2, u, a))
+        caches.append((x_in, h1, h1o, r1, wqkv, qn, qs, rq, kn, ks, rk, v, ve, v_gate, y2, lse_att, h2, h2o,
+                       r2, u, a))
+        if cfg.backout and i == L // 2 - 1:
+            x_mid = x
 
+    if cfg.backout:
+        x = x - P["backout_lambda"][0] * x_mid
     hf, rf = rms_norm(x, eps)
     hfo = op(hf)
     z = hfo @ P["lm_head"].T
@@ -300,8 +384,18 @@ def _forward_backward_chunk(P, ids, cfg, loss_scale, dtype, want_grads, want_log
     Gr["lm_head"] = dz.T @ hfo
     g = rms_norm_bwd(dz @ P["lm_head"], hf, rf)
     del dz
-    for i in reversed(range(cfg.n_layer)):
-        (h1, h1o, r1, wqkv, qn, qs, rq, kn, ks, rk, v, y2, lse_att, h2, h2o, r2, u, a) = caches[i]
+    if cfg.has_features:
+        for n in ("resid_lambda", "x0_lambda", "smear_w", "smear_lambda", "backout_lambda"):
+            Gr[n] = np.zeros(P[n].shape, dtype=dtype)
+    if cfg.backout:
+        Gr["backout_lambda"][0] = -np.sum(g * x_mid)
+        g_mid = -P["backout_lambda"][0] * g
+    g0 = np.zeros_like(g) if cfg.resid_lambdas else None   # gradient reaching x0 through the lambdas
+    for i in reversed(range(L)):
+        (x_in, h1, h1o, r1, wqkv, qn, qs, rq, kn, ks, rk, v, ve, v_gate, y2, lse_att, h2, h2o, r2, u,
+         a) = caches[i]
+        if cfg.backout and i == L // 2 - 1:
+            g = g + g_mid
         # MLP
         gb = op(g)
         da, Gr[f"wproj.{i}"] = _lin_bwd(a, P[f"wproj.{i}"], gb, fp8)
@@ -323,11 +417,45 @@ def _forward_backward_chunk(P, ids, cfg, loss_scale, dtype, want_grads, want_log
         dqkv = op(np.concatenate([t.transpose(0, 2, 1, 3).reshape(R, -1) for t in (dq, dk, dv)], axis=1))
         dh1, dwqkv = _lin_bwd(h1o, wqkv, dqkv, fp8)
         Gr[f"wq.{i}"], Gr[f"wk.{i}"], Gr[f"wv.{i}"] = dwqkv[:d], dwqkv[d:d + dkv], dwqkv[d + dkv:]
+        if ve is not None:
+            dv3 = dqkv[:, d + dkv:].reshape(R, Hkv, hd)       # gradient of v after the value embedding
+            dve = np.zeros(P[f"ve.{i}"].shape, dtype=dtype)
+            np.add.at(dve, inp, (v_gate[:, :, None] * dv3).reshape(R, dkv))
+            Gr[f"ve.{i}"] = dve
+            # gate = 3 sigmoid(z): dgate/dz = gate (1 - gate / 3)
+            dzg = np.sum(dv3 * ve, axis=-1) * v_gate * (1.0 - v_gate / 3.0)   # [R, Hkv]
+            Gr[f"ve_gate.{i}"] = dzg.T @ h1o[:, :VE_GATE_CH]
+            dh1 = dh1.copy()
+            dh1[:, :VE_GATE_CH] += dzg @ P[f"ve_gate.{i}"]
         g = g + rms_norm_bwd(dh1, h1, r1)
+        if cfg.resid_lambdas:
+            # x = resid_lambda x_in + x0_lambda x0
+            Gr["resid_lambda"][i] = np.sum(g * x_in)
+            Gr["x0_lambda"][i] = np.sum(g * x0)
+            g0 += P["x0_lambda"][i] * g
+            g = P["resid_lambda"][i] * g
         caches[i] = None
+    if g0 is not None:
+        g = g + g0
+    if cfg.smear:
+        # x_t = e_t + gate_t e_{t-1}, gate_t = lambda sigmoid(e_t[:24] . w)
+        dX = g.reshape(B, T, d)
+        de = dX.copy()
+        de[:, :-1] += s_gate[:, 1:, None] * dX[:, 1:]
+        dgate = np.sum(dX * prev, axis=-1)
+        dgate[:, 0] = 0.0
+        Gr["smear_lambda"][0] = np.sum(dgate * s_sig)
+        dzs = dgate * P["smear_lambda"][0] * s_sig * (1.0 - s_sig)
+        Gr["smear_w"] = np.einsum("bt,btc->c", dzs, e3[..., :SMEAR_CH])
+        de[..., :SMEAR_CH] += dzs[..., None] * P["smear_w"]
+        g = de.reshape(R, d)
     dwte = np.zeros(P["wte"].shape, dtype=dtype)
     np.add.at(dwte, inp, g)
     Gr["wte"] = dwte
+    for i in (range(L) if cfg.has_features else ()):
+        if f"ve.{i}" in P and f"ve.{i}" not in Gr:
+            Gr[f"ve.{i}"] = np.zeros(P[f"ve.{i}"].shape, dtype=dtype)
+            Gr[f"ve_gate.{i}"] = np.zeros(P[f"ve_gate.{i}"].shape, dtype=dtype)
     out["grads"] = Gr
     return out
 

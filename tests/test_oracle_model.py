@@ -367,3 +367,186 @@ def test_inputs_gqa_shapes():
     shp = dict(inputs.packed_tensors(dims))
     assert shp["wk.0"] == (128, 256) and shp["wv.3"] == (128, 256) and shp["wq.0"] == (256, 256)
     assert inputs.Dims.from_depth(4).d_kv == 256
+
+
+# ---------------------------------------------------------------------------
+# record-model features: value embeddings, smear, residual scaling, backout
+# ---------------------------------------------------------------------------
+
+TINY_FEAT = om.Config(n_layer=4, d_model=48, n_head=6, head_dim=8, hidden=96, vocab=31, n_kv_head=3,
+                      window=3, pattern="SL", value_embeds=True, smear=True, resid_lambdas=True, backout=True)
+
+
+def _feat_params(cfg, seed=0, scale=1.5):
+    """Matrices N(0, scale^2 / fan_in); scalars near their neutral values."""
+    g = np.random.default_rng(seed)
+    P = {}
+    for name, shape in om.param_shapes(cfg).items():
+        z = g.standard_normal(shape)
+        if name == "resid_lambda":
+            P[name] = 1.0 + 0.2 * z
+        elif name == "x0_lambda":
+            P[name] = 0.3 * z
+        elif name == "smear_lambda":
+            P[name] = 0.6 + 0.2 * z
+        elif name == "backout_lambda":
+            P[name] = 0.3 + 0.1 * z
+        else:
+            P[name] = z * scale / math.sqrt(shape[-1])
+    return P
+
+
+def test_feature_layout():
+    cfg = TINY_FEAT
+    names = om.param_names(cfg)
+    assert names[-5:] == ["resid_lambda", "x0_lambda", "smear_w", "smear_lambda", "backout_lambda"]
+    assert [n for n in names if n.startswith("ve.")] == ["ve.0", "ve.2"]
+    shp = om.param_shapes(cfg)
+    assert shp["ve.2"] == (31, 24) and shp["ve_gate.0"] == (3, om.VE_GATE_CH) and shp["smear_w"] == (24,)
+    # the packed order of the input generator matches (it adds only an unused pad)
+    dims = inputs.Dims.from_depth(4, 1000, n_kv_head=1, features="vsrb")
+    cfg4 = om.Config.from_depth(4, 1000, n_kv_head=1, features="vsrb")
+    packed = [(n, s) for n, s in inputs.packed_tensors(dims) if n != "pad"]
+    assert packed == [(n, om.param_shapes(cfg4)[n]) for n in om.param_names(cfg4)]
+    assert inputs.n_params(dims) % 4 == 0
+
+
+def test_finite_differences_features():
+    cfg = TINY_FEAT
+    P = _feat_params(cfg, seed=71)
+    ids = _tiny_ids(cfg, B=2, T=9, seed=72)
+    out = om.forward_backward(P, ids, cfg)
+    rng = np.random.default_rng(73)
+    h = 1e-5
+    for name in om.param_names(cfg):
+        W = P[name]
+        for _ in range(3):
+            idx = tuple(int(rng.integers(0, s)) for s in W.shape)
+            if name == "wte" or name.startswith("ve."):   # a row that is used
+                idx = (int(ids[0, int(rng.integers(0, ids.shape[1] - 1))]), idx[1])
+            old = W[idx]
+            W[idx] = old + h
+            lp = om.forward_backward(P, ids, cfg, want_grads=False)["loss"]
+            W[idx] = old - h
+            lm = om.forward_backward(P, ids, cfg, want_grads=False)["loss"]
+            W[idx] = old
+            fd = (lp - lm) / (2 * h)
+            an = out["grads"][name][idx]
+            assert abs(fd - an) / (abs(an) + 1e-4) < 1e-6, (name, idx, fd, an)
+
+
+def test_features_against_torch_autograd():
+    torch = pytest.importorskip("torch")
+    F = torch.nn.functional
+    cfg = TINY_FEAT
+    P = _feat_params(cfg, seed=81)
+    ids = _tiny_ids(cfg, B=2, T=10, seed=82)
+    out = om.forward_backward(P, ids, cfg)
+    tp = {k: torch.tensor(v, dtype=torch.float64, requires_grad=True) for k, v in P.items()}
+    B, T = ids.shape[0], ids.shape[1] - 1
+    d, H, Hkv, hd, L = cfg.d_model, cfg.n_head, cfg.n_kv_head, cfg.head_dim, cfg.n_layer
+    inp, tgt = torch.tensor(ids[:, :T]), torch.tensor(ids[:, 1:])
+    freq = cfg.rope_base ** (-torch.arange(0, hd, 2, dtype=torch.float64) / hd)
+    rot = torch.polar(torch.ones(T, hd // 2, dtype=torch.float64),
+                      torch.arange(T, dtype=torch.float64)[:, None] * freq[None, :])
+
+    def rope_t(x):
+        xc = torch.complex(x[..., : hd // 2], x[..., hd // 2:]) * rot
+        return torch.cat([xc.real, xc.imag], dim=-1)
+
+    def rms(x, n):
+        return F.rms_norm(x, (n,), eps=cfg.eps)
+
+    ii = torch.arange(T)[:, None]
+    jj = torch.arange(T)[None, :]
+    emb = tp["wte"][inp]                                      # [B, T, d]
+    # smear: shift the embeddings one step along the sequence (zero before the first)
+    shifted = F.pad(emb, (0, 0, 1, 0))[:, :T]
+    gate = tp["smear_lambda"] * torch.sigmoid(emb[..., :24] @ tp["smear_w"])
+    x = emb + gate.unsqueeze(-1) * shifted
+    x0 = x
+    for i in range(L):
+        x = tp["resid_lambda"][i] * x + tp["x0_lambda"][i] * x0
+        h = rms(x, d)
+        q = (h @ tp[f"wq.{i}"].T).view(B, T, H, hd).transpose(1, 2)
+        k = (h @ tp[f"wk.{i}"].T).view(B, T, Hkv, hd).transpose(1, 2)
+        v = (h @ tp[f"wv.{i}"].T).view(B, T, Hkv, hd)
+        if i % 2 == 0:
+            g = 3 * torch.sigmoid(h[..., :32] @ tp[f"ve_gate.{i}"].T)      # [B, T, Hkv]
+            v = v + g.unsqueeze(-1) * tp[f"ve.{i}"][inp].view(B, T, Hkv, hd)
+        v = v.transpose(1, 2)
+        q, k = rms(rope_t(q), hd), rms(rope_t(k), hd)
+        w = cfg.layer_window(i)
+        allowed = jj <= ii if w is None else (jj <= ii) & (jj >= ii - w)
+        y = F.scaled_dot_product_attention(q, k.repeat_interleave(H // Hkv, dim=1),
+                                           v.repeat_interleave(H // Hkv, dim=1), attn_mask=allowed)
+        x = x + y.transpose(1, 2).reshape(B, T, d) @ tp[f"wo.{i}"].T
+        h = rms(x, d)
+        x = x + F.relu(h @ tp[f"wfc.{i}"].T).square() @ tp[f"wproj.{i}"].T
+        if i == L // 2 - 1:
+            x_mid = x
+    x = x - tp["backout_lambda"] * x_mid
+    z = rms(x, d) @ tp["lm_head"].T
+    loss = F.cross_entropy(z.reshape(-1, cfg.vocab), tgt.reshape(-1))
+    loss.backward()
+    assert out["loss"] == pytest.approx(loss.item(), rel=1e-12)
+    for name in om.param_names(cfg):
+        ref = tp[name].grad.numpy()
+        assert np.abs(out["grads"][name] - ref).max() <= 1e-11 * max(1.0, np.abs(ref).max()), name
+
+
+def test_features_at_neutral_values_are_the_plain_model():
+    cfg = TINY_FEAT
+    plain = om.Config(**{**cfg.__dict__, "value_embeds": False, "smear": False, "resid_lambdas": False,
+                         "backout": False})
+    P = _feat_params(cfg, seed=91)
+    P["resid_lambda"][:] = 1.0
+    P["x0_lambda"][:] = 0.0
+    P["smear_lambda"][:] = 0.0
+    P["backout_lambda"][:] = 0.0
+    for i in cfg.ve_layers():
+        P[f"ve.{i}"][:] = 0.0
+    ids = _tiny_ids(cfg, B=2, T=9, seed=92)
+    a = om.forward_backward(P, ids, cfg)
+    b = om.forward_backward({n: P[n] for n in om.param_names(plain)}, ids, plain)
+    assert a["loss"] == pytest.approx(b["loss"], rel=1e-13)
+    for name in om.param_names(plain):
+        assert np.allclose(a["grads"][name], b["grads"][name], rtol=1e-11, atol=1e-14), name
+
+
+def test_features_are_causal():
+    """The loss of position t does not depend on inputs after t (smear reads the
+    previous token, never the next)."""
+    cfg = TINY_FEAT
+    P = _feat_params(cfg, seed=93)
+    ids = _tiny_ids(cfg, B=1, T=9, seed=94)
+    base = om.forward_backward(P, ids, cfg, want_grads=False)["row_loss"][0]
+    ids2 = ids.copy()
+    ids2[0, 6] = (ids2[0, 6] + 5) % cfg.vocab        # input of position 6 (target of position 5)
+    alt = om.forward_backward(P, ids2, cfg, want_grads=False)["row_loss"][0]
+    assert np.array_equal(base[:5], alt[:5])
+    assert not np.allclose(base[6:], alt[6:])
+
+
+def test_smear_leaves_the_first_position():
+    cfg = om.Config(**{**TINY_FEAT.__dict__, "value_embeds": False, "resid_lambdas": False, "backout": False})
+    plain = om.Config(**{**cfg.__dict__, "smear": False})
+    P = _feat_params(cfg, seed=95)
+    ids = _tiny_ids(cfg, B=2, T=9, seed=96)
+    a = om.forward_backward(P, ids, cfg, want_grads=False)["row_loss"]
+    b = om.forward_backward({n: P[n] for n in om.param_names(plain)}, ids, plain, want_grads=False)["row_loss"]
+    assert np.array_equal(a[:, 0], b[:, 0])
+    assert not np.allclose(a[:, 1:], b[:, 1:])
+
+
+def test_first_layer_lambdas_have_equal_gradients():
+    """Layer 0's input is x0 itself, so resid_lambda[0] and x0_lambda[0] act
+    on the same tensor: equal gradients, and only their sum matters."""
+    cfg = TINY_FEAT
+    P = _feat_params(cfg, seed=97)
+    ids = _tiny_ids(cfg, B=2, T=9, seed=98)
+    out = om.forward_backward(P, ids, cfg)
+    assert out["grads"]["resid_lambda"][0] == out["grads"]["x0_lambda"][0]
+    P2 = {k: v.copy() for k, v in P.items()}
+    P2["resid_lambda"][0], P2["x0_lambda"][0] = P["x0_lambda"][0], P["resid_lambda"][0]
+    assert om.forward_backward(P2, ids, cfg, want_grads=False)["loss"] == pytest.approx(out["loss"], rel=1e-14)
