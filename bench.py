@@ -208,6 +208,8 @@ def main():
     ap.add_argument("--n-kv-head", type=int, default=0, help="key/value heads (0: one per query head)")
     ap.add_argument("--window", type=int, default=0, help="left window of the short ('S') layers")
     ap.add_argument("--pattern", default="", help="layer pattern of S (windowed) / L (full) letters, e.g. SSSL")
+    ap.add_argument("--features", default="",
+                    help="record-model features: v (value embeddings), s (smear), r (residual scalars), b (backout)")
     ap.add_argument("--breakdown", action="store_true", help="print per-kernel times to stderr")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device-to-device copy of BYTES three times and exit (the reference "
@@ -239,9 +241,10 @@ def main():
     d, H = m.d, m.H
     prec = Bd.PREC_FP8 if args.precision == "fp8" else Bd.PREC_BF16
     dev = torch.device("cuda:0")
-    sh = Bd.shape(depth, V, T, B, prec, n_kv_head=args.n_kv_head, window=args.window, pattern=args.pattern)
+    sh = Bd.shape(depth, V, T, B, prec, n_kv_head=args.n_kv_head, window=args.window, pattern=args.pattern,
+                  features=args.features)
     n = Bd.param_count(sh)
-    dims = inputs.Dims.from_depth(depth, V, args.n_kv_head)
+    dims = inputs.Dims.from_depth(depth, V, args.n_kv_head, features=args.features)
     assert n == inputs.n_params(dims)
     master_np = inputs.master_weights(dims, inputs.SEED_W)
     master = torch.from_numpy(master_np).to(dev)
@@ -266,10 +269,15 @@ def main():
                            ws=torch.empty(Bd.muon_workspace_size(count, rows, cols), dtype=torch.uint8,
                                           device=dev)))
 
-    # AdamW for the embedding and the head (the two [V, d] tables)
+    # AdamW for the embedding and the head (the two [V, d] tables) and, with the
+    # record-model features, for everything after the head (value-embedding
+    # tables, their gates and the scalars)
+    lm = offs[1 + 6 * depth]
+    ranges = [(offs[0], V * d), (lm, V * d)]
+    if args.features:
+        ranges.append((lm + V * d, n - (lm + V * d)))
     adam = []
-    for start in (offs[0], offs[-1]):
-        size = V * d
+    for start, size in ranges:
         adam.append(dict(start=start, size=size, M=torch.zeros(size, dtype=torch.float32, device=dev),
                          V=torch.zeros(size, dtype=torch.float32, device=dev)))
     step_count = [0]
@@ -362,10 +370,12 @@ def main():
         "dtype": "bf16" if prec == Bd.PREC_BF16 else "fp8-e4m3/e5m2 block GEMMs, bf16 rest",
         "data": "synthetic: uniform token ids, N(0,1/fan_in) weights (seeded PCG64)",
         "config": {"workload": args.workload, "depth": depth, "d_model": d, "n_head": H,
-                   "n_kv_head": m.Hkv, "window": args.window, "pattern": args.pattern or "L", "seq_len": T,
+                   "n_kv_head": m.Hkv, "window": args.window, "pattern": args.pattern or "L",
+                   "features": args.features or "none", "seq_len": T,
                    "micro_batch": B, "vocab": V, "tokens_per_step": tok, "parallelism": "single GPU",
                    "optimizer": ("NorMuon" if args.normuon else "Muon") +
-                                " (5 Newton-Schulz iterations) on all block matrices, AdamW on embedding and head"},
+                                " (5 Newton-Schulz iterations) on all block matrices, AdamW on embedding and head" +
+                                (" and the record-model tensors" if args.features else "")},
         "mfu": (f_model + f_ns) / step_s / PEAK_BF16,
         "mfu_vs_mixed_peak": t_ideal / step_s if fp8 else None,
         "mfu_model": f_model / (fwd_bwd_ms / 1e3) / PEAK_BF16 if fwd_bwd_ms else None,

@@ -37,7 +37,12 @@ class GptError(RuntimeError):
 class Shape(ctypes.Structure):
     _fields_ = [("depth", ctypes.c_int32), ("vocab", ctypes.c_int32), ("seq_len", ctypes.c_int32),
                 ("batch", ctypes.c_int32), ("precision", ctypes.c_int32), ("n_kv_head", ctypes.c_int32),
-                ("window", ctypes.c_int32), ("pattern_len", ctypes.c_int32), ("pattern_long", ctypes.c_uint32)]
+                ("window", ctypes.c_int32), ("pattern_len", ctypes.c_int32), ("pattern_long", ctypes.c_uint32),
+                ("features", ctypes.c_uint32)]
+
+
+# record-model feature letters -> gpt_shape.features bits
+FEATURE_BITS = {"v": 1, "s": 2, "r": 4, "b": 8}
 
 
 class Params(ctypes.Structure):
@@ -124,16 +129,23 @@ def _stream(stream=None):
     return stream.cuda_stream if hasattr(stream, "cuda_stream") else stream
 
 
-def shape(depth, vocab, seq_len, batch, precision=PREC_BF16, n_kv_head=0, window=0, pattern=""):
+def shape(depth, vocab, seq_len, batch, precision=PREC_BF16, n_kv_head=0, window=0, pattern="", features=""):
     """pattern: string of 'S' (windowed) / 'L' (full causal) layers, repeated
-    over the depth (e.g. "SSSL"); empty = every layer full."""
+    over the depth (e.g. "SSSL"); empty = every layer full.  features: letters
+    of the record-model features, "v" value embeddings, "s" smear, "r"
+    per-layer residual scalars, "b" backout."""
+    fbits = 0
+    for ch in features:
+        if ch not in FEATURE_BITS:
+            raise ValueError("feature letters are v, s, r, b")
+        fbits |= FEATURE_BITS[ch]
     bits = 0
     for i, ch in enumerate(pattern):
         if ch not in "SL":
             raise ValueError("pattern letters are S and L")
         if ch == "L":
             bits |= 1 << i
-    return Shape(depth, vocab, seq_len, batch, precision, n_kv_head, window, len(pattern), bits)
+    return Shape(depth, vocab, seq_len, batch, precision, n_kv_head, window, len(pattern), bits, fbits)
 
 
 def param_count(sh):
@@ -144,7 +156,7 @@ def param_count(sh):
 
 def param_layout(sh):
     n = _i32()
-    cap = 2 + 6 * sh.depth
+    cap = 2 + 7 * sh.depth + 6
     offs = (_sz * cap)()
     _call("gpt_param_layout", ctypes.byref(sh), offs, cap, ctypes.byref(n))
     return [offs[i] for i in range(n.value)]

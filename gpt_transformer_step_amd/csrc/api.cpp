@@ -54,7 +54,7 @@ extern "C" const char* gpt_status_string(gpt_status s) {
 
 extern "C" const char* gpt_last_error(void) { return gs::g_err.c_str(); }
 
-extern "C" int32_t gpt_abi_version(void) { return 2; }
+extern "C" int32_t gpt_abi_version(void) { return 3; }
 
 // ---------------------------------------------------------------------------
 // shapes and layouts
@@ -66,7 +66,10 @@ struct Dims {
   int Hkv, dkv, dqkv;  // key/value heads, their width 128 Hkv, and the [q | k | v] width d + 2 dkv
   int window, pat_len;
   uint32_t pat_long;
+  uint32_t feat;  // GPT_FEAT_* bits
   long long N;  // tokens per step
+  bool has(uint32_t bit) const { return (feat & bit) != 0; }
+  bool ve_layer(int l) const { return has(GPT_FEAT_VALUE_EMBED) && (l % 2) == 0; }
   // left attention window of layer l (-1: full causal)
   int layer_window(int l) const {
     if (window <= 0 || pat_len <= 0) return -1;
@@ -97,6 +100,8 @@ int check_shape(const gpt_shape* s, Dims* o) {
   o->window = s->window;
   o->pat_len = s->pattern_len;
   o->pat_long = s->pattern_long;
+  if (s->features & ~15u) FAIL(GPT_ERR_SHAPE, "unknown feature bits");
+  o->feat = s->features;
   o->hidden = 4 * o->d;
   o->V = s->vocab;
   o->T = s->seq_len;
@@ -115,7 +120,15 @@ struct ParamLayout {
   size_t wo(const Dims& D, int l) const { return qkv(D, l) + (size_t)D.dqkv * D.d; }
   size_t fc(const Dims& D, int l) const { return s_end + (size_t)l * D.hidden * D.d; }
   size_t proj(const Dims& D, int l) const { return f_end + (size_t)l * D.d * D.hidden; }
-  size_t wte_end, s_end, f_end, p_end;
+  // record-model tensors (present when any feature bit is set); l even
+  size_t ve(const Dims& D, int l) const { return lm_end + (size_t)(l / 2) * D.V * D.dkv; }
+  size_t vg(const Dims& D, int l) const { return vg0 + (size_t)(l / 2) * D.Hkv * 32; }
+  size_t resid_l(int l) const { return sc + l; }
+  size_t x0lam(const Dims& D, int l) const { return sc + D.L + l; }
+  size_t smear_w(const Dims& D) const { return sc + 2 * (size_t)D.L; }
+  size_t smear_lam(const Dims& D) const { return sc + 2 * (size_t)D.L + 24; }
+  size_t backout(const Dims& D) const { return sc + 2 * (size_t)D.L + 25; }
+  size_t wte_end, s_end, f_end, p_end, lm_end, vg0, sc;
 };
 
 ParamLayout param_layout(const Dims& D) {
@@ -126,7 +139,15 @@ ParamLayout param_layout(const Dims& D) {
   p.f_end = p.s_end + (size_t)D.L * D.hidden * D.d;
   p.p_end = p.f_end + (size_t)D.L * D.d * D.hidden;
   p.lm_head = p.p_end;
-  p.total = p.lm_head + (size_t)D.V * D.d;
+  p.lm_end = p.lm_head + (size_t)D.V * D.d;
+  p.total = p.lm_end;
+  p.vg0 = p.sc = p.lm_end;
+  if (D.feat) {
+    const size_t nve = (size_t)(D.L / 2);
+    p.vg0 = p.lm_end + nve * D.V * D.dkv;
+    p.sc = p.vg0 + nve * D.Hkv * 32;
+    p.total = p.sc + 2 * (size_t)D.L + 32;  // resid, x0lam, w[24], lam, backout, 6 unused
+  }
   return p;
 }
 
@@ -145,9 +166,9 @@ extern "C" gpt_status gpt_param_layout(const gpt_shape* shape, size_t* offsets, 
   Dims D;
   TRY(check_shape(shape, &D));
   if (!n_tensors) FAIL(GPT_ERR_INVALID_ARG, "n_tensors is NULL");
-  const int n = 2 + 6 * D.L;
+  const int n = 2 + 6 * D.L + (D.feat ? D.L + 6 : 0);
   *n_tensors = n;
-  if (!offsets || capacity < n) FAIL(GPT_ERR_INVALID_ARG, "offsets NULL or capacity < 2 + 6*depth");
+  if (!offsets || capacity < n) FAIL(GPT_ERR_INVALID_ARG, "offsets NULL or capacity below the tensor count");
   const ParamLayout P = param_layout(D);
   int i = 0;
   offsets[i++] = P.wte;
@@ -160,6 +181,16 @@ extern "C" gpt_status gpt_param_layout(const gpt_shape* shape, size_t* offsets, 
   for (int l = 0; l < D.L; ++l) offsets[i++] = P.fc(D, l);
   for (int l = 0; l < D.L; ++l) offsets[i++] = P.proj(D, l);
   offsets[i++] = P.lm_head;
+  if (D.feat) {
+    for (int l = 0; l < D.L; l += 2) offsets[i++] = P.ve(D, l);
+    for (int l = 0; l < D.L; l += 2) offsets[i++] = P.vg(D, l);
+    offsets[i++] = P.resid_l(0);
+    offsets[i++] = P.x0lam(D, 0);
+    offsets[i++] = P.smear_w(D);
+    offsets[i++] = P.smear_lam(D);
+    offsets[i++] = P.backout(D);
+    offsets[i++] = P.backout(D) + 1;
+  }
   return GPT_OK;
 }
 
@@ -259,14 +290,14 @@ enum ProfCat {
   P_EMBED_FWD, P_RMSNORM_FWD, P_GEMM_QKV, P_ATTN_FWD, P_GEMM_O, P_GEMM_FC, P_GEMM_PROJ, P_CE_FWD,
   P_CE_REDUCE, P_CE_DZ, P_CE_DH, P_CE_DW, P_RMSNORM_BWD, P_PROJ_DGRAD, P_PROJ_WGRAD, P_FC_DGRAD,
   P_FC_WGRAD, P_O_DGRAD, P_O_WGRAD, P_ATTN_BWD_PRE, P_ATTN_BWD_KV, P_ATTN_BWD_Q, P_ROPE_BWD, P_QKV_DGRAD, P_QKV_WGRAD, P_EMBED_BWD,
-  P_FILL, P_MUON_ELEMWISE, P_NS_GRAM, P_NS_POLY, P_NS_UPDATE, P_FP8_QUANT, P_ADAMW, P_COUNT
+  P_FILL, P_MUON_ELEMWISE, P_NS_GRAM, P_NS_POLY, P_NS_UPDATE, P_FP8_QUANT, P_ADAMW, P_FEATURES, P_COUNT
 };
 const char* kProfNames[P_COUNT] = {
     "embed_fwd", "rmsnorm_fwd", "gemm_qkv_rope_fwd", "attn_fwd", "gemm_o_fwd", "gemm_fc_relu2_fwd",
     "gemm_proj_fwd", "gemm_ce_fwd", "ce_reduce", "gemm_ce_dlogits", "gemm_ce_dh", "gemm_ce_dw",
     "rmsnorm_bwd", "gemm_proj_dgrad", "gemm_proj_wgrad", "gemm_fc_dgrad", "gemm_fc_wgrad",
     "gemm_o_dgrad", "gemm_o_wgrad", "attn_bwd_delta", "attn_bwd_dkdv", "attn_bwd_dq", "rope_qknorm_bwd", "gemm_qkv_dgrad", "gemm_qkv_wgrad",
-    "embed_bwd", "fill", "muon_elementwise", "ns_gram", "ns_poly", "ns_update", "fp8_quant", "adamw"};
+    "embed_bwd", "fill", "muon_elementwise", "ns_gram", "ns_poly", "ns_update", "fp8_quant", "adamw", "features"};
 
 struct Profiler {
   uint64_t mask = 0;
@@ -369,6 +400,8 @@ struct Layer {
   // (for the weight gradients) and the weights' codes, plain and transposed
   size_t h1t, attt, h2t, actt;
   size_t wqkv8, wqkv8t, wo8, wo8t, wfc8, wfc8t, wproj8, wproj8t;
+  // record-model features: bf16 stream before the residual scaling; value-embedding gates [N, Hkv]
+  size_t xin, vgate;
 };
 
 // per-layer fp8 scales (fmax / amax of the tensor)
@@ -383,6 +416,10 @@ struct WS {
   // fp8 precision only: codes of the current product input (forward) and of
   // the current output gradient, plain and transposed (backward); scales
   size_t xq, dyq, dyqt, scales, qpart;
+  // record-model features: smear sigmoids [N]; x0 and x_mid [N, d] fp32;
+  // backward: gradient reaching x0 (g0), the head's stream gradient (gfin),
+  // value-embedding gate gradients [N, Hkv], partial sums of the reductions
+  size_t sig, x0, xmid, g0, gfin, dzve, fpart;
   size_t total;
 };
 
@@ -431,6 +468,26 @@ WS ws_layout(const Dims& D) {
     mx = std::max(mx, wgrad_part_elems(dd, hd, Nt));
     mx = std::max(mx, wgrad_part_elems(vocab_chunk(D), dd, Nt));
     w.wpart = take(std::max<size_t>(mx, 1) * 4);
+  }
+  w.sig = w.x0 = w.xmid = w.g0 = w.gfin = w.dzve = w.fpart = 0;
+  for (int l = 0; l < D.L; ++l) w.layer[l].xin = w.layer[l].vgate = 0;
+  if (D.feat) {
+    const size_t Nd = N * d;
+    w.sig = take(N * 4);
+    w.fpart = take((size_t)feature_partial_floats(D.Hkv) * 4);
+    if (D.has(GPT_FEAT_RESID_LAMBDA)) {
+      w.x0 = take(Nd * 4);
+      w.g0 = take(Nd * 4);
+      for (int l = 0; l < D.L; ++l) w.layer[l].xin = take(Nd * 2);
+    }
+    if (D.has(GPT_FEAT_BACKOUT)) {
+      w.xmid = take(Nd * 4);
+      w.gfin = take(Nd * 4);
+    }
+    if (D.has(GPT_FEAT_VALUE_EMBED)) {
+      w.dzve = take(N * Hkv * 4);
+      for (int l = 0; l < D.L; l += 2) w.layer[l].vgate = take(N * Hkv * 4);
+    }
   }
   w.xq = w.dyq = w.dyqt = w.scales = w.qpart = 0;
   if (D.prec == GPT_PREC_FP8) {
@@ -638,7 +695,18 @@ extern "C" gpt_status gpt_step_fwd(const gpt_shape* shape, const gpt_params* par
     a.scale_a = sx; a.scale_b = sw;
     return gemm_fp8(a, epi, 0, 0, s);
   };
-  { ProfScope ps_(P_EMBED_FWD, s); TRY(launch_embed_fwd(ids, W + P.wte, x, D.B, D.T, d, s)); }
+  const bool f_resid = D.has(GPT_FEAT_RESID_LAMBDA), f_smear = D.has(GPT_FEAT_SMEAR);
+  const bool f_back = D.has(GPT_FEAT_BACKOUT);
+  float* x0 = f_resid ? at<float>(ws, w.x0) : nullptr;
+  float* xmid = f_back ? at<float>(ws, w.xmid) : nullptr;
+  {
+    ProfScope ps_(P_EMBED_FWD, s);
+    if (f_smear || f_resid)  // gather (+ smear with the previous token), x0 kept for the residual scalars
+      TRY(launch_smear_fwd(ids, W + P.wte, f_smear ? W + P.smear_w(D) : nullptr, f_smear ? W + P.smear_lam(D) : nullptr,
+                           x, x0, at<float>(ws, w.sig), D.B, D.T, d, s));
+    else
+      TRY(launch_embed_fwd(ids, W + P.wte, x, D.B, D.T, d, s));
+  }
   long long act_slots = 0;
   for (int l = 0; l < D.L; ++l) {
     const Layer& L = w.layer[l];
@@ -648,7 +716,14 @@ extern "C" gpt_status gpt_step_fwd(const gpt_shape* shape, const gpt_params* par
     uint16_t* att = at<uint16_t>(ws, L.att);
     uint16_t* h2 = at<uint16_t>(ws, L.h2);
     uint16_t* act = at<uint16_t>(ws, L.act);
-    { ProfScope ps_(P_RMSNORM_FWD, s); TRY(launch_rmsnorm_fwd(x, h1, at<float>(ws, L.r1), N, d, s, qpart)); }
+    {
+      ProfScope ps_(P_RMSNORM_FWD, s);
+      if (f_resid)  // x <- resid_l x + x0lam_l x0, then the norm
+        TRY(launch_mix_rmsnorm_fwd(x, x0, W + P.resid_l(l), W + P.x0lam(D, l), 1.f, at<uint16_t>(ws, L.xin), h1,
+                                   at<float>(ws, L.r1), N, d, qpart, s));
+      else
+        TRY(launch_rmsnorm_fwd(x, h1, at<float>(ws, L.r1), N, d, s, qpart));
+    }
     TRY(quant_x(h1, d, L.h1t, sc ? sc + SC_H1 : nullptr, N));
     {
       GemmArgs a;  // [q | k | v] = h1 [Wq; Wk; Wv]^T, q and k rotated and RMS-normalised per head
@@ -660,6 +735,11 @@ extern "C" gpt_status gpt_step_fwd(const gpt_shape* shape, const gpt_params* par
       a.part = at<float>(ws, L.rq); a.zt = at<float>(ws, L.rk);
       TRY(block_fwd(a, EPI_QKV, d, f8 ? at<uint8_t>(ws, L.wqkv8) : nullptr, sc ? sc + SC_H1 : nullptr,
                     sc ? sc + SC_WQKV : nullptr));
+    }
+    if (D.ve_layer(l)) {  // v += 3 sigmoid(h1[:32] Wg^T) VE[token] per key/value head
+      ProfScope ps_(P_FEATURES, s);
+      TRY(launch_ve_fwd(ids, h1, d, W + P.vg(D, l), W + P.ve(D, l), qkv + d + D.dkv, D.dqkv, at<float>(ws, L.vgate),
+                        D.B, D.T, D.Hkv, s));
     }
     { ProfScope ps_(P_ATTN_FWD, s); TRY(launch_attn_fwd(qkv, qkv + d, qkv + d + D.dkv, D.dqkv, att, d, at<float>(ws, L.lse), D.B, D.H, D.Hkv, D.T, D.layer_window(l), s)); }
     TRY(quant_x(att, d, L.attt, sc ? sc + SC_ATT : nullptr, 0));
@@ -695,9 +775,24 @@ extern "C" gpt_status gpt_step_fwd(const gpt_shape* shape, const gpt_params* par
       TRY(block_fwd(a, EPI_RESID, hid, f8 ? at<uint8_t>(ws, L.wproj8) : nullptr,
                     sc ? sc + SC_ACT : nullptr, sc ? sc + SC_WPROJ : nullptr));
     }
+    if (f_back && l == D.L / 2 - 1) {  // the middle stream, for backout
+      ProfScope ps_(P_FEATURES, s);
+      auto copy = [&]() -> int {
+        GS_HIP_CHECK(hipMemcpyAsync(xmid, x, (size_t)N * d * 4, hipMemcpyDeviceToDevice, s));
+        return 0;
+      };
+      TRY(copy());
+    }
   }
   uint16_t* hf = at<uint16_t>(ws, w.hf);
-  { ProfScope ps_(P_RMSNORM_FWD, s); TRY(launch_rmsnorm_fwd(x, hf, at<float>(ws, w.rf), N, d, s)); }
+  {
+    ProfScope ps_(P_RMSNORM_FWD, s);
+    if (f_back)  // x <- x - backout x_mid, then the final norm
+      TRY(launch_mix_rmsnorm_fwd(x, xmid, nullptr, W + P.backout(D), -1.f, nullptr, hf, at<float>(ws, w.rf), N, d,
+                                 nullptr, s));
+    else
+      TRY(launch_rmsnorm_fwd(x, hf, at<float>(ws, w.rf), N, d, s));
+  }
   {
     GemmArgs a;  // per-tile (max, sum exp) of the logits hf W_lm^T, never stored
     ProfScope ps_(P_CE_FWD, s);
@@ -754,6 +849,18 @@ extern "C" gpt_status gpt_step_bwd_scaled(const gpt_shape* shape, const gpt_para
   uint16_t* dz = at<uint16_t>(ws, w.dz);
   float* wpart = at<float>(ws, w.wpart);
   const float* cs = at<float>(ws, w.cs);
+  const bool f_resid = D.has(GPT_FEAT_RESID_LAMBDA), f_smear = D.has(GPT_FEAT_SMEAR);
+  const bool f_back = D.has(GPT_FEAT_BACKOUT);
+  const long long Nd = (long long)N * d;
+  float* fpart = D.feat ? at<float>(ws, w.fpart) : nullptr;
+  float* g0 = f_resid ? at<float>(ws, w.g0) : nullptr;
+  float* gfin = f_back ? at<float>(ws, w.gfin) : nullptr;
+  float* dzve = D.has(GPT_FEAT_VALUE_EMBED) ? at<float>(ws, w.dzve) : nullptr;
+  if (D.feat && !acc) {
+    // value-embedding tables take atomics; a cleared feature bit leaves its gradients at 0
+    ProfScope ps_(P_FILL, s);
+    TRY(launch_fill_f32(G + P.lm_end, (long long)(P.total - P.lm_end), 0.f, s));
+  }
 
   // fused head + cross-entropy backward, one vocabulary chunk at a time
   const int vc = vocab_chunk(D);
@@ -784,6 +891,12 @@ extern "C" gpt_status gpt_step_bwd_scaled(const gpt_shape* shape, const gpt_para
   const bool f8 = D.prec == GPT_PREC_FP8;
   float* qpart = f8 ? at<float>(ws, w.qpart) : nullptr;
   { ProfScope ps_(P_RMSNORM_BWD, s); TRY(launch_rmsnorm_bwd(dh, hf, at<float>(ws, w.rf), g, g_bf, N, d, s, qpart)); }
+  if (f_back) {  // x_final = x_L - backout x_mid: d backout = -g . x_mid; g is kept for the middle layer
+    ProfScope ps_(P_FEATURES, s);
+    TRY(launch_backout_bwd(g, at<float>(ws, w.xmid), gfin, Nd, fpart, G + P.backout(D), acc, s));
+  }
+  // the per-row amax partials of g_bf (fp8) are valid only right after a norm backward wrote them
+  bool g_amax_ok = true;
 
   uint8_t* dyq = f8 ? at<uint8_t>(ws, w.dyq) : nullptr;
   uint8_t* dyqt = f8 ? at<uint8_t>(ws, w.dyqt) : nullptr;
@@ -813,8 +926,13 @@ extern "C" gpt_status gpt_step_bwd_scaled(const gpt_shape* shape, const gpt_para
     const uint16_t* att = at<uint16_t>(ws, L.att);
     const uint16_t* h2 = at<uint16_t>(ws, L.h2);
     const uint16_t* act = at<uint16_t>(ws, L.act);
+    if (f_back && l == D.L / 2 - 1) {  // the middle stream's share of the backout term
+      ProfScope ps_(P_FEATURES, s);
+      TRY(launch_axpy_stream(g, g_bf, gfin, W + P.backout(D), -1.f, Nd, s));
+      g_amax_ok = false;
+    }
     // ---- MLP ----
-    if (f8) TRY(quant_dy(g_bf, d, sc + SC_G_MLP, N));
+    if (f8) TRY(quant_dy(g_bf, d, sc + SC_G_MLP, g_amax_ok ? N : 0));
     {
       GemmArgs a;  // du = (g Wproj) * 2 relu(u)  with relu(u) = sqrt(act)
       ProfScope ps_(P_PROJ_DGRAD, s);
@@ -870,6 +988,11 @@ extern "C" gpt_status gpt_step_bwd_scaled(const gpt_shape* shape, const gpt_para
                                D.T, D.layer_window(l), s));
     }
     { ProfScope ps_(P_ROPE_BWD, s); TRY(launch_rope_qknorm_bwd(dq_acc, dqkv, qkv, at<float>(ws, L.rq), at<float>(ws, L.rk), cs, N, D.T, D.H, D.Hkv, s)); }
+    if (D.ve_layer(l)) {  // value embedding: dVE[token] += gate dv; gate-logit gradients dz
+      ProfScope ps_(P_FEATURES, s);
+      TRY(launch_ve_bwd(ids, dqkv + d + D.dkv, D.dqkv, W + P.ve(D, l), at<float>(ws, L.vgate), G + P.ve(D, l), dzve,
+                        D.B, D.T, D.Hkv, s));
+    }
     if (f8) TRY(quant_dy(dqkv, D.dqkv, sc + SC_DQKV, 0));
     {
       GemmArgs a;  // dh = dqkv [Wq; Wk; Wv]
@@ -885,10 +1008,31 @@ extern "C" gpt_status gpt_step_bwd_scaled(const gpt_shape* shape, const gpt_para
       if (f8) TRY(wgrad_fp8(dyqt, at<uint8_t>(ws, L.h1t), sc + SC_DQKV, sc + SC_H1, G + P.qkv(D, l), D.dqkv, d, N, acc, wpart, s));
       else TRY(wgrad(dqkv, D.dqkv, h1, d, G + P.qkv(D, l), D.dqkv, d, N, acc, wpart, s));
     }
+    if (D.ve_layer(l)) {  // the gate reads h1[:, :32]: dh[:, :32] += dz Wg; dWg = dz^T h1[:, :32]
+      ProfScope ps_(P_FEATURES, s);
+      TRY(launch_ve_dh(dzve, W + P.vg(D, l), dh, d, N, D.Hkv, s));
+      TRY(launch_ve_gate_grad(dzve, h1, d, N, D.Hkv, fpart, G + P.vg(D, l), acc, s));
+    }
     { ProfScope ps_(P_RMSNORM_BWD, s); TRY(launch_rmsnorm_bwd(dh, h1, at<float>(ws, L.r1), g, g_bf, N, d, s, qpart)); }
+    g_amax_ok = true;
+    if (f_resid) {  // x' = resid_l x_in + x0lam_l x0
+      ProfScope ps_(P_FEATURES, s);
+      TRY(launch_resid_bwd(g, g_bf, at<uint16_t>(ws, L.xin), at<float>(ws, w.x0), g0, l == D.L - 1,
+                           W + P.resid_l(l), W + P.x0lam(D, l), Nd, fpart, G + P.resid_l(l), G + P.x0lam(D, l), acc,
+                           s));
+      g_amax_ok = false;
+    }
   }
   if (!acc) { ProfScope ps_(P_FILL, s); TRY(launch_fill_f32(G + P.wte, (long long)D.V * d, 0.f, s)); }
-  { ProfScope ps_(P_EMBED_BWD, s); TRY(launch_embed_bwd(ids, g, G + P.wte, D.B, D.T, d, s)); }
+  const float* gemb = g;
+  if (f_smear || f_resid) {  // gradient of the embeddings: g + g0 through the smear backward (into dh)
+    ProfScope ps_(P_FEATURES, s);
+    TRY(launch_smear_bwd(ids, W + P.wte, f_smear ? W + P.smear_w(D) : nullptr, f_smear ? W + P.smear_lam(D) : nullptr,
+                         g, g0, at<float>(ws, w.sig), dh, fpart, G + P.smear_lam(D), G + P.smear_w(D), acc, D.B, D.T,
+                         d, s));
+    gemb = dh;
+  }
+  { ProfScope ps_(P_EMBED_BWD, s); TRY(launch_embed_bwd(ids, gemb, G + P.wte, D.B, D.T, d, s)); }
   return GPT_OK;
 }
 

@@ -52,6 +52,42 @@ long long normuon_part_floats(int count, int rows, int cols);
 int launch_adamw(float* W, uint16_t* Wb, const float* G, float* M, float* V, long long n, float lr, float b1,
                  float b2, float eps, float wd, float inv_bc1, float inv_bc2, float gs, hipStream_t s);
 
+// --- record-model features (features.hip) ----------------------------------
+// scalars (pa, pb, pc, slam) and small weights are device bf16 values
+// scratch floats of the partial-sum reductions below
+long long feature_partial_floats(int Hkv);
+// x = e_t + lam sigmoid(e_t[:24] . sw) e_{t-1} (token 0: e_0); x0 (nullable) = copy; sig = the sigmoids
+int launch_smear_fwd(const int* ids, const uint16_t* wte, const uint16_t* sw, const uint16_t* slam, float* x,
+                     float* x0, float* sig, int B, int T, int d, hipStream_t s);
+// de = backward of smear for dX = g (+ g0); d lam and d sw written (or added) to dlam / dw
+int launch_smear_bwd(const int* ids, const uint16_t* wte, const uint16_t* sw, const uint16_t* slam, const float* g,
+                     const float* g0, const float* sig, float* de, float* part, float* dlam, float* dw,
+                     bool accumulate, int B, int T, int d, hipStream_t s);
+// x <- a x + bsign b y (a = 1 when pa is NULL); xin (nullable) = bf16(old x); h, r = RMSNorm of new x
+int launch_mix_rmsnorm_fwd(float* x, const float* y, const uint16_t* pa, const uint16_t* pb, float bsign,
+                           uint16_t* xin, uint16_t* h, float* r, long long N, int d, float* amax_part, hipStream_t s);
+// v[:, head] += 3 sigmoid(h1[:32] . wg[head]) ve[id][head]; gate [N, Hkv] saved
+int launch_ve_fwd(const int* ids, const uint16_t* h1, int d, const uint16_t* wg, const uint16_t* ve, uint16_t* v,
+                  long long ldv, float* gate, int B, int T, int Hkv, hipStream_t s);
+// dve[id] += gate dv (atomics); dz = (dv . ve) gate (1 - gate / 3)
+int launch_ve_bwd(const int* ids, const uint16_t* dv, long long lddv, const uint16_t* ve, const float* gate,
+                  float* dve, float* dz, int B, int T, int Hkv, hipStream_t s);
+// dwg (+)= dz^T h1[:, :32]
+int launch_ve_gate_grad(const float* dz, const uint16_t* h1, int d, long long N, int Hkv, float* part, float* dwg,
+                        bool accumulate, hipStream_t s);
+// dh[:, :32] += dz wg
+int launch_ve_dh(const float* dz, const uint16_t* wg, float* dh, int d, long long N, int Hkv, hipStream_t s);
+// backward of x' = a x_in + b x0: da, db (+)= g.x_in, g.x0; g0 (first: =) += b g; g = a g; g_bf
+int launch_resid_bwd(float* g, uint16_t* g_bf, const uint16_t* xin, const float* x0, float* g0, bool g0_first,
+                     const uint16_t* pa, const uint16_t* pb, long long n, float* part, float* da, float* db,
+                     bool accumulate, hipStream_t s);
+// backout at the head: dlam (+)= -g . x_mid; gcopy = g
+int launch_backout_bwd(const float* g, const float* xm, float* gcopy, long long n, float* part, float* dlam,
+                       bool accumulate, hipStream_t s);
+// g += csign c y; g_bf = bf16(g)
+int launch_axpy_stream(float* g, uint16_t* g_bf, const float* y, const uint16_t* pc, float csign, long long n,
+                       hipStream_t s);
+
 // --- attention (attention.hip) ---------------------------------------------
 // H query heads, Hkv key/value heads (query head h reads head h / (H / Hkv));
 // window: left window (query i sees keys i - window .. i), -1 = full causal

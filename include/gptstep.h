@@ -80,6 +80,31 @@ typedef enum {
  *   pattern_long    bit i set = pattern position i is 'L' (full causal),
  *                   clear = 'S' (windowed); layer l takes position l % len.
  *                   "SSSL" is pattern_len 4, pattern_long 0x8. */
+/* Record-model features (the same model section: value embeddings in the
+ * ResFormer style; the efficiency tricks per-layer residual scaling, smear and
+ * backout), bits of gpt_shape.features:
+ *   GPT_FEAT_VALUE_EMBED  layers 0, 2, 4, ... add to v, per key/value head,
+ *                         gate * VE_l[token] with gate = 3 sigmoid(h[:32] .
+ *                         Wg_l[head]), h the attention input (normed stream)
+ *   GPT_FEAT_SMEAR        token t >= 1 adds lam sigmoid(e_t[:24] . w) e_{t-1}
+ *                         to its embedding e_t (within its sequence)
+ *   GPT_FEAT_RESID_LAMBDA layer l starts with x <- resid_l x + x0lam_l x0, x0
+ *                         the stream after the embedding (and smear)
+ *   GPT_FEAT_BACKOUT      before the final norm x <- x - backout x_mid, x_mid
+ *                         the stream after layer depth/2 - 1
+ * With features != 0 the packed parameters gain, after lm_head: VE_l [V, dkv]
+ * for l = 0, 2, ..; Wg_l [n_kv_head, 32] for the same l; then the scalar block
+ * resid [depth], x0lam [depth], w [24], lam [1], backout [1], 6 unused.
+ * Every one of them is present when any bit is set (a cleared bit leaves its
+ * parameters unused, gradient 0).  Scalars are read on the device from the
+ * bf16 copy, like every other parameter. */
+enum {
+  GPT_FEAT_VALUE_EMBED = 1,
+  GPT_FEAT_SMEAR = 2,
+  GPT_FEAT_RESID_LAMBDA = 4,
+  GPT_FEAT_BACKOUT = 8
+};
+
 typedef struct {
   int32_t depth;
   int32_t vocab;
@@ -90,6 +115,7 @@ typedef struct {
   int32_t window;
   int32_t pattern_len;
   uint32_t pattern_long;
+  uint32_t features; /* GPT_FEAT_* bits; 0 = the plain model */
 } gpt_shape;
 
 /* Packed parameter buffers, all with gpt_param_count() elements in the packed
@@ -109,7 +135,10 @@ typedef struct {
 gpt_status gpt_param_count(const gpt_shape* shape, size_t* n_params /* host */);
 
 /* Element offsets of the 2 + 6*depth tensors in packed order (wte, then per
- * layer wq wk wv wo, then each wfc, then each wproj, then lm_head).
+ * layer wq wk wv wo, then each wfc, then each wproj, then lm_head), followed
+ * when gpt_shape.features != 0 by the depth/2 value-embedding tables, the
+ * depth/2 gate matrices and the scalar block (resid, x0lam, w, lam, backout,
+ * unused): 2 + 6*depth + depth + 6 tensors in all.
  * `offsets` (host) must hold `capacity` entries; *n_tensors (host) receives
  * the count.  GPT_ERR_INVALID_ARG when capacity is too small. */
 gpt_status gpt_param_layout(const gpt_shape* shape, size_t* offsets, int32_t capacity,
@@ -209,7 +238,7 @@ const char* gpt_status_string(gpt_status status);
 const char* gpt_last_error(void);
 
 /* Library ABI version (bumped on any signature change; 2: gpt_shape carries
- * the attention variants). */
+ * the attention variants; 3: gpt_shape.features). */
 int32_t gpt_abi_version(void);
 
 #ifdef __cplusplus

@@ -384,11 +384,17 @@ def _forward_backward_chunk(P, ids, cfg, loss_scale, dtype, want_grads, want_log
     Gr["lm_head"] = dz.T @ hfo
     g = rms_norm_bwd(dz @ P["lm_head"], hf, rf)
     del dz
+    # the scalar gradients are sums over every stream element whose terms cancel
+    # to a small fraction of their magnitudes; Gabs holds the sum of the
+    # terms' absolute values (the scale that bounds a sum's rounding error)
+    Gabs = {}
     if cfg.has_features:
         for n in ("resid_lambda", "x0_lambda", "smear_w", "smear_lambda", "backout_lambda"):
             Gr[n] = np.zeros(P[n].shape, dtype=dtype)
+            Gabs[n] = np.zeros(P[n].shape, dtype=dtype)
     if cfg.backout:
         Gr["backout_lambda"][0] = -np.sum(g * x_mid)
+        Gabs["backout_lambda"][0] = np.sum(np.abs(g * x_mid))
         g_mid = -P["backout_lambda"][0] * g
     g0 = np.zeros_like(g) if cfg.resid_lambdas else None   # gradient reaching x0 through the lambdas
     for i in reversed(range(L)):
@@ -432,6 +438,8 @@ def _forward_backward_chunk(P, ids, cfg, loss_scale, dtype, want_grads, want_log
             # x = resid_lambda x_in + x0_lambda x0
             Gr["resid_lambda"][i] = np.sum(g * x_in)
             Gr["x0_lambda"][i] = np.sum(g * x0)
+            Gabs["resid_lambda"][i] = np.sum(np.abs(g * x_in))
+            Gabs["x0_lambda"][i] = np.sum(np.abs(g * x0))
             g0 += P["x0_lambda"][i] * g
             g = P["resid_lambda"][i] * g
         caches[i] = None
@@ -445,8 +453,12 @@ def _forward_backward_chunk(P, ids, cfg, loss_scale, dtype, want_grads, want_log
         dgate = np.sum(dX * prev, axis=-1)
         dgate[:, 0] = 0.0
         Gr["smear_lambda"][0] = np.sum(dgate * s_sig)
+        Gabs["smear_lambda"][0] = np.sum(np.abs(dX * prev) * s_sig[..., None])
         dzs = dgate * P["smear_lambda"][0] * s_sig * (1.0 - s_sig)
         Gr["smear_w"] = np.einsum("bt,btc->c", dzs, e3[..., :SMEAR_CH])
+        # dz_t itself is a sum over the channels of dX_t e_{t-1}
+        dzs_abs = np.sum(np.abs(dX * prev), axis=-1) * abs(P["smear_lambda"][0]) * s_sig * (1.0 - s_sig)
+        Gabs["smear_w"] = np.einsum("bt,btc->c", dzs_abs, np.abs(e3[..., :SMEAR_CH]))
         de[..., :SMEAR_CH] += dzs[..., None] * P["smear_w"]
         g = de.reshape(R, d)
     dwte = np.zeros(P["wte"].shape, dtype=dtype)
@@ -457,6 +469,7 @@ def _forward_backward_chunk(P, ids, cfg, loss_scale, dtype, want_grads, want_log
             Gr[f"ve.{i}"] = np.zeros(P[f"ve.{i}"].shape, dtype=dtype)
             Gr[f"ve_gate.{i}"] = np.zeros(P[f"ve_gate.{i}"].shape, dtype=dtype)
     out["grads"] = Gr
+    out["grad_abs"] = Gabs
     return out
 
 
@@ -483,7 +496,12 @@ def forward_backward(P, ids, cfg, dtype=np.float64, want_grads=True, want_logits
     rounded to bf16 (nearest even); products accumulate in `dtype`; norms,
     rotary, softmax and the residual stream stay in `dtype`.  With False
     (default) nothing is rounded and the result is the exact function of the
-    bf16 weights."""
+    bf16 weights.
+
+    ``grad_abs`` (with the record-model features): for each scalar parameter's
+    gradient, a sum over every stream element, the sum of its terms' absolute
+    values.  Those sums cancel to 1e-2 .. 1e-4 of that scale, so it, not the
+    gradient's own size, bounds the gradient's rounding error."""
     ids = np.asarray(ids)
     B, T1 = ids.shape
     T = T1 - 1
@@ -502,7 +520,7 @@ def forward_backward(P, ids, cfg, dtype=np.float64, want_grads=True, want_logits
         if fp8:
             raise ValueError("fp8 per-tensor scales need the whole batch at once")
         chunks = [(s, min(B, s + seq_chunk)) for s in range(0, B, seq_chunk)]
-    total, grads, row_loss, lse, logits = 0.0, None, [], [], []
+    total, grads, gabs, row_loss, lse, logits = 0.0, None, None, [], [], []
     for s, e in chunks:
         o = _forward_backward_chunk(P, ids[s:e], cfg, loss_scale, dtype, want_grads,
                                     want_logits, fp8, cos, sin, op)
@@ -513,15 +531,18 @@ def forward_backward(P, ids, cfg, dtype=np.float64, want_grads=True, want_logits
             logits.append(o["logits"])
         if want_grads:
             if grads is None:
-                grads = o["grads"]
+                grads, gabs = o["grads"], o["grad_abs"]
             else:
                 for k in grads:
                     grads[k] += o["grads"][k]
+                for k in gabs:
+                    gabs[k] += o["grad_abs"][k]
     out = {"loss": total / (B * T), "row_loss": np.concatenate(row_loss),
            "lse": np.concatenate(lse)}
     if want_logits:
         out["logits"] = np.concatenate(logits)
     if want_grads:
         out["grads"] = grads
+        out["grad_abs"] = gabs
     return out
 

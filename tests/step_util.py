@@ -13,14 +13,14 @@ class StepRun:
     """Device buffers of one configuration, filled from the seeded generators."""
 
     def __init__(self, depth, vocab, seq_len, batch, seed_ids=inputs.SEED_IDS, seed_w=inputs.SEED_W,
-                 precision_flag=0, n_kv_head=0, window=0, pattern=""):
+                 precision_flag=0, n_kv_head=0, window=0, pattern="", features=""):
         from gpt_transformer_step_amd import binding as B
         self.B = B
-        self.dims = inputs.Dims.from_depth(depth, vocab, n_kv_head)
+        self.dims = inputs.Dims.from_depth(depth, vocab, n_kv_head, features=features)
         self.depth, self.vocab, self.T, self.batch = depth, vocab, seq_len, batch
-        self.n_kv_head, self.window, self.pattern = n_kv_head, window, pattern
+        self.n_kv_head, self.window, self.pattern, self.features = n_kv_head, window, pattern, features
         self.shape = B.shape(depth, vocab, seq_len, batch, precision_flag, n_kv_head=n_kv_head, window=window,
-                             pattern=pattern)
+                             pattern=pattern, features=features)
         self.n = B.param_count(self.shape)
         assert self.n == inputs.n_params(self.dims)
         self.master_np = inputs.master_weights(self.dims, seed_w)
@@ -57,7 +57,8 @@ class StepRun:
         return {k: v.astype(np.float64) for k, v in inputs.unpack(self.dims, vals).items()}
 
     def oracle_cfg(self):
-        return om.Config.from_depth(self.depth, self.vocab, self.n_kv_head, self.window, self.pattern or "L")
+        return om.Config.from_depth(self.depth, self.vocab, self.n_kv_head, self.window, self.pattern or "L",
+                                    self.features)
 
 
 def oracle_run(run, want_logits=False, dtype=np.float64, seq_chunk=None, fp8=False, bf16_operands=False):

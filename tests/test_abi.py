@@ -43,7 +43,7 @@ def test_every_declared_symbol_is_exported(B):
 
 def test_abi_version_and_status_strings(B):
     lib = B.lib()
-    assert lib.gpt_abi_version() == 2
+    assert lib.gpt_abi_version() == 3
     for code, text in [(0, b"ok"), (-1, b"invalid argument"), (-2, b"invalid shape"),
                        (-3, b"workspace too small"), (-4, b"HIP runtime error"), (-5, b"unsupported")]:
         assert lib.gpt_status_string(code) == text
@@ -77,6 +77,32 @@ def test_param_count_and_layout(B):
         assert offs == expect
     # depth 20: 477.10 M parameters (block matrices 393.22 M + two 41.94 M tables)
     assert B.param_count(B.shape(20, 32768, 2048, 32)) == 477_102_080
+
+
+@pytest.mark.parametrize("depth,kv,features", [(4, 0, "vsrb"), (6, 1, "v"), (20, 5, "sr"), (2, 0, "b")])
+def test_param_layout_with_features(B, depth, kv, features):
+    """The library's packed order with the record-model tensors equals the
+    input generator's (value-embedding tables, gates, then the scalar block)."""
+    import numpy as np
+    from gpt_transformer_step_amd import inputs
+    sh = B.shape(depth, 1000, 64, 2, n_kv_head=kv, features=features)
+    dims = inputs.Dims.from_depth(depth, 1000, kv, features=features)
+    assert B.param_count(sh) == inputs.n_params(dims)
+    offs = B.param_layout(sh)
+    expect, o = [], 0
+    for _, shp in inputs.packed_tensors(dims):
+        expect.append(o)
+        o += int(np.prod(shp))
+    assert offs == expect
+    assert len(offs) == 2 + 7 * depth + 6
+
+
+def test_unknown_feature_bits_rejected(B):
+    sh = B.shape(2, 100, 8, 1)
+    sh.features = 16
+    with pytest.raises(B.GptError) as e:
+        B.param_count(sh)
+    assert e.value.code == -2
 
 
 def test_workspace_queries(B):

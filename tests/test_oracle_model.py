@@ -550,3 +550,20 @@ def test_first_layer_lambdas_have_equal_gradients():
     P2 = {k: v.copy() for k, v in P.items()}
     P2["resid_lambda"][0], P2["x0_lambda"][0] = P["x0_lambda"][0], P["resid_lambda"][0]
     assert om.forward_backward(P2, ids, cfg, want_grads=False)["loss"] == pytest.approx(out["loss"], rel=1e-14)
+
+
+def test_grad_abs_bounds_the_scalar_gradients():
+    """grad_abs is the sum of the absolute values of the terms of each scalar
+    gradient: never below the gradient's magnitude (triangle inequality), and
+    additive over sequence chunks."""
+    cfg = TINY_FEAT
+    P = _feat_params(cfg, seed=99)
+    ids = _tiny_ids(cfg, B=2, T=9, seed=100)
+    out = om.forward_backward(P, ids, cfg)
+    for name, a in out["grad_abs"].items():
+        assert np.all(a >= np.abs(out["grads"][name]) * (1 - 1e-12)), name
+        assert np.all(np.isfinite(a)), name
+    # chunked processing adds the per-chunk sums
+    chunked = om.forward_backward(P, ids, cfg, seq_chunk=1)
+    for name, a in out["grad_abs"].items():
+        assert np.allclose(chunked["grad_abs"][name], a, rtol=1e-12), name
