@@ -27,9 +27,9 @@
 //   only when a row max exceeds it by 2^8 (P <= 256), so most tiles skip the
 //   O rescale.  K/V tiles of 64 keys, double buffered.
 // Backward, two kernels and no atomics:
-//   * dK/dV: one workgroup = 128 keys (4 waves x 32) over query tiles of 32:
-//     S = Q K^T, dP = dO V^T, P = exp(S - lse), dS = P (dP - delta),
-//     dV^T += dO^T P, dK^T += Q^T dS;
+//   * dK/dV: one workgroup = 256 keys (8 waves x 32) over query tiles of 32
+//     streamed through a 4-stage LDS ring: S = Q K^T, dP = dO V^T,
+//     P = exp(S - lse), dS = P (dP - delta), dV^T += dO^T P, dK^T += Q^T dS;
 //   * dQ: one workgroup = 128 queries over key tiles of 64, shaped like the
 //     forward: S^T, dP^T recomputed, dQ^T += K^T dS^T.
 //   The dQ kernel recomputes two of the four products; in exchange dQ needs no
@@ -287,27 +287,108 @@ __global__ void __launch_bounds__(256) attn_bwd_pre_kernel(const uint16_t* __res
 // ---------------------------------------------------------------------------
 // dK, dV
 // ---------------------------------------------------------------------------
-constexpr int KV_KEYS = 128;
-constexpr int KV_Q = 32;
-constexpr int KV_SK = 0;                          // K of the block [128][256 B]
-constexpr int KV_STAGE0 = KV_SK + KV_KEYS * 256;  // two stages of:
-constexpr int KV_QN = 0;                          //   Q tile  [32][256 B]
-constexpr int KV_DN = KV_QN + KV_Q * 256;         //   dO tile [32][256 B]
-constexpr int KV_LSE = KV_DN + KV_Q * 256;        //   lse * log2e [32], then delta [32]
-constexpr int KV_STAGE = KV_LSE + 2 * KV_Q * 4;
-constexpr int KV_TOTAL = KV_STAGE0 + 2 * KV_STAGE;
+constexpr int KV_Q = 32;  // queries per tile
+
+// ---------------------------------------------------------------------------
+// One workgroup = 256 keys (8 waves x 32)
+// of one (batch, key/value head); Q / dO tiles of 32 queries and their
+// softmax statistics stream through a ring of K8_NS LDS stages filled by
+// direct buffer -> LDS loads issued K8_NS - 1 tiles ahead, so the load
+// latency (a few microseconds under load) is covered by several tiles of
+// MFMAs.  The barrier at the end of a tile waits only for the next tile's
+// loads (vmcnt), not for the ones in flight behind it.  Buffer loads take a
+// scalar base and one 32-bit offset per thread, which keeps the streaming
+// loads' addresses out of the (fully used) vector register budget.
+// ---------------------------------------------------------------------------
+constexpr int K8_KEYS = 256;
+constexpr int K8_NT = 512;
+// LDS: K of the block [256][256 B] and K8_NS ring stages, each its own
+// __shared__ array of Q [32][256 B], dO [32][256 B], lse [32] and delta [32].
+// Separate arrays carry separate alias scopes, so the compiler can tell that
+// an LDS read of one stage does not depend on the direct loads in flight into
+// another (with a single array it waits for all of them before every read).
+// The loop is unrolled by K8_NS so that each copy names its stages statically.
+constexpr int K8_NS = 4;
+constexpr int K8_QN = 0, K8_DN = KV_Q * 256, K8_ST = 2 * KV_Q * 256;
+constexpr int K8_STAGE = K8_ST + 2 * KV_Q * 4;
+constexpr int K8_TOTAL = K8_KEYS * 256 + K8_NS * K8_STAGE;
+constexpr int K8_LOADS = 3;                         // direct loads per thread per query tile
+// s_waitcnt immediate (gfx9 encoding): vmcnt = loads of the K8_NS - 2 tiles
+// issued after the next one; expcnt and lgkmcnt not waited for
+constexpr int K8_VMCNT = K8_LOADS * (K8_NS - 2);
+constexpr int K8_WAIT = (K8_VMCNT & 15) | ((K8_VMCNT >> 4) << 14) | (7 << 4) | (15 << 8);
+static_assert(K8_TOTAL <= 160 * 1024, "LDS budget");
+static_assert(K8_VMCNT < 64, "vmcnt range");
+
+// ROWS rows of 128 features from row r0 (clamped to T - 1) into a swizzled
+// tile, K8_NT threads: round i, wave w, lane l fills 16-byte slot 512 i + 64 w + l
+// Buffer resource (raw byte addressing, range num_bytes; gfx9 layout: base,
+// base_hi | stride 0, num_records, format word) from wave-uniform values.
+typedef int v4i_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ v4i_t buf_rsrc(const void* base, long long num_bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  v4i_t r;
+  r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+  r[1] = __builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32));
+  r[2] = __builtin_amdgcn_readfirstlane((int)min(num_bytes, (long long)0x7fffffff));
+  r[3] = 0x00020000;
+  return r;
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(size_t)(const __attribute__((address_space(3))) char*)p;
+}
+
+// Direct buffer -> LDS loads of this kernel, written as instructions the
+// compiler does not model: it would otherwise make every LDS read wait for
+// every such load in flight (it cannot tell the ring's stages apart), which
+// defeats loading several tiles ahead.  Ordering is the kernel's own: the
+// loads into a stage are issued after the barrier that ends its last reads,
+// and the barrier before its next reads follows an explicit vmcnt wait.
+// They have no register results; "memory" keeps the compiler from moving LDS
+// accesses across them.  M0 (the LDS base of the wave's write) is set here
+// only; nothing compiled in this kernel reads M0.
+__device__ __forceinline__ void dma16(v4i_t rsrc, int voffset, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %0, 0 offen lds"
+               :: "s"(rsrc), "v"(voffset), "s"(lds_base) : "memory");
+}
+__device__ __forceinline__ void dma4(v4i_t rsrc, int voffset, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dword %1, %0, 0 offen lds"
+               :: "s"(rsrc), "v"(voffset), "s"(lds_base) : "memory");
+}
+
+// ROWS rows of 128 features (row r0 + r clamped to T - 1) of a bf16 matrix
+// whose row 0 is byte 0 of rsrc, into a swizzled tile, K8_NT threads: round
+// i, wave w, lane l fills 16-byte slot 512 i + 64 w + l.  Offsets
+// (row * ld + chunk) * 2 fit 32 bits (T <= 16384, ld < 2^16).
+template <int ROWS>
+__device__ __forceinline__ void tile_dma8(v4i_t rsrc, int ld, int r0, int T, char* lds, int tid) {
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+#pragma unroll
+  for (int i = 0; i < ROWS * 16 / K8_NT; ++i) {
+    const int slot = tid + K8_NT * i;
+    const int r = slot >> 4, c = (slot & 15) ^ sigma(r);
+    const int row = min(r0 + r, T - 1);
+    dma16(rsrc, (row * ld + c * 8) * 2, lds_addr(lds + (K8_NT * i + 64 * wave) * 16));
+  }
+}
 
 template <bool GEN>
-__global__ void __launch_bounds__(256, 2)
-attn_bwd_kv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
-                   long long ld, const uint16_t* __restrict__ dout, long long ld_out, const float* __restrict__ lse,
-                   const float* __restrict__ delta, uint16_t* __restrict__ dk, uint16_t* __restrict__ dv,
-                   long long ld_dkv, int H, int Hkv, int T, int window_arg) {
-  __shared__ __attribute__((aligned(16))) char smem[KV_TOTAL];
+__global__ void __launch_bounds__(K8_NT, 1)
+attn_bwd_kv8_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+                    long long ld, const uint16_t* __restrict__ dout, long long ld_out, const float* __restrict__ lse,
+                    const float* __restrict__ delta, uint16_t* __restrict__ dk, uint16_t* __restrict__ dv,
+                    long long ld_dkv, int H, int Hkv, int T, int window_arg) {
+  static_assert(K8_NS == 4, "one __shared__ array per stage below");
+  __shared__ __attribute__((aligned(16))) char s_k[K8_KEYS * 256];
+  __shared__ __attribute__((aligned(16))) char s_st0[K8_STAGE];
+  __shared__ __attribute__((aligned(16))) char s_st1[K8_STAGE];
+  __shared__ __attribute__((aligned(16))) char s_st2[K8_STAGE];
+  __shared__ __attribute__((aligned(16))) char s_st3[K8_STAGE];
+  auto stage = [&](int j) -> char* { return j == 0 ? s_st0 : j == 1 ? s_st1 : j == 2 ? s_st2 : s_st3; };
   const int window = GEN ? window_arg : -1;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, lr = lane & 31, lh = lane >> 5;
   const int kb = blockIdx.x;
-  // one key/value head; its G query heads are processed one after the other
   const int bhk = blockIdx.y, b = bhk / Hkv, hk = bhk % Hkv;
   const int G = GEN ? H / Hkv : 1;
   const long long rowbase = (long long)b * T;
@@ -315,21 +396,9 @@ attn_bwd_kv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
   const uint16_t* vh = v + rowbase * ld + hk * 128;
   const float c = kScale * kLog2e;
 
-  const int k0 = kb * KV_KEYS;
+  const int k0 = kb * K8_KEYS;
   const int wk0 = k0 + wave * 32;
   const int mykey = wk0 + lr;
-
-  // V fragments of the wave's keys (B operand of dP = dO V^T: column = key)
-  bf16x8_t fv[8];
-  {
-    const int vrow = min(mykey, T - 1);
-#pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
-      const uint4 a = ld16(vh + (long long)vrow * ld + ks * 16 + lh * 8);
-      fv[ks] = *reinterpret_cast<const bf16x8_t*>(&a);
-    }
-  }
-  tile_load<KV_KEYS>(kh, ld, k0, T, smem + KV_SK, tid);
 
   f32x16_t dvt[4], dkt[4];
 #pragma unroll
@@ -339,91 +408,124 @@ attn_bwd_kv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
 
   const int nqt = (T + KV_Q - 1) / KV_Q;
   const int qt_first = k0 / KV_Q;
-  // last query tile that sees a key of the block (+1)
-  const int qt_end = window >= 0 ? min(nqt, (k0 + KV_KEYS - 1 + window) / KV_Q + 1) : nqt;
+  const int qt_end = window >= 0 ? min(nqt, (k0 + K8_KEYS - 1 + window) / KV_Q + 1) : nqt;
   const int nq = max(0, qt_end - qt_first);
-  const int n_it = G * nq;  // (query head, query tile) pairs
-  char* stages = smem + KV_STAGE0;
+  const int n_it = G * nq;  // (query head, query tile) pairs; block-uniform
 
-  // iteration it: query head hk G + it / nq, query tile qt_first + it % nq
   auto hq_of = [&](int it) { return GEN ? hk * G + it / nq : hk; };
-  auto q_of = [&](int it) { return q + rowbase * ld + hq_of(it) * 128; };
-  auto do_of = [&](int it) { return dout + rowbase * ld_out + hq_of(it) * 128; };
   auto qt_of = [&](int it) { return GEN ? qt_first + it % nq : qt_first + it; };
-  // threads < 64 hold the per-query statistics of a tile: lse (first 32), delta (next 32)
-  auto stat_of = [&](int it) -> float {
-    const long long row = ((long long)b * H + hq_of(it)) * T;
-    const int i = tid & 31, qq = qt_of(it) * KV_Q + i;
-    if (tid < KV_Q) return qq < T ? lse[row + qq] * kLog2e : INFINITY;
-    return qq < T ? delta[row + qq] : 0.f;
+  // the three direct loads of tile it (clamped to the last tile) into stage
+  // st: Q and dO (one 16-byte chunk per thread each) and the statistics
+  // (waves 0-3: lse, waves 4-7: delta, 8 values each from lanes 0-7)
+  auto issue = [&](int it, int st) {
+    it = min(it, n_it - 1);
+    const int hq = hq_of(it), q0 = qt_of(it) * KV_Q;
+    char* so = stage(st);
+    tile_dma8<KV_Q>(buf_rsrc(q + rowbase * ld + hq * 128, (long long)T * ld * 2), (int)ld, q0, T, so + K8_QN, tid);
+    tile_dma8<KV_Q>(buf_rsrc(dout + rowbase * ld_out + hq * 128, (long long)T * ld_out * 2), (int)ld_out, q0, T,
+                    so + K8_DN, tid);
+    const int wu = __builtin_amdgcn_readfirstlane(wave);
+    const float* src = (wu < 4 ? lse : delta) + ((long long)b * H + hq) * T;
+    const int qq = min(q0 + 8 * (wu & 3) + (lane & 7), T - 1);
+    const v4i_t rs = buf_rsrc(src, (long long)T * 4);
+    if (lane < 8) dma4(rs, qq * 4, lds_addr(so + K8_ST + 32 * wu));
   };
 
-  float stat = 0.f;
   if (n_it > 0) {
-    tile_load<KV_Q>(q_of(0), ld, qt_of(0) * KV_Q, T, stages + KV_QN, tid);
-    tile_load<KV_Q>(do_of(0), ld_out, qt_of(0) * KV_Q, T, stages + KV_DN, tid);
-    if (tid < 2 * KV_Q) reinterpret_cast<float*>(stages + KV_LSE)[tid] = stat_of(0);
-  }
-  __syncthreads();
-
-  for (int it = 0; it < n_it; ++it) {
-    const char* st = stages + (it & 1) * KV_STAGE;
-    char* so = stages + ((it + 1) & 1) * KV_STAGE;
-    const bool more = it + 1 < n_it;  // block-uniform
-    if (more) {
-      tile_load<KV_Q>(q_of(it + 1), ld, qt_of(it + 1) * KV_Q, T, so + KV_QN, tid);
-      tile_load<KV_Q>(do_of(it + 1), ld_out, qt_of(it + 1) * KV_Q, T, so + KV_DN, tid);
-      if (tid < 2 * KV_Q) stat = stat_of(it + 1);
-    }
-    const int q0 = qt_of(it) * KV_Q;
-    // wave-uniform: some query of the tile sees some key of the wave
-    if (q0 + KV_Q - 1 >= wk0 && (window < 0 || q0 <= wk0 + 31 + window)) {
-      f32x16_t sacc, dpacc;
+    tile_dma8<K8_KEYS>(buf_rsrc(kh, (long long)T * ld * 2), (int)ld, k0, T, s_k, tid);
 #pragma unroll
-      for (int e = 0; e < 16; ++e) { sacc[e] = 0.f; dpacc[e] = 0.f; }
+    for (int j = 0; j < K8_NS - 1; ++j) issue(j, j);
+    // V fragments of the wave's keys in registers (B operand of dP = dO V^T)
+    bf16x8_t fv[8];
+    {
+      const int vrow = min(mykey, T - 1);
 #pragma unroll
       for (int ks = 0; ks < 8; ++ks) {
-        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag16(st + KV_QN, lr, ks * 2 + lh),
-                                                       frag16(smem + KV_SK, wave * 32 + lr, ks * 2 + lh), sacc, 0, 0, 0);
-        dpacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag16(st + KV_DN, lr, ks * 2 + lh), fv[ks], dpacc, 0, 0, 0);
+        const uint4 a = ld16(vh + (long long)vrow * ld + ks * 16 + lh * 8);
+        fv[ks] = *reinterpret_cast<const bf16x8_t*>(&a);
       }
-      const float* slse = reinterpret_cast<const float*>(st + KV_LSE);
-      const float* sdel = slse + KV_Q;
-      const bool diag = (q0 < wk0 + 31) || (q0 + KV_Q > T) || (wk0 + 32 > T) ||
-                        (window >= 0 && q0 + KV_Q - 1 > wk0 + window);
-      // P and dS packed to bf16 in accumulator order (k-step s: values 8s .. 8s+7)
-      bf16x8_t fp[2], fs[2];
-#pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2) {
-        uint32_t* wp = reinterpret_cast<uint32_t*>(&fp[s2]);
-        uint32_t* wd = reinterpret_cast<uint32_t*>(&fs[s2]);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          float pv[2], dv2[2];
-#pragma unroll
-          for (int u = 0; u < 2; ++u) {
-            const int e = 8 * s2 + 2 * i + u;
-            const int ql = 8 * (e >> 2) + 4 * lh + (e & 3);
-            float pe = __builtin_amdgcn_exp2f(sacc[e] * c - slse[ql]);
-            if (diag)
-              pe = (mykey <= q0 + ql && mykey < T && (window < 0 || mykey >= q0 + ql - window)) ? pe : 0.f;
-            pv[u] = pe;
-            dv2[u] = pe * (dpacc[e] - sdel[ql]);
-          }
-          wp[i] = pack_bf2(pv[0], pv[1]);
-          wd[i] = pack_bf2(dv2[0], dv2[1]);
-        }
-      }
-#pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2)
-#pragma unroll
-        for (int et = 0; et < 4; ++et) {
-          dvt[et] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_tr(st + KV_DN, et, s2, lane), fp[s2], dvt[et], 0, 0, 0);
-          dkt[et] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_tr(st + KV_QN, et, s2, lane), fs[s2], dkt[et], 0, 0, 0);
-        }
     }
-    if (more && tid < 2 * KV_Q) reinterpret_cast<float*>(so + KV_LSE)[tid] = stat;
-    __syncthreads();
+    // everything of the prologue has landed (K, the first tiles, V)
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0xF70);  // vmcnt(0)
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+
+    for (int it0 = 0; it0 < n_it; it0 += K8_NS)
+#pragma unroll
+    for (int cur = 0; cur < K8_NS; ++cur) {
+      const int it = it0 + cur;
+      if (it >= n_it) break;  // block-uniform
+      const char* st = stage(cur);
+      // an opaque copy of the lane index: the per-lane LDS offsets below are
+      // recomputed each tile instead of being kept live across the loop
+      int lane_o = lane;
+      asm volatile("" : "+v"(lane_o));
+      const int lr = lane_o & 31, lh = lane_o >> 5;
+      // tile it + K8_NS - 1 into the stage read during tile it - 1
+      issue(it + K8_NS - 1, (cur + K8_NS - 1) % K8_NS);
+      const int q0 = qt_of(it) * KV_Q;
+      // wave-uniform: some query of the tile sees some key of the wave
+      if (q0 + KV_Q - 1 >= wk0 && (window < 0 || q0 <= wk0 + 31 + window)) {
+        f32x16_t sacc, dpacc;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) { sacc[e] = 0.f; dpacc[e] = 0.f; }
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) {
+          sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag16(st + K8_QN, lr, ks * 2 + lh),
+                                                         frag16(s_k, wave * 32 + lr, ks * 2 + lh), sacc, 0, 0,
+                                                         0);
+          dpacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag16(st + K8_DN, lr, ks * 2 + lh), fv[ks], dpacc, 0, 0, 0);
+        }
+        const float* slse = reinterpret_cast<const float*>(st + K8_ST);
+        const float* sdel = slse + KV_Q;
+        // rows past the sequence end carry the last row's statistics: masked
+        const bool diag = (q0 < wk0 + 31) || (q0 + KV_Q > T) || (wk0 + 32 > T) ||
+                          (window >= 0 && q0 + KV_Q - 1 > wk0 + window);
+        bf16x8_t fp[2], fs[2];
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2) {
+          uint32_t* wp = reinterpret_cast<uint32_t*>(&fp[s2]);
+          uint32_t* wd = reinterpret_cast<uint32_t*>(&fs[s2]);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            float pv[2], dv2[2];
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+              const int e = 8 * s2 + 2 * i + u;
+              const int ql = 8 * (e >> 2) + 4 * lh + (e & 3);
+              const float l2 = slse[ql] * kLog2e;
+              const float dl = sdel[ql];
+              float pe = __builtin_amdgcn_exp2f(sacc[e] * c - l2);
+              const bool vis =
+                  mykey <= q0 + ql && mykey < T && q0 + ql < T && (window < 0 || mykey >= q0 + ql - window);
+              pe = (!diag || vis) ? pe : 0.f;
+              pv[u] = pe;
+              dv2[u] = pe * (dpacc[e] - dl);
+            }
+            wp[i] = pack_bf2(pv[0], pv[1]);
+            wd[i] = pack_bf2(dv2[0], dv2[1]);
+          }
+        }
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+          for (int et = 0; et < 4; ++et) {
+            dvt[et] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_tr(st + K8_DN, et, s2, lane_o), fp[s2], dvt[et], 0, 0,
+                                                              0);
+            dkt[et] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_tr(st + K8_QN, et, s2, lane_o), fs[s2], dkt[et], 0, 0,
+                                                              0);
+          }
+      }
+      // the next tile has landed (only the K8_NS - 2 tiles behind it may be in
+      // flight) and every wave is done with this stage
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_waitcnt(K8_WAIT);
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+    }
+    // drain the trailing (re-issued) loads before the workgroup ends
+    __builtin_amdgcn_s_waitcnt(0xF70);  // vmcnt(0)
   }
 
   if (mykey < T) {
@@ -585,8 +687,9 @@ int launch_attn_bwd_part(int part, const uint16_t* q, const uint16_t* k, const u
                        delta, H, T, NH);
     GS_LAUNCH_CHECK("attn_bwd_pre");
   } else if (part == 1) {
-    hipLaunchKernelGGL(gen ? attn_bwd_kv_kernel<true> : attn_bwd_kv_kernel<false>, dim3((T + KV_KEYS - 1) / KV_KEYS, B * Hkv), dim3(256), 0, s, q, k, v,
-                       ld_qkv, dout, ld_out, lse, delta, dk, dv, ld_dkv, H, Hkv, T, window);
+    hipLaunchKernelGGL(gen ? attn_bwd_kv8_kernel<true> : attn_bwd_kv8_kernel<false>,
+                       dim3((T + K8_KEYS - 1) / K8_KEYS, B * Hkv), dim3(K8_NT), 0, s, q, k, v, ld_qkv, dout, ld_out, lse,
+                       delta, dk, dv, ld_dkv, H, Hkv, T, window);
     GS_LAUNCH_CHECK("attn_bwd_kv");
   } else {
     hipLaunchKernelGGL(gen ? attn_bwd_q_kernel<true> : attn_bwd_q_kernel<false>, dim3((T + DQ_Q - 1) / DQ_Q, B * H), dim3(256), 0, s, q, k, v, ld_qkv,
