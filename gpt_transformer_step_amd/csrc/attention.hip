@@ -9,7 +9,7 @@
 //
 // Layout and data movement (gfx950):
 //   * every LDS tile is a block of rows of 128 features (256 bytes) stored as
-//     in HBM, filled by direct global->LDS loads (global_load_lds_dwordx4);
+//     in HBM, filled by direct buffer->LDS loads (buffer_load_dwordx4 ... lds);
 //     rows past the sequence end are clamped to a valid row (they are always
 //     masked, so only finiteness matters);
 //   * 16-byte chunks are XOR-swizzled by sigma(r) = 4 (r & 3) + ((r >> 2) & 3),
@@ -94,21 +94,71 @@ __device__ __forceinline__ bf16x8_t pack_perm(const float* x, int s) {
 
 __device__ __forceinline__ uint4 ld16(const uint16_t* p) { return *reinterpret_cast<const uint4*>(p); }
 
-// Direct global -> LDS copy of ROWS rows of 128 features starting at row r0
-// of a [T, ld] bf16 matrix (rows >= T clamped to T-1) into a swizzled tile.
-// 256 threads; round i, wave w, lane l fills 16-byte slot 256 i + 64 w + l.
-template <int ROWS>
-__device__ __forceinline__ void tile_load(const uint16_t* __restrict__ base, long long ld, int r0, int T, char* lds,
-                                          int tid) {
+// Buffer resource (raw byte addressing, range num_bytes; gfx9 layout: base,
+// base_hi | stride 0, num_records, format word) from wave-uniform values.
+typedef int v4i_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ v4i_t buf_rsrc(const void* base, long long num_bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  v4i_t r;
+  r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+  r[1] = __builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32));
+  r[2] = __builtin_amdgcn_readfirstlane((int)min(num_bytes, (long long)0x7fffffff));
+  r[3] = 0x00020000;
+  return r;
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(size_t)(const __attribute__((address_space(3))) char*)p;
+}
+
+// Direct buffer -> LDS loads of this kernel, written as instructions the
+// compiler does not model: it would otherwise make every LDS read wait for
+// every such load in flight (it cannot tell the ring's stages apart), which
+// defeats loading several tiles ahead.  Ordering is the kernel's own: the
+// loads into a stage are issued after the barrier that ends its last reads,
+// and the barrier before its next reads follows an explicit vmcnt wait.
+// They have no register results; "memory" keeps the compiler from moving LDS
+// accesses across them.  M0 (the LDS base of the wave's write) is set here
+// only; nothing compiled in this kernel reads M0.
+__device__ __forceinline__ void dma16(v4i_t rsrc, int voffset, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %0, 0 offen lds"
+               :: "s"(rsrc), "v"(voffset), "s"(lds_base) : "memory");
+}
+__device__ __forceinline__ void dma4(v4i_t rsrc, int voffset, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dword %1, %0, 0 offen lds"
+               :: "s"(rsrc), "v"(voffset), "s"(lds_base) : "memory");
+}
+
+// Register operands loaded before a loop of direct loads: a use here makes
+// the compiler wait for them now, in the prologue (otherwise it may sink the
+// loads and wait for them inside the loop, where the counter also covers the
+// direct loads of the next tile).
+__device__ __forceinline__ void settle(const bf16x8_t& f) { asm volatile("" :: "v"(f)); }
+__device__ __forceinline__ void settle(const float& f) { asm volatile("" :: "v"(f)); }
+
+// Barrier after direct loads: the compiler does not see those loads, so the
+// wait for them (and for any other load in flight) is explicit; it also tells
+// the compiler that its own earlier loads have landed.
+__device__ __forceinline__ void dma_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xF70);  // vmcnt(0)
+  __syncthreads();
+  asm volatile("" ::: "memory");
+}
+
+// Copy of ROWS rows of 128 features (row r0 + r clamped to T - 1) of a bf16
+// matrix whose row 0 is byte 0 of rsrc into a swizzled tile, by NT threads:
+// round i, wave w, lane l fills 16-byte slot NT i + 64 w + l.  Offsets
+// (row * ld + chunk) * 2 fit 32 bits (T <= 16384, ld < 2^16).
+template <int ROWS, int NT>
+__device__ __forceinline__ void tile_dma(v4i_t rsrc, int ld, int r0, int T, char* lds, int tid) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 #pragma unroll
-  for (int i = 0; i < ROWS * 16 / 256; ++i) {
-    const int slot = tid + 256 * i;
+  for (int i = 0; i < ROWS * 16 / NT; ++i) {
+    const int slot = tid + NT * i;
     const int r = slot >> 4, c = (slot & 15) ^ sigma(r);
     const int row = min(r0 + r, T - 1);
-    lds_char* dst = (lds_char*)lds + (256 * i + 64 * wave) * 16;
-    __builtin_amdgcn_global_load_lds((const void*)(base + (long long)row * ld + c * 8),
-                                     (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
+    dma16(rsrc, (row * ld + c * 8) * 2, lds_addr(lds + (NT * i + 64 * wave) * 16));
   }
 }
 
@@ -152,6 +202,8 @@ attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, 
       const uint4 w = ld16(qh + (long long)qrow * ld + ks * 16 + lh * 8);
       fq[ks] = *reinterpret_cast<const bf16x8_t*>(&w);
     }
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) settle(fq[ks]);
   }
 
   f32x16_t o[4];
@@ -165,17 +217,18 @@ attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, 
   const int ntiles = last_key / FK + 1;
   const int j0 = window >= 0 ? max(0, q0 - window) / FK : 0;  // first key tile any query of the block sees
 
-  tile_load<FK>(kh, ld, j0 * FK, T, smem, tid);
-  tile_load<FK>(vh, ld, j0 * FK, T, smem + FK * 256, tid);
-  __syncthreads();
+  const v4i_t rk = buf_rsrc(kh, (long long)T * ld * 2), rv = buf_rsrc(vh, (long long)T * ld * 2);
+  tile_dma<FK, 256>(rk, (int)ld, j0 * FK, T, smem, tid);
+  tile_dma<FK, 256>(rv, (int)ld, j0 * FK, T, smem + FK * 256, tid);
+  dma_barrier();
 
   for (int j = j0; j < ntiles; ++j) {
     const char* sk = smem + ((j - j0) & 1) * F_STAGE;
     const char* sv = sk + FK * 256;
     if (j + 1 < ntiles) {  // block-uniform; the other stage was last read before the previous barrier
       char* nk = smem + ((j + 1 - j0) & 1) * F_STAGE;
-      tile_load<FK>(kh, ld, (j + 1) * FK, T, nk, tid);
-      tile_load<FK>(vh, ld, (j + 1) * FK, T, nk + FK * 256, tid);
+      tile_dma<FK, 256>(rk, (int)ld, (j + 1) * FK, T, nk, tid);
+      tile_dma<FK, 256>(rv, (int)ld, (j + 1) * FK, T, nk + FK * 256, tid);
     }
     const int key0 = j * FK;
     // wave-uniform: some key of the tile is visible to some query of the wave
@@ -245,7 +298,7 @@ attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, 
           o[et] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_tr(sv, et, st, lane), fp, o[et], 0, 0, 0);
       }
     }
-    __syncthreads();
+    dma_barrier();  // the next tile has landed; every wave is done with this one
   }
 
   l += __shfl_xor(l, 32, 64);
@@ -322,57 +375,6 @@ static_assert(K8_VMCNT < 64, "vmcnt range");
 
 // ROWS rows of 128 features from row r0 (clamped to T - 1) into a swizzled
 // tile, K8_NT threads: round i, wave w, lane l fills 16-byte slot 512 i + 64 w + l
-// Buffer resource (raw byte addressing, range num_bytes; gfx9 layout: base,
-// base_hi | stride 0, num_records, format word) from wave-uniform values.
-typedef int v4i_t __attribute__((ext_vector_type(4)));
-__device__ __forceinline__ v4i_t buf_rsrc(const void* base, long long num_bytes) {
-  const uint64_t a = reinterpret_cast<uint64_t>(base);
-  v4i_t r;
-  r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
-  r[1] = __builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32));
-  r[2] = __builtin_amdgcn_readfirstlane((int)min(num_bytes, (long long)0x7fffffff));
-  r[3] = 0x00020000;
-  return r;
-}
-
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-  return (uint32_t)(size_t)(const __attribute__((address_space(3))) char*)p;
-}
-
-// Direct buffer -> LDS loads of this kernel, written as instructions the
-// compiler does not model: it would otherwise make every LDS read wait for
-// every such load in flight (it cannot tell the ring's stages apart), which
-// defeats loading several tiles ahead.  Ordering is the kernel's own: the
-// loads into a stage are issued after the barrier that ends its last reads,
-// and the barrier before its next reads follows an explicit vmcnt wait.
-// They have no register results; "memory" keeps the compiler from moving LDS
-// accesses across them.  M0 (the LDS base of the wave's write) is set here
-// only; nothing compiled in this kernel reads M0.
-__device__ __forceinline__ void dma16(v4i_t rsrc, int voffset, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %0, 0 offen lds"
-               :: "s"(rsrc), "v"(voffset), "s"(lds_base) : "memory");
-}
-__device__ __forceinline__ void dma4(v4i_t rsrc, int voffset, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dword %1, %0, 0 offen lds"
-               :: "s"(rsrc), "v"(voffset), "s"(lds_base) : "memory");
-}
-
-// ROWS rows of 128 features (row r0 + r clamped to T - 1) of a bf16 matrix
-// whose row 0 is byte 0 of rsrc, into a swizzled tile, K8_NT threads: round
-// i, wave w, lane l fills 16-byte slot 512 i + 64 w + l.  Offsets
-// (row * ld + chunk) * 2 fit 32 bits (T <= 16384, ld < 2^16).
-template <int ROWS>
-__device__ __forceinline__ void tile_dma8(v4i_t rsrc, int ld, int r0, int T, char* lds, int tid) {
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-#pragma unroll
-  for (int i = 0; i < ROWS * 16 / K8_NT; ++i) {
-    const int slot = tid + K8_NT * i;
-    const int r = slot >> 4, c = (slot & 15) ^ sigma(r);
-    const int row = min(r0 + r, T - 1);
-    dma16(rsrc, (row * ld + c * 8) * 2, lds_addr(lds + (K8_NT * i + 64 * wave) * 16));
-  }
-}
-
 template <bool GEN>
 __global__ void __launch_bounds__(K8_NT, 1)
 attn_bwd_kv8_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
@@ -421,8 +423,8 @@ attn_bwd_kv8_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
     it = min(it, n_it - 1);
     const int hq = hq_of(it), q0 = qt_of(it) * KV_Q;
     char* so = stage(st);
-    tile_dma8<KV_Q>(buf_rsrc(q + rowbase * ld + hq * 128, (long long)T * ld * 2), (int)ld, q0, T, so + K8_QN, tid);
-    tile_dma8<KV_Q>(buf_rsrc(dout + rowbase * ld_out + hq * 128, (long long)T * ld_out * 2), (int)ld_out, q0, T,
+    tile_dma<KV_Q, K8_NT>(buf_rsrc(q + rowbase * ld + hq * 128, (long long)T * ld * 2), (int)ld, q0, T, so + K8_QN, tid);
+    tile_dma<KV_Q, K8_NT>(buf_rsrc(dout + rowbase * ld_out + hq * 128, (long long)T * ld_out * 2), (int)ld_out, q0, T,
                     so + K8_DN, tid);
     const int wu = __builtin_amdgcn_readfirstlane(wave);
     const float* src = (wu < 4 ? lse : delta) + ((long long)b * H + hq) * T;
@@ -432,7 +434,7 @@ attn_bwd_kv8_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
   };
 
   if (n_it > 0) {
-    tile_dma8<K8_KEYS>(buf_rsrc(kh, (long long)T * ld * 2), (int)ld, k0, T, s_k, tid);
+    tile_dma<K8_KEYS, K8_NT>(buf_rsrc(kh, (long long)T * ld * 2), (int)ld, k0, T, s_k, tid);
 #pragma unroll
     for (int j = 0; j < K8_NS - 1; ++j) issue(j, j);
     // V fragments of the wave's keys in registers (B operand of dP = dO V^T)
@@ -444,6 +446,8 @@ attn_bwd_kv8_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
         const uint4 a = ld16(vh + (long long)vrow * ld + ks * 16 + lh * 8);
         fv[ks] = *reinterpret_cast<const bf16x8_t*>(&a);
       }
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) settle(fv[ks]);
     }
     // everything of the prologue has landed (K, the first tiles, V)
     asm volatile("" ::: "memory");
@@ -589,6 +593,13 @@ attn_bwd_q_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k
   }
   const float lse2 = myq < T ? lse[(long long)bh * T + myq] * kLog2e : INFINITY;
   const float del = myq < T ? delta[(long long)bh * T + myq] : 0.f;
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) {
+    settle(fq[ks]);
+    settle(fd[ks]);
+  }
+  settle(lse2);
+  settle(del);
 
   f32x16_t dqt[4];
 #pragma unroll
@@ -599,17 +610,18 @@ attn_bwd_q_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k
   const int last_key = min(T - 1, q0 + DQ_Q - 1);
   const int ntiles = last_key / DQ_K + 1;
   const int j0 = window >= 0 ? max(0, q0 - window) / DQ_K : 0;
-  tile_load<DQ_K>(kh, ld, j0 * DQ_K, T, smem, tid);
-  tile_load<DQ_K>(vh, ld, j0 * DQ_K, T, smem + DQ_K * 256, tid);
-  __syncthreads();
+  const v4i_t rk = buf_rsrc(kh, (long long)T * ld * 2), rv = buf_rsrc(vh, (long long)T * ld * 2);
+  tile_dma<DQ_K, 256>(rk, (int)ld, j0 * DQ_K, T, smem, tid);
+  tile_dma<DQ_K, 256>(rv, (int)ld, j0 * DQ_K, T, smem + DQ_K * 256, tid);
+  dma_barrier();
 
   for (int j = j0; j < ntiles; ++j) {
     const char* sk = smem + ((j - j0) & 1) * DQ_STAGE;
     const char* sv = sk + DQ_K * 256;
     if (j + 1 < ntiles) {
       char* nk = smem + ((j + 1 - j0) & 1) * DQ_STAGE;
-      tile_load<DQ_K>(kh, ld, (j + 1) * DQ_K, T, nk, tid);
-      tile_load<DQ_K>(vh, ld, (j + 1) * DQ_K, T, nk + DQ_K * 256, tid);
+      tile_dma<DQ_K, 256>(rk, (int)ld, (j + 1) * DQ_K, T, nk, tid);
+      tile_dma<DQ_K, 256>(rv, (int)ld, (j + 1) * DQ_K, T, nk + DQ_K * 256, tid);
     }
     const int key0 = j * DQ_K;
     if (key0 <= wq0 + 31 && (window < 0 || key0 + DQ_K - 1 >= wq0 - window)) {  // wave-uniform
@@ -633,10 +645,9 @@ attn_bwd_q_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
           float pv = __builtin_amdgcn_exp2f(st2[kt][e] * c - lse2);
-          if (diag) {
-            const int key = key0 + kt * 32 + 8 * (e >> 2) + 4 * lh + (e & 3);
-            pv = (key <= myq && key < T && (window < 0 || key >= myq - window)) ? pv : 0.f;
-          }
+          const int key = key0 + kt * 32 + 8 * (e >> 2) + 4 * lh + (e & 3);
+          const bool vis = key <= myq && key < T && (window < 0 || key >= myq - window);
+          pv = (!diag || vis) ? pv : 0.f;
           ds[kt * 16 + e] = pv * (dpt[kt][e] - del);
         }
 #pragma unroll
@@ -647,7 +658,7 @@ attn_bwd_q_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k
           dqt[et] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_tr(sk, et, s4, lane), fs, dqt[et], 0, 0, 0);
       }
     }
-    __syncthreads();
+    dma_barrier();  // the next tile has landed; every wave is done with this one
   }
   if (myq < T) {
     float* dqr = dq_out + (rowbase + myq) * d + h * 128;
