@@ -216,7 +216,7 @@ struct TileLoader {
 // ---------------------------------------------------------------------------
 template <int EPI>
 __device__ __forceinline__ void epi4(const GemmArgs& p, int bi, int m, int n, const float* v, long long coff,
-                                     float& amx) {
+                                     float& amx, uint2 aux_w = make_uint2(0, 0)) {
   const bool full = (n + 3 < p.N);
   if constexpr (EPI == EPI_F32 || EPI == EPI_RESID || EPI == EPI_F32_ATOMIC) {
     float* C = reinterpret_cast<float*>(p.C) + (long long)bi * p.sC + coff + (long long)m * p.ldc + n;
@@ -253,7 +253,7 @@ __device__ __forceinline__ void epi4(const GemmArgs& p, int bi, int m, int n, co
     if constexpr (EPI == EPI_DRELU2) {
       const uint16_t* a = reinterpret_cast<const uint16_t*>(p.aux) + (long long)bi * p.sAux + (long long)m * p.ldaux + n;
       if (full) {
-        const uint2 w = *reinterpret_cast<const uint2*>(a);
+        const uint2 w = aux_w;  // fetched ahead by the caller
         o[0] *= 2.f * sqrtf(lo_bf(w.x)); o[1] *= 2.f * sqrtf(hi_bf(w.x));
         o[2] *= 2.f * sqrtf(lo_bf(w.y)); o[3] *= 2.f * sqrtf(hi_bf(w.y));
       } else {
@@ -590,10 +590,31 @@ __global__ void __launch_bounds__((Cfg<BM, BN>::NT), 1) gemm_kernel(GemmArgs p) 
     constexpr int CH = WN / 4;                   // 16-byte chunks per row
     static_assert(32 * ROWB * (Cfg<BM, BN>::NT / 64) <= 2 * STAGE, "epilogue staging exceeds LDS");
     char* wbuf = smem + wave * 32 * ROWB;
+    // DRELU2 reads the saved activation at every output: each 32-row block's
+    // words are fetched in one burst, the first block's before the staging
+    // barrier, so their latency overlaps the staging instead of being paid
+    // every few outputs
+    constexpr int NIT = 32 * CH / 64;
+    uint2 auxw[NIT];
+    auto fetch_aux = [&](int i) {
+      if constexpr (EPI == EPI_DRELU2) {
+        const uint16_t* ab = reinterpret_cast<const uint16_t*>(p.aux) + (long long)bi * p.sAux;
+#pragma unroll
+        for (int it = 0; it < NIT; ++it) {
+          const int q = it * 64 + lane;
+          const int m = m0 + wm * WM + i * 32 + q / CH;
+          const int n = n0 + wn * WN + (q % CH) * 4;
+          auxw[it] = (m < p.M && n + 3 < p.N) ? *reinterpret_cast<const uint2*>(ab + (long long)m * p.ldaux + n)
+                                               : make_uint2(0, 0);
+        }
+      }
+    };
+    fetch_aux(0);
     __syncthreads();  // every wave is done with the operand tiles
     float amx = 0.f;  // max |stored value| of this lane (bf16 epilogues with p.amax)
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
+      if (i > 0) fetch_aux(i);
 #pragma unroll
       for (int j = 0; j < TN; ++j)
 #pragma unroll
@@ -606,8 +627,8 @@ __global__ void __launch_bounds__((Cfg<BM, BN>::NT), 1) gemm_kernel(GemmArgs p) 
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-#pragma unroll 4
-      for (int it = 0; it < 32 * CH / 64; ++it) {
+#pragma unroll
+      for (int it = 0; it < NIT; ++it) {
         const int q = it * 64 + lane;
         const int rr = q / CH, cc = q % CH;
         const float4 v4 = *reinterpret_cast<const float4*>(wbuf + rr * ROWB + ((cc ^ (rr & 15)) << 4));
@@ -615,7 +636,7 @@ __global__ void __launch_bounds__((Cfg<BM, BN>::NT), 1) gemm_kernel(GemmArgs p) 
         const int n = n0 + wn * WN + cc * 4;
         if (m < p.M && n < p.N) {
           const float v[4] = {v4.x, v4.y, v4.z, v4.w};
-          epi4<(EPI == EPI_QKV ? (int)EPI_BF16 : EPI)>(p, bi, m, n, v, coff, amx);
+          epi4<(EPI == EPI_QKV ? (int)EPI_BF16 : EPI)>(p, bi, m, n, v, coff, amx, auxw[it]);
         }
       }
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
