@@ -438,6 +438,189 @@ __device__ __forceinline__ void mainloop(const GemmArgs& p, const void* A, const
 }
 
 // ---------------------------------------------------------------------------
+// bf16 interior tiles: a ring of RING_NS LDS stages of 64 bytes of k per row
+// (32 bf16, two MFMA k-steps), loaded RING_NS - 1 stages ahead, so a stage's
+// load latency (1-2 us under load) is covered by three stages of MFMAs
+// instead of one.  The ring takes the same LDS as the two 128-byte stages of
+// the general loop.  Loads are direct buffer -> LDS loads issued as
+// instructions the compiler does not model (with the builtin it makes every
+// LDS read wait for all loads in flight); the loop carries its own waits: at
+// the end of a stage, the next stage's loads have landed (vmcnt) and every
+// wave is done with this stage (barrier).  Per-lane byte offsets are loop
+// invariant; the k position goes in the scalar offset.
+// ---------------------------------------------------------------------------
+constexpr int RING_NS = 4;
+constexpr int RING_RB = 64;   // bytes of k per operand row per stage
+constexpr int RING_KBK = 32;  // bf16 k per stage
+
+typedef int v4i_t __attribute__((ext_vector_type(4)));
+
+// buffer resource (raw bytes, range num_bytes) from wave-uniform values
+__device__ __forceinline__ v4i_t ring_rsrc(const void* base, long long num_bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  v4i_t r;
+  r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+  r[1] = __builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32));
+  r[2] = __builtin_amdgcn_readfirstlane((int)min(num_bytes, (long long)0x7fffffff));
+  r[3] = 0x00020000;
+  return r;
+}
+
+// 16 bytes per lane from rsrc at voff + soff into LDS at lds + 16 lane (lds
+// wave-uniform).  No register results; "memory" keeps LDS accesses in place;
+// M0 is set here only and nothing compiled in the GEMM kernel reads it.
+__device__ __forceinline__ void ring_dma16(v4i_t rsrc, int voff, int soff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %3\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %0, %2 offen lds"
+               :: "s"(rsrc), "v"(voff), "s"(soff), "s"(lds) : "memory");
+}
+
+// k-contiguous ring tile: R rows of 64 bytes; the four 16-byte chunks of a row
+// XOR-swizzled by (r >> 2) & 3, so the 16 rows of a fragment read at one
+// logical chunk fill 16 distinct 16-byte bank groups
+__device__ __forceinline__ int ring_off_k(int r, int kc) { return r * RING_RB + ((kc ^ ((r >> 2) & 3)) << 4); }
+
+// True when every byte offset of the ring's loads fits 31 bits.
+__device__ __forceinline__ bool ring_fits(const GemmArgs& p, int BM, int BN, bool AK, bool BKC) {
+  const long long ea = AK ? (long long)BM * p.lda * 2 : (long long)p.K * p.lda * 2;
+  const long long eb = BKC ? (long long)BN * p.ldb * 2 : (long long)p.K * p.ldb * 2;
+  return ea < 0x7fffffffLL && eb < 0x7fffffffLL;
+}
+
+template <int R, bool KC, int NT>
+struct RingOperand {
+  static constexpr int NL = R * 4 / NT;  // 16-byte loads per thread per stage
+  v4i_t rsrc;
+  int voff[NL];
+  long long kstep;  // bytes per k element along the loaded direction
+
+  __device__ __forceinline__ void init(const char* X, long long ld, int row0, int K, int tid) {
+    if constexpr (KC) {
+      rsrc = ring_rsrc(X + (long long)row0 * ld * 2, (long long)R * ld * 2);
+      kstep = 2;
+    } else {
+      rsrc = ring_rsrc(X + (long long)row0 * 2, (long long)K * ld * 2);
+      kstep = ld * 2;
+    }
+#pragma unroll
+    for (int i = 0; i < NL; ++i) {
+      const int slot = tid + NT * i;
+      if constexpr (KC) {
+        const int r = slot >> 2, kc = (slot & 3) ^ ((r >> 2) & 3);
+        voff[i] = (int)(((long long)r * ld + kc * 8) * 2);
+      } else {
+        const int b = slot * 16;
+        const int k = b / (2 * R), rb = b % (2 * R);
+        const int i_el = (((rb >> 6) ^ (k & 3)) << 5) + ((rb & 63) >> 1);
+        voff[i] = (int)(((long long)k * ld + i_el) * 2);
+      }
+    }
+  }
+  // the stage at k element k0 into the LDS tile at lds (lane l of wave w in
+  // round i fills slot NT i + 64 w + l)
+  __device__ __forceinline__ void issue(int k0, char* lds, int wave) const {
+    const int soff = __builtin_amdgcn_readfirstlane((int)(k0 * kstep));
+#pragma unroll
+    for (int i = 0; i < NL; ++i)
+      ring_dma16(rsrc, voff[i], soff,
+                 (uint32_t)(size_t)(__attribute__((address_space(3))) char*)(lds + (NT * i + 64 * wave) * 16));
+  }
+  // MFMA fragment of rows r0 .. r0+31, k-step ks (0 or 1) of a stage
+  __device__ __forceinline__ static bf16x8_t frag(const char* lds, int r0, int ks, int lane) {
+    if constexpr (KC) {
+      return *reinterpret_cast<const bf16x8_t*>(lds + ring_off_k(r0 + (lane & 31), ks * 2 + (lane >> 5)));
+    } else {
+      const int g = lane >> 4, m = lane & 15;
+      const int i = r0 + 16 * (g & 1) + 4 * (m & 3);
+      const int k = ks * 16 + 8 * (g >> 1) + (m >> 2);
+      const v4s_t a = ds_read_tr(lds, lds_off_mn<R>(k, i));
+      const v4s_t b = ds_read_tr(lds, lds_off_mn<R>(k + 4, i));
+      bf16x8_t f;
+      f[0] = a[0]; f[1] = a[1]; f[2] = a[2]; f[3] = a[3];
+      f[4] = b[0]; f[5] = b[1]; f[6] = b[2]; f[7] = b[3];
+      return f;
+    }
+  }
+};
+
+template <int BM, int BN, bool AK, bool BKC>
+__device__ __forceinline__ void mainloop_ring(const GemmArgs& p, const char* A, const char* B, int m0, int n0,
+                                              int k_begin, int nk, char* smem, int tid,
+                                              f32x16_t (&acc)[Cfg<BM, BN>::TM][Cfg<BM, BN>::TN]) {
+  constexpr int NT = Cfg<BM, BN>::NT;
+  constexpr int WM = Cfg<BM, BN>::WM, WN = Cfg<BM, BN>::WN, TM = Cfg<BM, BN>::TM, TN = Cfg<BM, BN>::TN;
+  constexpr int A_BYTES = BM * RING_RB, STAGE = (BM + BN) * RING_RB;
+  using OA = RingOperand<BM, AK, NT>;
+  using OB = RingOperand<BN, BKC, NT>;
+  constexpr int NV = OA::NL + OB::NL;
+  constexpr int VM = NV * (RING_NS - 2);
+  constexpr int WAIT = (VM & 15) | ((VM >> 4) << 14) | (7 << 4) | (15 << 8);
+  static_assert(RING_NS * STAGE <= 2 * (BM + BN) * 128, "ring exceeds the LDS of the general loop");
+  static_assert(VM < 64, "vmcnt range");
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+  if (nk <= 0) return;
+  OA oa;
+  OB ob;
+  oa.init(A, p.lda, m0, p.K, tid);
+  ob.init(B, p.ldb, n0, p.K, tid);
+  // stage kt (clamped to the last: the trailing re-loads land in stages that
+  // are never read again) into ring slot st
+  auto issue = [&](int kt, int st) {
+    const int k0 = k_begin + min(kt, nk - 1) * RING_KBK;
+    char* so = smem + st * STAGE;
+    oa.issue(k0, so, wave);
+    ob.issue(k0, so + A_BYTES, wave);
+  };
+  auto stage_barrier = [&]() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(WAIT);
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  };
+#pragma unroll
+  for (int j = 0; j < RING_NS - 1; ++j) issue(j, j);
+  stage_barrier();  // stage 0 has landed
+
+  bf16x8_t fa[2][TM], fb[2][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i) fa[0][i] = OA::frag(smem, wm * WM + i * 32, 0, lane);
+#pragma unroll
+  for (int j = 0; j < TN; ++j) fb[0][j] = OB::frag(smem + A_BYTES, wn * WN + j * 32, 0, lane);
+
+  for (int kt = 0; kt < nk; ++kt) {
+    const char* sa = smem + (kt % RING_NS) * STAGE;
+    const char* sb = sa + A_BYTES;
+    // stage kt + 3 into the slot read during stage kt - 1
+    issue(kt + RING_NS - 1, (kt + RING_NS - 1) % RING_NS);
+    // k-step 0 with the fragments of k-step 1 loading
+#pragma unroll
+    for (int i = 0; i < TM; ++i) fa[1][i] = OA::frag(sa, wm * WM + i * 32, 1, lane);
+#pragma unroll
+    for (int j = 0; j < TN; ++j) fb[1][j] = OB::frag(sb, wn * WN + j * 32, 1, lane);
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[0][j], fa[0][i], acc[i][j], 0, 0, 0);
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[1][j], fa[1][i], acc[i][j], 0, 0, 0);
+    stage_barrier();  // stage kt + 1 has landed; every wave is done with stage kt
+    const char* na = smem + ((kt + 1) % RING_NS) * STAGE;
+#pragma unroll
+    for (int i = 0; i < TM; ++i) fa[0][i] = OA::frag(na, wm * WM + i * 32, 0, lane);
+#pragma unroll
+    for (int j = 0; j < TN; ++j) fb[0][j] = OB::frag(na + A_BYTES, wn * WN + j * 32, 0, lane);
+  }
+  // drain the trailing loads before the LDS is reused by the epilogue
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xF70);
+  asm volatile("" ::: "memory");
+}
+
+// ---------------------------------------------------------------------------
 // the kernel
 // ---------------------------------------------------------------------------
 template <int BM, int BN, bool AK, bool BKC, int EPI, int F8>
@@ -480,10 +663,19 @@ __global__ void __launch_bounds__((Cfg<BM, BN>::NT), 1) gemm_kernel(GemmArgs p) 
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
   const bool fast = (m0 + BM <= p.M) && (n0 + BN <= p.N) && (p.K % KBK == 0);
-  if (fast)
-    mainloop<BM, BN, AK, BKC, false, F8>(p, A, B, m0, n0, kt0, nk, smem, tid, acc);
-  else
-    mainloop<BM, BN, AK, BKC, true, F8>(p, A, B, m0, n0, kt0, nk, smem, tid, acc);
+  if constexpr (F8 == 0) {
+    if (fast && ring_fits(p, BM, BN, AK, BKC))
+      mainloop_ring<BM, BN, AK, BKC>(p, A, B, m0, n0, kt0 * KBK, nk * (KBK / RING_KBK), smem, tid, acc);
+    else if (fast)
+      mainloop<BM, BN, AK, BKC, false, F8>(p, A, B, m0, n0, kt0, nk, smem, tid, acc);
+    else
+      mainloop<BM, BN, AK, BKC, true, F8>(p, A, B, m0, n0, kt0, nk, smem, tid, acc);
+  } else {
+    if (fast)
+      mainloop<BM, BN, AK, BKC, false, F8>(p, A, B, m0, n0, kt0, nk, smem, tid, acc);
+    else
+      mainloop<BM, BN, AK, BKC, true, F8>(p, A, B, m0, n0, kt0, nk, smem, tid, acc);
+  }
   const int lr = lane & 31, lh = lane >> 5;
   if constexpr (F8 != 0) {
     // dequantise: the codes carry x * s_x, so the product carries s_a * s_b
