@@ -480,23 +480,24 @@ __device__ __forceinline__ void ring_dma16(v4i_t rsrc, int voff, int soff, uint3
 __device__ __forceinline__ int ring_off_k(int r, int kc) { return r * RING_RB + ((kc ^ ((r >> 2) & 3)) << 4); }
 
 // True when every byte offset of the ring's loads fits 31 bits.
-__device__ __forceinline__ bool ring_fits(const GemmArgs& p, int BM, int BN, bool AK, bool BKC) {
-  const long long ea = AK ? (long long)BM * p.lda * 2 : (long long)p.K * p.lda * 2;
-  const long long eb = BKC ? (long long)BN * p.ldb * 2 : (long long)p.K * p.ldb * 2;
+__device__ __forceinline__ bool ring_fits(const GemmArgs& p, int BM, int BN, bool AK, bool BKC, int ES) {
+  const long long ea = AK ? (long long)BM * p.lda * ES : (long long)p.K * p.lda * ES;
+  const long long eb = BKC ? (long long)BN * p.ldb * ES : (long long)p.K * p.ldb * ES;
   return ea < 0x7fffffffLL && eb < 0x7fffffffLL;
 }
 
-template <int R, bool KC, int NT>
+template <int R, bool KC, int NT, int ES = 2>
 struct RingOperand {
   static constexpr int NL = R * 4 / NT;  // 16-byte loads per thread per stage
+  static_assert(ES == 2 || KC, "fp8 operands are k-contiguous");
   v4i_t rsrc;
   int voff[NL];
   long long kstep;  // bytes per k element along the loaded direction
 
   __device__ __forceinline__ void init(const char* X, long long ld, int row0, int K, int tid) {
     if constexpr (KC) {
-      rsrc = ring_rsrc(X + (long long)row0 * ld * 2, (long long)R * ld * 2);
-      kstep = 2;
+      rsrc = ring_rsrc(X + (long long)row0 * ld * ES, (long long)R * ld * ES);
+      kstep = ES;
     } else {
       rsrc = ring_rsrc(X + (long long)row0 * 2, (long long)K * ld * 2);
       kstep = ld * 2;
@@ -506,7 +507,7 @@ struct RingOperand {
       const int slot = tid + NT * i;
       if constexpr (KC) {
         const int r = slot >> 2, kc = (slot & 3) ^ ((r >> 2) & 3);
-        voff[i] = (int)(((long long)r * ld + kc * 8) * 2);
+        voff[i] = (int)(((long long)r * ld + kc * (16 / ES)) * ES);
       } else {
         const int b = slot * 16;
         const int k = b / (2 * R), rb = b % (2 * R);
@@ -523,6 +524,19 @@ struct RingOperand {
     for (int i = 0; i < NL; ++i)
       ring_dma16(rsrc, voff[i], soff,
                  (uint32_t)(size_t)(__attribute__((address_space(3))) char*)(lds + (NT * i + 64 * wave) * 16));
+  }
+  // fp8 fragment of rows r0 .. r0+31 (the stage's 64 codes): lane l holds row
+  // r0 + l % 32 and the codes of chunks 2 (l / 32) + {0, 1}; both operands use
+  // the same assignment, which is all the MFMA needs
+  __device__ __forceinline__ static i32x8_t frag8(const char* lds, int r0, int lane) {
+    typedef int i32x4_t __attribute__((ext_vector_type(4)));
+    const int r = r0 + (lane & 31), c = (lane >> 5) * 2;
+    const i32x4_t a = *reinterpret_cast<const i32x4_t*>(lds + ring_off_k(r, c));
+    const i32x4_t b = *reinterpret_cast<const i32x4_t*>(lds + ring_off_k(r, c + 1));
+    i32x8_t f;
+    f[0] = a[0]; f[1] = a[1]; f[2] = a[2]; f[3] = a[3];
+    f[4] = b[0]; f[5] = b[1]; f[6] = b[2]; f[7] = b[3];
+    return f;
   }
   // MFMA fragment of rows r0 .. r0+31, k-step ks (0 or 1) of a stage
   __device__ __forceinline__ static bf16x8_t frag(const char* lds, int r0, int ks, int lane) {
@@ -620,6 +634,73 @@ __device__ __forceinline__ void mainloop_ring(const GemmArgs& p, const char* A, 
   asm volatile("" ::: "memory");
 }
 
+// fp8 interior tiles on the same ring: a stage holds 64 codes of k per row,
+// one MFMA k-step.  The stage's MFMAs are issued after the barrier that
+// releases the next stage, so they overlap that stage's fragment reads.
+template <int BM, int BN, int F8>
+__device__ __forceinline__ void mainloop_ring_f8(const GemmArgs& p, const char* A, const char* B, int m0, int n0,
+                                                 int k_begin, int nk, char* smem, int tid,
+                                                 f32x16_t (&acc)[Cfg<BM, BN>::TM][Cfg<BM, BN>::TN]) {
+  constexpr int NT = Cfg<BM, BN>::NT;
+  constexpr int WM = Cfg<BM, BN>::WM, WN = Cfg<BM, BN>::WN, TM = Cfg<BM, BN>::TM, TN = Cfg<BM, BN>::TN;
+  constexpr int A_BYTES = BM * RING_RB, STAGE = (BM + BN) * RING_RB;
+  constexpr int KBKR = RING_RB;  // fp8 codes of k per stage
+  using OA = RingOperand<BM, true, NT, 1>;
+  using OB = RingOperand<BN, true, NT, 1>;
+  constexpr int NV = OA::NL + OB::NL;
+  constexpr int VM = NV * (RING_NS - 2);
+  constexpr int WAIT = (VM & 15) | ((VM >> 4) << 14) | (7 << 4) | (15 << 8);
+  static_assert(VM < 64, "vmcnt range");
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+  if (nk <= 0) return;
+  OA oa;
+  OB ob;
+  oa.init(A, p.lda, m0, p.K, tid);
+  ob.init(B, p.ldb, n0, p.K, tid);
+  auto issue = [&](int kt, int st) {
+    const int k0 = k_begin + min(kt, nk - 1) * KBKR;
+    char* so = smem + st * STAGE;
+    oa.issue(k0, so, wave);
+    ob.issue(k0, so + A_BYTES, wave);
+  };
+  auto stage_barrier = [&]() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(WAIT);
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  };
+#pragma unroll
+  for (int j = 0; j < RING_NS - 1; ++j) issue(j, j);
+  stage_barrier();  // stage 0 has landed
+  i32x8_t fa[2][TM], fb[2][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i) fa[0][i] = OA::frag8(smem, wm * WM + i * 32, lane);
+#pragma unroll
+  for (int j = 0; j < TN; ++j) fb[0][j] = OB::frag8(smem + A_BYTES, wn * WN + j * 32, lane);
+  int cur = 0;
+  for (int kt = 0; kt < nk; ++kt) {
+    // stage kt + 3 into the slot of stage kt - 1 (read before the last barrier)
+    issue(kt + RING_NS - 1, (kt + RING_NS - 1) % RING_NS);
+    stage_barrier();  // stage kt + 1 has landed
+    const char* na = smem + ((kt + 1) % RING_NS) * STAGE;
+#pragma unroll
+    for (int i = 0; i < TM; ++i) fa[cur ^ 1][i] = OA::frag8(na, wm * WM + i * 32, lane);
+#pragma unroll
+    for (int j = 0; j < TN; ++j) fb[cur ^ 1][j] = OB::frag8(na + A_BYTES, wn * WN + j * 32, lane);
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb[cur][j], fa[cur][i], acc[i][j], f8_fmt_b(F8),
+                                                                    f8_fmt_a(F8), 0, 127, 0, 127);
+    cur ^= 1;
+  }
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xF70);
+  asm volatile("" ::: "memory");
+}
+
 // ---------------------------------------------------------------------------
 // the kernel
 // ---------------------------------------------------------------------------
@@ -664,14 +745,16 @@ __global__ void __launch_bounds__((Cfg<BM, BN>::NT), 1) gemm_kernel(GemmArgs p) 
 
   const bool fast = (m0 + BM <= p.M) && (n0 + BN <= p.N) && (p.K % KBK == 0);
   if constexpr (F8 == 0) {
-    if (fast && ring_fits(p, BM, BN, AK, BKC))
+    if (fast && ring_fits(p, BM, BN, AK, BKC, 2))
       mainloop_ring<BM, BN, AK, BKC>(p, A, B, m0, n0, kt0 * KBK, nk * (KBK / RING_KBK), smem, tid, acc);
     else if (fast)
       mainloop<BM, BN, AK, BKC, false, F8>(p, A, B, m0, n0, kt0, nk, smem, tid, acc);
     else
       mainloop<BM, BN, AK, BKC, true, F8>(p, A, B, m0, n0, kt0, nk, smem, tid, acc);
   } else {
-    if (fast)
+    if (fast && ring_fits(p, BM, BN, AK, BKC, 1))
+      mainloop_ring_f8<BM, BN, F8>(p, A, B, m0, n0, kt0 * KBK, nk * (KBK / RING_RB), smem, tid, acc);
+    else if (fast)
       mainloop<BM, BN, AK, BKC, false, F8>(p, A, B, m0, n0, kt0, nk, smem, tid, acc);
     else
       mainloop<BM, BN, AK, BKC, true, F8>(p, A, B, m0, n0, kt0, nk, smem, tid, acc);
