@@ -251,10 +251,10 @@ extern "C" gpt_status gpt_op_quantize_fp8(const void* x, int32_t x_dtype, int64_
   if (fmt != GPT_FP8_E4M3 && fmt != GPT_FP8_E5M2) FAIL(GPT_ERR_UNSUPPORTED, "unknown fp8 format");
   if ((rows % 16) || (cols % 16)) FAIL(GPT_ERR_INVALID_ARG, "rows and cols must be multiples of 16");
   if ((long long)rows * cols / 4 >= (1LL << 31)) FAIL(GPT_ERR_INVALID_ARG, "tensor too large");
-  if (ldx < cols || (ldx % 4)) FAIL(GPT_ERR_INVALID_ARG, "ldx must be >= cols and a multiple of 4");
-  if (q && (ldq < cols || (ldq % 4))) FAIL(GPT_ERR_INVALID_ARG, "ldq must be >= cols and a multiple of 4");
+  if (ldx < cols || (ldx % 8)) FAIL(GPT_ERR_INVALID_ARG, "ldx must be >= cols and a multiple of 8");
+  if (q && (ldq < cols || (ldq % 8))) FAIL(GPT_ERR_INVALID_ARG, "ldq must be >= cols and a multiple of 8");
   if (qt && (ldqt < rows || (ldqt % 16))) FAIL(GPT_ERR_INVALID_ARG, "ldqt must be >= rows and a multiple of 16");
-  if (((uintptr_t)x & (x_dtype == GPT_DTYPE_F32 ? 15 : 7)) || ((uintptr_t)q & 3) || ((uintptr_t)qt & 15))
+  if (((uintptr_t)x & 15) || ((uintptr_t)q & 7) || ((uintptr_t)qt & 15))
     FAIL(GPT_ERR_INVALID_ARG, "misaligned pointer");
   TRY(quantize_fp8(x, x_dtype == GPT_DTYPE_F32, ldx, rows, cols, fmt, partial, scale, q, ldq, qt, ldqt, S(stream)));
   return GPT_OK;

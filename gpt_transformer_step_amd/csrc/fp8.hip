@@ -156,6 +156,86 @@ __global__ void __launch_bounds__(256) fp8_quant_kernel(const void* __restrict__
   }
 }
 
+// 128 x 128 tile per block; thread t owns the 8 x 8 block at rows 8 (t / 16),
+// columns 8 (t % 16): 16-byte loads (a wave covers four 256-byte row
+// segments), 8-byte code stores, and the transposed codes through LDS,
+// written as 16-byte row chunks.  rows % 16 == 0 and cols % 16 == 0, so
+// every 8-row or 8-column block lies wholly inside or outside the tensor.
+constexpr int kQT2 = 128;
+constexpr int kLDT2 = kQT2 + 8;  // LDS row (bytes) of the transposed tile, padded against bank conflicts
+
+template <bool F32>
+__device__ __forceinline__ void load8(const void* x, long long idx, float* v) {
+  if constexpr (F32) {
+    const float4 a = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(x) + idx);
+    const float4 b = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(x) + idx + 4);
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+  } else {
+    const uint4 w = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(x) + idx);
+    v[0] = lo_bf(w.x); v[1] = hi_bf(w.x); v[2] = lo_bf(w.y); v[3] = hi_bf(w.y);
+    v[4] = lo_bf(w.z); v[5] = hi_bf(w.z); v[6] = lo_bf(w.w); v[7] = hi_bf(w.w);
+  }
+}
+
+template <bool F32, int FMT>
+__global__ void __launch_bounds__(256) fp8_quant128_kernel(const void* __restrict__ x, long long ldx, int rows,
+                                                          int cols, const float* __restrict__ scale,
+                                                          uint8_t* __restrict__ q, long long ldq,
+                                                          uint8_t* __restrict__ qt, long long ldqt) {
+  __shared__ __attribute__((aligned(16))) uint8_t tile[kQT2 * kLDT2];
+  const int t = threadIdx.x;
+  const int r0 = blockIdx.y * kQT2, c0 = blockIdx.x * kQT2;
+  const int rb = 8 * (t >> 4), cb = 8 * (t & 15);
+  const float s = scale[0];
+  const float fm = fmax_of(FMT);
+  const bool in = (r0 + rb < rows) && (c0 + cb < cols);
+  uint2 rw[8];  // codes of row i, columns 0..7
+  if (in) {
+    float v[8][8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) load8<F32>(x, (long long)(r0 + rb + i) * ldx + c0 + cb, v[i]);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v[i][j] = fminf(fmaxf(v[i][j] * s, -fm), fm);
+      rw[i] = make_uint2(cvt2<FMT>(v[i][0], v[i][1]) | (cvt2<FMT>(v[i][2], v[i][3]) << 16),
+                         cvt2<FMT>(v[i][4], v[i][5]) | (cvt2<FMT>(v[i][6], v[i][7]) << 16));
+    }
+    if (q) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) *reinterpret_cast<uint2*>(q + (long long)(r0 + rb + i) * ldq + c0 + cb) = rw[i];
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) rw[i] = make_uint2(0u, 0u);
+  }
+  if (!qt) return;  // launch-uniform
+  // column j of the 8 x 8 block (rows rb .. rb+7) into row cb + j of the transposed tile
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    uint32_t lo = 0, hi = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t wi = j < 4 ? rw[i].x : rw[i].y, wj = j < 4 ? rw[i + 4].x : rw[i + 4].y;
+      lo |= ((wi >> (8 * (j & 3))) & 0xffu) << (8 * i);
+      hi |= ((wj >> (8 * (j & 3))) & 0xffu) << (8 * i);
+    }
+    *reinterpret_cast<uint2*>(tile + (cb + j) * kLDT2 + rb) = make_uint2(lo, hi);
+  }
+  __syncthreads();
+  // row c of the transposed tile = column c0 + c of x: 128 codes in 8 chunks of 16
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int idx = t + 256 * k;
+    const int c = idx >> 3, seg = 16 * (idx & 7);
+    if (c0 + c < cols && r0 + seg < rows) {
+      const uint2* src = reinterpret_cast<const uint2*>(tile + c * kLDT2 + seg);
+      const uint2 a = src[0], b = src[1];
+      *reinterpret_cast<uint4*>(qt + (long long)(c0 + c) * ldqt + r0 + seg) = make_uint4(a.x, a.y, b.x, b.y);
+    }
+  }
+}
+
 }  // namespace
 
 int fp8_partials(long long rows, long long cols) {
@@ -179,8 +259,8 @@ int launch_fp8_amax_scale(const void* x, int is_f32, long long ldx, int rows, in
 int launch_fp8_quant(const void* x, int is_f32, long long ldx, int rows, int cols, int fmt, const float* scale,
                      uint8_t* q, long long ldq, uint8_t* qt, long long ldqt, hipStream_t s) {
   if (rows <= 0 || cols <= 0) return 0;
-  dim3 grid((cols + kQT - 1) / kQT, (rows + kQT - 1) / kQT);
-#define GS_Q(F, M) hipLaunchKernelGGL((fp8_quant_kernel<F, M>), grid, dim3(256), 0, s, x, ldx, rows, cols, scale, q, ldq, qt, ldqt)
+  dim3 grid((cols + kQT2 - 1) / kQT2, (rows + kQT2 - 1) / kQT2);
+#define GS_Q(F, M) hipLaunchKernelGGL((fp8_quant128_kernel<F, M>), grid, dim3(256), 0, s, x, ldx, rows, cols, scale, q, ldq, qt, ldqt)
   if (is_f32) {
     if (fmt) GS_Q(true, 1); else GS_Q(true, 0);
   } else {

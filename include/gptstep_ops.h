@@ -48,8 +48,8 @@ enum { GPT_FP8_E4M3 = 0, GPT_FP8_E5M2 = 1 };
  * q (nullable): codes [rows, cols] with leading dimension ldq;
  * qt (nullable): the same codes transposed, [cols, rows], leading dimension ldqt.
  * partial: device fp32 scratch of gpt_fp8_partials(rows, cols) floats.
- * Needs rows % 16 == 0, cols % 16 == 0, rows*cols < 2^33, ldx % 4 == 0,
- * ldq % 4 == 0, ldqt % 16 == 0; x 16-byte aligned (fp32) or 8-byte (bf16). */
+ * Needs rows % 16 == 0, cols % 16 == 0, rows*cols < 2^33, ldx % 8 == 0,
+ * ldq % 8 == 0, ldqt % 16 == 0; x and qt 16-byte aligned, q 8-byte aligned. */
 int32_t gpt_fp8_partials(int32_t rows, int32_t cols);
 gpt_status gpt_op_quantize_fp8(const void* x, int32_t x_dtype, int64_t ldx, int32_t rows, int32_t cols,
                                int32_t fmt, float* scale, uint8_t* q, int64_t ldq, uint8_t* qt,
