@@ -22,9 +22,6 @@ namespace gs {
 
 namespace {
 
-constexpr int kQT = 64;        // quantiser tile: 64 x 64 elements, 256 threads of 4 x 4
-constexpr int kLDT = kQT + 4;  // LDS row (bytes) of the transposed tile, padded against bank conflicts
-
 __device__ __forceinline__ float fmax_of(int fmt) { return fmt ? 57344.f : 448.f; }
 
 template <bool F32>
@@ -109,51 +106,6 @@ template <int FMT>
 __device__ __forceinline__ uint32_t cvt2(float a, float b) {
   if constexpr (FMT == 0) return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false) & 0xffffu;
   else return (uint32_t)__builtin_amdgcn_cvt_pk_bf8_f32(a, b, 0, false) & 0xffffu;
-}
-
-// One 64 x 64 tile per block; thread t owns the 4 x 4 block at rows
-// 4 (t / 16), columns 4 (t % 16).  rows % 16 == 0 and cols % 16 == 0.
-template <bool F32, int FMT>
-__global__ void __launch_bounds__(256) fp8_quant_kernel(const void* __restrict__ x, long long ldx, int rows, int cols,
-                                                       const float* __restrict__ scale, uint8_t* __restrict__ q,
-                                                       long long ldq, uint8_t* __restrict__ qt, long long ldqt) {
-  __shared__ __attribute__((aligned(16))) uint8_t tile[kQT * kLDT];
-  const int t = threadIdx.x;
-  const int r0 = blockIdx.y * kQT, c0 = blockIdx.x * kQT;
-  const int rb = 4 * (t >> 4), cb = 4 * (t & 15);
-  const float s = scale[0];
-  const float fm = fmax_of(FMT);
-  const bool in = (r0 + rb < rows) && (c0 + cb < cols);
-  uint32_t rw[4] = {0u, 0u, 0u, 0u};  // row words: codes of row i, columns 0..3
-  if (in) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      float v[4];
-      load4<F32>(x, (long long)(r0 + rb + i) * ldx + c0 + cb, v);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) v[j] = fminf(fmaxf(v[j] * s, -fm), fm);
-      rw[i] = cvt2<FMT>(v[0], v[1]) | (cvt2<FMT>(v[2], v[3]) << 16);
-    }
-    if (q) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) *reinterpret_cast<uint32_t*>(q + (long long)(r0 + rb + i) * ldq + c0 + cb) = rw[i];
-    }
-  }
-  if (!qt) return;
-  // column words: codes of column j, rows 0..3, into the transposed tile
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const uint32_t cw = ((rw[0] >> (8 * j)) & 0xffu) | (((rw[1] >> (8 * j)) & 0xffu) << 8) |
-                        (((rw[2] >> (8 * j)) & 0xffu) << 16) | (((rw[3] >> (8 * j)) & 0xffu) << 24);
-    *reinterpret_cast<uint32_t*>(tile + (cb + j) * kLDT + rb) = cw;
-  }
-  __syncthreads();
-  // row c of the transposed tile = column c0 + c of x: 64 codes, 16 per thread
-  const int c = t >> 2, seg = 16 * (t & 3);
-  if (c0 + c < cols && r0 + seg < rows) {
-    const uint32_t* src = reinterpret_cast<const uint32_t*>(tile + c * kLDT + seg);
-    *reinterpret_cast<uint4*>(qt + (long long)(c0 + c) * ldqt + r0 + seg) = make_uint4(src[0], src[1], src[2], src[3]);
-  }
 }
 
 // 128 x 128 tile per block; thread t owns the 8 x 8 block at rows 8 (t / 16),
