@@ -29,8 +29,10 @@
 //     lane's accumulators hold one output row and groups of 4 consecutive
 //     columns: stores are 8/16-byte vectors and row reductions (the
 //     cross-entropy epilogue) stay inside a lane pair.
-//   * Workgroup ids are remapped so each of the 8 XCDs walks a contiguous
-//     range of tiles, rasterised in groups of 8 row tiles for L2 reuse.
+//   * Workgroup ids (over the whole grid: tiles x batch x k-splits) are
+//     remapped so each of the 8 XCDs walks a contiguous range of the
+//     (batch, split, tile) order, tiles rasterised in groups of 8 row tiles
+//     for L2 reuse.
 
 #pragma once
 
@@ -51,6 +53,9 @@ constexpr int stage_k(int f8) { return f8 ? 128 : 64; }
 // Workgroup shape per tile size: 256x256 tiles use 8 waves (two per SIMD, so
 // one wave's LDS waits overlap the other's MFMAs), 128x128 tiles use 4.  The
 // waves form a (NT/128) x 2 grid; each wave owns 64 rows and BN/2 columns.
+// (Four 128x128 waves, one per SIMD, read a third less LDS per MFMA but
+// measured slower here: a lone wave per SIMD leaves the fragment-read and
+// barrier latencies exposed.)
 template <int BM, int BN>
 struct Cfg {
   static constexpr int NT = BM == 256 ? 512 : 256;
@@ -566,10 +571,14 @@ __device__ __forceinline__ void mainloop_ring(const GemmArgs& p, const char* A, 
   using OA = RingOperand<BM, AK, NT>;
   using OB = RingOperand<BN, BKC, NT>;
   constexpr int NV = OA::NL + OB::NL;
-  constexpr int VM = NV * (RING_NS - 2);
+  // mid-stage wait: stage kt + 1 has landed while the RING_NS - 3 stages
+  // issued after it may still be in flight
+  constexpr int VM = NV * (RING_NS - 3);
   constexpr int WAIT = (VM & 15) | ((VM >> 4) << 14) | (7 << 4) | (15 << 8);
+  constexpr int VM0 = NV * (RING_NS - 2);  // prologue: stage 0 has landed
+  constexpr int WAIT0 = (VM0 & 15) | ((VM0 >> 4) << 14) | (7 << 4) | (15 << 8);
   static_assert(RING_NS * STAGE <= 2 * (BM + BN) * 128, "ring exceeds the LDS of the general loop");
-  static_assert(VM < 64, "vmcnt range");
+  static_assert(VM0 < 64, "vmcnt range");
   const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
   if (nk <= 0) return;
@@ -577,7 +586,7 @@ __device__ __forceinline__ void mainloop_ring(const GemmArgs& p, const char* A, 
   OB ob;
   oa.init(A, p.lda, m0, p.K, tid);
   ob.init(B, p.ldb, n0, p.K, tid);
-  // stage kt (clamped to the last: the trailing re-loads land in stages that
+  // stage kt (clamped to the last: the trailing re-loads land in slots that
   // are never read again) into ring slot st
   auto issue = [&](int kt, int st) {
     const int k0 = k_begin + min(kt, nk - 1) * RING_KBK;
@@ -585,15 +594,12 @@ __device__ __forceinline__ void mainloop_ring(const GemmArgs& p, const char* A, 
     oa.issue(k0, so, wave);
     ob.issue(k0, so + A_BYTES, wave);
   };
-  auto stage_barrier = [&]() {
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_waitcnt(WAIT);
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-  };
 #pragma unroll
   for (int j = 0; j < RING_NS - 1; ++j) issue(j, j);
-  stage_barrier();  // stage 0 has landed
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(WAIT0);
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
 
   bf16x8_t fa[2][TM], fb[2][TN];
 #pragma unroll
@@ -601,12 +607,15 @@ __device__ __forceinline__ void mainloop_ring(const GemmArgs& p, const char* A, 
 #pragma unroll
   for (int j = 0; j < TN; ++j) fb[0][j] = OB::frag(smem + A_BYTES, wn * WN + j * 32, 0, lane);
 
+  // One wave per SIMD, so the loop hides its own LDS latency: the barrier
+  // sits between the two k-steps of a stage, and each k-step's MFMAs run
+  // while the fragments of the next k-step load.  Slot safety: the slot
+  // refilled after the barrier of stage kt held stage kt - 1, whose last
+  // fragments every wave consumed (k-step 1 MFMAs of kt - 1) before that
+  // barrier.
   for (int kt = 0; kt < nk; ++kt) {
     const char* sa = smem + (kt % RING_NS) * STAGE;
     const char* sb = sa + A_BYTES;
-    // stage kt + 3 into the slot read during stage kt - 1
-    issue(kt + RING_NS - 1, (kt + RING_NS - 1) % RING_NS);
-    // k-step 0 with the fragments of k-step 1 loading
 #pragma unroll
     for (int i = 0; i < TM; ++i) fa[1][i] = OA::frag(sa, wm * WM + i * 32, 1, lane);
 #pragma unroll
@@ -616,17 +625,21 @@ __device__ __forceinline__ void mainloop_ring(const GemmArgs& p, const char* A, 
 #pragma unroll
       for (int j = 0; j < TN; ++j)
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[0][j], fa[0][i], acc[i][j], 0, 0, 0);
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-      for (int j = 0; j < TN; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[1][j], fa[1][i], acc[i][j], 0, 0, 0);
-    stage_barrier();  // stage kt + 1 has landed; every wave is done with stage kt
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(WAIT);  // stage kt + 1 has landed (this wave's loads)
+    __builtin_amdgcn_s_barrier();      // ... and every wave's; stage kt - 1 is free
+    asm volatile("" ::: "memory");
+    issue(kt + RING_NS - 1, (kt + RING_NS - 1) % RING_NS);
     const char* na = smem + ((kt + 1) % RING_NS) * STAGE;
 #pragma unroll
     for (int i = 0; i < TM; ++i) fa[0][i] = OA::frag(na, wm * WM + i * 32, 0, lane);
 #pragma unroll
     for (int j = 0; j < TN; ++j) fb[0][j] = OB::frag(na + A_BYTES, wn * WN + j * 32, 0, lane);
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[1][j], fa[1][i], acc[i][j], 0, 0, 0);
   }
   // drain the trailing loads before the LDS is reused by the epilogue
   asm volatile("" ::: "memory");
@@ -636,7 +649,9 @@ __device__ __forceinline__ void mainloop_ring(const GemmArgs& p, const char* A, 
 
 // fp8 interior tiles on the same ring: a stage holds 64 codes of k per row,
 // one MFMA k-step.  The stage's MFMAs are issued after the barrier that
-// releases the next stage, so they overlap that stage's fragment reads.
+// releases the next stage, so they overlap that stage's fragment reads; the
+// slot refilled after that barrier held the stage whose MFMAs every wave
+// issued before it.
 template <int BM, int BN, int F8>
 __device__ __forceinline__ void mainloop_ring_f8(const GemmArgs& p, const char* A, const char* B, int m0, int n0,
                                                  int k_begin, int nk, char* smem, int tid,
@@ -648,9 +663,9 @@ __device__ __forceinline__ void mainloop_ring_f8(const GemmArgs& p, const char* 
   using OA = RingOperand<BM, true, NT, 1>;
   using OB = RingOperand<BN, true, NT, 1>;
   constexpr int NV = OA::NL + OB::NL;
-  constexpr int VM = NV * (RING_NS - 2);
-  constexpr int WAIT = (VM & 15) | ((VM >> 4) << 14) | (7 << 4) | (15 << 8);
-  static_assert(VM < 64, "vmcnt range");
+  constexpr int VM = NV * (RING_NS - 3);   // stage kt + 1 has landed
+  constexpr int VM0 = NV * (RING_NS - 2);  // prologue: stage 0 has landed
+  static_assert(VM0 < 64, "vmcnt range");
   const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
   if (nk <= 0) return;
@@ -664,37 +679,44 @@ __device__ __forceinline__ void mainloop_ring_f8(const GemmArgs& p, const char* 
     oa.issue(k0, so, wave);
     ob.issue(k0, so + A_BYTES, wave);
   };
-  auto stage_barrier = [&]() {
+  auto stage_barrier = [&](auto vm) {
+    constexpr int V = decltype(vm)::value;
     asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_waitcnt(WAIT);
+    __builtin_amdgcn_s_waitcnt((V & 15) | ((V >> 4) << 14) | (7 << 4) | (15 << 8));
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
   };
 #pragma unroll
   for (int j = 0; j < RING_NS - 1; ++j) issue(j, j);
-  stage_barrier();  // stage 0 has landed
+  stage_barrier(std::integral_constant<int, VM0>());
   i32x8_t fa[2][TM], fb[2][TN];
 #pragma unroll
   for (int i = 0; i < TM; ++i) fa[0][i] = OA::frag8(smem, wm * WM + i * 32, lane);
 #pragma unroll
   for (int j = 0; j < TN; ++j) fb[0][j] = OB::frag8(smem + A_BYTES, wn * WN + j * 32, lane);
-  int cur = 0;
-  for (int kt = 0; kt < nk; ++kt) {
-    // stage kt + 3 into the slot of stage kt - 1 (read before the last barrier)
-    issue(kt + RING_NS - 1, (kt + RING_NS - 1) % RING_NS);
-    stage_barrier();  // stage kt + 1 has landed
+  // one stage: the next stage's fragments into (na_, nb_) while the MFMAs
+  // of this one run on (ca, cb); two stages per trip keep the fragment
+  // buffers statically indexed (registers, not private memory)
+  auto step = [&](int kt, const i32x8_t (&ca)[TM], const i32x8_t (&cb)[TN], i32x8_t (&na_)[TM],
+                  i32x8_t (&nb_)[TN]) {
+    stage_barrier(std::integral_constant<int, VM>());
+    issue(kt + RING_NS - 1, (kt + RING_NS - 1) % RING_NS);  // into the slot of stage kt - 1
     const char* na = smem + ((kt + 1) % RING_NS) * STAGE;
 #pragma unroll
-    for (int i = 0; i < TM; ++i) fa[cur ^ 1][i] = OA::frag8(na, wm * WM + i * 32, lane);
+    for (int i = 0; i < TM; ++i) na_[i] = OA::frag8(na, wm * WM + i * 32, lane);
 #pragma unroll
-    for (int j = 0; j < TN; ++j) fb[cur ^ 1][j] = OB::frag8(na + A_BYTES, wn * WN + j * 32, lane);
+    for (int j = 0; j < TN; ++j) nb_[j] = OB::frag8(na + A_BYTES, wn * WN + j * 32, lane);
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
       for (int j = 0; j < TN; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb[cur][j], fa[cur][i], acc[i][j], f8_fmt_b(F8),
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(cb[j], ca[i], acc[i][j], f8_fmt_b(F8),
                                                                     f8_fmt_a(F8), 0, 127, 0, 127);
-    cur ^= 1;
+  };
+  for (int kt = 0; kt < nk; kt += 2) {
+    step(kt, fa[0], fb[0], fa[1], fb[1]);
+    if (kt + 1 >= nk) break;
+    step(kt + 1, fa[1], fb[1], fa[0], fb[0]);
   }
   asm volatile("" ::: "memory");
   __builtin_amdgcn_s_waitcnt(0xF70);
@@ -714,7 +736,14 @@ __global__ void __launch_bounds__((Cfg<BM, BN>::NT), 1) gemm_kernel(GemmArgs p) 
   const int wm = wave >> 1, wn = wave & 1;
 
   const int tiles_m = (p.M + BM - 1) / BM, tiles_n = (p.N + BN - 1) / BN;
-  const int lid = xcd_remap(blockIdx.x, gridDim.x);
+  // The dispatcher hands workgroup x + gx y to XCD (x + gx y) % 8; remapping
+  // that linear id gives each XCD a contiguous run of (batch/split, tile)
+  // order, so the blocks resident on one XCD share a k range and neighbouring
+  // row and column panels in its L2.
+  const int nblk = gridDim.x * gridDim.y;
+  const int lin = xcd_remap(blockIdx.x + gridDim.x * blockIdx.y, nblk);
+  const int yb = lin / gridDim.x;
+  const int lid = lin - yb * gridDim.x;
   constexpr int GM = 8;
   const int group = lid / (GM * tiles_n);
   const int first_m = group * GM;
@@ -724,7 +753,7 @@ __global__ void __launch_bounds__((Cfg<BM, BN>::NT), 1) gemm_kernel(GemmArgs p) 
   const int tile_n = in_group / gsz;
   const int m0 = tile_m * BM, n0 = tile_n * BN;
 
-  const int bi = blockIdx.y / p.k_split, split = blockIdx.y % p.k_split;
+  const int bi = yb / p.k_split, split = yb % p.k_split;
   constexpr int KBK = stage_k(F8);
   const int nk_all = (p.K + KBK - 1) / KBK;
   const int nk_per = (nk_all + p.k_split - 1) / p.k_split;
@@ -772,52 +801,51 @@ __global__ void __launch_bounds__((Cfg<BM, BN>::NT), 1) gemm_kernel(GemmArgs p) 
   }
 
   // ----------------------------- epilogue ---------------------------------
-  if constexpr (EPI == EPI_QKV) {
-    // Each wave owns 128 columns = one head (tiles are 256 wide).  Lane row m
-    // holds head features e = j*32 + 8g + 4lh + r; the rotation partner
-    // e + 64 sits in the same lane at j + 2, the other half of the head in
-    // lane ^ 32.  The rotated, normalised values replace the accumulators and
-    // are stored by the coalesced path below.
-    static_assert(WN == 128, "EPI_QKV needs 128 columns per wave");
-    const int nb = n0 + wn * WN;  // first column of this wave's head
-    const int dmodel = p.n_head * 128;
-    const int nkv = p.n_kv_head ? p.n_kv_head : p.n_head;
-    if (nb < dmodel + nkv * 128) {  // q or k head (wave-uniform)
+  // Rotary embedding + RMS normalisation of q / k heads, applied to row block
+  // i of the accumulators just before it is staged (one row block at a time
+  // keeps the working set in registers).  Each wave owns 128 columns = one
+  // head (tiles are 256 wide).  Lane row m holds head features
+  // e = j*32 + 8g + 4lh + r; the rotation partner e + 64 sits in the same
+  // lane at j + 2, the other half of the head in lane ^ 32.
+  auto qkv_rows = [&](int i) {
+    if constexpr (EPI == EPI_QKV) {
+      static_assert(WN == 128, "EPI_QKV needs 128 columns per wave");
+      const int nb = n0 + wn * WN;  // first column of this wave's head
+      const int dmodel = p.n_head * 128;
+      const int nkv = p.n_kv_head ? p.n_kv_head : p.n_head;
+      if (nb >= dmodel + nkv * 128) return;  // v head (wave-uniform)
+      const int m = m0 + wm * WM + i * 32 + lr;
+      const int t = (m < p.M) ? m % p.row_T : 0;
+      float ss = 0.f;
 #pragma unroll
-      for (int i = 0; i < TM; ++i) {
-        const int m = m0 + wm * WM + i * 32 + lr;
-        const int t = (m < p.M) ? m % p.row_T : 0;
-        float ss = 0.f;
+      for (int j = 0; j < 2; ++j)
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+        for (int g = 0; g < 4; ++g) {
+          const int e = j * 32 + 8 * g + 4 * lh;
+          const float4 c4 = *reinterpret_cast<const float4*>(p.rope + (long long)t * 64 + e);
+          const float4 s4 = *reinterpret_cast<const float4*>(p.rope + (long long)p.row_T * 64 + (long long)t * 64 + e);
+          const float cc[4] = {c4.x, c4.y, c4.z, c4.w}, sn[4] = {s4.x, s4.y, s4.z, s4.w};
 #pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const int e = j * 32 + 8 * g + 4 * lh;
-            const float4 c4 = *reinterpret_cast<const float4*>(p.rope + (long long)t * 64 + e);
-            const float4 s4 = *reinterpret_cast<const float4*>(p.rope + (long long)p.row_T * 64 + (long long)t * 64 + e);
-            const float cc[4] = {c4.x, c4.y, c4.z, c4.w}, sn[4] = {s4.x, s4.y, s4.z, s4.w};
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              const float x1 = acc[i][j][4 * g + r], x2 = acc[i][j + 2][4 * g + r];
-              const float y1 = x1 * cc[r] - x2 * sn[r], y2 = x1 * sn[r] + x2 * cc[r];
-              acc[i][j][4 * g + r] = y1;
-              acc[i][j + 2][4 * g + r] = y2;
-              ss += y1 * y1 + y2 * y2;
-            }
+          for (int r = 0; r < 4; ++r) {
+            const float x1 = acc[i][j][4 * g + r], x2 = acc[i][j + 2][4 * g + r];
+            const float y1 = x1 * cc[r] - x2 * sn[r], y2 = x1 * sn[r] + x2 * cc[r];
+            acc[i][j][4 * g + r] = y1;
+            acc[i][j + 2][4 * g + r] = y2;
+            ss += y1 * y1 + y2 * y2;
           }
-        ss += __shfl_xor(ss, 32, 64);
-        const float rr = 1.0f / sqrtf(ss / 128.f + 1e-6f);
-#pragma unroll
-        for (int j = 0; j < TN; ++j)
-#pragma unroll
-          for (int e = 0; e < 16; ++e) acc[i][j][e] *= rr;
-        if (lh == 0 && m < p.M) {
-          if (nb < dmodel) p.part[(long long)m * p.n_head + nb / 128] = rr;
-          else p.zt[(long long)m * nkv + (nb - dmodel) / 128] = rr;
         }
+      ss += __shfl_xor(ss, 32, 64);
+      const float rr = 1.0f / sqrtf(ss / 128.f + 1e-6f);
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[i][j][e] *= rr;
+      if (lh == 0 && m < p.M) {
+        if (nb < dmodel) p.part[(long long)m * p.n_head + nb / 128] = rr;
+        else p.zt[(long long)m * nkv + (nb - dmodel) / 128] = rr;
       }
     }
-  }
+  };
   if constexpr (EPI == EPI_CE_FWD) {
     // Per row: max and sum of exp over this wave's WN columns, merged with
     // the partner lane (lane ^ 32) that holds the other half of the columns.
@@ -890,6 +918,7 @@ __global__ void __launch_bounds__((Cfg<BM, BN>::NT), 1) gemm_kernel(GemmArgs p) 
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
       if (i > 0) fetch_aux(i);
+      qkv_rows(i);
 #pragma unroll
       for (int j = 0; j < TN; ++j)
 #pragma unroll
