@@ -53,9 +53,9 @@ constexpr int stage_k(int f8) { return f8 ? 128 : 64; }
 // Workgroup shape per tile size: 256x256 tiles use 8 waves (two per SIMD, so
 // one wave's LDS waits overlap the other's MFMAs), 128x128 tiles use 4.  The
 // waves form a (NT/128) x 2 grid; each wave owns 64 rows and BN/2 columns.
-// (Four 128x128 waves, one per SIMD, read a third less LDS per MFMA but
-// measured slower here: a lone wave per SIMD leaves the fragment-read and
-// barrier latencies exposed.)
+// (Four 128x128 waves, one per SIMD, read a third less LDS per MFMA and leave
+// registers for a deeper operand prefetch, but measured slower here: a lone
+// wave per SIMD leaves every fragment-read and barrier latency exposed.)
 template <int BM, int BN>
 struct Cfg {
   static constexpr int NT = BM == 256 ? 512 : 256;
@@ -443,25 +443,20 @@ __device__ __forceinline__ void mainloop(const GemmArgs& p, const void* A, const
 }
 
 // ---------------------------------------------------------------------------
-// bf16 interior tiles: a ring of RING_NS LDS stages of 64 bytes of k per row
-// (32 bf16, two MFMA k-steps), loaded RING_NS - 1 stages ahead, so a stage's
-// load latency (1-2 us under load) is covered by three stages of MFMAs
-// instead of one.  The ring takes the same LDS as the two 128-byte stages of
-// the general loop.  Loads are direct buffer -> LDS loads issued as
-// instructions the compiler does not model (with the builtin it makes every
-// LDS read wait for all loads in flight); the loop carries its own waits: at
-// the end of a stage, the next stage's loads have landed (vmcnt) and every
-// wave is done with this stage (barrier).  Per-lane byte offsets are loop
-// invariant; the k position goes in the scalar offset.
+// Interior tiles: two LDS blocks of 128 bytes of k per operand row (64 bf16
+// or 128 fp8 codes; the layouts of the general loop), double buffered, loaded
+// by direct buffer -> LDS loads issued as instructions the compiler does not
+// model (with the builtin it makes every LDS read wait for all loads in
+// flight); the loop carries its own waits.  Whole 128-byte rows per block
+// matter: a wave's 16-byte-per-lane load then covers whole cache lines, while
+// 64-byte half rows fetch each line from L2 twice and stall the address unit
+// on the L1.  Per-lane byte offsets are loop invariant; the k position goes
+// in the scalar offset.
 // ---------------------------------------------------------------------------
-constexpr int RING_NS = 4;
-constexpr int RING_RB = 64;   // bytes of k per operand row per stage
-constexpr int RING_KBK = 32;  // bf16 k per stage
-
 typedef int v4i_t __attribute__((ext_vector_type(4)));
 
 // buffer resource (raw bytes, range num_bytes) from wave-uniform values
-__device__ __forceinline__ v4i_t ring_rsrc(const void* base, long long num_bytes) {
+__device__ __forceinline__ v4i_t dma_rsrc(const void* base, long long num_bytes) {
   const uint64_t a = reinterpret_cast<uint64_t>(base);
   v4i_t r;
   r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
@@ -474,26 +469,24 @@ __device__ __forceinline__ v4i_t ring_rsrc(const void* base, long long num_bytes
 // 16 bytes per lane from rsrc at voff + soff into LDS at lds + 16 lane (lds
 // wave-uniform).  No register results; "memory" keeps LDS accesses in place;
 // M0 is set here only and nothing compiled in the GEMM kernel reads it.
-__device__ __forceinline__ void ring_dma16(v4i_t rsrc, int voff, int soff, uint32_t lds) {
+__device__ __forceinline__ void dma16(v4i_t rsrc, int voff, int soff, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %3\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %0, %2 offen lds"
                :: "s"(rsrc), "v"(voff), "s"(soff), "s"(lds) : "memory");
 }
 
-// k-contiguous ring tile: R rows of 64 bytes; the four 16-byte chunks of a row
-// XOR-swizzled by (r >> 2) & 3, so the 16 rows of a fragment read at one
-// logical chunk fill 16 distinct 16-byte bank groups
-__device__ __forceinline__ int ring_off_k(int r, int kc) { return r * RING_RB + ((kc ^ ((r >> 2) & 3)) << 4); }
-
-// True when every byte offset of the ring's loads fits 31 bits.
-__device__ __forceinline__ bool ring_fits(const GemmArgs& p, int BM, int BN, bool AK, bool BKC, int ES) {
+// True when every byte offset of the block loads fits 31 bits.
+__device__ __forceinline__ bool dma_fits(const GemmArgs& p, int BM, int BN, bool AK, bool BKC, int ES) {
   const long long ea = AK ? (long long)BM * p.lda * ES : (long long)p.K * p.lda * ES;
   const long long eb = BKC ? (long long)BN * p.ldb * ES : (long long)p.K * p.ldb * ES;
   return ea < 0x7fffffffLL && eb < 0x7fffffffLL;
 }
 
-template <int R, bool KC, int NT, int ES = 2>
-struct RingOperand {
-  static constexpr int NL = R * 4 / NT;  // 16-byte loads per thread per stage
+// The loads of one operand tile (R rows x 128 bytes of k) into the LDS
+// layout TileLoader reads fragments from: lane l of wave w in round i fills
+// the 16-byte slot NT i + 64 w + l.
+template <int R, bool KC, int NT, int ES>
+struct DmaOperand {
+  static constexpr int NL = R * 8 / NT;  // 16-byte loads per thread per block
   static_assert(ES == 2 || KC, "fp8 operands are k-contiguous");
   v4i_t rsrc;
   int voff[NL];
@@ -501,17 +494,17 @@ struct RingOperand {
 
   __device__ __forceinline__ void init(const char* X, long long ld, int row0, int K, int tid) {
     if constexpr (KC) {
-      rsrc = ring_rsrc(X + (long long)row0 * ld * ES, (long long)R * ld * ES);
+      rsrc = dma_rsrc(X + (long long)row0 * ld * ES, (long long)R * ld * ES);
       kstep = ES;
     } else {
-      rsrc = ring_rsrc(X + (long long)row0 * 2, (long long)K * ld * 2);
+      rsrc = dma_rsrc(X + (long long)row0 * 2, (long long)K * ld * 2);
       kstep = ld * 2;
     }
 #pragma unroll
     for (int i = 0; i < NL; ++i) {
       const int slot = tid + NT * i;
       if constexpr (KC) {
-        const int r = slot >> 2, kc = (slot & 3) ^ ((r >> 2) & 3);
+        const int r = slot >> 3, kc = (slot & 7) ^ ((r >> 1) & 7);
         voff[i] = (int)(((long long)r * ld + kc * (16 / ES)) * ES);
       } else {
         const int b = slot * 16;
@@ -521,64 +514,36 @@ struct RingOperand {
       }
     }
   }
-  // the stage at k element k0 into the LDS tile at lds (lane l of wave w in
-  // round i fills slot NT i + 64 w + l)
-  __device__ __forceinline__ void issue(int k0, char* lds, int wave) const {
-    const int soff = __builtin_amdgcn_readfirstlane((int)(k0 * kstep));
-#pragma unroll
-    for (int i = 0; i < NL; ++i)
-      ring_dma16(rsrc, voff[i], soff,
-                 (uint32_t)(size_t)(__attribute__((address_space(3))) char*)(lds + (NT * i + 64 * wave) * 16));
-  }
-  // fp8 fragment of rows r0 .. r0+31 (the stage's 64 codes): lane l holds row
-  // r0 + l % 32 and the codes of chunks 2 (l / 32) + {0, 1}; both operands use
-  // the same assignment, which is all the MFMA needs
-  __device__ __forceinline__ static i32x8_t frag8(const char* lds, int r0, int lane) {
-    typedef int i32x4_t __attribute__((ext_vector_type(4)));
-    const int r = r0 + (lane & 31), c = (lane >> 5) * 2;
-    const i32x4_t a = *reinterpret_cast<const i32x4_t*>(lds + ring_off_k(r, c));
-    const i32x4_t b = *reinterpret_cast<const i32x4_t*>(lds + ring_off_k(r, c + 1));
-    i32x8_t f;
-    f[0] = a[0]; f[1] = a[1]; f[2] = a[2]; f[3] = a[3];
-    f[4] = b[0]; f[5] = b[1]; f[6] = b[2]; f[7] = b[3];
-    return f;
-  }
-  // MFMA fragment of rows r0 .. r0+31, k-step ks (0 or 1) of a stage
-  __device__ __forceinline__ static bf16x8_t frag(const char* lds, int r0, int ks, int lane) {
-    if constexpr (KC) {
-      return *reinterpret_cast<const bf16x8_t*>(lds + ring_off_k(r0 + (lane & 31), ks * 2 + (lane >> 5)));
-    } else {
-      const int g = lane >> 4, m = lane & 15;
-      const int i = r0 + 16 * (g & 1) + 4 * (m & 3);
-      const int k = ks * 16 + 8 * (g >> 1) + (m >> 2);
-      const v4s_t a = ds_read_tr(lds, lds_off_mn<R>(k, i));
-      const v4s_t b = ds_read_tr(lds, lds_off_mn<R>(k + 4, i));
-      bf16x8_t f;
-      f[0] = a[0]; f[1] = a[1]; f[2] = a[2]; f[3] = a[3];
-      f[4] = b[0]; f[5] = b[1]; f[6] = b[2]; f[7] = b[3];
-      return f;
-    }
-  }
 };
 
-template <int BM, int BN, bool AK, bool BKC>
-__device__ __forceinline__ void mainloop_ring(const GemmArgs& p, const char* A, const char* B, int m0, int n0,
-                                              int k_begin, int nk, char* smem, int tid,
-                                              f32x16_t (&acc)[Cfg<BM, BN>::TM][Cfg<BM, BN>::TN]) {
+// Block kt of the loop: barrier (block kt landed, every wave done reading
+// block kt - 1), then walk the block's k-steps with the fragments of each
+// k-step read while the MFMAs of the previous one run; the last k-step's
+// MFMAs run after the next barrier, covering the first fragment reads of the
+// next block.  The loads of block kt + 1 (into the other buffer) are spread
+// over the first DMA_PHASES k-steps, between the two halves of an MFMA batch
+// (slightly faster than one burst after the barrier, which backs up the
+// address unit; spreading them further leaves the last ones too little time).
+constexpr int DMA_PHASES = 2;
+template <int BM, int BN, bool AK, bool BKC, int F8>
+__device__ __forceinline__ void mainloop_dma(const GemmArgs& p, const char* A, const char* B, int m0, int n0,
+                                             int kt0, int nk, char* smem, int tid,
+                                             f32x16_t (&acc)[Cfg<BM, BN>::TM][Cfg<BM, BN>::TN]) {
   constexpr int NT = Cfg<BM, BN>::NT;
   constexpr int WM = Cfg<BM, BN>::WM, WN = Cfg<BM, BN>::WN, TM = Cfg<BM, BN>::TM, TN = Cfg<BM, BN>::TN;
-  constexpr int A_BYTES = BM * RING_RB, STAGE = (BM + BN) * RING_RB;
-  using OA = RingOperand<BM, AK, NT>;
-  using OB = RingOperand<BN, BKC, NT>;
-  constexpr int NV = OA::NL + OB::NL;
-  // mid-stage wait: stage kt + 1 has landed while the RING_NS - 3 stages
-  // issued after it may still be in flight
-  constexpr int VM = NV * (RING_NS - 3);
-  constexpr int WAIT = (VM & 15) | ((VM >> 4) << 14) | (7 << 4) | (15 << 8);
-  constexpr int VM0 = NV * (RING_NS - 2);  // prologue: stage 0 has landed
-  constexpr int WAIT0 = (VM0 & 15) | ((VM0 >> 4) << 14) | (7 << 4) | (15 << 8);
-  static_assert(RING_NS * STAGE <= 2 * (BM + BN) * 128, "ring exceeds the LDS of the general loop");
-  static_assert(VM0 < 64, "vmcnt range");
+  constexpr int ES = F8 ? 1 : 2;
+  constexpr int KBK = stage_k(F8);                // k elements per block
+  constexpr int KS = F8 ? 2 : 4;                  // MFMA k-steps per block
+  constexpr int A_BYTES = BM * 128, STAGE = (BM + BN) * 128;
+  using OA = DmaOperand<BM, AK, NT, ES>;
+  using OB = DmaOperand<BN, BKC, NT, ES>;
+  using LA = TileLoader<BM, AK, NT, ES>;
+  using LB = TileLoader<BN, BKC, NT, ES>;
+  using FragT = typename std::conditional<F8 != 0, i32x8_t, bf16x8_t>::type;
+  constexpr int NV = OA::NL + OB::NL;                                   // loads per thread per block
+  constexpr int PH = DMA_PHASES < KS ? DMA_PHASES : KS;                 // k-steps the loads spread over
+  constexpr int PER = (NV + PH - 1) / PH;                               // loads per k-step
+  static_assert(KS % 2 == 0, "fragment buffers alternate within a block");
   const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
   if (nk <= 0) return;
@@ -586,138 +551,98 @@ __device__ __forceinline__ void mainloop_ring(const GemmArgs& p, const char* A, 
   OB ob;
   oa.init(A, p.lda, m0, p.K, tid);
   ob.init(B, p.ldb, n0, p.K, tid);
-  // stage kt (clamped to the last: the trailing re-loads land in slots that
-  // are never read again) into ring slot st
-  auto issue = [&](int kt, int st) {
-    const int k0 = k_begin + min(kt, nk - 1) * RING_KBK;
-    char* so = smem + st * STAGE;
-    oa.issue(k0, so, wave);
-    ob.issue(k0, so + A_BYTES, wave);
+  // loads [PER ph, PER (ph + 1)) of block kt (clamped: the trailing re-load
+  // lands in a buffer never read again)
+  auto issue = [&](int kt, int ph) {
+    const int k0 = (kt0 + min(kt, nk - 1)) * KBK;
+    char* so = smem + (kt & 1) * STAGE;
+    const int soa = __builtin_amdgcn_readfirstlane((int)(k0 * oa.kstep));
+    const int sob = __builtin_amdgcn_readfirstlane((int)(k0 * ob.kstep));
+#pragma unroll
+    for (int d = 0; d < NV; ++d) {
+      if (d / PER != ph) continue;
+      if (d < OA::NL)
+        dma16(oa.rsrc, oa.voff[d], soa,
+              (uint32_t)(size_t)(__attribute__((address_space(3))) char*)(so + (NT * d + 64 * wave) * 16));
+      else
+        dma16(ob.rsrc, ob.voff[d - OA::NL], sob,
+              (uint32_t)(size_t)(__attribute__((address_space(3))) char*)(so + A_BYTES +
+                                                                          (NT * (d - OA::NL) + 64 * wave) * 16));
+    }
   };
+  auto issue_all = [&](int kt) {
 #pragma unroll
-  for (int j = 0; j < RING_NS - 1; ++j) issue(j, j);
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_waitcnt(WAIT0);
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-
-  bf16x8_t fa[2][TM], fb[2][TN];
-#pragma unroll
-  for (int i = 0; i < TM; ++i) fa[0][i] = OA::frag(smem, wm * WM + i * 32, 0, lane);
-#pragma unroll
-  for (int j = 0; j < TN; ++j) fb[0][j] = OB::frag(smem + A_BYTES, wn * WN + j * 32, 0, lane);
-
-  // One wave per SIMD, so the loop hides its own LDS latency: the barrier
-  // sits between the two k-steps of a stage, and each k-step's MFMAs run
-  // while the fragments of the next k-step load.  Slot safety: the slot
-  // refilled after the barrier of stage kt held stage kt - 1, whose last
-  // fragments every wave consumed (k-step 1 MFMAs of kt - 1) before that
-  // barrier.
-  for (int kt = 0; kt < nk; ++kt) {
-    const char* sa = smem + (kt % RING_NS) * STAGE;
-    const char* sb = sa + A_BYTES;
-#pragma unroll
-    for (int i = 0; i < TM; ++i) fa[1][i] = OA::frag(sa, wm * WM + i * 32, 1, lane);
-#pragma unroll
-    for (int j = 0; j < TN; ++j) fb[1][j] = OB::frag(sb, wn * WN + j * 32, 1, lane);
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-      for (int j = 0; j < TN; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[0][j], fa[0][i], acc[i][j], 0, 0, 0);
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_waitcnt(WAIT);  // stage kt + 1 has landed (this wave's loads)
-    __builtin_amdgcn_s_barrier();      // ... and every wave's; stage kt - 1 is free
-    asm volatile("" ::: "memory");
-    issue(kt + RING_NS - 1, (kt + RING_NS - 1) % RING_NS);
-    const char* na = smem + ((kt + 1) % RING_NS) * STAGE;
-#pragma unroll
-    for (int i = 0; i < TM; ++i) fa[0][i] = OA::frag(na, wm * WM + i * 32, 0, lane);
-#pragma unroll
-    for (int j = 0; j < TN; ++j) fb[0][j] = OB::frag(na + A_BYTES, wn * WN + j * 32, 0, lane);
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-      for (int j = 0; j < TN; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[1][j], fa[1][i], acc[i][j], 0, 0, 0);
-  }
-  // drain the trailing loads before the LDS is reused by the epilogue
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_waitcnt(0xF70);
-  asm volatile("" ::: "memory");
-}
-
-// fp8 interior tiles on the same ring: a stage holds 64 codes of k per row,
-// one MFMA k-step.  The stage's MFMAs are issued after the barrier that
-// releases the next stage, so they overlap that stage's fragment reads; the
-// slot refilled after that barrier held the stage whose MFMAs every wave
-// issued before it.
-template <int BM, int BN, int F8>
-__device__ __forceinline__ void mainloop_ring_f8(const GemmArgs& p, const char* A, const char* B, int m0, int n0,
-                                                 int k_begin, int nk, char* smem, int tid,
-                                                 f32x16_t (&acc)[Cfg<BM, BN>::TM][Cfg<BM, BN>::TN]) {
-  constexpr int NT = Cfg<BM, BN>::NT;
-  constexpr int WM = Cfg<BM, BN>::WM, WN = Cfg<BM, BN>::WN, TM = Cfg<BM, BN>::TM, TN = Cfg<BM, BN>::TN;
-  constexpr int A_BYTES = BM * RING_RB, STAGE = (BM + BN) * RING_RB;
-  constexpr int KBKR = RING_RB;  // fp8 codes of k per stage
-  using OA = RingOperand<BM, true, NT, 1>;
-  using OB = RingOperand<BN, true, NT, 1>;
-  constexpr int NV = OA::NL + OB::NL;
-  constexpr int VM = NV * (RING_NS - 3);   // stage kt + 1 has landed
-  constexpr int VM0 = NV * (RING_NS - 2);  // prologue: stage 0 has landed
-  static_assert(VM0 < 64, "vmcnt range");
-  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave >> 1, wn = wave & 1;
-  if (nk <= 0) return;
-  OA oa;
-  OB ob;
-  oa.init(A, p.lda, m0, p.K, tid);
-  ob.init(B, p.ldb, n0, p.K, tid);
-  auto issue = [&](int kt, int st) {
-    const int k0 = k_begin + min(kt, nk - 1) * KBKR;
-    char* so = smem + st * STAGE;
-    oa.issue(k0, so, wave);
-    ob.issue(k0, so + A_BYTES, wave);
+    for (int ph = 0; ph < PH; ++ph) issue(kt, ph);
   };
-  auto stage_barrier = [&](auto vm) {
-    constexpr int V = decltype(vm)::value;
+  auto barrier = [&]() {
     asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_waitcnt((V & 15) | ((V >> 4) << 14) | (7 << 4) | (15 << 8));
+    __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0): block landed, this wave's reads done
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
   };
+  FragT f0a[TM], f0b[TN], f1a[TM], f1b[TN];
+  auto read = [&](const char* st, int ks, FragT (&fa)[TM], FragT (&fb)[TN]) {
 #pragma unroll
-  for (int j = 0; j < RING_NS - 1; ++j) issue(j, j);
-  stage_barrier(std::integral_constant<int, VM0>());
-  i32x8_t fa[2][TM], fb[2][TN];
+    for (int i = 0; i < TM; ++i) {
+      if constexpr (F8) fa[i] = LA::frag8(st, wm * WM + i * 32, ks, lane);
+      else fa[i] = LA::frag(st, wm * WM + i * 32, ks, lane);
+    }
 #pragma unroll
-  for (int i = 0; i < TM; ++i) fa[0][i] = OA::frag8(smem, wm * WM + i * 32, lane);
-#pragma unroll
-  for (int j = 0; j < TN; ++j) fb[0][j] = OB::frag8(smem + A_BYTES, wn * WN + j * 32, lane);
-  // one stage: the next stage's fragments into (na_, nb_) while the MFMAs
-  // of this one run on (ca, cb); two stages per trip keep the fragment
-  // buffers statically indexed (registers, not private memory)
-  auto step = [&](int kt, const i32x8_t (&ca)[TM], const i32x8_t (&cb)[TN], i32x8_t (&na_)[TM],
-                  i32x8_t (&nb_)[TN]) {
-    stage_barrier(std::integral_constant<int, VM>());
-    issue(kt + RING_NS - 1, (kt + RING_NS - 1) % RING_NS);  // into the slot of stage kt - 1
-    const char* na = smem + ((kt + 1) % RING_NS) * STAGE;
-#pragma unroll
-    for (int i = 0; i < TM; ++i) na_[i] = OA::frag8(na, wm * WM + i * 32, lane);
-#pragma unroll
-    for (int j = 0; j < TN; ++j) nb_[j] = OB::frag8(na + A_BYTES, wn * WN + j * 32, lane);
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-      for (int j = 0; j < TN; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(cb[j], ca[i], acc[i][j], f8_fmt_b(F8),
-                                                                    f8_fmt_a(F8), 0, 127, 0, 127);
+    for (int j = 0; j < TN; ++j) {
+      if constexpr (F8) fb[j] = LB::frag8(st + A_BYTES, wn * WN + j * 32, ks, lane);
+      else fb[j] = LB::frag(st + A_BYTES, wn * WN + j * 32, ks, lane);
+    }
   };
-  for (int kt = 0; kt < nk; kt += 2) {
-    step(kt, fa[0], fb[0], fa[1], fb[1]);
-    if (kt + 1 >= nk) break;
-    step(kt + 1, fa[1], fb[1], fa[0], fb[0]);
+  // one MFMA batch (a k-step) with the loads of phase ph of block kt between
+  // its halves (ph < 0: none)
+  auto mfma = [&](const FragT (&fa)[TM], const FragT (&fb)[TN], int kt, int ph) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      if (i == TM / 2 && ph >= 0 && ph < PH) {
+        __builtin_amdgcn_sched_barrier(0);
+        issue(kt, ph);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        if constexpr (F8)
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb[j], fa[i], acc[i][j], f8_fmt_b(F8),
+                                                                      f8_fmt_a(F8), 0, 127, 0, 127);
+        else
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[j], fa[i], acc[i][j], 0, 0, 0);
+      }
+    }
+  };
+  // k-steps 1 .. KS-1 of block st: read k-step ks while the MFMAs of ks - 1
+  // run (scheduling fences keep each read batch ahead of the MFMA batch that
+  // covers it; left alone, the scheduler sinks reads next to their uses)
+  auto body = [&](const char* st, int kt) {
+#pragma unroll
+    for (int ks = 1; ks < KS; ++ks) {
+      if (ks & 1) read(st, ks, f1a, f1b);
+      else read(st, ks, f0a, f0b);
+      __builtin_amdgcn_sched_barrier(0);
+      if (ks & 1) mfma(f0a, f0b, kt + 1, ks);
+      else mfma(f1a, f1b, kt + 1, ks);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  issue_all(0);
+  barrier();
+  read(smem, 0, f0a, f0b);
+  issue(1, 0);
+  body(smem, 0);
+  for (int kt = 1; kt < nk; ++kt) {
+    const char* st = smem + (kt & 1) * STAGE;
+    barrier();
+    read(st, 0, f0a, f0b);
+    __builtin_amdgcn_sched_barrier(0);
+    mfma(f1a, f1b, kt + 1, 0);  // last k-step of block kt - 1
+    __builtin_amdgcn_sched_barrier(0);
+    body(st, kt);
   }
+  mfma(f1a, f1b, 0, -1);
+  // drain the trailing loads before the LDS is reused by the epilogue
   asm volatile("" ::: "memory");
   __builtin_amdgcn_s_waitcnt(0xF70);
   asm volatile("" ::: "memory");
@@ -773,21 +698,12 @@ __global__ void __launch_bounds__((Cfg<BM, BN>::NT), 1) gemm_kernel(GemmArgs p) 
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
   const bool fast = (m0 + BM <= p.M) && (n0 + BN <= p.N) && (p.K % KBK == 0);
-  if constexpr (F8 == 0) {
-    if (fast && ring_fits(p, BM, BN, AK, BKC, 2))
-      mainloop_ring<BM, BN, AK, BKC>(p, A, B, m0, n0, kt0 * KBK, nk * (KBK / RING_KBK), smem, tid, acc);
-    else if (fast)
-      mainloop<BM, BN, AK, BKC, false, F8>(p, A, B, m0, n0, kt0, nk, smem, tid, acc);
-    else
-      mainloop<BM, BN, AK, BKC, true, F8>(p, A, B, m0, n0, kt0, nk, smem, tid, acc);
-  } else {
-    if (fast && ring_fits(p, BM, BN, AK, BKC, 1))
-      mainloop_ring_f8<BM, BN, F8>(p, A, B, m0, n0, kt0 * KBK, nk * (KBK / RING_RB), smem, tid, acc);
-    else if (fast)
-      mainloop<BM, BN, AK, BKC, false, F8>(p, A, B, m0, n0, kt0, nk, smem, tid, acc);
-    else
-      mainloop<BM, BN, AK, BKC, true, F8>(p, A, B, m0, n0, kt0, nk, smem, tid, acc);
-  }
+  if (fast && dma_fits(p, BM, BN, AK, BKC, ES))
+    mainloop_dma<BM, BN, AK, BKC, F8>(p, A, B, m0, n0, kt0, nk, smem, tid, acc);
+  else if (fast)
+    mainloop<BM, BN, AK, BKC, false, F8>(p, A, B, m0, n0, kt0, nk, smem, tid, acc);
+  else
+    mainloop<BM, BN, AK, BKC, true, F8>(p, A, B, m0, n0, kt0, nk, smem, tid, acc);
   const int lr = lane & 31, lh = lane >> 5;
   if constexpr (F8 != 0) {
     // dequantise: the codes carry x * s_x, so the product carries s_a * s_b
