@@ -525,16 +525,32 @@ WS ws_layout(const Dims& D) {
 template <class T>
 inline T* at(void* ws, size_t off) { return reinterpret_cast<T*>(reinterpret_cast<char*>(ws) + off); }
 
-// k-splits for a weight-gradient product (small output, long K): enough
-// workgroups to fill the chip; each split writes a partial that a small
-// reduction adds up (no atomics, deterministic)
+// k-splits for a weight-gradient product (small output, long K): each split
+// writes a partial that a small reduction adds up (no atomics,
+// deterministic).  The split count fills the chip's workgroup slots (one
+// 256x256 workgroup per CU, two 128x128 ones) as evenly as possible: the
+// smallest count whose last wave is within 2.5% of the best fill, with 256x256
+// tiles whenever some count up to 20 reaches the 512 workgroups that select
+// them, and at least 2048 k per split.
 inline int wgrad_splits(int M, int N, int K) {
   const long long t256 = (long long)((M + 255) / 256) * ((N + 255) / 256);
   if (t256 >= 256) return 1;
-  long long ks = (512 + t256 - 1) / t256;
-  ks = std::min<long long>(ks, std::max(1, K / 2048));
-  ks = std::min<long long>(ks, 16);
-  return (int)std::max<long long>(ks, 1);
+  const long long t128 = (long long)((M + 127) / 128) * ((N + 127) / 128);
+  const int kmax = std::max(1, K / 2048);
+  const bool big = M >= 256 && N >= 256 && t256 * 20 >= 512;
+  const long long tiles = big ? t256 : t128, slots = big ? 256 : 512;
+  const int lo = big ? (int)((512 + t256 - 1) / t256) : 1;
+  const int hi = std::min(big ? 20 : 16, kmax);
+  if (lo > hi) return std::max(1, std::min(kmax, 16));
+  auto fill = [&](int ks) {
+    const long long b = tiles * ks;
+    return (double)b / (double)(((b + slots - 1) / slots) * slots);
+  };
+  double best = 0.0;
+  for (int ks = lo; ks <= hi; ++ks) best = std::max(best, fill(ks));
+  for (int ks = lo; ks <= hi; ++ks)
+    if (fill(ks) >= best - 0.025) return ks;
+  return lo;
 }
 
 inline size_t wgrad_part_elems(int M, int N, int K) {
