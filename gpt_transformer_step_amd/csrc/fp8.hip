@@ -87,16 +87,28 @@ __global__ void __launch_bounds__(256) amax_partial_kernel(const void* __restric
   if (threadIdx.x == 0) partial[blockIdx.x] = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
 }
 
-__global__ void __launch_bounds__(256) fp8_scale_kernel(const float* __restrict__ partial, long long np, int fmt,
-                                                       float* __restrict__ scale) {
-  float m = 0.f;
-  for (long long i = threadIdx.x; i < np; i += 256) m = fmaxf(m, partial[i]);
-  m = wave_max(m);
-  __shared__ float red[4];
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+// One workgroup of 1024 threads: the partial maxima (up to a few tens of
+// thousands) are read with eight independent loads in flight per thread, so
+// the reduction costs a few load latencies rather than one per 256 values.
+constexpr int kScaleNT = 1024;
+__global__ void __launch_bounds__(kScaleNT) fp8_scale_kernel(const float* __restrict__ partial, long long np,
+                                                            int fmt, float* __restrict__ scale) {
+  float m[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  long long i = threadIdx.x;
+  for (; i + 7 * kScaleNT < np; i += 8 * kScaleNT) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u) m[u] = fmaxf(m[u], partial[i + u * kScaleNT]);
+  }
+  for (; i < np; i += kScaleNT) m[0] = fmaxf(m[0], partial[i]);
+  float mm = fmaxf(fmaxf(fmaxf(m[0], m[1]), fmaxf(m[2], m[3])), fmaxf(fmaxf(m[4], m[5]), fmaxf(m[6], m[7])));
+  mm = wave_max(mm);
+  __shared__ float red[kScaleNT / 64];
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = mm;
   __syncthreads();
   if (threadIdx.x == 0) {
-    const float amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    float amax = 0.f;
+#pragma unroll
+    for (int w = 0; w < kScaleNT / 64; ++w) amax = fmaxf(amax, red[w]);
     scale[0] = amax > 0.f ? fmax_of(fmt) / amax : 1.f;
   }
 }
@@ -203,7 +215,7 @@ int launch_fp8_amax_scale(const void* x, int is_f32, long long ldx, int rows, in
   else
     hipLaunchKernelGGL(amax_partial_kernel<false>, dim3(np), dim3(256), 0, s, x, ldx, rows, cols, partial);
   GS_LAUNCH_CHECK("amax_partial");
-  hipLaunchKernelGGL(fp8_scale_kernel, dim3(1), dim3(256), 0, s, partial, (long long)np, fmt, scale);
+  hipLaunchKernelGGL(fp8_scale_kernel, dim3(1), dim3(kScaleNT), 0, s, partial, (long long)np, fmt, scale);
   GS_LAUNCH_CHECK("fp8_scale");
   return 0;
 }
@@ -233,7 +245,7 @@ int quantize_fp8(const void* x, int is_f32, long long ldx, int rows, int cols, i
 int quantize_fp8_partials(const void* x, int is_f32, long long ldx, int rows, int cols, int fmt,
                           const float* partial, long long np, float* scale, uint8_t* q, long long ldq, uint8_t* qt,
                           long long ldqt, hipStream_t s) {
-  hipLaunchKernelGGL(fp8_scale_kernel, dim3(1), dim3(256), 0, s, partial, np, fmt, scale);
+  hipLaunchKernelGGL(fp8_scale_kernel, dim3(1), dim3(kScaleNT), 0, s, partial, np, fmt, scale);
   GS_LAUNCH_CHECK("fp8_scale");
   return launch_fp8_quant(x, is_f32, ldx, rows, cols, fmt, scale, q, ldq, qt, ldqt, s);
 }
