@@ -321,20 +321,25 @@ attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, 
 // ============================================================================
 // backward
 // ============================================================================
-// delta[b,h,t] = sum_e dout * out.  One wave per (token, head).
+// delta[b,h,t] = sum_e dout * out.  16 lanes per (token, head), 8 features
+// (16 bytes of each operand) per lane.
 __global__ void __launch_bounds__(256) attn_bwd_pre_kernel(const uint16_t* __restrict__ out,
                                                            const uint16_t* __restrict__ dout, long long ld_out,
                                                            float* __restrict__ delta, int H, int T, long long NH) {
-  const int lane = threadIdx.x & 63;
-  const long long w = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int j = threadIdx.x & 15;
+  const long long w = (long long)blockIdx.x * 16 + (threadIdx.x >> 4);
   if (w >= NH) return;
   const long long n = w / H;
   const int h = (int)(w % H);
-  const uint32_t ow = reinterpret_cast<const uint32_t*>(out + n * ld_out + h * 128)[lane];
-  const uint32_t dw = reinterpret_cast<const uint32_t*>(dout + n * ld_out + h * 128)[lane];
-  const float s = wave_sum(lo_bf(ow) * lo_bf(dw) + hi_bf(ow) * hi_bf(dw));
+  const uint4 ow = *reinterpret_cast<const uint4*>(out + n * ld_out + h * 128 + 8 * j);
+  const uint4 dw = *reinterpret_cast<const uint4*>(dout + n * ld_out + h * 128 + 8 * j);
+  float s = lo_bf(ow.x) * lo_bf(dw.x) + hi_bf(ow.x) * hi_bf(dw.x) + lo_bf(ow.y) * lo_bf(dw.y) +
+            hi_bf(ow.y) * hi_bf(dw.y) + lo_bf(ow.z) * lo_bf(dw.z) + hi_bf(ow.z) * hi_bf(dw.z) +
+            lo_bf(ow.w) * lo_bf(dw.w) + hi_bf(ow.w) * hi_bf(dw.w);
+#pragma unroll
+  for (int o = 8; o > 0; o >>= 1) s += __shfl_xor(s, o, 64);
   const long long b = n / T, t = n % T;
-  if (lane == 0) delta[(b * H + h) * T + t] = s;
+  if (j == 0) delta[(b * H + h) * T + t] = s;
 }
 
 // ---------------------------------------------------------------------------
@@ -694,7 +699,7 @@ int launch_attn_bwd_part(int part, const uint16_t* q, const uint16_t* k, const u
   const bool gen = Hkv != H || window >= 0;
   if (part == 0) {
     const long long NH = (long long)B * T * H;
-    hipLaunchKernelGGL(attn_bwd_pre_kernel, dim3((unsigned)((NH + 3) / 4)), dim3(256), 0, s, out, dout, ld_out,
+    hipLaunchKernelGGL(attn_bwd_pre_kernel, dim3((unsigned)((NH + 15) / 16)), dim3(256), 0, s, out, dout, ld_out,
                        delta, H, T, NH);
     GS_LAUNCH_CHECK("attn_bwd_pre");
   } else if (part == 1) {
