@@ -221,7 +221,7 @@ struct TileLoader {
 // ---------------------------------------------------------------------------
 template <int EPI>
 __device__ __forceinline__ void epi4(const GemmArgs& p, int bi, int m, int n, const float* v, long long coff,
-                                     float& amx, uint2 aux_w = make_uint2(0, 0)) {
+                                     float& amx) {
   const bool full = (n + 3 < p.N);
   if constexpr (EPI == EPI_F32 || EPI == EPI_RESID || EPI == EPI_F32_ATOMIC) {
     float* C = reinterpret_cast<float*>(p.C) + (long long)bi * p.sC + coff + (long long)m * p.ldc + n;
@@ -257,13 +257,7 @@ __device__ __forceinline__ void epi4(const GemmArgs& p, int bi, int m, int n, co
     }
     if constexpr (EPI == EPI_DRELU2) {
       const uint16_t* a = reinterpret_cast<const uint16_t*>(p.aux) + (long long)bi * p.sAux + (long long)m * p.ldaux + n;
-      if (full) {
-        const uint2 w = aux_w;  // fetched ahead by the caller
-        o[0] *= 2.f * sqrtf(lo_bf(w.x)); o[1] *= 2.f * sqrtf(hi_bf(w.x));
-        o[2] *= 2.f * sqrtf(lo_bf(w.y)); o[3] *= 2.f * sqrtf(hi_bf(w.y));
-      } else {
-        for (int j = 0; j < 4; ++j) o[j] = (n + j < p.N) ? o[j] * 2.f * sqrtf(bf2f(a[j])) : 0.f;
-      }
+      for (int j = 0; j < 4; ++j) o[j] = (n + j < p.N) ? o[j] * 2.f * sqrtf(bf2f(a[j])) : 0.f;
     }
     if constexpr (EPI == EPI_NS_POLY) {
       const float* a = reinterpret_cast<const float*>(p.aux) + (long long)bi * p.sAux + (long long)m * p.ldaux + n;
@@ -323,6 +317,52 @@ __device__ __forceinline__ void epi4(const GemmArgs& p, int bi, int m, int n, co
   }
 }
 
+
+// bf16-output epilogues on 8 consecutive columns n .. n+7 of row m (16-byte
+// stores; C rows and the saved activation 16-byte aligned)
+template <int EPI>
+__device__ __forceinline__ void epi8(const GemmArgs& p, int bi, int m, int n, const float* v, float& amx,
+                                     uint4 aux_w) {
+  static_assert(EPI == EPI_BF16 || EPI == EPI_RELU2 || EPI == EPI_DRELU2, "bf16 store epilogues");
+  const bool full = (n + 7 < p.N);
+  uint16_t* C = reinterpret_cast<uint16_t*>(p.C) + (long long)bi * p.sC + (long long)m * p.ldc + n;
+  float o[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) o[j] = v[j];
+  if constexpr (EPI == EPI_RELU2) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) { const float r = fmaxf(o[j], 0.f); o[j] = r * r; }
+  }
+  if constexpr (EPI == EPI_DRELU2) {
+    if (full) {
+      const uint32_t w[4] = {aux_w.x, aux_w.y, aux_w.z, aux_w.w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        o[2 * j] *= 2.f * sqrtf(lo_bf(w[j]));
+        o[2 * j + 1] *= 2.f * sqrtf(hi_bf(w[j]));
+      }
+    } else {
+      const uint16_t* a = reinterpret_cast<const uint16_t*>(p.aux) + (long long)bi * p.sAux + (long long)m * p.ldaux + n;
+      for (int j = 0; j < 8; ++j) o[j] = (n + j < p.N) ? o[j] * 2.f * sqrtf(bf2f(a[j])) : 0.f;
+    }
+  }
+  if (full) {
+    const uint4 w = make_uint4(pack_bf2(o[0], o[1]), pack_bf2(o[2], o[3]), pack_bf2(o[4], o[5]), pack_bf2(o[6], o[7]));
+    *reinterpret_cast<uint4*>(C) = w;
+    if (p.amax) {
+      const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) amx = fmaxf(amx, fmaxf(fabsf(lo_bf(ww[j])), fabsf(hi_bf(ww[j]))));
+    }
+  } else {
+    for (int j = 0; j < 8; ++j)
+      if (n + j < p.N) {
+        const uint16_t b = f2bf(o[j]);
+        C[j] = b;
+        if (p.amax) amx = fmaxf(amx, fabsf(bf2f(b)));
+      }
+  }
+}
 
 // ---------------------------------------------------------------------------
 // K loop: double-buffered LDS stages, fragments double-buffered in registers,
@@ -814,17 +854,25 @@ __global__ void __launch_bounds__((Cfg<BM, BN>::NT), 1) gemm_kernel(GemmArgs p) 
     // barrier, so their latency overlaps the staging instead of being paid
     // every few outputs
     constexpr int NIT = 32 * CH / 64;
-    uint2 auxw[NIT];
+    // bf16 stores go out 8 columns (16 bytes) per lane when rows are 16-byte
+    // aligned: half the store instructions of the 4-column path
+    constexpr bool W8E = EPI == EPI_BF16 || EPI == EPI_RELU2 || EPI == EPI_DRELU2 || EPI == EPI_QKV;
+    constexpr int CH2 = CH / 2, NIT8 = 32 * CH2 / 64;
+    const bool w8 = W8E && (p.ldc % 8 == 0) && (EPI != EPI_DRELU2 || p.ldaux % 8 == 0);
+    // (the ReLU^2-derivative epilogue always takes the 8-column path: its
+    // launches keep C and the saved activation 16-byte aligned, and the 4-column
+    // path reads the activation per element)
+    uint4 auxw8[NIT8];
     auto fetch_aux = [&](int i) {
       if constexpr (EPI == EPI_DRELU2) {
         const uint16_t* ab = reinterpret_cast<const uint16_t*>(p.aux) + (long long)bi * p.sAux;
 #pragma unroll
-        for (int it = 0; it < NIT; ++it) {
+        for (int it = 0; it < NIT8; ++it) {
           const int q = it * 64 + lane;
-          const int m = m0 + wm * WM + i * 32 + q / CH;
-          const int n = n0 + wn * WN + (q % CH) * 4;
-          auxw[it] = (m < p.M && n + 3 < p.N) ? *reinterpret_cast<const uint2*>(ab + (long long)m * p.ldaux + n)
-                                               : make_uint2(0, 0);
+          const int m = m0 + wm * WM + i * 32 + q / CH2;
+          const int n = n0 + wn * WN + (q % CH2) * 8;
+          auxw8[it] = (w8 && m < p.M && n + 7 < p.N) ? *reinterpret_cast<const uint4*>(ab + (long long)m * p.ldaux + n)
+                                                      : make_uint4(0, 0, 0, 0);
         }
       }
     };
@@ -847,16 +895,34 @@ __global__ void __launch_bounds__((Cfg<BM, BN>::NT), 1) gemm_kernel(GemmArgs p) 
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      if (w8) {
+        if constexpr (W8E) {
 #pragma unroll
-      for (int it = 0; it < NIT; ++it) {
-        const int q = it * 64 + lane;
-        const int rr = q / CH, cc = q % CH;
-        const float4 v4 = *reinterpret_cast<const float4*>(wbuf + rr * ROWB + ((cc ^ (rr & 15)) << 4));
-        const int m = m0 + wm * WM + i * 32 + rr;
-        const int n = n0 + wn * WN + cc * 4;
-        if (m < p.M && n < p.N) {
-          const float v[4] = {v4.x, v4.y, v4.z, v4.w};
-          epi4<(EPI == EPI_QKV ? (int)EPI_BF16 : EPI)>(p, bi, m, n, v, coff, amx, auxw[it]);
+          for (int it = 0; it < NIT8; ++it) {
+            const int q = it * 64 + lane;
+            const int rr = q / CH2, cc = 2 * (q % CH2);
+            const float4 a4 = *reinterpret_cast<const float4*>(wbuf + rr * ROWB + ((cc ^ (rr & 15)) << 4));
+            const float4 b4 = *reinterpret_cast<const float4*>(wbuf + rr * ROWB + (((cc + 1) ^ (rr & 15)) << 4));
+            const int m = m0 + wm * WM + i * 32 + rr;
+            const int n = n0 + wn * WN + cc * 4;
+            if (m < p.M && n < p.N) {
+              const float v[8] = {a4.x, a4.y, a4.z, a4.w, b4.x, b4.y, b4.z, b4.w};
+              epi8<(EPI == EPI_QKV ? (int)EPI_BF16 : EPI)>(p, bi, m, n, v, amx, auxw8[it]);
+            }
+          }
+        }
+      } else {
+#pragma unroll
+        for (int it = 0; it < NIT; ++it) {
+          const int q = it * 64 + lane;
+          const int rr = q / CH, cc = q % CH;
+          const float4 v4 = *reinterpret_cast<const float4*>(wbuf + rr * ROWB + ((cc ^ (rr & 15)) << 4));
+          const int m = m0 + wm * WM + i * 32 + rr;
+          const int n = n0 + wn * WN + cc * 4;
+          if (m < p.M && n < p.N) {
+            const float v[4] = {v4.x, v4.y, v4.z, v4.w};
+            epi4<(EPI == EPI_QKV ? (int)EPI_BF16 : EPI)>(p, bi, m, n, v, coff, amx);
+          }
         }
       }
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
