@@ -221,7 +221,7 @@ struct TileLoader {
 // ---------------------------------------------------------------------------
 template <int EPI>
 __device__ __forceinline__ void epi4(const GemmArgs& p, int bi, int m, int n, const float* v, long long coff,
-                                     float& amx) {
+                                     float& amx, bool have_c = false, float4 cpre = make_float4(0.f, 0.f, 0.f, 0.f)) {
   const bool full = (n + 3 < p.N);
   if constexpr (EPI == EPI_F32 || EPI == EPI_RESID || EPI == EPI_F32_ATOMIC) {
     float* C = reinterpret_cast<float*>(p.C) + (long long)bi * p.sC + coff + (long long)m * p.ldc + n;
@@ -232,7 +232,7 @@ __device__ __forceinline__ void epi4(const GemmArgs& p, int bi, int m, int n, co
     } else if (full) {
       float4 o = make_float4(v[0], v[1], v[2], v[3]);
       if (EPI == EPI_RESID || p.beta != 0.f) {
-        const float4 c = *reinterpret_cast<const float4*>(C);
+        const float4 c = have_c ? cpre : *reinterpret_cast<const float4*>(C);
         const float b = (EPI == EPI_RESID) ? 1.f : p.beta;
         o.x += b * c.x; o.y += b * c.y; o.z += b * c.z; o.w += b * c.w;
       }
@@ -283,7 +283,7 @@ __device__ __forceinline__ void epi4(const GemmArgs& p, int bi, int m, int n, co
     if (full) {
       o[0] = v[0]; o[1] = v[1]; o[2] = v[2]; o[3] = v[3];
       if (EPI == EPI_NS_UPD) {
-        const float4 c = *reinterpret_cast<const float4*>(C);
+        const float4 c = have_c ? cpre : *reinterpret_cast<const float4*>(C);
         o[0] += p.beta * c.x; o[1] += p.beta * c.y; o[2] += p.beta * c.z; o[3] += p.beta * c.w;
       }
       *reinterpret_cast<float4*>(C) = make_float4(o[0], o[1], o[2], o[3]);
@@ -876,12 +876,37 @@ __global__ void __launch_bounds__((Cfg<BM, BN>::NT), 1) gemm_kernel(GemmArgs p) 
         }
       }
     };
+    // Epilogues that read C (residual add, NS update, fp32 with beta) fetch a
+    // row block's C chunks in one burst before staging it: read one at a time
+    // between the stores, each load would wait out the stores before it (the
+    // compiler cannot tell the addresses apart)
+    constexpr bool READS_C = EPI == EPI_RESID || EPI == EPI_NS_UPD || EPI == EPI_F32;
+    const bool cread = READS_C && (EPI != EPI_F32 || p.beta != 0.f);
+    float4 cpre[READS_C ? NIT : 1];
+    auto fetch_c = [&](int i) {
+      if constexpr (READS_C) {
+        if (!cread) return;
+        const float* Cb = reinterpret_cast<const float*>(p.C) + (long long)bi * p.sC + coff;
+#pragma unroll
+        for (int it = 0; it < NIT; ++it) {
+          const int q = it * 64 + lane;
+          const int m = m0 + wm * WM + i * 32 + q / CH;
+          const int n = n0 + wn * WN + (q % CH) * 4;
+          cpre[it] = (m < p.M && n + 3 < p.N) ? *reinterpret_cast<const float4*>(Cb + (long long)m * p.ldc + n)
+                                               : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+      }
+    };
     fetch_aux(0);
+    fetch_c(0);
     __syncthreads();  // every wave is done with the operand tiles
     float amx = 0.f;  // max |stored value| of this lane (bf16 epilogues with p.amax)
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
-      if (i > 0) fetch_aux(i);
+      if (i > 0) {
+        fetch_aux(i);
+        fetch_c(i);
+      }
       qkv_rows(i);
 #pragma unroll
       for (int j = 0; j < TN; ++j)
@@ -921,7 +946,10 @@ __global__ void __launch_bounds__((Cfg<BM, BN>::NT), 1) gemm_kernel(GemmArgs p) 
           const int n = n0 + wn * WN + cc * 4;
           if (m < p.M && n < p.N) {
             const float v[4] = {v4.x, v4.y, v4.z, v4.w};
-            epi4<(EPI == EPI_QKV ? (int)EPI_BF16 : EPI)>(p, bi, m, n, v, coff, amx);
+            if constexpr (READS_C)
+              epi4<EPI>(p, bi, m, n, v, coff, amx, cread && n + 3 < p.N, cpre[it]);
+            else
+              epi4<(EPI == EPI_QKV ? (int)EPI_BF16 : EPI)>(p, bi, m, n, v, coff, amx);
           }
         }
       }
