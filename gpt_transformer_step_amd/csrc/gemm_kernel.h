@@ -260,8 +260,12 @@ __device__ __forceinline__ void epi4(const GemmArgs& p, int bi, int m, int n, co
       for (int j = 0; j < 4; ++j) o[j] = (n + j < p.N) ? o[j] * 2.f * sqrtf(bf2f(a[j])) : 0.f;
     }
     if constexpr (EPI == EPI_NS_POLY) {
-      const float* a = reinterpret_cast<const float*>(p.aux) + (long long)bi * p.sAux + (long long)m * p.ldaux + n;
-      for (int j = 0; j < 4; ++j) o[j] = (n + j < p.N) ? o[j] + p.beta * a[j] : 0.f;
+      if (have_c) {
+        o[0] += p.beta * cpre.x; o[1] += p.beta * cpre.y; o[2] += p.beta * cpre.z; o[3] += p.beta * cpre.w;
+      } else {
+        const float* a = reinterpret_cast<const float*>(p.aux) + (long long)bi * p.sAux + (long long)m * p.ldaux + n;
+        for (int j = 0; j < 4; ++j) o[j] = (n + j < p.N) ? o[j] + p.beta * a[j] : 0.f;
+      }
     }
     if (full) {
       const uint2 w = make_uint2(pack_bf2(o[0], o[1]), pack_bf2(o[2], o[3]));
@@ -876,24 +880,32 @@ __global__ void __launch_bounds__((Cfg<BM, BN>::NT), 1) gemm_kernel(GemmArgs p) 
         }
       }
     };
-    // Epilogues that read C (residual add, NS update, fp32 with beta) fetch a
-    // row block's C chunks in one burst before staging it: read one at a time
-    // between the stores, each load would wait out the stores before it (the
-    // compiler cannot tell the addresses apart)
-    constexpr bool READS_C = EPI == EPI_RESID || EPI == EPI_NS_UPD || EPI == EPI_F32;
-    const bool cread = READS_C && (EPI != EPI_F32 || p.beta != 0.f);
+    // Epilogues that read memory per output (C for the residual add, the NS
+    // update and fp32 with beta; the fp32 A of the NS polynomial) fetch a row
+    // block's values in one burst
+    // before staging it: read one at a time between the stores, each load
+    // would wait out the stores before it (the compiler cannot tell the
+    // addresses apart)
+    constexpr bool READS_C = EPI == EPI_RESID || EPI == EPI_NS_UPD || EPI == EPI_F32 || EPI == EPI_NS_POLY;
+    const bool cread = READS_C && (EPI != EPI_F32 || p.beta != 0.f) && (EPI != EPI_NS_POLY || p.ldaux % 4 == 0);
     float4 cpre[READS_C ? NIT : 1];
     auto fetch_c = [&](int i) {
       if constexpr (READS_C) {
         if (!cread) return;
-        const float* Cb = reinterpret_cast<const float*>(p.C) + (long long)bi * p.sC + coff;
 #pragma unroll
         for (int it = 0; it < NIT; ++it) {
           const int q = it * 64 + lane;
           const int m = m0 + wm * WM + i * 32 + q / CH;
           const int n = n0 + wn * WN + (q % CH) * 4;
-          cpre[it] = (m < p.M && n + 3 < p.N) ? *reinterpret_cast<const float4*>(Cb + (long long)m * p.ldc + n)
-                                               : make_float4(0.f, 0.f, 0.f, 0.f);
+          float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
+          if constexpr (EPI == EPI_NS_POLY) {
+            const float* a = reinterpret_cast<const float*>(p.aux) + (long long)bi * p.sAux;
+            if (m < p.M && n + 3 < p.N) x = *reinterpret_cast<const float4*>(a + (long long)m * p.ldaux + n);
+          } else {
+            const float* Cb = reinterpret_cast<const float*>(p.C) + (long long)bi * p.sC + coff;
+            if (m < p.M && n + 3 < p.N) x = *reinterpret_cast<const float4*>(Cb + (long long)m * p.ldc + n);
+          }
+          cpre[it] = x;
         }
       }
     };
