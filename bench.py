@@ -195,6 +195,40 @@ def cpu_baseline(wl, m, seed_ids, seed_w):
                        f"({step_s:.0f} s)")}
 
 
+def ns_standalone(args):
+    """Newton-Schulz alone: normalisation, 5 iterations of A = X^T X,
+    B = b A + c A A, X = a X + X B, and the copy-out, on one matrix."""
+    import torch
+    from gpt_transformer_step_amd import binding as Bd
+    from gpt_transformer_step_amd import inputs
+    dev = torch.device("cuda:0")
+    res = {}
+    for rows, cols in ((1664, 6656), (1664, 1664)):
+        G = torch.from_numpy(inputs.normal_matrix(rows, cols, inputs.SEED_NS)[0]).to(dev)
+        O = torch.empty_like(G)
+        ws = torch.empty(Bd.muon_workspace_size(1, rows, cols), dtype=torch.uint8, device=dev)
+        for _ in range(max(1, args.warmup)):
+            Bd.muon_update(G, NS5, ws, O_out=O)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.steps):
+            Bd.muon_update(G, NS5, ws, O_out=O)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / args.steps
+        s_, l_ = min(rows, cols), max(rows, cols)
+        flops = 5 * (4 * l_ * s_ * s_ + 2 * s_ ** 3)
+        res[f"{rows}x{cols}"] = {"ms": ms, "tflops": flops / ms / 1e9, "frac": flops / (ms * 1e-3) / PEAK_BF16,
+                                 "flops": flops}
+    tot_ms = sum(r["ms"] for r in res.values())
+    tot_fl = sum(r["flops"] for r in res.values())
+    print(json.dumps({"metric": "Newton-Schulz standalone, 5 iterations (TFLOP/s)", "value": tot_fl / tot_ms / 1e9,
+                      "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+                      "higher_is_better": True, "dtype": "bf16", "data": "synthetic: N(0,1) fp32 (seeded PCG64)",
+                      "config": {"workload": "ns-standalone", "shapes": list(res)}, "per_shape": res}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -211,6 +245,9 @@ def main():
     ap.add_argument("--features", default="",
                     help="record-model features: v (value embeddings), s (smear), r (residual scalars), b (backout)")
     ap.add_argument("--breakdown", action="store_true", help="print per-kernel times to stderr")
+    ap.add_argument("--ns-standalone", action="store_true",
+                    help="only time Newton-Schulz (5 iterations, muon_update with no momentum and no apply) on "
+                         "N(0,1) 1664x6656 and 1664x1664 matrices and print one JSON line")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device-to-device copy of BYTES three times and exit (the reference "
                          "for scaling the HBM byte counters of a profiler)")
@@ -224,6 +261,9 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"copy_bytes_read": 4 * n, "copy_bytes_written": 4 * n, "copies": 3}), flush=True)
+        return
+    if args.ns_standalone:
+        ns_standalone(args)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the step runs on a "
