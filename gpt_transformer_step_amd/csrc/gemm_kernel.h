@@ -536,24 +536,28 @@ struct DmaOperand {
   int voff[NL];
   long long kstep;  // bytes per k element along the loaded direction
 
-  __device__ __forceinline__ void init(const char* X, long long ld, int row0, int K, int tid) {
+  // nrows: rows (KC) or elements (MN, a multiple of 8) of the operand from
+  // row0 on; a tile reaching past them re-reads the last valid row / 16-byte
+  // chunk instead (its products land in output rows / columns that are never
+  // stored), so every load stays inside the operand
+  __device__ __forceinline__ void init(const char* X, long long ld, int row0, int nrows, int K, int tid) {
     if constexpr (KC) {
-      rsrc = dma_rsrc(X + (long long)row0 * ld * ES, (long long)R * ld * ES);
+      rsrc = dma_rsrc(X + (long long)row0 * ld * ES, (long long)min(R, nrows) * ld * ES);
       kstep = ES;
     } else {
-      rsrc = dma_rsrc(X + (long long)row0 * 2, (long long)K * ld * 2);
+      rsrc = dma_rsrc(X + (long long)row0 * 2, ((long long)K * ld - row0) * 2);
       kstep = ld * 2;
     }
 #pragma unroll
     for (int i = 0; i < NL; ++i) {
       const int slot = tid + NT * i;
       if constexpr (KC) {
-        const int r = slot >> 3, kc = (slot & 7) ^ ((r >> 1) & 7);
+        const int r = min(slot >> 3, nrows - 1), kc = (slot & 7) ^ (((slot >> 3) >> 1) & 7);
         voff[i] = (int)(((long long)r * ld + kc * (16 / ES)) * ES);
       } else {
         const int b = slot * 16;
         const int k = b / (2 * R), rb = b % (2 * R);
-        const int i_el = (((rb >> 6) ^ (k & 3)) << 5) + ((rb & 63) >> 1);
+        const int i_el = min((((rb >> 6) ^ (k & 3)) << 5) + ((rb & 63) >> 1), nrows - 8);
         voff[i] = (int)(((long long)k * ld + i_el) * 2);
       }
     }
@@ -593,8 +597,8 @@ __device__ __forceinline__ void mainloop_dma(const GemmArgs& p, const char* A, c
   if (nk <= 0) return;
   OA oa;
   OB ob;
-  oa.init(A, p.lda, m0, p.K, tid);
-  ob.init(B, p.ldb, n0, p.K, tid);
+  oa.init(A, p.lda, m0, p.M - m0, p.K, tid);
+  ob.init(B, p.ldb, n0, p.N - n0, p.K, tid);
   // loads [PER ph, PER (ph + 1)) of block kt (clamped: the trailing re-load
   // lands in a buffer never read again)
   auto issue = [&](int kt, int ph) {
@@ -741,10 +745,15 @@ __global__ void __launch_bounds__((Cfg<BM, BN>::NT), 1) gemm_kernel(GemmArgs p) 
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
-  const bool fast = (m0 + BM <= p.M) && (n0 + BN <= p.N) && (p.K % KBK == 0);
+  // the block-load loop takes every tile whose K is whole blocks; a tile
+  // reaching past M or N needs that dimension a multiple of 8 when it is the
+  // contiguous one (16-byte chunks either wholly inside or outside)
+  const bool fast = (p.K % KBK == 0) && (m0 + BM <= p.M || AK || p.M % 8 == 0) &&
+                    (n0 + BN <= p.N || BKC || p.N % 8 == 0);
+  const bool interior = (m0 + BM <= p.M) && (n0 + BN <= p.N) && (p.K % KBK == 0);
   if (fast && dma_fits(p, BM, BN, AK, BKC, ES))
     mainloop_dma<BM, BN, AK, BKC, F8>(p, A, B, m0, n0, kt0, nk, smem, tid, acc);
-  else if (fast)
+  else if (interior)
     mainloop<BM, BN, AK, BKC, false, F8>(p, A, B, m0, n0, kt0, nk, smem, tid, acc);
   else
     mainloop<BM, BN, AK, BKC, true, F8>(p, A, B, m0, n0, kt0, nk, smem, tid, acc);

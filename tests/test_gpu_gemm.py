@@ -37,6 +37,13 @@ CASES = [
     (1024, 768, 512, 1, 0, 1),
     (1024, 768, 520, 1, 1, 1),
     (777, 1030, 64, 1, 0, 0),
+    # ragged 256-wide tiles whose K is whole blocks (the block-load loop with
+    # clamped rows / chunks), every layout; and ragged 128-wide tiles
+    (4992, 1664, 128, 4, 0, 0),
+    (4992, 1664, 128, 4, 0, 1),
+    (4992, 1664, 128, 4, 1, 0),
+    (4992, 1664, 128, 4, 1, 1),
+    (1000, 1064, 128, 1, 1, 1),
 ]
 
 
