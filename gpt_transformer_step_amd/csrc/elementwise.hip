@@ -100,7 +100,10 @@ __global__ void __launch_bounds__(256) embed_bwd_kernel(const int* __restrict__ 
   }
 }
 
-// h = x * r, r = 1/sqrt(mean(x^2) + eps); one wave per row
+// h = x * r, r = 1/sqrt(mean(x^2) + eps); one wave per row.  MC = float4
+// chunks per lane (ceil(d / 256)): a compile-time count keeps the row in as
+// few registers as it needs, so more waves fit per SIMD.
+template <int MC>
 __global__ void __launch_bounds__(256) rmsnorm_fwd_kernel(const float* __restrict__ x, uint16_t* __restrict__ h,
                                    float* __restrict__ r, long long N, int d, float* __restrict__ amax_part) {
   const int lane = threadIdx.x & 63;
@@ -108,10 +111,10 @@ __global__ void __launch_bounds__(256) rmsnorm_fwd_kernel(const float* __restric
   if (n >= N) return;
   const int nc = d / 4;
   const float* xr = x + n * d;
-  float4 v[kMaxChunks];
+  float4 v[MC];
   float ss = 0.f;
 #pragma unroll
-  for (int i = 0; i < kMaxChunks; ++i) {
+  for (int i = 0; i < MC; ++i) {
     const int c = i * 64 + lane;
     if (c < nc) {
       v[i] = *reinterpret_cast<const float4*>(xr + c * 4);
@@ -123,7 +126,7 @@ __global__ void __launch_bounds__(256) rmsnorm_fwd_kernel(const float* __restric
   uint16_t* hr = h + n * d;
   float amx = 0.f;
 #pragma unroll
-  for (int i = 0; i < kMaxChunks; ++i) {
+  for (int i = 0; i < MC; ++i) {
     const int c = i * 64 + lane;
     if (c < nc) {
       const uint2 w = make_uint2(pack_bf2(v[i].x * rr, v[i].y * rr), pack_bf2(v[i].z * rr, v[i].w * rr));
@@ -139,7 +142,9 @@ __global__ void __launch_bounds__(256) rmsnorm_fwd_kernel(const float* __restric
   if (lane == 0) r[n] = rr;
 }
 
-// g += r * (dh - h * mean(dh * h)); g_bf = bf16(g); one wave per row
+// g += r * (dh - h * mean(dh * h)); g_bf = bf16(g); one wave per row (MC as
+// in the forward)
+template <int MC>
 __global__ void __launch_bounds__(256) rmsnorm_bwd_kernel(const float* __restrict__ dh, const uint16_t* __restrict__ h,
                                    const float* __restrict__ r, float* __restrict__ g,
                                    uint16_t* __restrict__ g_bf, long long N, int d, float* __restrict__ amax_part) {
@@ -147,10 +152,10 @@ __global__ void __launch_bounds__(256) rmsnorm_bwd_kernel(const float* __restric
   const long long n = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (n >= N) return;
   const int nc = d / 4;
-  float4 dv[kMaxChunks], hv[kMaxChunks];
+  float4 dv[MC], hv[MC];
   float dot = 0.f;
 #pragma unroll
-  for (int i = 0; i < kMaxChunks; ++i) {
+  for (int i = 0; i < MC; ++i) {
     const int c = i * 64 + lane;
     if (c < nc) {
       dv[i] = *reinterpret_cast<const float4*>(dh + n * d + c * 4);
@@ -163,7 +168,7 @@ __global__ void __launch_bounds__(256) rmsnorm_bwd_kernel(const float* __restric
   const float rr = r[n];
   float amx = 0.f;
 #pragma unroll
-  for (int i = 0; i < kMaxChunks; ++i) {
+  for (int i = 0; i < MC; ++i) {
     const int c = i * 64 + lane;
     if (c < nc) {
       float4 gv = *reinterpret_cast<const float4*>(g + n * d + c * 4);
@@ -569,15 +574,43 @@ int launch_embed_bwd(const int* ids, const float* g, float* dwte, int B, int T, 
   return 0;
 }
 
+// one instantiation per chunk count 1 .. kMaxChunks (d <= 4096)
+#define GS_MC_SWITCH(mc, CALL) \
+  switch (mc) {                \
+    case 1: CALL(1); break;    \
+    case 2: CALL(2); break;    \
+    case 3: CALL(3); break;    \
+    case 4: CALL(4); break;    \
+    case 5: CALL(5); break;    \
+    case 6: CALL(6); break;    \
+    case 7: CALL(7); break;    \
+    case 8: CALL(8); break;    \
+    case 9: CALL(9); break;    \
+    case 10: CALL(10); break;  \
+    case 11: CALL(11); break;  \
+    case 12: CALL(12); break;  \
+    case 13: CALL(13); break;  \
+    case 14: CALL(14); break;  \
+    case 15: CALL(15); break;  \
+    default: CALL(16); break;  \
+  }
+static_assert(kMaxChunks == 16, "chunk-count switch");
+
 int launch_rmsnorm_fwd(const float* x, uint16_t* h, float* r, long long N, int d, hipStream_t s, float* amax_part) {
-  hipLaunchKernelGGL(rmsnorm_fwd_kernel, dim3(nblocks(N, 4)), dim3(256), 0, s, x, h, r, N, d, amax_part);
+  const int mc = (d / 4 + 63) / 64;
+#define GS_RF(M) hipLaunchKernelGGL((rmsnorm_fwd_kernel<M>), dim3(nblocks(N, 4)), dim3(256), 0, s, x, h, r, N, d, amax_part)
+  GS_MC_SWITCH(mc, GS_RF)
+#undef GS_RF
   GS_LAUNCH_CHECK("rmsnorm_fwd");
   return 0;
 }
 
 int launch_rmsnorm_bwd(const float* dh, const uint16_t* h, const float* r, float* g, uint16_t* g_bf,
                        long long N, int d, hipStream_t s, float* amax_part) {
-  hipLaunchKernelGGL(rmsnorm_bwd_kernel, dim3(nblocks(N, 4)), dim3(256), 0, s, dh, h, r, g, g_bf, N, d, amax_part);
+  const int mc = (d / 4 + 63) / 64;
+#define GS_RB(M) hipLaunchKernelGGL((rmsnorm_bwd_kernel<M>), dim3(nblocks(N, 4)), dim3(256), 0, s, dh, h, r, g, g_bf, N, d, amax_part)
+  GS_MC_SWITCH(mc, GS_RB)
+#undef GS_RB
   GS_LAUNCH_CHECK("rmsnorm_bwd");
   return 0;
 }
