@@ -144,6 +144,7 @@ __global__ void __launch_bounds__(256) smear_bwd_kernel(const int* __restrict__ 
 // when NULL), b = bsign * *pb (bf16 scalars).  xin (nullable) keeps bf16(x)
 // from before the mix.
 // ---------------------------------------------------------------------------
+template <int MC>  // float4 chunks per lane, ceil(d / 256)
 __global__ void __launch_bounds__(256) mix_rmsnorm_fwd_kernel(float* __restrict__ x, const float* __restrict__ y,
                                                               const uint16_t* __restrict__ pa,
                                                               const uint16_t* __restrict__ pb, float bsign,
@@ -157,10 +158,10 @@ __global__ void __launch_bounds__(256) mix_rmsnorm_fwd_kernel(float* __restrict_
   const float a = pa ? bfv(pa) : 1.f, bb = bsign * bfv(pb);
   float* xr = x + n * d;
   const float* yr = y + n * d;
-  float4 v[kMaxChunks];
+  float4 v[MC];
   float ss = 0.f;
 #pragma unroll
-  for (int i = 0; i < kMaxChunks; ++i) {
+  for (int i = 0; i < MC; ++i) {
     const int c = i * 64 + lane;
     if (c < nc) {
       const float4 xv = *reinterpret_cast<const float4*>(xr + c * 4);
@@ -177,7 +178,7 @@ __global__ void __launch_bounds__(256) mix_rmsnorm_fwd_kernel(float* __restrict_
   uint16_t* hr = h + n * d;
   float amx = 0.f;
 #pragma unroll
-  for (int i = 0; i < kMaxChunks; ++i) {
+  for (int i = 0; i < MC; ++i) {
     const int c = i * 64 + lane;
     if (c < nc) {
       const uint2 w = make_uint2(pack_bf2(v[i].x * rr, v[i].y * rr), pack_bf2(v[i].z * rr, v[i].w * rr));
@@ -425,8 +426,22 @@ int launch_smear_bwd(const int* ids, const uint16_t* wte, const uint16_t* sw, co
 
 int launch_mix_rmsnorm_fwd(float* x, const float* y, const uint16_t* pa, const uint16_t* pb, float bsign,
                            uint16_t* xin, uint16_t* h, float* r, long long N, int d, float* amax_part, hipStream_t s) {
-  hipLaunchKernelGGL(mix_rmsnorm_fwd_kernel, dim3(nblocks(N, 4)), dim3(256), 0, s, x, y, pa, pb, bsign, xin, h, r, N, d,
-                     amax_part);
+  const int mc = (d / 4 + 63) / 64;
+#define GS_MR(M)                                                                                                     \
+  hipLaunchKernelGGL((mix_rmsnorm_fwd_kernel<M>), dim3(nblocks(N, 4)), dim3(256), 0, s, x, y, pa, pb, bsign, xin, h, \
+                     r, N, d, amax_part)
+  switch (mc) {
+    case 1: GS_MR(1); break;
+    case 2: GS_MR(2); break;
+    case 3: GS_MR(3); break;
+    case 4: GS_MR(4); break;
+    case 5: GS_MR(5); break;
+    case 6: GS_MR(6); break;
+    case 7: GS_MR(7); break;
+    case 8: GS_MR(8); break;
+    default: GS_MR(kMaxChunks); break;
+  }
+#undef GS_MR
   GS_LAUNCH_CHECK("mix_rmsnorm_fwd");
   return 0;
 }
