@@ -717,7 +717,7 @@ __global__ void __launch_bounds__((Cfg<BM, BN>::NT), 1) gemm_kernel(GemmArgs p) 
   const int lin = xcd_remap(blockIdx.x + gridDim.x * blockIdx.y, nblk);
   const int yb = lin / gridDim.x;
   const int lid = lin - yb * gridDim.x;
-  constexpr int GM = 8;
+  constexpr int GM = 4;
   const int group = lid / (GM * tiles_n);
   const int first_m = group * GM;
   const int gsz = min(tiles_m - first_m, GM);
