@@ -146,6 +146,16 @@ __device__ __forceinline__ void dma_barrier() {
   asm volatile("" ::: "memory");
 }
 
+// Linear block index in an order that keeps all blocks of one (sequence,
+// head) on one XCD: the dispatcher deals workgroups x + gx y round robin to
+// the 8 XCDs, so consecutive blocks would otherwise fetch the same K/V (or
+// Q/dO) stream into 8 different L2s.  Each XCD instead walks a contiguous run
+// of heads, one head's blocks after another, keeping the head's stream
+// resident in its own L2.
+__device__ __forceinline__ int xcd_block(int gx) {
+  return xcd_remap(blockIdx.x + gx * blockIdx.y, gx * gridDim.y);
+}
+
 // Copy of ROWS rows of 128 features (row r0 + r clamped to T - 1) of a bf16
 // matrix whose row 0 is byte 0 of rsrc into a swizzled tile, by NT threads:
 // round i, wave w, lane l fills 16-byte slot NT i + 64 w + l.  Offsets
@@ -180,8 +190,9 @@ attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, 
   const int window = GEN ? window_arg : -1;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, lr = lane & 31, lh = lane >> 5;
   const int nqb = (T + FQ - 1) / FQ;
-  const int qb = nqb - 1 - blockIdx.x;  // longest rows first
-  const int bh = blockIdx.y, b = bh / H, h = bh % H;
+  const int bx = xcd_block(gridDim.x), bhq = bx / gridDim.x;
+  const int qb = nqb - 1 - (bx - bhq * gridDim.x);  // longest rows first
+  const int bh = bhq, b = bh / H, h = bh % H;
   const int hk = GEN ? h / (H / Hkv) : h;  // key/value head of this query head
   const long long rowbase = (long long)b * T;
   const uint16_t* qh = q + rowbase * ld + h * 128;
@@ -395,8 +406,9 @@ attn_bwd_kv8_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
   auto stage = [&](int j) -> char* { return j == 0 ? s_st0 : j == 1 ? s_st1 : j == 2 ? s_st2 : s_st3; };
   const int window = GEN ? window_arg : -1;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, lr = lane & 31, lh = lane >> 5;
-  const int kb = blockIdx.x;
-  const int bhk = blockIdx.y, b = bhk / Hkv, hk = bhk % Hkv;
+  const int bx = xcd_block(gridDim.x), bhk = bx / gridDim.x;
+  const int kb = bx - bhk * gridDim.x;
+  const int b = bhk / Hkv, hk = bhk % Hkv;
   const int G = GEN ? H / Hkv : 1;
   const long long rowbase = (long long)b * T;
   const uint16_t* kh = k + rowbase * ld + hk * 128;
@@ -571,8 +583,9 @@ attn_bwd_q_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k
   const int window = GEN ? window_arg : -1;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, lr = lane & 31, lh = lane >> 5;
   const int nqb = (T + DQ_Q - 1) / DQ_Q;
-  const int qb = nqb - 1 - blockIdx.x;  // longest rows first
-  const int bh = blockIdx.y, b = bh / H, h = bh % H;
+  const int bx = xcd_block(gridDim.x), bhq = bx / gridDim.x;
+  const int qb = nqb - 1 - (bx - bhq * gridDim.x);  // longest rows first
+  const int bh = bhq, b = bh / H, h = bh % H;
   const int hk = GEN ? h / (H / Hkv) : h;
   const long long rowbase = (long long)b * T;
   const int d = H * 128;
