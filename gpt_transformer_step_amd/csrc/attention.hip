@@ -92,6 +92,19 @@ __device__ __forceinline__ bf16x8_t pack_perm(const float* x, int s) {
   return f;
 }
 
+// An empty statement the compiler may not move or drop: placed in the body of
+// a wave-uniform branch it keeps the branch, where the compiler would
+// otherwise turn a cheap-looking body into selects executed on every pass.
+__device__ __forceinline__ void keep_branch() { asm volatile(""); }
+
+// max of three floats in one instruction: the scores are finite or -inf, so
+// the NaN quieting fmaxf adds in front of every operand is not needed
+__device__ __forceinline__ float max3(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+
 __device__ __forceinline__ uint4 ld16(const uint16_t* p) { return *reinterpret_cast<const uint4*>(p); }
 
 // Buffer resource (raw byte addressing, range num_bytes; gfx9 layout: base,
@@ -259,6 +272,7 @@ attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, 
       // folded into the exponent: p = exp2(s c - m)
       float x[32];
       if (diag) {
+        keep_branch();
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
@@ -275,7 +289,7 @@ attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, 
       }
       float tmax = x[0];
 #pragma unroll
-      for (int i = 1; i + 1 < 32; i += 2) tmax = fmaxf(tmax, fmaxf(x[i], x[i + 1]));
+      for (int i = 1; i + 1 < 32; i += 2) tmax = max3(tmax, x[i], x[i + 1]);
       tmax = fmaxf(tmax, x[31]);
       tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64)) * c;
       const bool need = tmax > m + kRescale;
@@ -504,30 +518,39 @@ attn_bwd_kv8_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
         const bool diag = (q0 < wk0 + 31) || (q0 + KV_Q > T) || (wk0 + 32 > T) ||
                           (window >= 0 && q0 + KV_Q - 1 > wk0 + window);
         bf16x8_t fp[2], fs[2];
+        // P and dS of the tile as bf16 B fragments; the visibility test only
+        // on tiles that need it (wave-uniform branch)
+        auto p_ds = [&](auto masked) {
+          constexpr bool MASK = decltype(masked)::value;
 #pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2) {
-          uint32_t* wp = reinterpret_cast<uint32_t*>(&fp[s2]);
-          uint32_t* wd = reinterpret_cast<uint32_t*>(&fs[s2]);
+          for (int s2 = 0; s2 < 2; ++s2) {
+            uint32_t* wp = reinterpret_cast<uint32_t*>(&fp[s2]);
+            uint32_t* wd = reinterpret_cast<uint32_t*>(&fs[s2]);
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            float pv[2], dv2[2];
+            for (int i = 0; i < 4; ++i) {
+              float pv[2], dv2[2];
 #pragma unroll
-            for (int u = 0; u < 2; ++u) {
-              const int e = 8 * s2 + 2 * i + u;
-              const int ql = 8 * (e >> 2) + 4 * lh + (e & 3);
-              const float l2 = slse[ql] * kLog2e;
-              const float dl = sdel[ql];
-              float pe = __builtin_amdgcn_exp2f(sacc[e] * c - l2);
-              const bool vis =
-                  mykey <= q0 + ql && mykey < T && q0 + ql < T && (window < 0 || mykey >= q0 + ql - window);
-              pe = (!diag || vis) ? pe : 0.f;
-              pv[u] = pe;
-              dv2[u] = pe * (dpacc[e] - dl);
+              for (int u = 0; u < 2; ++u) {
+                const int e = 8 * s2 + 2 * i + u;
+                const int ql = 8 * (e >> 2) + 4 * lh + (e & 3);
+                const float l2 = slse[ql] * kLog2e;
+                const float dl = sdel[ql];
+                float pe = __builtin_amdgcn_exp2f(sacc[e] * c - l2);
+                if constexpr (MASK) {
+                  const bool vis =
+                      mykey <= q0 + ql && mykey < T && q0 + ql < T && (window < 0 || mykey >= q0 + ql - window);
+                  pe = vis ? pe : 0.f;
+                }
+                pv[u] = pe;
+                dv2[u] = pe * (dpacc[e] - dl);
+              }
+              wp[i] = pack_bf2(pv[0], pv[1]);
+              wd[i] = pack_bf2(dv2[0], dv2[1]);
             }
-            wp[i] = pack_bf2(pv[0], pv[1]);
-            wd[i] = pack_bf2(dv2[0], dv2[1]);
           }
-        }
+        };
+        if (diag) p_ds(std::integral_constant<bool, true>{});
+        else p_ds(std::integral_constant<bool, false>{});
 #pragma unroll
         for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
@@ -661,13 +684,22 @@ attn_bwd_q_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          float pv = __builtin_amdgcn_exp2f(st2[kt][e] * c - lse2);
-          const int key = key0 + kt * 32 + 8 * (e >> 2) + 4 * lh + (e & 3);
-          const bool vis = key <= myq && key < T && (window < 0 || key >= myq - window);
-          pv = (!diag || vis) ? pv : 0.f;
-          ds[kt * 16 + e] = pv * (dpt[kt][e] - del);
-        }
+        for (int e = 0; e < 16; ++e) ds[kt * 16 + e] = __builtin_amdgcn_exp2f(st2[kt][e] * c - lse2);
+      if (diag) {  // wave-uniform: the visibility test only on tiles that need it
+        keep_branch();
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const int key = key0 + kt * 32 + 8 * (e >> 2) + 4 * lh + (e & 3);
+            const bool vis = key <= myq && key < T && (window < 0 || key >= myq - window);
+            ds[kt * 16 + e] = vis ? ds[kt * 16 + e] : 0.f;
+          }
+      }
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) ds[kt * 16 + e] *= dpt[kt][e] - del;
 #pragma unroll
       for (int s4 = 0; s4 < 4; ++s4) {
         const bf16x8_t fs = pack_perm(ds, s4);
