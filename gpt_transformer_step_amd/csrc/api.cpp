@@ -1173,34 +1173,53 @@ int muon_impl(float* Wt, uint16_t* W_bf16, const float* Gm, float* M, float* O_o
   const int gram_split = gram_splits(count, rows, cols);
   float* gpart = at<float>(ws, m.gpart);
   int cur = 0;
+  // A = X^T X and B = b A + c A A are symmetric: when the batch holds more
+  // 128 x 128 tiles than the chip has CUs, both products compute only the
+  // tiles on and above the diagonal, and the bf16 copies the next product
+  // reads in full are mirrored (with fewer tiles all of them run in one wave
+  // anyway, and the mirror would only add time).  The fp32 A is read only by the polynomial's epilogue, at the
+  // positions it writes, which lie inside the Gram's computed tiles when the
+  // polynomial's tiles are no larger than the Gram's (else the fp32 A is
+  // mirrored too).
+  const long long t128 = (sm + 127) / 128;
+  const int sym = (long long)count * t128 * t128 > 256 ? 1 : 0;
+  GemmArgs ga;
+  ga.M = sm; ga.N = sm; ga.K = lrow; ga.batch = count; ga.sym = sym;
+  ga.lda = sm; ga.sA = sX; ga.a_kcontig = 0;
+  ga.ldb = sm; ga.sB = sX; ga.b_kcontig = 0;
+  ga.C = A; ga.ldc = sm; ga.sC = sA; ga.C2 = Ab; ga.ldc2 = sm; ga.sC2 = sA;
+  if (gram_split > 1) {
+    // split-K partials [split][count][sm][sm], then A = sum, Ab = bf16(A)
+    ga.C = gpart; ga.k_split = gram_split; ga.split_stride = sA * count;
+  }
+  GemmArgs gp;
+  gp.M = sm; gp.N = sm; gp.K = sm; gp.batch = count; gp.sym = sym;
+  gp.A = Ab; gp.lda = sm; gp.sA = sA;
+  gp.B = Ab; gp.ldb = sm; gp.sB = sA; gp.b_kcontig = 0;
+  gp.C = Bb; gp.ldc = sm; gp.sC = sA;
+  gp.aux = A; gp.ldaux = sm; gp.sAux = sA;
+  const bool mirror_a32 = sym && gemm_tile_n(gp) > gemm_tile_n(ga);
   for (int it = 0; it < ns_steps; ++it) {
     const float ca = coeffs[3 * it], cb = coeffs[3 * it + 1], cc = coeffs[3 * it + 2];
     {
-      GemmArgs a;  // A = X^T X (fp32 and bf16)
       ProfScope ps_(P_NS_GRAM, s);
-      a.M = sm; a.N = sm; a.K = lrow; a.batch = count;
-      a.A = Xb[cur]; a.lda = sm; a.sA = sX; a.a_kcontig = 0;
-      a.B = Xb[cur]; a.ldb = sm; a.sB = sX; a.b_kcontig = 0;
-      a.C = A; a.ldc = sm; a.sC = sA; a.C2 = Ab; a.ldc2 = sm; a.sC2 = sA;
+      GemmArgs a = ga;  // A = X^T X (fp32 and bf16)
+      a.A = Xb[cur]; a.B = Xb[cur];
       if (gram_split <= 1) {
         TRY(gemm_bf16(a, EPI_F32_BF16, s));
       } else {
-        // split-K partials [split][count][sm][sm], then A = sum, Ab = bf16(A)
-        a.C = gpart; a.sC = sA; a.k_split = gram_split; a.split_stride = sA * count;
         TRY(gemm_bf16(a, EPI_F32, s));
         TRY(launch_splitk_reduce(gpart, gram_split, sA * count, A, Ab, sA * count, 0.f, s));
       }
+      if (sym) TRY(launch_sym_mirror(Ab, 0, sm, sm, sA, count, s));
+      if (mirror_a32) TRY(launch_sym_mirror(A, 1, sm, sm, sA, count, s));
     }
     {
-      GemmArgs a;  // B = b A + c A A
       ProfScope ps_(P_NS_POLY, s);
-      a.M = sm; a.N = sm; a.K = sm; a.batch = count;
-      a.A = Ab; a.lda = sm; a.sA = sA;
-      a.B = Ab; a.ldb = sm; a.sB = sA; a.b_kcontig = 0;
-      a.C = Bb; a.ldc = sm; a.sC = sA;
-      a.aux = A; a.ldaux = sm; a.sAux = sA;
+      GemmArgs a = gp;  // B = b A + c A A
       a.alpha = cc; a.beta = cb;
       TRY(gemm_bf16(a, EPI_NS_POLY, s));
+      if (sym) TRY(launch_sym_mirror(Bb, 0, sm, sm, sA, count, s));
     }
     {
       GemmArgs a;  // X = a X + X B

@@ -302,6 +302,35 @@ __global__ void splitk_reduce_kernel(const float* __restrict__ part, int nsplit,
   }
 }
 
+// ------------------------ symmetric matrix mirror ---------------------------
+// C[b][i][j] = C[b][j][i] for i > j: 64 x 64 blocks (bi, bj), bi >= bj, of
+// the lower triangle, each read from its mirror block (bj, bi) through LDS.
+// Reads touch only elements with i < j (or the block's own upper part on the
+// diagonal) and writes only i > j, so no element is both read and written.
+template <typename T>
+__global__ void __launch_bounds__(256) sym_mirror_kernel(T* __restrict__ C, int n, long long ld, long long stride) {
+  __shared__ T tile[64][65];
+  // block index -> (bi, bj), bi >= bj, row by row of the lower triangle
+  const int x = blockIdx.x;
+  int bi = (int)((sqrtf(8.f * x + 1.f) - 1.f) * 0.5f);
+  while (bi * (bi + 1) / 2 > x) --bi;
+  while ((bi + 1) * (bi + 2) / 2 <= x) ++bi;
+  const int bj = x - bi * (bi + 1) / 2;
+  T* c = C + (long long)blockIdx.y * stride;
+  const int r0 = bj * 64, c0 = bi * 64;  // source block: rows r0.., columns c0..
+  for (int e = threadIdx.x; e < 64 * 64; e += 256) {
+    const int rr = e >> 6, cc = e & 63;
+    const int gr = r0 + rr, gc = c0 + cc;
+    if (gr < n && gc < n && gr < gc) tile[rr][cc] = c[(long long)gr * ld + gc];
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < 64 * 64; e += 256) {
+    const int rr = e >> 6, cc = e & 63;  // destination row c0 + rr, column r0 + cc
+    const int gi = c0 + rr, gj = r0 + cc;
+    if (gi < n && gj < n && gi > gj) c[(long long)gi * ld + gj] = tile[cc][rr];
+  }
+}
+
 // ---------------------------- Muon elementwise ------------------------------
 __global__ void muon_momentum_kernel(float* __restrict__ M, const float* __restrict__ G, long long n, float mu) {
   long long i = ((long long)blockIdx.x * blockDim.x + threadIdx.x) * 4;
@@ -643,6 +672,18 @@ int launch_splitk_reduce(const float* part, int nsplit, long long stride, float*
   const int blocks = (int)std::min<long long>(nblocks(n, 1024), 8192);
   hipLaunchKernelGGL(splitk_reduce_kernel, dim3(blocks), dim3(256), 0, s, part, nsplit, stride, out, out_bf, n, beta);
   GS_LAUNCH_CHECK("splitk_reduce");
+  return 0;
+}
+
+int launch_sym_mirror(void* C, int is_f32, int n, long long ld, long long stride, int count, hipStream_t s) {
+  if (n <= 1 || count <= 0) return 0;
+  const int nb = (n + 63) / 64;
+  dim3 grid(nb * (nb + 1) / 2, count);
+  if (is_f32)
+    hipLaunchKernelGGL(sym_mirror_kernel<float>, grid, dim3(256), 0, s, static_cast<float*>(C), n, ld, stride);
+  else
+    hipLaunchKernelGGL(sym_mirror_kernel<uint16_t>, grid, dim3(256), 0, s, static_cast<uint16_t*>(C), n, ld, stride);
+  GS_LAUNCH_CHECK("sym_mirror");
   return 0;
 }
 

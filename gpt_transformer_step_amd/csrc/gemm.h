@@ -49,6 +49,8 @@ struct GemmArgs {
   int n_kv_head = 0;              // EPI_QKV: key/value heads (0 = n_head); columns [q | k | v]
   const float* scale_a = nullptr;  // fp8: device scalars; v *= 1 / (scale_a * scale_b)
   const float* scale_b = nullptr;
+  int sym = 0;                     // M == N, symmetric product: only tiles with tile_m <= tile_n are
+                                   // computed; the caller fills the rest (launch_sym_mirror)
   float* amax = nullptr;           // bf16 epilogues: per-wave max |stored value| at
                                    // amax[block * waves + wave] (block = x + gridDim.x * y)
 };

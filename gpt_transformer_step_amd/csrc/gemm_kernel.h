@@ -717,13 +717,22 @@ __global__ void __launch_bounds__((Cfg<BM, BN>::NT), 1) gemm_kernel(GemmArgs p) 
   const int lin = xcd_remap(blockIdx.x + gridDim.x * blockIdx.y, nblk);
   const int yb = lin / gridDim.x;
   const int lid = lin - yb * gridDim.x;
-  constexpr int GM = 4;
-  const int group = lid / (GM * tiles_n);
-  const int first_m = group * GM;
-  const int gsz = min(tiles_m - first_m, GM);
-  const int in_group = lid - group * GM * tiles_n;
-  const int tile_m = first_m + in_group % gsz;
-  const int tile_n = in_group / gsz;
+  int tile_m, tile_n;
+  if (p.sym) {
+    // upper triangle of a square tile grid, row by row (row r holds tiles_n - r tiles)
+    int r = 0, rem = lid;
+    while (rem >= tiles_n - r) rem -= tiles_n - r++;
+    tile_m = r;
+    tile_n = r + rem;
+  } else {
+    constexpr int GM = 4;
+    const int group = lid / (GM * tiles_n);
+    const int first_m = group * GM;
+    const int gsz = min(tiles_m - first_m, GM);
+    const int in_group = lid - group * GM * tiles_n;
+    tile_m = first_m + in_group % gsz;
+    tile_n = in_group / gsz;
+  }
   const int m0 = tile_m * BM, n0 = tile_n * BN;
 
   const int bi = yb / p.k_split, split = yb % p.k_split;
@@ -990,7 +999,8 @@ __global__ void __launch_bounds__((Cfg<BM, BN>::NT), 1) gemm_kernel(GemmArgs p) 
 
 template <int BM, int BN, bool AK, bool BKC, int EPI, int F8 = 0>
 int launch_t(const GemmArgs& a, hipStream_t s) {
-  const int tiles = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
+  const int tm = (a.M + BM - 1) / BM;
+  const int tiles = a.sym ? tm * (tm + 1) / 2 : tm * ((a.N + BN - 1) / BN);
   dim3 grid(tiles, a.batch * a.k_split);
   hipLaunchKernelGGL((gemm_kernel<BM, BN, AK, BKC, EPI, F8>), grid, dim3(Cfg<BM, BN>::NT), 0, s, a);
   GS_LAUNCH_CHECK(std::string(F8 ? "gemm_fp8" : "gemm_bf16"));

@@ -26,6 +26,8 @@ int launch_ce_reduce(const float* part, int nparts, const float* zt, float* lse,
                      float* lse_out, long long N, hipStream_t s);
 int launch_loss_mean(const float* row_loss, float* loss, long long N, hipStream_t s);
 // out[0..n) = beta * out + sum_{s < nsplit} part[s * stride + i]; optional bf16 copy out_bf
+// C[b][i][j] = C[b][j][i] for i > j (n x n matrices, row stride ld, batch stride stride)
+int launch_sym_mirror(void* C, int is_f32, int n, long long ld, long long stride, int count, hipStream_t s);
 int launch_splitk_reduce(const float* part, int nsplit, long long stride, float* out, uint16_t* out_bf, long long n,
                          float beta, hipStream_t s);
 
