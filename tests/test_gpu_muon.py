@@ -33,8 +33,10 @@ def B():
     return binding
 
 
+# (4, 1280, 1280) and (3, 1280, 2048) take the symmetric Gram / polynomial
+# path (more 128x128 tiles than CUs); the latter also splits the Gram over K
 @pytest.mark.parametrize("count,rows,cols", [(3, 256, 256), (2, 512, 128), (2, 128, 512), (1, 136, 200),
-                                             (4, 1280, 1280)])
+                                             (4, 1280, 1280), (3, 1280, 2048)])
 @pytest.mark.parametrize("table", ["ns5", "printed2"])
 def test_muon_update_parity(B, count, rows, cols, table):
     say(f"muon count={count} {rows}x{cols} table={table}")
