@@ -347,15 +347,30 @@ __global__ void muon_momentum_kernel(float* __restrict__ M, const float* __restr
   }
 }
 
-// partial[b * nblk + blk] = sum of squares of chunk blk of matrix b
-__global__ void frob_partial_kernel(const float* __restrict__ X, float* __restrict__ partial,
-                                    long long per, int nblk) {
+// partial[b * nblk + blk] = sum of squares of chunk blk of matrix b; per is a
+// multiple of 4 (the matrices' sides are multiples of 8), read as float4 with
+// four loads in flight per thread
+__global__ void __launch_bounds__(256) frob_partial_kernel(const float* __restrict__ X, float* __restrict__ partial,
+                                                           long long per, int nblk) {
   const int b = blockIdx.y, blk = blockIdx.x;
-  const long long chunk = (per + nblk - 1) / nblk;
-  const long long beg = blk * chunk, end = min(per, beg + chunk);
-  const float* x = X + (long long)b * per;
-  float s = 0.f;
-  for (long long i = beg + threadIdx.x; i < end; i += blockDim.x) s += x[i] * x[i];
+  const long long per4 = per / 4;
+  const long long chunk = (per4 + nblk - 1) / nblk;
+  const long long beg = blk * chunk, end = min(per4, beg + chunk);
+  const float4* x = reinterpret_cast<const float4*>(X + (long long)b * per);
+  float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
+  long long i = beg + threadIdx.x;
+  for (; i + 3 * 256 < end; i += 4 * 256) {
+    const float4 a = x[i], c = x[i + 256], d = x[i + 512], e = x[i + 768];
+    s0 += a.x * a.x + a.y * a.y + a.z * a.z + a.w * a.w;
+    s1 += c.x * c.x + c.y * c.y + c.z * c.z + c.w * c.w;
+    s2 += d.x * d.x + d.y * d.y + d.z * d.z + d.w * d.w;
+    s3 += e.x * e.x + e.y * e.y + e.z * e.z + e.w * e.w;
+  }
+  for (; i < end; i += 256) {
+    const float4 a = x[i];
+    s0 += a.x * a.x + a.y * a.y + a.z * a.z + a.w * a.w;
+  }
+  float s = (s0 + s1) + (s2 + s3);
   __shared__ float red[4];
   s = wave_sum(s);
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = s;
