@@ -530,8 +530,10 @@ inline T* at(void* ws, size_t off) { return reinterpret_cast<T*>(reinterpret_cas
 // deterministic).  The split count fills the chip's workgroup slots (one
 // 256x256 workgroup per CU, two 128x128 ones) as evenly as possible: the
 // smallest count whose last wave is within 2.5% of the best fill, with 256x256
-// tiles whenever some count up to 20 reaches the 512 workgroups that select
-// them, and at least 2048 k per split.
+// tiles whenever some count up to 20 reaches 512 workgroups, and at least 2048
+// k per split.  The count may stop at 500 workgroups (the big-tile threshold
+// of the launch): for the d20 MLP products (100 tiles) that is 5 splits
+// instead of 10, half the partial traffic for the same 98 % fill.
 inline int wgrad_splits(int M, int N, int K) {
   const long long t256 = (long long)((M + 255) / 256) * ((N + 255) / 256);
   if (t256 >= 256) return 1;
@@ -539,7 +541,7 @@ inline int wgrad_splits(int M, int N, int K) {
   const int kmax = std::max(1, K / 2048);
   const bool big = M >= 256 && N >= 256 && t256 * 20 >= 512;
   const long long tiles = big ? t256 : t128, slots = big ? 256 : 512;
-  const int lo = big ? (int)((512 + t256 - 1) / t256) : 1;
+  const int lo = big ? (int)((500 + t256 - 1) / t256) : 1;
   const int hi = std::min(big ? 20 : 16, kmax);
   if (lo > hi) return std::max(1, std::min(kmax, 16));
   auto fill = [&](int ks) {

@@ -1007,9 +1007,11 @@ int launch_t(const GemmArgs& a, hipStream_t s) {
   return 0;
 }
 
+// 256x256 tiles (one workgroup per CU) once a launch has about two waves of
+// them (500: a 100-tile product split 5 ways qualifies); 128x128 below
 inline bool use_big_tile(const GemmArgs& a) {
   const long long big = (long long)((a.M + 255) / 256) * ((a.N + 255) / 256) * a.batch * a.k_split;
-  return a.M >= 256 && a.N >= 256 && big >= 512;
+  return a.M >= 256 && a.N >= 256 && big >= 500;
 }
 
 template <bool AK, bool BKC, int EPI, int F8 = 0>
