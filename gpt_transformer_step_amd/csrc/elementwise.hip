@@ -307,17 +307,67 @@ __global__ void splitk_reduce_kernel(const float* __restrict__ part, int nsplit,
 // the lower triangle, each read from its mirror block (bj, bi) through LDS.
 // Reads touch only elements with i < j (or the block's own upper part on the
 // diagonal) and writes only i > j, so no element is both read and written.
-template <typename T>
-__global__ void __launch_bounds__(256) sym_mirror_kernel(T* __restrict__ C, int n, long long ld, long long stride) {
-  __shared__ T tile[64][65];
+// bf16 n x n matrices, n a multiple of 8 (so 8-element chunks lie wholly
+// inside or outside).  Off-diagonal blocks move 16-byte chunks: the source
+// block is read row-wise into LDS and each thread writes 8 consecutive
+// elements of a destination row (a column of the source block); diagonal
+// blocks copy element by element where i > j.
+constexpr int kMirP = 72;  // LDS row pitch (elements) of the 64 x 64 block
+__global__ void __launch_bounds__(256) sym_mirror_bf16_kernel(uint16_t* __restrict__ C, int n, long long ld,
+                                                              long long stride) {
+  __shared__ __attribute__((aligned(16))) uint16_t tile[64 * kMirP];
   // block index -> (bi, bj), bi >= bj, row by row of the lower triangle
   const int x = blockIdx.x;
   int bi = (int)((sqrtf(8.f * x + 1.f) - 1.f) * 0.5f);
   while (bi * (bi + 1) / 2 > x) --bi;
   while ((bi + 1) * (bi + 2) / 2 <= x) ++bi;
   const int bj = x - bi * (bi + 1) / 2;
-  T* c = C + (long long)blockIdx.y * stride;
+  uint16_t* c = C + (long long)blockIdx.y * stride;
   const int r0 = bj * 64, c0 = bi * 64;  // source block: rows r0.., columns c0..
+  // source rows as 16-byte chunks: 64 rows x 8 chunks, two per thread
+  for (int e = threadIdx.x; e < 512; e += 256) {
+    const int rr = e >> 3, ch = (e & 7) * 8;
+    const int gr = r0 + rr, gc = c0 + ch;
+    if (gr < n && gc < n)
+      *reinterpret_cast<uint4*>(tile + rr * kMirP + ch) = *reinterpret_cast<const uint4*>(c + (long long)gr * ld + gc);
+  }
+  __syncthreads();
+  if (bi > bj) {
+    // destination row c0 + rr, columns r0 + ch .. + 7 = tile column rr, rows ch .. ch + 7
+    for (int e = threadIdx.x; e < 512; e += 256) {
+      const int rr = e >> 3, ch = (e & 7) * 8;
+      const int gi = c0 + rr, gj = r0 + ch;
+      if (gi < n && gj < n) {
+        uint32_t w[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+          w[k] = (uint32_t)tile[(ch + 2 * k) * kMirP + rr] | ((uint32_t)tile[(ch + 2 * k + 1) * kMirP + rr] << 16);
+        *reinterpret_cast<uint4*>(c + (long long)gi * ld + gj) = make_uint4(w[0], w[1], w[2], w[3]);
+      }
+    }
+  } else {
+    for (int e = threadIdx.x; e < 64 * 64; e += 256) {
+      const int rr = e >> 6, cc = e & 63;  // destination row c0 + rr, column r0 + cc
+      const int gi = c0 + rr, gj = r0 + cc;
+      if (gi < n && gj < n && gi > gj) c[(long long)gi * ld + gj] = tile[cc * kMirP + rr];
+    }
+  }
+}
+
+// fp32 matrices (any n): C[b][i][j] = C[b][j][i] for i > j, 64 x 64 blocks
+// (bi, bj), bi >= bj, of the lower triangle, each read from its mirror block
+// (bj, bi) through LDS.  Reads touch only elements with i < j (or the block's
+// own upper part on the diagonal) and writes only i > j.
+__global__ void __launch_bounds__(256) sym_mirror_f32_kernel(float* __restrict__ C, int n, long long ld,
+                                                             long long stride) {
+  __shared__ float tile[64][65];
+  const int x = blockIdx.x;
+  int bi = (int)((sqrtf(8.f * x + 1.f) - 1.f) * 0.5f);
+  while (bi * (bi + 1) / 2 > x) --bi;
+  while ((bi + 1) * (bi + 2) / 2 <= x) ++bi;
+  const int bj = x - bi * (bi + 1) / 2;
+  float* c = C + (long long)blockIdx.y * stride;
+  const int r0 = bj * 64, c0 = bi * 64;
   for (int e = threadIdx.x; e < 64 * 64; e += 256) {
     const int rr = e >> 6, cc = e & 63;
     const int gr = r0 + rr, gc = c0 + cc;
@@ -325,7 +375,7 @@ __global__ void __launch_bounds__(256) sym_mirror_kernel(T* __restrict__ C, int 
   }
   __syncthreads();
   for (int e = threadIdx.x; e < 64 * 64; e += 256) {
-    const int rr = e >> 6, cc = e & 63;  // destination row c0 + rr, column r0 + cc
+    const int rr = e >> 6, cc = e & 63;
     const int gi = c0 + rr, gj = r0 + cc;
     if (gi < n && gj < n && gi > gj) c[(long long)gi * ld + gj] = tile[cc][rr];
   }
@@ -694,10 +744,15 @@ int launch_sym_mirror(void* C, int is_f32, int n, long long ld, long long stride
   if (n <= 1 || count <= 0) return 0;
   const int nb = (n + 63) / 64;
   dim3 grid(nb * (nb + 1) / 2, count);
-  if (is_f32)
-    hipLaunchKernelGGL(sym_mirror_kernel<float>, grid, dim3(256), 0, s, static_cast<float*>(C), n, ld, stride);
-  else
-    hipLaunchKernelGGL(sym_mirror_kernel<uint16_t>, grid, dim3(256), 0, s, static_cast<uint16_t*>(C), n, ld, stride);
+  if (is_f32) {
+    hipLaunchKernelGGL(sym_mirror_f32_kernel, grid, dim3(256), 0, s, static_cast<float*>(C), n, ld, stride);
+  } else {
+    if ((n % 8) || (ld % 8) || (stride % 8) || (reinterpret_cast<uintptr_t>(C) % 16)) {
+      set_error("sym_mirror: bf16 matrices need n, ld, stride multiples of 8 and a 16-byte aligned base");
+      return -3;
+    }
+    hipLaunchKernelGGL(sym_mirror_bf16_kernel, grid, dim3(256), 0, s, static_cast<uint16_t*>(C), n, ld, stride);
+  }
   GS_LAUNCH_CHECK("sym_mirror");
   return 0;
 }
