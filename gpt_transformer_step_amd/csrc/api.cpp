@@ -289,14 +289,14 @@ namespace {
 enum ProfCat {
   P_EMBED_FWD, P_RMSNORM_FWD, P_GEMM_QKV, P_ATTN_FWD, P_GEMM_O, P_GEMM_FC, P_GEMM_PROJ, P_CE_FWD,
   P_CE_REDUCE, P_CE_DZ, P_CE_DH, P_CE_DW, P_RMSNORM_BWD, P_PROJ_DGRAD, P_PROJ_WGRAD, P_FC_DGRAD,
-  P_FC_WGRAD, P_O_DGRAD, P_O_WGRAD, P_ATTN_BWD_PRE, P_ATTN_BWD_KV, P_ATTN_BWD_Q, P_ROPE_BWD, P_QKV_DGRAD, P_QKV_WGRAD, P_EMBED_BWD,
+  P_FC_WGRAD, P_O_DGRAD, P_O_WGRAD, P_ATTN_BWD_KV, P_ATTN_BWD_Q, P_ROPE_BWD, P_QKV_DGRAD, P_QKV_WGRAD, P_EMBED_BWD,
   P_FILL, P_MUON_ELEMWISE, P_NS_GRAM, P_NS_POLY, P_NS_UPDATE, P_FP8_QUANT, P_ADAMW, P_FEATURES, P_COUNT
 };
 const char* kProfNames[P_COUNT] = {
     "embed_fwd", "rmsnorm_fwd", "gemm_qkv_rope_fwd", "attn_fwd", "gemm_o_fwd", "gemm_fc_relu2_fwd",
     "gemm_proj_fwd", "gemm_ce_fwd", "ce_reduce", "gemm_ce_dlogits", "gemm_ce_dh", "gemm_ce_dw",
     "rmsnorm_bwd", "gemm_proj_dgrad", "gemm_proj_wgrad", "gemm_fc_dgrad", "gemm_fc_wgrad",
-    "gemm_o_dgrad", "gemm_o_wgrad", "attn_bwd_delta", "attn_bwd_dkdv", "attn_bwd_dq", "rope_qknorm_bwd", "gemm_qkv_dgrad", "gemm_qkv_wgrad",
+    "gemm_o_dgrad", "gemm_o_wgrad", "attn_bwd_dkdv", "attn_bwd_dq", "rope_qknorm_bwd", "gemm_qkv_dgrad", "gemm_qkv_wgrad",
     "embed_bwd", "fill", "muon_elementwise", "ns_gram", "ns_poly", "ns_update", "fp8_quant", "adamw", "features"};
 
 struct Profiler {
@@ -999,8 +999,8 @@ extern "C" gpt_status gpt_step_bwd_scaled(const gpt_shape* shape, const gpt_para
       if (f8) TRY(wgrad_fp8(dyqt, at<uint8_t>(ws, L.attt), sc + SC_G_ATT, sc + SC_ATT, G + P.wo(D, l), d, d, N, acc, wpart, s));
       else TRY(wgrad(g_bf, d, att, d, G + P.wo(D, l), d, d, N, acc, wpart, s));
     }
-    for (int part = 0; part < 3; ++part) {
-      ProfScope ps_(part == 0 ? P_ATTN_BWD_PRE : part == 1 ? P_ATTN_BWD_KV : P_ATTN_BWD_Q, s);
+    for (int part = 0; part < 2; ++part) {  // dQ (and delta), then dK/dV
+      ProfScope ps_(part == 0 ? P_ATTN_BWD_Q : P_ATTN_BWD_KV, s);
       TRY(launch_attn_bwd_part(part, qkv, qkv + d, qkv + d + D.dkv, D.dqkv, att, dout, d, at<float>(ws, L.lse),
                                at<float>(ws, w.delta), dq_acc, dqkv + d, dqkv + d + D.dkv, D.dqkv, D.B, D.H, D.Hkv,
                                D.T, D.layer_window(l), s));

@@ -30,8 +30,10 @@
 //   * dK/dV: one workgroup = 256 keys (8 waves x 32) over query tiles of 32
 //     streamed through a 4-stage LDS ring: S = Q K^T, dP = dO V^T,
 //     P = exp(S - lse), dS = P (dP - delta), dV^T += dO^T P, dK^T += Q^T dS;
-//   * dQ: one workgroup = 128 queries over key tiles of 64, shaped like the
-//     forward: S^T, dP^T recomputed, dQ^T += K^T dS^T.
+//   * dQ (launched first): one workgroup = 128 queries over key tiles of 64,
+//     shaped like the forward: S^T, dP^T recomputed, dQ^T += K^T dS^T; it
+//     also computes delta = rowsum(dO O) of its queries and stores it for the
+//     dK/dV kernel.
 //   The dQ kernel recomputes two of the four products; in exchange dQ needs no
 //   fp32 atomics and the result is deterministic.
 
@@ -346,27 +348,6 @@ attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, 
 // ============================================================================
 // backward
 // ============================================================================
-// delta[b,h,t] = sum_e dout * out.  16 lanes per (token, head), 8 features
-// (16 bytes of each operand) per lane.
-__global__ void __launch_bounds__(256) attn_bwd_pre_kernel(const uint16_t* __restrict__ out,
-                                                           const uint16_t* __restrict__ dout, long long ld_out,
-                                                           float* __restrict__ delta, int H, int T, long long NH) {
-  const int j = threadIdx.x & 15;
-  const long long w = (long long)blockIdx.x * 16 + (threadIdx.x >> 4);
-  if (w >= NH) return;
-  const long long n = w / H;
-  const int h = (int)(w % H);
-  const uint4 ow = *reinterpret_cast<const uint4*>(out + n * ld_out + h * 128 + 8 * j);
-  const uint4 dw = *reinterpret_cast<const uint4*>(dout + n * ld_out + h * 128 + 8 * j);
-  float s = lo_bf(ow.x) * lo_bf(dw.x) + hi_bf(ow.x) * hi_bf(dw.x) + lo_bf(ow.y) * lo_bf(dw.y) +
-            hi_bf(ow.y) * hi_bf(dw.y) + lo_bf(ow.z) * lo_bf(dw.z) + hi_bf(ow.z) * hi_bf(dw.z) +
-            lo_bf(ow.w) * lo_bf(dw.w) + hi_bf(ow.w) * hi_bf(dw.w);
-#pragma unroll
-  for (int o = 8; o > 0; o >>= 1) s += __shfl_xor(s, o, 64);
-  const long long b = n / T, t = n % T;
-  if (j == 0) delta[(b * H + h) * T + t] = s;
-}
-
 // ---------------------------------------------------------------------------
 // dK, dV
 // ---------------------------------------------------------------------------
@@ -599,9 +580,9 @@ constexpr int DQ_STAGE = 2 * DQ_K * 256;  // K tile + V tile
 template <bool GEN>
 __global__ void __launch_bounds__(256, 2)
 attn_bwd_q_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
-                  long long ld, const uint16_t* __restrict__ dout, long long ld_out, const float* __restrict__ lse,
-                  const float* __restrict__ delta, float* __restrict__ dq_out, int H, int Hkv, int T,
-                  int window_arg) {
+                  long long ld, const uint16_t* __restrict__ out, const uint16_t* __restrict__ dout, long long ld_out,
+                  const float* __restrict__ lse, float* __restrict__ delta, float* __restrict__ dq_out, int H,
+                  int Hkv, int T, int window_arg) {
   __shared__ __attribute__((aligned(16))) char smem[2 * DQ_STAGE];
   const int window = GEN ? window_arg : -1;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, lr = lane & 31, lh = lane >> 5;
@@ -622,18 +603,38 @@ attn_bwd_q_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k
   const int wq0 = q0 + wave * 32;
   const int myq = wq0 + lr;
   bf16x8_t fq[8], fd[8];
+  uint4 ow8[8];  // the same features of O (for delta), loaded in the same batch
   {
     const int qrow = min(myq, T - 1);
+    const uint16_t* oh = out + rowbase * ld_out + h * 128;
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) {
       const uint4 a = ld16(qh + (long long)qrow * ld + ks * 16 + lh * 8);
       const uint4 bq = ld16(doh + (long long)qrow * ld_out + ks * 16 + lh * 8);
+      ow8[ks] = ld16(oh + (long long)qrow * ld_out + ks * 16 + lh * 8);
       fq[ks] = *reinterpret_cast<const bf16x8_t*>(&a);
       fd[ks] = *reinterpret_cast<const bf16x8_t*>(&bq);
     }
   }
   const float lse2 = myq < T ? lse[(long long)bh * T + myq] * kLog2e : INFINITY;
-  const float del = myq < T ? delta[(long long)bh * T + myq] : 0.f;
+  // delta = rowsum(dO * O) of this lane's query: the lane holds half of the
+  // dO row (the fragments above), its partner lane ^ 32 the other half; the
+  // dK/dV kernel, launched after this one, reads the stored values
+  float del;
+  {
+    float part = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      const uint4 ow = ow8[ks];
+      const uint32_t* dw = reinterpret_cast<const uint32_t*>(&fd[ks]);
+      part += lo_bf(ow.x) * lo_bf(dw[0]) + hi_bf(ow.x) * hi_bf(dw[0]) + lo_bf(ow.y) * lo_bf(dw[1]) +
+              hi_bf(ow.y) * hi_bf(dw[1]) + lo_bf(ow.z) * lo_bf(dw[2]) + hi_bf(ow.z) * hi_bf(dw[2]) +
+              lo_bf(ow.w) * lo_bf(dw[3]) + hi_bf(ow.w) * hi_bf(dw[3]);
+    }
+    part += __shfl_xor(part, 32, 64);
+    del = myq < T ? part : 0.f;
+    if (lh == 0 && myq < T) delta[(long long)bh * T + myq] = part;
+  }
 #pragma unroll
   for (int ks = 0; ks < 8; ++ks) {
     settle(fq[ks]);
@@ -742,20 +743,15 @@ int launch_attn_bwd_part(int part, const uint16_t* q, const uint16_t* k, const u
                          int window, hipStream_t s) {
   if (B <= 0 || T <= 0) return 0;
   const bool gen = Hkv != H || window >= 0;
-  if (part == 0) {
-    const long long NH = (long long)B * T * H;
-    hipLaunchKernelGGL(attn_bwd_pre_kernel, dim3((unsigned)((NH + 15) / 16)), dim3(256), 0, s, out, dout, ld_out,
-                       delta, H, T, NH);
-    GS_LAUNCH_CHECK("attn_bwd_pre");
-  } else if (part == 1) {
+  if (part == 0) {  // dQ, and delta for the dK/dV kernel
+    hipLaunchKernelGGL(gen ? attn_bwd_q_kernel<true> : attn_bwd_q_kernel<false>, dim3((T + DQ_Q - 1) / DQ_Q, B * H),
+                       dim3(256), 0, s, q, k, v, ld_qkv, out, dout, ld_out, lse, delta, dq, H, Hkv, T, window);
+    GS_LAUNCH_CHECK("attn_bwd_q");
+  } else {
     hipLaunchKernelGGL(gen ? attn_bwd_kv8_kernel<true> : attn_bwd_kv8_kernel<false>,
                        dim3((T + K8_KEYS - 1) / K8_KEYS, B * Hkv), dim3(K8_NT), 0, s, q, k, v, ld_qkv, dout, ld_out, lse,
                        delta, dk, dv, ld_dkv, H, Hkv, T, window);
     GS_LAUNCH_CHECK("attn_bwd_kv");
-  } else {
-    hipLaunchKernelGGL(gen ? attn_bwd_q_kernel<true> : attn_bwd_q_kernel<false>, dim3((T + DQ_Q - 1) / DQ_Q, B * H), dim3(256), 0, s, q, k, v, ld_qkv,
-                       dout, ld_out, lse, delta, dq, H, Hkv, T, window);
-    GS_LAUNCH_CHECK("attn_bwd_q");
   }
   return 0;
 }
@@ -764,7 +760,7 @@ int launch_attn_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, lon
                     const uint16_t* out, const uint16_t* dout, long long ld_out, const float* lse, float* delta,
                     float* dq, uint16_t* dk, uint16_t* dv, long long ld_dkv, int B, int H, int Hkv, int T,
                     int window, hipStream_t s) {
-  for (int part = 0; part < 3; ++part) {
+  for (int part = 0; part < 2; ++part) {
     const int rc = launch_attn_bwd_part(part, q, k, v, ld_qkv, out, dout, ld_out, lse, delta, dq, dk, dv, ld_dkv, B,
                                         H, Hkv, T, window, s);
     if (rc) return rc;

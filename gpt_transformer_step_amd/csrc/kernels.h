@@ -100,7 +100,8 @@ int launch_attn_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, lon
                     const uint16_t* out, const uint16_t* dout, long long ld_out, const float* lse,
                     float* delta, float* dq, uint16_t* dk, uint16_t* dv, long long ld_dkv, int B,
                     int H, int Hkv, int T, int window, hipStream_t s);
-// one of the three backward kernels: 0 = delta = rowsum(dout * out), 1 = dK/dV, 2 = dQ
+// one of the two backward kernels, in this order: 0 = dQ (also writes delta = rowsum(dout * out)),
+// 1 = dK/dV (reads delta)
 int launch_attn_bwd_part(int part, const uint16_t* q, const uint16_t* k, const uint16_t* v, long long ld_qkv,
                          const uint16_t* out, const uint16_t* dout, long long ld_out, const float* lse, float* delta,
                          float* dq, uint16_t* dk, uint16_t* dv, long long ld_dkv, int B, int H, int Hkv, int T,
