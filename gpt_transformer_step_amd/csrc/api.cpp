@@ -1229,7 +1229,8 @@ int muon_impl(float* Wt, uint16_t* W_bf16, const float* Gm, float* M, float* O_o
       a.M = lrow; a.N = sm; a.K = sm; a.batch = count;
       a.A = Xb[cur]; a.lda = sm; a.sA = sX;
       a.B = Bb; a.ldb = sm; a.sB = sA; a.b_kcontig = 0;
-      a.C = X; a.ldc = sm; a.sC = sX; a.C2 = Xb[cur ^ 1]; a.ldc2 = sm; a.sC2 = sX;
+      a.C = X; a.ldc = sm; a.sC = sX; a.ldc2 = sm; a.sC2 = sX;
+      a.C2 = it + 1 < ns_steps ? Xb[cur ^ 1] : nullptr;  // the last X is read in fp32 only
       a.beta = ca;
       TRY(gemm_bf16(a, EPI_NS_UPD, s));
     }

@@ -291,14 +291,15 @@ __device__ __forceinline__ void epi4(const GemmArgs& p, int bi, int m, int n, co
         o[0] += p.beta * c.x; o[1] += p.beta * c.y; o[2] += p.beta * c.z; o[3] += p.beta * c.w;
       }
       *reinterpret_cast<float4*>(C) = make_float4(o[0], o[1], o[2], o[3]);
-      *reinterpret_cast<uint2*>(C2) = make_uint2(pack_bf2(o[0], o[1]), pack_bf2(o[2], o[3]));
+      if (EPI != EPI_NS_UPD || p.C2)  // the last NS iteration needs no bf16 copy
+        *reinterpret_cast<uint2*>(C2) = make_uint2(pack_bf2(o[0], o[1]), pack_bf2(o[2], o[3]));
     } else {
       for (int j = 0; j < 4; ++j)
         if (n + j < p.N) {
           float x = v[j];
           if (EPI == EPI_NS_UPD) x += p.beta * C[j];
           C[j] = x;
-          C2[j] = f2bf(x);
+          if (EPI != EPI_NS_UPD || p.C2) C2[j] = f2bf(x);
         }
     }
   } else if constexpr (EPI == EPI_CE_BWD) {
