@@ -412,7 +412,7 @@ struct WS {
   size_t cs, x, hf, rf, part, zt, lse, row_loss;
   std::vector<Layer> layer;
   // backward scratch
-  size_t g, g_bf, dh, du, dout, delta, dq_acc, dqkv, dz, wpart;
+  size_t g, g_bf, dh, du, dout, delta, dq_acc, dqkv, dz, wpart, emb;
   // fp8 precision only: codes of the current product input (forward) and of
   // the current output gradient, plain and transposed (backward); scales
   size_t xq, dyq, dyqt, scales, qpart;
@@ -456,6 +456,7 @@ WS ws_layout(const Dims& D) {
   w.du = take(N * D.hidden * 2);
   w.dout = take(N * d * 2);
   w.delta = take(N * H * 4);
+  w.emb = take(embed_bwd_workspace((long long)N, D.V));
   w.dq_acc = take(N * d * 4);
   w.dqkv = take(N * dq3 * 2);
   w.dz = take(N * (size_t)vocab_chunk(D) * 2);
@@ -1041,7 +1042,6 @@ extern "C" gpt_status gpt_step_bwd_scaled(const gpt_shape* shape, const gpt_para
       g_amax_ok = false;
     }
   }
-  if (!acc) { ProfScope ps_(P_FILL, s); TRY(launch_fill_f32(G + P.wte, (long long)D.V * d, 0.f, s)); }
   const float* gemb = g;
   if (f_smear || f_resid) {  // gradient of the embeddings: g + g0 through the smear backward (into dh)
     ProfScope ps_(P_FEATURES, s);
@@ -1050,7 +1050,10 @@ extern "C" gpt_status gpt_step_bwd_scaled(const gpt_shape* shape, const gpt_para
                          d, s));
     gemb = dh;
   }
-  { ProfScope ps_(P_EMBED_BWD, s); TRY(launch_embed_bwd(ids, gemb, G + P.wte, D.B, D.T, d, s)); }
+  {  // writes every row of the embedding gradient (adds to it when accumulating)
+    ProfScope ps_(P_EMBED_BWD, s);
+    TRY(launch_embed_bwd(ids, gemb, G + P.wte, D.B, D.T, d, D.V, acc, at<void>(ws, w.emb), s));
+  }
   return GPT_OK;
 }
 

@@ -81,22 +81,106 @@ __global__ void __launch_bounds__(256) embed_fwd_kernel(const int* __restrict__ 
   }
 }
 
-// dwte[ids[b, t], :] += g[n, :]
-__global__ void __launch_bounds__(256) embed_bwd_kernel(const int* __restrict__ ids, const float* __restrict__ g,
-                                 float* __restrict__ dwte, int B, int T, int d) {
+// Embedding backward without atomics, deterministic: a stable counting sort
+// of the token ids (tokens of one id keep their order), then one wave per
+// vocabulary row sums its tokens' gradient rows in token order.
+//   emb_rank:   per 1024-token block, each token's rank among the block's
+//               tokens of its id, and the block's count of each id (written
+//               by the id's last token in the block; the array is zeroed first)
+//   emb_blocks: per id, exclusive prefix of its counts over the blocks (in
+//               place) and its total
+//   emb_scan:   exclusive prefix of the totals over the ids (one workgroup)
+//   emb_place:  token n goes to position off[id] + block prefix + rank
+//   emb_gather: dwte[v] (+)= sum of g over the tokens of v
+constexpr int kEmbBlk = 1024;
+__device__ __forceinline__ int token_id(const int* ids, long long n, int T) {
+  return ids[(n / T) * (T + 1) + n % T];
+}
+
+__global__ void __launch_bounds__(kEmbBlk) emb_rank_kernel(const int* __restrict__ ids, long long N, int T, int V,
+                                                           int* __restrict__ blockcnt, int* __restrict__ rank) {
+  __shared__ int sid[kEmbBlk];
+  const long long n0 = (long long)blockIdx.x * kEmbBlk;
+  const int cnt = (int)min((long long)kEmbBlk, N - n0);
+  const int t = threadIdx.x;
+  sid[t] = t < cnt ? token_id(ids, n0 + t, T) : -1;
+  __syncthreads();
+  if (t >= cnt) return;
+  const int id = sid[t];
+  int r = 0;
+  bool last = true;
+  for (int j = 0; j < cnt; ++j) {
+    const bool same = sid[j] == id;
+    r += (same && j < t) ? 1 : 0;
+    last = last && !(same && j > t);
+  }
+  rank[n0 + t] = r;
+  if (last) blockcnt[(long long)blockIdx.x * V + id] = r + 1;
+}
+
+__global__ void __launch_bounds__(256) emb_blocks_kernel(int* __restrict__ blockcnt, int nb, int V,
+                                                         int* __restrict__ total) {
+  const int v = blockIdx.x * 256 + threadIdx.x;
+  if (v >= V) return;
+  int run = 0;
+  for (int b = 0; b < nb; ++b) {
+    const int c = blockcnt[(long long)b * V + v];
+    blockcnt[(long long)b * V + v] = run;
+    run += c;
+  }
+  total[v] = run;
+}
+
+// off[v] = sum of total[u] for u < v, off[V] = N; one workgroup of 1024
+__global__ void __launch_bounds__(1024) emb_scan_kernel(const int* __restrict__ total, int V, int* __restrict__ off) {
+  __shared__ int part[1024];
+  const int t = threadIdx.x;
+  const int per = (V + 1023) / 1024;
+  const int beg = min(V, t * per), end = min(V, beg + per);
+  int s = 0;
+  for (int v = beg; v < end; ++v) s += total[v];
+  part[t] = s;
+  __syncthreads();
+  for (int o = 1; o < 1024; o <<= 1) {  // inclusive scan over the 1024 partial sums
+    const int x = t >= o ? part[t - o] : 0;
+    __syncthreads();
+    part[t] += x;
+    __syncthreads();
+  }
+  int run = part[t] - s;
+  for (int v = beg; v < end; ++v) {
+    off[v] = run;
+    run += total[v];
+  }
+  if (t == 1023) off[V] = part[1023];
+}
+
+__global__ void __launch_bounds__(256) emb_place_kernel(const int* __restrict__ ids, long long N, int T, int V,
+                                                        const int* __restrict__ blockcnt, const int* __restrict__ rank,
+                                                        const int* __restrict__ off, int* __restrict__ perm) {
+  const long long n = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (n >= N) return;
+  const int id = token_id(ids, n, T);
+  const long long b = n / kEmbBlk;
+  perm[off[id] + blockcnt[b * V + id] + rank[n]] = (int)n;
+}
+
+// one wave per vocabulary row; d a multiple of 4
+__global__ void __launch_bounds__(256) emb_gather_kernel(const int* __restrict__ off, const int* __restrict__ perm,
+                                                         const float* __restrict__ g, float* __restrict__ dwte, int V,
+                                                         int d, int accumulate) {
   const int lane = threadIdx.x & 63;
-  const long long n = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (n >= (long long)B * T) return;
-  const int b = (int)(n / T), t = (int)(n % T);
-  const long long id = ids[(long long)b * (T + 1) + t];
-  float* dst = dwte + id * d;
-  const float* src = g + n * d;
+  const int v = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (v >= V) return;
+  const int beg = off[v], end = off[v + 1];
+  float* dst = dwte + (long long)v * d;
   for (int c = lane; c < d / 4; c += 64) {
-    const float4 v = *reinterpret_cast<const float4*>(src + c * 4);
-    unsafeAtomicAdd(dst + c * 4 + 0, v.x);
-    unsafeAtomicAdd(dst + c * 4 + 1, v.y);
-    unsafeAtomicAdd(dst + c * 4 + 2, v.z);
-    unsafeAtomicAdd(dst + c * 4 + 3, v.w);
+    float4 a = accumulate ? *reinterpret_cast<const float4*>(dst + c * 4) : make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int j = beg; j < end; ++j) {
+      const float4 x = *reinterpret_cast<const float4*>(g + (long long)perm[j] * d + c * 4);
+      a.x += x.x; a.y += x.y; a.z += x.z; a.w += x.w;
+    }
+    *reinterpret_cast<float4*>(dst + c * 4) = a;
   }
 }
 
@@ -662,9 +746,37 @@ int launch_embed_fwd(const int* ids, const uint16_t* wte, float* x, int B, int T
   return 0;
 }
 
-int launch_embed_bwd(const int* ids, const float* g, float* dwte, int B, int T, int d, hipStream_t s) {
-  hipLaunchKernelGGL(embed_bwd_kernel, dim3(nblocks((long long)B * T, 4)), dim3(256), 0, s, ids, g, dwte, B, T, d);
-  GS_LAUNCH_CHECK("embed_bwd");
+size_t embed_bwd_workspace(long long N, int V) {
+  const long long nb = (N + kEmbBlk - 1) / kEmbBlk;
+  return (size_t)(nb * V + V + (V + 1) + 2 * N) * 4;
+}
+
+int launch_embed_bwd(const int* ids, const float* g, float* dwte, int B, int T, int d, int V, bool accumulate,
+                     void* ws, hipStream_t s) {
+  const long long N = (long long)B * T;
+  if (N <= 0 || V <= 0) return 0;
+  const int nb = (int)((N + kEmbBlk - 1) / kEmbBlk);
+  int* blockcnt = static_cast<int*>(ws);
+  int* total = blockcnt + (long long)nb * V;
+  int* off = total + V;
+  int* rank = off + V + 1;
+  int* perm = rank + N;
+  {
+    const int rc = launch_fill_f32(reinterpret_cast<float*>(blockcnt), (long long)nb * V, 0.f, s);  // int 0 = float 0
+    if (rc) return rc;
+  }
+  hipLaunchKernelGGL(emb_rank_kernel, dim3(nb), dim3(kEmbBlk), 0, s, ids, N, T, V, blockcnt, rank);
+  GS_LAUNCH_CHECK("emb_rank");
+  hipLaunchKernelGGL(emb_blocks_kernel, dim3((V + 255) / 256), dim3(256), 0, s, blockcnt, nb, V, total);
+  GS_LAUNCH_CHECK("emb_blocks");
+  hipLaunchKernelGGL(emb_scan_kernel, dim3(1), dim3(1024), 0, s, total, V, off);
+  GS_LAUNCH_CHECK("emb_scan");
+  hipLaunchKernelGGL(emb_place_kernel, dim3((unsigned)((N + 255) / 256)), dim3(256), 0, s, ids, N, T, V, blockcnt,
+                     rank, off, perm);
+  GS_LAUNCH_CHECK("emb_place");
+  hipLaunchKernelGGL(emb_gather_kernel, dim3((V + 3) / 4), dim3(256), 0, s, off, perm, g, dwte, V, d,
+                     accumulate ? 1 : 0);
+  GS_LAUNCH_CHECK("emb_gather");
   return 0;
 }
 

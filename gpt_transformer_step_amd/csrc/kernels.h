@@ -12,7 +12,11 @@ int launch_fill_f32(float* p, long long n, float v, hipStream_t s);
 int launch_cast_bf16(const float* src, uint16_t* dst, long long n, hipStream_t s);
 int launch_rope_table(float* cos_sin /* [T, 64] cos then [T, 64] sin */, int T, hipStream_t s);
 int launch_embed_fwd(const int* ids, const uint16_t* wte, float* x, int B, int T, int d, hipStream_t s);
-int launch_embed_bwd(const int* ids, const float* g, float* dwte, int B, int T, int d, hipStream_t s);
+// dwte[v] (+)= sum of g rows of the tokens with id v (ids in [0, V), rows of
+// T + 1 ids per sequence); ws holds embed_bwd_workspace(B T, V) bytes
+size_t embed_bwd_workspace(long long N, int V);
+int launch_embed_bwd(const int* ids, const float* g, float* dwte, int B, int T, int d, int V, bool accumulate,
+                     void* ws, hipStream_t s);
 // amax_part (nullable): per-row max |stored bf16 value| at amax_part[row]
 int launch_rmsnorm_fwd(const float* x, uint16_t* h, float* r, long long N, int d, hipStream_t s,
                        float* amax_part = nullptr);
