@@ -647,7 +647,7 @@ __global__ void __launch_bounds__(256) nm_finalize_kernel(const float* __restric
 
 // output tiles over W [rows, cols]; X oriented [l, s] (transposed when TR);
 // nsc (nullable): NorMuon scale per row (nm_rows) or per column of W
-template <bool TR>
+template <bool TR, bool VEC>
 __global__ void muon_apply_kernel(const float* __restrict__ X, float* __restrict__ W, uint16_t* __restrict__ Wb,
                                   float* __restrict__ O_out, int rows, int cols, float lr, float wd,
                                   const float* __restrict__ nsc, int nm_rows) {
@@ -666,6 +666,37 @@ __global__ void muon_apply_kernel(const float* __restrict__ X, float* __restrict
     __syncthreads();
   }
   const float decay = 1.f - lr * wd;
+  if (VEC) {
+    // 4 consecutive columns per thread: cols % 8 == 0 and 16-byte aligned
+    // X, W, O_out (8-byte aligned Wb), checked by the launcher
+    for (int e = threadIdx.x; e < 64 * 16; e += 256) {
+      const int rr = e / 16, c4 = (e % 16) * 4;
+      const int gr = r0 + rr, gc = c0 + c4;
+      if (gr < rows && gc < cols) {
+        const long long idx = (long long)gr * cols + gc;
+        float o[4];
+        if (TR) {
+          o[0] = tile[c4][rr]; o[1] = tile[c4 + 1][rr]; o[2] = tile[c4 + 2][rr]; o[3] = tile[c4 + 3][rr];
+        } else {
+          const float4 v = *reinterpret_cast<const float4*>(x + idx);
+          o[0] = v.x; o[1] = v.y; o[2] = v.z; o[3] = v.w;
+        }
+        if (nsc) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) o[j] *= nm_rows ? nsc[(long long)b * rows + gr] : nsc[(long long)b * cols + gc + j];
+        }
+        if (O_out) *reinterpret_cast<float4*>(O_out + base + idx) = make_float4(o[0], o[1], o[2], o[3]);
+        if (W) {
+          float4 w = *reinterpret_cast<const float4*>(W + base + idx);
+          w.x = w.x * decay - lr * o[0]; w.y = w.y * decay - lr * o[1];
+          w.z = w.z * decay - lr * o[2]; w.w = w.w * decay - lr * o[3];
+          *reinterpret_cast<float4*>(W + base + idx) = w;
+          if (Wb) *reinterpret_cast<uint2*>(Wb + base + idx) = make_uint2(pack_bf2(w.x, w.y), pack_bf2(w.z, w.w));
+        }
+      }
+    }
+    return;
+  }
   for (int e = threadIdx.x; e < 64 * 64; e += 256) {
     const int rr = e / 64, cc = e % 64;
     const int gr = r0 + rr, gc = c0 + cc;
@@ -936,12 +967,16 @@ int launch_muon_apply(const float* X, float* W, uint16_t* Wb, float* O_out, int 
                       float lr, float wd, const float* nsc, int nm_rows, hipStream_t s) {
   const bool tr = rows < cols;
   dim3 grid((cols + 63) / 64, (rows + 63) / 64, count);
-  if (tr)
-    hipLaunchKernelGGL(muon_apply_kernel<true>, grid, dim3(256), 0, s, X, W, Wb, O_out, rows, cols, lr, wd, nsc,
-                       nm_rows);
-  else
-    hipLaunchKernelGGL(muon_apply_kernel<false>, grid, dim3(256), 0, s, X, W, Wb, O_out, rows, cols, lr, wd, nsc,
-                       nm_rows);
+  auto al = [](const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; };
+  const bool vec = cols % 4 == 0 && al(X, 16) && al(W, 16) && al(O_out, 16) && al(Wb, 8);
+#define GS_MA(T_, V_) hipLaunchKernelGGL((muon_apply_kernel<T_, V_>), grid, dim3(256), 0, s, X, W, Wb, O_out, rows, \
+                                         cols, lr, wd, nsc, nm_rows)
+  if (tr) {
+    if (vec) GS_MA(true, true); else GS_MA(true, false);
+  } else {
+    if (vec) GS_MA(false, true); else GS_MA(false, false);
+  }
+#undef GS_MA
   GS_LAUNCH_CHECK("muon_apply");
   return 0;
 }
