@@ -78,6 +78,48 @@ def test_standalone_ns_full_size(B, rows, cols):
     assert e <= 1e-2 and c >= 0.999
 
 
+# The groups one step updates, at the batch sizes the step uses: the S, F and
+# P groups of the depth-20 model (4 x 20 [1280, 1280], 20 [5120, 1280], 20
+# [1280, 5120]) and the depth-26 square group (4 x 26 [1664, 1664], ragged
+# 256-row tiles).  These batches have more 256x256 tiles than the big-tile
+# threshold, so the Gram and polynomial products run on 256x256 tiles with
+# only the tiles on and above the diagonal computed and the bf16 copies
+# mirrored -- the launches the benchmark times.  The whole batch runs in one
+# call; three matrices (first, middle, last) are compared with the float64
+# oracle.
+BENCH_GROUPS = [(80, 1280, 1280), (20, 5120, 1280), (20, 1280, 5120), (104, 1664, 1664)]
+
+
+def _group_inputs(count, rows, cols, seed):
+    g = np.random.Generator(np.random.PCG64(seed))
+    W = g.standard_normal((count, rows, cols), dtype=np.float32) * np.float32(0.02)
+    G = g.standard_normal((count, rows, cols), dtype=np.float32) * np.float32(1e-3)
+    M = g.standard_normal((count, rows, cols), dtype=np.float32) * np.float32(1e-3)
+    return W, G, M
+
+
+@pytest.mark.parametrize("count,rows,cols", BENCH_GROUPS)
+def test_muon_update_bench_groups(B, count, rows, cols):
+    say(f"muon bench group count={count} {rows}x{cols}")
+    W, G, M = _group_inputs(count, rows, cols, rows + cols + count)
+    dW, dG, dM = (torch.from_numpy(a).cuda() for a in (W, G, M))
+    dWb = torch.empty((count, rows, cols), dtype=torch.bfloat16, device="cuda")
+    dO = torch.empty((count, rows, cols), dtype=torch.float32, device="cuda")
+    ws = torch.empty(B.muon_workspace_size(count, rows, cols), dtype=torch.uint8, device="cuda")
+    lr, mu, wd = 0.02, 0.95, 0.1
+    B.muon_update(dG, NS5, ws, W=dW, W_bf16=dWb, M=dM, O_out=dO, lr=lr, momentum=mu, weight_decay=wd)
+    torch.cuda.synchronize()
+    for i in (0, count // 2, count - 1):
+        Wn, Mn, O = om.muon_update(W[i], G[i], M[i], NS5, lr, mu, wd)
+        got = dO[i].cpu().numpy()
+        e, c = rel_l2(got, O), cosine(got, O)
+        say(f"  [{i}] O rel_l2 {e:.3e} cos {c:.6f}")
+        assert e <= 1e-2 and c >= 0.999
+        assert rel_l2(dM[i].cpu().numpy(), Mn) < 1e-6
+        assert np.abs(dW[i].cpu().numpy() - Wn).max() <= 1e-2 * lr * np.abs(O).max() + 1e-6
+        assert torch.equal(dWb[i], dW[i].to(torch.bfloat16))
+
+
 def test_muon_rejects_bad_args(B):
     G = torch.zeros((1, 64, 64), device="cuda")
     ws = torch.empty(B.muon_workspace_size(1, 64, 64), dtype=torch.uint8, device="cuda")

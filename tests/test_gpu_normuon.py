@@ -86,3 +86,45 @@ def test_normuon_keeps_update_norm_on_gpu(B):
         say(f"  [{i}] ||O|| {n0:.6f} ||O'|| {n1:.6f} neuron RMS spread {rms.max() / rms.min() - 1:.2e}")
         assert abs(n1 - n0) <= 1e-5 * n0
         assert np.allclose(rms, n0 / np.sqrt(rows * cols), rtol=1e-4)
+
+
+# The depth-20 and depth-26 groups at the batch sizes the step uses (see the
+# Muon test of the same name): the Newton-Schulz products take the 256x256
+# symmetric tiles, and the per-neuron statistics run over full batches.  Two
+# steps, so the second-moment history enters; three matrices compared.
+BENCH_GROUPS = [(80, 1280, 1280), (20, 5120, 1280), (20, 1280, 5120), (104, 1664, 1664)]
+
+
+@pytest.mark.parametrize("count,rows,cols", BENCH_GROUPS)
+def test_normuon_update_bench_groups(B, count, rows, cols):
+    per_row = True
+    say(f"normuon bench group count={count} {rows}x{cols}")
+    g = np.random.Generator(np.random.PCG64(rows * 7 + cols + count))
+    W = g.standard_normal((count, rows, cols), dtype=np.float32) * np.float32(0.02)
+    dW = torch.from_numpy(W).cuda()
+    dM = torch.zeros((count, rows, cols), dtype=torch.float32, device="cuda")
+    dV = torch.zeros((count, rows), dtype=torch.float32, device="cuda")
+    dWb = torch.empty((count, rows, cols), dtype=torch.bfloat16, device="cuda")
+    dO = torch.empty((count, rows, cols), dtype=torch.float32, device="cuda")
+    ws = torch.empty(B.muon_workspace_size(count, rows, cols), dtype=torch.uint8, device="cuda")
+    lr, mu, wd, beta2, eps = 0.02, 0.95, 0.1, 0.95, 1e-8
+    pick = (0, count // 2, count - 1)
+    rW = {i: W[i].astype(np.float64) for i in pick}
+    rM = {i: np.zeros((rows, cols)) for i in pick}
+    rV = {i: np.zeros(rows) for i in pick}
+    for step in range(2):
+        sc = np.exp(g.uniform(-2, 2, (count, rows, 1))).astype(np.float32)
+        G = g.standard_normal((count, rows, cols), dtype=np.float32) * sc * np.float32(1e-3)
+        B.normuon_update(torch.from_numpy(G).cuda(), NS5, ws, dV, W=dW, W_bf16=dWb, M=dM, O_out=dO, lr=lr,
+                         momentum=mu, weight_decay=wd, beta2=beta2, eps=eps, per_row=per_row)
+        torch.cuda.synchronize()
+        for i in pick:
+            rW[i], rM[i], O = om.normuon_update(rW[i], G[i], rM[i], rV[i], NS5, lr, mu, wd, beta2=beta2, eps_v=eps,
+                                                axis=1)
+            got = dO[i].cpu().numpy()
+            e, c = rel_l2(got, O), cosine(got, O)
+            ev = rel_l2(dV[i].cpu().numpy(), rV[i])
+            say(f"  step {step} [{i}] O' rel_l2 {e:.3e} cos {c:.6f}  V rel_l2 {ev:.3e}")
+            assert e <= 1e-2 and c >= 0.999 and ev <= 1e-2
+            assert np.abs(dW[i].cpu().numpy() - rW[i]).max() <= 1e-2 * lr * np.abs(O).max() + 1e-6
+            assert torch.equal(dWb[i], dW[i].to(torch.bfloat16))
