@@ -135,6 +135,7 @@ class Config:
 # ----------------------------------------------------------------------------
 
 SMEAR_CH = 24      # embedding channels feeding the smear gate (as printed)
+BF16_JITTER = 2.0 ** -24   # relative perturbation before a bf16 rounding (fp32 unit roundoff)
 VE_GATE_CH = 32    # channels of the attention input feeding the value-embedding gate
 
 
@@ -190,10 +191,11 @@ def attention_mask(T, window=None):
     return m
 
 
-def causal_attention(q, k, v, window=None):
+def causal_attention(q, k, v, window=None, rnd=None):
     """softmax(q k^T / sqrt(hd) with masked keys removed) v (attention_mask).
     q, k, v: [..., T, hd].  Returns (y, lse) with lse the row log-sum-exp of
-    the scaled, masked scores."""
+    the scaled, masked scores.  rnd (optional): the rounding applied to the
+    probabilities as the operand of the product with v (bf16 mode)."""
     T, hd = q.shape[-2], q.shape[-1]
     s = (q @ np.swapaxes(k, -1, -2)) / np.sqrt(hd)
     mask = attention_mask(T, window)
@@ -203,22 +205,27 @@ def causal_attention(q, k, v, window=None):
     den = np.sum(e, axis=-1, keepdims=True)
     p = e / den
     lse = (m + np.log(den))[..., 0]
+    if rnd is not None:
+        p = rnd(p)
     return p @ v, lse
 
 
-def causal_attention_bwd(q, k, v, y, dy, lse, window=None):
+def causal_attention_bwd(q, k, v, y, dy, lse, window=None, rnd=None):
     """Backward of causal_attention with P recomputed from lse:
     dV = P^T dY; dP = dY V^T; dS = P * (dP - rowsum(dY * Y)); dQ = dS K / sqrt(hd);
-    dK = dS^T Q / sqrt(hd)."""
+    dK = dS^T Q / sqrt(hd).  rnd (optional): the rounding applied to P and dS
+    as operands of the products dV, dQ and dK (bf16 mode)."""
     T, hd = q.shape[-2], q.shape[-1]
     scale = 1.0 / np.sqrt(hd)
     s = (q @ np.swapaxes(k, -1, -2)) * scale
     mask = attention_mask(T, window)
     p = np.where(mask, 0.0, np.exp(s - lse[..., None]))
-    dv = np.swapaxes(p, -1, -2) @ dy
+    dv = np.swapaxes(p if rnd is None else rnd(p), -1, -2) @ dy
     dp = dy @ np.swapaxes(v, -1, -2)
     dsum = np.sum(dy * y, axis=-1, keepdims=True)
     ds = p * (dp - dsum)
+    if rnd is not None:
+        ds = rnd(ds)
     dq = (ds @ k) * scale
     dk = (np.swapaxes(ds, -1, -2) @ q) * scale
     return dq, dk, dv
@@ -301,7 +308,7 @@ def param_shapes(cfg):
 # the step
 # ----------------------------------------------------------------------------
 
-def _forward_backward_chunk(P, ids, cfg, loss_scale, dtype, want_grads, want_logits, fp8, cos, sin, op):
+def _forward_backward_chunk(P, ids, cfg, loss_scale, dtype, want_grads, want_logits, fp8, cos, sin, op, rnd):
     B, T1 = ids.shape
     T = T1 - 1
     d, H, hd = cfg.d_model, cfg.n_head, cfg.head_dim
@@ -352,7 +359,7 @@ def _forward_backward_chunk(P, ids, cfg, loss_scale, dtype, want_grads, want_log
         qs, ks = op(qn), op(kn)
         # query head h reads key/value head h // G
         win = cfg.layer_window(i)
-        y, lse_att = causal_attention(qs, np.repeat(ks, G, axis=1), np.repeat(v, G, axis=1), win)
+        y, lse_att = causal_attention(qs, np.repeat(ks, G, axis=1), np.repeat(v, G, axis=1), win, rnd=rnd)
         y2 = op(y.transpose(0, 2, 1, 3).reshape(R, d))
         x = x + _lin_fwd(y2, P[f"wo.{i}"], fp8)
         h2, r2 = rms_norm(x, eps)
@@ -382,7 +389,7 @@ def _forward_backward_chunk(P, ids, cfg, loss_scale, dtype, want_grads, want_log
     dz = op(cross_entropy_bwd(z, tgt, lse, loss_scale))
     del z
     Gr["lm_head"] = dz.T @ hfo
-    g = rms_norm_bwd(dz @ P["lm_head"], hf, rf)
+    g = rms_norm_bwd(dz @ P["lm_head"], hfo, rf)
     del dz
     # the scalar gradients are sums over every stream element whose terms cancel
     # to a small fraction of their magnitudes; Gabs holds the sum of the
@@ -405,21 +412,22 @@ def _forward_backward_chunk(P, ids, cfg, loss_scale, dtype, want_grads, want_log
         # MLP
         gb = op(g)
         da, Gr[f"wproj.{i}"] = _lin_bwd(a, P[f"wproj.{i}"], gb, fp8)
-        du = op(da * 2.0 * np.maximum(u, 0.0))
+        # d relu(u)^2 / du = 2 relu(u) = 2 sqrt(a), read from the stored activation
+        du = op(da * 2.0 * np.sqrt(a))
         dh2, Gr[f"wfc.{i}"] = _lin_bwd(h2o, P[f"wfc.{i}"], du, fp8)
-        g = g + rms_norm_bwd(dh2, h2, r2)
+        g = g + rms_norm_bwd(dh2, h2o, r2)
         # attention
         gb = op(g)
         dy2, Gr[f"wo.{i}"] = _lin_bwd(y2, P[f"wo.{i}"], gb, fp8)
         dy = op(dy2).reshape(B, T, H, hd).transpose(0, 2, 1, 3)
         y = y2.reshape(B, T, H, hd).transpose(0, 2, 1, 3)
         dqn, dkf, dvf = causal_attention_bwd(qs, np.repeat(ks, G, axis=1), np.repeat(v, G, axis=1), y, dy,
-                                             lse_att, cfg.layer_window(i))
+                                             lse_att, cfg.layer_window(i), rnd=rnd)
         # a key/value head collects the gradients of its G query heads
         dkn = dkf.reshape(B, Hkv, G, T, hd).sum(axis=2)
         dv = dvf.reshape(B, Hkv, G, T, hd).sum(axis=2)
-        dq = rope_bwd(rms_norm_bwd(dqn, qn, rq), cos, sin)
-        dk = rope_bwd(rms_norm_bwd(dkn, kn, rk), cos, sin)
+        dq = rope_bwd(rms_norm_bwd(dqn, qs, rq), cos, sin)
+        dk = rope_bwd(rms_norm_bwd(dkn, ks, rk), cos, sin)
         dqkv = op(np.concatenate([t.transpose(0, 2, 1, 3).reshape(R, -1) for t in (dq, dk, dv)], axis=1))
         dh1, dwqkv = _lin_bwd(h1o, wqkv, dqkv, fp8)
         Gr[f"wq.{i}"], Gr[f"wk.{i}"], Gr[f"wv.{i}"] = dwqkv[:d], dwqkv[d:d + dkv], dwqkv[d + dkv:]
@@ -433,7 +441,7 @@ def _forward_backward_chunk(P, ids, cfg, loss_scale, dtype, want_grads, want_log
             Gr[f"ve_gate.{i}"] = dzg.T @ h1o[:, :VE_GATE_CH]
             dh1 = dh1.copy()
             dh1[:, :VE_GATE_CH] += dzg @ P[f"ve_gate.{i}"]
-        g = g + rms_norm_bwd(dh1, h1, r1)
+        g = g + rms_norm_bwd(dh1, h1o, r1)
         if cfg.resid_lambdas:
             # x = resid_lambda x_in + x0_lambda x0
             Gr["resid_lambda"][i] = np.sum(g * x_in)
@@ -474,7 +482,7 @@ def _forward_backward_chunk(P, ids, cfg, loss_scale, dtype, want_grads, want_log
 
 
 def forward_backward(P, ids, cfg, dtype=np.float64, want_grads=True, want_logits=False,
-                     fp8=False, seq_chunk=None, bf16_operands=False):
+                     fp8=False, seq_chunk=None, bf16_operands=False, jitter_seed=None):
     """One training step's forward and backward.
 
     P: dict name -> array (the bf16-rounded weight values, see precision.py);
@@ -486,17 +494,33 @@ def forward_backward(P, ids, cfg, dtype=np.float64, want_grads=True, want_logits
     are independent up to the loss mean); not allowed with fp8, whose
     per-tensor scales span the whole batch.
 
-    bf16_operands: every operand of a matrix product holds bf16 values -- the
-    precision passage's compute dtype (dev.to "3. Gestión de Precisión":
-    F.linear(x, W.to(x.dtype)) with x in bf16 on bf16-capable GPUs; the
-    attention call receives bf16 q, k, v).  The activations entering a
-    product (normed inputs, q/k/v, attention output, ReLU^2 output, head
-    input) and the gradients entering a product (dlogits, residual gradient,
-    MLP hidden gradient, attention output gradient, q/k/v gradient) are
-    rounded to bf16 (nearest even); products accumulate in `dtype`; norms,
-    rotary, softmax and the residual stream stay in `dtype`.  With False
-    (default) nothing is rounded and the result is the exact function of the
-    bf16 weights.
+    bf16_operands: the precision passage's compute dtype (dev.to "3. Gestión
+    de Precisión": the weight is cast to the activation's dtype for every
+    matrix product, bf16 on bf16-capable GPUs; the flash-attention call takes
+    bf16 q, k, v).  Reading taken: every operand of every matrix product holds
+    bf16 values, and an activation is kept once, in bf16, for the backward.
+    Rounded (nearest even), in the forward: the normed block inputs h1, h2
+    and the head input; q and k after rotary + QK norm; v; the attention
+    probabilities P as the operand of P v; the attention output; the ReLU^2
+    output a.  In the backward: dlogits; the residual gradient entering the
+    output projections' products; the MLP hidden gradient du; the attention
+    output gradient dO; P and dS as operands of dV = P^T dO, dQ = dS K and
+    dK = dS^T Q; the q/k/v gradient.  The ReLU^2 derivative 2 relu(u) is read
+    from the stored activation as 2 sqrt(a), and each RMS-norm backward reads
+    its stored (rounded) output.  Products accumulate in `dtype`; norm
+    statistics, rotary, softmax and the residual stream stay in `dtype`.
+    With False (default) nothing is rounded and the result is the exact
+    function of the bf16 weights (2 sqrt(relu(u)^2) = 2 relu(u) exactly).
+
+    jitter_seed (bf16 mode only): every value is multiplied by
+    (1 + 2^-24 xi), xi ~ N(0, 1) from PCG64(jitter_seed), right before it is
+    rounded to bf16.  2^-24 is the fp32 unit roundoff: each seed gives one
+    more bf16 computation of the step whose products were summed in another
+    fp32 order.  A chain of bf16 roundings is chaotic at the level of its own
+    rounding noise (a relative change far below one bf16 ulp flips a few
+    roundings, whose changes flip more), so a set of seeds measures how far
+    any bf16 computation of the step lands from the exact result -- the
+    spread a correct bf16 implementation cannot get below.
 
     ``grad_abs`` (with the record-model features): for each scalar parameter's
     gradient, a sum over every stream element, the sum of its terms' absolute
@@ -507,12 +531,19 @@ def forward_backward(P, ids, cfg, dtype=np.float64, want_grads=True, want_logits
     T = T1 - 1
     P = {k: np.asarray(v, dtype=dtype) for k, v in P.items()}
     cos, sin = rope_tables(T, cfg.head_dim, cfg.rope_base, dtype)
+    if jitter_seed is not None and not bf16_operands:
+        raise ValueError("jitter_seed perturbs the bf16 roundings; it needs bf16_operands=True")
+    jit = np.random.Generator(np.random.PCG64(jitter_seed)) if jitter_seed is not None else None
     if bf16_operands:
         def op(t):
+            if jit is not None:
+                t = t * (1.0 + BF16_JITTER * jit.standard_normal(np.shape(t)))
             return _precision.round_bf16(t).astype(dtype)
+        rnd = op
     else:
         def op(t):
             return t
+        rnd = None
     loss_scale = 1.0 / (B * T)
     if seq_chunk is None or seq_chunk >= B:
         chunks = [(0, B)]
@@ -523,7 +554,7 @@ def forward_backward(P, ids, cfg, dtype=np.float64, want_grads=True, want_logits
     total, grads, gabs, row_loss, lse, logits = 0.0, None, None, [], [], []
     for s, e in chunks:
         o = _forward_backward_chunk(P, ids[s:e], cfg, loss_scale, dtype, want_grads,
-                                    want_logits, fp8, cos, sin, op)
+                                    want_logits, fp8, cos, sin, op, rnd)
         total += o["loss_sum"]
         row_loss.append(o["row_loss"])
         lse.append(o["lse"])
