@@ -20,10 +20,11 @@ def bf16_bits(x):
     NaN inputs map to a quiet NaN; overflow past the largest finite bf16
     rounds to infinity (IEEE behaviour)."""
     x = np.ascontiguousarray(x, dtype=np.float32)
-    u = x.view(np.uint32).astype(np.uint64)
-    lsb = (u >> 16) & 1
-    rounded = (u + 0x7FFF + lsb) >> 16
-    out = rounded.astype(np.uint16)
+    u = x.view(np.uint32)
+    # u + 0x7FFF + lsb stays below 2^32 for every non-NaN pattern (the largest,
+    # -inf = 0xFF800000, gains at most 0x8000); NaNs are patched below
+    rounded = u + (np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1)))
+    out = (rounded >> np.uint32(16)).astype(np.uint16)
     nan = np.isnan(x)
     if nan.any():
         out[nan] = ((u[nan] >> 16) | 0x40).astype(np.uint16)
