@@ -289,14 +289,14 @@ namespace {
 enum ProfCat {
   P_EMBED_FWD, P_RMSNORM_FWD, P_GEMM_QKV, P_ATTN_FWD, P_GEMM_O, P_GEMM_FC, P_GEMM_PROJ, P_CE_FWD,
   P_CE_REDUCE, P_CE_DZ, P_CE_DH, P_CE_DW, P_RMSNORM_BWD, P_PROJ_DGRAD, P_PROJ_WGRAD, P_FC_DGRAD,
-  P_FC_WGRAD, P_O_DGRAD, P_O_WGRAD, P_ATTN_BWD_KV, P_ATTN_BWD_Q, P_ROPE_BWD, P_QKV_DGRAD, P_QKV_WGRAD, P_EMBED_BWD,
+  P_FC_WGRAD, P_O_DGRAD, P_O_WGRAD, P_ATTN_BWD_KV, P_ATTN_BWD_Q, P_QKV_DGRAD, P_QKV_WGRAD, P_EMBED_BWD,
   P_FILL, P_MUON_ELEMWISE, P_NS_GRAM, P_NS_POLY, P_NS_UPDATE, P_FP8_QUANT, P_ADAMW, P_FEATURES, P_COUNT
 };
 const char* kProfNames[P_COUNT] = {
     "embed_fwd", "rmsnorm_fwd", "gemm_qkv_rope_fwd", "attn_fwd", "gemm_o_fwd", "gemm_fc_relu2_fwd",
     "gemm_proj_fwd", "gemm_ce_fwd", "ce_reduce", "gemm_ce_dlogits", "gemm_ce_dh", "gemm_ce_dw",
     "rmsnorm_bwd", "gemm_proj_dgrad", "gemm_proj_wgrad", "gemm_fc_dgrad", "gemm_fc_wgrad",
-    "gemm_o_dgrad", "gemm_o_wgrad", "attn_bwd_dkdv", "attn_bwd_dq", "rope_qknorm_bwd", "gemm_qkv_dgrad", "gemm_qkv_wgrad",
+    "gemm_o_dgrad", "gemm_o_wgrad", "attn_bwd_dkdv", "attn_bwd_dq", "gemm_qkv_dgrad", "gemm_qkv_wgrad",
     "embed_bwd", "fill", "muon_elementwise", "ns_gram", "ns_poly", "ns_update", "fp8_quant", "adamw", "features"};
 
 struct Profiler {
@@ -412,7 +412,7 @@ struct WS {
   size_t cs, x, hf, rf, part, zt, lse, row_loss;
   std::vector<Layer> layer;
   // backward scratch
-  size_t g, g_bf, dh, du, dout, delta, dq_acc, dqkv, dz, wpart, emb;
+  size_t g, g_bf, dh, du, dout, delta, dqkv, dz, wpart, emb;
   // fp8 precision only: codes of the current product input (forward) and of
   // the current output gradient, plain and transposed (backward); scales
   size_t xq, dyq, dyqt, scales, qpart;
@@ -457,7 +457,6 @@ WS ws_layout(const Dims& D) {
   w.dout = take(N * d * 2);
   w.delta = take(N * H * 4);
   w.emb = take(embed_bwd_workspace((long long)N, D.V));
-  w.dq_acc = take(N * d * 4);
   w.dqkv = take(N * dq3 * 2);
   w.dz = take(N * (size_t)vocab_chunk(D) * 2);
   {
@@ -864,7 +863,6 @@ extern "C" gpt_status gpt_step_bwd_scaled(const gpt_shape* shape, const gpt_para
   uint16_t* du = at<uint16_t>(ws, w.du);
   uint16_t* dout = at<uint16_t>(ws, w.dout);
   uint16_t* dqkv = at<uint16_t>(ws, w.dqkv);
-  float* dq_acc = at<float>(ws, w.dq_acc);
   uint16_t* dz = at<uint16_t>(ws, w.dz);
   float* wpart = at<float>(ws, w.wpart);
   const float* cs = at<float>(ws, w.cs);
@@ -1000,13 +998,15 @@ extern "C" gpt_status gpt_step_bwd_scaled(const gpt_shape* shape, const gpt_para
       if (f8) TRY(wgrad_fp8(dyqt, at<uint8_t>(ws, L.attt), sc + SC_G_ATT, sc + SC_ATT, G + P.wo(D, l), d, d, N, acc, wpart, s));
       else TRY(wgrad(g_bf, d, att, d, G + P.wo(D, l), d, d, N, acc, wpart, s));
     }
-    for (int part = 0; part < 2; ++part) {  // dQ (and delta), then dK/dV
+    // dQ (and delta), then dK/dV; both leave through the QK-norm + rotary
+    // backward into dqkv (bf16): the gradients of the raw q, k heads, and dv
+    const QkNormBwd fuse{at<float>(ws, L.rq), at<float>(ws, L.rk), cs, dqkv};
+    for (int part = 0; part < 2; ++part) {
       ProfScope ps_(part == 0 ? P_ATTN_BWD_Q : P_ATTN_BWD_KV, s);
       TRY(launch_attn_bwd_part(part, qkv, qkv + d, qkv + d + D.dkv, D.dqkv, att, dout, d, at<float>(ws, L.lse),
-                               at<float>(ws, w.delta), dq_acc, dqkv + d, dqkv + d + D.dkv, D.dqkv, D.B, D.H, D.Hkv,
-                               D.T, D.layer_window(l), s));
+                               at<float>(ws, w.delta), nullptr, dqkv + d, dqkv + d + D.dkv, D.dqkv, D.B, D.H, D.Hkv,
+                               D.T, D.layer_window(l), s, &fuse));
     }
-    { ProfScope ps_(P_ROPE_BWD, s); TRY(launch_rope_qknorm_bwd(dq_acc, dqkv, qkv, at<float>(ws, L.rq), at<float>(ws, L.rk), cs, N, D.T, D.H, D.Hkv, s)); }
     if (D.ve_layer(l)) {  // value embedding: dVE[token] += gate dv; gate-logit gradients dz
       ProfScope ps_(P_FEATURES, s);
       TRY(launch_ve_bwd(ids, dqkv + d + D.dkv, D.dqkv, W + P.ve(D, l), at<float>(ws, L.vgate), G + P.ve(D, l), dzve,

@@ -23,9 +23,10 @@
 // Forward: one workgroup = 128 queries (4 waves x 32) of one (batch, head).
 //   Each wave computes S^T = K Q^T, so a lane owns one query (its partner
 //   lane ^ 32 the other half of the keys): row max = one lane swap per tile,
-//   row sum = none until the end.  O^T += V^T P^T.  The reference max moves
-//   only when a row max exceeds it by 2^8 (P <= 256), so most tiles skip the
-//   O rescale.  K/V tiles of 64 keys, double buffered.
+//   row sum = none until the end.  O^T += V^T P^T with P rounded to bf16 and
+//   the row sum l of the unrounded P (fp32), O = O / l at the end.  The
+//   reference max moves only when a row max exceeds it by 2^8 (P <= 256), so
+//   most tiles skip the O rescale.  K/V tiles of 64 keys, double buffered.
 // Backward, two kernels and no atomics:
 //   * dK/dV: one workgroup = 256 keys (8 waves x 32) over query tiles of 32
 //     streamed through a 4-stage LDS ring: S = Q K^T, dP = dO V^T,
@@ -169,6 +170,56 @@ __device__ __forceinline__ void dma_barrier() {
 // resident in its own L2.
 __device__ __forceinline__ int xcd_block(int gx) {
   return xcd_remap(blockIdx.x + gx * blockIdx.y, gx * gridDim.y);
+}
+
+// RMS-norm + rotary backward of one 128-wide q or k head (the model's QK
+// normalisation after the rotation), fused into the epilogue of the attention
+// backward kernels.  acc holds the head's gradient in accumulator order: lane
+// half lh holds features et*32 + 8*(e>>2) + 4*lh + (e&3) of element e of
+// acc[et], the partner lane ^ 32 the other half.  With dy = scale * acc the
+// gradient of the stored normed, rotated head y (bf16 row yrow) and r its
+// inverse RMS: dx = r (dy - y mean(dy y)), then the inverse rotation of the
+// pairs (i, i + 64) at position t (cos table [T][64], then sin [T][64]); the
+// result goes out as bf16.  Features i and i + 64 sit in acc[et] and
+// acc[et + 2] of the same lane, so the rotation needs no exchange.
+__device__ __forceinline__ void qknorm_rope_bwd_store(const f32x16_t* acc, float scale, const uint16_t* yrow, float r,
+                                                      const float* cs, int T, int t, int lh, uint16_t* out) {
+  uint2 yw[4][4];
+  float dot = 0.f;
+#pragma unroll
+  for (int et = 0; et < 4; ++et)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      yw[et][g] = *reinterpret_cast<const uint2*>(yrow + et * 32 + 8 * g + 4 * lh);
+      dot += acc[et][4 * g] * lo_bf(yw[et][g].x) + acc[et][4 * g + 1] * hi_bf(yw[et][g].x) +
+             acc[et][4 * g + 2] * lo_bf(yw[et][g].y) + acc[et][4 * g + 3] * hi_bf(yw[et][g].y);
+    }
+  dot += __shfl_xor(dot, 32, 64);
+  const float mean = dot * scale * (1.f / 128.f);
+  const float* cr = cs + t * 64;
+  const float* sr = cs + (long long)T * 64 + t * 64;
+#pragma unroll
+  for (int et = 0; et < 2; ++et)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int i = et * 32 + 8 * g + 4 * lh;
+      const float4 c = *reinterpret_cast<const float4*>(cr + i);
+      const float4 sn = *reinterpret_cast<const float4*>(sr + i);
+      const float y1[4] = {lo_bf(yw[et][g].x), hi_bf(yw[et][g].x), lo_bf(yw[et][g].y), hi_bf(yw[et][g].y)};
+      const float y2[4] = {lo_bf(yw[et + 2][g].x), hi_bf(yw[et + 2][g].x), lo_bf(yw[et + 2][g].y),
+                           hi_bf(yw[et + 2][g].y)};
+      const float cc[4] = {c.x, c.y, c.z, c.w}, ss[4] = {sn.x, sn.y, sn.z, sn.w};
+      float o1[4], o2[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const float d1 = r * (acc[et][4 * g + u] * scale - y1[u] * mean);
+        const float d2 = r * (acc[et + 2][4 * g + u] * scale - y2[u] * mean);
+        o1[u] = d1 * cc[u] + d2 * ss[u];
+        o2[u] = -d1 * ss[u] + d2 * cc[u];
+      }
+      *reinterpret_cast<uint2*>(out + i) = make_uint2(pack_bf2(o1[0], o1[1]), pack_bf2(o1[2], o1[3]));
+      *reinterpret_cast<uint2*>(out + i + 64) = make_uint2(pack_bf2(o2[0], o2[1]), pack_bf2(o2[2], o2[3]));
+    }
 }
 
 // Copy of ROWS rows of 128 features (row r0 + r clamped to T - 1) of a bf16
@@ -386,12 +437,15 @@ static_assert(K8_VMCNT < 64, "vmcnt range");
 
 // ROWS rows of 128 features from row r0 (clamped to T - 1) into a swizzled
 // tile, K8_NT threads: round i, wave w, lane l fills 16-byte slot 512 i + 64 w + l
-template <bool GEN>
+// FUSE: dK leaves through the QK-norm + rotary backward (rk: inverse RMS of
+// each key head [N, Hkv]; cs: rotary table), else as the raw gradient.
+template <bool GEN, bool FUSE>
 __global__ void __launch_bounds__(K8_NT, 1)
 attn_bwd_kv8_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
                     long long ld, const uint16_t* __restrict__ dout, long long ld_out, const float* __restrict__ lse,
                     const float* __restrict__ delta, uint16_t* __restrict__ dk, uint16_t* __restrict__ dv,
-                    long long ld_dkv, int H, int Hkv, int T, int window_arg) {
+                    long long ld_dkv, int H, int Hkv, int T, int window_arg, const float* __restrict__ rk,
+                    const float* __restrict__ cs) {
   static_assert(K8_NS == 4, "one __shared__ array per stage below");
   __shared__ __attribute__((aligned(16))) char s_k[K8_KEYS * 256];
   __shared__ __attribute__((aligned(16))) char s_st0[K8_STAGE];
@@ -561,12 +615,16 @@ attn_bwd_kv8_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int e = et * 32 + 8 * g + 4 * lh;
-        *reinterpret_cast<uint2*>(dkr + e) =
-            make_uint2(pack_bf2(dkt[et][4 * g] * kScale, dkt[et][4 * g + 1] * kScale),
-                       pack_bf2(dkt[et][4 * g + 2] * kScale, dkt[et][4 * g + 3] * kScale));
+        if constexpr (!FUSE)
+          *reinterpret_cast<uint2*>(dkr + e) =
+              make_uint2(pack_bf2(dkt[et][4 * g] * kScale, dkt[et][4 * g + 1] * kScale),
+                         pack_bf2(dkt[et][4 * g + 2] * kScale, dkt[et][4 * g + 3] * kScale));
         *reinterpret_cast<uint2*>(dvr + e) =
             make_uint2(pack_bf2(dvt[et][4 * g], dvt[et][4 * g + 1]), pack_bf2(dvt[et][4 * g + 2], dvt[et][4 * g + 3]));
       }
+    if constexpr (FUSE)
+      qknorm_rope_bwd_store(dkt, kScale, kh + (long long)mykey * ld, rk[(rowbase + mykey) * Hkv + hk], cs, T, mykey,
+                            lh, dkr);
   }
 }
 
@@ -577,12 +635,16 @@ constexpr int DQ_Q = 128;
 constexpr int DQ_K = 64;
 constexpr int DQ_STAGE = 2 * DQ_K * 256;  // K tile + V tile
 
-template <bool GEN>
+// FUSE: dQ leaves through the QK-norm + rotary backward as bf16 into dq_bf
+// (row stride ld_dq; rq: inverse RMS of each query head [N, H]; cs: rotary
+// table), else as the raw fp32 gradient into dq_out (row stride 128 H).
+template <bool GEN, bool FUSE>
 __global__ void __launch_bounds__(256, 2)
 attn_bwd_q_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
                   long long ld, const uint16_t* __restrict__ out, const uint16_t* __restrict__ dout, long long ld_out,
                   const float* __restrict__ lse, float* __restrict__ delta, float* __restrict__ dq_out, int H,
-                  int Hkv, int T, int window_arg) {
+                  int Hkv, int T, int window_arg, uint16_t* __restrict__ dq_bf, long long ld_dq,
+                  const float* __restrict__ rq, const float* __restrict__ cs) {
   __shared__ __attribute__((aligned(16))) char smem[2 * DQ_STAGE];
   const int window = GEN ? window_arg : -1;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, lr = lane & 31, lh = lane >> 5;
@@ -712,15 +774,20 @@ attn_bwd_q_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k
     dma_barrier();  // the next tile has landed; every wave is done with this one
   }
   if (myq < T) {
-    float* dqr = dq_out + (rowbase + myq) * d + h * 128;
+    if constexpr (FUSE) {
+      qknorm_rope_bwd_store(dqt, kScale, qh + (long long)myq * ld, rq[(rowbase + myq) * H + h], cs, T, myq, lh,
+                            dq_bf + (rowbase + myq) * ld_dq + h * 128);
+    } else {
+      float* dqr = dq_out + (rowbase + myq) * d + h * 128;
 #pragma unroll
-    for (int et = 0; et < 4; ++et)
+      for (int et = 0; et < 4; ++et)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int e = et * 32 + 8 * g + 4 * lh;
-        *reinterpret_cast<float4*>(dqr + e) = make_float4(dqt[et][4 * g] * kScale, dqt[et][4 * g + 1] * kScale,
-                                                          dqt[et][4 * g + 2] * kScale, dqt[et][4 * g + 3] * kScale);
-      }
+        for (int g = 0; g < 4; ++g) {
+          const int e = et * 32 + 8 * g + 4 * lh;
+          *reinterpret_cast<float4*>(dqr + e) = make_float4(dqt[et][4 * g] * kScale, dqt[et][4 * g + 1] * kScale,
+                                                            dqt[et][4 * g + 2] * kScale, dqt[et][4 * g + 3] * kScale);
+        }
+    }
   }
 }
 
@@ -740,17 +807,24 @@ int launch_attn_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, lon
 int launch_attn_bwd_part(int part, const uint16_t* q, const uint16_t* k, const uint16_t* v, long long ld_qkv,
                          const uint16_t* out, const uint16_t* dout, long long ld_out, const float* lse, float* delta,
                          float* dq, uint16_t* dk, uint16_t* dv, long long ld_dkv, int B, int H, int Hkv, int T,
-                         int window, hipStream_t s) {
+                         int window, hipStream_t s, const QkNormBwd* fuse) {
   if (B <= 0 || T <= 0) return 0;
   const bool gen = Hkv != H || window >= 0;
+  const float* rq = fuse ? fuse->rq : nullptr;
+  const float* rk = fuse ? fuse->rk : nullptr;
+  const float* cs = fuse ? fuse->cs : nullptr;
+  uint16_t* dq_bf = fuse ? fuse->dq : nullptr;
   if (part == 0) {  // dQ, and delta for the dK/dV kernel
-    hipLaunchKernelGGL(gen ? attn_bwd_q_kernel<true> : attn_bwd_q_kernel<false>, dim3((T + DQ_Q - 1) / DQ_Q, B * H),
-                       dim3(256), 0, s, q, k, v, ld_qkv, out, dout, ld_out, lse, delta, dq, H, Hkv, T, window);
+    auto kern = fuse ? (gen ? attn_bwd_q_kernel<true, true> : attn_bwd_q_kernel<false, true>)
+                     : (gen ? attn_bwd_q_kernel<true, false> : attn_bwd_q_kernel<false, false>);
+    hipLaunchKernelGGL(kern, dim3((T + DQ_Q - 1) / DQ_Q, B * H), dim3(256), 0, s, q, k, v, ld_qkv, out, dout, ld_out,
+                       lse, delta, dq, H, Hkv, T, window, dq_bf, ld_dkv, rq, cs);
     GS_LAUNCH_CHECK("attn_bwd_q");
   } else {
-    hipLaunchKernelGGL(gen ? attn_bwd_kv8_kernel<true> : attn_bwd_kv8_kernel<false>,
-                       dim3((T + K8_KEYS - 1) / K8_KEYS, B * Hkv), dim3(K8_NT), 0, s, q, k, v, ld_qkv, dout, ld_out, lse,
-                       delta, dk, dv, ld_dkv, H, Hkv, T, window);
+    auto kern = fuse ? (gen ? attn_bwd_kv8_kernel<true, true> : attn_bwd_kv8_kernel<false, true>)
+                     : (gen ? attn_bwd_kv8_kernel<true, false> : attn_bwd_kv8_kernel<false, false>);
+    hipLaunchKernelGGL(kern, dim3((T + K8_KEYS - 1) / K8_KEYS, B * Hkv), dim3(K8_NT), 0, s, q, k, v, ld_qkv, dout,
+                       ld_out, lse, delta, dk, dv, ld_dkv, H, Hkv, T, window, rk, cs);
     GS_LAUNCH_CHECK("attn_bwd_kv");
   }
   return 0;
@@ -762,7 +836,7 @@ int launch_attn_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, lon
                     int window, hipStream_t s) {
   for (int part = 0; part < 2; ++part) {
     const int rc = launch_attn_bwd_part(part, q, k, v, ld_qkv, out, dout, ld_out, lse, delta, dq, dk, dv, ld_dkv, B,
-                                        H, Hkv, T, window, s);
+                                        H, Hkv, T, window, s, nullptr);
     if (rc) return rc;
   }
   return 0;

@@ -273,55 +273,6 @@ __global__ void __launch_bounds__(256) rmsnorm_bwd_kernel(const float* __restric
   }
 }
 
-// dx for one head: d_rot = r (dy - y mean(dy y)); dx = R^T d_rot.  Half a
-// wave (32 lanes) per head: lane j holds features 2j, 2j+1 and their rotation
-// partners 64 + 2j, 65 + 2j (8-byte fp32 / 4-byte bf16 accesses), the mean
-// reduced over the 32 lanes.
-__device__ __forceinline__ void rope_norm_head_bwd2(float2 dy1, float2 dy2, const uint16_t* y, float rr,
-                                                    const float* cs, int T, int t, int j, uint16_t* out) {
-  const uint32_t yw1 = *reinterpret_cast<const uint32_t*>(y + 2 * j);
-  const uint32_t yw2 = *reinterpret_cast<const uint32_t*>(y + 64 + 2 * j);
-  const float y1a = lo_bf(yw1), y1b = hi_bf(yw1), y2a = lo_bf(yw2), y2b = hi_bf(yw2);
-  float dot = dy1.x * y1a + dy1.y * y1b + dy2.x * y2a + dy2.y * y2b;
-#pragma unroll
-  for (int o = 16; o > 0; o >>= 1) dot += __shfl_xor(dot, o, 64);
-  dot /= 128.f;
-  const float d1a = rr * (dy1.x - y1a * dot), d1b = rr * (dy1.y - y1b * dot);
-  const float d2a = rr * (dy2.x - y2a * dot), d2b = rr * (dy2.y - y2b * dot);
-  const float2 c = *reinterpret_cast<const float2*>(cs + t * 64 + 2 * j);
-  const float2 sn = *reinterpret_cast<const float2*>(cs + T * 64 + t * 64 + 2 * j);
-  *reinterpret_cast<uint32_t*>(out + 2 * j) = pack_bf2(d1a * c.x + d2a * sn.x, d1b * c.y + d2b * sn.y);
-  *reinterpret_cast<uint32_t*>(out + 64 + 2 * j) = pack_bf2(-d1a * sn.x + d2a * c.x, -d1b * sn.y + d2b * c.y);
-}
-
-// one half-wave per (token, head slot): slots 0 .. H-1 are the query heads
-// (gradient from dq_acc, fp32 [N, 128 H]), slots H .. H+Hkv-1 the key heads
-// (gradient in place in dqkv); rows of qkv / dqkv are d + 2 dkv wide
-__global__ void __launch_bounds__(256) rope_qknorm_bwd_kernel(const float* __restrict__ dq_acc, uint16_t* __restrict__ dqkv,
-                                       const uint16_t* __restrict__ qkv, const float* __restrict__ rq,
-                                       const float* __restrict__ rk, const float* __restrict__ cs,
-                                       long long N, int T, int H, int Hkv) {
-  const int j = threadIdx.x & 31;
-  const int HS = H + Hkv;
-  const long long w = (long long)blockIdx.x * 8 + (threadIdx.x >> 5);
-  if (w >= N * HS) return;
-  const long long n = w / HS;
-  const int hh = (int)(w % HS), t = (int)(n % T);
-  const int d = H * 128, ldq = d + 2 * Hkv * 128;
-  if (hh < H) {
-    const float* dq = dq_acc + n * d + hh * 128;
-    rope_norm_head_bwd2(*reinterpret_cast<const float2*>(dq + 2 * j), *reinterpret_cast<const float2*>(dq + 64 + 2 * j),
-                        qkv + n * ldq + hh * 128, rq[n * H + hh], cs, T, t, j, dqkv + n * ldq + hh * 128);
-  } else {
-    const int hk = hh - H;
-    uint16_t* dk = dqkv + n * ldq + d + hk * 128;
-    const uint32_t k1 = *reinterpret_cast<const uint32_t*>(dk + 2 * j);
-    const uint32_t k2 = *reinterpret_cast<const uint32_t*>(dk + 64 + 2 * j);
-    rope_norm_head_bwd2(make_float2(lo_bf(k1), hi_bf(k1)), make_float2(lo_bf(k2), hi_bf(k2)),
-                        qkv + n * ldq + d + hk * 128, rk[n * Hkv + hk], cs, T, t, j, dk);
-  }
-}
-
 // lse = log-sum-exp over the per-tile (max, sum exp) partials; loss = lse - z[target]
 __global__ void __launch_bounds__(256) ce_reduce_kernel(const float2* __restrict__ part, int nparts, const float* __restrict__ zt,
                                  float* __restrict__ lse, float* __restrict__ row_loss,
@@ -849,14 +800,6 @@ int launch_rmsnorm_bwd(const float* dh, const uint16_t* h, const float* r, float
   GS_MC_SWITCH(mc, GS_RB)
 #undef GS_RB
   GS_LAUNCH_CHECK("rmsnorm_bwd");
-  return 0;
-}
-
-int launch_rope_qknorm_bwd(const float* dq_acc, uint16_t* dqkv, const uint16_t* qkv, const float* rq,
-                           const float* rk, const float* cs, long long N, int T, int H, int Hkv, hipStream_t s) {
-  hipLaunchKernelGGL(rope_qknorm_bwd_kernel, dim3(nblocks(N * (H + Hkv), 8)), dim3(256), 0, s, dq_acc, dqkv, qkv,
-                     rq, rk, cs, N, T, H, Hkv);
-  GS_LAUNCH_CHECK("rope_qknorm_bwd");
   return 0;
 }
 

@@ -22,10 +22,6 @@ int launch_rmsnorm_fwd(const float* x, uint16_t* h, float* r, long long N, int d
                        float* amax_part = nullptr);
 int launch_rmsnorm_bwd(const float* dh, const uint16_t* h, const float* r, float* g, uint16_t* g_bf,
                        long long N, int d, hipStream_t s, float* amax_part = nullptr);
-// one wave per (token, head) over the n_head query heads and n_kv_head key heads
-int launch_rope_qknorm_bwd(const float* dq_acc, uint16_t* dqkv, const uint16_t* qkv, const float* rq,
-                           const float* rk, const float* cos_sin, long long N, int T, int H, int Hkv,
-                           hipStream_t s);
 int launch_ce_reduce(const float* part, int nparts, const float* zt, float* lse, float* row_loss,
                      float* lse_out, long long N, hipStream_t s);
 int launch_loss_mean(const float* row_loss, float* loss, long long N, hipStream_t s);
@@ -104,12 +100,23 @@ int launch_attn_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, lon
                     const uint16_t* out, const uint16_t* dout, long long ld_out, const float* lse,
                     float* delta, float* dq, uint16_t* dk, uint16_t* dv, long long ld_dkv, int B,
                     int H, int Hkv, int T, int window, hipStream_t s);
+// The QK-norm + rotary backward fused into the attention backward: q and k
+// are the stored normed, rotated heads; rq [N, H] and rk [N, Hkv] their
+// inverse RMS; cs the rotary table; dq (bf16, row stride ld_dkv) receives the
+// gradient of the raw query heads, dk that of the raw key heads.
+struct QkNormBwd {
+  const float* rq;
+  const float* rk;
+  const float* cs;
+  uint16_t* dq;
+};
 // one of the two backward kernels, in this order: 0 = dQ (also writes delta = rowsum(dout * out)),
-// 1 = dK/dV (reads delta)
+// 1 = dK/dV (reads delta).  fuse NULL: raw gradients (dq fp32 [N, 128 H], dk bf16);
+// else the gradients of the raw heads through the QK-norm and rotary backward.
 int launch_attn_bwd_part(int part, const uint16_t* q, const uint16_t* k, const uint16_t* v, long long ld_qkv,
                          const uint16_t* out, const uint16_t* dout, long long ld_out, const float* lse, float* delta,
                          float* dq, uint16_t* dk, uint16_t* dv, long long ld_dkv, int B, int H, int Hkv, int T,
-                         int window, hipStream_t s);
+                         int window, hipStream_t s, const QkNormBwd* fuse);
 
 // --- fp8 quantisation (fp8.hip) --------------------------------------------
 // Tensors are [rows, cols] with row stride ld (elements); rows % 16 == 0,
