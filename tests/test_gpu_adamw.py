@@ -20,7 +20,7 @@ import torch
 from gpu_util import cosine, rel_l2, say
 from oracle import adamw as oadamw
 from oracle import precision
-from step_util import StepRun, oracle_run
+from step_util import StepRun, check_rows, grad_rows, members, oracle_run
 from gpt_transformer_step_amd import inputs
 
 pytestmark = pytest.mark.gpu
@@ -84,13 +84,4 @@ def test_gradient_accumulation_two_micro_batches():
     run.ids_np = ids_all
     run.batch = Bn
     exact = oracle_run(run)
-    floor_ref = oracle_run(run, bf16_operands=True)
-    bad = []
-    for name, r in exact["grads"].items():
-        gg = np.asarray(grads[name], dtype=np.float64)
-        e, c = rel_l2(gg, r), cosine(gg, r)
-        tol = max(1e-2, 1.5 * rel_l2(floor_ref["grads"][name], r))
-        if not (e <= tol and c >= 0.999):
-            bad.append(f"{name}: rel_l2 {e:.3e} (bar {tol:.3e}) cos {c:.6f}")
-    say(f"  {len(exact['grads'])} gradients checked")
-    assert not bad, bad
+    check_rows(grad_rows(grads, exact["grads"], [m["grads"] for m in members(run)], 1e-2), "accumulated: ")

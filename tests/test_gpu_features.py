@@ -5,55 +5,39 @@ window layers), the fp8 path, and gradient accumulation.
 
 Bars: those of the whole-step parity test (loss relative error and row lse
 rel L2 <= 1e-2; every gradient tensor, the value-embedding tables and gates
-included, cosine >= 0.999 and rel L2 <= max(1e-2, 1.5 F) with F the
-bf16-operand floor of that tensor); the fp8 run takes the fp8 bars of the fp8
-parity test.
+included, against the exact oracle at max(1e-2, the bf16 ensemble's distance
+(1 + kappa)) and cosine >= 0.999); the fp8 run takes the fp8 bars.
 
 The scalar gradients (residual and x0 scalars, smear weight and scale,
 backout scale) are single sums over all B*T*d stream elements whose terms
-cancel: |sum t_i| is 1e-2 .. 2e-4 of sum |t_i| on these inputs.  A relative
-bar on such a sum measures the cancellation, not the arithmetic, so each
-element is held to the error bound of a sum whose terms each carry two bf16
-roundings: |gpu - oracle| <= max(1e-2 |oracle|, 2^-8 sum |t_i|), with sum |t_i|
-from the oracle (grad_abs); vectors also need cosine >= 0.999."""
+cancel.  Each element is held to max(1e-2 |exact|, 4 SCALAR_NOISE sum |terms|),
+SCALAR_NOISE the measured rms error of a jittered bf16 run relative to the
+sum of the terms' absolute values (the oracle's grad_abs); on the bf16
+configurations below that bar is smaller than every scalar gradient except
+near-zero components of the smear weight vector (covered by its cosine), so a
+kernel that writes 0 fails.  fp8 adds its quantisation noise (rms up to
+1.1e-3 of sum |terms|, measured the same way): the fp8 method itself cannot
+resolve some of the scalars, and the fp8 test holds them to that noise."""
 
 import numpy as np
 import pytest
 import torch
 
 from gpu_util import cosine, from_dev, rel_l2, say
-from step_util import StepRun, oracle_run
+from step_util import StepRun, check_scalars, members, oracle_run
 from test_gpu_step import check_grads
 
 pytestmark = pytest.mark.gpu
 
 SCALARS = ("resid_lambda", "x0_lambda", "smear_w", "smear_lambda", "backout_lambda")
+# rms error of a jittered fp8 + bf16 run of the oracle on the scalar gradients,
+# relative to sum |terms|: 1.4e-4 .. 1.1e-3 (depth 4, four seeds)
+SCALAR_NOISE_FP8 = 1.2e-3
 
 
-def check_scalars(got, ref, tau=2.0 ** -8, rel=1e-2, extra=None, cos_min=None):
-    """Elementwise bar max(rel |ref|, tau * sum |terms|) (+ extra, an
-    elementwise allowance) on the scalar gradients; cosine >= 0.999 (or
-    cos_min[name]) for the vectors."""
-    bad = []
-    for name in SCALARS:
-        g = np.asarray(got[name], dtype=np.float64)
-        r = ref["grads"][name]
-        bar = np.maximum(rel * np.abs(r), tau * ref["grad_abs"][name])
-        if extra is not None:
-            bar = np.maximum(bar, extra[name])
-        err = np.abs(g - r)
-        worst = float(np.max(err / np.maximum(bar, 1e-30)))
-        say(f"  {name}: max |err| / bar {worst:.3f}  (gpu {g[:2]}, oracle {r[:2]})")
-        if np.any(err > bar):
-            bad.append(f"{name}: err {err} bar {bar}")
-        cmin = 0.999 if cos_min is None else cos_min[name]
-        if g.size > 1 and np.linalg.norm(r) > 0 and cosine(g, r) < cmin:
-            bad.append(f"{name}: cos {cosine(g, r):.6f} (bar {cmin:.6f})")
-    assert not bad, bad
+def _without(names, d):
+    return [k for k in d if k not in names]
 
-
-def _without(d, names):
-    return {k: v for k, v in d.items() if k not in names}
 
 CONFIGS = [
     # depth, vocab, seq_len, batch, n_kv_head, window, pattern, features
@@ -82,10 +66,9 @@ def test_step_parity_features(depth, vocab, T, B, n_kv_head, window, pattern, fe
     e = rel_l2(from_dev(run.row_lse), ref["lse"].reshape(-1))
     say(f"  row lse rel_l2 {e:.3e}")
     assert e <= 1e-2
-    floor = oracle_run(run, bf16_operands=True)
     got = run.grads()
-    check_scalars(got, ref)
-    check_grads(got, _without(ref["grads"], SCALARS), floor["grads"])
+    check_scalars(got, ref, SCALARS)
+    check_grads(got, ref["grads"], members(run), names=_without(SCALARS, ref["grads"]))
 
 
 def test_features_fp8():
@@ -96,29 +79,14 @@ def test_features_fp8():
     run.bwd()
     torch.cuda.synchronize()
     loss = float(run.loss.item())
-    ref = oracle_run(run, fp8=True, bf16_operands=True)
-    f8x = oracle_run(run, fp8=True)
-    fl = abs(ref["loss"] - f8x["loss"]) / abs(ref["loss"])
-    say(f"  loss gpu {loss:.6f} fp8+bf16 oracle {ref['loss']:.6f} fp8 oracle {f8x['loss']:.6f}")
-    assert abs(loss - ref["loss"]) / abs(ref["loss"]) <= max(1e-2, 1.5 * fl)
+    ref = oracle_run(run)
+    say(f"  loss gpu {loss:.6f} exact oracle {ref['loss']:.6f}")
+    assert abs(loss - ref["loss"]) / abs(ref["loss"]) <= 5e-2
     grads = run.grads()
-    # scalars: the conditioning bar, widened by the distance the fp8 oracle's
-    # own bf16 rounding moves each of them; the cosine floor as for the other
-    # fp8 gradients
-    check_scalars(grads, ref, extra={n: 1.5 * np.abs(ref["grads"][n] - f8x["grads"][n]) for n in SCALARS},
-                  cos_min={n: min(0.999, 1.0 - 1.5 * (1.0 - cosine(ref["grads"][n], f8x["grads"][n])))
-                           for n in SCALARS})
-    bad = []
-    for name, r in _without(ref["grads"], SCALARS).items():
-        g = np.asarray(grads[name], dtype=np.float64)
-        assert np.all(np.isfinite(g)), name
-        e, c = rel_l2(g, r), cosine(g, r)
-        tol = max(1e-2, 1.5 * rel_l2(r, f8x["grads"][name]))
-        cos_min = min(0.999, 1.0 - 1.5 * (1.0 - cosine(r, f8x["grads"][name])))
-        if not (e <= tol and c >= cos_min):
-            bad.append(f"{name}: rel_l2 {e:.2e} (bar {tol:.2e}) cos {c:.6f} (bar {cos_min:.6f})")
-    say(f"  {len(ref['grads'])} gradients checked")
-    assert not bad, bad
+    # the elementwise bar at the fp8 noise bounds every element; vectors of 4 to 24
+    # noisy elements give no stable cosine, so none is asked for
+    check_scalars(grads, ref, SCALARS, noise=SCALAR_NOISE_FP8, cos_min=-1.0)
+    check_grads(grads, ref["grads"], members(run, fp8=True), base=5e-2, names=_without(SCALARS, ref["grads"]))
 
 
 def test_features_accumulate_adds():

@@ -12,19 +12,18 @@ GPT_PREC_FP8 against the oracle's fp8 fake-quant mode.
   (so it is per block, not accumulated), and it is not subnormal flushing
   (the diagnostic below compares both).  That is far below fp8's own
   quantisation step (2^-4 relative for E4M3).
-* Step: the GPU computes with bf16 activations feeding the fp8 quantiser, so
-  its closest definition is the oracle with fp8=True and bf16_operands=True.
-  Bars per quantity: loss relative error and lse / gradient rel L2 <=
-  max(1e-2, 1.5 F8), where F8 is the distance between that oracle and the
-  fp8 oracle without bf16 rounding (the code flips that bf16 rounding alone
-  causes), and gradient cosine >= min(0.999, 1 - 1.5 (1 - c8)) with c8 the
-  cosine between those two oracles.  Against the exact oracle (no fp8) the
-  bar is max(5e-2, 1.5 Q), Q being the fp8 oracle's own distance from the
-  exact one.  Per-tensor E5M2 gradients are coarse (2 mantissa bits): at
-  depth 2 the fp8 oracle is 10-20 % (rel L2) from the exact gradients, and
-  rounding the activations to bf16 before quantising moves them by a similar
-  amount, so a fixed 0.999 cosine would reject the method itself.  A wrong
-  scale, transpose or format would still move them by O(1).
+* Step: against the exact oracle (no fp8, nothing rounded).  The fp8
+  method moves every gradient by its own quantisation noise -- per-tensor
+  E5M2 output gradients have 2 mantissa bits; at depth 2-8 the oracle's fp8
+  mode is 15-25 % (rel L2) from the exact gradients -- and, like bf16, that
+  noise is chaotic: two fp8 computations that differ only in summation order
+  flip different codes and land 15-25 % apart.  The bar therefore comes from
+  the oracle's fp8 + bf16 mode run with a jitter seed (one more valid fp8
+  computation of the step): each gradient tensor rel L2 <= max(5e-2,
+  d_m (1 + kappa)) and cosine >= min(0.999, 1 - (1 - c_m)(1 + kappa)^2) with
+  d_m, c_m that member's distance and cosine; loss relative error and row lse
+  rel L2 <= 5e-2.  A wrong scale, transpose or format moves a gradient by
+  O(1), far outside that spread.
 """
 
 import numpy as np
@@ -33,7 +32,7 @@ import torch
 
 from gpu_util import cosine, rel_l2, say, to_dev_bf16
 from oracle import fp8 as ofp8
-from step_util import StepRun, oracle_run
+from step_util import StepRun, check_rows, grad_rows, members, oracle_run
 
 pytestmark = pytest.mark.gpu
 
@@ -138,10 +137,6 @@ CONFIGS = [
 ]
 
 
-def _bar(e, floor, base):
-    return e <= max(base, 1.5 * floor)
-
-
 @pytest.mark.parametrize("depth,vocab,T,Bn,attn", CONFIGS)
 def test_step_fp8_parity(depth, vocab, T, Bn, attn):
     B = _B()
@@ -153,41 +148,14 @@ def test_step_fp8_parity(depth, vocab, T, Bn, attn):
     torch.cuda.synchronize()
     loss = float(run.loss.item())
     lse = run.row_lse.cpu().numpy().astype(np.float64)
-    grads = run.grads()
-
-    ref = oracle_run(run, fp8=True, bf16_operands=True)     # closest definition
-    f8x = oracle_run(run, fp8=True)                         # fp8 without bf16 rounding
-    exact = oracle_run(run)                                 # no fp8, no rounding
-    say(f"  loss gpu {loss:.6f}  fp8+bf16 oracle {ref['loss']:.6f}  fp8 oracle {f8x['loss']:.6f}  "
-        f"exact {exact['loss']:.6f}")
-    fl = abs(ref["loss"] - f8x["loss"]) / abs(ref["loss"])
-    assert _bar(abs(loss - ref["loss"]) / abs(ref["loss"]), fl, 1e-2)
-    q_l = abs(ref["loss"] - exact["loss"]) / abs(exact["loss"])
-    assert _bar(abs(loss - exact["loss"]) / abs(exact["loss"]), q_l, 5e-2)
-    e_lse = rel_l2(lse, ref["lse"])
-    say(f"  lse rel_l2 vs fp8 oracle {e_lse:.2e}")
-    assert _bar(e_lse, rel_l2(ref["lse"], f8x["lse"]), 1e-2)
-
-    bad, worst = [], (0.0, "")
-    for name, r in ref["grads"].items():
-        g = np.asarray(grads[name], dtype=np.float64)
-        assert np.all(np.isfinite(g)), name
-        e, c = rel_l2(g, r), cosine(g, r)
-        floor = rel_l2(r, f8x["grads"][name])
-        tol = max(1e-2, 1.5 * floor)
-        cos_min = min(0.999, 1.0 - 1.5 * (1.0 - cosine(r, f8x["grads"][name])))
-        ex = exact["grads"][name]
-        e_x = rel_l2(g, ex)
-        q = rel_l2(r, ex)
-        tol_x = max(5e-2, 1.5 * q)
-        if e / tol > worst[0]:
-            worst = (e / tol, f"{name}: rel_l2 {e:.2e} (floor {floor:.2e}) cos {c:.6f}; vs exact {e_x:.2e} "
-                              f"(fp8 oracle {q:.2e})")
-        if not (e <= tol and c >= cos_min and e_x <= tol_x):
-            bad.append(f"{name}: rel_l2 {e:.2e} (floor {floor:.2e}) cos {c:.6f}; vs exact {e_x:.2e} "
-                       f"(fp8 oracle {q:.2e})")
-    say(f"  worst gradient vs its bar: {worst[1]}")
-    assert not bad, bad
+    exact = oracle_run(run)
+    mems = members(run, fp8=True)
+    say(f"  loss gpu {loss:.6f}  exact {exact['loss']:.6f}  fp8 member {mems[0]['loss']:.6f}")
+    assert abs(loss - exact["loss"]) <= 5e-2 * abs(exact["loss"])
+    e_lse = rel_l2(lse, exact["lse"])
+    say(f"  lse rel_l2 {e_lse:.2e} (member {rel_l2(mems[0]['lse'], exact['lse']):.2e})")
+    assert e_lse <= 5e-2
+    check_rows(grad_rows(run.grads(), exact["grads"], [m["grads"] for m in mems], 5e-2))
 
 
 def test_fp8_rejects_ragged_token_count():

@@ -3,13 +3,11 @@ same seeded token ids and bf16-valued weights.
 
 Bars, against the exact float64 oracle (metrics in float64):
   * loss relative error <= 1e-2; row log-sum-exp and logits rel L2 <= 1e-2;
-  * every gradient tensor: cosine >= 0.999 and rel L2 <= max(1e-2, 1.5 F),
-    where F is the bf16 noise floor of that tensor on these inputs: the
-    distance between the oracle's bf16-operand mode (every matrix-product
-    operand rounded to bf16, the pages' compute dtype) and its exact mode.
-    Rounding the activations to bf16 alone moves the most sensitive tensors
-    (q/k weights of the last layers) by 1-2 %, above 1e-2; the GPU must be no
-    further from the exact result than that rounding puts any bf16 step.
+  * every gradient tensor: rel L2 <= max(1e-2, d_m (1 + kappa)) and cosine
+    >= 0.999, d_m the distance of a jittered run of the oracle's bf16 mode
+    (the precision passage's arithmetic with another fp32 summation order)
+    from the exact gradient -- the spread no bf16 computation gets below (see
+    step_util: on the q / k weights of deeper layers it is above 1e-2).
 The target-logit pick is checked bit-exactly against the logits the same
 kernel writes."""
 
@@ -18,7 +16,7 @@ import pytest
 import torch
 
 from gpu_util import cosine, from_dev, rel_l2, say
-from step_util import StepRun, oracle_run
+from step_util import StepRun, check_rows, grad_rows, members, oracle_run
 
 pytestmark = pytest.mark.gpu
 
@@ -30,25 +28,9 @@ CONFIGS = [
 ]
 
 
-def check_grads(got, exact, floor_ref, cos_min=0.999):
-    """got / exact / floor_ref: dicts name -> gradient.  floor_ref is the
-    bf16-operand oracle (None: plain 1e-2 bar)."""
-    worst = (0.0, 1.0, None, 0.0)
-    bad = []
-    for name, r in exact.items():
-        g = np.asarray(got[name], dtype=np.float64)
-        assert np.all(np.isfinite(g)), name
-        e = rel_l2(g, r)
-        c = cosine(g, r)
-        floor = rel_l2(floor_ref[name], r) if floor_ref is not None else 0.0
-        tol = max(1e-2, 1.5 * floor)
-        if e / tol > worst[0] / max(1e-2, 1.5 * worst[3]):
-            worst = (e, c, name, floor)
-        if not (e <= tol and c >= cos_min):
-            bad.append(f"{name}: rel_l2 {e:.3e} (floor {floor:.3e}) cos {c:.6f}")
-    say(f"  worst gradient vs tolerance: {worst[2]} rel_l2 {worst[0]:.3e} bf16 floor {worst[3]:.3e} "
-        f"cos {worst[1]:.6f}")
-    assert not bad, bad
+def check_grads(got, exact, mems, base=1e-2, names=None, label=""):
+    """Every gradient tensor against the exact oracle at the ensemble bar."""
+    check_rows(grad_rows(got, exact, [m["grads"] for m in mems], base, names), label)
 
 
 @pytest.mark.parametrize("depth,vocab,T,B", CONFIGS)
@@ -77,8 +59,7 @@ def test_step_parity(depth, vocab, T, B):
         zt = run.ws_tensor(9).cpu().numpy()
         tgt = run.ids_np[:, 1:].reshape(-1)
         assert np.array_equal(zt, logits.cpu().numpy()[np.arange(len(tgt)), tgt])
-    floor = oracle_run(run, bf16_operands=True)
-    check_grads(run.grads(), ref["grads"], floor["grads"])
+    check_grads(run.grads(), ref["grads"], members(run))
 
 
 GQA_WINDOW_CONFIGS = [
@@ -106,8 +87,7 @@ def test_step_parity_gqa_window(depth, vocab, T, B, n_kv_head, window, pattern):
     e = rel_l2(from_dev(run.row_lse), ref["lse"].reshape(-1))
     say(f"  row lse rel_l2 {e:.3e}")
     assert e <= 1e-2
-    floor = oracle_run(run, bf16_operands=True)
-    check_grads(run.grads(), ref["grads"], floor["grads"])
+    check_grads(run.grads(), ref["grads"], members(run))
 
 
 def test_bwd_accumulate_adds():
