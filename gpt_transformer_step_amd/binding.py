@@ -64,6 +64,7 @@ _SIGS = {
     "muon_workspace_size": [_i32, _i32, _i32, _P(_sz)],
     "muon_update": [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _P(_f32), _i32, _f32, _f32, _f32,
                     _vp, _sz, _vp],
+    "muon_update_noalloc": [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _P(_f32), _i32, _f32, _f32, _f32, _vp],
     "normuon_update": [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _P(_f32), _i32, _f32, _f32, _f32,
                        _f32, _f32, _vp, _sz, _vp],
     "gpt_op_gemm": [_i32, _i32, _i32, _i32, _vp, _i32, _i64, _i64, _vp, _i32, _i64, _i64, _vp, _i32,
@@ -226,6 +227,23 @@ def muon_update(G, coeffs, ws, W=None, W_bf16=None, M=None, O_out=None, lr=0.02,
     _call("muon_update", _ptr(W), _ptr(W_bf16), _ptr(G), _ptr(M), _ptr(O_out), count, rows, cols,
           carr, len(coeffs), lr, momentum, weight_decay, _ptr(ws), ws.numel() * ws.element_size(),
           _stream(stream))
+
+
+def muon_update_noalloc(G, coeffs, W=None, W_bf16=None, M=None, O_out=None, lr=0.02, momentum=0.95,
+                        weight_decay=0.0, stream=None):
+    """muon_update with the library's own per-GPU scratch (no workspace, no
+    allocation); raises GptError (code -3) when the shape needs more scratch."""
+    if G.dim() == 2:
+        count, rows, cols = 1, G.shape[0], G.shape[1]
+    else:
+        count, rows, cols = G.shape
+    flat = [float(x) for t in coeffs for x in t]
+    carr = (_f32 * len(flat))(*flat)
+    _call("muon_update_noalloc", _ptr(W), _ptr(W_bf16), _ptr(G), _ptr(M), _ptr(O_out), count, rows, cols, carr,
+          len(coeffs), lr, momentum, weight_decay, _stream(stream))
+
+
+NOALLOC_SCRATCH_BYTES = 160 * 1024 * 1024
 
 
 def normuon_update(G, coeffs, ws, V, W=None, W_bf16=None, M=None, O_out=None, lr=0.02, momentum=0.95,

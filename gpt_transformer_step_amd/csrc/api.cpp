@@ -5,6 +5,7 @@
 #include <algorithm>
 #include <string.h>
 
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -1261,6 +1262,52 @@ extern "C" gpt_status muon_update(float* Wt, uint16_t* W_bf16, const float* Gm, 
                                   size_t ws_bytes, gpt_stream_t stream) {
   return (gpt_status)muon_impl(Wt, W_bf16, Gm, M, O_out, count, rows, cols, coeffs, ns_steps, lr, momentum, weight_decay,
                    nullptr, ws, ws_bytes, stream);
+}
+
+// ---------------------------------------------------------------------------
+// Muon without any allocation: the workspace is a file-scope device array
+// ---------------------------------------------------------------------------
+// Every GPU the library runs on holds its own copy of `scratch` until the
+// process ends.  Host code never passes the array's name to a kernel (on the
+// host it is only a stand-in): the device address of this GPU's copy comes
+// from hipGetSymbolAddress, taken once per device with that device current.
+static __device__ __align__(256) unsigned char scratch[GPT_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+int scratch_ptr(void** out) {
+  int dev = 0;
+  GS_HIP_CHECK(hipGetDevice(&dev));
+  if (dev < 0 || dev >= kMaxDevices) FAIL(GPT_ERR_UNSUPPORTED, "device index beyond the scratch table");
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    GS_HIP_CHECK(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)));
+    if (!p || ((uintptr_t)p % kAlign)) FAIL(GPT_ERR_HIP, "scratch symbol address missing or misaligned");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return 0;
+}
+}  // namespace
+
+extern "C" gpt_status muon_update_noalloc(float* Wt, uint16_t* W_bf16, const float* Gm, float* M, float* O_out,
+                                          int32_t count, int32_t rows, int32_t cols, const float* coeffs,
+                                          int32_t ns_steps, float lr, float momentum, float weight_decay,
+                                          gpt_stream_t stream) {
+  TRY(check_muon_shape(count, rows, cols));
+  const size_t need = muon_layout(count, rows, cols).total;
+  if (need > (size_t)GPT_NOALLOC_SCRATCH_BYTES)
+    FAIL(GPT_ERR_WORKSPACE, "muon_update_noalloc: these matrices need " + std::to_string(need) +
+                                " bytes of scratch, more than the " + std::to_string((size_t)GPT_NOALLOC_SCRATCH_BYTES) +
+                                " the library holds per GPU; call muon_update with a workspace");
+  void* ws = nullptr;
+  TRY(scratch_ptr(&ws));
+  return (gpt_status)muon_impl(Wt, W_bf16, Gm, M, O_out, count, rows, cols, coeffs, ns_steps, lr, momentum,
+                               weight_decay, nullptr, ws, (size_t)GPT_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 extern "C" gpt_status normuon_update(float* Wt, uint16_t* W_bf16, const float* Gm, float* M, float* V,

@@ -22,7 +22,8 @@
  *   - Pointers are DEVICE pointers unless the comment says "host".
  *   - The caller owns all memory.  The library never allocates or frees
  *     device memory; scratch space comes from a caller-provided workspace
- *     whose size is queried first.
+ *     whose size is queried first (muon_update_noalloc alone uses a device
+ *     array the library holds instead).
  *   - Every call validates its arguments on the host first and returns a
  *     status; no argument error ever reaches the device.  Kernel launch
  *     failures return GPT_ERR_HIP with details in gpt_last_error().
@@ -231,6 +232,24 @@ gpt_status normuon_update(float* W, uint16_t* W_bf16, const float* G, float* M, 
                           int32_t count, int32_t rows, int32_t cols, int32_t per_row, const float* coeffs,
                           int32_t ns_steps, float lr, float momentum, float weight_decay, float beta2, float eps,
                           void* ws, size_t ws_bytes, gpt_stream_t stream);
+
+/* muon_update for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same arguments and results as muon_update, without the workspace
+ * arguments.  Its scratch space is a device array the library holds on each
+ * GPU it runs on, GPT_NOALLOC_SCRATCH_BYTES bytes, until the process ends;
+ * the call makes no allocation of any kind.  Shapes whose
+ * muon_workspace_size() exceeds that size return GPT_ERR_WORKSPACE (the
+ * message names both sizes).  Every call on one GPU shares that GPU's array:
+ * calls that overlap on one GPU (different streams, or threads) race, and
+ * must be ordered by the caller.  Nothing in the array needs to be cleared
+ * between calls.  GPT_ERR_HIP if the array's device address cannot be
+ * taken. */
+#define GPT_NOALLOC_SCRATCH_BYTES (160u * 1024u * 1024u)
+gpt_status muon_update_noalloc(float* W, uint16_t* W_bf16, const float* G, float* M, float* O_out,
+                               int32_t count, int32_t rows, int32_t cols, const float* coeffs,
+                               int32_t ns_steps, float lr, float momentum, float weight_decay,
+                               gpt_stream_t stream);
 
 /* Text of a status, and the message of the last failing call on this thread
  * (empty when none).  Both return static or thread-local storage. */
