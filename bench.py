@@ -15,7 +15,16 @@ MFU counts algorithmic FLOPs only: 6 (12 L d^2 + V d) per token for the
 matrix products, 6 L d T per token for the causal half of attention, plus
 5 Newton-Schulz iterations of (4 l s^2 + 2 s^3) per block matrix; recomputed
 scores and logits are not counted.  Peak: MI355X dense bf16 MFMA,
-2.5166 PFLOP/s.
+2.5166 PFLOP/s.  Also reported: mfu_model (forward + backward time only),
+mfu_palm (the PaLM convention: 6 (12 L d^2 + V d) + 12 L d T per token, the
+whole attention square, over the step time), and the same MFU against the
+matrix-core rate an MFMA-only probe sustains in the same run
+(mfu_vs_achievable_peak).
+
+The default bf16 run also times the fp8 step (--precision fp8) right after,
+on the same resident token ids and the same initial weights and optimizer
+state: fp8_ms_per_step, fp8_speedup = bf16 / fp8 step time, and the fp8 MFU
+against the mixed peak (block products at the fp8 peak, the rest at bf16).
 """
 
 import argparse
@@ -94,6 +103,15 @@ def alg_flops(m):
         l, s_ = max(rows, cols), min(rows, cols)
         f_ns += 5 * (4 * l * s_ * s_ + 2 * s_ ** 3)
     return f_model, f_ns
+
+
+def palm_flops(m):
+    """Model FLOPs of one forward+backward in the PaLM convention: 6 per
+    parameter-token for the matrices (embedding included, as above) and
+    12 L d T per token for attention over the whole T x T square."""
+    d, dkv, N = m.d, m.dkv, m.N
+    per_layer = d * (d + 2 * dkv) + d * d + 8 * d * d
+    return 6.0 * (m.L * per_layer + m.V * d) * N + 12.0 * m.L * d * m.T * N
 
 
 def muon_runs(mats):
@@ -229,6 +247,138 @@ def ns_standalone(args):
                       "config": {"workload": "ns-standalone", "shapes": list(res)}, "per_shape": res}), flush=True)
 
 
+def achievable_peak():
+    """Dense bf16 matrix-core rate an MFMA-only probe sustains (FLOP/s): one
+    workgroup of 4 waves per SIMD slot pair on every CU, timed with events."""
+    import torch
+    from gpt_transformer_step_amd import binding as Bd
+    blocks, iters = 256 * 8, 4096
+    out = torch.empty(blocks * 256, dtype=torch.float32, device="cuda:0")
+    Bd.probe_mfma(0, blocks, 64, out)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    flops = Bd.probe_mfma(0, blocks, iters, out)
+    e1.record()
+    torch.cuda.synchronize()
+    return flops / (e0.elapsed_time(e1) * 1e-3)
+
+
+def run_precision(args, m, prec, master0, ids, dims, profile):
+    """Warm-up, (optionally) the per-category pass, then the timed steps of one
+    precision, from the initial weights master0 and zero optimizer state."""
+    import torch
+    from gpt_transformer_step_amd import binding as Bd
+    depth, V, T, B = m.L, m.V, m.T, m.B
+    dev = master0.device
+    sh = Bd.shape(depth, V, T, B, prec, n_kv_head=args.n_kv_head, window=args.window, pattern=args.pattern,
+                  features=args.features)
+    n = Bd.param_count(sh)
+    assert n == master0.numel()
+    master = master0.clone()
+    bf16 = torch.empty(n, dtype=torch.bfloat16, device=dev)
+    Bd.cast_bf16(master, bf16)
+    grad = torch.zeros(n, dtype=torch.float32, device=dev)
+    ws = torch.empty(Bd.workspace_size(sh), dtype=torch.uint8, device=dev)
+    params = Bd.make_params(master, bf16, grad)
+    loss = torch.zeros(1, dtype=torch.float32, device=dev)
+    offs = Bd.param_layout(sh)
+    # one muon_update per run of adjacent same-shape block matrices: the three
+    # groups (q/k/v/o, MLP in, MLP out) when every head has its own key/value
+    # head; with grouped heads wq/wo and wk/wv pairs differ in shape
+    groups = []
+    for st, count, rows, cols in muon_runs(m.block_mats(offs)):
+        size = count * rows * cols
+        groups.append(dict(count=count, rows=rows, cols=cols, start=st,
+                           M=torch.zeros(size, dtype=torch.float32, device=dev),
+                           V=torch.zeros(count * rows, dtype=torch.float32, device=dev) if args.normuon else None,
+                           ws=torch.empty(Bd.muon_workspace_size(count, rows, cols), dtype=torch.uint8,
+                                          device=dev)))
+
+    # AdamW for the embedding and the head (the two [V, d] tables) and, with the
+    # record-model features, for everything after the head (value-embedding
+    # tables, their gates and the scalars)
+    d = m.d
+    lm = offs[1 + 6 * depth]
+    ranges = [(offs[0], V * d), (lm, V * d)]
+    if args.features:
+        ranges.append((lm + V * d, n - (lm + V * d)))
+    adam = []
+    for start, size in ranges:
+        adam.append(dict(start=start, size=size, M=torch.zeros(size, dtype=torch.float32, device=dev),
+                         V=torch.zeros(size, dtype=torch.float32, device=dev)))
+    step_count = [0]
+
+    def step():
+        Bd.step_fwd(sh, params, ids, loss, ws)
+        Bd.step_bwd(sh, params, ids, ws)
+        step_count[0] += 1
+        for ad in adam:
+            st, size = ad["start"], ad["size"]
+            Bd.adamw_update(master[st:st + size], grad[st:st + size], ad["M"], ad["V"], step_count[0], lr=0.004,
+                            beta1=0.8, beta2=0.95, eps=1e-10, weight_decay=0.0, W_bf16=bf16[st:st + size])
+        for gr in groups:
+            st, size = gr["start"], gr["count"] * gr["rows"] * gr["cols"]
+            view = (gr["count"], gr["rows"], gr["cols"])
+            if args.normuon:
+                Bd.normuon_update(grad[st:st + size].view(view), NS5, gr["ws"], gr["V"],
+                                  W=master[st:st + size].view(view), W_bf16=bf16[st:st + size].view(view),
+                                  M=gr["M"], lr=0.02, momentum=0.95, weight_decay=0.0, beta2=0.95, eps=1e-8)
+            else:
+                Bd.muon_update(grad[st:st + size].view(view), NS5, gr["ws"], W=master[st:st + size].view(view),
+                               W_bf16=bf16[st:st + size].view(view), M=gr["M"], lr=0.02, momentum=0.95,
+                               weight_decay=0.0)
+
+    tag = "fp8" if prec == Bd.PREC_FP8 else "bf16"
+    print(f"bench: inputs resident ({args.workload}, {tag}); warm-up", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    first_loss = float(loss.item())
+    out = dict(first_loss=first_loss, breakdown=None, dom=None, dom_ms=None, dom_cnt=None)
+    if profile:
+        print("bench: warm-up done; per-category pass", file=sys.stderr, flush=True)
+        # per-kernel-category pass (untimed) to find the dominant kernel
+        cats = Bd.profile_categories()
+        Bd.profile_reset()
+        Bd.profile_enable((1 << len(cats)) - 1)
+        step()
+        torch.cuda.synchronize()
+        breakdown = {}
+        for i, c in enumerate(cats):
+            t, cnt = Bd.profile_read(i)
+            if cnt:
+                breakdown[c] = (t, cnt)
+        Bd.profile_enable(0)
+        Bd.profile_reset()
+        contractions = {c: v for c, v in breakdown.items() if kernel_flops(c, m)}
+        dom = max(contractions, key=lambda c: contractions[c][0])
+        dom_idx = cats.index(dom)
+        print(f"bench: dominant contraction {dom}; timed steps", file=sys.stderr, flush=True)
+        # the dominant kernel bracketed by HIP events on its launch stream
+        Bd.profile_enable(1 << dom_idx)
+        out.update(breakdown=breakdown, dom=dom)
+    # timed region: K steps between two events on the launch stream
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(args.steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    out["ms"] = e0.elapsed_time(e1) / args.steps
+    if profile:
+        dom_ms, dom_cnt = Bd.profile_read(dom_idx)
+        Bd.profile_enable(0)
+        Bd.profile_reset()
+        out.update(dom_ms=dom_ms, dom_cnt=dom_cnt)
+    out["last_loss"] = float(loss.item())
+    print(f"bench: {tag} {out['ms']:.2f} ms per step", file=sys.stderr, flush=True)
+    del ws, groups, adam, grad, bf16, master
+    torch.cuda.empty_cache()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -237,6 +387,7 @@ def main():
     ap.add_argument("--workload", default="d20", choices=["d2", "d12", "d20", "d26"])
     ap.add_argument("--precision", default="bf16", choices=["bf16", "fp8"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-fp8", action="store_true", help="skip the fp8 step timed after the bf16 one")
     ap.add_argument("--normuon", action="store_true",
                     help="NorMuon per-neuron rescale after Newton-Schulz (normuon_update)")
     ap.add_argument("--n-kv-head", type=int, default=0, help="key/value heads (0: one per query head)")
@@ -281,107 +432,18 @@ def main():
     d, H = m.d, m.H
     prec = Bd.PREC_FP8 if args.precision == "fp8" else Bd.PREC_BF16
     dev = torch.device("cuda:0")
-    sh = Bd.shape(depth, V, T, B, prec, n_kv_head=args.n_kv_head, window=args.window, pattern=args.pattern,
-                  features=args.features)
-    n = Bd.param_count(sh)
     dims = inputs.Dims.from_depth(depth, V, args.n_kv_head, features=args.features)
-    assert n == inputs.n_params(dims)
-    master_np = inputs.master_weights(dims, inputs.SEED_W)
-    master = torch.from_numpy(master_np).to(dev)
-    del master_np
-    bf16 = torch.empty(n, dtype=torch.bfloat16, device=dev)
-    Bd.cast_bf16(master, bf16)
-    grad = torch.zeros(n, dtype=torch.float32, device=dev)
+    master0 = torch.from_numpy(inputs.master_weights(dims, inputs.SEED_W)).to(dev)
     ids = torch.from_numpy(inputs.token_ids(B, T, V, inputs.SEED_IDS)).to(dev)
-    ws = torch.empty(Bd.workspace_size(sh), dtype=torch.uint8, device=dev)
-    params = Bd.make_params(master, bf16, grad)
-    loss = torch.zeros(1, dtype=torch.float32, device=dev)
-    offs = Bd.param_layout(sh)
-    # one muon_update per run of adjacent same-shape block matrices: the three
-    # groups (q/k/v/o, MLP in, MLP out) when every head has its own key/value
-    # head; with grouped heads wq/wo and wk/wv pairs differ in shape
-    groups = []
-    for st, count, rows, cols in muon_runs(m.block_mats(offs)):
-        size = count * rows * cols
-        groups.append(dict(count=count, rows=rows, cols=cols, start=st,
-                           M=torch.zeros(size, dtype=torch.float32, device=dev),
-                           V=torch.zeros(count * rows, dtype=torch.float32, device=dev) if args.normuon else None,
-                           ws=torch.empty(Bd.muon_workspace_size(count, rows, cols), dtype=torch.uint8,
-                                          device=dev)))
+    ach_peak = achievable_peak()
 
-    # AdamW for the embedding and the head (the two [V, d] tables) and, with the
-    # record-model features, for everything after the head (value-embedding
-    # tables, their gates and the scalars)
-    lm = offs[1 + 6 * depth]
-    ranges = [(offs[0], V * d), (lm, V * d)]
-    if args.features:
-        ranges.append((lm + V * d, n - (lm + V * d)))
-    adam = []
-    for start, size in ranges:
-        adam.append(dict(start=start, size=size, M=torch.zeros(size, dtype=torch.float32, device=dev),
-                         V=torch.zeros(size, dtype=torch.float32, device=dev)))
-    step_count = [0]
-
-    def step():
-        Bd.step_fwd(sh, params, ids, loss, ws)
-        Bd.step_bwd(sh, params, ids, ws)
-        step_count[0] += 1
-        for ad in adam:
-            st, size = ad["start"], ad["size"]
-            Bd.adamw_update(master[st:st + size], grad[st:st + size], ad["M"], ad["V"], step_count[0], lr=0.004,
-                            beta1=0.8, beta2=0.95, eps=1e-10, weight_decay=0.0, W_bf16=bf16[st:st + size])
-        for gr in groups:
-            st, size = gr["start"], gr["count"] * gr["rows"] * gr["cols"]
-            view = (gr["count"], gr["rows"], gr["cols"])
-            if args.normuon:
-                Bd.normuon_update(grad[st:st + size].view(view), NS5, gr["ws"], gr["V"],
-                                  W=master[st:st + size].view(view), W_bf16=bf16[st:st + size].view(view),
-                                  M=gr["M"], lr=0.02, momentum=0.95, weight_decay=0.0, beta2=0.95, eps=1e-8)
-            else:
-                Bd.muon_update(grad[st:st + size].view(view), NS5, gr["ws"], W=master[st:st + size].view(view),
-                               W_bf16=bf16[st:st + size].view(view), M=gr["M"], lr=0.02, momentum=0.95,
-                               weight_decay=0.0)
-
-    print(f"bench: inputs resident ({args.workload}, {args.precision}); warm-up", file=sys.stderr, flush=True)
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    first_loss = float(loss.item())
-    print("bench: warm-up done; per-category pass", file=sys.stderr, flush=True)
-
-    # per-kernel-category pass (untimed) to find the dominant kernel
-    cats = Bd.profile_categories()
-    Bd.profile_reset()
-    Bd.profile_enable((1 << len(cats)) - 1)
-    step()
-    torch.cuda.synchronize()
-    breakdown = {}
-    for i, c in enumerate(cats):
-        t, cnt = Bd.profile_read(i)
-        if cnt:
-            breakdown[c] = (t, cnt)
-    Bd.profile_enable(0)
-    Bd.profile_reset()
-    contractions = {c: v for c, v in breakdown.items() if kernel_flops(c, m)}
-    dom = max(contractions, key=lambda c: contractions[c][0])
-    dom_idx = cats.index(dom)
-
-    print(f"bench: dominant contraction {dom}; timed steps", file=sys.stderr, flush=True)
-    # timed region: K steps; the dominant kernel bracketed by HIP events on its launch stream
-    Bd.profile_enable(1 << dom_idx)
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    e0.record()
-    for _ in range(args.steps):
-        step()
-    e1.record()
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / args.steps
-    dom_ms, dom_cnt = Bd.profile_read(dom_idx)
-    Bd.profile_enable(0)
-    Bd.profile_reset()
-    last_loss = float(loss.item())
+    res = run_precision(args, m, prec, master0, ids, dims, profile=True)
+    fp8_res = None
+    if prec == Bd.PREC_BF16 and not args.no_fp8 and not args.features:
+        print("bench: fp8 step on the same inputs", file=sys.stderr, flush=True)
+        fp8_res = run_precision(args, m, Bd.PREC_FP8, master0, ids, dims, profile=False)
+    ms, first_loss, last_loss = res["ms"], res["first_loss"], res["last_loss"]
+    breakdown, dom, dom_ms, dom_cnt = res["breakdown"], res["dom"], res["dom_ms"], res["dom_cnt"]
 
     f_model, f_ns = alg_flops(m)
     tok = B * T
@@ -417,6 +479,9 @@ def main():
                                 " (5 Newton-Schulz iterations) on all block matrices, AdamW on embedding and head" +
                                 (" and the record-model tensors" if args.features else "")},
         "mfu": (f_model + f_ns) / step_s / PEAK_BF16,
+        "mfu_vs_achievable_peak": (f_model + f_ns) / step_s / ach_peak,
+        "achievable_peak_tflops": ach_peak / 1e12,
+        "mfu_palm": palm_flops(m) / step_s / PEAK_BF16,
         "mfu_vs_mixed_peak": t_ideal / step_s if fp8 else None,
         "mfu_model": f_model / (fwd_bwd_ms / 1e3) / PEAK_BF16 if fwd_bwd_ms else None,
         "tflops": (f_model + f_ns) / step_s / 1e12,
@@ -427,6 +492,12 @@ def main():
                      "launches": dom_cnt},
         "breakdown_ms_per_step": {k: round(v[0], 3) for k, v in sorted(breakdown.items(), key=lambda kv: -kv[1][0])},
     }
+    if fp8_res is not None:
+        f_block = block_gemm_flops(m)
+        t8_ideal = f_block / PEAK_FP8 + (f_model + f_ns - f_block) / PEAK_BF16
+        out.update({"fp8_ms_per_step": fp8_res["ms"], "fp8_tokens_per_s": tok / (fp8_res["ms"] / 1e3),
+                    "fp8_speedup": ms / fp8_res["ms"], "fp8_mfu_vs_mixed_peak": t8_ideal / (fp8_res["ms"] / 1e3),
+                    "fp8_loss": [fp8_res["first_loss"], fp8_res["last_loss"]]})
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(args.workload, m, inputs.SEED_IDS, inputs.SEED_W)
     print(json.dumps(out), flush=True)

@@ -722,9 +722,9 @@ extern "C" gpt_status gpt_step_fwd(const gpt_shape* shape, const gpt_params* par
     ProfScope ps_(P_EMBED_FWD, s);
     if (f_smear || f_resid)  // gather (+ smear with the previous token), x0 kept for the residual scalars
       TRY(launch_smear_fwd(ids, W + P.wte, f_smear ? W + P.smear_w(D) : nullptr, f_smear ? W + P.smear_lam(D) : nullptr,
-                           x, x0, at<float>(ws, w.sig), D.B, D.T, d, s));
+                           x, x0, at<float>(ws, w.sig), D.B, D.T, d, D.V, s));
     else
-      TRY(launch_embed_fwd(ids, W + P.wte, x, D.B, D.T, d, s));
+      TRY(launch_embed_fwd(ids, W + P.wte, x, D.B, D.T, d, D.V, s));
   }
   long long act_slots = 0;
   for (int l = 0; l < D.L; ++l) {
@@ -758,7 +758,7 @@ extern "C" gpt_status gpt_step_fwd(const gpt_shape* shape, const gpt_params* par
     if (D.ve_layer(l)) {  // v += 3 sigmoid(h1[:32] Wg^T) VE[token] per key/value head
       ProfScope ps_(P_FEATURES, s);
       TRY(launch_ve_fwd(ids, h1, d, W + P.vg(D, l), W + P.ve(D, l), qkv + d + D.dkv, D.dqkv, at<float>(ws, L.vgate),
-                        D.B, D.T, D.Hkv, s));
+                        D.B, D.T, D.Hkv, D.V, s));
     }
     { ProfScope ps_(P_ATTN_FWD, s); TRY(launch_attn_fwd(qkv, qkv + d, qkv + d + D.dkv, D.dqkv, att, d, at<float>(ws, L.lse), D.B, D.H, D.Hkv, D.T, D.layer_window(l), s)); }
     TRY(quant_x(att, d, L.attt, sc ? sc + SC_ATT : nullptr, 0));
@@ -875,9 +875,14 @@ extern "C" gpt_status gpt_step_bwd_scaled(const gpt_shape* shape, const gpt_para
   float* gfin = f_back ? at<float>(ws, w.gfin) : nullptr;
   float* dzve = D.has(GPT_FEAT_VALUE_EMBED) ? at<float>(ws, w.dzve) : nullptr;
   if (D.feat && !acc) {
-    // value-embedding tables take atomics; a cleared feature bit leaves its gradients at 0
+    // the value-embedding tables are gathered onto these zeros; a cleared feature bit leaves its gradients at 0
     ProfScope ps_(P_FILL, s);
     TRY(launch_fill_f32(G + P.lm_end, (long long)(P.total - P.lm_end), 0.f, s));
+  }
+  if (D.has(GPT_FEAT_VALUE_EMBED)) {
+    // the token ids' stable sort, shared by the value-embedding tables and the token embedding
+    ProfScope ps_(P_EMBED_BWD, s);
+    TRY(launch_embed_sort(ids, D.B, D.T, D.V, at<void>(ws, w.emb), s));
   }
 
   // fused head + cross-entropy backward, one vocabulary chunk at a time
@@ -1010,8 +1015,13 @@ extern "C" gpt_status gpt_step_bwd_scaled(const gpt_shape* shape, const gpt_para
     }
     if (D.ve_layer(l)) {  // value embedding: dVE[token] += gate dv; gate-logit gradients dz
       ProfScope ps_(P_FEATURES, s);
-      TRY(launch_ve_bwd(ids, dqkv + d + D.dkv, D.dqkv, W + P.ve(D, l), at<float>(ws, L.vgate), G + P.ve(D, l), dzve,
-                        D.B, D.T, D.Hkv, s));
+      // per-token contributions gate dv (fp32, in du's memory: du is dead once the
+      // MLP weight gradients are done, and holds 2 N 4d >= 4 N dkv bytes), then
+      // each table row sums its tokens' contributions in token order
+      float* vec = reinterpret_cast<float*>(du);
+      TRY(launch_ve_bwd(ids, dqkv + d + D.dkv, D.dqkv, W + P.ve(D, l), at<float>(ws, L.vgate), vec, dzve, D.B, D.T,
+                        D.Hkv, D.V, s));
+      TRY(launch_embed_gather(vec, G + P.ve(D, l), (long long)N, D.dkv, D.V, true, at<void>(ws, w.emb), s));
     }
     if (f8) TRY(quant_dy(dqkv, D.dqkv, sc + SC_DQKV, 0));
     {
@@ -1048,12 +1058,13 @@ extern "C" gpt_status gpt_step_bwd_scaled(const gpt_shape* shape, const gpt_para
     ProfScope ps_(P_FEATURES, s);
     TRY(launch_smear_bwd(ids, W + P.wte, f_smear ? W + P.smear_w(D) : nullptr, f_smear ? W + P.smear_lam(D) : nullptr,
                          g, g0, at<float>(ws, w.sig), dh, fpart, G + P.smear_lam(D), G + P.smear_w(D), acc, D.B, D.T,
-                         d, s));
+                         d, D.V, s));
     gemb = dh;
   }
   {  // writes every row of the embedding gradient (adds to it when accumulating)
     ProfScope ps_(P_EMBED_BWD, s);
-    TRY(launch_embed_bwd(ids, gemb, G + P.wte, D.B, D.T, d, D.V, acc, at<void>(ws, w.emb), s));
+    if (!D.has(GPT_FEAT_VALUE_EMBED)) TRY(launch_embed_sort(ids, D.B, D.T, D.V, at<void>(ws, w.emb), s));
+    TRY(launch_embed_gather(gemb, G + P.wte, N, d, D.V, acc, at<void>(ws, w.emb), s));
   }
   return GPT_OK;
 }

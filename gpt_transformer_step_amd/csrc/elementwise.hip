@@ -64,18 +64,20 @@ __global__ void rope_table_kernel(float* cs, int T) {
   cs[T * 64 + idx] = (float)sin(ang);
 }
 
-// x[n, :] = wte[ids[b, t], :] for n = b*T + t (bf16 -> fp32, exact)
+// x[n, :] = wte[ids[b, t], :] for n = b*T + t (bf16 -> fp32, exact); an id
+// outside [0, V) reads nothing and gives a zero row
 __global__ void __launch_bounds__(256) embed_fwd_kernel(const int* __restrict__ ids, const uint16_t* __restrict__ wte,
-                                 float* __restrict__ x, int B, int T, int d) {
+                                 float* __restrict__ x, int B, int T, int d, int V) {
   const int lane = threadIdx.x & 63;
   const long long n = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (n >= (long long)B * T) return;
   const int b = (int)(n / T), t = (int)(n % T);
   const long long id = ids[(long long)b * (T + 1) + t];
-  const uint16_t* src = wte + id * d;
+  const bool ok = id >= 0 && id < V;
+  const uint16_t* src = wte + (ok ? id : 0) * d;
   float* dst = x + n * d;
   for (int c = lane; c < d / 8; c += 64) {
-    const uint4 w = *reinterpret_cast<const uint4*>(src + c * 8);
+    const uint4 w = ok ? *reinterpret_cast<const uint4*>(src + c * 8) : make_uint4(0u, 0u, 0u, 0u);
     *reinterpret_cast<float4*>(dst + c * 8) = make_float4(lo_bf(w.x), hi_bf(w.x), lo_bf(w.y), hi_bf(w.y));
     *reinterpret_cast<float4*>(dst + c * 8 + 4) = make_float4(lo_bf(w.z), hi_bf(w.z), lo_bf(w.w), hi_bf(w.w));
   }
@@ -92,6 +94,7 @@ __global__ void __launch_bounds__(256) embed_fwd_kernel(const int* __restrict__ 
 //   emb_scan:   exclusive prefix of the totals over the ids (one workgroup)
 //   emb_place:  token n goes to position off[id] + block prefix + rank
 //   emb_gather: dwte[v] (+)= sum of g over the tokens of v
+// Ids outside [0, V) take no part: they are neither counted nor placed.
 constexpr int kEmbBlk = 1024;
 __device__ __forceinline__ int token_id(const int* ids, long long n, int T) {
   return ids[(n / T) * (T + 1) + n % T];
@@ -103,10 +106,12 @@ __global__ void __launch_bounds__(kEmbBlk) emb_rank_kernel(const int* __restrict
   const long long n0 = (long long)blockIdx.x * kEmbBlk;
   const int cnt = (int)min((long long)kEmbBlk, N - n0);
   const int t = threadIdx.x;
-  sid[t] = t < cnt ? token_id(ids, n0 + t, T) : -1;
+  int tid_ = t < cnt ? token_id(ids, n0 + t, T) : -1;
+  sid[t] = (tid_ >= 0 && tid_ < V) ? tid_ : -1;
   __syncthreads();
   if (t >= cnt) return;
   const int id = sid[t];
+  if (id < 0) return;
   int r = 0;
   bool last = true;
   for (int j = 0; j < cnt; ++j) {
@@ -161,6 +166,7 @@ __global__ void __launch_bounds__(256) emb_place_kernel(const int* __restrict__ 
   const long long n = (long long)blockIdx.x * 256 + threadIdx.x;
   if (n >= N) return;
   const int id = token_id(ids, n, T);
+  if (id < 0 || id >= V) return;
   const long long b = n / kEmbBlk;
   perm[off[id] + blockcnt[b * V + id] + rank[n]] = (int)n;
 }
@@ -722,8 +728,8 @@ int launch_rope_table(float* cs, int T, hipStream_t s) {
   return 0;
 }
 
-int launch_embed_fwd(const int* ids, const uint16_t* wte, float* x, int B, int T, int d, hipStream_t s) {
-  hipLaunchKernelGGL(embed_fwd_kernel, dim3(nblocks((long long)B * T, 4)), dim3(256), 0, s, ids, wte, x, B, T, d);
+int launch_embed_fwd(const int* ids, const uint16_t* wte, float* x, int B, int T, int d, int V, hipStream_t s) {
+  hipLaunchKernelGGL(embed_fwd_kernel, dim3(nblocks((long long)B * T, 4)), dim3(256), 0, s, ids, wte, x, B, T, d, V);
   GS_LAUNCH_CHECK("embed_fwd");
   return 0;
 }
@@ -733,8 +739,7 @@ size_t embed_bwd_workspace(long long N, int V) {
   return (size_t)(nb * V + V + (V + 1) + 2 * N) * 4;
 }
 
-int launch_embed_bwd(const int* ids, const float* g, float* dwte, int B, int T, int d, int V, bool accumulate,
-                     void* ws, hipStream_t s) {
+int launch_embed_sort(const int* ids, int B, int T, int V, void* ws, hipStream_t s) {
   const long long N = (long long)B * T;
   if (N <= 0 || V <= 0) return 0;
   const int nb = (int)((N + kEmbBlk - 1) / kEmbBlk);
@@ -756,7 +761,16 @@ int launch_embed_bwd(const int* ids, const float* g, float* dwte, int B, int T, 
   hipLaunchKernelGGL(emb_place_kernel, dim3((unsigned)((N + 255) / 256)), dim3(256), 0, s, ids, N, T, V, blockcnt,
                      rank, off, perm);
   GS_LAUNCH_CHECK("emb_place");
-  hipLaunchKernelGGL(emb_gather_kernel, dim3((V + 3) / 4), dim3(256), 0, s, off, perm, g, dwte, V, d,
+  return 0;
+}
+
+int launch_embed_gather(const float* g, float* dst, long long N, int d, int V, bool accumulate, const void* ws,
+                        hipStream_t s) {
+  if (N <= 0 || V <= 0) return 0;
+  const int nb = (int)((N + kEmbBlk - 1) / kEmbBlk);
+  const int* off = static_cast<const int*>(ws) + (long long)nb * V + V;
+  const int* perm = off + V + 1 + N;
+  hipLaunchKernelGGL(emb_gather_kernel, dim3((V + 3) / 4), dim3(256), 0, s, off, perm, g, dst, V, d,
                      accumulate ? 1 : 0);
   GS_LAUNCH_CHECK("emb_gather");
   return 0;

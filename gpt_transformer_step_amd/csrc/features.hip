@@ -6,7 +6,9 @@
 // row, 16-byte accesses, scalars read on the device from the bf16 parameter
 // copy (no host round trip).  Scalar and gate gradients are per-workgroup
 // partial sums reduced by reduce_partials_kernel (deterministic, no atomics);
-// only the value-embedding tables take fp32 atomics, as the token embedding.
+// the value-embedding tables' gradients go through the token embedding's
+// stable sort and gather, so they are deterministic too.  A token id outside
+// [0, V) is never used as an index: its embedding rows count as zero.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -37,28 +39,30 @@ __device__ __forceinline__ float sigm(float z) { return 1.f / (1.f + expf(-z)); 
 __global__ void __launch_bounds__(256) smear_fwd_kernel(const int* __restrict__ ids, const uint16_t* __restrict__ wte,
                                                         const uint16_t* __restrict__ sw, const uint16_t* __restrict__ slam,
                                                         float* __restrict__ x, float* __restrict__ x0,
-                                                        float* __restrict__ sig_out, int B, int T, int d) {
+                                                        float* __restrict__ sig_out, int B, int T, int d, int V) {
   const int lane = threadIdx.x & 63;
   const long long n = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (n >= (long long)B * T) return;
   const int b = (int)(n / T), t = (int)(n % T);
   const long long row = (long long)b * (T + 1) + t;
-  const uint16_t* e = wte + (long long)ids[row] * d;
+  const int id = ids[row], idp = t > 0 ? ids[row - 1] : id;
+  const float ok = (id >= 0 && id < V) ? 1.f : 0.f, okp = (idp >= 0 && idp < V) ? 1.f : 0.f;
+  const uint16_t* e = wte + (long long)(ok != 0.f ? id : 0) * d;
   // slam NULL: no smear (plain gather, optionally copied to x0)
-  float z = (slam && lane < kSmearCh) ? bfv(e + lane) * bfv(sw + lane) : 0.f;
+  float z = (slam && lane < kSmearCh) ? ok * bfv(e + lane) * bfv(sw + lane) : 0.f;
   z = wave_sum(z);
   const float sg = sigm(z);
-  const float gate = (slam && t > 0) ? bfv(slam) * sg : 0.f;
-  const uint16_t* ep = t > 0 ? wte + (long long)ids[row - 1] * d : e;
+  const float gate = (slam && t > 0) ? bfv(slam) * sg * okp : 0.f;
+  const uint16_t* ep = okp != 0.f ? wte + (long long)idp * d : e;
   float* xr = x + n * d;
   float* x0r = x0 ? x0 + n * d : nullptr;
   for (int c = lane; c < d / 8; c += 64) {
     const uint4 w = *reinterpret_cast<const uint4*>(e + c * 8);
     const uint4 p = *reinterpret_cast<const uint4*>(ep + c * 8);
-    const float4 lo = make_float4(lo_bf(w.x) + gate * lo_bf(p.x), hi_bf(w.x) + gate * hi_bf(p.x),
-                                  lo_bf(w.y) + gate * lo_bf(p.y), hi_bf(w.y) + gate * hi_bf(p.y));
-    const float4 hi = make_float4(lo_bf(w.z) + gate * lo_bf(p.z), hi_bf(w.z) + gate * hi_bf(p.z),
-                                  lo_bf(w.w) + gate * lo_bf(p.w), hi_bf(w.w) + gate * hi_bf(p.w));
+    const float4 lo = make_float4(ok * lo_bf(w.x) + gate * lo_bf(p.x), ok * hi_bf(w.x) + gate * hi_bf(p.x),
+                                  ok * lo_bf(w.y) + gate * lo_bf(p.y), ok * hi_bf(w.y) + gate * hi_bf(p.y));
+    const float4 hi = make_float4(ok * lo_bf(w.z) + gate * lo_bf(p.z), ok * hi_bf(w.z) + gate * hi_bf(p.z),
+                                  ok * lo_bf(w.w) + gate * lo_bf(p.w), ok * hi_bf(w.w) + gate * hi_bf(p.w));
     *reinterpret_cast<float4*>(xr + c * 8) = lo;
     *reinterpret_cast<float4*>(xr + c * 8 + 4) = hi;
     if (x0r) {
@@ -79,7 +83,7 @@ __global__ void __launch_bounds__(256) smear_bwd_kernel(const int* __restrict__ 
                                                         const uint16_t* __restrict__ sw, const uint16_t* __restrict__ slam,
                                                         const float* __restrict__ g, const float* __restrict__ g0,
                                                         const float* __restrict__ sig, float* __restrict__ de,
-                                                        float* __restrict__ part, int B, int T, int d) {
+                                                        float* __restrict__ part, int B, int T, int d, int V) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const long long N = (long long)B * T;
   // slam NULL: no smear, de = g + g0 only
@@ -88,9 +92,13 @@ __global__ void __launch_bounds__(256) smear_bwd_kernel(const int* __restrict__ 
   for (long long n = (long long)blockIdx.x * 4 + wave; n < N; n += (long long)gridDim.x * 4) {
     const int b = (int)(n / T), t = (int)(n % T);
     const long long row = (long long)b * (T + 1) + t;
-    const uint16_t* e = wte + (long long)ids[row] * d;
-    const bool has_prev = t > 0, has_next = t + 1 < T;
-    const uint16_t* ep = has_prev ? wte + (long long)ids[row - 1] * d : e;
+    const int id = ids[row];
+    const bool ok = id >= 0 && id < V;
+    const uint16_t* e = wte + (long long)(ok ? id : 0) * d;
+    const int idp = t > 0 ? ids[row - 1] : -1;
+    // an out-of-range previous token was gathered as a zero row: nothing to smear
+    const bool has_prev = t > 0 && idp >= 0 && idp < V, has_next = t + 1 < T;
+    const uint16_t* ep = has_prev ? wte + (long long)idp * d : e;
     const float st = sig[n];
     const float gnext = has_next ? lam * sig[n + 1] : 0.f;
     const float* gr = g + n * d;
@@ -125,7 +133,7 @@ __global__ void __launch_bounds__(256) smear_bwd_kernel(const int* __restrict__ 
       }
       *reinterpret_cast<float4*>(der + c * 4) = v;
     }
-    if (lane < kSmearCh) acc += dz * bfv(e + lane);
+    if (lane < kSmearCh && ok) acc += dz * bfv(e + lane);
     if (lane == kSmearCh) acc += dot * st;
   }
   __shared__ float red[4][kSmearCh + 1];
@@ -202,7 +210,7 @@ __global__ void __launch_bounds__(256) ve_fwd_kernel(const int* __restrict__ ids
                                                      int d, const uint16_t* __restrict__ wg,
                                                      const uint16_t* __restrict__ ve, uint16_t* __restrict__ v,
                                                      long long ldv, float* __restrict__ gate_out, int B, int T,
-                                                     int Hkv) {
+                                                     int Hkv, int V) {
   const int lane = threadIdx.x & 63;
   const long long n = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (n >= (long long)B * T) return;
@@ -223,7 +231,8 @@ __global__ void __launch_bounds__(256) ve_fwd_kernel(const int* __restrict__ ids
     if (hh < Hkv) {
       const float gh = j == 0 ? g4[0] : j == 1 ? g4[1] : j == 2 ? g4[2] : g4[3];
       const int e0 = hh * 128 + (lane & 15) * 8;
-      const uint4 q = *reinterpret_cast<const uint4*>(ve + id * dkv + e0);
+      const uint4 q = (id >= 0 && id < V) ? *reinterpret_cast<const uint4*>(ve + id * dkv + e0)
+                                          : make_uint4(0u, 0u, 0u, 0u);
       uint4* vp = reinterpret_cast<uint4*>(v + n * ldv + e0);
       const uint4 a = *vp;
       *vp = make_uint4(pack_bf2(lo_bf(a.x) + gh * lo_bf(q.x), hi_bf(a.x) + gh * hi_bf(q.x)),
@@ -235,11 +244,12 @@ __global__ void __launch_bounds__(256) ve_fwd_kernel(const int* __restrict__ ids
   }
 }
 
-// dVE[id][h] += gate_h dv[:, h] (fp32 atomics); dz_h = (dv_h . VE[id][h]) gate_h (1 - gate_h / 3)
+// Per token: contrib[n][h] = gate_h dv[:, h] (fp32 [N, dkv], summed into the
+// table by the embedding gather); dz_h = (dv_h . VE[id][h]) gate_h (1 - gate_h / 3)
 __global__ void __launch_bounds__(256) ve_bwd_kernel(const int* __restrict__ ids, const uint16_t* __restrict__ dv,
                                                      long long lddv, const uint16_t* __restrict__ ve,
-                                                     const float* __restrict__ gate, float* __restrict__ dve,
-                                                     float* __restrict__ dz, int B, int T, int Hkv) {
+                                                     const float* __restrict__ gate, float* __restrict__ contrib,
+                                                     float* __restrict__ dz, int B, int T, int Hkv, int V) {
   const int lane = threadIdx.x & 63;
   const long long n = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (n >= (long long)B * T) return;
@@ -254,7 +264,8 @@ __global__ void __launch_bounds__(256) ve_bwd_kernel(const int* __restrict__ ids
     float dot = 0.f;
     if (ok) {
       const uint4 a = *reinterpret_cast<const uint4*>(dv + n * lddv + e0);
-      const uint4 q = *reinterpret_cast<const uint4*>(ve + id * dkv + e0);
+      const uint4 q = (id >= 0 && id < V) ? *reinterpret_cast<const uint4*>(ve + id * dkv + e0)
+                                          : make_uint4(0u, 0u, 0u, 0u);
       const uint32_t aw[4] = {a.x, a.y, a.z, a.w}, qw[4] = {q.x, q.y, q.z, q.w};
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
@@ -270,9 +281,9 @@ __global__ void __launch_bounds__(256) ve_bwd_kernel(const int* __restrict__ ids
     if (ok) {
       const float gh = gate[n * Hkv + hh];
       if ((lane & 15) == 0) dz[n * Hkv + hh] = dot * gh * (1.f - gh * (1.f / 3.f));
-      float* dst = dve + id * dkv + e0;
-#pragma unroll
-      for (int k = 0; k < 8; ++k) unsafeAtomicAdd(dst + k, gh * dvv[k]);
+      float* dst = contrib + n * dkv + e0;
+      *reinterpret_cast<float4*>(dst) = make_float4(gh * dvv[0], gh * dvv[1], gh * dvv[2], gh * dvv[3]);
+      *reinterpret_cast<float4*>(dst + 4) = make_float4(gh * dvv[4], gh * dvv[5], gh * dvv[6], gh * dvv[7]);
     }
   }
 }
@@ -401,18 +412,18 @@ static int reduce_to(const float* part, int nparts, int nvals, float* out, float
 }
 
 int launch_smear_fwd(const int* ids, const uint16_t* wte, const uint16_t* sw, const uint16_t* slam, float* x,
-                     float* x0, float* sig, int B, int T, int d, hipStream_t s) {
+                     float* x0, float* sig, int B, int T, int d, int V, hipStream_t s) {
   hipLaunchKernelGGL(smear_fwd_kernel, dim3(nblocks((long long)B * T, 4)), dim3(256), 0, s, ids, wte, sw, slam, x, x0,
-                     sig, B, T, d);
+                     sig, B, T, d, V);
   GS_LAUNCH_CHECK("smear_fwd");
   return 0;
 }
 
 int launch_smear_bwd(const int* ids, const uint16_t* wte, const uint16_t* sw, const uint16_t* slam, const float* g,
                      const float* g0, const float* sig, float* de, float* part, float* dlam, float* dw,
-                     bool accumulate, int B, int T, int d, hipStream_t s) {
+                     bool accumulate, int B, int T, int d, int V, hipStream_t s) {
   hipLaunchKernelGGL(smear_bwd_kernel, dim3(kFeatBlocks), dim3(256), 0, s, ids, wte, sw, slam, g, g0, sig, de, part,
-                     B, T, d);
+                     B, T, d, V);
   GS_LAUNCH_CHECK("smear_bwd");
   if (!slam) return 0;
   // part rows: [d lam, d w_0 .. d w_23]; d lam and d w are separate parameter slots
@@ -447,17 +458,17 @@ int launch_mix_rmsnorm_fwd(float* x, const float* y, const uint16_t* pa, const u
 }
 
 int launch_ve_fwd(const int* ids, const uint16_t* h1, int d, const uint16_t* wg, const uint16_t* ve, uint16_t* v,
-                  long long ldv, float* gate, int B, int T, int Hkv, hipStream_t s) {
+                  long long ldv, float* gate, int B, int T, int Hkv, int V, hipStream_t s) {
   hipLaunchKernelGGL(ve_fwd_kernel, dim3(nblocks((long long)B * T, 4)), dim3(256), 0, s, ids, h1, d, wg, ve, v, ldv,
-                     gate, B, T, Hkv);
+                     gate, B, T, Hkv, V);
   GS_LAUNCH_CHECK("ve_fwd");
   return 0;
 }
 
 int launch_ve_bwd(const int* ids, const uint16_t* dv, long long lddv, const uint16_t* ve, const float* gate,
-                  float* dve, float* dz, int B, int T, int Hkv, hipStream_t s) {
-  hipLaunchKernelGGL(ve_bwd_kernel, dim3(nblocks((long long)B * T, 4)), dim3(256), 0, s, ids, dv, lddv, ve, gate, dve,
-                     dz, B, T, Hkv);
+                  float* contrib, float* dz, int B, int T, int Hkv, int V, hipStream_t s) {
+  hipLaunchKernelGGL(ve_bwd_kernel, dim3(nblocks((long long)B * T, 4)), dim3(256), 0, s, ids, dv, lddv, ve, gate,
+                     contrib, dz, B, T, Hkv, V);
   GS_LAUNCH_CHECK("ve_bwd");
   return 0;
 }

@@ -10,7 +10,6 @@ namespace gs {
 enum Epi {
   EPI_F32 = 0,     // C f32 = v + beta * C
   EPI_BF16,        // C bf16 = v
-  EPI_F32_ATOMIC,  // C f32 += v (atomic; split-K partial sums)
   EPI_RESID,       // C f32 += v (residual stream add; one writer per element)
   EPI_RELU2,       // C bf16 = max(v, 0)^2
   EPI_DRELU2,      // C bf16 = v * 2 sqrt(aux_bf16)       (ReLU^2 backward from a = relu(u)^2)
@@ -42,7 +41,7 @@ struct GemmArgs {
   float* part = nullptr;         // CE partials: float2 [M, nparts]
   int nparts = 0;
   float* zt = nullptr;           // CE target logit [M]
-  int k_split = 1;               // > 1: EPI_F32_ATOMIC, or EPI_F32 writing one partial per split
+  int k_split = 1;               // > 1: EPI_F32 writing one partial per split
   long long split_stride = 0;    // EPI_F32 with k_split > 1: split s writes C + s * split_stride
   const float* rope = nullptr;    // EPI_QKV: cos [row_T, 64] then sin [row_T, 64]
   int n_head = 0;                 // EPI_QKV: query heads

@@ -1,7 +1,8 @@
 // fp8 GEMM dispatch.  Both operands are k-contiguous fp8 codes.  Forward
 // products are E4M3 x E4M3 (gemm_f8_e4e4.hip); data- and weight-gradient
 // products are E5M2 (output gradient) x E4M3 (gemm_f8_e5e4.hip); the other
-// two pairings exist with the plain fp32 epilogue (gemm_f8_misc.hip).  Each
+// two pairings exist with the plain fp32 epilogue (gemm_f8_e4e5.hip,
+// gemm_f8_e5e5.hip).  Each
 // format pair is compiled in its own translation unit (the compiler's
 // optimiser fails on one that holds the scaled fp8 MFMA with two different
 // format pairs).

@@ -223,13 +223,9 @@ template <int EPI>
 __device__ __forceinline__ void epi4(const GemmArgs& p, int bi, int m, int n, const float* v, long long coff,
                                      float& amx, bool have_c = false, float4 cpre = make_float4(0.f, 0.f, 0.f, 0.f)) {
   const bool full = (n + 3 < p.N);
-  if constexpr (EPI == EPI_F32 || EPI == EPI_RESID || EPI == EPI_F32_ATOMIC) {
+  if constexpr (EPI == EPI_F32 || EPI == EPI_RESID) {
     float* C = reinterpret_cast<float*>(p.C) + (long long)bi * p.sC + coff + (long long)m * p.ldc + n;
-    if (EPI == EPI_F32_ATOMIC) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        if (n + j < p.N) unsafeAtomicAdd(C + j, v[j]);
-    } else if (full) {
+    if (full) {
       float4 o = make_float4(v[0], v[1], v[2], v[3]);
       if (EPI == EPI_RESID || p.beta != 0.f) {
         const float4 c = have_c ? cpre : *reinterpret_cast<const float4*>(C);

@@ -11,12 +11,16 @@ namespace gs {
 int launch_fill_f32(float* p, long long n, float v, hipStream_t s);
 int launch_cast_bf16(const float* src, uint16_t* dst, long long n, hipStream_t s);
 int launch_rope_table(float* cos_sin /* [T, 64] cos then [T, 64] sin */, int T, hipStream_t s);
-int launch_embed_fwd(const int* ids, const uint16_t* wte, float* x, int B, int T, int d, hipStream_t s);
-// dwte[v] (+)= sum of g rows of the tokens with id v (ids in [0, V), rows of
-// T + 1 ids per sequence); ws holds embed_bwd_workspace(B T, V) bytes
+int launch_embed_fwd(const int* ids, const uint16_t* wte, float* x, int B, int T, int d, int V, hipStream_t s);
+// scratch bytes of the embedding backward's sort (rows of T + 1 ids per
+// sequence; ids outside [0, V) take no part)
 size_t embed_bwd_workspace(long long N, int V);
-int launch_embed_bwd(const int* ids, const float* g, float* dwte, int B, int T, int d, int V, bool accumulate,
-                     void* ws, hipStream_t s);
+// stable counting sort of the token ids (ws: embed_bwd_workspace bytes), then
+// dst[v] (+)= sum over the tokens of id v, in token order, of g [N, d] rows
+// (d % 4 == 0); the gather may run several times on one sort
+int launch_embed_sort(const int* ids, int B, int T, int V, void* ws, hipStream_t s);
+int launch_embed_gather(const float* g, float* dst, long long N, int d, int V, bool accumulate, const void* ws,
+                        hipStream_t s);
 // amax_part (nullable): per-row max |stored bf16 value| at amax_part[row]
 int launch_rmsnorm_fwd(const float* x, uint16_t* h, float* r, long long N, int d, hipStream_t s,
                        float* amax_part = nullptr);
@@ -60,20 +64,21 @@ int launch_adamw(float* W, uint16_t* Wb, const float* G, float* M, float* V, lon
 long long feature_partial_floats(int Hkv);
 // x = e_t + lam sigmoid(e_t[:24] . sw) e_{t-1} (token 0: e_0); x0 (nullable) = copy; sig = the sigmoids
 int launch_smear_fwd(const int* ids, const uint16_t* wte, const uint16_t* sw, const uint16_t* slam, float* x,
-                     float* x0, float* sig, int B, int T, int d, hipStream_t s);
+                     float* x0, float* sig, int B, int T, int d, int V, hipStream_t s);
 // de = backward of smear for dX = g (+ g0); d lam and d sw written (or added) to dlam / dw
 int launch_smear_bwd(const int* ids, const uint16_t* wte, const uint16_t* sw, const uint16_t* slam, const float* g,
                      const float* g0, const float* sig, float* de, float* part, float* dlam, float* dw,
-                     bool accumulate, int B, int T, int d, hipStream_t s);
+                     bool accumulate, int B, int T, int d, int V, hipStream_t s);
 // x <- a x + bsign b y (a = 1 when pa is NULL); xin (nullable) = bf16(old x); h, r = RMSNorm of new x
 int launch_mix_rmsnorm_fwd(float* x, const float* y, const uint16_t* pa, const uint16_t* pb, float bsign,
                            uint16_t* xin, uint16_t* h, float* r, long long N, int d, float* amax_part, hipStream_t s);
 // v[:, head] += 3 sigmoid(h1[:32] . wg[head]) ve[id][head]; gate [N, Hkv] saved
 int launch_ve_fwd(const int* ids, const uint16_t* h1, int d, const uint16_t* wg, const uint16_t* ve, uint16_t* v,
-                  long long ldv, float* gate, int B, int T, int Hkv, hipStream_t s);
-// dve[id] += gate dv (atomics); dz = (dv . ve) gate (1 - gate / 3)
+                  long long ldv, float* gate, int B, int T, int Hkv, int V, hipStream_t s);
+// contrib [N, dkv] fp32 = gate dv per token (the table gradient is its sum per
+// id, by launch_embed_gather); dz = (dv . ve) gate (1 - gate / 3)
 int launch_ve_bwd(const int* ids, const uint16_t* dv, long long lddv, const uint16_t* ve, const float* gate,
-                  float* dve, float* dz, int B, int T, int Hkv, hipStream_t s);
+                  float* contrib, float* dz, int B, int T, int Hkv, int V, hipStream_t s);
 // dwg (+)= dz^T h1[:, :32]
 int launch_ve_gate_grad(const float* dz, const uint16_t* h1, int d, long long N, int Hkv, float* part, float* dwg,
                         bool accumulate, hipStream_t s);

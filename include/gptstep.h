@@ -30,8 +30,12 @@
  *   - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL = the
  *     default stream).  No call synchronises the device; results (including
  *     the loss) are in device memory when the stream reaches them.
+ *   - Token ids belong in [0, vocab).  An id outside that range is never
+ *     used as an index: its embedding (and value-embedding) rows are taken
+ *     as zero and it adds nothing to any gradient; the loss of a position
+ *     whose target is outside the range is undefined.
  *   - Preconditions that are not checked (they would need a device sync):
- *     0 <= id < vocab for every token id; device buffers of the stated sizes;
+ *     device buffers of the stated sizes;
  *     gpt_step_bwd follows gpt_step_fwd on the same stream with the same
  *     shape, parameters, ids and workspace, with no other use of that
  *     workspace in between.

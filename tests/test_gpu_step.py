@@ -125,3 +125,44 @@ def test_embedding_gather_bit_exact():
     wte = run.bf16[: off[1]].float().cpu().numpy().reshape(run.vocab, -1)
     inp = run.ids_np[:, :-1].reshape(-1)
     assert np.array_equal(x, wte[inp])
+
+
+@pytest.mark.parametrize("features", ["", "vs"])
+def test_out_of_range_ids_are_ignored(features):
+    """An id outside [0, vocab) at position 0 of each sequence (an input,
+    never a target) reads nothing and adds nothing: the step equals, bit for
+    bit, the step with a valid unused id k there whose embedding (and
+    value-embedding) rows are zero -- except the gradient of those rows,
+    which is 0 with the out-of-range id."""
+    depth, V, T, Bn = 2, 1024, 64, 2
+    runs = {}
+    for mode in ("oob", "zero_row"):
+        run = StepRun(depth, V, T, Bn, features=features)
+        ids = run.ids_np.copy()
+        k = int(np.setdiff1d(np.arange(V), ids)[0])   # an id that appears nowhere
+        ids[:, 0] = V + 7 if mode == "oob" else k
+        run.ids = torch.from_numpy(ids).cuda()
+        offs = run.B.param_layout(run.shape)
+        d = 64 * depth
+        with torch.no_grad():
+            run.bf16[offs[0] + k * d: offs[0] + (k + 1) * d] = 0
+            if "v" in features:
+                for l in range(0, depth, 2):
+                    ve = offs[2 + 6 * depth + l // 2]
+                    run.bf16[ve + k * d: ve + (k + 1) * d] = 0
+        run.fwd()
+        run.bwd()
+        torch.cuda.synchronize()
+        runs[mode] = (float(run.loss.item()), run.grad.cpu().numpy(), offs, k)
+    (la, ga, offs, k), (lb, gb, _, _) = runs["oob"], runs["zero_row"]
+    say(f"  loss with id {V + 7}: {la:.6f}; with zero row {k}: {lb:.6f}")
+    assert np.isfinite(la) and la == lb
+    d = 64 * depth
+    rows = [slice(offs[0] + k * d, offs[0] + (k + 1) * d)]
+    if "v" in features:
+        rows += [slice(offs[2 + 6 * depth + l // 2] + k * d, offs[2 + 6 * depth + l // 2] + (k + 1) * d)
+                 for l in range(0, depth, 2)]
+    for r in rows:
+        assert np.all(ga[r] == 0)
+        ga[r] = gb[r] = 0
+    assert np.array_equal(ga, gb)
