@@ -383,15 +383,23 @@ namespace {
 constexpr size_t kAlign = 256;
 inline size_t al(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
-// vocabulary chunk of the fused head backward (columns of dlogits held at once)
+// The head works on vocabulary chunks of vocab_chunk columns.  The forward
+// keeps exp(z - m) of every logit (fp16) chunk-major, [chunk][N][chunk_ld]; the
+// backward turns one chunk at a time into dlogits [N][chunk_ld] (bf16).
 inline int vocab_chunk(const Dims& D) { return D.V < 8192 ? D.V : 8192; }
+inline int chunk_ld(const Dims& D) { return (vocab_chunk(D) + 7) / 8 * 8; }
+inline int n_chunks(const Dims& D) { return (D.V + vocab_chunk(D) - 1) / vocab_chunk(D); }
 
-inline int ce_nparts(const Dims& D) {
+// Tile width of every head-forward launch, fixed from the whole vocabulary so
+// that all chunks agree on the (max, sum) column groups: one group per wave,
+// half a tile.  8192 is a multiple of both widths, so chunks start on tiles.
+inline int ce_tile(const Dims& D) {
   GemmArgs a;
   a.M = (int)D.N; a.N = D.V; a.K = D.d; a.batch = 1; a.k_split = 1;
-  const int bn = gemm_tile_n(a);
-  return ((D.V + bn - 1) / bn) * 2;
+  return gemm_tile_n(a);
 }
+inline int ce_group(const Dims& D) { return ce_tile(D) / 2; }
+inline int ce_nparts(const Dims& D) { return ((D.V + ce_tile(D) - 1) / ce_tile(D)) * 2; }
 
 inline size_t wgrad_part_elems(int M, int N, int K);
 
@@ -410,7 +418,7 @@ enum Fp8Scale { SC_H1, SC_ATT, SC_H2, SC_ACT, SC_WQKV, SC_WO, SC_WFC, SC_WPROJ, 
                 SC_DQKV, SC_COUNT = 16 };
 
 struct WS {
-  size_t cs, x, hf, rf, part, zt, lse, row_loss;
+  size_t cs, x, hf, rf, part, zt, lse, row_loss, ez;
   std::vector<Layer> layer;
   // backward scratch
   size_t g, g_bf, dh, du, dout, delta, dqkv, dz, wpart, emb;
@@ -448,6 +456,7 @@ WS ws_layout(const Dims& D) {
   w.hf = take(N * d * 2);
   w.rf = take(N * 4);
   w.part = take(N * (size_t)ce_nparts(D) * 8);
+  w.ez = take((size_t)n_chunks(D) * N * (size_t)chunk_ld(D) * 2);
   w.zt = take(N * 4);
   w.lse = take(N * 4);
   w.row_loss = take(N * 4);
@@ -459,7 +468,7 @@ WS ws_layout(const Dims& D) {
   w.delta = take(N * H * 4);
   w.emb = take(embed_bwd_workspace((long long)N, D.V));
   w.dqkv = take(N * dq3 * 2);
-  w.dz = take(N * (size_t)vocab_chunk(D) * 2);
+  w.dz = take(N * (size_t)chunk_ld(D) * 2);
   {
     const int Nt = (int)D.N, dd = D.d, hd = D.hidden;
     size_t mx = 0;
@@ -760,7 +769,7 @@ extern "C" gpt_status gpt_step_fwd(const gpt_shape* shape, const gpt_params* par
       TRY(launch_ve_fwd(ids, h1, d, W + P.vg(D, l), W + P.ve(D, l), qkv + d + D.dkv, D.dqkv, at<float>(ws, L.vgate),
                         D.B, D.T, D.Hkv, D.V, s));
     }
-    { ProfScope ps_(P_ATTN_FWD, s); TRY(launch_attn_fwd(qkv, qkv + d, qkv + d + D.dkv, D.dqkv, att, d, at<float>(ws, L.lse), D.B, D.H, D.Hkv, D.T, D.layer_window(l), s)); }
+    { ProfScope ps_(P_ATTN_FWD, s); TRY(launch_attn_fwd(qkv, qkv + d, qkv + d + D.dkv, D.dqkv, att, d, at<float>(ws, L.lse), D.B, D.H, D.Hkv, D.T, D.layer_window(l), s, true)); }
     TRY(quant_x(att, d, L.attt, sc ? sc + SC_ATT : nullptr, 0));
     {
       GemmArgs a;  // x += att Wo^T
@@ -812,13 +821,18 @@ extern "C" gpt_status gpt_step_fwd(const gpt_shape* shape, const gpt_params* par
     else
       TRY(launch_rmsnorm_fwd(x, hf, at<float>(ws, w.rf), N, d, s));
   }
-  {
-    GemmArgs a;  // per-tile (max, sum exp) of the logits hf W_lm^T, never stored
+  for (int c0 = 0; c0 < D.V; c0 += vocab_chunk(D)) {
+    // per-wave (max m, sum exp) of the logits hf W_lm^T and the target logit;
+    // exp(z - m) is kept (fp16) for the backward
+    GemmArgs a;
     ProfScope ps_(P_CE_FWD, s);
-    a.M = N; a.N = D.V; a.K = d;
-    a.A = hf; a.lda = d; a.B = W + P.lm_head; a.ldb = d;
-    a.row_i = ids; a.row_T = D.T; a.col_offset = 0;
-    a.part = at<float>(ws, w.part); a.nparts = ce_nparts(D); a.zt = at<float>(ws, w.zt);
+    a.M = N; a.N = std::min(vocab_chunk(D), D.V - c0); a.K = d;
+    a.A = hf; a.lda = d; a.B = W + P.lm_head + (size_t)c0 * d; a.ldb = d;
+    a.C = at<uint16_t>(ws, w.ez) + (size_t)c0 * N; a.ldc = chunk_ld(D);  // chunk c0 / vocab_chunk
+    a.row_i = ids; a.row_T = D.T; a.col_offset = c0;
+    a.part = at<float>(ws, w.part) + (size_t)(c0 / ce_tile(D)) * 4; a.nparts = ce_nparts(D);
+    a.zt = at<float>(ws, w.zt);
+    a.tile = ce_tile(D);
     TRY(gemm_bf16(a, EPI_CE_FWD, s));
   }
   { ProfScope ps_(P_CE_REDUCE, s); TRY(launch_ce_reduce(at<float>(ws, w.part), ce_nparts(D), at<float>(ws, w.zt), at<float>(ws, w.lse),
@@ -885,30 +899,26 @@ extern "C" gpt_status gpt_step_bwd_scaled(const gpt_shape* shape, const gpt_para
     TRY(launch_embed_sort(ids, D.B, D.T, D.V, at<void>(ws, w.emb), s));
   }
 
-  // fused head + cross-entropy backward, one vocabulary chunk at a time
-  const int vc = vocab_chunk(D);
-  for (int c0 = 0; c0 < D.V; c0 += vc) {
-    const int nv = std::min(vc, D.V - c0);
+  // head + cross-entropy backward from the exponentials the forward kept, one
+  // vocabulary chunk at a time: dz = bf16(loss_scale (softmax(z) - onehot(target))),
+  // dh (+)= dz W_lm[chunk], dW_lm[chunk] (+)= dz^T hf
+  const int lz = chunk_ld(D);
+  for (int c0 = 0; c0 < D.V; c0 += vocab_chunk(D)) {
+    const int nv = std::min(vocab_chunk(D), D.V - c0);
     {
-      GemmArgs a;  // dz = (softmax(hf W_lm^T) - onehot(target)) / N, this chunk's columns
       ProfScope ps_(P_CE_DZ, s);
-      a.M = N; a.N = nv; a.K = d;
-      a.A = hf; a.lda = d; a.B = W + P.lm_head + (size_t)c0 * d; a.ldb = d;
-      a.C = dz; a.ldc = vc;
-      a.row_f = at<float>(ws, w.lse); a.row_i = ids; a.row_T = D.T; a.col_offset = c0;
-      a.beta = loss_scale;
-      TRY(gemm_bf16(a, EPI_CE_BWD, s));
+      TRY(launch_ce_dz(at<uint16_t>(ws, w.ez) + (size_t)c0 * N, dz, at<float>(ws, w.part), ce_nparts(D), ce_group(D),
+                       c0, at<float>(ws, w.lse), ids, D.T, N, nv, lz, loss_scale, s));
     }
     {
-      GemmArgs a;  // dh (+)= dz W_lm[chunk]
+      GemmArgs a;
       ProfScope ps_(P_CE_DH, s);
       a.M = N; a.N = d; a.K = nv;
-      a.A = dz; a.lda = vc; a.B = W + P.lm_head + (size_t)c0 * d; a.ldb = d; a.b_kcontig = 0;
+      a.A = dz; a.lda = lz; a.B = W + P.lm_head + (size_t)c0 * d; a.ldb = d; a.b_kcontig = 0;
       a.C = dh; a.ldc = d; a.beta = c0 > 0 ? 1.f : 0.f;
       TRY(gemm_bf16(a, EPI_F32, s));
     }
-    // dW_lm[chunk] (+)= dz^T hf
-    { ProfScope ps_(P_CE_DW, s); TRY(wgrad(dz, vc, hf, d, G + P.lm_head + (size_t)c0 * d, nv, d, N, acc, wpart, s)); }
+    { ProfScope ps_(P_CE_DW, s); TRY(wgrad(dz, lz, hf, d, G + P.lm_head + (size_t)c0 * d, nv, d, N, acc, wpart, s)); }
   }
   { ProfScope ps_(P_FILL, s); TRY(launch_fill_f32(g, (long long)N * d, 0.f, s)); }
   const bool f8 = D.prec == GPT_PREC_FP8;
@@ -1172,18 +1182,18 @@ int muon_impl(float* Wt, uint16_t* W_bf16, const float* Gm, float* M, float* O_o
   const long long per = (long long)rows * cols;
   const int lrow = std::max(rows, cols), sm = std::min(rows, cols);
 
-  const float* src = Gm;
-  if (M) {
-    { ProfScope ps_(P_MUON_ELEMWISE, s); TRY(launch_muon_momentum(M, Gm, per * count, momentum, s)); }
-    src = M;
-  }
+  const float* src = M ? M : Gm;
   float* partial = at<float>(ws, m.partial);
   float* X = at<float>(ws, m.X);
   uint16_t* Xb[2] = {at<uint16_t>(ws, m.Xb0), at<uint16_t>(ws, m.Xb1)};
   float* A = at<float>(ws, m.A);
   uint16_t* Ab = at<uint16_t>(ws, m.Ab);
   uint16_t* Bb = at<uint16_t>(ws, m.Bb);
-  { ProfScope ps_(P_MUON_ELEMWISE, s); TRY(launch_frob_partial(src, partial, count, per, kFrobBlocks, s)); }
+  {  // M <- momentum M + G with the Frobenius partials of the new M, or the partials of G alone
+    ProfScope ps_(P_MUON_ELEMWISE, s);
+    if (M) TRY(launch_momentum_frob(M, Gm, momentum, partial, count, per, kFrobBlocks, s));
+    else TRY(launch_frob_partial(src, partial, count, per, kFrobBlocks, s));
+  }
   { ProfScope ps_(P_MUON_ELEMWISE, s); TRY(launch_ns_init(src, partial, kFrobBlocks, X, Xb[0], count, rows, cols, 1e-7f, s)); }
 
   const long long sX = (long long)lrow * sm, sA = (long long)sm * sm;

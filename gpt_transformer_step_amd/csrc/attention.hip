@@ -251,7 +251,7 @@ template <bool GEN>
 __global__ void __launch_bounds__(256, 2)
 attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
                 long long ld, uint16_t* __restrict__ out, long long ld_out, float* __restrict__ lse, int H, int Hkv,
-                int T, int window_arg) {
+                int T, int window_arg, int lse_log2) {
   __shared__ __attribute__((aligned(16))) char smem[2 * F_STAGE];
   const int window = GEN ? window_arg : -1;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, lr = lane & 31, lh = lane >> 5;
@@ -392,7 +392,8 @@ attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, 
             make_uint2(pack_bf2(o[et][4 * g] * inv, o[et][4 * g + 1] * inv),
                        pack_bf2(o[et][4 * g + 2] * inv, o[et][4 * g + 3] * inv));
       }
-    if (lh == 0) lse[(long long)bh * T + myq] = m * kLn2 + logf(l);
+    // lse_log2: in log2 units (the backward kernels' exponent), else natural
+    if (lh == 0) lse[(long long)bh * T + myq] = lse_log2 ? m + __log2f(l) : m * kLn2 + logf(l);
   }
 }
 
@@ -568,7 +569,7 @@ attn_bwd_kv8_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
               for (int u = 0; u < 2; ++u) {
                 const int e = 8 * s2 + 2 * i + u;
                 const int ql = 8 * (e >> 2) + 4 * lh + (e & 3);
-                const float l2 = slse[ql] * kLog2e;
+                const float l2 = FUSE ? slse[ql] : slse[ql] * kLog2e;  // FUSE: lse stored in log2 units
                 const float dl = sdel[ql];
                 float pe = __builtin_amdgcn_exp2f(sacc[e] * c - l2);
                 if constexpr (MASK) {
@@ -678,7 +679,8 @@ attn_bwd_q_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k
       fd[ks] = *reinterpret_cast<const bf16x8_t*>(&bq);
     }
   }
-  const float lse2 = myq < T ? lse[(long long)bh * T + myq] * kLog2e : INFINITY;
+  // FUSE: lse stored in log2 units by the forward
+  const float lse2 = myq < T ? (FUSE ? lse[(long long)bh * T + myq] : lse[(long long)bh * T + myq] * kLog2e) : INFINITY;
   // delta = rowsum(dO * O) of this lane's query: the lane holds half of the
   // dO row (the fragments above), its partner lane ^ 32 the other half; the
   // dK/dV kernel, launched after this one, reads the stored values
@@ -794,12 +796,13 @@ attn_bwd_q_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k
 }  // namespace
 
 int launch_attn_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, long long ld_qkv, uint16_t* out,
-                    long long ld_out, float* lse, int B, int H, int Hkv, int T, int window, hipStream_t s) {
+                    long long ld_out, float* lse, int B, int H, int Hkv, int T, int window, hipStream_t s,
+                    bool lse_log2) {
   if (B <= 0 || T <= 0) return 0;
   dim3 grid((T + FQ - 1) / FQ, B * H);
   const bool gen = Hkv != H || window >= 0;
   hipLaunchKernelGGL(gen ? attn_fwd_kernel<true> : attn_fwd_kernel<false>, grid, dim3(256), 0, s, q, k, v, ld_qkv, out,
-                     ld_out, lse, H, Hkv, T, window);
+                     ld_out, lse, H, Hkv, T, window, lse_log2 ? 1 : 0);
   GS_LAUNCH_CHECK("attn_fwd");
   return 0;
 }

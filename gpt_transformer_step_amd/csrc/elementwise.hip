@@ -279,6 +279,45 @@ __global__ void __launch_bounds__(256) rmsnorm_bwd_kernel(const float* __restric
   }
 }
 
+// Cross-entropy gradient of one vocabulary chunk (columns c0 .. c0+nv-1) from
+// the exponentials the forward kept, one wave per row: e = exp(z - mx_g) (fp16)
+// with mx_g the row max of each group of cw columns (the .x of that group's
+// (max, sum) partial), so softmax(z)[v] = e[v] exp(mx_g - lse).
+// dz[n, j] = bf16(scale (softmax[c0 + j] - [c0 + j == target(n)])); the target
+// of token n = b T + t is ids[b, t + 1].  Rows are ld elements apart in e and
+// dz (ld % 4 == 0; cw and c0 multiples of 4).
+__global__ void __launch_bounds__(256) ce_dz_kernel(const uint16_t* __restrict__ e, uint16_t* __restrict__ dz,
+                                                    const float2* __restrict__ part, int nparts, int cw, int c0,
+                                                    const float* __restrict__ lse, const int* __restrict__ ids, int T,
+                                                    long long N, int nv, int ld, float scale) {
+  const int lane = threadIdx.x & 63;
+  const long long n = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (n >= N) return;
+  const int b = (int)(n / T), t = (int)(n % T);
+  const int tgt = ids[(long long)b * (T + 1) + t + 1] - c0;  // chunk column of the target (may be outside)
+  const float l = lse[n];
+  const float2* pr = part + n * nparts;
+  const uint16_t* er = e + n * ld;
+  uint16_t* row = dz + n * ld;
+  typedef _Float16 h4_t __attribute__((ext_vector_type(4)));
+  for (int c = lane * 4; c < nv; c += 256) {
+    const float f = __expf(pr[(c0 + c) / cw].x - l);  // the 4 columns share a group
+    if (c + 3 < nv) {
+      const h4_t h = *reinterpret_cast<const h4_t*>(er + c);
+      const float o0 = ((float)h[0] * f - (c == tgt ? 1.f : 0.f)) * scale;
+      const float o1 = ((float)h[1] * f - (c + 1 == tgt ? 1.f : 0.f)) * scale;
+      const float o2 = ((float)h[2] * f - (c + 2 == tgt ? 1.f : 0.f)) * scale;
+      const float o3 = ((float)h[3] * f - (c + 3 == tgt ? 1.f : 0.f)) * scale;
+      *reinterpret_cast<uint2*>(row + c) = make_uint2(pack_bf2(o0, o1), pack_bf2(o2, o3));
+    } else {
+      for (int j = c; j < nv; ++j) {
+        const float ej = (float)*reinterpret_cast<const _Float16*>(er + j);
+        row[j] = f2bf((ej * __expf(pr[(c0 + j) / cw].x - l) - (j == tgt ? 1.f : 0.f)) * scale);
+      }
+    }
+  }
+}
+
 // lse = log-sum-exp over the per-tile (max, sum exp) partials; loss = lse - z[target]
 __global__ void __launch_bounds__(256) ce_reduce_kernel(const float2* __restrict__ part, int nparts, const float* __restrict__ zt,
                                  float* __restrict__ lse, float* __restrict__ row_loss,
@@ -423,19 +462,43 @@ __global__ void __launch_bounds__(256) sym_mirror_f32_kernel(float* __restrict__
 }
 
 // ---------------------------- Muon elementwise ------------------------------
-__global__ void muon_momentum_kernel(float* __restrict__ M, const float* __restrict__ G, long long n, float mu) {
-  long long i = ((long long)blockIdx.x * blockDim.x + threadIdx.x) * 4;
-  const long long stride = (long long)gridDim.x * blockDim.x * 4;
-  for (; i < n; i += stride) {
-    if (i + 3 < n) {
-      float4 m = *reinterpret_cast<const float4*>(M + i);
-      const float4 g = *reinterpret_cast<const float4*>(G + i);
-      m.x = mu * m.x + g.x; m.y = mu * m.y + g.y; m.z = mu * m.z + g.z; m.w = mu * m.w + g.w;
-      *reinterpret_cast<float4*>(M + i) = m;
-    } else {
-      for (int j = 0; i + j < n; ++j) M[i + j] = mu * M[i + j] + G[i + j];
-    }
+// Momentum and the Frobenius partials in one pass: M <- mu M + G over chunk
+// blk of matrix b, partial[b * nblk + blk] = sum of squares of the new M
+// (per a multiple of 4; float4 accesses, two in flight per thread)
+__global__ void __launch_bounds__(256) momentum_frob_kernel(float* __restrict__ M, const float* __restrict__ G,
+                                                            float mu, float* __restrict__ partial, long long per,
+                                                            int nblk) {
+  const int b = blockIdx.y, blk = blockIdx.x;
+  const long long per4 = per / 4;
+  const long long chunk = (per4 + nblk - 1) / nblk;
+  const long long beg = blk * chunk, end = min(per4, beg + chunk);
+  float4* m4 = reinterpret_cast<float4*>(M + (long long)b * per);
+  const float4* g4 = reinterpret_cast<const float4*>(G + (long long)b * per);
+  float s0 = 0.f, s1 = 0.f;
+  long long i = beg + threadIdx.x;
+  for (; i + 256 < end; i += 2 * 256) {
+    float4 a = m4[i], c = m4[i + 256];
+    const float4 ga = g4[i], gc = g4[i + 256];
+    a.x = mu * a.x + ga.x; a.y = mu * a.y + ga.y; a.z = mu * a.z + ga.z; a.w = mu * a.w + ga.w;
+    c.x = mu * c.x + gc.x; c.y = mu * c.y + gc.y; c.z = mu * c.z + gc.z; c.w = mu * c.w + gc.w;
+    m4[i] = a;
+    m4[i + 256] = c;
+    s0 += a.x * a.x + a.y * a.y + a.z * a.z + a.w * a.w;
+    s1 += c.x * c.x + c.y * c.y + c.z * c.z + c.w * c.w;
   }
+  for (; i < end; i += 256) {
+    float4 a = m4[i];
+    const float4 ga = g4[i];
+    a.x = mu * a.x + ga.x; a.y = mu * a.y + ga.y; a.z = mu * a.z + ga.z; a.w = mu * a.w + ga.w;
+    m4[i] = a;
+    s0 += a.x * a.x + a.y * a.y + a.z * a.z + a.w * a.w;
+  }
+  float s = s0 + s1;
+  __shared__ float red[4];
+  s = wave_sum(s);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = s;
+  __syncthreads();
+  if (threadIdx.x == 0) partial[(long long)b * nblk + blk] = red[0] + red[1] + red[2] + red[3];
 }
 
 // partial[b * nblk + blk] = sum of squares of chunk blk of matrix b; per is a
@@ -817,6 +880,15 @@ int launch_rmsnorm_bwd(const float* dh, const uint16_t* h, const float* r, float
   return 0;
 }
 
+int launch_ce_dz(const uint16_t* e, uint16_t* dz, const float* part, int nparts, int cw, int c0, const float* lse,
+                 const int* ids, int T, long long N, int nv, int ld, float scale, hipStream_t s) {
+  if (N <= 0 || nv <= 0) return 0;
+  hipLaunchKernelGGL(ce_dz_kernel, dim3(nblocks(N, 4)), dim3(256), 0, s, e, dz, reinterpret_cast<const float2*>(part),
+                     nparts, cw, c0, lse, ids, T, N, nv, ld, scale);
+  GS_LAUNCH_CHECK("ce_dz");
+  return 0;
+}
+
 int launch_ce_reduce(const float* part, int nparts, const float* zt, float* lse, float* row_loss,
                      float* lse_out, long long N, hipStream_t s) {
   hipLaunchKernelGGL(ce_reduce_kernel, dim3(nblocks(N, 4)), dim3(256), 0, s,
@@ -857,10 +929,10 @@ int launch_sym_mirror(void* C, int is_f32, int n, long long ld, long long stride
   return 0;
 }
 
-int launch_muon_momentum(float* M, const float* G, long long n, float mu, hipStream_t s) {
-  const int blocks = (int)std::min<long long>(nblocks(n, 1024), 16384);
-  hipLaunchKernelGGL(muon_momentum_kernel, dim3(blocks), dim3(256), 0, s, M, G, n, mu);
-  GS_LAUNCH_CHECK("muon_momentum");
+int launch_momentum_frob(float* M, const float* G, float mu, float* partial, int count, long long per, int nblk,
+                         hipStream_t s) {
+  hipLaunchKernelGGL(momentum_frob_kernel, dim3(nblk, count), dim3(256), 0, s, M, G, mu, partial, per, nblk);
+  GS_LAUNCH_CHECK("momentum_frob");
   return 0;
 }
 

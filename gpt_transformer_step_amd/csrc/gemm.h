@@ -16,8 +16,9 @@ enum Epi {
   EPI_F32_BF16,    // C f32 = v, C2 bf16 = v
   EPI_NS_POLY,     // C bf16 = beta * aux_f32 + v         (B = b A + c A A, alpha = c, beta = b)
   EPI_NS_UPD,      // x = beta * C_f32 + v; C f32 = x; C2 bf16 = x  (X = a X + X B)
-  EPI_CE_FWD,      // per-row partial (max, sum exp) over the tile's columns + target logit
-  EPI_CE_BWD,      // C bf16 = alpha * (exp(raw - lse[m]) - [col == tgt[m]])
+  EPI_CE_FWD,      // per-row partial (max mx, sum exp) over each wave's columns + target logit;
+                   // with C given, also C fp16 = exp(v - mx), kept for the backward
+  EPI_F16,         // C fp16 = v (the stored exponentials of EPI_CE_FWD; not launched alone)
   EPI_QKV,         // [q | k | v] projection: rotate + RMS-normalise each 128-wide q/k head,
                    // C bf16; per (row, head) 1/rms to rq / rk (part, zt); needs 256-wide tiles
   EPI_COUNT
@@ -50,6 +51,8 @@ struct GemmArgs {
   const float* scale_b = nullptr;
   int sym = 0;                     // M == N, symmetric product: only tiles with tile_m <= tile_n are
                                    // computed; the caller fills the rest (launch_sym_mirror)
+  int tile = 0;                    // 0: tile chosen from the sizes; 128 or 256 forces that tile
+                                   // (launches that must agree on their column groups)
   float* amax = nullptr;           // bf16 epilogues: per-wave max |stored value| at
                                    // amax[block * waves + wave] (block = x + gridDim.x * y)
 };

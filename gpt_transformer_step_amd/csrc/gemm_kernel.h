@@ -223,6 +223,12 @@ template <int EPI>
 __device__ __forceinline__ void epi4(const GemmArgs& p, int bi, int m, int n, const float* v, long long coff,
                                      float& amx, bool have_c = false, float4 cpre = make_float4(0.f, 0.f, 0.f, 0.f)) {
   const bool full = (n + 3 < p.N);
+  if constexpr (EPI == EPI_F16) {
+    _Float16* H = reinterpret_cast<_Float16*>(p.C) + (long long)bi * p.sC + (long long)m * p.ldc + n;
+    for (int j = 0; j < 4; ++j)
+      if (n + j < p.N) H[j] = (_Float16)v[j];
+    return;
+  }
   if constexpr (EPI == EPI_F32 || EPI == EPI_RESID) {
     float* C = reinterpret_cast<float*>(p.C) + (long long)bi * p.sC + coff + (long long)m * p.ldc + n;
     if (full) {
@@ -298,23 +304,6 @@ __device__ __forceinline__ void epi4(const GemmArgs& p, int bi, int m, int n, co
           if (EPI != EPI_NS_UPD || p.C2) C2[j] = f2bf(x);
         }
     }
-  } else if constexpr (EPI == EPI_CE_BWD) {
-    uint16_t* C = reinterpret_cast<uint16_t*>(p.C) + (long long)m * p.ldc + n;
-    const int row_b = m / p.row_T, row_t = m - row_b * p.row_T;
-    const int tgt = p.row_i[(long long)row_b * (p.row_T + 1) + row_t + 1] - p.col_offset;
-    const float lse = p.row_f[m];
-    float o[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      // v already carries alpha = 1; the 1/(B*T) factor is in beta
-      o[j] = (__expf(v[j] - lse) - ((n + j) == tgt ? 1.f : 0.f)) * p.beta;
-    }
-    if (full) {
-      *reinterpret_cast<uint2*>(C) = make_uint2(pack_bf2(o[0], o[1]), pack_bf2(o[2], o[3]));
-    } else {
-      for (int j = 0; j < 4; ++j)
-        if (n + j < p.N) C[j] = f2bf(o[j]);
-    }
   }
 }
 
@@ -324,8 +313,22 @@ __device__ __forceinline__ void epi4(const GemmArgs& p, int bi, int m, int n, co
 template <int EPI>
 __device__ __forceinline__ void epi8(const GemmArgs& p, int bi, int m, int n, const float* v, float& amx,
                                      uint4 aux_w) {
-  static_assert(EPI == EPI_BF16 || EPI == EPI_RELU2 || EPI == EPI_DRELU2, "bf16 store epilogues");
+  static_assert(EPI == EPI_BF16 || EPI == EPI_RELU2 || EPI == EPI_DRELU2 || EPI == EPI_F16, "16-bit store epilogues");
   const bool full = (n + 7 < p.N);
+  if constexpr (EPI == EPI_F16) {
+    _Float16* H = reinterpret_cast<_Float16*>(p.C) + (long long)bi * p.sC + (long long)m * p.ldc + n;
+    if (full) {
+      typedef _Float16 h8_t __attribute__((ext_vector_type(8)));
+      h8_t h;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) h[j] = (_Float16)v[j];
+      *reinterpret_cast<h8_t*>(H) = h;
+    } else {
+      for (int j = 0; j < 8; ++j)
+        if (n + j < p.N) H[j] = (_Float16)v[j];
+    }
+    return;
+  }
   uint16_t* C = reinterpret_cast<uint16_t*>(p.C) + (long long)bi * p.sC + (long long)m * p.ldc + n;
   float o[8];
 #pragma unroll
@@ -844,21 +847,29 @@ __global__ void __launch_bounds__((Cfg<BM, BN>::NT), 1) gemm_kernel(GemmArgs p) 
         }
       mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
       float s = 0.f;
+      const bool keep = p.C != nullptr;  // launch-uniform: the exponentials are stored
 #pragma unroll
       for (int j = 0; j < TN; ++j)
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
           const int n = n0 + wn * WN + j * 32 + 8 * (e >> 2) + 4 * lh + (e & 3);
-          if (n < p.N) s += __expf(acc[i][j][e] * p.alpha - mx);
+          const float pe = n < p.N ? __expf(acc[i][j][e] * p.alpha - mx) : 0.f;
+          s += pe;
+          if (keep) acc[i][j][e] = pe;
         }
       s += __shfl_xor(s, 32, 64);
       if (lh == 0 && m < p.M && n0 + wn * WN < p.N) {
         reinterpret_cast<float2*>(p.part)[(long long)m * p.nparts + tile_n * 2 + wn] = make_float2(mx, s);
       }
     }
-  } else {
+  }
+  // The staged store (for the cross-entropy forward: the exponentials exp(z - mx) as
+  // fp16, when C is given; acc holds them already, so the scale is 1)
+  constexpr int SE = EPI == EPI_CE_FWD ? (int)EPI_F16 : EPI;
+  const float alpha_st = EPI == EPI_CE_FWD ? 1.f : p.alpha;
+  if (EPI != EPI_CE_FWD || p.C != nullptr) {  // launch-uniform
     // split-K partials: split s writes its own slice of C (reduced afterwards)
-    const long long coff = (EPI == EPI_F32 && p.k_split > 1) ? (long long)split * p.split_stride : 0;
+    const long long coff = (SE == EPI_F32 && p.k_split > 1) ? (long long)split * p.split_stride : 0;
     // Coalesced epilogue: each wave stages its accumulators, 32 rows at a
     // time, in its own LDS region (16-byte chunks XOR-swizzled by row, so
     // both the row-per-lane writes and the row-contiguous reads are
@@ -875,15 +886,15 @@ __global__ void __launch_bounds__((Cfg<BM, BN>::NT), 1) gemm_kernel(GemmArgs p) 
     constexpr int NIT = 32 * CH / 64;
     // bf16 stores go out 8 columns (16 bytes) per lane when rows are 16-byte
     // aligned: half the store instructions of the 4-column path
-    constexpr bool W8E = EPI == EPI_BF16 || EPI == EPI_RELU2 || EPI == EPI_DRELU2 || EPI == EPI_QKV;
+    constexpr bool W8E = SE == EPI_BF16 || SE == EPI_RELU2 || SE == EPI_DRELU2 || SE == EPI_QKV || SE == EPI_F16;
     constexpr int CH2 = CH / 2, NIT8 = 32 * CH2 / 64;
-    const bool w8 = W8E && (p.ldc % 8 == 0) && (EPI != EPI_DRELU2 || p.ldaux % 8 == 0);
+    const bool w8 = W8E && (p.ldc % 8 == 0) && (SE != EPI_DRELU2 || p.ldaux % 8 == 0);
     // (the ReLU^2-derivative epilogue always takes the 8-column path: its
     // launches keep C and the saved activation 16-byte aligned, and the 4-column
     // path reads the activation per element)
     uint4 auxw8[NIT8];
     auto fetch_aux = [&](int i) {
-      if constexpr (EPI == EPI_DRELU2) {
+      if constexpr (SE == EPI_DRELU2) {
         const uint16_t* ab = reinterpret_cast<const uint16_t*>(p.aux) + (long long)bi * p.sAux;
 #pragma unroll
         for (int it = 0; it < NIT8; ++it) {
@@ -901,8 +912,8 @@ __global__ void __launch_bounds__((Cfg<BM, BN>::NT), 1) gemm_kernel(GemmArgs p) 
     // before staging it: read one at a time between the stores, each load
     // would wait out the stores before it (the compiler cannot tell the
     // addresses apart)
-    constexpr bool READS_C = EPI == EPI_RESID || EPI == EPI_NS_UPD || EPI == EPI_F32 || EPI == EPI_NS_POLY;
-    const bool cread = READS_C && (EPI != EPI_F32 || p.beta != 0.f) && (EPI != EPI_NS_POLY || p.ldaux % 4 == 0);
+    constexpr bool READS_C = SE == EPI_RESID || SE == EPI_NS_UPD || SE == EPI_F32 || SE == EPI_NS_POLY;
+    const bool cread = READS_C && (SE != EPI_F32 || p.beta != 0.f) && (SE != EPI_NS_POLY || p.ldaux % 4 == 0);
     float4 cpre[READS_C ? NIT : 1];
     auto fetch_c = [&](int i) {
       if constexpr (READS_C) {
@@ -913,7 +924,7 @@ __global__ void __launch_bounds__((Cfg<BM, BN>::NT), 1) gemm_kernel(GemmArgs p) 
           const int m = m0 + wm * WM + i * 32 + q / CH;
           const int n = n0 + wn * WN + (q % CH) * 4;
           float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
-          if constexpr (EPI == EPI_NS_POLY) {
+          if constexpr (SE == EPI_NS_POLY) {
             const float* a = reinterpret_cast<const float*>(p.aux) + (long long)bi * p.sAux;
             if (m < p.M && n + 3 < p.N) x = *reinterpret_cast<const float4*>(a + (long long)m * p.ldaux + n);
           } else {
@@ -941,8 +952,8 @@ __global__ void __launch_bounds__((Cfg<BM, BN>::NT), 1) gemm_kernel(GemmArgs p) 
         for (int g = 0; g < 4; ++g) {
           const int cc = (j * 32 + 8 * g + 4 * lh) >> 2;
           *reinterpret_cast<float4*>(wbuf + lr * ROWB + ((cc ^ (lr & 15)) << 4)) =
-              make_float4(acc[i][j][4 * g] * p.alpha, acc[i][j][4 * g + 1] * p.alpha,
-                          acc[i][j][4 * g + 2] * p.alpha, acc[i][j][4 * g + 3] * p.alpha);
+              make_float4(acc[i][j][4 * g] * alpha_st, acc[i][j][4 * g + 1] * alpha_st,
+                          acc[i][j][4 * g + 2] * alpha_st, acc[i][j][4 * g + 3] * alpha_st);
         }
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_wave_barrier();
@@ -959,7 +970,7 @@ __global__ void __launch_bounds__((Cfg<BM, BN>::NT), 1) gemm_kernel(GemmArgs p) 
             const int n = n0 + wn * WN + cc * 4;
             if (m < p.M && n < p.N) {
               const float v[8] = {a4.x, a4.y, a4.z, a4.w, b4.x, b4.y, b4.z, b4.w};
-              epi8<(EPI == EPI_QKV ? (int)EPI_BF16 : EPI)>(p, bi, m, n, v, amx, auxw8[it]);
+              epi8<(SE == EPI_QKV ? (int)EPI_BF16 : SE)>(p, bi, m, n, v, amx, auxw8[it]);
             }
           }
         }
@@ -974,9 +985,9 @@ __global__ void __launch_bounds__((Cfg<BM, BN>::NT), 1) gemm_kernel(GemmArgs p) 
           if (m < p.M && n < p.N) {
             const float v[4] = {v4.x, v4.y, v4.z, v4.w};
             if constexpr (READS_C)
-              epi4<EPI>(p, bi, m, n, v, coff, amx, cread && n + 3 < p.N, cpre[it]);
+              epi4<SE>(p, bi, m, n, v, coff, amx, cread && n + 3 < p.N, cpre[it]);
             else
-              epi4<(EPI == EPI_QKV ? (int)EPI_BF16 : EPI)>(p, bi, m, n, v, coff, amx);
+              epi4<(SE == EPI_QKV ? (int)EPI_BF16 : SE)>(p, bi, m, n, v, coff, amx);
           }
         }
       }
@@ -984,7 +995,7 @@ __global__ void __launch_bounds__((Cfg<BM, BN>::NT), 1) gemm_kernel(GemmArgs p) 
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     }
-    if constexpr (EPI == EPI_BF16 || EPI == EPI_RELU2 || EPI == EPI_DRELU2) {
+    if constexpr (SE == EPI_BF16 || SE == EPI_RELU2 || SE == EPI_DRELU2) {
       if (p.amax) {  // launch-uniform
         const float wm_ = wave_max(amx);
         if (lane == 0)
@@ -1007,6 +1018,7 @@ int launch_t(const GemmArgs& a, hipStream_t s) {
 // 256x256 tiles (one workgroup per CU) once a launch has about two waves of
 // them (500: a 100-tile product split 5 ways qualifies); 128x128 below
 inline bool use_big_tile(const GemmArgs& a) {
+  if (a.tile) return a.tile == 256;
   const long long big = (long long)((a.M + 255) / 256) * ((a.N + 255) / 256) * a.batch * a.k_split;
   return a.M >= 256 && a.N >= 256 && big >= 500;
 }

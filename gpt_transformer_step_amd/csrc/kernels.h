@@ -26,6 +26,12 @@ int launch_rmsnorm_fwd(const float* x, uint16_t* h, float* r, long long N, int d
                        float* amax_part = nullptr);
 int launch_rmsnorm_bwd(const float* dh, const uint16_t* h, const float* r, float* g, uint16_t* g_bf,
                        long long N, int d, hipStream_t s, float* amax_part = nullptr);
+// dz [N, ld] bf16 = scale (softmax - onehot(target)) on the nv vocabulary
+// columns c0 .. c0+nv-1, from the fp16 exponentials e [N, ld] = exp(z - mx)
+// the cross-entropy forward kept, mx from its (max, sum) partials [N, nparts]
+// of cw columns each
+int launch_ce_dz(const uint16_t* e, uint16_t* dz, const float* part, int nparts, int cw, int c0, const float* lse,
+                 const int* ids, int T, long long N, int nv, int ld, float scale, hipStream_t s);
 int launch_ce_reduce(const float* part, int nparts, const float* zt, float* lse, float* row_loss,
                      float* lse_out, long long N, hipStream_t s);
 int launch_loss_mean(const float* row_loss, float* loss, long long N, hipStream_t s);
@@ -36,7 +42,10 @@ int launch_splitk_reduce(const float* part, int nsplit, long long stride, float*
                          float beta, hipStream_t s);
 
 // --- Muon elementwise (elementwise.hip) ------------------------------------
-int launch_muon_momentum(float* M, const float* G, long long n, float mu, hipStream_t s);
+// M <- mu M + G (count matrices of per elements, 16-byte aligned) and the
+// Frobenius partial sums of the new M, as launch_frob_partial writes them
+int launch_momentum_frob(float* M, const float* G, float mu, float* partial, int count, long long per, int nblk,
+                         hipStream_t s);
 int launch_frob_partial(const float* X, float* partial, int count, long long per, int nblk,
                         hipStream_t s);
 // X[b] (oriented [l, s]) = src[b] / (||src[b]|| + eps); transposed when rows < cols
@@ -98,9 +107,11 @@ int launch_axpy_stream(float* g, uint16_t* g_bf, const float* y, const uint16_t*
 // --- attention (attention.hip) ---------------------------------------------
 // H query heads, Hkv key/value heads (query head h reads head h / (H / Hkv));
 // window: left window (query i sees keys i - window .. i), -1 = full causal
+// lse [B, H, T]: natural log-sum-exp of each row's scaled scores, or (lse_log2)
+// in log2 units, the form the fused backward kernels (QkNormBwd given) read
 int launch_attn_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, long long ld_qkv,
                     uint16_t* out, long long ld_out, float* lse, int B, int H, int Hkv, int T, int window,
-                    hipStream_t s);
+                    hipStream_t s, bool lse_log2 = false);
 int launch_attn_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, long long ld_qkv,
                     const uint16_t* out, const uint16_t* dout, long long ld_out, const float* lse,
                     float* delta, float* dq, uint16_t* dk, uint16_t* dv, long long ld_dkv, int B,
@@ -116,8 +127,9 @@ struct QkNormBwd {
   uint16_t* dq;
 };
 // one of the two backward kernels, in this order: 0 = dQ (also writes delta = rowsum(dout * out)),
-// 1 = dK/dV (reads delta).  fuse NULL: raw gradients (dq fp32 [N, 128 H], dk bf16);
-// else the gradients of the raw heads through the QK-norm and rotary backward.
+// 1 = dK/dV (reads delta).  fuse NULL: raw gradients (dq fp32 [N, 128 H], dk bf16), lse in
+// natural units; else the gradients of the raw heads through the QK-norm and rotary
+// backward, lse in log2 units.
 int launch_attn_bwd_part(int part, const uint16_t* q, const uint16_t* k, const uint16_t* v, long long ld_qkv,
                          const uint16_t* out, const uint16_t* dout, long long ld_out, const float* lse, float* delta,
                          float* dq, uint16_t* dk, uint16_t* dv, long long ld_dkv, int B, int H, int Hkv, int T,
