@@ -575,7 +575,12 @@ attn_bwd_kv8_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
                 if constexpr (MASK) {
                   const bool vis =
                       mykey <= q0 + ql && mykey < T && q0 + ql < T && (window < 0 || mykey >= q0 + ql - window);
-                  pe = vis ? pe : 0.f;
+                  // causal only: a bit mask, not a select (as a select the
+                  // compiler turns each element into a branch around the
+                  // exponential; the windowed variant has no registers to spare
+                  // for the straight-line form)
+                  if constexpr (GEN) pe = vis ? pe : 0.f;
+                  else pe = __int_as_float(__float_as_int(pe) & -(int)vis);
                 }
                 pv[u] = pe;
                 dv2[u] = pe * (dpacc[e] - dl);
