@@ -1108,7 +1108,7 @@ namespace {
 constexpr int kFrobBlocks = 64;
 
 struct MuonWS {
-  size_t partial, X, Xb0, Xb1, A, Ab, Bb, gpart, nm_part, nm_scale, total;
+  size_t partial, X, Xb0, Xb1, Ab, Bb, gpart, nm_part, nm_scale, total;
 };
 
 // k-splits of the Gram products X^T X (a few output tiles, long K)
@@ -1129,7 +1129,6 @@ MuonWS muon_layout(int count, int rows, int cols) {
   m.X = take(n * 4);
   m.Xb0 = take(n * 2);
   m.Xb1 = take(n * 2);
-  m.A = take((size_t)count * sm * sm * 4);
   m.Ab = take((size_t)count * sm * sm * 2);
   m.Bb = take((size_t)count * sm * sm * 2);
   const int gs_ = gram_splits(count, rows, cols);
@@ -1186,7 +1185,6 @@ int muon_impl(float* Wt, uint16_t* W_bf16, const float* Gm, float* M, float* O_o
   float* partial = at<float>(ws, m.partial);
   float* X = at<float>(ws, m.X);
   uint16_t* Xb[2] = {at<uint16_t>(ws, m.Xb0), at<uint16_t>(ws, m.Xb1)};
-  float* A = at<float>(ws, m.A);
   uint16_t* Ab = at<uint16_t>(ws, m.Ab);
   uint16_t* Bb = at<uint16_t>(ws, m.Bb);
   {  // M <- momentum M + G with the Frobenius partials of the new M, or the partials of G alone
@@ -1202,21 +1200,21 @@ int muon_impl(float* Wt, uint16_t* W_bf16, const float* Gm, float* M, float* O_o
   int cur = 0;
   // A = X^T X and B = b A + c A A are symmetric: when the batch holds more
   // 128 x 128 tiles than the chip has CUs, both products compute only the
-  // tiles on and above the diagonal, and the bf16 copies the next product
-  // reads in full are mirrored (with fewer tiles all of them run in one wave
-  // anyway, and the mirror would only add time).  The fp32 A is read only by the polynomial's epilogue, at the
-  // positions it writes, which lie inside the Gram's computed tiles when the
-  // polynomial's tiles are no larger than the Gram's (else the fp32 A is
-  // mirrored too).
+  // tiles on and above the diagonal, and their bf16 outputs, which the next
+  // product reads in full, are mirrored (with fewer tiles all of them run in
+  // one wave anyway, and the mirror would only add time).  A is kept in bf16
+  // only, like the iteration's other operands: the polynomial's epilogue
+  // reads the same bf16 A its product reads (the b A term then carries one
+  // bf16 rounding, as B itself does when it is stored).
   const long long t128 = (sm + 127) / 128;
   const int sym = (long long)count * t128 * t128 > 256 ? 1 : 0;
   GemmArgs ga;
   ga.M = sm; ga.N = sm; ga.K = lrow; ga.batch = count; ga.sym = sym;
   ga.lda = sm; ga.sA = sX; ga.a_kcontig = 0;
   ga.ldb = sm; ga.sB = sX; ga.b_kcontig = 0;
-  ga.C = A; ga.ldc = sm; ga.sC = sA; ga.C2 = Ab; ga.ldc2 = sm; ga.sC2 = sA;
+  ga.C = Ab; ga.ldc = sm; ga.sC = sA;
   if (gram_split > 1) {
-    // split-K partials [split][count][sm][sm], then A = sum, Ab = bf16(A)
+    // split-K partials [split][count][sm][sm], then Ab = bf16(sum)
     ga.C = gpart; ga.k_split = gram_split; ga.split_stride = sA * count;
   }
   GemmArgs gp;
@@ -1224,22 +1222,20 @@ int muon_impl(float* Wt, uint16_t* W_bf16, const float* Gm, float* M, float* O_o
   gp.A = Ab; gp.lda = sm; gp.sA = sA;
   gp.B = Ab; gp.ldb = sm; gp.sB = sA; gp.b_kcontig = 0;
   gp.C = Bb; gp.ldc = sm; gp.sC = sA;
-  gp.aux = A; gp.ldaux = sm; gp.sAux = sA;
-  const bool mirror_a32 = sym && gemm_tile_n(gp) > gemm_tile_n(ga);
+  gp.aux = Ab; gp.ldaux = sm; gp.sAux = sA;
   for (int it = 0; it < ns_steps; ++it) {
     const float ca = coeffs[3 * it], cb = coeffs[3 * it + 1], cc = coeffs[3 * it + 2];
     {
       ProfScope ps_(P_NS_GRAM, s);
-      GemmArgs a = ga;  // A = X^T X (fp32 and bf16)
+      GemmArgs a = ga;  // A = X^T X (bf16)
       a.A = Xb[cur]; a.B = Xb[cur];
       if (gram_split <= 1) {
-        TRY(gemm_bf16(a, EPI_F32_BF16, s));
+        TRY(gemm_bf16(a, EPI_BF16, s));
       } else {
         TRY(gemm_bf16(a, EPI_F32, s));
-        TRY(launch_splitk_reduce(gpart, gram_split, sA * count, A, Ab, sA * count, 0.f, s));
+        TRY(launch_splitk_reduce(gpart, gram_split, sA * count, nullptr, Ab, sA * count, 0.f, s));
       }
       if (sym) TRY(launch_sym_mirror(Ab, 0, sm, sm, sA, count, s));
-      if (mirror_a32) TRY(launch_sym_mirror(A, 1, sm, sm, sA, count, s));
     }
     {
       ProfScope ps_(P_NS_POLY, s);

@@ -356,7 +356,8 @@ __global__ void loss_mean_kernel(const float* __restrict__ row_loss, float* __re
   }
 }
 
-// out = beta * out + sum of nsplit partials (stride elements apart); optional bf16 copy
+// out = beta * out + sum of nsplit partials (stride elements apart); optional
+// bf16 copy; out may be null (bf16 copy only, beta 0)
 __global__ void splitk_reduce_kernel(const float* __restrict__ part, int nsplit, long long stride,
                                      float* __restrict__ out, uint16_t* __restrict__ out_bf, long long n, float beta) {
   long long i = ((long long)blockIdx.x * blockDim.x + threadIdx.x) * 4;
@@ -369,13 +370,13 @@ __global__ void splitk_reduce_kernel(const float* __restrict__ part, int nsplit,
         const float4 v = *reinterpret_cast<const float4*>(part + sp * stride + i);
         acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
       }
-      *reinterpret_cast<float4*>(out + i) = acc;
+      if (out) *reinterpret_cast<float4*>(out + i) = acc;
       if (out_bf) *reinterpret_cast<uint2*>(out_bf + i) = make_uint2(pack_bf2(acc.x, acc.y), pack_bf2(acc.z, acc.w));
     } else {
       for (long long j = i; j < n; ++j) {
         float a = beta != 0.f ? beta * out[j] : 0.f;
         for (int sp = 0; sp < nsplit; ++sp) a += part[sp * stride + j];
-        out[j] = a;
+        if (out) out[j] = a;
         if (out_bf) out_bf[j] = f2bf(a);
       }
     }
@@ -906,6 +907,10 @@ int launch_loss_mean(const float* row_loss, float* loss, long long N, hipStream_
 int launch_splitk_reduce(const float* part, int nsplit, long long stride, float* out, uint16_t* out_bf, long long n,
                          float beta, hipStream_t s) {
   if (n <= 0) return 0;
+  if (!out && (beta != 0.f || !out_bf)) {
+    set_error("splitk_reduce: without an fp32 output beta must be 0 and the bf16 output given");
+    return -1;
+  }
   const int blocks = (int)std::min<long long>(nblocks(n, 1024), 8192);
   hipLaunchKernelGGL(splitk_reduce_kernel, dim3(blocks), dim3(256), 0, s, part, nsplit, stride, out, out_bf, n, beta);
   GS_LAUNCH_CHECK("splitk_reduce");

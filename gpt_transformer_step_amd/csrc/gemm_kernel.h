@@ -262,12 +262,8 @@ __device__ __forceinline__ void epi4(const GemmArgs& p, int bi, int m, int n, co
       for (int j = 0; j < 4; ++j) o[j] = (n + j < p.N) ? o[j] * 2.f * sqrtf(bf2f(a[j])) : 0.f;
     }
     if constexpr (EPI == EPI_NS_POLY) {
-      if (have_c) {
-        o[0] += p.beta * cpre.x; o[1] += p.beta * cpre.y; o[2] += p.beta * cpre.z; o[3] += p.beta * cpre.w;
-      } else {
-        const float* a = reinterpret_cast<const float*>(p.aux) + (long long)bi * p.sAux + (long long)m * p.ldaux + n;
-        for (int j = 0; j < 4; ++j) o[j] = (n + j < p.N) ? o[j] + p.beta * a[j] : 0.f;
-      }
+      const uint16_t* a = reinterpret_cast<const uint16_t*>(p.aux) + (long long)bi * p.sAux + (long long)m * p.ldaux + n;
+      for (int j = 0; j < 4; ++j) o[j] = (n + j < p.N) ? o[j] + p.beta * bf2f(a[j]) : 0.f;
     }
     if (full) {
       const uint2 w = make_uint2(pack_bf2(o[0], o[1]), pack_bf2(o[2], o[3]));
@@ -282,7 +278,7 @@ __device__ __forceinline__ void epi4(const GemmArgs& p, int bi, int m, int n, co
           if (p.amax) amx = fmaxf(amx, fabsf(bf2f(b)));
         }
     }
-  } else if constexpr (EPI == EPI_F32_BF16 || EPI == EPI_NS_UPD) {
+  } else if constexpr (EPI == EPI_NS_UPD) {
     float* C = reinterpret_cast<float*>(p.C) + (long long)bi * p.sC + (long long)m * p.ldc + n;
     uint16_t* C2 = reinterpret_cast<uint16_t*>(p.C2) + (long long)bi * p.sC2 + (long long)m * p.ldc2 + n;
     float o[4];
@@ -313,7 +309,8 @@ __device__ __forceinline__ void epi4(const GemmArgs& p, int bi, int m, int n, co
 template <int EPI>
 __device__ __forceinline__ void epi8(const GemmArgs& p, int bi, int m, int n, const float* v, float& amx,
                                      uint4 aux_w) {
-  static_assert(EPI == EPI_BF16 || EPI == EPI_RELU2 || EPI == EPI_DRELU2 || EPI == EPI_F16, "16-bit store epilogues");
+  static_assert(EPI == EPI_BF16 || EPI == EPI_RELU2 || EPI == EPI_DRELU2 || EPI == EPI_NS_POLY || EPI == EPI_F16,
+                "16-bit store epilogues");
   const bool full = (n + 7 < p.N);
   if constexpr (EPI == EPI_F16) {
     _Float16* H = reinterpret_cast<_Float16*>(p.C) + (long long)bi * p.sC + (long long)m * p.ldc + n;
@@ -348,6 +345,19 @@ __device__ __forceinline__ void epi8(const GemmArgs& p, int bi, int m, int n, co
     } else {
       const uint16_t* a = reinterpret_cast<const uint16_t*>(p.aux) + (long long)bi * p.sAux + (long long)m * p.ldaux + n;
       for (int j = 0; j < 8; ++j) o[j] = (n + j < p.N) ? o[j] * 2.f * sqrtf(bf2f(a[j])) : 0.f;
+    }
+  }
+  if constexpr (EPI == EPI_NS_POLY) {
+    if (full) {
+      const uint32_t w[4] = {aux_w.x, aux_w.y, aux_w.z, aux_w.w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        o[2 * j] += p.beta * lo_bf(w[j]);
+        o[2 * j + 1] += p.beta * hi_bf(w[j]);
+      }
+    } else {
+      const uint16_t* a = reinterpret_cast<const uint16_t*>(p.aux) + (long long)bi * p.sAux + (long long)m * p.ldaux + n;
+      for (int j = 0; j < 8; ++j) o[j] = (n + j < p.N) ? o[j] + p.beta * bf2f(a[j]) : 0.f;
     }
   }
   if (full) {
@@ -879,22 +889,24 @@ __global__ void __launch_bounds__((Cfg<BM, BN>::NT), 1) gemm_kernel(GemmArgs p) 
     constexpr int CH = WN / 4;                   // 16-byte chunks per row
     static_assert(32 * ROWB * (Cfg<BM, BN>::NT / 64) <= 2 * STAGE, "epilogue staging exceeds LDS");
     char* wbuf = smem + wave * 32 * ROWB;
-    // DRELU2 reads the saved activation at every output: each 32-row block's
-    // words are fetched in one burst, the first block's before the staging
-    // barrier, so their latency overlaps the staging instead of being paid
-    // every few outputs
+    // DRELU2 reads the saved activation, NS_POLY the bf16 Gram matrix, at
+    // every output: each 32-row block's words are fetched in one burst, the
+    // first block's before the staging barrier, so their latency overlaps the
+    // staging instead of being paid every few outputs
     constexpr int NIT = 32 * CH / 64;
     // bf16 stores go out 8 columns (16 bytes) per lane when rows are 16-byte
     // aligned: half the store instructions of the 4-column path
-    constexpr bool W8E = SE == EPI_BF16 || SE == EPI_RELU2 || SE == EPI_DRELU2 || SE == EPI_QKV || SE == EPI_F16;
+    constexpr bool W8E = SE == EPI_BF16 || SE == EPI_RELU2 || SE == EPI_DRELU2 || SE == EPI_QKV || SE == EPI_F16 ||
+                         SE == EPI_NS_POLY;
+    constexpr bool AUX8 = SE == EPI_DRELU2 || SE == EPI_NS_POLY;  // bf16 aux read per output
     constexpr int CH2 = CH / 2, NIT8 = 32 * CH2 / 64;
-    const bool w8 = W8E && (p.ldc % 8 == 0) && (SE != EPI_DRELU2 || p.ldaux % 8 == 0);
+    const bool w8 = W8E && (p.ldc % 8 == 0) && (!AUX8 || p.ldaux % 8 == 0);
     // (the ReLU^2-derivative epilogue always takes the 8-column path: its
     // launches keep C and the saved activation 16-byte aligned, and the 4-column
     // path reads the activation per element)
     uint4 auxw8[NIT8];
     auto fetch_aux = [&](int i) {
-      if constexpr (SE == EPI_DRELU2) {
+      if constexpr (AUX8) {
         const uint16_t* ab = reinterpret_cast<const uint16_t*>(p.aux) + (long long)bi * p.sAux;
 #pragma unroll
         for (int it = 0; it < NIT8; ++it) {
@@ -906,14 +918,12 @@ __global__ void __launch_bounds__((Cfg<BM, BN>::NT), 1) gemm_kernel(GemmArgs p) 
         }
       }
     };
-    // Epilogues that read memory per output (C for the residual add, the NS
-    // update and fp32 with beta; the fp32 A of the NS polynomial) fetch a row
-    // block's values in one burst
-    // before staging it: read one at a time between the stores, each load
-    // would wait out the stores before it (the compiler cannot tell the
-    // addresses apart)
-    constexpr bool READS_C = SE == EPI_RESID || SE == EPI_NS_UPD || SE == EPI_F32 || SE == EPI_NS_POLY;
-    const bool cread = READS_C && (SE != EPI_F32 || p.beta != 0.f) && (SE != EPI_NS_POLY || p.ldaux % 4 == 0);
+    // Epilogues that read fp32 C per output (the residual add, the NS update
+    // and fp32 with beta) fetch a row block's values in one burst before
+    // staging it: read one at a time between the stores, each load would wait
+    // out the stores before it (the compiler cannot tell the addresses apart)
+    constexpr bool READS_C = SE == EPI_RESID || SE == EPI_NS_UPD || SE == EPI_F32;
+    const bool cread = READS_C && (SE != EPI_F32 || p.beta != 0.f);
     float4 cpre[READS_C ? NIT : 1];
     auto fetch_c = [&](int i) {
       if constexpr (READS_C) {
@@ -924,13 +934,8 @@ __global__ void __launch_bounds__((Cfg<BM, BN>::NT), 1) gemm_kernel(GemmArgs p) 
           const int m = m0 + wm * WM + i * 32 + q / CH;
           const int n = n0 + wn * WN + (q % CH) * 4;
           float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
-          if constexpr (SE == EPI_NS_POLY) {
-            const float* a = reinterpret_cast<const float*>(p.aux) + (long long)bi * p.sAux;
-            if (m < p.M && n + 3 < p.N) x = *reinterpret_cast<const float4*>(a + (long long)m * p.ldaux + n);
-          } else {
-            const float* Cb = reinterpret_cast<const float*>(p.C) + (long long)bi * p.sC + coff;
-            if (m < p.M && n + 3 < p.N) x = *reinterpret_cast<const float4*>(Cb + (long long)m * p.ldc + n);
-          }
+          const float* Cb = reinterpret_cast<const float*>(p.C) + (long long)bi * p.sC + coff;
+          if (m < p.M && n + 3 < p.N) x = *reinterpret_cast<const float4*>(Cb + (long long)m * p.ldc + n);
           cpre[it] = x;
         }
       }
