@@ -874,7 +874,8 @@ extern "C" gpt_status gpt_step_bwd_scaled(const gpt_shape* shape, const gpt_para
   uint16_t* hf = at<uint16_t>(ws, w.hf);
   float* g = at<float>(ws, w.g);
   uint16_t* g_bf = at<uint16_t>(ws, w.g_bf);
-  float* dh = at<float>(ws, w.dh);
+  float* dh = at<float>(ws, w.dh);                    // the head's data gradient (fp32, summed over vocabulary chunks)
+  uint16_t* dh16 = reinterpret_cast<uint16_t*>(dh);  // the blocks' (bf16 product outputs), same memory
   uint16_t* du = at<uint16_t>(ws, w.du);
   uint16_t* dout = at<uint16_t>(ws, w.dout);
   uint16_t* dqkv = at<uint16_t>(ws, w.dqkv);
@@ -923,7 +924,7 @@ extern "C" gpt_status gpt_step_bwd_scaled(const gpt_shape* shape, const gpt_para
   { ProfScope ps_(P_FILL, s); TRY(launch_fill_f32(g, (long long)N * d, 0.f, s)); }
   const bool f8 = D.prec == GPT_PREC_FP8;
   float* qpart = f8 ? at<float>(ws, w.qpart) : nullptr;
-  { ProfScope ps_(P_RMSNORM_BWD, s); TRY(launch_rmsnorm_bwd(dh, hf, at<float>(ws, w.rf), g, g_bf, N, d, s, qpart)); }
+  { ProfScope ps_(P_RMSNORM_BWD, s); TRY(launch_rmsnorm_bwd(dh, false, hf, at<float>(ws, w.rf), g, g_bf, N, d, s, qpart)); }
   if (f_back) {  // x_final = x_L - backout x_mid: d backout = -g . x_mid; g is kept for the middle layer
     ProfScope ps_(P_FEATURES, s);
     TRY(launch_backout_bwd(g, at<float>(ws, w.xmid), gfin, Nd, fpart, G + P.backout(D), acc, s));
@@ -984,20 +985,20 @@ extern "C" gpt_status gpt_step_bwd_scaled(const gpt_shape* shape, const gpt_para
     }
     if (f8) TRY(quant_dy(du, hid, sc + SC_DU, du_slots));
     {
-      GemmArgs a;  // dh = du Wfc
+      GemmArgs a;  // dh = du Wfc (bf16)
       ProfScope ps_(P_FC_DGRAD, s);
       a.M = N; a.N = d; a.K = hid;
       a.A = du; a.lda = hid; a.B = W + P.fc(D, l); a.ldb = d; a.b_kcontig = 0;
-      a.C = dh; a.ldc = d;
-      if (f8) TRY(dgrad_fp8(a, EPI_F32, hid, at<uint8_t>(ws, L.wfc8t), sc + SC_DU, sc + SC_WFC));
-      else TRY(gemm_bf16(a, EPI_F32, s));
+      a.C = dh16; a.ldc = d;
+      if (f8) TRY(dgrad_fp8(a, EPI_BF16, hid, at<uint8_t>(ws, L.wfc8t), sc + SC_DU, sc + SC_WFC));
+      else TRY(gemm_bf16(a, EPI_BF16, s));
     }
     {
       ProfScope ps_(P_FC_WGRAD, s);  // dWfc = du^T h2
       if (f8) TRY(wgrad_fp8(dyqt, at<uint8_t>(ws, L.h2t), sc + SC_DU, sc + SC_H2, G + P.fc(D, l), hid, d, N, acc, wpart, s));
       else TRY(wgrad(du, hid, h2, d, G + P.fc(D, l), hid, d, N, acc, wpart, s));
     }
-    { ProfScope ps_(P_RMSNORM_BWD, s); TRY(launch_rmsnorm_bwd(dh, h2, at<float>(ws, L.r2), g, g_bf, N, d, s, qpart)); }
+    { ProfScope ps_(P_RMSNORM_BWD, s); TRY(launch_rmsnorm_bwd(dh16, true, h2, at<float>(ws, L.r2), g, g_bf, N, d, s, qpart)); }
     // ---- attention ----
     if (f8) TRY(quant_dy(g_bf, d, sc + SC_G_ATT, N));
     {
@@ -1035,13 +1036,13 @@ extern "C" gpt_status gpt_step_bwd_scaled(const gpt_shape* shape, const gpt_para
     }
     if (f8) TRY(quant_dy(dqkv, D.dqkv, sc + SC_DQKV, 0));
     {
-      GemmArgs a;  // dh = dqkv [Wq; Wk; Wv]
+      GemmArgs a;  // dh = dqkv [Wq; Wk; Wv] (bf16)
       ProfScope ps_(P_QKV_DGRAD, s);
       a.M = N; a.N = d; a.K = D.dqkv;
       a.A = dqkv; a.lda = D.dqkv; a.B = W + P.qkv(D, l); a.ldb = d; a.b_kcontig = 0;
-      a.C = dh; a.ldc = d;
-      if (f8) TRY(dgrad_fp8(a, EPI_F32, D.dqkv, at<uint8_t>(ws, L.wqkv8t), sc + SC_DQKV, sc + SC_WQKV));
-      else TRY(gemm_bf16(a, EPI_F32, s));
+      a.C = dh16; a.ldc = d;
+      if (f8) TRY(dgrad_fp8(a, EPI_BF16, D.dqkv, at<uint8_t>(ws, L.wqkv8t), sc + SC_DQKV, sc + SC_WQKV));
+      else TRY(gemm_bf16(a, EPI_BF16, s));
     }
     {
       ProfScope ps_(P_QKV_WGRAD, s);  // dWqkv = dqkv^T h1
@@ -1050,10 +1051,10 @@ extern "C" gpt_status gpt_step_bwd_scaled(const gpt_shape* shape, const gpt_para
     }
     if (D.ve_layer(l)) {  // the gate reads h1[:, :32]: dh[:, :32] += dz Wg; dWg = dz^T h1[:, :32]
       ProfScope ps_(P_FEATURES, s);
-      TRY(launch_ve_dh(dzve, W + P.vg(D, l), dh, d, N, D.Hkv, s));
+      TRY(launch_ve_dh(dzve, W + P.vg(D, l), dh16, d, N, D.Hkv, s));
       TRY(launch_ve_gate_grad(dzve, h1, d, N, D.Hkv, fpart, G + P.vg(D, l), acc, s));
     }
-    { ProfScope ps_(P_RMSNORM_BWD, s); TRY(launch_rmsnorm_bwd(dh, h1, at<float>(ws, L.r1), g, g_bf, N, d, s, qpart)); }
+    { ProfScope ps_(P_RMSNORM_BWD, s); TRY(launch_rmsnorm_bwd(dh16, true, h1, at<float>(ws, L.r1), g, g_bf, N, d, s, qpart)); }
     g_amax_ok = true;
     if (f_resid) {  // x' = resid_l x_in + x0lam_l x0
       ProfScope ps_(P_FEATURES, s);

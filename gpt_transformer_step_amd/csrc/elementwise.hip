@@ -233,9 +233,10 @@ __global__ void __launch_bounds__(256) rmsnorm_fwd_kernel(const float* __restric
 }
 
 // g += r * (dh - h * mean(dh * h)); g_bf = bf16(g); one wave per row (MC as
-// in the forward)
-template <int MC>
-__global__ void __launch_bounds__(256) rmsnorm_bwd_kernel(const float* __restrict__ dh, const uint16_t* __restrict__ h,
+// in the forward).  dh is the bf16 output of a data-gradient product (DH16),
+// or an fp32 sum of such products, rounded to bf16 as it is read.
+template <int MC, bool DH16>
+__global__ void __launch_bounds__(256) rmsnorm_bwd_kernel(const void* __restrict__ dhv, const uint16_t* __restrict__ h,
                                    const float* __restrict__ r, float* __restrict__ g,
                                    uint16_t* __restrict__ g_bf, long long N, int d, float* __restrict__ amax_part) {
   const int lane = threadIdx.x & 63;
@@ -248,7 +249,13 @@ __global__ void __launch_bounds__(256) rmsnorm_bwd_kernel(const float* __restric
   for (int i = 0; i < MC; ++i) {
     const int c = i * 64 + lane;
     if (c < nc) {
-      dv[i] = *reinterpret_cast<const float4*>(dh + n * d + c * 4);
+      if constexpr (DH16) {
+        const uint2 q = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(dhv) + n * d + c * 4);
+        dv[i] = make_float4(lo_bf(q.x), hi_bf(q.x), lo_bf(q.y), hi_bf(q.y));
+      } else {
+        const float4 f = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(dhv) + n * d + c * 4);
+        dv[i] = make_float4(bf2f(f2bf(f.x)), bf2f(f2bf(f.y)), bf2f(f2bf(f.z)), bf2f(f2bf(f.w)));
+      }
       const uint2 w = *reinterpret_cast<const uint2*>(h + n * d + c * 4);
       hv[i] = make_float4(lo_bf(w.x), hi_bf(w.x), lo_bf(w.y), hi_bf(w.y));
       dot += dv[i].x * hv[i].x + dv[i].y * hv[i].y + dv[i].z * hv[i].z + dv[i].w * hv[i].w;
@@ -871,10 +878,16 @@ int launch_rmsnorm_fwd(const float* x, uint16_t* h, float* r, long long N, int d
   return 0;
 }
 
-int launch_rmsnorm_bwd(const float* dh, const uint16_t* h, const float* r, float* g, uint16_t* g_bf,
+int launch_rmsnorm_bwd(const void* dh, bool dh_bf16, const uint16_t* h, const float* r, float* g, uint16_t* g_bf,
                        long long N, int d, hipStream_t s, float* amax_part) {
   const int mc = (d / 4 + 63) / 64;
-#define GS_RB(M) hipLaunchKernelGGL((rmsnorm_bwd_kernel<M>), dim3(nblocks(N, 4)), dim3(256), 0, s, dh, h, r, g, g_bf, N, d, amax_part)
+#define GS_RB(M)                                                                                              \
+  if (dh_bf16)                                                                                                \
+    hipLaunchKernelGGL((rmsnorm_bwd_kernel<M, true>), dim3(nblocks(N, 4)), dim3(256), 0, s, dh, h, r, g, g_bf, N, d, \
+                       amax_part);                                                                           \
+  else                                                                                                        \
+    hipLaunchKernelGGL((rmsnorm_bwd_kernel<M, false>), dim3(nblocks(N, 4)), dim3(256), 0, s, dh, h, r, g, g_bf, N, d, \
+                       amax_part);
   GS_MC_SWITCH(mc, GS_RB)
 #undef GS_RB
   GS_LAUNCH_CHECK("rmsnorm_bwd");

@@ -302,16 +302,17 @@ __global__ void __launch_bounds__(256) ve_gate_grad_kernel(const float* __restri
   }
 }
 
-// dh[n, c] += sum_h dz[n, h] Wg[h][c]  (c < 32)
+// dh[n, c] = bf16(dh[n, c] + bf16(sum_h dz[n, h] Wg[h][c]))  (c < 32): the gate's
+// share of the gradient of h1 joins the q/k/v product's in the same bf16 tensor
 __global__ void __launch_bounds__(256) ve_dh_kernel(const float* __restrict__ dz, const uint16_t* __restrict__ wg,
-                                                    float* __restrict__ dh, int d, long long N, int Hkv) {
+                                                    uint16_t* __restrict__ dh, int d, long long N, int Hkv) {
   const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
   if (i >= N * kVeCh) return;
   const long long n = i / kVeCh;
   const int c = (int)(i % kVeCh);
   float acc = 0.f;
   for (int hh = 0; hh < Hkv; ++hh) acc += dz[n * Hkv + hh] * bfv(wg + hh * kVeCh + c);
-  dh[n * d + c] += acc;
+  dh[n * d + c] = f2bf(bf2f(dh[n * d + c]) + bf2f(f2bf(acc)));
 }
 
 // ---------------------------------------------------------------------------
@@ -480,7 +481,7 @@ int launch_ve_gate_grad(const float* dz, const uint16_t* h1, int d, long long N,
   return reduce_to(part, kFeatBlocks, Hkv * kVeCh, dwg, 1.f, accumulate, s);
 }
 
-int launch_ve_dh(const float* dz, const uint16_t* wg, float* dh, int d, long long N, int Hkv, hipStream_t s) {
+int launch_ve_dh(const float* dz, const uint16_t* wg, uint16_t* dh, int d, long long N, int Hkv, hipStream_t s) {
   hipLaunchKernelGGL(ve_dh_kernel, dim3(nblocks(N * kVeCh, 256)), dim3(256), 0, s, dz, wg, dh, d, N, Hkv);
   GS_LAUNCH_CHECK("ve_dh");
   return 0;

@@ -904,7 +904,7 @@ __global__ void __launch_bounds__((Cfg<BM, BN>::NT), 1) gemm_kernel(GemmArgs p) 
     // (the ReLU^2-derivative epilogue always takes the 8-column path: its
     // launches keep C and the saved activation 16-byte aligned, and the 4-column
     // path reads the activation per element)
-    uint4 auxw8[NIT8];
+    uint4 auxw8[AUX8 ? TM : 1][NIT8];
     auto fetch_aux = [&](int i) {
       if constexpr (AUX8) {
         const uint16_t* ab = reinterpret_cast<const uint16_t*>(p.aux) + (long long)bi * p.sAux;
@@ -913,7 +913,7 @@ __global__ void __launch_bounds__((Cfg<BM, BN>::NT), 1) gemm_kernel(GemmArgs p) 
           const int q = it * 64 + lane;
           const int m = m0 + wm * WM + i * 32 + q / CH2;
           const int n = n0 + wn * WN + (q % CH2) * 8;
-          auxw8[it] = (w8 && m < p.M && n + 7 < p.N) ? *reinterpret_cast<const uint4*>(ab + (long long)m * p.ldaux + n)
+          auxw8[i][it] = (w8 && m < p.M && n + 7 < p.N) ? *reinterpret_cast<const uint4*>(ab + (long long)m * p.ldaux + n)
                                                       : make_uint4(0, 0, 0, 0);
         }
       }
@@ -940,14 +940,17 @@ __global__ void __launch_bounds__((Cfg<BM, BN>::NT), 1) gemm_kernel(GemmArgs p) 
         }
       }
     };
-    fetch_aux(0);
+    // every row block's aux words at once (16 bytes per lane per 8 columns):
+    // fetched between the stores of an earlier block, a load waits for those
+    // stores to complete
+#pragma unroll
+    for (int i = 0; i < TM; ++i) fetch_aux(i);
     fetch_c(0);
     __syncthreads();  // every wave is done with the operand tiles
     float amx = 0.f;  // max |stored value| of this lane (bf16 epilogues with p.amax)
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
       if (i > 0) {
-        fetch_aux(i);
         fetch_c(i);
       }
       qkv_rows(i);
@@ -975,7 +978,7 @@ __global__ void __launch_bounds__((Cfg<BM, BN>::NT), 1) gemm_kernel(GemmArgs p) 
             const int n = n0 + wn * WN + cc * 4;
             if (m < p.M && n < p.N) {
               const float v[8] = {a4.x, a4.y, a4.z, a4.w, b4.x, b4.y, b4.z, b4.w};
-              epi8<(SE == EPI_QKV ? (int)EPI_BF16 : SE)>(p, bi, m, n, v, amx, auxw8[it]);
+              epi8<(SE == EPI_QKV ? (int)EPI_BF16 : SE)>(p, bi, m, n, v, amx, auxw8[AUX8 ? i : 0][it]);
             }
           }
         }

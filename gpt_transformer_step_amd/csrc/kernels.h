@@ -24,7 +24,8 @@ int launch_embed_gather(const float* g, float* dst, long long N, int d, int V, b
 // amax_part (nullable): per-row max |stored bf16 value| at amax_part[row]
 int launch_rmsnorm_fwd(const float* x, uint16_t* h, float* r, long long N, int d, hipStream_t s,
                        float* amax_part = nullptr);
-int launch_rmsnorm_bwd(const float* dh, const uint16_t* h, const float* r, float* g, uint16_t* g_bf,
+// dh: bf16 (dh_bf16) or fp32, rounded to bf16 as it is read
+int launch_rmsnorm_bwd(const void* dh, bool dh_bf16, const uint16_t* h, const float* r, float* g, uint16_t* g_bf,
                        long long N, int d, hipStream_t s, float* amax_part = nullptr);
 // dz [N, ld] bf16 = scale (softmax - onehot(target)) on the nv vocabulary
 // columns c0 .. c0+nv-1, from the fp16 exponentials e [N, ld] = exp(z - mx)
@@ -91,8 +92,8 @@ int launch_ve_bwd(const int* ids, const uint16_t* dv, long long lddv, const uint
 // dwg (+)= dz^T h1[:, :32]
 int launch_ve_gate_grad(const float* dz, const uint16_t* h1, int d, long long N, int Hkv, float* part, float* dwg,
                         bool accumulate, hipStream_t s);
-// dh[:, :32] += dz wg
-int launch_ve_dh(const float* dz, const uint16_t* wg, float* dh, int d, long long N, int Hkv, hipStream_t s);
+// dh[:, :32] = bf16(dh[:, :32] + bf16(dz wg)), dh bf16
+int launch_ve_dh(const float* dz, const uint16_t* wg, uint16_t* dh, int d, long long N, int Hkv, hipStream_t s);
 // backward of x' = a x_in + b x0: da, db (+)= g.x_in, g.x0; g0 (first: =) += b g; g = a g; g_bf
 int launch_resid_bwd(float* g, uint16_t* g_bf, const uint16_t* xin, const float* x0, float* g0, bool g0_first,
                      const uint16_t* pa, const uint16_t* pb, long long n, float* part, float* da, float* db,

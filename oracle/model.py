@@ -389,7 +389,7 @@ def _forward_backward_chunk(P, ids, cfg, loss_scale, dtype, want_grads, want_log
     dz = op(cross_entropy_bwd(z, tgt, lse, loss_scale))
     del z
     Gr["lm_head"] = dz.T @ hfo
-    g = rms_norm_bwd(dz @ P["lm_head"], hfo, rf)
+    g = rms_norm_bwd(op(dz @ P["lm_head"]), hfo, rf)
     del dz
     # the scalar gradients are sums over every stream element whose terms cancel
     # to a small fraction of their magnitudes; Gabs holds the sum of the
@@ -415,7 +415,7 @@ def _forward_backward_chunk(P, ids, cfg, loss_scale, dtype, want_grads, want_log
         # d relu(u)^2 / du = 2 relu(u) = 2 sqrt(a), read from the stored activation
         du = op(da * 2.0 * np.sqrt(a))
         dh2, Gr[f"wfc.{i}"] = _lin_bwd(h2o, P[f"wfc.{i}"], du, fp8)
-        g = g + rms_norm_bwd(dh2, h2o, r2)
+        g = g + rms_norm_bwd(op(dh2), h2o, r2)
         # attention
         gb = op(g)
         dy2, Gr[f"wo.{i}"] = _lin_bwd(y2, P[f"wo.{i}"], gb, fp8)
@@ -430,6 +430,7 @@ def _forward_backward_chunk(P, ids, cfg, loss_scale, dtype, want_grads, want_log
         dk = rope_bwd(rms_norm_bwd(dkn, ks, rk), cos, sin)
         dqkv = op(np.concatenate([t.transpose(0, 2, 1, 3).reshape(R, -1) for t in (dq, dk, dv)], axis=1))
         dh1, dwqkv = _lin_bwd(h1o, wqkv, dqkv, fp8)
+        dh1 = op(dh1)
         Gr[f"wq.{i}"], Gr[f"wk.{i}"], Gr[f"wv.{i}"] = dwqkv[:d], dwqkv[d:d + dkv], dwqkv[d + dkv:]
         if ve is not None:
             dv3 = dqkv[:, d + dkv:].reshape(R, Hkv, hd)       # gradient of v after the value embedding
@@ -439,8 +440,9 @@ def _forward_backward_chunk(P, ids, cfg, loss_scale, dtype, want_grads, want_log
             # gate = 3 sigmoid(z): dgate/dz = gate (1 - gate / 3)
             dzg = np.sum(dv3 * ve, axis=-1) * v_gate * (1.0 - v_gate / 3.0)   # [R, Hkv]
             Gr[f"ve_gate.{i}"] = dzg.T @ h1o[:, :VE_GATE_CH]
+            # the gate's share of dh1 joins the products' in the same bf16 tensor
             dh1 = dh1.copy()
-            dh1[:, :VE_GATE_CH] += dzg @ P[f"ve_gate.{i}"]
+            dh1[:, :VE_GATE_CH] = op(dh1[:, :VE_GATE_CH] + op(dzg @ P[f"ve_gate.{i}"]))
         g = g + rms_norm_bwd(dh1, h1o, r1)
         if cfg.resid_lambdas:
             # x = resid_lambda x_in + x0_lambda x0
@@ -505,7 +507,10 @@ def forward_backward(P, ids, cfg, dtype=np.float64, want_grads=True, want_logits
     output a.  In the backward: dlogits; the residual gradient entering the
     output projections' products; the MLP hidden gradient du; the attention
     output gradient dO; P and dS as operands of dV = P^T dO, dQ = dS K and
-    dK = dS^T Q; the q/k/v gradient.  The ReLU^2 derivative 2 relu(u) is read
+    dK = dS^T Q; the q/k/v gradient; the data gradient entering each RMS-norm
+    backward (the head's, the fc product's, the q/k/v product's -- with value
+    embeddings the gate's share is rounded and added to the latter in bf16).
+    The ReLU^2 derivative 2 relu(u) is read
     from the stored activation as 2 sqrt(a), and each RMS-norm backward reads
     its stored (rounded) output.  Products accumulate in `dtype`; norm
     statistics, rotary, softmax and the residual stream stay in `dtype`.

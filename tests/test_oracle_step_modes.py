@@ -163,12 +163,12 @@ def test_bf16_mode_rounds_exactly_the_documented_tensors(monkeypatch):
     for i in range(cfg.n_layer):
         want += [("h1", val(f"h1.{i}")), ("v", val(f"v.{i}")), ("q", val(f"q.{i}")), ("k", val(f"k.{i}")),
                  ("P", val(f"p.{i}")), ("y", val(f"y.{i}")), ("h2", val(f"h2.{i}")), ("a", val(f"a.{i}"))]
-    want += [("hf", val("hf")), ("dz", grad("z"))]
+    want += [("hf", val("hf")), ("dz", grad("z")), ("dhf", grad("hf"))]
     for i in reversed(range(cfg.n_layer)):
         dqkv = grad(f"qkv.{i}")
-        want += [("g mlp", grad(f"xm.{i}")), ("du", grad(f"u.{i}")), ("g attn", grad(f"xa.{i}")),
-                 ("dO", grad(f"y.{i}")), ("P bwd", val(f"p.{i}")), ("dS", grad(f"s.{i}").nan_to_num(0.0)),
-                 ("dqkv", dqkv)]
+        want += [("g mlp", grad(f"xm.{i}")), ("du", grad(f"u.{i}")), ("dh2", grad(f"h2.{i}")),
+                 ("g attn", grad(f"xa.{i}")), ("dO", grad(f"y.{i}")), ("P bwd", val(f"p.{i}")),
+                 ("dS", grad(f"s.{i}").nan_to_num(0.0)), ("dqkv", dqkv), ("dh1", grad(f"h1.{i}"))]
     assert len(seen) == len(want), [w[0] for w in want]
     for j, ((name, ref), got) in enumerate(zip(want, seen)):
         ref = ref.numpy()
