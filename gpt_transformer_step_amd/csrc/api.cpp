@@ -1193,7 +1193,7 @@ int muon_impl(float* Wt, uint16_t* W_bf16, const float* Gm, float* M, float* O_o
     if (M) TRY(launch_momentum_frob(M, Gm, momentum, partial, count, per, kFrobBlocks, s));
     else TRY(launch_frob_partial(src, partial, count, per, kFrobBlocks, s));
   }
-  { ProfScope ps_(P_MUON_ELEMWISE, s); TRY(launch_ns_init(src, partial, kFrobBlocks, X, Xb[0], count, rows, cols, 1e-7f, s)); }
+  { ProfScope ps_(P_MUON_ELEMWISE, s); TRY(launch_ns_init(src, partial, kFrobBlocks, nullptr, Xb[0], count, rows, cols, 1e-7f, s)); }
 
   const long long sX = (long long)lrow * sm, sA = (long long)sm * sm;
   const int gram_split = gram_splits(count, rows, cols);
@@ -1246,15 +1246,18 @@ int muon_impl(float* Wt, uint16_t* W_bf16, const float* Gm, float* M, float* O_o
       if (sym) TRY(launch_sym_mirror(Bb, 0, sm, sm, sA, count, s));
     }
     {
-      GemmArgs a;  // X = a X + X B
+      // X = a X + X B, X kept in bf16 (as the iteration's products read it);
+      // the last one in fp32 for the apply
+      GemmArgs a;
       ProfScope ps_(P_NS_UPDATE, s);
       a.M = lrow; a.N = sm; a.K = sm; a.batch = count;
       a.A = Xb[cur]; a.lda = sm; a.sA = sX;
       a.B = Bb; a.ldb = sm; a.sB = sA; a.b_kcontig = 0;
-      a.C = X; a.ldc = sm; a.sC = sX; a.ldc2 = sm; a.sC2 = sX;
-      a.C2 = it + 1 < ns_steps ? Xb[cur ^ 1] : nullptr;  // the last X is read in fp32 only
+      a.aux = Xb[cur]; a.ldaux = sm; a.sAux = sX;
       a.beta = ca;
-      TRY(gemm_bf16(a, EPI_NS_UPD, s));
+      const bool last = it + 1 == ns_steps;
+      a.C = last ? static_cast<void*>(X) : static_cast<void*>(Xb[cur ^ 1]); a.ldc = sm; a.sC = sX;
+      TRY(gemm_bf16(a, last ? EPI_NS_UPD : EPI_NS_POLY, s));
     }
     cur ^= 1;
   }

@@ -546,7 +546,8 @@ __device__ __forceinline__ float frob_norm(const float* partial, int b, int nblk
   return (float)sqrt(s);
 }
 
-// 64x64 output tiles, 256 threads; TR: out[i][j] = in[j][i]
+// 64x64 output tiles, 256 threads; TR: out[i][j] = in[j][i]; X (the fp32
+// copy) nullable: the iteration reads only the bf16 one
 template <bool TR>
 __global__ void ns_init_kernel(const float* __restrict__ src, const float* __restrict__ partial, int nblk,
                                float* __restrict__ X, uint16_t* __restrict__ Xb, int rows, int cols,
@@ -573,7 +574,7 @@ __global__ void ns_init_kernel(const float* __restrict__ src, const float* __res
       const int gi = i0 + ii, gj = j0 + jj;
       if (gi < lr && gj < ls) {
         const float v = tile[jj][ii] * inv;
-        out[(long long)gi * ls + gj] = v;
+        if (X) out[(long long)gi * ls + gj] = v;
         outb[(long long)gi * ls + gj] = f2bf(v);
       }
     }
@@ -583,7 +584,7 @@ __global__ void ns_init_kernel(const float* __restrict__ src, const float* __res
       const int gi = i0 + ii, gj = j0 + jj;
       if (gi < lr && gj < ls) {
         const float v = in[(long long)gi * ls + gj] * inv;
-        out[(long long)gi * ls + gj] = v;
+        if (X) out[(long long)gi * ls + gj] = v;
         outb[(long long)gi * ls + gj] = f2bf(v);
       }
     }

@@ -5,7 +5,7 @@ both neuron axes.
 
 Bars: the rescaled update O' rel L2 <= 1e-2 and cosine >= 0.999 (the Muon
 bar); the second moments V rel L2 <= 1e-2 (they are mean squares of O, so
-twice O's relative error); updated weights within 1e-2 * lr * max|O'| of the
+twice O's relative error); updated weights within W_LINF * lr * max|O'| of the
 oracle's; the bf16 copy equal to the GPU's own fp32 weights rounded."""
 
 import numpy as np
@@ -16,6 +16,15 @@ from gpu_util import cosine, rel_l2, say
 from oracle import muon as om
 
 pytestmark = pytest.mark.gpu
+
+# Elementwise bound on an updated weight, as a fraction of lr * max|O|.  The
+# iterates are bf16 (dev.to "2. Optimizador Muon", NorMuon lines: the
+# orthogonalised update is cast to float for its statistics and the scale is
+# cast back to the update's dtype), so every element of O carries the
+# roundings of its iterates: 2^-9 relative each, times |a| (1.875 for the
+# textbook quintic) in the last update, accumulated over five updates --
+# about 1 % of max|O| at worst (measured 1.1 %), against rel L2 2e-3 .. 4e-3.
+W_LINF = 2e-2
 
 NS5 = [om.NS5_QUINTIC] * 5
 
@@ -61,7 +70,7 @@ def test_normuon_update_parity(B, count, rows, cols, per_row):
             say(f"  step {step} [{i}] O' rel_l2 {e:.3e} cos {c:.6f}  V rel_l2 {ev:.3e}")
             assert e <= 1e-2 and c >= 0.999 and ev <= 1e-2
             assert rel_l2(dM[i].cpu().numpy(), rM[i]) < 1e-6
-            assert np.abs(dW[i].cpu().numpy() - rW[i]).max() <= 1e-2 * lr * np.abs(O).max() + 1e-6
+            assert np.abs(dW[i].cpu().numpy() - rW[i]).max() <= W_LINF * lr * np.abs(O).max() + 1e-6
             assert torch.equal(dWb[i], dW[i].to(torch.bfloat16))
 
 
@@ -126,5 +135,5 @@ def test_normuon_update_bench_groups(B, count, rows, cols):
             ev = rel_l2(dV[i].cpu().numpy(), rV[i])
             say(f"  step {step} [{i}] O' rel_l2 {e:.3e} cos {c:.6f}  V rel_l2 {ev:.3e}")
             assert e <= 1e-2 and c >= 0.999 and ev <= 1e-2
-            assert np.abs(dW[i].cpu().numpy() - rW[i]).max() <= 1e-2 * lr * np.abs(O).max() + 1e-6
+            assert np.abs(dW[i].cpu().numpy() - rW[i]).max() <= W_LINF * lr * np.abs(O).max() + 1e-6
             assert torch.equal(dWb[i], dW[i].to(torch.bfloat16))
