@@ -525,7 +525,9 @@ WS ws_layout(const Dims& D) {
     // one per wave of the [N, 4d] bf16 products
     GemmArgs ga;
     ga.M = (int)D.N; ga.N = D.hidden; ga.K = d;
-    const long long slots = std::max<long long>(std::max<long long>(kFp8Partials, (long long)D.N), gemm_amax_slots(ga));
+    long long slots = std::max<long long>(std::max<long long>(kFp8Partials, (long long)D.N), gemm_amax_slots(ga));
+    slots = std::max(slots, std::max(attn_fwd_amax_slots(D.B, D.H, D.T), attn_bwd_amax_slots(D.B, D.H, D.Hkv, D.T)));
+    slots = std::max(slots, (long long)D.L * kFp8Partials);  // the batched weight quantisation
     w.qpart = take((size_t)slots * 4);
   }
   w.total = o;
@@ -692,20 +694,35 @@ extern "C" gpt_status gpt_step_fwd(const gpt_shape* shape, const gpt_params* par
   float* qpart = f8 ? at<float>(ws, w.qpart) : nullptr;
   uint8_t* xq = f8 ? at<uint8_t>(ws, w.xq) : nullptr;
   if (f8) {
-    // E4M3 codes of every block weight, plain (forward) and transposed (data gradient)
+    // E4M3 codes of every block weight, plain (forward) and transposed (data
+    // gradient), one scale per tensor: one batched launch per weight kind over
+    // all layers (same shape, a fixed stride apart in the packed parameters and
+    // in the per-layer workspace)
     ProfScope ps_(P_FP8_QUANT, s);
-    for (int l = 0; l < D.L; ++l) {
-      const Layer& L = w.layer[l];
-      float* sc = at<float>(ws, w.scales) + (size_t)l * SC_COUNT;
-      TRY(quantize_fp8(W + P.qkv(D, l), 0, d, D.dqkv, d, 0, qpart, sc + SC_WQKV, at<uint8_t>(ws, L.wqkv8), d,
-                       at<uint8_t>(ws, L.wqkv8t), D.dqkv, s));
-      TRY(quantize_fp8(W + P.wo(D, l), 0, d, d, d, 0, qpart, sc + SC_WO, at<uint8_t>(ws, L.wo8), d,
-                       at<uint8_t>(ws, L.wo8t), d, s));
-      TRY(quantize_fp8(W + P.fc(D, l), 0, d, hid, d, 0, qpart, sc + SC_WFC, at<uint8_t>(ws, L.wfc8), d,
-                       at<uint8_t>(ws, L.wfc8t), hid, s));
-      TRY(quantize_fp8(W + P.proj(D, l), 0, hid, d, hid, 0, qpart, sc + SC_WPROJ, at<uint8_t>(ws, L.wproj8), hid,
-                       at<uint8_t>(ws, L.wproj8t), d, s));
-    }
+    float* sc0 = at<float>(ws, w.scales);
+    auto kind = [&](auto poff, size_t Layer::*q8, size_t Layer::*q8t, int rows, int cols, int sc_slot) -> int {
+      const long long sx = (long long)(poff(1) - poff(0));
+      const long long sq = (long long)(w.layer[1].*q8 - w.layer[0].*q8);
+      bool uniform = true;
+      for (int l = 1; l < D.L; ++l)
+        uniform = uniform && (long long)(poff(l) - poff(0)) == l * sx &&
+                  (long long)(w.layer[l].*q8 - w.layer[0].*q8) == l * sq &&
+                  (long long)(w.layer[l].*q8t - w.layer[0].*q8t) == l * sq;
+      // one launch for all layers, or (were the strides not uniform) one per layer
+      const int cnt = uniform ? D.L : 1;
+      for (int l0 = 0; l0 < D.L; l0 += cnt) {
+        const Layer& L = w.layer[l0];
+        float* scl = sc0 + (size_t)l0 * SC_COUNT + sc_slot;
+        TRY(launch_fp8_amax_scale(W + poff(l0), 0, cols, rows, cols, 0, qpart, scl, s, cnt, sx, SC_COUNT));
+        TRY(launch_fp8_quant(W + poff(l0), 0, cols, rows, cols, 0, scl, at<uint8_t>(ws, L.*q8), cols,
+                             at<uint8_t>(ws, L.*q8t), rows, s, cnt, sx, SC_COUNT, sq));
+      }
+      return 0;
+    };
+    TRY(kind([&](int l) { return P.qkv(D, l); }, &Layer::wqkv8, &Layer::wqkv8t, D.dqkv, d, SC_WQKV));
+    TRY(kind([&](int l) { return P.wo(D, l); }, &Layer::wo8, &Layer::wo8t, d, d, SC_WO));
+    TRY(kind([&](int l) { return P.fc(D, l); }, &Layer::wfc8, &Layer::wfc8t, hid, d, SC_WFC));
+    TRY(kind([&](int l) { return P.proj(D, l); }, &Layer::wproj8, &Layer::wproj8t, d, hid, SC_WPROJ));
   }
   // y (op)= X W^T for one block product: bf16 operands, or (fp8) the E4M3 codes
   // of X (quantised here; the transposed codes are kept for the weight
@@ -769,8 +786,13 @@ extern "C" gpt_status gpt_step_fwd(const gpt_shape* shape, const gpt_params* par
       TRY(launch_ve_fwd(ids, h1, d, W + P.vg(D, l), W + P.ve(D, l), qkv + d + D.dkv, D.dqkv, at<float>(ws, L.vgate),
                         D.B, D.T, D.Hkv, D.V, s));
     }
-    { ProfScope ps_(P_ATTN_FWD, s); TRY(launch_attn_fwd(qkv, qkv + d, qkv + d + D.dkv, D.dqkv, att, d, at<float>(ws, L.lse), D.B, D.H, D.Hkv, D.T, D.layer_window(l), s, true)); }
-    TRY(quant_x(att, d, L.attt, sc ? sc + SC_ATT : nullptr, 0));
+    {
+      // fp8: the kernel also leaves the per-wave amax partials of its output
+      ProfScope ps_(P_ATTN_FWD, s);
+      TRY(launch_attn_fwd(qkv, qkv + d, qkv + d + D.dkv, D.dqkv, att, d, at<float>(ws, L.lse), D.B, D.H, D.Hkv, D.T,
+                          D.layer_window(l), s, true, qpart));
+    }
+    TRY(quant_x(att, d, L.attt, sc ? sc + SC_ATT : nullptr, f8 ? attn_fwd_amax_slots(D.B, D.H, D.T) : 0));
     {
       GemmArgs a;  // x += att Wo^T
       ProfScope ps_(P_GEMM_O, s);
@@ -1017,7 +1039,8 @@ extern "C" gpt_status gpt_step_bwd_scaled(const gpt_shape* shape, const gpt_para
     }
     // dQ (and delta), then dK/dV; both leave through the QK-norm + rotary
     // backward into dqkv (bf16): the gradients of the raw q, k heads, and dv
-    const QkNormBwd fuse{at<float>(ws, L.rq), at<float>(ws, L.rk), cs, dqkv};
+    // (fp8: with the per-wave amax partials of dqkv)
+    const QkNormBwd fuse{at<float>(ws, L.rq), at<float>(ws, L.rk), cs, dqkv, qpart};
     for (int part = 0; part < 2; ++part) {
       ProfScope ps_(part == 0 ? P_ATTN_BWD_Q : P_ATTN_BWD_KV, s);
       TRY(launch_attn_bwd_part(part, qkv, qkv + d, qkv + d + D.dkv, D.dqkv, att, dout, d, at<float>(ws, L.lse),
@@ -1034,7 +1057,7 @@ extern "C" gpt_status gpt_step_bwd_scaled(const gpt_shape* shape, const gpt_para
                         D.Hkv, D.V, s));
       TRY(launch_embed_gather(vec, G + P.ve(D, l), (long long)N, D.dkv, D.V, true, at<void>(ws, w.emb), s));
     }
-    if (f8) TRY(quant_dy(dqkv, D.dqkv, sc + SC_DQKV, 0));
+    if (f8) TRY(quant_dy(dqkv, D.dqkv, sc + SC_DQKV, attn_bwd_amax_slots(D.B, D.H, D.Hkv, D.T)));
     {
       GemmArgs a;  // dh = dqkv [Wq; Wk; Wv] (bf16)
       ProfScope ps_(P_QKV_DGRAD, s);

@@ -182,7 +182,21 @@ __device__ __forceinline__ int xcd_block(int gx) {
 // pairs (i, i + 64) at position t (cos table [T][64], then sin [T][64]); the
 // result goes out as bf16.  Features i and i + 64 sit in acc[et] and
 // acc[et + 2] of the same lane, so the rotation needs no exchange.
-__device__ __forceinline__ void qknorm_rope_bwd_store(const f32x16_t* acc, float scale, const uint16_t* yrow, float r,
+// max |value| of the two bf16 values of a stored word pair
+__device__ __forceinline__ float absmax_w(uint2 w) {
+  return fmaxf(fmaxf(fabsf(lo_bf(w.x)), fabsf(hi_bf(w.x))), fmaxf(fabsf(lo_bf(w.y)), fabsf(hi_bf(w.y))));
+}
+
+// One wave's max |stored value| into amax[slot] (fp8 scale partials; no-op
+// without amax).  Every lane of the wave calls it.
+__device__ __forceinline__ void store_wave_amax(float* amax, long long slot, float m) {
+  if (!amax) return;
+  m = wave_max(m);
+  if ((threadIdx.x & 63) == 0) amax[slot] = m;
+}
+
+// Returns the max |stored value| of the lane.
+__device__ __forceinline__ float qknorm_rope_bwd_store(const f32x16_t* acc, float scale, const uint16_t* yrow, float r,
                                                       const float* cs, int T, int t, int lh, uint16_t* out) {
   uint2 yw[4][4];
   float dot = 0.f;
@@ -196,6 +210,7 @@ __device__ __forceinline__ void qknorm_rope_bwd_store(const f32x16_t* acc, float
     }
   dot += __shfl_xor(dot, 32, 64);
   const float mean = dot * scale * (1.f / 128.f);
+  float amx = 0.f;
   const float* cr = cs + t * 64;
   const float* sr = cs + (long long)T * 64 + t * 64;
 #pragma unroll
@@ -217,9 +232,13 @@ __device__ __forceinline__ void qknorm_rope_bwd_store(const f32x16_t* acc, float
         o1[u] = d1 * cc[u] + d2 * ss[u];
         o2[u] = -d1 * ss[u] + d2 * cc[u];
       }
-      *reinterpret_cast<uint2*>(out + i) = make_uint2(pack_bf2(o1[0], o1[1]), pack_bf2(o1[2], o1[3]));
-      *reinterpret_cast<uint2*>(out + i + 64) = make_uint2(pack_bf2(o2[0], o2[1]), pack_bf2(o2[2], o2[3]));
+      const uint2 w1 = make_uint2(pack_bf2(o1[0], o1[1]), pack_bf2(o1[2], o1[3]));
+      const uint2 w2 = make_uint2(pack_bf2(o2[0], o2[1]), pack_bf2(o2[2], o2[3]));
+      *reinterpret_cast<uint2*>(out + i) = w1;
+      *reinterpret_cast<uint2*>(out + i + 64) = w2;
+      amx = fmaxf(amx, fmaxf(absmax_w(w1), absmax_w(w2)));
     }
+  return amx;
 }
 
 // Copy of ROWS rows of 128 features (row r0 + r clamped to T - 1) of a bf16
@@ -251,7 +270,7 @@ template <bool GEN>
 __global__ void __launch_bounds__(256, 2)
 attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
                 long long ld, uint16_t* __restrict__ out, long long ld_out, float* __restrict__ lse, int H, int Hkv,
-                int T, int window_arg, int lse_log2) {
+                int T, int window_arg, int lse_log2, float* __restrict__ amax) {
   __shared__ __attribute__((aligned(16))) char smem[2 * F_STAGE];
   const int window = GEN ? window_arg : -1;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, lr = lane & 31, lh = lane >> 5;
@@ -380,6 +399,7 @@ attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, 
   }
 
   l += __shfl_xor(l, 32, 64);
+  float amx = 0.f;  // max |stored value| of the lane (fp8 scale partials)
   if (myq < T) {
     const float inv = 1.f / l;
     uint16_t* orow = out + (rowbase + myq) * ld_out + h * 128;
@@ -388,13 +408,15 @@ attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, 
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int e = et * 32 + 8 * g + 4 * lh;
-        *reinterpret_cast<uint2*>(orow + e) =
-            make_uint2(pack_bf2(o[et][4 * g] * inv, o[et][4 * g + 1] * inv),
-                       pack_bf2(o[et][4 * g + 2] * inv, o[et][4 * g + 3] * inv));
+        const uint2 w = make_uint2(pack_bf2(o[et][4 * g] * inv, o[et][4 * g + 1] * inv),
+                                   pack_bf2(o[et][4 * g + 2] * inv, o[et][4 * g + 3] * inv));
+        *reinterpret_cast<uint2*>(orow + e) = w;
+        amx = fmaxf(amx, absmax_w(w));
       }
     // lse_log2: in log2 units (the backward kernels' exponent), else natural
     if (lh == 0) lse[(long long)bh * T + myq] = lse_log2 ? m + __log2f(l) : m * kLn2 + logf(l);
   }
+  store_wave_amax(amax, ((long long)blockIdx.x + (long long)gridDim.x * blockIdx.y) * 4 + wave, amx);
 }
 
 // ============================================================================
@@ -446,7 +468,7 @@ attn_bwd_kv8_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
                     long long ld, const uint16_t* __restrict__ dout, long long ld_out, const float* __restrict__ lse,
                     const float* __restrict__ delta, uint16_t* __restrict__ dk, uint16_t* __restrict__ dv,
                     long long ld_dkv, int H, int Hkv, int T, int window_arg, const float* __restrict__ rk,
-                    const float* __restrict__ cs) {
+                    const float* __restrict__ cs, float* __restrict__ amax) {
   static_assert(K8_NS == 4, "one __shared__ array per stage below");
   __shared__ __attribute__((aligned(16))) char s_k[K8_KEYS * 256];
   __shared__ __attribute__((aligned(16))) char s_st0[K8_STAGE];
@@ -613,6 +635,7 @@ attn_bwd_kv8_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
     __builtin_amdgcn_s_waitcnt(0xF70);  // vmcnt(0)
   }
 
+  float amx = 0.f;  // max |stored dK, dV value| of the lane (fp8 scale partials)
   if (mykey < T) {
     uint16_t* dkr = dk + (rowbase + mykey) * ld_dkv + hk * 128;
     uint16_t* dvr = dv + (rowbase + mykey) * ld_dkv + hk * 128;
@@ -621,17 +644,22 @@ attn_bwd_kv8_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int e = et * 32 + 8 * g + 4 * lh;
-        if constexpr (!FUSE)
-          *reinterpret_cast<uint2*>(dkr + e) =
-              make_uint2(pack_bf2(dkt[et][4 * g] * kScale, dkt[et][4 * g + 1] * kScale),
-                         pack_bf2(dkt[et][4 * g + 2] * kScale, dkt[et][4 * g + 3] * kScale));
-        *reinterpret_cast<uint2*>(dvr + e) =
-            make_uint2(pack_bf2(dvt[et][4 * g], dvt[et][4 * g + 1]), pack_bf2(dvt[et][4 * g + 2], dvt[et][4 * g + 3]));
+        if constexpr (!FUSE) {
+          const uint2 w = make_uint2(pack_bf2(dkt[et][4 * g] * kScale, dkt[et][4 * g + 1] * kScale),
+                                     pack_bf2(dkt[et][4 * g + 2] * kScale, dkt[et][4 * g + 3] * kScale));
+          *reinterpret_cast<uint2*>(dkr + e) = w;
+          amx = fmaxf(amx, absmax_w(w));
+        }
+        const uint2 w = make_uint2(pack_bf2(dvt[et][4 * g], dvt[et][4 * g + 1]),
+                                   pack_bf2(dvt[et][4 * g + 2], dvt[et][4 * g + 3]));
+        *reinterpret_cast<uint2*>(dvr + e) = w;
+        amx = fmaxf(amx, absmax_w(w));
       }
     if constexpr (FUSE)
-      qknorm_rope_bwd_store(dkt, kScale, kh + (long long)mykey * ld, rk[(rowbase + mykey) * Hkv + hk], cs, T, mykey,
-                            lh, dkr);
+      amx = fmaxf(amx, qknorm_rope_bwd_store(dkt, kScale, kh + (long long)mykey * ld, rk[(rowbase + mykey) * Hkv + hk],
+                                             cs, T, mykey, lh, dkr));
   }
+  store_wave_amax(amax, ((long long)blockIdx.x + (long long)gridDim.x * blockIdx.y) * 8 + wave, amx);
 }
 
 // ---------------------------------------------------------------------------
@@ -650,7 +678,7 @@ attn_bwd_q_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k
                   long long ld, const uint16_t* __restrict__ out, const uint16_t* __restrict__ dout, long long ld_out,
                   const float* __restrict__ lse, float* __restrict__ delta, float* __restrict__ dq_out, int H,
                   int Hkv, int T, int window_arg, uint16_t* __restrict__ dq_bf, long long ld_dq,
-                  const float* __restrict__ rq, const float* __restrict__ cs) {
+                  const float* __restrict__ rq, const float* __restrict__ cs, float* __restrict__ amax) {
   __shared__ __attribute__((aligned(16))) char smem[2 * DQ_STAGE];
   const int window = GEN ? window_arg : -1;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, lr = lane & 31, lh = lane >> 5;
@@ -780,10 +808,11 @@ attn_bwd_q_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k
     }
     dma_barrier();  // the next tile has landed; every wave is done with this one
   }
+  float amx = 0.f;  // max |stored dQ value| of the lane (fp8 scale partials; fused form only)
   if (myq < T) {
     if constexpr (FUSE) {
-      qknorm_rope_bwd_store(dqt, kScale, qh + (long long)myq * ld, rq[(rowbase + myq) * H + h], cs, T, myq, lh,
-                            dq_bf + (rowbase + myq) * ld_dq + h * 128);
+      amx = qknorm_rope_bwd_store(dqt, kScale, qh + (long long)myq * ld, rq[(rowbase + myq) * H + h], cs, T, myq, lh,
+                                  dq_bf + (rowbase + myq) * ld_dq + h * 128);
     } else {
       float* dqr = dq_out + (rowbase + myq) * d + h * 128;
 #pragma unroll
@@ -796,18 +825,25 @@ attn_bwd_q_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k
         }
     }
   }
+  store_wave_amax(amax, ((long long)blockIdx.x + (long long)gridDim.x * blockIdx.y) * 4 + wave, amx);
 }
 
 }  // namespace
 
+long long attn_fwd_amax_slots(int B, int H, int T) { return (long long)((T + FQ - 1) / FQ) * B * H * 4; }
+
+long long attn_bwd_amax_slots(int B, int H, int Hkv, int T) {
+  return (long long)((T + DQ_Q - 1) / DQ_Q) * B * H * 4 + (long long)((T + K8_KEYS - 1) / K8_KEYS) * B * Hkv * 8;
+}
+
 int launch_attn_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, long long ld_qkv, uint16_t* out,
                     long long ld_out, float* lse, int B, int H, int Hkv, int T, int window, hipStream_t s,
-                    bool lse_log2) {
+                    bool lse_log2, float* amax) {
   if (B <= 0 || T <= 0) return 0;
   dim3 grid((T + FQ - 1) / FQ, B * H);
   const bool gen = Hkv != H || window >= 0;
   hipLaunchKernelGGL(gen ? attn_fwd_kernel<true> : attn_fwd_kernel<false>, grid, dim3(256), 0, s, q, k, v, ld_qkv, out,
-                     ld_out, lse, H, Hkv, T, window, lse_log2 ? 1 : 0);
+                     ld_out, lse, H, Hkv, T, window, lse_log2 ? 1 : 0, amax);
   GS_LAUNCH_CHECK("attn_fwd");
   return 0;
 }
@@ -822,17 +858,19 @@ int launch_attn_bwd_part(int part, const uint16_t* q, const uint16_t* k, const u
   const float* rk = fuse ? fuse->rk : nullptr;
   const float* cs = fuse ? fuse->cs : nullptr;
   uint16_t* dq_bf = fuse ? fuse->dq : nullptr;
+  float* amax = fuse ? fuse->amax : nullptr;  // dQ kernel's waves, then the dK/dV kernel's
   if (part == 0) {  // dQ, and delta for the dK/dV kernel
     auto kern = fuse ? (gen ? attn_bwd_q_kernel<true, true> : attn_bwd_q_kernel<false, true>)
                      : (gen ? attn_bwd_q_kernel<true, false> : attn_bwd_q_kernel<false, false>);
     hipLaunchKernelGGL(kern, dim3((T + DQ_Q - 1) / DQ_Q, B * H), dim3(256), 0, s, q, k, v, ld_qkv, out, dout, ld_out,
-                       lse, delta, dq, H, Hkv, T, window, dq_bf, ld_dkv, rq, cs);
+                       lse, delta, dq, H, Hkv, T, window, dq_bf, ld_dkv, rq, cs, amax);
     GS_LAUNCH_CHECK("attn_bwd_q");
   } else {
     auto kern = fuse ? (gen ? attn_bwd_kv8_kernel<true, true> : attn_bwd_kv8_kernel<false, true>)
                      : (gen ? attn_bwd_kv8_kernel<true, false> : attn_bwd_kv8_kernel<false, false>);
     hipLaunchKernelGGL(kern, dim3((T + K8_KEYS - 1) / K8_KEYS, B * Hkv), dim3(K8_NT), 0, s, q, k, v, ld_qkv, dout,
-                       ld_out, lse, delta, dk, dv, ld_dkv, H, Hkv, T, window, rk, cs);
+                       ld_out, lse, delta, dk, dv, ld_dkv, H, Hkv, T, window, rk, cs,
+                       amax ? amax + (long long)((T + DQ_Q - 1) / DQ_Q) * B * H * 4 : nullptr);
     GS_LAUNCH_CHECK("attn_bwd_kv");
   }
   return 0;

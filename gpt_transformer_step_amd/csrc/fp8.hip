@@ -54,10 +54,14 @@ __device__ __forceinline__ float amax16(const void* x, long long idx) {
   }
 }
 
+// Batched over blockIdx.y: tensor b starts sx elements after tensor b - 1 and
+// writes its partials gridDim.x floats after b - 1's.
 template <bool F32>
-__global__ void __launch_bounds__(256) amax_partial_kernel(const void* __restrict__ x, long long ldx, int rows,
-                                                          int cols, float* __restrict__ partial) {
+__global__ void __launch_bounds__(256) amax_partial_kernel(const void* __restrict__ xv, long long ldx, int rows,
+                                                          int cols, float* __restrict__ partial, long long sx) {
   constexpr int EPC = F32 ? 4 : 8;  // elements per 16 bytes
+  const void* x = reinterpret_cast<const char*>(xv) + (long long)blockIdx.y * sx * (F32 ? 4 : 2);
+  partial += (long long)blockIdx.y * gridDim.x;
   float m = 0.f;
   if (ldx == cols) {
     const long long n16 = (long long)rows * cols / EPC;
@@ -91,8 +95,11 @@ __global__ void __launch_bounds__(256) amax_partial_kernel(const void* __restric
 // thousands) are read with eight independent loads in flight per thread, so
 // the reduction costs a few load latencies rather than one per 256 values.
 constexpr int kScaleNT = 1024;
+// (batched: workgroup b reduces partials b np .. and writes scale[b sstride])
 __global__ void __launch_bounds__(kScaleNT) fp8_scale_kernel(const float* __restrict__ partial, long long np,
-                                                            int fmt, float* __restrict__ scale) {
+                                                            int fmt, float* __restrict__ scale, long long sstride) {
+  partial += (long long)blockIdx.x * np;
+  scale += (long long)blockIdx.x * sstride;
   float m[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   long long i = threadIdx.x;
   for (; i + 7 * kScaleNT < np; i += 8 * kScaleNT) {
@@ -141,12 +148,19 @@ __device__ __forceinline__ void load8(const void* x, long long idx, float* v) {
   }
 }
 
+// Batched over blockIdx.z with element strides sx (x), ss (scale), sq (q, qt).
 template <bool F32, int FMT>
-__global__ void __launch_bounds__(256) fp8_quant128_kernel(const void* __restrict__ x, long long ldx, int rows,
+__global__ void __launch_bounds__(256) fp8_quant128_kernel(const void* __restrict__ xv, long long ldx, int rows,
                                                           int cols, const float* __restrict__ scale,
                                                           uint8_t* __restrict__ q, long long ldq,
-                                                          uint8_t* __restrict__ qt, long long ldqt) {
+                                                          uint8_t* __restrict__ qt, long long ldqt, long long sx,
+                                                          long long ss, long long sq) {
   __shared__ __attribute__((aligned(16))) uint8_t tile[kQT2 * kLDT2];
+  const int bz = blockIdx.z;
+  const void* x = reinterpret_cast<const char*>(xv) + (long long)bz * sx * (F32 ? 4 : 2);
+  scale += (long long)bz * ss;
+  if (q) q += (long long)bz * sq;
+  if (qt) qt += (long long)bz * sq;
   const int t = threadIdx.x;
   const int r0 = blockIdx.y * kQT2, c0 = blockIdx.x * kQT2;
   const int rb = 8 * (t >> 4), cb = 8 * (t & 15);
@@ -208,23 +222,25 @@ int fp8_partials(long long rows, long long cols) {
 }
 
 int launch_fp8_amax_scale(const void* x, int is_f32, long long ldx, int rows, int cols, int fmt, float* partial,
-                          float* scale, hipStream_t s) {
+                          float* scale, hipStream_t s, int count, long long sx, long long sscale) {
   const int np = fp8_partials(rows, cols);
+  if (count <= 0) return 0;
   if (is_f32)
-    hipLaunchKernelGGL(amax_partial_kernel<true>, dim3(np), dim3(256), 0, s, x, ldx, rows, cols, partial);
+    hipLaunchKernelGGL(amax_partial_kernel<true>, dim3(np, count), dim3(256), 0, s, x, ldx, rows, cols, partial, sx);
   else
-    hipLaunchKernelGGL(amax_partial_kernel<false>, dim3(np), dim3(256), 0, s, x, ldx, rows, cols, partial);
+    hipLaunchKernelGGL(amax_partial_kernel<false>, dim3(np, count), dim3(256), 0, s, x, ldx, rows, cols, partial, sx);
   GS_LAUNCH_CHECK("amax_partial");
-  hipLaunchKernelGGL(fp8_scale_kernel, dim3(1), dim3(kScaleNT), 0, s, partial, (long long)np, fmt, scale);
+  hipLaunchKernelGGL(fp8_scale_kernel, dim3(count), dim3(kScaleNT), 0, s, partial, (long long)np, fmt, scale, sscale);
   GS_LAUNCH_CHECK("fp8_scale");
   return 0;
 }
 
 int launch_fp8_quant(const void* x, int is_f32, long long ldx, int rows, int cols, int fmt, const float* scale,
-                     uint8_t* q, long long ldq, uint8_t* qt, long long ldqt, hipStream_t s) {
-  if (rows <= 0 || cols <= 0) return 0;
-  dim3 grid((cols + kQT2 - 1) / kQT2, (rows + kQT2 - 1) / kQT2);
-#define GS_Q(F, M) hipLaunchKernelGGL((fp8_quant128_kernel<F, M>), grid, dim3(256), 0, s, x, ldx, rows, cols, scale, q, ldq, qt, ldqt)
+                     uint8_t* q, long long ldq, uint8_t* qt, long long ldqt, hipStream_t s, int count, long long sx,
+                     long long sscale, long long sq) {
+  if (rows <= 0 || cols <= 0 || count <= 0) return 0;
+  dim3 grid((cols + kQT2 - 1) / kQT2, (rows + kQT2 - 1) / kQT2, count);
+#define GS_Q(F, M) hipLaunchKernelGGL((fp8_quant128_kernel<F, M>), grid, dim3(256), 0, s, x, ldx, rows, cols, scale, q, ldq, qt, ldqt, sx, sscale, sq)
   if (is_f32) {
     if (fmt) GS_Q(true, 1); else GS_Q(true, 0);
   } else {
@@ -245,7 +261,7 @@ int quantize_fp8(const void* x, int is_f32, long long ldx, int rows, int cols, i
 int quantize_fp8_partials(const void* x, int is_f32, long long ldx, int rows, int cols, int fmt,
                           const float* partial, long long np, float* scale, uint8_t* q, long long ldq, uint8_t* qt,
                           long long ldqt, hipStream_t s) {
-  hipLaunchKernelGGL(fp8_scale_kernel, dim3(1), dim3(kScaleNT), 0, s, partial, np, fmt, scale);
+  hipLaunchKernelGGL(fp8_scale_kernel, dim3(1), dim3(kScaleNT), 0, s, partial, np, fmt, scale, 0LL);
   GS_LAUNCH_CHECK("fp8_scale");
   return launch_fp8_quant(x, is_f32, ldx, rows, cols, fmt, scale, q, ldq, qt, ldqt, s);
 }

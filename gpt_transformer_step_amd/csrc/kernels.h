@@ -110,9 +110,12 @@ int launch_axpy_stream(float* g, uint16_t* g_bf, const float* y, const uint16_t*
 // window: left window (query i sees keys i - window .. i), -1 = full causal
 // lse [B, H, T]: natural log-sum-exp of each row's scaled scores, or (lse_log2)
 // in log2 units, the form the fused backward kernels (QkNormBwd given) read
+// amax (nullable): per-wave max |stored output| (attn_fwd_amax_slots of them)
 int launch_attn_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, long long ld_qkv,
                     uint16_t* out, long long ld_out, float* lse, int B, int H, int Hkv, int T, int window,
-                    hipStream_t s, bool lse_log2 = false);
+                    hipStream_t s, bool lse_log2 = false, float* amax = nullptr);
+long long attn_fwd_amax_slots(int B, int H, int T);
+long long attn_bwd_amax_slots(int B, int H, int Hkv, int T);
 int launch_attn_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, long long ld_qkv,
                     const uint16_t* out, const uint16_t* dout, long long ld_out, const float* lse,
                     float* delta, float* dq, uint16_t* dk, uint16_t* dv, long long ld_dkv, int B,
@@ -126,6 +129,7 @@ struct QkNormBwd {
   const float* rk;
   const float* cs;
   uint16_t* dq;
+  float* amax;  // nullable: per-wave max |stored dq, dk, dv| (attn_bwd_amax_slots of them)
 };
 // one of the two backward kernels, in this order: 0 = dQ (also writes delta = rowsum(dout * out)),
 // 1 = dK/dV (reads delta).  fuse NULL: raw gradients (dq fp32 [N, 128 H], dk bf16), lse in
@@ -141,12 +145,16 @@ int launch_attn_bwd_part(int part, const uint16_t* q, const uint16_t* k, const u
 // cols % 16 == 0, rows * cols / 4 < 2^31.  fmt 0 = E4M3, 1 = E5M2.
 constexpr int kFp8Partials = 1024;  // floats of `partial` scratch per tensor
 int fp8_partials(long long rows, long long cols);
-// scale[0] = fmax / max|x| (1 when x == 0)
+// scale[0] = fmax / max|x| (1 when x == 0).  Batched: count tensors of one
+// shape, tensor b at x + b sx (elements), its scale at scale[b sscale]; the
+// partials need count * fp8_partials(rows, cols) floats.
 int launch_fp8_amax_scale(const void* x, int is_f32, long long ldx, int rows, int cols, int fmt, float* partial,
-                          float* scale, hipStream_t s);
-// q[r, c] = code(x[r, c] * scale) and / or qt[c, r] = the same code (each nullable)
+                          float* scale, hipStream_t s, int count = 1, long long sx = 0, long long sscale = 0);
+// q[r, c] = code(x[r, c] * scale) and / or qt[c, r] = the same code (each nullable);
+// batched as above, tensor b's codes at q + b sq and qt + b sq
 int launch_fp8_quant(const void* x, int is_f32, long long ldx, int rows, int cols, int fmt, const float* scale,
-                     uint8_t* q, long long ldq, uint8_t* qt, long long ldqt, hipStream_t s);
+                     uint8_t* q, long long ldq, uint8_t* qt, long long ldqt, hipStream_t s, int count = 1,
+                     long long sx = 0, long long sscale = 0, long long sq = 0);
 int quantize_fp8(const void* x, int is_f32, long long ldx, int rows, int cols, int fmt, float* partial, float* scale,
                  uint8_t* q, long long ldq, uint8_t* qt, long long ldqt, hipStream_t s);
 // the same with the amax already reduced by the producer into np partials
