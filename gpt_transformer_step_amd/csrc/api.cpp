@@ -539,36 +539,50 @@ inline T* at(void* ws, size_t off) { return reinterpret_cast<T*>(reinterpret_cas
 
 // k-splits for a weight-gradient product (small output, long K): each split
 // writes a partial that a small reduction adds up (no atomics,
-// deterministic).  The split count fills the chip's workgroup slots (one
-// 256x256 workgroup per CU, two 128x128 ones) as evenly as possible: the
-// smallest count whose last wave is within 2.5% of the best fill, with 256x256
-// tiles whenever some count up to 20 reaches 512 workgroups, and at least 2048
-// k per split.  The count may stop at 500 workgroups (the big-tile threshold
-// of the launch): for the d20 MLP products (100 tiles) that is 5 splits
-// instead of 10, half the partial traffic for the same 98 % fill.
-inline int wgrad_splits(int M, int N, int K) {
-  const long long t256 = (long long)((M + 255) / 256) * ((N + 255) / 256);
-  if (t256 >= 256) return 1;
+// deterministic), at least 2048 k per split.  Outputs of at least 256 x 256
+// take 256 x 256 tiles (one workgroup per CU) and the split count that
+// minimises the modelled time rounds(ks) / ks + 0.008 ks: the waves of
+// workgroups the launch needs over the work each workgroup does, plus the
+// partial traffic and per-workgroup overhead that grow with the count (fit to
+// the d20 products, measured without the reduction: the output projection's
+// 25 tiles take 10 splits, 0.196 ms against 0.264 ms with 128 x 128 tiles; the
+// q/k/v product's 75 take 3, 0.557 against 0.617 ms with 10; the MLP
+// products' 100 take 5).  Smaller outputs take 128 x 128 tiles (two
+// workgroups per CU) and the smallest count whose last wave is within 2.5 %
+// of the best fill.
+struct WgradPlan {
+  int ks;    // k splits (1: none)
+  int tile;  // forced tile width (0: the launch's own choice)
+};
+inline WgradPlan wgrad_plan(int M, int N, int K) {
+  const int kmax = std::max(1, std::min(32, K / 2048));
+  if (M >= 256 && N >= 256) {
+    const long long t256 = (long long)((M + 255) / 256) * ((N + 255) / 256);
+    if (t256 >= 256) return {1, 0};
+    double best = 1e30;
+    int bk = 1;
+    for (int ks = 1; ks <= kmax; ++ks) {
+      const double rounds = (double)((t256 * ks + 255) / 256);
+      const double cost = rounds / ks + 0.008 * ks;
+      if (cost < best - 1e-9) { best = cost; bk = ks; }
+    }
+    return {bk, 256};
+  }
   const long long t128 = (long long)((M + 127) / 128) * ((N + 127) / 128);
-  const int kmax = std::max(1, K / 2048);
-  const bool big = M >= 256 && N >= 256 && t256 * 20 >= 512;
-  const long long tiles = big ? t256 : t128, slots = big ? 256 : 512;
-  const int lo = big ? (int)((500 + t256 - 1) / t256) : 1;
-  const int hi = std::min(big ? 20 : 16, kmax);
-  if (lo > hi) return std::max(1, std::min(kmax, 16));
+  const int hi = std::min(16, kmax);
   auto fill = [&](int ks) {
-    const long long b = tiles * ks;
-    return (double)b / (double)(((b + slots - 1) / slots) * slots);
+    const long long b = t128 * ks;
+    return (double)b / (double)(((b + 511) / 512) * 512);
   };
   double best = 0.0;
-  for (int ks = lo; ks <= hi; ++ks) best = std::max(best, fill(ks));
-  for (int ks = lo; ks <= hi; ++ks)
-    if (fill(ks) >= best - 0.025) return ks;
-  return lo;
+  for (int ks = 1; ks <= hi; ++ks) best = std::max(best, fill(ks));
+  for (int ks = 1; ks <= hi; ++ks)
+    if (fill(ks) >= best - 0.025) return {ks, 128};
+  return {1, 128};
 }
 
 inline size_t wgrad_part_elems(int M, int N, int K) {
-  const int ks = wgrad_splits(M, N, K);
+  const int ks = wgrad_plan(M, N, K).ks;
   return ks > 1 ? (size_t)ks * M * N : 0;
 }
 
@@ -579,16 +593,17 @@ int wgrad(const void* A, long long lda, const void* B, long long ldb, float* C, 
   a.M = M; a.N = N; a.K = K;
   a.A = A; a.lda = lda; a.a_kcontig = 0;
   a.B = B; a.ldb = ldb; a.b_kcontig = 0;
-  const int ks = wgrad_splits(M, N, K);
-  if (ks == 1) {
+  const WgradPlan pl = wgrad_plan(M, N, K);
+  a.tile = pl.tile;
+  if (pl.ks == 1) {
     a.C = C; a.ldc = N;
     a.beta = accumulate ? 1.f : 0.f;
     return gemm_bf16(a, EPI_F32, s);
   }
-  a.C = part; a.ldc = N; a.k_split = ks; a.split_stride = (long long)M * N; a.beta = 0.f;
+  a.C = part; a.ldc = N; a.k_split = pl.ks; a.split_stride = (long long)M * N; a.beta = 0.f;
   int rc = gemm_bf16(a, EPI_F32, s);
   if (rc) return rc;
-  return launch_splitk_reduce(part, ks, (long long)M * N, C, nullptr, (long long)M * N, accumulate ? 1.f : 0.f, s);
+  return launch_splitk_reduce(part, pl.ks, (long long)M * N, C, nullptr, (long long)M * N, accumulate ? 1.f : 0.f, s);
 }
 
 // fp8 weight gradient: C[M,N] (+)= A B^T / (sa sb) with A = dY^T codes
@@ -599,16 +614,17 @@ int wgrad_fp8(const uint8_t* A, const uint8_t* B, const float* sa, const float* 
   a.M = M; a.N = N; a.K = K;
   a.A = A; a.lda = K; a.B = B; a.ldb = K;
   a.scale_a = sa; a.scale_b = sb;
-  const int ks = wgrad_splits(M, N, K);
-  if (ks == 1) {
+  const WgradPlan pl = wgrad_plan(M, N, K);
+  a.tile = pl.tile;
+  if (pl.ks == 1) {
     a.C = C; a.ldc = N;
     a.beta = accumulate ? 1.f : 0.f;
     return gemm_fp8(a, EPI_F32, 1, 0, s);
   }
-  a.C = part; a.ldc = N; a.k_split = ks; a.split_stride = (long long)M * N; a.beta = 0.f;
+  a.C = part; a.ldc = N; a.k_split = pl.ks; a.split_stride = (long long)M * N; a.beta = 0.f;
   int rc = gemm_fp8(a, EPI_F32, 1, 0, s);
   if (rc) return rc;
-  return launch_splitk_reduce(part, ks, (long long)M * N, C, nullptr, (long long)M * N, accumulate ? 1.f : 0.f, s);
+  return launch_splitk_reduce(part, pl.ks, (long long)M * N, C, nullptr, (long long)M * N, accumulate ? 1.f : 0.f, s);
 }
 
 }  // namespace
