@@ -764,19 +764,26 @@ attn_bwd_q_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k
     }
     const int key0 = j * DQ_K;
     if (key0 <= wq0 + 31 && (window < 0 || key0 + DQ_K - 1 >= wq0 - window)) {  // wave-uniform
+      // the scores first, then dP = dO V^T: the exponentials of the scores
+      // (below) only need the former and can run under the latter
       f32x16_t st2[2], dpt[2];
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt) {
 #pragma unroll
         for (int e = 0; e < 16; ++e) { st2[kt][e] = 0.f; dpt[kt][e] = 0.f; }
+      }
 #pragma unroll
-        for (int ks = 0; ks < 8; ++ks) {
+      for (int ks = 0; ks < 8; ++ks)
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
           st2[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag16(sk, kt * 32 + lr, ks * 2 + lh), fq[ks], st2[kt],
                                                             0, 0, 0);
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks)
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
           dpt[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag16(sv, kt * 32 + lr, ks * 2 + lh), fd[ks], dpt[kt],
                                                             0, 0, 0);
-        }
-      }
       const bool diag = (key0 + DQ_K - 1 > wq0) || (key0 + DQ_K > T) || (window >= 0 && key0 < wq0 + 31 - window);
       float ds[32];
 #pragma unroll
