@@ -560,60 +560,53 @@ attn_bwd_kv8_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
       const int q0 = qt_of(it) * KV_Q;
       // wave-uniform: some query of the tile sees some key of the wave
       if (q0 + KV_Q - 1 >= wk0 && (window < 0 || q0 <= wk0 + 31 + window)) {
+        // the scores first, then dP = dO V^T: P = exp2(S c - lse) needs only
+        // the former and runs under the latter (same straight-line block)
         f32x16_t sacc, dpacc;
 #pragma unroll
         for (int e = 0; e < 16; ++e) { sacc[e] = 0.f; dpacc[e] = 0.f; }
 #pragma unroll
-        for (int ks = 0; ks < 8; ++ks) {
+        for (int ks = 0; ks < 8; ++ks)
           sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag16(st + K8_QN, lr, ks * 2 + lh),
-                                                         frag16(s_k, wave * 32 + lr, ks * 2 + lh), sacc, 0, 0,
-                                                         0);
+                                                         frag16(s_k, wave * 32 + lr, ks * 2 + lh), sacc, 0, 0, 0);
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks)
           dpacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag16(st + K8_DN, lr, ks * 2 + lh), fv[ks], dpacc, 0, 0, 0);
-        }
         const float* slse = reinterpret_cast<const float*>(st + K8_ST);
         const float* sdel = slse + KV_Q;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int ql = 8 * (e >> 2) + 4 * lh + (e & 3);
+          const float l2 = FUSE ? slse[ql] : slse[ql] * kLog2e;  // FUSE: lse stored in log2 units
+          sacc[e] = __builtin_amdgcn_exp2f(sacc[e] * c - l2);  // P, in place of S
+        }
         // rows past the sequence end carry the last row's statistics: masked
         const bool diag = (q0 < wk0 + 31) || (q0 + KV_Q > T) || (wk0 + 32 > T) ||
                           (window >= 0 && q0 + KV_Q - 1 > wk0 + window);
-        bf16x8_t fp[2], fs[2];
-        // P and dS of the tile as bf16 B fragments; the visibility test only
-        // on tiles that need it (wave-uniform branch)
-        auto p_ds = [&](auto masked) {
-          constexpr bool MASK = decltype(masked)::value;
+        if (diag) {  // wave-uniform: the visibility test only on tiles that need it
+          keep_branch();
 #pragma unroll
-          for (int s2 = 0; s2 < 2; ++s2) {
-            uint32_t* wp = reinterpret_cast<uint32_t*>(&fp[s2]);
-            uint32_t* wd = reinterpret_cast<uint32_t*>(&fs[s2]);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              float pv[2], dv2[2];
-#pragma unroll
-              for (int u = 0; u < 2; ++u) {
-                const int e = 8 * s2 + 2 * i + u;
-                const int ql = 8 * (e >> 2) + 4 * lh + (e & 3);
-                const float l2 = FUSE ? slse[ql] : slse[ql] * kLog2e;  // FUSE: lse stored in log2 units
-                const float dl = sdel[ql];
-                float pe = __builtin_amdgcn_exp2f(sacc[e] * c - l2);
-                if constexpr (MASK) {
-                  const bool vis =
-                      mykey <= q0 + ql && mykey < T && q0 + ql < T && (window < 0 || mykey >= q0 + ql - window);
-                  // causal only: a bit mask, not a select (as a select the
-                  // compiler turns each element into a branch around the
-                  // exponential; the windowed variant has no registers to spare
-                  // for the straight-line form)
-                  if constexpr (GEN) pe = vis ? pe : 0.f;
-                  else pe = __int_as_float(__float_as_int(pe) & -(int)vis);
-                }
-                pv[u] = pe;
-                dv2[u] = pe * (dpacc[e] - dl);
-              }
-              wp[i] = pack_bf2(pv[0], pv[1]);
-              wd[i] = pack_bf2(dv2[0], dv2[1]);
-            }
+          for (int e = 0; e < 16; ++e) {
+            const int ql = 8 * (e >> 2) + 4 * lh + (e & 3);
+            const bool vis =
+                mykey <= q0 + ql && mykey < T && q0 + ql < T && (window < 0 || mykey >= q0 + ql - window);
+            sacc[e] = __int_as_float(__float_as_int(sacc[e]) & -(int)vis);
           }
-        };
-        if (diag) p_ds(std::integral_constant<bool, true>{});
-        else p_ds(std::integral_constant<bool, false>{});
+        }
+        // P and dS = P (dP - delta) of the tile as bf16 B fragments
+        bf16x8_t fp[2], fs[2];
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2) {
+          uint32_t* wp = reinterpret_cast<uint32_t*>(&fp[s2]);
+          uint32_t* wd = reinterpret_cast<uint32_t*>(&fs[s2]);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int e0 = 8 * s2 + 2 * i, e1 = e0 + 1;
+            wp[i] = pack_bf2(sacc[e0], sacc[e1]);
+            wd[i] = pack_bf2(sacc[e0] * (dpacc[e0] - sdel[8 * (e0 >> 2) + 4 * lh + (e0 & 3)]),
+                             sacc[e1] * (dpacc[e1] - sdel[8 * (e1 >> 2) + 4 * lh + (e1 & 3)]));
+          }
+        }
 #pragma unroll
         for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
