@@ -217,6 +217,28 @@ struct TileLoader {
 };
 
 // ---------------------------------------------------------------------------
+// Output stores are non-temporal: a tile's outputs are written once and read
+// by a later kernel, and marked so they do not displace the operand panels
+// the other workgroups are streaming (the d20 MLP product with bf16 output:
+// 0.79 -> 0.74 ms; 65536x1280x1280: 0.20 -> 0.185 ms).
+// ---------------------------------------------------------------------------
+typedef unsigned int u32x4_nt __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2_nt __attribute__((ext_vector_type(2)));
+typedef float f32x4_nt __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ void st_nt(void* p, uint4 w) {
+  const u32x4_nt v = {w.x, w.y, w.z, w.w};
+  __builtin_nontemporal_store(v, reinterpret_cast<u32x4_nt*>(p));
+}
+__device__ __forceinline__ void st_nt(void* p, uint2 w) {
+  const u32x2_nt v = {w.x, w.y};
+  __builtin_nontemporal_store(v, reinterpret_cast<u32x2_nt*>(p));
+}
+__device__ __forceinline__ void st_nt(float* p, float4 f) {
+  const f32x4_nt v = {f.x, f.y, f.z, f.w};
+  __builtin_nontemporal_store(v, reinterpret_cast<f32x4_nt*>(p));
+}
+
+// ---------------------------------------------------------------------------
 // epilogues on 4 consecutive columns n .. n+3 of row m
 // ---------------------------------------------------------------------------
 template <int EPI>
@@ -238,7 +260,7 @@ __device__ __forceinline__ void epi4(const GemmArgs& p, int bi, int m, int n, co
         const float b = (EPI == EPI_RESID) ? 1.f : p.beta;
         o.x += b * c.x; o.y += b * c.y; o.z += b * c.z; o.w += b * c.w;
       }
-      *reinterpret_cast<float4*>(C) = o;
+      st_nt(C, o);
     } else {
       for (int j = 0; j < 4; ++j)
         if (n + j < p.N) {
@@ -267,7 +289,7 @@ __device__ __forceinline__ void epi4(const GemmArgs& p, int bi, int m, int n, co
     }
     if (full) {
       const uint2 w = make_uint2(pack_bf2(o[0], o[1]), pack_bf2(o[2], o[3]));
-      *reinterpret_cast<uint2*>(C) = w;
+      st_nt(C, w);
       if (p.amax)
         amx = fmaxf(amx, fmaxf(fmaxf(fabsf(lo_bf(w.x)), fabsf(hi_bf(w.x))), fmaxf(fabsf(lo_bf(w.y)), fabsf(hi_bf(w.y)))));
     } else {
@@ -286,8 +308,8 @@ __device__ __forceinline__ void epi4(const GemmArgs& p, int bi, int m, int n, co
       if (have_c) w = make_uint2(__float_as_uint(cpre.x), __float_as_uint(cpre.y));
       else w = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(p.aux) + (long long)bi * p.sAux +
                                                 (long long)m * p.ldaux + n);
-      *reinterpret_cast<float4*>(C) = make_float4(v[0] + p.beta * lo_bf(w.x), v[1] + p.beta * hi_bf(w.x),
-                                                  v[2] + p.beta * lo_bf(w.y), v[3] + p.beta * hi_bf(w.y));
+      st_nt(C, make_float4(v[0] + p.beta * lo_bf(w.x), v[1] + p.beta * hi_bf(w.x), v[2] + p.beta * lo_bf(w.y),
+                           v[3] + p.beta * hi_bf(w.y)));
     } else {
       const uint16_t* a = reinterpret_cast<const uint16_t*>(p.aux) + (long long)bi * p.sAux + (long long)m * p.ldaux + n;
       for (int j = 0; j < 4; ++j)
@@ -312,7 +334,8 @@ __device__ __forceinline__ void epi8(const GemmArgs& p, int bi, int m, int n, co
       h8_t h;
 #pragma unroll
       for (int j = 0; j < 8; ++j) h[j] = (_Float16)v[j];
-      *reinterpret_cast<h8_t*>(H) = h;
+      const uint4 hw = *reinterpret_cast<const uint4*>(&h);
+      st_nt(H, hw);
     } else {
       for (int j = 0; j < 8; ++j)
         if (n + j < p.N) H[j] = (_Float16)v[j];
@@ -355,7 +378,7 @@ __device__ __forceinline__ void epi8(const GemmArgs& p, int bi, int m, int n, co
   }
   if (full) {
     const uint4 w = make_uint4(pack_bf2(o[0], o[1]), pack_bf2(o[2], o[3]), pack_bf2(o[4], o[5]), pack_bf2(o[6], o[7]));
-    *reinterpret_cast<uint4*>(C) = w;
+    st_nt(C, w);
     if (p.amax) {
       const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
