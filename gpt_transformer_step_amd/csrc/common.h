@@ -43,6 +43,23 @@ __device__ __forceinline__ float wave_sum(float v) {
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
   return v;
 }
+// Non-temporal vector stores (data written once and read by a later kernel)
+typedef unsigned int u32x4_nt __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2_nt __attribute__((ext_vector_type(2)));
+typedef float f32x4_nt __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ void st_nt(void* p, uint4 w) {
+  const u32x4_nt v = {w.x, w.y, w.z, w.w};
+  __builtin_nontemporal_store(v, reinterpret_cast<u32x4_nt*>(p));
+}
+__device__ __forceinline__ void st_nt(void* p, uint2 w) {
+  const u32x2_nt v = {w.x, w.y};
+  __builtin_nontemporal_store(v, reinterpret_cast<u32x2_nt*>(p));
+}
+__device__ __forceinline__ void st_nt(float* p, float4 f) {
+  const f32x4_nt v = {f.x, f.y, f.z, f.w};
+  __builtin_nontemporal_store(v, reinterpret_cast<f32x4_nt*>(p));
+}
+
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));

@@ -273,7 +273,7 @@ __global__ void __launch_bounds__(256) rmsnorm_bwd_kernel(const void* __restrict
       gv.y += rr * (dv[i].y - hv[i].y * dot);
       gv.z += rr * (dv[i].z - hv[i].z * dot);
       gv.w += rr * (dv[i].w - hv[i].w * dot);
-      *reinterpret_cast<float4*>(g + n * d + c * 4) = gv;
+      st_nt(g + n * d + c * 4, gv);  // read again only by the next norm backward
       const uint2 w = make_uint2(pack_bf2(gv.x, gv.y), pack_bf2(gv.z, gv.w));
       *reinterpret_cast<uint2*>(g_bf + n * d + c * 4) = w;
       if (amax_part)
@@ -719,8 +719,8 @@ __global__ void muon_apply_kernel(const float* __restrict__ X, float* __restrict
           float4 w = *reinterpret_cast<const float4*>(W + base + idx);
           w.x = w.x * decay - lr * o[0]; w.y = w.y * decay - lr * o[1];
           w.z = w.z * decay - lr * o[2]; w.w = w.w * decay - lr * o[3];
-          *reinterpret_cast<float4*>(W + base + idx) = w;
-          if (Wb) *reinterpret_cast<uint2*>(Wb + base + idx) = make_uint2(pack_bf2(w.x, w.y), pack_bf2(w.z, w.w));
+          st_nt(W + base + idx, w);  // the weights are read by the next step
+          if (Wb) st_nt(Wb + base + idx, make_uint2(pack_bf2(w.x, w.y), pack_bf2(w.z, w.w)));
         }
       }
     }
@@ -766,10 +766,11 @@ __global__ void __launch_bounds__(256) adamw_kernel(float* __restrict__ W, uint1
       v[j] = b2 * v[j] + (1.f - b2) * gj * gj;
       w[j] = w[j] * decay - lr * (m[j] * inv_bc1) / (sqrtf(v[j] * inv_bc2) + eps);
     }
-    reinterpret_cast<float4*>(M)[i] = make_float4(m[0], m[1], m[2], m[3]);
-    reinterpret_cast<float4*>(V)[i] = make_float4(v[0], v[1], v[2], v[3]);
-    reinterpret_cast<float4*>(W)[i] = make_float4(w[0], w[1], w[2], w[3]);
-    if (Wb) reinterpret_cast<uint2*>(Wb)[i] = make_uint2(pack_bf2(w[0], w[1]), pack_bf2(w[2], w[3]));
+    // the state and weights are read by the next step
+    st_nt(M + 4 * i, make_float4(m[0], m[1], m[2], m[3]));
+    st_nt(V + 4 * i, make_float4(v[0], v[1], v[2], v[3]));
+    st_nt(W + 4 * i, make_float4(w[0], w[1], w[2], w[3]));
+    if (Wb) st_nt(Wb + 4 * i, make_uint2(pack_bf2(w[0], w[1]), pack_bf2(w[2], w[3])));
   }
 }
 

@@ -222,21 +222,7 @@ struct TileLoader {
 // the other workgroups are streaming (the d20 MLP product with bf16 output:
 // 0.79 -> 0.74 ms; 65536x1280x1280: 0.20 -> 0.185 ms).
 // ---------------------------------------------------------------------------
-typedef unsigned int u32x4_nt __attribute__((ext_vector_type(4)));
-typedef unsigned int u32x2_nt __attribute__((ext_vector_type(2)));
-typedef float f32x4_nt __attribute__((ext_vector_type(4)));
-__device__ __forceinline__ void st_nt(void* p, uint4 w) {
-  const u32x4_nt v = {w.x, w.y, w.z, w.w};
-  __builtin_nontemporal_store(v, reinterpret_cast<u32x4_nt*>(p));
-}
-__device__ __forceinline__ void st_nt(void* p, uint2 w) {
-  const u32x2_nt v = {w.x, w.y};
-  __builtin_nontemporal_store(v, reinterpret_cast<u32x2_nt*>(p));
-}
-__device__ __forceinline__ void st_nt(float* p, float4 f) {
-  const f32x4_nt v = {f.x, f.y, f.z, f.w};
-  __builtin_nontemporal_store(v, reinterpret_cast<f32x4_nt*>(p));
-}
+// (st_nt: common.h)
 
 // ---------------------------------------------------------------------------
 // epilogues on 4 consecutive columns n .. n+3 of row m
