@@ -1275,14 +1275,14 @@ int muon_impl(float* Wt, uint16_t* W_bf16, const float* Gm, float* M, float* O_o
         TRY(gemm_bf16(a, EPI_F32, s));
         TRY(launch_splitk_reduce(gpart, gram_split, sA * count, nullptr, Ab, sA * count, 0.f, s));
       }
-      if (sym) TRY(launch_sym_mirror(Ab, 0, sm, sm, sA, count, s));
+      if (sym) TRY(launch_sym_mirror(Ab, sm, sm, sA, count, s));
     }
     {
       ProfScope ps_(P_NS_POLY, s);
       GemmArgs a = gp;  // B = b A + c A A
       a.alpha = cc; a.beta = cb;
       TRY(gemm_bf16(a, EPI_NS_POLY, s));
-      if (sym) TRY(launch_sym_mirror(Bb, 0, sm, sm, sA, count, s));
+      if (sym) TRY(launch_sym_mirror(Bb, sm, sm, sA, count, s));
     }
     {
       // X = a X + X B, X kept in bf16 (as the iteration's products read it);

@@ -442,33 +442,6 @@ __global__ void __launch_bounds__(256) sym_mirror_bf16_kernel(uint16_t* __restri
   }
 }
 
-// fp32 matrices (any n): C[b][i][j] = C[b][j][i] for i > j, 64 x 64 blocks
-// (bi, bj), bi >= bj, of the lower triangle, each read from its mirror block
-// (bj, bi) through LDS.  Reads touch only elements with i < j (or the block's
-// own upper part on the diagonal) and writes only i > j.
-__global__ void __launch_bounds__(256) sym_mirror_f32_kernel(float* __restrict__ C, int n, long long ld,
-                                                             long long stride) {
-  __shared__ float tile[64][65];
-  const int x = blockIdx.x;
-  int bi = (int)((sqrtf(8.f * x + 1.f) - 1.f) * 0.5f);
-  while (bi * (bi + 1) / 2 > x) --bi;
-  while ((bi + 1) * (bi + 2) / 2 <= x) ++bi;
-  const int bj = x - bi * (bi + 1) / 2;
-  float* c = C + (long long)blockIdx.y * stride;
-  const int r0 = bj * 64, c0 = bi * 64;
-  for (int e = threadIdx.x; e < 64 * 64; e += 256) {
-    const int rr = e >> 6, cc = e & 63;
-    const int gr = r0 + rr, gc = c0 + cc;
-    if (gr < n && gc < n && gr < gc) tile[rr][cc] = c[(long long)gr * ld + gc];
-  }
-  __syncthreads();
-  for (int e = threadIdx.x; e < 64 * 64; e += 256) {
-    const int rr = e >> 6, cc = e & 63;
-    const int gi = c0 + rr, gj = r0 + cc;
-    if (gi < n && gj < n && gi > gj) c[(long long)gi * ld + gj] = tile[cc][rr];
-  }
-}
-
 // ---------------------------- Muon elementwise ------------------------------
 // Momentum and the Frobenius partials in one pass: M <- mu M + G over chunk
 // blk of matrix b, partial[b * nblk + blk] = sum of squares of the new M
@@ -932,19 +905,15 @@ int launch_splitk_reduce(const float* part, int nsplit, long long stride, float*
   return 0;
 }
 
-int launch_sym_mirror(void* C, int is_f32, int n, long long ld, long long stride, int count, hipStream_t s) {
+int launch_sym_mirror(uint16_t* C, int n, long long ld, long long stride, int count, hipStream_t s) {
   if (n <= 1 || count <= 0) return 0;
   const int nb = (n + 63) / 64;
   dim3 grid(nb * (nb + 1) / 2, count);
-  if (is_f32) {
-    hipLaunchKernelGGL(sym_mirror_f32_kernel, grid, dim3(256), 0, s, static_cast<float*>(C), n, ld, stride);
-  } else {
-    if ((n % 8) || (ld % 8) || (stride % 8) || (reinterpret_cast<uintptr_t>(C) % 16)) {
-      set_error("sym_mirror: bf16 matrices need n, ld, stride multiples of 8 and a 16-byte aligned base");
-      return -3;
-    }
-    hipLaunchKernelGGL(sym_mirror_bf16_kernel, grid, dim3(256), 0, s, static_cast<uint16_t*>(C), n, ld, stride);
+  if ((n % 8) || (ld % 8) || (stride % 8) || (reinterpret_cast<uintptr_t>(C) % 16)) {
+    set_error("sym_mirror: bf16 matrices need n, ld, stride multiples of 8 and a 16-byte aligned base");
+    return -3;
   }
+  hipLaunchKernelGGL(sym_mirror_bf16_kernel, grid, dim3(256), 0, s, C, n, ld, stride);
   GS_LAUNCH_CHECK("sym_mirror");
   return 0;
 }

@@ -36,9 +36,10 @@ int launch_ce_dz(const uint16_t* e, uint16_t* dz, const float* part, int nparts,
 int launch_ce_reduce(const float* part, int nparts, const float* zt, float* lse, float* row_loss,
                      float* lse_out, long long N, hipStream_t s);
 int launch_loss_mean(const float* row_loss, float* loss, long long N, hipStream_t s);
-// out[0..n) = beta * out + sum_{s < nsplit} part[s * stride + i]; optional bf16 copy out_bf
-// C[b][i][j] = C[b][j][i] for i > j (n x n matrices, row stride ld, batch stride stride)
-int launch_sym_mirror(void* C, int is_f32, int n, long long ld, long long stride, int count, hipStream_t s);
+// C[b][i][j] = C[b][j][i] for i > j (bf16 n x n matrices, row stride ld, batch stride stride)
+int launch_sym_mirror(uint16_t* C, int n, long long ld, long long stride, int count, hipStream_t s);
+// out[0..n) = beta * out + sum_{s < nsplit} part[s * stride + i]; optional bf16 copy out_bf;
+// out nullable (then beta 0 and out_bf given)
 int launch_splitk_reduce(const float* part, int nsplit, long long stride, float* out, uint16_t* out_bf, long long n,
                          float beta, hipStream_t s);
 
