@@ -552,13 +552,16 @@ __global__ void ns_init_kernel(const float* __restrict__ src, const float* __res
       }
     }
   } else {
-    for (int e = threadIdx.x; e < 64 * 64; e += 256) {
-      const int ii = e / 64, jj = e % 64;
+    // 4 consecutive elements per thread (ls % 8 == 0: rows of 16-byte chunks)
+    for (int e = threadIdx.x; e < 64 * 16; e += 256) {
+      const int ii = e / 16, jj = (e % 16) * 4;
       const int gi = i0 + ii, gj = j0 + jj;
       if (gi < lr && gj < ls) {
-        const float v = in[(long long)gi * ls + gj] * inv;
-        if (X) out[(long long)gi * ls + gj] = v;
-        outb[(long long)gi * ls + gj] = f2bf(v);
+        const long long o = (long long)gi * ls + gj;
+        float4 v = *reinterpret_cast<const float4*>(in + o);
+        v.x *= inv; v.y *= inv; v.z *= inv; v.w *= inv;
+        if (X) *reinterpret_cast<float4*>(out + o) = v;
+        *reinterpret_cast<uint2*>(outb + o) = make_uint2(pack_bf2(v.x, v.y), pack_bf2(v.z, v.w));
       }
     }
   }
