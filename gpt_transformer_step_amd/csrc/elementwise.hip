@@ -535,20 +535,25 @@ __global__ void ns_init_kernel(const float* __restrict__ src, const float* __res
   const int i0 = blockIdx.y * 64, j0 = blockIdx.x * 64;
   __shared__ float tile[64][65];
   if (TR) {
-    // in is [ls rows? no: in is [rows, cols] = [ls, lr]; out[i][j] = in[j][i]
-    for (int e = threadIdx.x; e < 64 * 64; e += 256) {
-      const int jj = e / 64, ii = e % 64;  // read in[j0+jj][i0+ii] coalesced along ii
+    // in is [rows, cols] = [ls, lr]; out[i][j] = in[j][i]; 4 consecutive
+    // elements per thread on both sides (lr, ls multiples of 8)
+    for (int e = threadIdx.x; e < 64 * 16; e += 256) {
+      const int jj = e / 16, ii = (e % 16) * 4;  // read in[j0+jj][i0+ii ..] coalesced along ii
       const int gj = j0 + jj, gi = i0 + ii;
-      tile[jj][ii] = (gj < ls && gi < lr) ? in[(long long)gj * lr + gi] : 0.f;
+      float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (gj < ls && gi < lr) v = *reinterpret_cast<const float4*>(in + (long long)gj * lr + gi);
+      tile[jj][ii] = v.x; tile[jj][ii + 1] = v.y; tile[jj][ii + 2] = v.z; tile[jj][ii + 3] = v.w;
     }
     __syncthreads();
-    for (int e = threadIdx.x; e < 64 * 64; e += 256) {
-      const int ii = e / 64, jj = e % 64;
+    for (int e = threadIdx.x; e < 64 * 16; e += 256) {
+      const int ii = e / 16, jj = (e % 16) * 4;
       const int gi = i0 + ii, gj = j0 + jj;
       if (gi < lr && gj < ls) {
-        const float v = tile[jj][ii] * inv;
-        if (X) out[(long long)gi * ls + gj] = v;
-        outb[(long long)gi * ls + gj] = f2bf(v);
+        const long long o = (long long)gi * ls + gj;
+        const float4 v = make_float4(tile[jj][ii] * inv, tile[jj + 1][ii] * inv, tile[jj + 2][ii] * inv,
+                                     tile[jj + 3][ii] * inv);
+        if (X) *reinterpret_cast<float4*>(out + o) = v;
+        *reinterpret_cast<uint2*>(outb + o) = make_uint2(pack_bf2(v.x, v.y), pack_bf2(v.z, v.w));
       }
     }
   } else {
