@@ -1148,7 +1148,7 @@ namespace {
 constexpr int kFrobBlocks = 64;
 
 struct MuonWS {
-  size_t partial, X, Xb0, Xb1, Ab, Bb, gpart, nm_part, nm_scale, total;
+  size_t partial, Xb0, Xb1, Ab, Bb, gpart, nm_part, nm_scale, total;
 };
 
 // k-splits of the Gram products X^T X (a few output tiles, long K)
@@ -1166,7 +1166,6 @@ MuonWS muon_layout(int count, int rows, int cols) {
   const size_t n = (size_t)count * rows * cols;
   const size_t sm = (size_t)std::min(rows, cols);
   m.partial = take((size_t)count * kFrobBlocks * 4);
-  m.X = take(n * 4);
   m.Xb0 = take(n * 2);
   m.Xb1 = take(n * 2);
   m.Ab = take((size_t)count * sm * sm * 2);
@@ -1223,7 +1222,6 @@ int muon_impl(float* Wt, uint16_t* W_bf16, const float* Gm, float* M, float* O_o
 
   const float* src = M ? M : Gm;
   float* partial = at<float>(ws, m.partial);
-  float* X = at<float>(ws, m.X);
   uint16_t* Xb[2] = {at<uint16_t>(ws, m.Xb0), at<uint16_t>(ws, m.Xb1)};
   uint16_t* Ab = at<uint16_t>(ws, m.Ab);
   uint16_t* Bb = at<uint16_t>(ws, m.Bb);
@@ -1285,8 +1283,9 @@ int muon_impl(float* Wt, uint16_t* W_bf16, const float* Gm, float* M, float* O_o
       if (sym) TRY(launch_sym_mirror(Bb, sm, sm, sA, count, s));
     }
     {
-      // X = a X + X B, X kept in bf16 (as the iteration's products read it);
-      // the last one in fp32 for the apply
+      // X = a X + X B, X kept in bf16 (as the iteration's products read it;
+      // the orthogonalised update leaves in bf16): the polynomial's epilogue
+      // form, beta X + (X B)
       GemmArgs a;
       ProfScope ps_(P_NS_UPDATE, s);
       a.M = lrow; a.N = sm; a.K = sm; a.batch = count;
@@ -1294,12 +1293,12 @@ int muon_impl(float* Wt, uint16_t* W_bf16, const float* Gm, float* M, float* O_o
       a.B = Bb; a.ldb = sm; a.sB = sA; a.b_kcontig = 0;
       a.aux = Xb[cur]; a.ldaux = sm; a.sAux = sX;
       a.beta = ca;
-      const bool last = it + 1 == ns_steps;
-      a.C = last ? static_cast<void*>(X) : static_cast<void*>(Xb[cur ^ 1]); a.ldc = sm; a.sC = sX;
-      TRY(gemm_bf16(a, last ? EPI_NS_UPD : EPI_NS_POLY, s));
+      a.C = Xb[cur ^ 1]; a.ldc = sm; a.sC = sX;
+      TRY(gemm_bf16(a, EPI_NS_POLY, s));
     }
     cur ^= 1;
   }
+  const uint16_t* X = Xb[cur];  // the last update's output
   const float* nsc = nullptr;
   if (nm) {
     ProfScope ps_(P_MUON_ELEMWISE, s);

@@ -581,16 +581,17 @@ constexpr int kNmRows = 256;  // stored rows per workgroup of the column statist
 
 // part[w] = sum of squares of stored row w (all matrices' rows in sequence);
 // one wave per row, 16-byte loads (s % 4 == 0)
-__global__ void __launch_bounds__(256) nm_rowsq_kernel(const float* __restrict__ X, float* __restrict__ part, int sm,
-                                                       long long nrows) {
+__global__ void __launch_bounds__(256) nm_rowsq_kernel(const uint16_t* __restrict__ X, float* __restrict__ part,
+                                                       int sm, long long nrows) {
   const int lane = threadIdx.x & 63;
   const long long w = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (w >= nrows) return;
-  const float* x = X + w * sm;
+  const uint16_t* x = X + w * sm;
   float acc = 0.f;
   for (int c = lane * 4; c < sm; c += 256) {
-    const float4 v = *reinterpret_cast<const float4*>(x + c);
-    acc += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+    const uint2 q = *reinterpret_cast<const uint2*>(x + c);
+    const float a = lo_bf(q.x), b = hi_bf(q.x), e = lo_bf(q.y), f = hi_bf(q.y);
+    acc += a * a + b * b + e * e + f * f;
   }
   acc = wave_sum(acc);
   if (lane == 0) part[w] = acc;
@@ -598,7 +599,7 @@ __global__ void __launch_bounds__(256) nm_rowsq_kernel(const float* __restrict__
 
 // part[(b nch + ch) s + c] = sum over stored rows ch*kNmRows .. of X[b][r][c]^2;
 // a workgroup covers 64 columns (one per lane) and 4 interleaved row groups
-__global__ void __launch_bounds__(256) nm_colsq_kernel(const float* __restrict__ X, float* __restrict__ part, int l,
+__global__ void __launch_bounds__(256) nm_colsq_kernel(const uint16_t* __restrict__ X, float* __restrict__ part, int l,
                                                        int sm, int nch) {
   const int b = blockIdx.z, ch = blockIdx.y;
   const int lane = threadIdx.x & 63, g = threadIdx.x >> 6;
@@ -606,9 +607,9 @@ __global__ void __launch_bounds__(256) nm_colsq_kernel(const float* __restrict__
   const int r0 = ch * kNmRows, r1 = min(l, r0 + kNmRows);
   float acc = 0.f;
   if (c < sm) {
-    const float* x = X + (long long)b * l * sm + c;
+    const uint16_t* x = X + (long long)b * l * sm + c;
     for (int r = r0 + g; r < r1; r += 4) {
-      const float v = x[(long long)r * sm];
+      const float v = bf2f(x[(long long)r * sm]);
       acc += v * v;
     }
   }
@@ -658,11 +659,11 @@ __global__ void __launch_bounds__(256) nm_finalize_kernel(const float* __restric
 // output tiles over W [rows, cols]; X oriented [l, s] (transposed when TR);
 // nsc (nullable): NorMuon scale per row (nm_rows) or per column of W
 template <bool TR, bool VEC>
-__global__ void muon_apply_kernel(const float* __restrict__ X, float* __restrict__ W, uint16_t* __restrict__ Wb,
+__global__ void muon_apply_kernel(const uint16_t* __restrict__ X, float* __restrict__ W, uint16_t* __restrict__ Wb,
                                   float* __restrict__ O_out, int rows, int cols, float lr, float wd,
                                   const float* __restrict__ nsc, int nm_rows) {
   const int b = blockIdx.z;
-  const float* x = X + (long long)b * rows * cols;
+  const uint16_t* x = X + (long long)b * rows * cols;
   const long long base = (long long)b * rows * cols;
   const int r0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
   __shared__ float tile[64][65];
@@ -671,14 +672,14 @@ __global__ void muon_apply_kernel(const float* __restrict__ X, float* __restrict
     for (int e = threadIdx.x; e < 64 * 64; e += 256) {
       const int cc = e / 64, rr = e % 64;
       const int gc = c0 + cc, gr = r0 + rr;
-      tile[cc][rr] = (gc < cols && gr < rows) ? x[(long long)gc * rows + gr] : 0.f;
+      tile[cc][rr] = (gc < cols && gr < rows) ? bf2f(x[(long long)gc * rows + gr]) : 0.f;
     }
     __syncthreads();
   }
   const float decay = 1.f - lr * wd;
   if (VEC) {
     // 4 consecutive columns per thread: cols % 8 == 0 and 16-byte aligned
-    // X, W, O_out (8-byte aligned Wb), checked by the launcher
+    // W, O_out (8-byte aligned X, Wb), checked by the launcher
     for (int e = threadIdx.x; e < 64 * 16; e += 256) {
       const int rr = e / 16, c4 = (e % 16) * 4;
       const int gr = r0 + rr, gc = c0 + c4;
@@ -688,8 +689,8 @@ __global__ void muon_apply_kernel(const float* __restrict__ X, float* __restrict
         if (TR) {
           o[0] = tile[c4][rr]; o[1] = tile[c4 + 1][rr]; o[2] = tile[c4 + 2][rr]; o[3] = tile[c4 + 3][rr];
         } else {
-          const float4 v = *reinterpret_cast<const float4*>(x + idx);
-          o[0] = v.x; o[1] = v.y; o[2] = v.z; o[3] = v.w;
+          const uint2 q = *reinterpret_cast<const uint2*>(x + idx);
+          o[0] = lo_bf(q.x); o[1] = hi_bf(q.x); o[2] = lo_bf(q.y); o[3] = hi_bf(q.y);
         }
         if (nsc) {
 #pragma unroll
@@ -712,7 +713,7 @@ __global__ void muon_apply_kernel(const float* __restrict__ X, float* __restrict
     const int gr = r0 + rr, gc = c0 + cc;
     if (gr < rows && gc < cols) {
       const long long idx = (long long)gr * cols + gc;
-      float o = TR ? tile[cc][rr] : x[idx];
+      float o = TR ? tile[cc][rr] : bf2f(x[idx]);
       if (nsc) o *= nm_rows ? nsc[(long long)b * rows + gr] : nsc[(long long)b * cols + gc];
       if (O_out) O_out[base + idx] = o;
       if (W) {
@@ -963,7 +964,7 @@ int launch_adamw(float* W, uint16_t* Wb, const float* G, float* M, float* V, lon
   return 0;
 }
 
-int launch_normuon_scale(const float* X, float* part, float* V, float* scale, int count, int rows, int cols,
+int launch_normuon_scale(const uint16_t* X, float* part, float* V, float* scale, int count, int rows, int cols,
                          int per_row, float beta2, float eps, hipStream_t s) {
   const bool tr = rows < cols;
   const int l = tr ? cols : rows, sm = tr ? rows : cols;
@@ -989,12 +990,12 @@ long long normuon_part_floats(int count, int rows, int cols) {
   return (long long)count * std::max<long long>(l, (long long)sm * ((l + kNmRows - 1) / kNmRows));
 }
 
-int launch_muon_apply(const float* X, float* W, uint16_t* Wb, float* O_out, int count, int rows, int cols,
+int launch_muon_apply(const uint16_t* X, float* W, uint16_t* Wb, float* O_out, int count, int rows, int cols,
                       float lr, float wd, const float* nsc, int nm_rows, hipStream_t s) {
   const bool tr = rows < cols;
   dim3 grid((cols + 63) / 64, (rows + 63) / 64, count);
   auto al = [](const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; };
-  const bool vec = cols % 4 == 0 && al(X, 16) && al(W, 16) && al(O_out, 16) && al(Wb, 8);
+  const bool vec = cols % 4 == 0 && al(X, 8) && al(W, 16) && al(O_out, 16) && al(Wb, 8);
 #define GS_MA(T_, V_) hipLaunchKernelGGL((muon_apply_kernel<T_, V_>), grid, dim3(256), 0, s, X, W, Wb, O_out, rows, \
                                          cols, lr, wd, nsc, nm_rows)
   if (tr) {

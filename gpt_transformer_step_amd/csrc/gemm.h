@@ -13,9 +13,8 @@ enum Epi {
   EPI_RESID,       // C f32 += v (residual stream add; one writer per element)
   EPI_RELU2,       // C bf16 = max(v, 0)^2
   EPI_DRELU2,      // C bf16 = v * 2 sqrt(aux_bf16)       (ReLU^2 backward from a = relu(u)^2)
-  EPI_NS_POLY,     // C bf16 = beta * aux_bf16 + v        (B = b A + c A A, alpha = c, beta = b)
-  EPI_NS_UPD,      // C f32 = beta * aux_bf16 + v  (the last X = a X + X B; the earlier ones
-                   // are EPI_NS_POLY with aux = X)
+  EPI_NS_POLY,     // C bf16 = beta * aux_bf16 + v        (B = b A + c A A, alpha = c, beta = b;
+                   // and X = a X + X B with aux = X, beta = a)
   EPI_CE_FWD,      // per-row partial (max mx, sum exp) over each wave's columns + target logit;
                    // with C given, also C fp16 = exp(v - mx), kept for the backward
   EPI_F16,         // C fp16 = v (the stored exponentials of EPI_CE_FWD; not launched alone)

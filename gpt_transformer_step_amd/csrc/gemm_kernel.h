@@ -286,21 +286,7 @@ __device__ __forceinline__ void epi4(const GemmArgs& p, int bi, int m, int n, co
           if (p.amax) amx = fmaxf(amx, fabsf(bf2f(b)));
         }
     }
-  } else if constexpr (EPI == EPI_NS_UPD) {
-    // aux words of the 4 columns prefetched (have_c: cpre.x / cpre.y hold them)
-    float* C = reinterpret_cast<float*>(p.C) + (long long)bi * p.sC + (long long)m * p.ldc + n;
-    if (full) {
-      uint2 w;
-      if (have_c) w = make_uint2(__float_as_uint(cpre.x), __float_as_uint(cpre.y));
-      else w = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(p.aux) + (long long)bi * p.sAux +
-                                                (long long)m * p.ldaux + n);
-      st_nt(C, make_float4(v[0] + p.beta * lo_bf(w.x), v[1] + p.beta * hi_bf(w.x), v[2] + p.beta * lo_bf(w.y),
-                           v[3] + p.beta * hi_bf(w.y)));
-    } else {
-      const uint16_t* a = reinterpret_cast<const uint16_t*>(p.aux) + (long long)bi * p.sAux + (long long)m * p.ldaux + n;
-      for (int j = 0; j < 4; ++j)
-        if (n + j < p.N) C[j] = v[j] + p.beta * bf2f(a[j]);
-    }
+
   }
 }
 
@@ -924,10 +910,8 @@ __global__ void __launch_bounds__((Cfg<BM, BN>::NT), 1) gemm_kernel(GemmArgs p) 
     // and fp32 with beta) fetch a row block's values in one burst before
     // staging it: read one at a time between the stores, each load would wait
     // out the stores before it (the compiler cannot tell the addresses apart)
-    // (the last Newton-Schulz update reads the bf16 X the same way: 8 bytes
-    // per 4 columns, carried in the low half of the prefetch registers)
-    constexpr bool READS_C = SE == EPI_RESID || SE == EPI_NS_UPD || SE == EPI_F32;
-    const bool cread = READS_C && (SE != EPI_F32 || p.beta != 0.f) && (SE != EPI_NS_UPD || p.ldaux % 4 == 0);
+    constexpr bool READS_C = SE == EPI_RESID || SE == EPI_F32;
+    const bool cread = READS_C && (SE != EPI_F32 || p.beta != 0.f);
     float4 cpre[READS_C ? NIT : 1];
     auto fetch_c = [&](int i) {
       if constexpr (READS_C) {
@@ -938,17 +922,8 @@ __global__ void __launch_bounds__((Cfg<BM, BN>::NT), 1) gemm_kernel(GemmArgs p) 
           const int m = m0 + wm * WM + i * 32 + q / CH;
           const int n = n0 + wn * WN + (q % CH) * 4;
           float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
-          if constexpr (SE == EPI_NS_UPD) {
-            const uint16_t* ab = reinterpret_cast<const uint16_t*>(p.aux) + (long long)bi * p.sAux;
-            if (m < p.M && n + 3 < p.N) {
-              const uint2 w = *reinterpret_cast<const uint2*>(ab + (long long)m * p.ldaux + n);
-              x.x = __uint_as_float(w.x);
-              x.y = __uint_as_float(w.y);
-            }
-          } else {
-            const float* Cb = reinterpret_cast<const float*>(p.C) + (long long)bi * p.sC + coff;
-            if (m < p.M && n + 3 < p.N) x = *reinterpret_cast<const float4*>(Cb + (long long)m * p.ldc + n);
-          }
+          const float* Cb = reinterpret_cast<const float*>(p.C) + (long long)bi * p.sC + coff;
+          if (m < p.M && n + 3 < p.N) x = *reinterpret_cast<const float4*>(Cb + (long long)m * p.ldc + n);
           cpre[it] = x;
         }
       }

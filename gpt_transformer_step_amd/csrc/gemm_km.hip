@@ -10,7 +10,6 @@ int gemm_bf16_km(const GemmArgs& a, int epi, hipStream_t s) {
     case EPI_BF16: return launch_tiles<true, false, EPI_BF16>(a, s);
     case EPI_DRELU2: return launch_tiles<true, false, EPI_DRELU2>(a, s);
     case EPI_NS_POLY: return launch_tiles<true, false, EPI_NS_POLY>(a, s);
-    case EPI_NS_UPD: return launch_tiles<true, false, EPI_NS_UPD>(a, s);
     default:
       set_error("gemm_bf16: epilogue not built for this operand layout");
       return -5;
