@@ -145,7 +145,9 @@ def check_scalars(got, exact, names, noise=SCALAR_NOISE, cos_min=0.999):
         r = exact["grads"][name]
         bar = np.maximum(1e-2 * np.abs(r), 4.0 * noise * exact["grad_abs"][name])
         err = np.abs(g - r)
-        say(f"  {name}: max |err| / bar {float(np.max(err / bar)):.3f}; bar / |grad| "
+        # (a scalar whose feature is off has gradient 0 and bar 0 on both sides)
+        ratio = np.where(bar > 0, err / np.where(bar > 0, bar, 1.0), np.where(err > 0, np.inf, 0.0))
+        say(f"  {name}: max |err| / bar {float(np.max(ratio)):.3f}; bar / |grad| "
             f"{float(np.max(bar / np.maximum(np.abs(r), 1e-30))):.3f} (gpu {g[:2]}, oracle {r[:2]})")
         if np.any(err > bar):
             bad.append(f"{name}: err {err} bar {bar}")
