@@ -19,6 +19,11 @@ long long gemm_amax_slots(const GemmArgs& a) {
 
 int gemm_bf16(const GemmArgs& a, int epi, hipStream_t s) {
   if (a.M <= 0 || a.N <= 0 || a.batch <= 0) return 0;
+  // the cross-entropy epilogue takes the row max on the unscaled products
+  if (epi == EPI_CE_FWD && !(a.alpha > 0.f)) {
+    set_error("gemm: the cross-entropy epilogue needs alpha > 0");
+    return -1;
+  }
   if (a.a_kcontig && a.b_kcontig) return gemm_bf16_kk(a, epi, s);
   if (a.a_kcontig) return gemm_bf16_km(a, epi, s);
   if (a.b_kcontig) return gemm_bf16_mk(a, epi, s);

@@ -50,6 +50,37 @@ constexpr int f8_fmt_a(int f8) { return (f8 - 1) & 1; }
 constexpr int f8_fmt_b(int f8) { return (f8 - 1) >> 1; }
 // K elements per LDS stage (128 bytes per row)
 constexpr int stage_k(int f8) { return f8 ? 128 : 64; }
+
+// max of three finite floats in one instruction (fmaxf quiets NaN operands
+// first, one more instruction per operand)
+__device__ __forceinline__ float fmax3(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+
+// element idx = 16 j + e of a lane's accumulator row acc[0..TN)[0..16), by a
+// select tree over the index bits (per-lane index, no dynamic register access)
+template <int TN>
+__device__ __forceinline__ float pick_acc(const f32x16_t (&row)[TN], int idx) {
+  static_assert((TN & (TN - 1)) == 0 && TN <= 4, "TN: 1, 2 or 4");
+  const int j = idx >> 4;
+  float v[16];
+#pragma unroll
+  for (int e = 0; e < 16; ++e) {
+    float x = row[0][e];
+#pragma unroll
+    for (int jj = 1; jj < TN; ++jj) x = j == jj ? row[jj][e] : x;
+    v[e] = x;
+  }
+#pragma unroll
+  for (int h = 8; h >= 1; h >>= 1) {
+    const bool hi = (idx & h) != 0;
+#pragma unroll
+    for (int k = 0; k < h; ++k) v[k] = hi ? v[k + h] : v[k];
+  }
+  return v[0];
+}
 // Workgroup shape per tile size: 256x256 tiles use 8 waves (two per SIMD, so
 // one wave's LDS waits overlap the other's MFMAs), 128x128 tiles use 4.  The
 // waves form a (NT/128) x 2 grid; each wave owns 64 rows and BN/2 columns.
@@ -825,6 +856,9 @@ __global__ void __launch_bounds__((Cfg<BM, BN>::NT), 1) gemm_kernel(GemmArgs p) 
   if constexpr (EPI == EPI_CE_FWD) {
     // Per row: max and sum of exp over this wave's WN columns, merged with
     // the partner lane (lane ^ 32) that holds the other half of the columns.
+    // Element (j, e) of a lane is column cb + 4 lh + 32 j + 8 (e >> 2) + (e & 3).
+    const int cb = n0 + wn * WN;
+    const bool fulln = cb + WN <= p.N;  // wave-uniform: every column of the wave exists
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
       const int m = m0 + wm * WM + i * 32 + lr;
@@ -832,6 +866,38 @@ __global__ void __launch_bounds__((Cfg<BM, BN>::NT), 1) gemm_kernel(GemmArgs p) 
       if (m < p.M) {
         const int row_b = m / p.row_T, row_t = m - row_b * p.row_T;
         tgt = p.row_i[(long long)row_b * (p.row_T + 1) + row_t + 1] - p.col_offset;
+      }
+      if (fulln) {
+        // No column checks.  The max is taken on the raw accumulators
+        // (alpha > 0) with three-operand maxes (finite values: no NaN
+        // quieting), the exponentials as exp2 with alpha log2(e) folded in,
+        // and the target logit is picked by a select tree over its element
+        // index instead of a compare and a store per element.
+        float mr = acc[i][0][0];
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+          for (int e = (j == 0 ? 1 : 0); e < 16; e += 2)
+            mr = (e + 1 < 16) ? fmax3(mr, acc[i][j][e], acc[i][j][e + 1]) : fmaxf(mr, acc[i][j][e]);
+        mr = fmaxf(mr, __shfl_xor(mr, 32, 64));
+        const int rel = tgt - cb - 4 * lh;  // 32 j + 8 g + u when this lane holds the target
+        if (m < p.M && rel >= 0 && rel < WN && (rel & 4) == 0)
+          p.zt[m] = pick_acc<TN>(acc[i], ((rel >> 5) << 4) | ((rel >> 1) & 12) | (rel & 3)) * p.alpha;
+        const float a2 = p.alpha * 1.4426950408889634f, ms = mr * a2;
+        float s = 0.f;
+        const bool keep = p.C != nullptr;  // launch-uniform: the exponentials are stored
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const float pe = __builtin_amdgcn_exp2f(__builtin_fmaf(acc[i][j][e], a2, -ms));
+            s += pe;
+            if (keep) acc[i][j][e] = pe;
+          }
+        s += __shfl_xor(s, 32, 64);
+        if (lh == 0 && m < p.M) reinterpret_cast<float2*>(p.part)[(long long)m * p.nparts + tile_n * 2 + wn] =
+            make_float2(mr * p.alpha, s);
+        continue;
       }
       float mx = -INFINITY;
 #pragma unroll
