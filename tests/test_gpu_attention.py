@@ -78,8 +78,9 @@ def test_attention_fwd_bwd(B, Bn, H, T):
 
 
 def test_attention_full_size_sampled(B):
-    """depth-20 shape (32 sequences x 10 heads x 2048): the oracle checks two
-    sampled (sequence, head) pairs; every output is checked finite."""
+    """depth-20 shape (32 sequences x 10 heads x 2048), forward and backward
+    as the step launches them: the oracle checks sampled (sequence, head)
+    pairs (out and lse; dq, dk, dv); every output is checked finite."""
     Bn, H, T = 32, 10, 2048
     d = H * 128
     say(f"attention full size B={Bn} H={H} T={T}")
@@ -102,6 +103,33 @@ def test_attention_full_size_sampled(B):
         say(f"  (b={b}, h={h}) out rel_l2 {e:.3e}")
         assert e <= 1e-2
         assert np.abs(lse[b, h].cpu().numpy() - l).max() < 1e-3
+
+    gen.manual_seed(12)
+    dout = torch.randn((Bn * T, d), generator=gen, device="cuda").to(torch.bfloat16)
+    delta = torch.empty((Bn, H, T), dtype=torch.float32, device="cuda")
+    dq_acc = torch.empty((Bn * T, d), dtype=torch.float32, device="cuda")
+    dkv = torch.zeros((Bn * T, 3 * d), dtype=torch.bfloat16, device="cuda")
+    dkvv = dkv.view(torch.int16)
+    B.attention_bwd(qv, qv[:, d:], qv[:, 2 * d:], out, dout, lse, delta, dq_acc, dkvv[:, d:], dkvv[:, 2 * d:],
+                    Bn, H, T, 3 * d, d, 3 * d)
+    torch.cuda.synchronize()
+    assert torch.isfinite(dq_acc).all() and torch.isfinite(dkv.float()).all()
+    for (b, h) in [(0, 0), (13, 4), (31, 9)]:
+        rows = qkv[b * T:(b + 1) * T].float().cpu().numpy().astype(np.float64)
+        q, k, v = (rows[:, o + h * 128: o + (h + 1) * 128][None, None] for o in (0, d, 2 * d))
+        # reference backward on the GPU's own (bf16) output, as the kernels use it
+        y_dev = out[b * T:(b + 1) * T, h * 128:(h + 1) * 128].float().cpu().numpy().astype(np.float64)[None, None]
+        dy = dout[b * T:(b + 1) * T, h * 128:(h + 1) * 128].float().cpu().numpy().astype(np.float64)[None, None]
+        _, l_ref = om.causal_attention(q, k, v)
+        dq_r, dk_r, dv_r = om.causal_attention_bwd(q, k, v, y_dev, dy, l_ref)
+        got = {"dq": dq_acc[b * T:(b + 1) * T, h * 128:(h + 1) * 128],
+               "dk": dkv[b * T:(b + 1) * T, d + h * 128: d + (h + 1) * 128],
+               "dv": dkv[b * T:(b + 1) * T, 2 * d + h * 128: 2 * d + (h + 1) * 128]}
+        for name, ref in (("dq", dq_r), ("dk", dk_r), ("dv", dv_r)):
+            g_np = got[name].float().cpu().numpy()
+            e, c = rel_l2(g_np, ref[0, 0]), cosine(g_np, ref[0, 0])
+            say(f"  (b={b}, h={h}) {name} rel_l2 {e:.3e} cos {c:.6f}")
+            assert e <= 1e-2 and c >= 0.999
 
 
 @pytest.mark.parametrize("Bn,H,Hkv,T,window", [
