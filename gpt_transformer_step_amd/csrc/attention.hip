@@ -359,10 +359,13 @@ attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, 
 #pragma unroll
           for (int e = 0; e < 16; ++e) x[kt * 16 + e] = s[kt][e];
       }
-      float tmax = x[0];
+      // row max as four independent chains of 8 (dependency depth 6, not 16)
+      float t4[4];
 #pragma unroll
-      for (int i = 1; i + 1 < 32; i += 2) tmax = max3(tmax, x[i], x[i + 1]);
-      tmax = fmaxf(tmax, x[31]);
+      for (int j = 0; j < 4; ++j)
+        t4[j] = max3(max3(max3(x[8 * j], x[8 * j + 1], x[8 * j + 2]), x[8 * j + 3], x[8 * j + 4]), x[8 * j + 5],
+                     fmaxf(x[8 * j + 6], x[8 * j + 7]));
+      float tmax = fmaxf(max3(t4[0], t4[1], t4[2]), t4[3]);
       tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64)) * c;
       const bool need = tmax > m + kRescale;
       if (__any(need)) {
@@ -379,13 +382,13 @@ attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, 
       }
       // a row that has seen no visible key yet keeps m = -inf; its p are 0
       const float msafe = m == -INFINITY ? 0.f : m;
-      float psum = 0.f;
+      float ps4[4] = {0.f, 0.f, 0.f, 0.f};  // four independent partial sums
 #pragma unroll
       for (int i = 0; i < 32; ++i) {
         x[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(x[i], c, -msafe));
-        psum += x[i];
+        ps4[i & 3] += x[i];
       }
-      l += psum;
+      l += (ps4[0] + ps4[1]) + (ps4[2] + ps4[3]);
       // O^T += V^T P^T over the 64 keys (4 k-steps of 16)
 #pragma unroll
       for (int st = 0; st < 4; ++st) {
