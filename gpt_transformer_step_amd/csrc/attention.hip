@@ -547,17 +547,50 @@ attn_bwd_kv8_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
 
+    // The lane's LDS byte offsets inside a tile, all below 2^16, two per
+    // register, computed once: o16[k] the fragment reads of row lr at k-steps
+    // 2k and 2k+1; otr[et] the two transpose reads of frag_tr(., et, 0, .)
+    // (k-step s2 adds 16 rows, 4096 bytes).  Opaque to the compiler, so it
+    // keeps these 8 registers instead of recomputing some 90 offset
+    // instructions per tile (all 16 offsets unpacked do not fit beside the
+    // accumulators).
+    uint32_t o16[4], otr[4];
+#pragma unroll
+    for (int k2 = 0; k2 < 4; ++k2) o16[k2] = toff(lr, 4 * k2 + lh) | (toff(lr, 4 * k2 + 2 + lh) << 16);
+    {
+      const int g = lane >> 4, m = lane & 15;
+      const int r = 4 * (g >> 1) + (m >> 2);
+#pragma unroll
+      for (int et = 0; et < 4; ++et) {
+        const int i = et * 32 + 16 * (g & 1) + 4 * (m & 3);
+        const int sub = (i & 7) * 2;
+        otr[et] = (toff(r, i >> 3) + sub) | ((toff(r + 8, i >> 3) + sub) << 16);
+      }
+    }
+#pragma unroll
+    for (int k2 = 0; k2 < 4; ++k2) asm volatile("" : "+v"(o16[k2]), "+v"(otr[k2]));
+    const char* sk_w = s_k + __builtin_amdgcn_readfirstlane(wave) * 32 * 256;  // the wave's 32 keys
+    auto off16 = [&](int ks) -> int {
+      const uint32_t w = o16[ks >> 1];
+      return (ks & 1) ? (int)(w >> 16) : (int)(w & 0xffffu);
+    };
+    auto frag_o = [&](const char* base, int off) -> bf16x8_t { return *reinterpret_cast<const bf16x8_t*>(base + off); };
+    auto frag_tr_o = [&](const char* base, int et, int s2) -> bf16x8_t {
+      const uint32_t w = otr[et];
+      const v4s_t a = tr_read(base, (int)(w & 0xffffu) + 4096 * s2);
+      const v4s_t b = tr_read(base, (int)(w >> 16) + 4096 * s2);
+      bf16x8_t f;
+      f[0] = a[0]; f[1] = a[1]; f[2] = a[2]; f[3] = a[3];
+      f[4] = b[0]; f[5] = b[1]; f[6] = b[2]; f[7] = b[3];
+      return f;
+    };
+
     for (int it0 = 0; it0 < n_it; it0 += K8_NS)
 #pragma unroll
     for (int cur = 0; cur < K8_NS; ++cur) {
       const int it = it0 + cur;
       if (it >= n_it) break;  // block-uniform
       const char* st = stage(cur);
-      // an opaque copy of the lane index: the per-lane LDS offsets below are
-      // recomputed each tile instead of being kept live across the loop
-      int lane_o = lane;
-      asm volatile("" : "+v"(lane_o));
-      const int lr = lane_o & 31, lh = lane_o >> 5;
       // tile it + K8_NS - 1 into the stage read during tile it - 1
       issue(it + K8_NS - 1, (cur + K8_NS - 1) % K8_NS);
       const int q0 = qt_of(it) * KV_Q;
@@ -570,11 +603,11 @@ attn_bwd_kv8_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
         for (int e = 0; e < 16; ++e) { sacc[e] = 0.f; dpacc[e] = 0.f; }
 #pragma unroll
         for (int ks = 0; ks < 8; ++ks)
-          sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag16(st + K8_QN, lr, ks * 2 + lh),
-                                                         frag16(s_k, wave * 32 + lr, ks * 2 + lh), sacc, 0, 0, 0);
+          sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_o(st + K8_QN, off16(ks)), frag_o(sk_w, off16(ks)), sacc,
+                                                         0, 0, 0);
 #pragma unroll
         for (int ks = 0; ks < 8; ++ks)
-          dpacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag16(st + K8_DN, lr, ks * 2 + lh), fv[ks], dpacc, 0, 0, 0);
+          dpacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_o(st + K8_DN, off16(ks)), fv[ks], dpacc, 0, 0, 0);
         const float* slse = reinterpret_cast<const float*>(st + K8_ST);
         const float* sdel = slse + KV_Q;
 #pragma unroll
@@ -614,10 +647,8 @@ attn_bwd_kv8_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
         for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
           for (int et = 0; et < 4; ++et) {
-            dvt[et] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_tr(st + K8_DN, et, s2, lane_o), fp[s2], dvt[et], 0, 0,
-                                                              0);
-            dkt[et] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_tr(st + K8_QN, et, s2, lane_o), fs[s2], dkt[et], 0, 0,
-                                                              0);
+            dvt[et] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_tr_o(st + K8_DN, et, s2), fp[s2], dvt[et], 0, 0, 0);
+            dkt[et] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_tr_o(st + K8_QN, et, s2), fs[s2], dkt[et], 0, 0, 0);
           }
       }
       // the next tile has landed (only the K8_NS - 2 tiles behind it may be in
