@@ -33,8 +33,8 @@
 //     P = exp(S - lse), dS = P (dP - delta), dV^T += dO^T P, dK^T += Q^T dS;
 //   * dQ (launched first): one workgroup = 128 queries over key tiles of 64,
 //     shaped like the forward: S^T, dP^T recomputed, dQ^T += K^T dS^T; it
-//     also computes delta = rowsum(dO O) of its queries and stores it for the
-//     dK/dV kernel.
+//     also computes delta = rowsum(dO O) of its queries and stores -delta for
+//     the dK/dV kernel (whose dP accumulates onto it).
 //   The dQ kernel recomputes two of the four products; in exchange dQ needs no
 //   fp32 atomics and the result is deterministic.
 
@@ -598,9 +598,13 @@ attn_bwd_kv8_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
       if (q0 + KV_Q - 1 >= wk0 && (window < 0 || q0 <= wk0 + 31 + window)) {
         // the scores first, then dP = dO V^T: P = exp2(S c - lse) needs only
         // the former and runs under the latter (same straight-line block)
+        // dP accumulates onto -delta (stored negated by the dQ kernel), so it
+        // leaves the products as dP - delta
+        const float* slse = reinterpret_cast<const float*>(st + K8_ST);
+        const float* sndel = slse + KV_Q;
         f32x16_t sacc, dpacc;
 #pragma unroll
-        for (int e = 0; e < 16; ++e) { sacc[e] = 0.f; dpacc[e] = 0.f; }
+        for (int e = 0; e < 16; ++e) { sacc[e] = 0.f; dpacc[e] = sndel[8 * (e >> 2) + 4 * lh + (e & 3)]; }
 #pragma unroll
         for (int ks = 0; ks < 8; ++ks)
           sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_o(st + K8_QN, off16(ks)), frag_o(sk_w, off16(ks)), sacc,
@@ -608,8 +612,6 @@ attn_bwd_kv8_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
 #pragma unroll
         for (int ks = 0; ks < 8; ++ks)
           dpacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_o(st + K8_DN, off16(ks)), fv[ks], dpacc, 0, 0, 0);
-        const float* slse = reinterpret_cast<const float*>(st + K8_ST);
-        const float* sdel = slse + KV_Q;
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
           const int ql = 8 * (e >> 2) + 4 * lh + (e & 3);
@@ -639,8 +641,7 @@ attn_bwd_kv8_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
           for (int i = 0; i < 4; ++i) {
             const int e0 = 8 * s2 + 2 * i, e1 = e0 + 1;
             wp[i] = pack_bf2(sacc[e0], sacc[e1]);
-            wd[i] = pack_bf2(sacc[e0] * (dpacc[e0] - sdel[8 * (e0 >> 2) + 4 * lh + (e0 & 3)]),
-                             sacc[e1] * (dpacc[e1] - sdel[8 * (e1 >> 2) + 4 * lh + (e1 & 3)]));
+            wd[i] = pack_bf2(sacc[e0] * dpacc[e0], sacc[e1] * dpacc[e1]);
           }
         }
 #pragma unroll
@@ -743,7 +744,7 @@ attn_bwd_q_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k
   const float lse2 = myq < T ? (FUSE ? lse[(long long)bh * T + myq] : lse[(long long)bh * T + myq] * kLog2e) : INFINITY;
   // delta = rowsum(dO * O) of this lane's query: the lane holds half of the
   // dO row (the fragments above), its partner lane ^ 32 the other half; the
-  // dK/dV kernel, launched after this one, reads the stored values
+  // dK/dV kernel, launched after this one, reads the stored values (negated)
   float del;
   {
     float part = 0.f;
@@ -757,7 +758,7 @@ attn_bwd_q_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k
     }
     part += __shfl_xor(part, 32, 64);
     del = myq < T ? part : 0.f;
-    if (lh == 0 && myq < T) delta[(long long)bh * T + myq] = part;
+    if (lh == 0 && myq < T) delta[(long long)bh * T + myq] = -part;  // negated: the dK/dV kernel's dP starts there
   }
 #pragma unroll
   for (int ks = 0; ks < 8; ++ks) {

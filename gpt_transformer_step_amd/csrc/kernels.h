@@ -132,8 +132,8 @@ struct QkNormBwd {
   uint16_t* dq;
   float* amax;  // nullable: per-wave max |stored dq, dk, dv| (attn_bwd_amax_slots of them)
 };
-// one of the two backward kernels, in this order: 0 = dQ (also writes delta = rowsum(dout * out)),
-// 1 = dK/dV (reads delta).  fuse NULL: raw gradients (dq fp32 [N, 128 H], dk bf16), lse in
+// one of the two backward kernels, in this order: 0 = dQ (also writes -rowsum(dout * out) into
+// delta), 1 = dK/dV (reads it).  fuse NULL: raw gradients (dq fp32 [N, 128 H], dk bf16), lse in
 // natural units; else the gradients of the raw heads through the QK-norm and rotary
 // backward, lse in log2 units.
 int launch_attn_bwd_part(int part, const uint16_t* q, const uint16_t* k, const uint16_t* v, long long ld_qkv,

@@ -83,7 +83,7 @@ gpt_status gpt_op_attention_fwd(int32_t batch, int32_t n_head, int32_t n_kv_head
  *   dq_acc fp32, element (b,t,h,e) at dq_acc[(b*T+t) * H*128 + h*128 + e] (written);
  *   dk, dv bf16 in the k/v layout with leading dimension ld_dkv (written; a
  *   key/value head receives the sum over its query heads);
- *   delta: fp32 scratch [B, H, T] (receives rowsum(dout * out)). */
+ *   delta: fp32 scratch [B, H, T] (receives -rowsum(dout * out)). */
 gpt_status gpt_op_attention_bwd(int32_t batch, int32_t n_head, int32_t n_kv_head, int32_t seq_len, int32_t window,
                                 const uint16_t* q, const uint16_t* k, const uint16_t* v, int64_t ld_qkv,
                                 const uint16_t* out, const uint16_t* dout, int64_t ld_out,
