@@ -28,8 +28,8 @@
 //   reference max moves only when a row max exceeds it by 2^8 (P <= 256), so
 //   most tiles skip the O rescale.  K/V tiles of 64 keys, double buffered.
 // Backward, two kernels and no atomics:
-//   * dK/dV: one workgroup = 256 keys (8 waves x 32) over query tiles of 32
-//     streamed through a 4-stage LDS ring: S = Q K^T, dP = dO V^T,
+//   * dK/dV: one workgroup = 128 keys (4 waves x 32), two per CU, over
+//     query tiles of 32 streamed through a 2-stage LDS ring: S = Q K^T, dP = dO V^T,
 //     P = exp(S - lse), dS = P (dP - delta), dV^T += dO^T P, dK^T += Q^T dS;
 //   * dQ (launched first): one workgroup = 128 queries over key tiles of 64,
 //     shaped like the forward: S^T, dP^T recomputed, dQ^T += K^T dS^T; it
@@ -431,31 +431,34 @@ attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, 
 constexpr int KV_Q = 32;  // queries per tile
 
 // ---------------------------------------------------------------------------
-// One workgroup = 256 keys (8 waves x 32)
-// of one (batch, key/value head); Q / dO tiles of 32 queries and their
-// softmax statistics stream through a ring of K8_NS LDS stages filled by
-// direct buffer -> LDS loads issued K8_NS - 1 tiles ahead, so the load
-// latency (a few microseconds under load) is covered by several tiles of
-// MFMAs.  The barrier at the end of a tile waits only for the next tile's
-// loads (vmcnt), not for the ones in flight behind it.  Buffer loads take a
+// One workgroup = 128 keys (4 waves x 32) of one (batch, key/value head),
+// two workgroups per CU; Q / dO tiles of 32 queries and their softmax
+// statistics stream through a ring of K8_NS LDS stages filled by direct
+// buffer -> LDS loads issued K8_NS - 1 tiles ahead.  Two independent
+// workgroups on a CU (one wave of each per SIMD) drift apart between their
+// barriers, so one's exponentials and LDS reads run under the other's MFMAs;
+// with one workgroup of 256 keys and a 4-stage ring every wave of a SIMD sat
+// in the same phase (18.6 against 22.7 ms per d20 step).  The end-of-tile
+// barrier waits for the next tile's loads (vmcnt).  Buffer loads take a
 // scalar base and one 32-bit offset per thread, which keeps the streaming
 // loads' addresses out of the (fully used) vector register budget.
 // ---------------------------------------------------------------------------
-constexpr int K8_KEYS = 256;
-constexpr int K8_NT = 512;
-// LDS: K of the block [256][256 B] and K8_NS ring stages, each its own
+constexpr int K8_KEYS = 128;
+constexpr int K8_NT = 256;
+// LDS: K of the block [128][256 B] and K8_NS ring stages, each its own
 // __shared__ array of Q [32][256 B], dO [32][256 B], lse [32] and delta [32].
 // Separate arrays carry separate alias scopes, so the compiler can tell that
 // an LDS read of one stage does not depend on the direct loads in flight into
 // another (with a single array it waits for all of them before every read).
 // The loop is unrolled by K8_NS so that each copy names its stages statically.
-constexpr int K8_NS = 4;
+constexpr int K8_NS = 2;
 constexpr int K8_QN = 0, K8_DN = KV_Q * 256, K8_ST = 2 * KV_Q * 256;
 constexpr int K8_STAGE = K8_ST + 2 * KV_Q * 4;
 constexpr int K8_TOTAL = K8_KEYS * 256 + K8_NS * K8_STAGE;
-constexpr int K8_LOADS = 3;                         // direct loads per thread per query tile
+constexpr int K8_LOADS = 2 * (KV_Q * 16 / K8_NT) + 1;  // direct loads per thread per query tile
 // s_waitcnt immediate (gfx9 encoding): vmcnt = loads of the K8_NS - 2 tiles
-// issued after the next one; expcnt and lgkmcnt not waited for
+// issued after the next one (none with two stages); expcnt and lgkmcnt not
+// waited for
 constexpr int K8_VMCNT = K8_LOADS * (K8_NS - 2);
 constexpr int K8_WAIT = (K8_VMCNT & 15) | ((K8_VMCNT >> 4) << 14) | (7 << 4) | (15 << 8);
 static_assert(K8_TOTAL <= 160 * 1024, "LDS budget");
@@ -466,19 +469,17 @@ static_assert(K8_VMCNT < 64, "vmcnt range");
 // FUSE: dK leaves through the QK-norm + rotary backward (rk: inverse RMS of
 // each key head [N, Hkv]; cs: rotary table), else as the raw gradient.
 template <bool GEN, bool FUSE>
-__global__ void __launch_bounds__(K8_NT, 1)
+__global__ void __launch_bounds__(K8_NT, 2)
 attn_bwd_kv8_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
                     long long ld, const uint16_t* __restrict__ dout, long long ld_out, const float* __restrict__ lse,
                     const float* __restrict__ delta, uint16_t* __restrict__ dk, uint16_t* __restrict__ dv,
                     long long ld_dkv, int H, int Hkv, int T, int window_arg, const float* __restrict__ rk,
                     const float* __restrict__ cs, float* __restrict__ amax) {
-  static_assert(K8_NS == 4, "one __shared__ array per stage below");
+  static_assert(K8_NS == 2, "one __shared__ array per stage below");
   __shared__ __attribute__((aligned(16))) char s_k[K8_KEYS * 256];
   __shared__ __attribute__((aligned(16))) char s_st0[K8_STAGE];
   __shared__ __attribute__((aligned(16))) char s_st1[K8_STAGE];
-  __shared__ __attribute__((aligned(16))) char s_st2[K8_STAGE];
-  __shared__ __attribute__((aligned(16))) char s_st3[K8_STAGE];
-  auto stage = [&](int j) -> char* { return j == 0 ? s_st0 : j == 1 ? s_st1 : j == 2 ? s_st2 : s_st3; };
+  auto stage = [&](int j) -> char* { return j == 0 ? s_st0 : s_st1; };
   const int window = GEN ? window_arg : -1;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, lr = lane & 31, lh = lane >> 5;
   const int bx = xcd_block(gridDim.x), bhk = bx / gridDim.x;
@@ -515,14 +516,22 @@ attn_bwd_kv8_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
     it = min(it, n_it - 1);
     const int hq = hq_of(it), q0 = qt_of(it) * KV_Q;
     char* so = stage(st);
-    tile_dma<KV_Q, K8_NT>(buf_rsrc(q + rowbase * ld + hq * 128, (long long)T * ld * 2), (int)ld, q0, T, so + K8_QN, tid);
+    // an opaque thread index: the load offsets are recomputed per tile
+    // rather than held across the loop
+    int tid_o = tid;
+    asm volatile("" : "+v"(tid_o));
+    tile_dma<KV_Q, K8_NT>(buf_rsrc(q + rowbase * ld + hq * 128, (long long)T * ld * 2), (int)ld, q0, T, so + K8_QN,
+                          tid_o);
     tile_dma<KV_Q, K8_NT>(buf_rsrc(dout + rowbase * ld_out + hq * 128, (long long)T * ld_out * 2), (int)ld_out, q0, T,
-                    so + K8_DN, tid);
+                          so + K8_DN, tid_o);
+    // statistics: the first half of the waves load lse, the second -delta,
+    // PER values each (lanes 0 .. PER - 1)
+    constexpr int NWV = K8_NT / 64, PER = 2 * KV_Q / NWV;
     const int wu = __builtin_amdgcn_readfirstlane(wave);
-    const float* src = (wu < 4 ? lse : delta) + ((long long)b * H + hq) * T;
-    const int qq = min(q0 + 8 * (wu & 3) + (lane & 7), T - 1);
+    const float* src = (wu < NWV / 2 ? lse : delta) + ((long long)b * H + hq) * T;
+    const int qq = min(q0 + PER * (wu % (NWV / 2)) + (lane % PER), T - 1);
     const v4i_t rs = buf_rsrc(src, (long long)T * 4);
-    if (lane < 8) dma4(rs, qq * 4, lds_addr(so + K8_ST + 32 * wu));
+    if (lane < PER) dma4(rs, qq * 4, lds_addr(so + K8_ST + 4 * PER * wu));
   };
 
   if (n_it > 0) {
@@ -687,7 +696,7 @@ attn_bwd_kv8_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
       amx = fmaxf(amx, qknorm_rope_bwd_store(dkt, kScale, kh + (long long)mykey * ld, rk[(rowbase + mykey) * Hkv + hk],
                                              cs, T, mykey, lh, dkr));
   }
-  store_wave_amax(amax, ((long long)blockIdx.x + (long long)gridDim.x * blockIdx.y) * 8 + wave, amx);
+  store_wave_amax(amax, ((long long)blockIdx.x + (long long)gridDim.x * blockIdx.y) * (K8_NT / 64) + wave, amx);
 }
 
 // ---------------------------------------------------------------------------
@@ -868,7 +877,7 @@ attn_bwd_q_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k
 long long attn_fwd_amax_slots(int B, int H, int T) { return (long long)((T + FQ - 1) / FQ) * B * H * 4; }
 
 long long attn_bwd_amax_slots(int B, int H, int Hkv, int T) {
-  return (long long)((T + DQ_Q - 1) / DQ_Q) * B * H * 4 + (long long)((T + K8_KEYS - 1) / K8_KEYS) * B * Hkv * 8;
+  return (long long)((T + DQ_Q - 1) / DQ_Q) * B * H * 4 + (long long)((T + K8_KEYS - 1) / K8_KEYS) * B * Hkv * (K8_NT / 64);
 }
 
 int launch_attn_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, long long ld_qkv, uint16_t* out,
