@@ -702,15 +702,19 @@ attn_bwd_kv8_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
 // ---------------------------------------------------------------------------
 // dQ
 // ---------------------------------------------------------------------------
-constexpr int DQ_Q = 128;
-constexpr int DQ_K = 64;
+// (64 queries and 32-key tiles, four workgroups per CU, needed 276 registers,
+// one wave per SIMD: dQ 14.3 -> 22.9 ms per d20 step)
+constexpr int DQ_Q = 128;                  // queries per workgroup (32 per wave)
+constexpr int DQ_NT = DQ_Q * 2;            // threads
+constexpr int DQ_K = 64;                   // keys per tile
+constexpr int DQ_KT = DQ_K / 32;           // 32-key blocks per tile
 constexpr int DQ_STAGE = 2 * DQ_K * 256;  // K tile + V tile
 
 // FUSE: dQ leaves through the QK-norm + rotary backward as bf16 into dq_bf
 // (row stride ld_dq; rq: inverse RMS of each query head [N, H]; cs: rotary
 // table), else as the raw fp32 gradient into dq_out (row stride 128 H).
 template <bool GEN, bool FUSE>
-__global__ void __launch_bounds__(256, 2)
+__global__ void __launch_bounds__(DQ_NT, 512 / DQ_NT)
 attn_bwd_q_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
                   long long ld, const uint16_t* __restrict__ out, const uint16_t* __restrict__ dout, long long ld_out,
                   const float* __restrict__ lse, float* __restrict__ delta, float* __restrict__ dq_out, int H,
@@ -787,8 +791,8 @@ attn_bwd_q_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k
   const int ntiles = last_key / DQ_K + 1;
   const int j0 = window >= 0 ? max(0, q0 - window) / DQ_K : 0;
   const v4i_t rk = buf_rsrc(kh, (long long)T * ld * 2), rv = buf_rsrc(vh, (long long)T * ld * 2);
-  tile_dma<DQ_K, 256>(rk, (int)ld, j0 * DQ_K, T, smem, tid);
-  tile_dma<DQ_K, 256>(rv, (int)ld, j0 * DQ_K, T, smem + DQ_K * 256, tid);
+  tile_dma<DQ_K, DQ_NT>(rk, (int)ld, j0 * DQ_K, T, smem, tid);
+  tile_dma<DQ_K, DQ_NT>(rv, (int)ld, j0 * DQ_K, T, smem + DQ_K * 256, tid);
   dma_barrier();
 
   for (int j = j0; j < ntiles; ++j) {
@@ -796,41 +800,41 @@ attn_bwd_q_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k
     const char* sv = sk + DQ_K * 256;
     if (j + 1 < ntiles) {
       char* nk = smem + ((j + 1 - j0) & 1) * DQ_STAGE;
-      tile_dma<DQ_K, 256>(rk, (int)ld, (j + 1) * DQ_K, T, nk, tid);
-      tile_dma<DQ_K, 256>(rv, (int)ld, (j + 1) * DQ_K, T, nk + DQ_K * 256, tid);
+      tile_dma<DQ_K, DQ_NT>(rk, (int)ld, (j + 1) * DQ_K, T, nk, tid);
+      tile_dma<DQ_K, DQ_NT>(rv, (int)ld, (j + 1) * DQ_K, T, nk + DQ_K * 256, tid);
     }
     const int key0 = j * DQ_K;
     if (key0 <= wq0 + 31 && (window < 0 || key0 + DQ_K - 1 >= wq0 - window)) {  // wave-uniform
       // the scores first, then dP = dO V^T: the exponentials of the scores
       // (below) only need the former and can run under the latter
-      f32x16_t st2[2], dpt[2];
+      f32x16_t st2[DQ_KT], dpt[DQ_KT];
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
+      for (int kt = 0; kt < DQ_KT; ++kt) {
 #pragma unroll
         for (int e = 0; e < 16; ++e) { st2[kt][e] = 0.f; dpt[kt][e] = 0.f; }
       }
 #pragma unroll
       for (int ks = 0; ks < 8; ++ks)
 #pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
+        for (int kt = 0; kt < DQ_KT; ++kt)
           st2[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag16(sk, kt * 32 + lr, ks * 2 + lh), fq[ks], st2[kt],
                                                             0, 0, 0);
 #pragma unroll
       for (int ks = 0; ks < 8; ++ks)
 #pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
+        for (int kt = 0; kt < DQ_KT; ++kt)
           dpt[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag16(sv, kt * 32 + lr, ks * 2 + lh), fd[ks], dpt[kt],
                                                             0, 0, 0);
       const bool diag = (key0 + DQ_K - 1 > wq0) || (key0 + DQ_K > T) || (window >= 0 && key0 < wq0 + 31 - window);
-      float ds[32];
+      float ds[DQ_KT * 16];
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
+      for (int kt = 0; kt < DQ_KT; ++kt)
 #pragma unroll
         for (int e = 0; e < 16; ++e) ds[kt * 16 + e] = __builtin_amdgcn_exp2f(st2[kt][e] * c - lse2);
       if (diag) {  // wave-uniform: the visibility test only on tiles that need it
         keep_branch();
 #pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
+        for (int kt = 0; kt < DQ_KT; ++kt)
 #pragma unroll
           for (int e = 0; e < 16; ++e) {
             const int key = key0 + kt * 32 + 8 * (e >> 2) + 4 * lh + (e & 3);
@@ -839,11 +843,11 @@ attn_bwd_q_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k
           }
       }
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
+      for (int kt = 0; kt < DQ_KT; ++kt)
 #pragma unroll
         for (int e = 0; e < 16; ++e) ds[kt * 16 + e] *= dpt[kt][e] - del;
 #pragma unroll
-      for (int s4 = 0; s4 < 4; ++s4) {
+      for (int s4 = 0; s4 < 2 * DQ_KT; ++s4) {
         const bf16x8_t fs = pack_perm(ds, s4);
 #pragma unroll
         for (int et = 0; et < 4; ++et)
@@ -869,7 +873,7 @@ attn_bwd_q_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k
         }
     }
   }
-  store_wave_amax(amax, ((long long)blockIdx.x + (long long)gridDim.x * blockIdx.y) * 4 + wave, amx);
+  store_wave_amax(amax, ((long long)blockIdx.x + (long long)gridDim.x * blockIdx.y) * (DQ_NT / 64) + wave, amx);
 }
 
 }  // namespace
@@ -877,7 +881,8 @@ attn_bwd_q_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k
 long long attn_fwd_amax_slots(int B, int H, int T) { return (long long)((T + FQ - 1) / FQ) * B * H * 4; }
 
 long long attn_bwd_amax_slots(int B, int H, int Hkv, int T) {
-  return (long long)((T + DQ_Q - 1) / DQ_Q) * B * H * 4 + (long long)((T + K8_KEYS - 1) / K8_KEYS) * B * Hkv * (K8_NT / 64);
+  return (long long)((T + DQ_Q - 1) / DQ_Q) * B * H * (DQ_NT / 64) +
+         (long long)((T + K8_KEYS - 1) / K8_KEYS) * B * Hkv * (K8_NT / 64);
 }
 
 int launch_attn_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, long long ld_qkv, uint16_t* out,
@@ -906,7 +911,7 @@ int launch_attn_bwd_part(int part, const uint16_t* q, const uint16_t* k, const u
   if (part == 0) {  // dQ, and delta for the dK/dV kernel
     auto kern = fuse ? (gen ? attn_bwd_q_kernel<true, true> : attn_bwd_q_kernel<false, true>)
                      : (gen ? attn_bwd_q_kernel<true, false> : attn_bwd_q_kernel<false, false>);
-    hipLaunchKernelGGL(kern, dim3((T + DQ_Q - 1) / DQ_Q, B * H), dim3(256), 0, s, q, k, v, ld_qkv, out, dout, ld_out,
+    hipLaunchKernelGGL(kern, dim3((T + DQ_Q - 1) / DQ_Q, B * H), dim3(DQ_NT), 0, s, q, k, v, ld_qkv, out, dout, ld_out,
                        lse, delta, dq, H, Hkv, T, window, dq_bf, ld_dkv, rq, cs, amax);
     GS_LAUNCH_CHECK("attn_bwd_q");
   } else {
@@ -914,7 +919,7 @@ int launch_attn_bwd_part(int part, const uint16_t* q, const uint16_t* k, const u
                      : (gen ? attn_bwd_kv8_kernel<true, false> : attn_bwd_kv8_kernel<false, false>);
     hipLaunchKernelGGL(kern, dim3((T + K8_KEYS - 1) / K8_KEYS, B * Hkv), dim3(K8_NT), 0, s, q, k, v, ld_qkv, dout,
                        ld_out, lse, delta, dk, dv, ld_dkv, H, Hkv, T, window, rk, cs,
-                       amax ? amax + (long long)((T + DQ_Q - 1) / DQ_Q) * B * H * 4 : nullptr);
+                       amax ? amax + (long long)((T + DQ_Q - 1) / DQ_Q) * B * H * (DQ_NT / 64) : nullptr);
     GS_LAUNCH_CHECK("attn_bwd_kv");
   }
   return 0;
