@@ -446,7 +446,7 @@ constexpr int KV_Q = 32;  // queries per tile
 constexpr int K8_KEYS = 128;
 constexpr int K8_NT = 256;
 // LDS: K of the block [128][256 B] and K8_NS ring stages, each its own
-// __shared__ array of Q [32][256 B], dO [32][256 B], lse [32] and delta [32].
+// __shared__ array of Q [32][256 B], dO [32][256 B], lse [32] and -delta [32].
 // Separate arrays carry separate alias scopes, so the compiler can tell that
 // an LDS read of one stage does not depend on the direct loads in flight into
 // another (with a single array it waits for all of them before every read).
@@ -464,8 +464,6 @@ constexpr int K8_WAIT = (K8_VMCNT & 15) | ((K8_VMCNT >> 4) << 14) | (7 << 4) | (
 static_assert(K8_TOTAL <= 160 * 1024, "LDS budget");
 static_assert(K8_VMCNT < 64, "vmcnt range");
 
-// ROWS rows of 128 features from row r0 (clamped to T - 1) into a swizzled
-// tile, K8_NT threads: round i, wave w, lane l fills 16-byte slot 512 i + 64 w + l
 // FUSE: dK leaves through the QK-norm + rotary backward (rk: inverse RMS of
 // each key head [N, Hkv]; cs: rotary table), else as the raw gradient.
 template <bool GEN, bool FUSE>
@@ -509,9 +507,9 @@ attn_bwd_kv8_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
 
   auto hq_of = [&](int it) { return GEN ? hk * G + it / nq : hk; };
   auto qt_of = [&](int it) { return GEN ? qt_first + it % nq : qt_first + it; };
-  // the three direct loads of tile it (clamped to the last tile) into stage
-  // st: Q and dO (one 16-byte chunk per thread each) and the statistics
-  // (waves 0-3: lse, waves 4-7: delta, 8 values each from lanes 0-7)
+  // the K8_LOADS direct loads of tile it (clamped to the last tile) into
+  // stage st: Q and dO (two 16-byte chunks per thread each) and the
+  // statistics (one per thread of lanes 0 .. PER - 1, below)
   auto issue = [&](int it, int st) {
     it = min(it, n_it - 1);
     const int hq = hq_of(it), q0 = qt_of(it) * KV_Q;
