@@ -78,7 +78,7 @@ _SIGS = {
     "gpt_profile_read": [_i32, _P(ctypes.c_double), _P(_i32)],
     "gpt_probe_mfma": [_i32, _i32, _i32, _vp, _P(ctypes.c_double), _vp],
     "gpt_op_quantize_fp8": [_vp, _i32, _i64, _i32, _i32, _i32, _vp, _vp, _i64, _vp, _i64, _vp, _vp],
-    "gpt_op_gemm_fp8": [_i32, _i32, _i32, _vp, _i32, _i64, _vp, _i32, _i64, _vp, _i64, _vp, _vp, _f32, _vp],
+    "gpt_op_gemm_fp8": [_i32, _i32, _i32, _vp, _i32, _i32, _i64, _vp, _i32, _i32, _i64, _vp, _i64, _vp, _vp, _f32, _vp],
 }
 
 EXPORTED = ["gpt_status_string", "gpt_last_error", "gpt_abi_version", "gpt_profile_num_categories",
@@ -328,8 +328,11 @@ def quantize_fp8(x, fmt, scale, partial, q=None, qt=None, rows=None, cols=None, 
 
 
 def gemm_fp8(A, fmt_a, B, fmt_b, C, M, N, K, scale_a, scale_b, lda=None, ldb=None, ldc=None, beta=0.0,
-             stream=None):
-    """C fp32 [M, N] = dec(A) dec(B)^T / (scale_a scale_b) (+ beta C); A [M, K]
-    and B [N, K] uint8 codes."""
-    _call("gpt_op_gemm_fp8", M, N, K, _ptr(A), fmt_a, lda or K, _ptr(B), fmt_b, ldb or K, _ptr(C), ldc or N,
-          _ptr(scale_a), _ptr(scale_b), beta, _stream(stream))
+             a_layout=LAYOUT_K, b_layout=LAYOUT_K, stream=None):
+    """C fp32 [M, N] = dec(A) dec(B)^T / (scale_a scale_b) (+ beta C); A and
+    B uint8 codes, logically [M, K] and [N, K]: stored as such (LAYOUT_K) or
+    transposed, [K, M] / [K, N] (LAYOUT_MN)."""
+    lda = lda or (K if a_layout == LAYOUT_K else M)
+    ldb = ldb or (K if b_layout == LAYOUT_K else N)
+    _call("gpt_op_gemm_fp8", M, N, K, _ptr(A), fmt_a, a_layout, lda, _ptr(B), fmt_b, b_layout, ldb, _ptr(C),
+          ldc or N, _ptr(scale_a), _ptr(scale_b), beta, _stream(stream))

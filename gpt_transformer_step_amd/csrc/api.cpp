@@ -261,21 +261,30 @@ extern "C" gpt_status gpt_op_quantize_fp8(const void* x, int32_t x_dtype, int64_
   return GPT_OK;
 }
 
-extern "C" gpt_status gpt_op_gemm_fp8(int32_t M, int32_t N, int32_t K, const uint8_t* A, int32_t fmt_a, int64_t lda,
-                                      const uint8_t* B, int32_t fmt_b, int64_t ldb, float* C, int64_t ldc,
-                                      const float* scale_a, const float* scale_b, float beta, gpt_stream_t stream) {
+extern "C" gpt_status gpt_op_gemm_fp8(int32_t M, int32_t N, int32_t K, const uint8_t* A, int32_t fmt_a,
+                                      int32_t a_layout, int64_t lda, const uint8_t* B, int32_t fmt_b,
+                                      int32_t b_layout, int64_t ldb, float* C, int64_t ldc, const float* scale_a,
+                                      const float* scale_b, float beta, gpt_stream_t stream) {
   if (M < 0 || N < 0 || K < 0) FAIL(GPT_ERR_INVALID_ARG, "negative size");
   if (M == 0 || N == 0) return GPT_OK;
   if (!A || !B || !C || !scale_a || !scale_b) FAIL(GPT_ERR_INVALID_ARG, "NULL pointer");
   if ((fmt_a != GPT_FP8_E4M3 && fmt_a != GPT_FP8_E5M2) || (fmt_b != GPT_FP8_E4M3 && fmt_b != GPT_FP8_E5M2))
     FAIL(GPT_ERR_UNSUPPORTED, "unknown fp8 format");
+  if ((a_layout != GPT_LAYOUT_K_CONTIG && a_layout != GPT_LAYOUT_MN_CONTIG) ||
+      (b_layout != GPT_LAYOUT_K_CONTIG && b_layout != GPT_LAYOUT_MN_CONTIG))
+    FAIL(GPT_ERR_INVALID_ARG, "unknown operand layout");
+  const bool ak = a_layout == GPT_LAYOUT_K_CONTIG, bk = b_layout == GPT_LAYOUT_K_CONTIG;
+  if (!(ak && bk) && !(fmt_a == GPT_FP8_E5M2 && fmt_b == GPT_FP8_E4M3 && !bk))
+    FAIL(GPT_ERR_UNSUPPORTED, "m/n-contiguous fp8 operands: E5M2 x E4M3 with B m/n-contiguous only");
   if (K % 16) FAIL(GPT_ERR_INVALID_ARG, "K must be a multiple of 16");
-  if (lda < K || ldb < K || ldc < N || (lda % 16) || (ldb % 16) || (ldc % 4))
-    FAIL(GPT_ERR_INVALID_ARG, "lda, ldb must be >= K and multiples of 16; ldc >= N and a multiple of 4");
+  if ((!ak && M % 16) || (!bk && N % 16))
+    FAIL(GPT_ERR_INVALID_ARG, "an m/n-contiguous operand needs its rows (M or N) a multiple of 16");
+  if (lda < (ak ? K : M) || ldb < (bk ? K : N) || ldc < N || (lda % 16) || (ldb % 16) || (ldc % 4))
+    FAIL(GPT_ERR_INVALID_ARG, "lda, ldb must cover the contiguous dimension and be multiples of 16; ldc >= N and a multiple of 4");
   if (((uintptr_t)A | (uintptr_t)B | (uintptr_t)C) & 15) FAIL(GPT_ERR_INVALID_ARG, "pointers must be 16-byte aligned");
   GemmArgs a;
   a.M = M; a.N = N; a.K = K;
-  a.A = A; a.lda = lda; a.B = B; a.ldb = ldb;
+  a.A = A; a.lda = lda; a.a_kcontig = ak; a.B = B; a.ldb = ldb; a.b_kcontig = bk;
   a.C = C; a.ldc = ldc; a.beta = beta;
   a.scale_a = scale_a; a.scale_b = scale_b;
   TRY(gemm_fp8(a, EPI_F32, fmt_a, fmt_b, S(stream)));
@@ -405,10 +414,12 @@ inline size_t wgrad_part_elems(int M, int N, int K);
 
 struct Layer {
   size_t h1, r1, qkv, rq, rk, att, lse, h2, r2, act;
-  // fp8 precision only: transposed E4M3 codes of the block-product inputs
-  // (for the weight gradients) and the weights' codes, plain and transposed
-  size_t h1t, attt, h2t, actt;
-  size_t wqkv8, wqkv8t, wo8, wo8t, wfc8, wfc8t, wproj8, wproj8t;
+  // fp8 precision only: E4M3 codes of the block-product inputs [N, cols]
+  // (the forward product's A operand, kept for the weight gradient, which
+  // reads them as stored) and of the weights [out, in] (forward B operand;
+  // the data gradient reads them as stored)
+  size_t h1q, attq, h2q, actq;
+  size_t wqkv8, wo8, wfc8, wproj8;
   // record-model features: bf16 stream before the residual scaling; value-embedding gates [N, Hkv]
   size_t xin, vgate;
 };
@@ -422,9 +433,9 @@ struct WS {
   std::vector<Layer> layer;
   // backward scratch
   size_t g, g_bf, dh, du, dout, delta, dqkv, dz, wpart, emb;
-  // fp8 precision only: codes of the current product input (forward) and of
-  // the current output gradient, plain and transposed (backward); scales
-  size_t xq, dyq, dyqt, scales, qpart;
+  // fp8 precision only: codes of the current output gradient [N, cols]
+  // (backward); scales; amax partials
+  size_t dyq, scales, qpart;
   // record-model features: smear sigmoids [N]; x0 and x_mid [N, d] fp32;
   // backward: gradient reaching x0 (g0), the head's stream gradient (gfin),
   // value-embedding gate gradients [N, Hkv], partial sums of the reductions
@@ -499,27 +510,21 @@ WS ws_layout(const Dims& D) {
       for (int l = 0; l < D.L; l += 2) w.layer[l].vgate = take(N * Hkv * 4);
     }
   }
-  w.xq = w.dyq = w.dyqt = w.scales = w.qpart = 0;
+  w.dyq = w.scales = w.qpart = 0;
   if (D.prec == GPT_PREC_FP8) {
     const size_t dd = (size_t)d * d, hd = (size_t)D.hidden;
     for (int l = 0; l < D.L; ++l) {
       Layer& L = w.layer[l];
-      L.h1t = take(N * d);
-      L.attt = take(N * d);
-      L.h2t = take(N * d);
-      L.actt = take(N * hd);
+      L.h1q = take(N * d);
+      L.attq = take(N * d);
+      L.h2q = take(N * d);
+      L.actq = take(N * hd);
       L.wqkv8 = take((size_t)D.dqkv * d);
-      L.wqkv8t = take((size_t)D.dqkv * d);
       L.wo8 = take(dd);
-      L.wo8t = take(dd);
       L.wfc8 = take(hd * d);
-      L.wfc8t = take(hd * d);
       L.wproj8 = take(hd * d);
-      L.wproj8t = take(hd * d);
     }
-    w.xq = take(N * hd);
     w.dyq = take(N * hd);
-    w.dyqt = take(N * hd);
     w.scales = take((size_t)D.L * SC_COUNT * 4);
     // amax partials: the standalone reduction, one per row (norm kernels), or
     // one per wave of the [N, 4d] bf16 products
@@ -606,13 +611,13 @@ int wgrad(const void* A, long long lda, const void* B, long long ldb, float* C, 
   return launch_splitk_reduce(part, pl.ks, (long long)M * N, C, nullptr, (long long)M * N, accumulate ? 1.f : 0.f, s);
 }
 
-// fp8 weight gradient: C[M,N] (+)= A B^T / (sa sb) with A = dY^T codes
-// [M][K] (E5M2) and B = X^T codes [N][K] (E4M3), both k-contiguous
+// fp8 weight gradient: C[M,N] (+)= dY^T X / (sa sb) from the codes as
+// stored: dY [K][M] (E5M2) and X [K][N] (E4M3), both m/n-contiguous
 int wgrad_fp8(const uint8_t* A, const uint8_t* B, const float* sa, const float* sb, float* C, int M, int N, int K,
               bool accumulate, float* part, hipStream_t s) {
   GemmArgs a;
   a.M = M; a.N = N; a.K = K;
-  a.A = A; a.lda = K; a.B = B; a.ldb = K;
+  a.A = A; a.lda = M; a.a_kcontig = 0; a.B = B; a.ldb = N; a.b_kcontig = 0;
   a.scale_a = sa; a.scale_b = sb;
   const WgradPlan pl = wgrad_plan(M, N, K);
   a.tile = pl.tile;
@@ -708,47 +713,47 @@ extern "C" gpt_status gpt_step_fwd(const gpt_shape* shape, const gpt_params* par
   const bool f8 = D.prec == GPT_PREC_FP8;
   const int hid = D.hidden;
   float* qpart = f8 ? at<float>(ws, w.qpart) : nullptr;
-  uint8_t* xq = f8 ? at<uint8_t>(ws, w.xq) : nullptr;
+  const uint8_t* xq = nullptr;  // codes of the current product input
   if (f8) {
-    // E4M3 codes of every block weight, plain (forward) and transposed (data
-    // gradient), one scale per tensor: one batched launch per weight kind over
-    // all layers (same shape, a fixed stride apart in the packed parameters and
-    // in the per-layer workspace)
+    // E4M3 codes of every block weight, one scale per tensor: one batched
+    // launch per weight kind over all layers (same shape, a fixed stride apart
+    // in the packed parameters and in the per-layer workspace)
     ProfScope ps_(P_FP8_QUANT, s);
     float* sc0 = at<float>(ws, w.scales);
-    auto kind = [&](auto poff, size_t Layer::*q8, size_t Layer::*q8t, int rows, int cols, int sc_slot) -> int {
+    auto kind = [&](auto poff, size_t Layer::*q8, int rows, int cols, int sc_slot) -> int {
       const long long sx = (long long)(poff(1) - poff(0));
       const long long sq = (long long)(w.layer[1].*q8 - w.layer[0].*q8);
       bool uniform = true;
       for (int l = 1; l < D.L; ++l)
         uniform = uniform && (long long)(poff(l) - poff(0)) == l * sx &&
-                  (long long)(w.layer[l].*q8 - w.layer[0].*q8) == l * sq &&
-                  (long long)(w.layer[l].*q8t - w.layer[0].*q8t) == l * sq;
+                  (long long)(w.layer[l].*q8 - w.layer[0].*q8) == l * sq;
       // one launch for all layers, or (were the strides not uniform) one per layer
       const int cnt = uniform ? D.L : 1;
       for (int l0 = 0; l0 < D.L; l0 += cnt) {
         const Layer& L = w.layer[l0];
         float* scl = sc0 + (size_t)l0 * SC_COUNT + sc_slot;
         TRY(launch_fp8_amax_scale(W + poff(l0), 0, cols, rows, cols, 0, qpart, scl, s, cnt, sx, SC_COUNT));
-        TRY(launch_fp8_quant(W + poff(l0), 0, cols, rows, cols, 0, scl, at<uint8_t>(ws, L.*q8), cols,
-                             at<uint8_t>(ws, L.*q8t), rows, s, cnt, sx, SC_COUNT, sq));
+        TRY(launch_fp8_quant(W + poff(l0), 0, cols, rows, cols, 0, scl, at<uint8_t>(ws, L.*q8), cols, nullptr, 0,
+                             s, cnt, sx, SC_COUNT, sq));
       }
       return 0;
     };
-    TRY(kind([&](int l) { return P.qkv(D, l); }, &Layer::wqkv8, &Layer::wqkv8t, D.dqkv, d, SC_WQKV));
-    TRY(kind([&](int l) { return P.wo(D, l); }, &Layer::wo8, &Layer::wo8t, d, d, SC_WO));
-    TRY(kind([&](int l) { return P.fc(D, l); }, &Layer::wfc8, &Layer::wfc8t, hid, d, SC_WFC));
-    TRY(kind([&](int l) { return P.proj(D, l); }, &Layer::wproj8, &Layer::wproj8t, d, hid, SC_WPROJ));
+    TRY(kind([&](int l) { return P.qkv(D, l); }, &Layer::wqkv8, D.dqkv, d, SC_WQKV));
+    TRY(kind([&](int l) { return P.wo(D, l); }, &Layer::wo8, d, d, SC_WO));
+    TRY(kind([&](int l) { return P.fc(D, l); }, &Layer::wfc8, hid, d, SC_WFC));
+    TRY(kind([&](int l) { return P.proj(D, l); }, &Layer::wproj8, d, hid, SC_WPROJ));
   }
   // y (op)= X W^T for one block product: bf16 operands, or (fp8) the E4M3 codes
-  // of X (quantised here; the transposed codes are kept for the weight
-  // gradient) and of W
+  // of X (quantised here into the layer's buffer, which the weight gradient
+  // reads again) and of W
   // np > 0: the producer already wrote np amax partials into qpart
-  auto quant_x = [&](const uint16_t* X, int K, size_t xt_off, float* sx, long long np) -> int {
+  auto quant_x = [&](const uint16_t* X, int K, size_t xq_off, float* sx, long long np) -> int {
     if (!f8) return 0;
     ProfScope ps_(P_FP8_QUANT, s);
-    if (np > 0) return quantize_fp8_partials(X, 0, K, N, K, 0, qpart, np, sx, xq, K, at<uint8_t>(ws, xt_off), N, s);
-    return quantize_fp8(X, 0, K, N, K, 0, qpart, sx, xq, K, at<uint8_t>(ws, xt_off), N, s);
+    uint8_t* q = at<uint8_t>(ws, xq_off);
+    xq = q;
+    if (np > 0) return quantize_fp8_partials(X, 0, K, N, K, 0, qpart, np, sx, q, K, nullptr, 0, s);
+    return quantize_fp8(X, 0, K, N, K, 0, qpart, sx, q, K, nullptr, 0, s);
   };
   auto block_fwd = [&](GemmArgs& a, int epi, int K, const uint8_t* w8, const float* sx, const float* sw) -> int {
     if (!f8) return gemm_bf16(a, epi, s);
@@ -785,7 +790,7 @@ extern "C" gpt_status gpt_step_fwd(const gpt_shape* shape, const gpt_params* par
       else
         TRY(launch_rmsnorm_fwd(x, h1, at<float>(ws, L.r1), N, d, s, qpart));
     }
-    TRY(quant_x(h1, d, L.h1t, sc ? sc + SC_H1 : nullptr, N));
+    TRY(quant_x(h1, d, L.h1q, sc ? sc + SC_H1 : nullptr, N));
     {
       GemmArgs a;  // [q | k | v] = h1 [Wq; Wk; Wv]^T, q and k rotated and RMS-normalised per head
       ProfScope ps_(P_GEMM_QKV, s);
@@ -808,7 +813,7 @@ extern "C" gpt_status gpt_step_fwd(const gpt_shape* shape, const gpt_params* par
       TRY(launch_attn_fwd(qkv, qkv + d, qkv + d + D.dkv, D.dqkv, att, d, at<float>(ws, L.lse), D.B, D.H, D.Hkv, D.T,
                           D.layer_window(l), s, true, qpart));
     }
-    TRY(quant_x(att, d, L.attt, sc ? sc + SC_ATT : nullptr, f8 ? attn_fwd_amax_slots(D.B, D.H, D.T) : 0));
+    TRY(quant_x(att, d, L.attq, sc ? sc + SC_ATT : nullptr, f8 ? attn_fwd_amax_slots(D.B, D.H, D.T) : 0));
     {
       GemmArgs a;  // x += att Wo^T
       ProfScope ps_(P_GEMM_O, s);
@@ -819,7 +824,7 @@ extern "C" gpt_status gpt_step_fwd(const gpt_shape* shape, const gpt_params* par
                     sc ? sc + SC_WO : nullptr));
     }
     { ProfScope ps_(P_RMSNORM_FWD, s); TRY(launch_rmsnorm_fwd(x, h2, at<float>(ws, L.r2), N, d, s, qpart)); }
-    TRY(quant_x(h2, d, L.h2t, sc ? sc + SC_H2 : nullptr, N));
+    TRY(quant_x(h2, d, L.h2q, sc ? sc + SC_H2 : nullptr, N));
     {
       GemmArgs a;  // act = relu(h2 Wfc^T)^2
       ProfScope ps_(P_GEMM_FC, s);
@@ -831,7 +836,7 @@ extern "C" gpt_status gpt_step_fwd(const gpt_shape* shape, const gpt_params* par
       TRY(block_fwd(a, EPI_RELU2, d, f8 ? at<uint8_t>(ws, L.wfc8) : nullptr, sc ? sc + SC_H2 : nullptr,
                     sc ? sc + SC_WFC : nullptr));
     }
-    TRY(quant_x(act, hid, L.actt, sc ? sc + SC_ACT : nullptr, act_slots));
+    TRY(quant_x(act, hid, L.actq, sc ? sc + SC_ACT : nullptr, act_slots));
     {
       GemmArgs a;  // x += act Wproj^T
       ProfScope ps_(P_GEMM_PROJ, s);
@@ -971,20 +976,20 @@ extern "C" gpt_status gpt_step_bwd_scaled(const gpt_shape* shape, const gpt_para
   bool g_amax_ok = true;
 
   uint8_t* dyq = f8 ? at<uint8_t>(ws, w.dyq) : nullptr;
-  uint8_t* dyqt = f8 ? at<uint8_t>(ws, w.dyqt) : nullptr;
-  // E5M2 codes of an output gradient dY [N, cols], plain and transposed
+  // E5M2 codes of an output gradient dY [N, cols] (the data gradient reads
+  // them k-contiguous, the weight gradient m-contiguous)
   // np > 0: the producer already wrote np amax partials into qpart
   auto quant_dy = [&](const uint16_t* dy, int cols, float* sdy, long long np) -> int {
     ProfScope ps_(P_FP8_QUANT, s);
-    if (np > 0) return quantize_fp8_partials(dy, 0, cols, N, cols, 1, qpart, np, sdy, dyq, cols, dyqt, N, s);
-    return quantize_fp8(dy, 0, cols, N, cols, 1, qpart, sdy, dyq, cols, dyqt, N, s);
+    if (np > 0) return quantize_fp8_partials(dy, 0, cols, N, cols, 1, qpart, np, sdy, dyq, cols, nullptr, 0, s);
+    return quantize_fp8(dy, 0, cols, N, cols, 1, qpart, sdy, dyq, cols, nullptr, 0, s);
   };
   // data gradient dX [N, cols_x] = dY W for a weight W [cols_dy, cols_x]: fp8
-  // operands are the dY codes and the transposed weight codes W^T [cols_x, cols_dy]
-  auto dgrad_fp8 = [&](GemmArgs& a, int epi, int cols_dy, const uint8_t* wt8, const float* sdy,
+  // operands are the dY codes and the weight codes as stored (n-contiguous)
+  auto dgrad_fp8 = [&](GemmArgs& a, int epi, int cols_dy, int cols_x, const uint8_t* w8, const float* sdy,
                        const float* sw) -> int {
     a.A = dyq; a.lda = cols_dy; a.a_kcontig = 1;
-    a.B = wt8; a.ldb = cols_dy; a.b_kcontig = 1;
+    a.B = w8; a.ldb = cols_x; a.b_kcontig = 0;
     a.scale_a = sdy; a.scale_b = sw;
     return gemm_fp8(a, epi, 1, 0, s);
   };
@@ -1013,12 +1018,12 @@ extern "C" gpt_status gpt_step_bwd_scaled(const gpt_shape* shape, const gpt_para
       a.C = du; a.ldc = hid; a.aux = act; a.ldaux = hid;
       a.amax = qpart;  // NULL for bf16
       du_slots = f8 ? gemm_amax_slots(a) : 0;
-      if (f8) TRY(dgrad_fp8(a, EPI_DRELU2, d, at<uint8_t>(ws, L.wproj8t), sc + SC_G_MLP, sc + SC_WPROJ));
+      if (f8) TRY(dgrad_fp8(a, EPI_DRELU2, d, hid, at<uint8_t>(ws, L.wproj8), sc + SC_G_MLP, sc + SC_WPROJ));
       else TRY(gemm_bf16(a, EPI_DRELU2, s));
     }
     {
       ProfScope ps_(P_PROJ_WGRAD, s);  // dWproj = g^T act
-      if (f8) TRY(wgrad_fp8(dyqt, at<uint8_t>(ws, L.actt), sc + SC_G_MLP, sc + SC_ACT, G + P.proj(D, l), d, hid, N, acc, wpart, s));
+      if (f8) TRY(wgrad_fp8(dyq, at<uint8_t>(ws, L.actq), sc + SC_G_MLP, sc + SC_ACT, G + P.proj(D, l), d, hid, N, acc, wpart, s));
       else TRY(wgrad(g_bf, d, act, hid, G + P.proj(D, l), d, hid, N, acc, wpart, s));
     }
     if (f8) TRY(quant_dy(du, hid, sc + SC_DU, du_slots));
@@ -1028,12 +1033,12 @@ extern "C" gpt_status gpt_step_bwd_scaled(const gpt_shape* shape, const gpt_para
       a.M = N; a.N = d; a.K = hid;
       a.A = du; a.lda = hid; a.B = W + P.fc(D, l); a.ldb = d; a.b_kcontig = 0;
       a.C = dh16; a.ldc = d;
-      if (f8) TRY(dgrad_fp8(a, EPI_BF16, hid, at<uint8_t>(ws, L.wfc8t), sc + SC_DU, sc + SC_WFC));
+      if (f8) TRY(dgrad_fp8(a, EPI_BF16, hid, d, at<uint8_t>(ws, L.wfc8), sc + SC_DU, sc + SC_WFC));
       else TRY(gemm_bf16(a, EPI_BF16, s));
     }
     {
       ProfScope ps_(P_FC_WGRAD, s);  // dWfc = du^T h2
-      if (f8) TRY(wgrad_fp8(dyqt, at<uint8_t>(ws, L.h2t), sc + SC_DU, sc + SC_H2, G + P.fc(D, l), hid, d, N, acc, wpart, s));
+      if (f8) TRY(wgrad_fp8(dyq, at<uint8_t>(ws, L.h2q), sc + SC_DU, sc + SC_H2, G + P.fc(D, l), hid, d, N, acc, wpart, s));
       else TRY(wgrad(du, hid, h2, d, G + P.fc(D, l), hid, d, N, acc, wpart, s));
     }
     { ProfScope ps_(P_RMSNORM_BWD, s); TRY(launch_rmsnorm_bwd(dh16, true, h2, at<float>(ws, L.r2), g, g_bf, N, d, s, qpart)); }
@@ -1045,12 +1050,12 @@ extern "C" gpt_status gpt_step_bwd_scaled(const gpt_shape* shape, const gpt_para
       a.M = N; a.N = d; a.K = d;
       a.A = g_bf; a.lda = d; a.B = W + P.wo(D, l); a.ldb = d; a.b_kcontig = 0;
       a.C = dout; a.ldc = d;
-      if (f8) TRY(dgrad_fp8(a, EPI_BF16, d, at<uint8_t>(ws, L.wo8t), sc + SC_G_ATT, sc + SC_WO));
+      if (f8) TRY(dgrad_fp8(a, EPI_BF16, d, d, at<uint8_t>(ws, L.wo8), sc + SC_G_ATT, sc + SC_WO));
       else TRY(gemm_bf16(a, EPI_BF16, s));
     }
     {
       ProfScope ps_(P_O_WGRAD, s);  // dWo = g^T att
-      if (f8) TRY(wgrad_fp8(dyqt, at<uint8_t>(ws, L.attt), sc + SC_G_ATT, sc + SC_ATT, G + P.wo(D, l), d, d, N, acc, wpart, s));
+      if (f8) TRY(wgrad_fp8(dyq, at<uint8_t>(ws, L.attq), sc + SC_G_ATT, sc + SC_ATT, G + P.wo(D, l), d, d, N, acc, wpart, s));
       else TRY(wgrad(g_bf, d, att, d, G + P.wo(D, l), d, d, N, acc, wpart, s));
     }
     // dQ (and delta), then dK/dV; both leave through the QK-norm + rotary
@@ -1080,12 +1085,12 @@ extern "C" gpt_status gpt_step_bwd_scaled(const gpt_shape* shape, const gpt_para
       a.M = N; a.N = d; a.K = D.dqkv;
       a.A = dqkv; a.lda = D.dqkv; a.B = W + P.qkv(D, l); a.ldb = d; a.b_kcontig = 0;
       a.C = dh16; a.ldc = d;
-      if (f8) TRY(dgrad_fp8(a, EPI_BF16, D.dqkv, at<uint8_t>(ws, L.wqkv8t), sc + SC_DQKV, sc + SC_WQKV));
+      if (f8) TRY(dgrad_fp8(a, EPI_BF16, D.dqkv, d, at<uint8_t>(ws, L.wqkv8), sc + SC_DQKV, sc + SC_WQKV));
       else TRY(gemm_bf16(a, EPI_BF16, s));
     }
     {
       ProfScope ps_(P_QKV_WGRAD, s);  // dWqkv = dqkv^T h1
-      if (f8) TRY(wgrad_fp8(dyqt, at<uint8_t>(ws, L.h1t), sc + SC_DQKV, sc + SC_H1, G + P.qkv(D, l), D.dqkv, d, N, acc, wpart, s));
+      if (f8) TRY(wgrad_fp8(dyq, at<uint8_t>(ws, L.h1q), sc + SC_DQKV, sc + SC_H1, G + P.qkv(D, l), D.dqkv, d, N, acc, wpart, s));
       else TRY(wgrad(dqkv, D.dqkv, h1, d, G + P.qkv(D, l), D.dqkv, d, N, acc, wpart, s));
     }
     if (D.ve_layer(l)) {  // the gate reads h1[:, :32]: dh[:, :32] += dz Wg; dWg = dz^T h1[:, :32]

@@ -21,8 +21,9 @@
 //     is read as MFMA fragments with 16-byte loads; an m/n-contiguous bf16 tile
 //     (the weight-gradient, data-gradient and Gram operands) is read with the
 //     gfx950 transpose load ds_read_b64_tr_b16, two per fragment, so no bf16
-//     product needs a transposed copy in HBM.  fp8 operands are always
-//     k-contiguous (the quantiser writes transposed copies where needed).
+//     product needs a transposed copy in HBM; an m/n-contiguous fp8 tile (the
+//     data- and weight-gradient operands) with ds_read_b64_tr_b8, four per
+//     fragment, so the quantiser writes each tensor's codes once.
 //     Both layouts are XOR-swizzled so fragment reads are bank-conflict free
 //     (64 banks of 4 bytes, 16-lane groups per 16-byte read).
 //   * The MFMA is issued with the operands swapped (B tile as src0), so each
@@ -113,8 +114,22 @@ __device__ __forceinline__ int lds_off_mn(int k, int i) {
   return k * (2 * R) + ((((i >> 5) ^ (k & 3))) << 6) + ((i & 31) << 1);
 }
 
+// mn-contiguous fp8 LDS tile: 128 rows (k) of R codes (R bytes) stored as in
+// memory; 32-byte units XOR-swizzled by the row (R = 256: k & 7; R = 128:
+// (k >> 1) & 3, two rows per 256-byte line of the 64 banks), so the 8
+// consecutive k rows x 32 codes that half a wave's transpose read touches
+// land in 8 distinct groups of 8 banks.
+template <int R>
+__device__ __forceinline__ int lds_off_mn8(int k, int m) {
+  static_assert(R == 128 || R == 256, "fp8 mn tile rows of 128 or 256 codes");
+  const int f = R == 256 ? (k & 7) : ((k >> 1) & 3);
+  return k * R + (((m >> 5) ^ f) << 5) + (m & 31);
+}
+
 typedef short v4s_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4s_t lds_v4s_t;
+typedef int v2i_t __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) v2i_t lds_v2i_t;
 
 // transpose read: within each 16-lane group, lane j receives element j % 4 of
 // the 8 bytes loaded by lanes 4t + j / 4 (t = 0..3)
@@ -124,17 +139,24 @@ __device__ __forceinline__ v4s_t ds_read_tr(const char* lds_generic, int byte_of
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s_t*)(base + byte_off));
 }
 
+// 8-bit transpose read: within each 16-lane group, lane j receives byte j % 8
+// of the 8 bytes loaded by lanes 2t + j / 8 (t = 0..7), as its byte t
+__device__ __forceinline__ v2i_t ds_read_tr8(const char* lds_generic, int byte_off) {
+  const __attribute__((address_space(3))) char* base =
+      (const __attribute__((address_space(3))) char*)(lds_generic);
+  return __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i_t*)(base + byte_off));
+}
+
 // ---------------------------------------------------------------------------
 // global -> register staging of one operand tile (R rows x 128 bytes of k):
 // R*8 chunks of 16 B, R*8/NT per thread, for either layout.  ES = bytes per
-// element (2: bf16, 1: fp8 codes; fp8 tiles are k-contiguous only).
+// element (2: bf16, 1: fp8 codes).
 // ---------------------------------------------------------------------------
 template <int R, bool KC, int NT, int ES = 2>
 struct TileLoader {
   static constexpr int kRegs = R * 8 / NT;
   static constexpr int EPC = 16 / ES;   // elements per 16-byte chunk
   static constexpr int KBK = 128 / ES;  // k elements per stage
-  static_assert(ES == 2 || KC, "fp8 operands must be k-contiguous");
   uint4 v[kRegs];
 
   template <bool GUARD>
@@ -151,15 +173,15 @@ struct TileLoader {
         gr = row0 + (c >> 3);
         gk = k0 + (c & 7) * EPC;
       } else {
-        gk = k0 + c / (R / 8);
-        gr = row0 + (c % (R / 8)) * 8;
+        gk = k0 + c / (R / EPC);
+        gr = row0 + (c % (R / EPC)) * EPC;
       }
       const long long base = KC ? (long long)gr * ld + gk : (long long)gk * ld + gr;
       if (full) {
         v[i] = *reinterpret_cast<const uint4*>(Xb + base * ES);
       } else if constexpr (ES == 1) {
-        // fp8: K is a multiple of 16 (checked on the host), so a chunk is
-        // either wholly inside the operand or wholly outside
+        // fp8: K and an m/n-contiguous operand's rows are multiples of 16
+        // (checked on the host), so a chunk is wholly inside or outside
         v[i] = (gr < rows && gk < K) ? *reinterpret_cast<const uint4*>(Xb + base) : make_uint4(0, 0, 0, 0);
       } else {
         uint32_t w[4];
@@ -195,11 +217,13 @@ struct TileLoader {
       if constexpr (KC) {
         const int r = slot >> 3, kc = (slot & 7) ^ ((r >> 1) & 7);
         src = (long long)(row0 + r) * ld + k0 + kc * EPC;
-      } else {
+      } else if constexpr (ES == 2) {
         const int b = slot * 16;
         const int k = b / (2 * R), rb = b % (2 * R);
         const int i_el = (((rb >> 6) ^ (k & 3)) << 5) + ((rb & 63) >> 1);
         src = (long long)(k0 + k) * ld + row0 + i_el;
+      } else {
+        src = (long long)(k0 + (slot * 16) / R) * ld + row0 + mn8_elem(slot);
       }
       __attribute__((address_space(3))) char* dst =
           (__attribute__((address_space(3))) char*)(lds) + (NT * i + 64 * wave) * 16;
@@ -211,7 +235,9 @@ struct TileLoader {
 #pragma unroll
     for (int i = 0; i < kRegs; ++i) {
       const int c = tid + NT * i;
-      const int off = KC ? lds_off_k(c >> 3, c & 7) : lds_off_mn<R>(c / (R / 8), (c % (R / 8)) * 8);
+      const int off = KC ? lds_off_k(c >> 3, c & 7)
+                         : (ES == 2 ? lds_off_mn<R>(c / (R / 8), (c % (R / 8)) * 8)
+                                    : lds_off_mn8<R>(c / (R / 16), (c % (R / 16)) * 16));
       *reinterpret_cast<uint4*>(lds + off) = v[i];
     }
   }
@@ -238,17 +264,41 @@ struct TileLoader {
   // r0 + l % 32 and the 32 codes of 16-byte chunks 4 ks + 2 (l / 32) + {0, 1}.
   // (Any assignment of the 64 k values to (lane half, byte) works as long as
   // both operands use the same one: the MFMA pairs equal positions.)
+  // An m/n-contiguous tile gives the same assignment (byte p of lane half h
+  // = k 64 ks + 32 h + p) through four transpose reads: read q of lane l
+  // loads the 8 codes at k row 64 ks + 32 (l / 32) + 8 q + (l % 16) / 2,
+  // columns r0 + 16 ((l / 16) % 2) + 8 (l % 2) + 0..7, so lane l receives
+  // column r0 + l % 32 of k rows 64 ks + 32 (l / 32) + 8 q + 0..7.
   __device__ __forceinline__ static i32x8_t frag8(const char* lds, int r0, int ks, int lane) {
-    // native vector loads (a struct-typed load here makes the compiler wait
-    // for every direct global -> LDS load in flight before the read)
-    typedef int i32x4_t __attribute__((ext_vector_type(4)));
-    const int r = r0 + (lane & 31), c = ks * 4 + (lane >> 5) * 2;
-    const i32x4_t a = *reinterpret_cast<const i32x4_t*>(lds + lds_off_k(r, c));
-    const i32x4_t b = *reinterpret_cast<const i32x4_t*>(lds + lds_off_k(r, c + 1));
     i32x8_t f;
-    f[0] = a[0]; f[1] = a[1]; f[2] = a[2]; f[3] = a[3];
-    f[4] = b[0]; f[5] = b[1]; f[6] = b[2]; f[7] = b[3];
+    if constexpr (KC) {
+      // native vector loads (a struct-typed load here makes the compiler wait
+      // for every direct global -> LDS load in flight before the read)
+      typedef int i32x4_t __attribute__((ext_vector_type(4)));
+      const int r = r0 + (lane & 31), c = ks * 4 + (lane >> 5) * 2;
+      const i32x4_t a = *reinterpret_cast<const i32x4_t*>(lds + lds_off_k(r, c));
+      const i32x4_t b = *reinterpret_cast<const i32x4_t*>(lds + lds_off_k(r, c + 1));
+      f[0] = a[0]; f[1] = a[1]; f[2] = a[2]; f[3] = a[3];
+      f[4] = b[0]; f[5] = b[1]; f[6] = b[2]; f[7] = b[3];
+    } else {
+      const int m = r0 + 16 * ((lane >> 4) & 1) + 8 * (lane & 1);
+      const int kb = ks * 64 + 32 * (lane >> 5) + ((lane & 15) >> 1);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const v2i_t x = ds_read_tr8(lds, lds_off_mn8<R>(kb + 8 * q, m));
+        f[2 * q] = x[0];
+        f[2 * q + 1] = x[1];
+      }
+    }
     return f;
+  }
+
+  // element offset (along the rows) of the 16-byte chunk that the swizzled
+  // mn-contiguous fp8 layout places in LDS slot `slot` (k row slot * 16 / R)
+  __device__ __forceinline__ static int mn8_elem(int slot) {
+    const int b = slot * 16, k = b / R, rb = b % R;
+    const int f = R == 256 ? (k & 7) : ((k >> 1) & 3);
+    return (((rb >> 5) ^ f) << 5) + (rb & 31);
   }
 };
 
@@ -422,7 +472,7 @@ __device__ __forceinline__ void mainloop(const GemmArgs& p, const void* A, const
   constexpr int KS = F8 ? 2 : 4;                                 // MFMA k-steps per stage
   constexpr int NM = TM * TN;                                    // MFMAs per k-step
   constexpr int NV = LA::kRegs + LB::kRegs;                      // global loads per tile
-  constexpr int ND = F8 ? 2 * (TM + TN) : (AK ? 1 : 2) * TM + (BKC ? 1 : 2) * TN;  // LDS reads per k-step
+  constexpr int ND = F8 ? (AK ? 2 : 4) * TM + (BKC ? 2 : 4) * TN : (AK ? 1 : 2) * TM + (BKC ? 1 : 2) * TN;  // LDS reads per k-step
   const int lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   if (nk <= 0) return;
@@ -565,12 +615,11 @@ __device__ __forceinline__ bool dma_fits(const GemmArgs& p, int BM, int BN, bool
 template <int R, bool KC, int NT, int ES>
 struct DmaOperand {
   static constexpr int NL = R * 8 / NT;  // 16-byte loads per thread per block
-  static_assert(ES == 2 || KC, "fp8 operands are k-contiguous");
   v4i_t rsrc;
   int voff[NL];
   long long kstep;  // bytes per k element along the loaded direction
 
-  // nrows: rows (KC) or elements (MN, a multiple of 8) of the operand from
+  // nrows: rows (KC) or elements (MN, a multiple of 16 / ES) of the operand from
   // row0 on; a tile reaching past them re-reads the last valid row / 16-byte
   // chunk instead (its products land in output rows / columns that are never
   // stored), so every load stays inside the operand
@@ -579,8 +628,8 @@ struct DmaOperand {
       rsrc = dma_rsrc(X + (long long)row0 * ld * ES, (long long)min(R, nrows) * ld * ES);
       kstep = ES;
     } else {
-      rsrc = dma_rsrc(X + (long long)row0 * 2, ((long long)K * ld - row0) * 2);
-      kstep = ld * 2;
+      rsrc = dma_rsrc(X + (long long)row0 * ES, ((long long)K * ld - row0) * ES);
+      kstep = ld * ES;
     }
 #pragma unroll
     for (int i = 0; i < NL; ++i) {
@@ -588,11 +637,15 @@ struct DmaOperand {
       if constexpr (KC) {
         const int r = min(slot >> 3, nrows - 1), kc = (slot & 7) ^ (((slot >> 3) >> 1) & 7);
         voff[i] = (int)(((long long)r * ld + kc * (16 / ES)) * ES);
-      } else {
+      } else if constexpr (ES == 2) {
         const int b = slot * 16;
         const int k = b / (2 * R), rb = b % (2 * R);
         const int i_el = min((((rb >> 6) ^ (k & 3)) << 5) + ((rb & 63) >> 1), nrows - 8);
         voff[i] = (int)(((long long)k * ld + i_el) * 2);
+      } else {
+        const int k = (slot * 16) / R;
+        const int i_el = min(TileLoader<R, false, NT, 1>::mn8_elem(slot), nrows - 16);
+        voff[i] = (int)((long long)k * ld + i_el);
       }
     }
   }
@@ -789,10 +842,11 @@ __global__ void __launch_bounds__((Cfg<BM, BN>::NT), 1) gemm_kernel(GemmArgs p) 
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
   // the block-load loop takes every tile whose K is whole blocks; a tile
-  // reaching past M or N needs that dimension a multiple of 8 when it is the
-  // contiguous one (16-byte chunks either wholly inside or outside)
-  const bool fast = (p.K % KBK == 0) && (m0 + BM <= p.M || AK || p.M % 8 == 0) &&
-                    (n0 + BN <= p.N || BKC || p.N % 8 == 0);
+  // reaching past M or N needs that dimension a multiple of 8 bf16 / 16 fp8
+  // elements when it is the contiguous one (16-byte chunks either wholly
+  // inside or outside)
+  const bool fast = (p.K % KBK == 0) && (m0 + BM <= p.M || AK || p.M % (16 / ES) == 0) &&
+                    (n0 + BN <= p.N || BKC || p.N % (16 / ES) == 0);
   const bool interior = (m0 + BM <= p.M) && (n0 + BN <= p.N) && (p.K % KBK == 0);
   if (fast && dma_fits(p, BM, BN, AK, BKC, ES))
     mainloop_dma<BM, BN, AK, BKC, F8>(p, A, B, m0, n0, kt0, nk, smem, tid, acc);

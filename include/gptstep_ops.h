@@ -55,15 +55,23 @@ gpt_status gpt_op_quantize_fp8(const void* x, int32_t x_dtype, int64_t ldx, int3
                                int32_t fmt, float* scale, uint8_t* q, int64_t ldq, uint8_t* qt,
                                int64_t ldqt, float* partial, gpt_stream_t stream);
 
-/* fp8 matrix product with fp32 accumulation, both operands k-contiguous:
+/* fp8 matrix product with fp32 accumulation (the fp8 linear layers of the
+ * precision passage above):
  *   C[m, n] = sum_k dec(A[m, k]) dec(B[n, k]) / (scale_a[0] * scale_b[0])  (+ beta * C[m, n])
- * A: codes [M, K] (format fmt_a, leading dimension lda); B: codes [N, K]
- * (format fmt_b, ldb); C fp32 [M, N] (ldc); scale_a, scale_b: device fp32
- * scalars (the quantisation scales of the two operands).  K % 16 == 0, lda
- * and ldb multiples of 16, ldc of 4; pointers 16-byte aligned. */
-gpt_status gpt_op_gemm_fp8(int32_t M, int32_t N, int32_t K, const uint8_t* A, int32_t fmt_a, int64_t lda,
-                           const uint8_t* B, int32_t fmt_b, int64_t ldb, float* C, int64_t ldc,
-                           const float* scale_a, const float* scale_b, float beta, gpt_stream_t stream);
+ * A: logical codes [M, K] in format fmt_a, B: logical [N, K] in fmt_b, each
+ * in one of the operand layouts above (GPT_LAYOUT_K_CONTIG: element (r, k)
+ * at X[r * ld + k]; GPT_LAYOUT_MN_CONTIG: at X[k * ld + r]); C fp32 [M, N]
+ * (ldc); scale_a, scale_b: device fp32 scalars (the quantisation scales of
+ * the two operands).  Both k-contiguous: any format pair.  m/n-contiguous
+ * operands (the codes of an output gradient and of an activation or weight
+ * read as stored, for the weight and data gradients): A E5M2, B E4M3, B
+ * m/n-contiguous, A either; the m/n-contiguous operand's rows (M or N) a
+ * multiple of 16.  K % 16 == 0; lda, ldb >= the operand's contiguous
+ * dimension and multiples of 16; ldc >= N, a multiple of 4; pointers 16-byte
+ * aligned.  Other combinations return GPT_ERR_UNSUPPORTED. */
+gpt_status gpt_op_gemm_fp8(int32_t M, int32_t N, int32_t K, const uint8_t* A, int32_t fmt_a, int32_t a_layout,
+                           int64_t lda, const uint8_t* B, int32_t fmt_b, int32_t b_layout, int64_t ldb, float* C,
+                           int64_t ldc, const float* scale_a, const float* scale_b, float beta, gpt_stream_t stream);
 
 /* Causal multi-head attention forward with head width 128 (dev.to page,
  * "5. Unificación Flash Attention": flash_attn_func(q, k, v, causal=True,

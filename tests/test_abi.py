@@ -190,11 +190,23 @@ def test_fp8_ops_reject_on_host(B):
     assert rc == -5   # unknown format
     rc = lib.gpt_op_quantize_fp8(fake, 1, 64, 16, 64, 0, None, fake, 64, None, 0, fake, None)
     assert rc == -1   # scale is NULL
-    rc = lib.gpt_op_gemm_fp8(64, 64, 24, fake, 0, 32, fake, 0, 32, fake, 64, fake, fake, 0.0, None)
+    K, MN = 0, 1
+    rc = lib.gpt_op_gemm_fp8(64, 64, 24, fake, 0, K, 32, fake, 0, K, 32, fake, 64, fake, fake, 0.0, None)
     assert rc == -1   # K not a multiple of 16
-    rc = lib.gpt_op_gemm_fp8(64, 64, 32, fake, 0, 32, fake, 0, 32, fake, 64, None, fake, 0.0, None)
+    rc = lib.gpt_op_gemm_fp8(64, 64, 32, fake, 0, K, 32, fake, 0, K, 32, fake, 64, None, fake, 0.0, None)
     assert rc == -1   # scale_a NULL
-    assert lib.gpt_op_gemm_fp8(0, 64, 32, None, 0, 32, None, 0, 32, None, 64, None, None, 0.0, None) == 0
+    assert lib.gpt_op_gemm_fp8(0, 64, 32, None, 0, K, 32, None, 0, K, 32, None, 64, None, None, 0.0, None) == 0
+    # m/n-contiguous operands: E5M2 x E4M3 with B m/n-contiguous only
+    rc = lib.gpt_op_gemm_fp8(64, 64, 32, fake, 0, K, 32, fake, 0, MN, 64, fake, 64, fake, fake, 0.0, None)
+    assert rc == -5
+    rc = lib.gpt_op_gemm_fp8(64, 64, 32, fake, 1, MN, 64, fake, 0, K, 32, fake, 64, fake, fake, 0.0, None)
+    assert rc == -5
+    rc = lib.gpt_op_gemm_fp8(64, 64, 32, fake, 1, K, 32, fake, 0, 2, 64, fake, 64, fake, fake, 0.0, None)
+    assert rc == -1   # unknown layout
+    rc = lib.gpt_op_gemm_fp8(64, 40, 32, fake, 1, K, 32, fake, 0, MN, 48, fake, 64, fake, fake, 0.0, None)
+    assert rc == -1   # m/n-contiguous B with N not a multiple of 16
+    rc = lib.gpt_op_gemm_fp8(64, 64, 32, fake, 1, MN, 32, fake, 0, MN, 64, fake, 64, fake, fake, 0.0, None)
+    assert rc == -1   # lda below M for an m-contiguous A
     assert B.fp8_partials(65536, 1280) == 1024 and B.fp8_partials(16, 16) == 1
 
 

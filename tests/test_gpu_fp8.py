@@ -128,6 +128,33 @@ def test_gemm_fp8(fa, fb, M, N, K):
     assert e <= 2e-4
 
 
+@pytest.mark.parametrize("a_mn", [False, True])
+@pytest.mark.parametrize("M,N,K", [(256, 256, 512), (304, 208, 144), (1280, 5120, 1024), (512, 768, 65536 // 8)])
+def test_gemm_fp8_mn_operands(a_mn, M, N, K):
+    """E5M2 x E4M3 with the codes read as stored: B n-contiguous (data
+    gradient), and A m-contiguous too (weight gradient); ragged K (144: not
+    whole 128-code blocks) and tiles reaching past M and N (304, 208)."""
+    B = _B()
+    say(f"gemm_fp8 mn a_mn={a_mn} M={M} N={N} K={K}")
+    g = np.random.default_rng(M * 3 + N + K + a_mn)
+    A = _random_codes(g, (M, K), 1)
+    Bm = _random_codes(g, (N, K), 0)
+    sa, sb = np.float32(0.75), np.float32(2.5)
+    dA = torch.from_numpy(np.ascontiguousarray(A.T) if a_mn else A).cuda()
+    dB = torch.from_numpy(np.ascontiguousarray(Bm.T)).cuda()
+    C = torch.full((M, N), 0.5, dtype=torch.float32, device="cuda")
+    dsa = torch.tensor([sa], dtype=torch.float32, device="cuda")
+    dsb = torch.tensor([sb], dtype=torch.float32, device="cuda")
+    beta = 0.25 if M < 1000 else 0.0
+    B.gemm_fp8(dA, 1, dB, 0, C, M, N, K, dsa, dsb, beta=beta, a_layout=B.LAYOUT_MN if a_mn else B.LAYOUT_K,
+               b_layout=B.LAYOUT_MN)
+    torch.cuda.synchronize()
+    ref = ofp8.decode(A, "e5m2") @ ofp8.decode(Bm, "e4m3").T / (float(sa) * float(sb)) + beta * 0.5
+    e = rel_l2(C.cpu().numpy().astype(np.float64), ref)
+    say(f"  rel_l2 {e:.2e}")
+    assert e <= 2e-4
+
+
 CONFIGS = [
     # depth, vocab, seq_len, batch, (n_kv_head, window, pattern)
     (2, 32768, 128, 2, (0, 0, "")),
