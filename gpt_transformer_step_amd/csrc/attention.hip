@@ -803,32 +803,46 @@ attn_bwd_q_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k
     }
     const int key0 = j * DQ_K;
     if (key0 <= wq0 + 31 && (window < 0 || key0 + DQ_K - 1 >= wq0 - window)) {  // wave-uniform
-      // the scores first, then dP = dO V^T: the exponentials of the scores
-      // (below) only need the former and can run under the latter
+      // the scores first, then dP = dO V^T, as one run of 16 k-steps (K
+      // fragments, then V) whose fragments are read one k-step ahead of the
+      // MFMAs that use them (read next to their use, every MFMA waited for
+      // its LDS read); the exponentials of the scores run between the dP
+      // MFMAs, four per k-step
       f32x16_t st2[DQ_KT], dpt[DQ_KT];
 #pragma unroll
       for (int kt = 0; kt < DQ_KT; ++kt) {
 #pragma unroll
         for (int e = 0; e < 16; ++e) { st2[kt][e] = 0.f; dpt[kt][e] = 0.f; }
       }
-#pragma unroll
-      for (int ks = 0; ks < 8; ++ks)
-#pragma unroll
-        for (int kt = 0; kt < DQ_KT; ++kt)
-          st2[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag16(sk, kt * 32 + lr, ks * 2 + lh), fq[ks], st2[kt],
-                                                            0, 0, 0);
-#pragma unroll
-      for (int ks = 0; ks < 8; ++ks)
-#pragma unroll
-        for (int kt = 0; kt < DQ_KT; ++kt)
-          dpt[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag16(sv, kt * 32 + lr, ks * 2 + lh), fd[ks], dpt[kt],
-                                                            0, 0, 0);
-      const bool diag = (key0 + DQ_K - 1 > wq0) || (key0 + DQ_K > T) || (window >= 0 && key0 < wq0 + 31 - window);
       float ds[DQ_KT * 16];
+      bf16x8_t fkv[2][DQ_KT];
 #pragma unroll
-      for (int kt = 0; kt < DQ_KT; ++kt)
+      for (int kt = 0; kt < DQ_KT; ++kt) fkv[0][kt] = frag16(sk, kt * 32 + lr, lh);
 #pragma unroll
-        for (int e = 0; e < 16; ++e) ds[kt * 16 + e] = __builtin_amdgcn_exp2f(st2[kt][e] * c - lse2);
+      for (int i = 0; i < 16; ++i) {  // i < 8: scores, k-step i; i >= 8: dP, k-step i - 8
+        if (i + 1 < 16) {
+#pragma unroll
+          for (int kt = 0; kt < DQ_KT; ++kt)
+            fkv[(i + 1) & 1][kt] = frag16(i + 1 < 8 ? sk : sv, kt * 32 + lr, ((i + 1) & 7) * 2 + lh);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int kt = 0; kt < DQ_KT; ++kt) {
+          if (i < 8)
+            st2[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fkv[i & 1][kt], fq[i], st2[kt], 0, 0, 0);
+          else
+            dpt[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fkv[i & 1][kt], fd[i - 8], dpt[kt], 0, 0, 0);
+        }
+        if (i >= 8) {
+#pragma unroll
+          for (int u = 0; u < DQ_KT * 2; ++u) {
+            const int x = (i - 8) * DQ_KT * 2 + u;
+            ds[x] = __builtin_amdgcn_exp2f(st2[x >> 4][x & 15] * c - lse2);
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      const bool diag = (key0 + DQ_K - 1 > wq0) || (key0 + DQ_K > T) || (window >= 0 && key0 < wq0 + 31 - window);
       if (diag) {  // wave-uniform: the visibility test only on tiles that need it
         keep_branch();
 #pragma unroll
