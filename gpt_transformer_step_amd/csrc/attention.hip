@@ -329,15 +329,27 @@ attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, 
     const int key0 = j * FK;
     // wave-uniform: some key of the tile is visible to some query of the wave
     if (key0 <= wq0 + 31 && (window < 0 || key0 + FK - 1 >= wq0 - window)) {
+      // S^T over the 64 keys: the two 32-key halves' MFMAs alternate, with
+      // each k-step's K fragments read one k-step ahead
       f32x16_t s[2];
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
+      for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
         for (int e = 0; e < 16; ++e) s[kt][e] = 0.f;
+      bf16x8_t fk[2][2];
 #pragma unroll
-        for (int ks = 0; ks < 8; ++ks)
-          s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag16(sk, kt * 32 + lr, ks * 2 + lh), fq[ks], s[kt], 0,
-                                                          0, 0);
+      for (int kt = 0; kt < 2; ++kt) fk[0][kt] = frag16(sk, kt * 32 + lr, lh);
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) {
+        if (ks + 1 < 8) {
+#pragma unroll
+          for (int kt = 0; kt < 2; ++kt) fk[(ks + 1) & 1][kt] = frag16(sk, kt * 32 + lr, (ks + 1) * 2 + lh);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+          s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fk[ks & 1][kt], fq[ks], s[kt], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
       }
       const bool diag = (key0 + FK - 1 > wq0) || (key0 + FK > T) || (window >= 0 && key0 < wq0 + 31 - window);
       // raw scores; the max is taken on raw scores (c > 0) and the scale is
