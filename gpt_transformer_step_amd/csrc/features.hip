@@ -327,18 +327,38 @@ __global__ void __launch_bounds__(256) resid_bwd_kernel(float* __restrict__ g, u
                                                         float* __restrict__ part) {
   const float a = bfv(pa), bb = bfv(pb);
   float s_in = 0.f, s_0 = 0.f;
-  for (long long i = (long long)blockIdx.x * 256 + threadIdx.x; i < n4; i += (long long)gridDim.x * 256) {
-    float4 gv = reinterpret_cast<const float4*>(g)[i];
-    const uint2 xw = reinterpret_cast<const uint2*>(xin)[i];
-    const float4 zv = reinterpret_cast<const float4*>(x0)[i];
-    s_in += gv.x * lo_bf(xw.x) + gv.y * hi_bf(xw.x) + gv.z * lo_bf(xw.y) + gv.w * hi_bf(xw.y);
-    s_0 += gv.x * zv.x + gv.y * zv.y + gv.z * zv.z + gv.w * zv.w;
-    float4 o = g0_first ? make_float4(0.f, 0.f, 0.f, 0.f) : reinterpret_cast<const float4*>(g0)[i];
-    o.x += bb * gv.x; o.y += bb * gv.y; o.z += bb * gv.z; o.w += bb * gv.w;
-    reinterpret_cast<float4*>(g0)[i] = o;
-    gv.x *= a; gv.y *= a; gv.z *= a; gv.w *= a;
-    reinterpret_cast<float4*>(g)[i] = gv;
-    reinterpret_cast<uint2*>(g_bf)[i] = make_uint2(pack_bf2(gv.x, gv.y), pack_bf2(gv.z, gv.w));
+  // two chunks per thread and iteration, every load of both issued before
+  // the stores (one chunk at a time left the streams' loads waiting behind
+  // the previous chunk's stores)
+  const long long stride = (long long)gridDim.x * 256;
+  for (long long i0 = (long long)blockIdx.x * 256 + threadIdx.x; i0 < n4; i0 += 2 * stride) {
+    float4 gv[2], zv[2], o[2];
+    uint2 xw[2];
+    bool ok[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const long long i = i0 + u * stride;
+      ok[u] = i < n4;
+      const long long j = ok[u] ? i : i0;
+      gv[u] = reinterpret_cast<const float4*>(g)[j];
+      xw[u] = reinterpret_cast<const uint2*>(xin)[j];
+      zv[u] = reinterpret_cast<const float4*>(x0)[j];
+      o[u] = g0_first ? make_float4(0.f, 0.f, 0.f, 0.f) : reinterpret_cast<const float4*>(g0)[j];
+    }
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      if (!ok[u]) continue;
+      const long long i = i0 + u * stride;
+      float4 gg = gv[u];
+      s_in += gg.x * lo_bf(xw[u].x) + gg.y * hi_bf(xw[u].x) + gg.z * lo_bf(xw[u].y) + gg.w * hi_bf(xw[u].y);
+      s_0 += gg.x * zv[u].x + gg.y * zv[u].y + gg.z * zv[u].z + gg.w * zv[u].w;
+      float4 oo = o[u];
+      oo.x += bb * gg.x; oo.y += bb * gg.y; oo.z += bb * gg.z; oo.w += bb * gg.w;
+      reinterpret_cast<float4*>(g0)[i] = oo;
+      gg.x *= a; gg.y *= a; gg.z *= a; gg.w *= a;
+      reinterpret_cast<float4*>(g)[i] = gg;
+      reinterpret_cast<uint2*>(g_bf)[i] = make_uint2(pack_bf2(gg.x, gg.y), pack_bf2(gg.z, gg.w));
+    }
   }
   s_in = wave_sum(s_in);
   s_0 = wave_sum(s_0);
@@ -384,14 +404,31 @@ __global__ void __launch_bounds__(256) axpy_stream_kernel(float* __restrict__ g,
 }
 
 // out[v] = beta out[v] + scale sum_p part[p nvals + v]
+// Value v = sum over p < nparts of part[p * nvals + v], one workgroup per
+// value: fixed per-thread strides, then a fixed tree in LDS, in double (a
+// thread per value summing the partials one after another took about 150 us
+// per reduction, each load waited for).  Values v < nlo go to out_lo[v], the
+// others to out_hi[v - nlo] (two parameter slots in one launch);
+// out = beta out + scale sum.
 __global__ void __launch_bounds__(256) reduce_partials_kernel(const float* __restrict__ part, int nparts, int nvals,
-                                                              float* __restrict__ out, float scale, float beta) {
-  const int v = blockIdx.x * 256 + threadIdx.x;
-  if (v >= nvals) return;
+                                                              float* __restrict__ out_lo, int nlo,
+                                                              float* __restrict__ out_hi, float scale, float beta) {
+  const int v = blockIdx.x;
   double s = 0.0;
-  for (int p = 0; p < nparts; ++p) s += part[(long long)p * nvals + v];
-  const float r = scale * (float)s;
-  out[v] = beta != 0.f ? beta * out[v] + r : r;
+  for (int p = threadIdx.x; p < nparts; p += 256) s += part[(long long)p * nvals + v];
+  __shared__ double red[256];
+  red[threadIdx.x] = s;
+  __syncthreads();
+#pragma unroll
+  for (int w = 128; w > 0; w >>= 1) {
+    if (threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    float* o = v < nlo ? out_lo + v : out_hi + (v - nlo);
+    const float r = scale * (float)red[0];
+    *o = beta != 0.f ? beta * *o + r : r;
+  }
 }
 
 }  // namespace
@@ -404,12 +441,18 @@ long long feature_partial_floats(int Hkv) {
                              (long long)kFeatBlocks * Hkv * kVeCh) + 64;
 }
 
-static int reduce_to(const float* part, int nparts, int nvals, float* out, float scale, bool accumulate,
-                     hipStream_t s) {
-  hipLaunchKernelGGL(reduce_partials_kernel, dim3((nvals + 255) / 256), dim3(256), 0, s, part, nparts, nvals, out,
+// values [0, nlo) into out_lo, [nlo, nvals) into out_hi
+static int reduce_to2(const float* part, int nparts, int nvals, float* out_lo, int nlo, float* out_hi, float scale,
+                      bool accumulate, hipStream_t s) {
+  hipLaunchKernelGGL(reduce_partials_kernel, dim3(nvals), dim3(256), 0, s, part, nparts, nvals, out_lo, nlo, out_hi,
                      scale, accumulate ? 1.f : 0.f);
   GS_LAUNCH_CHECK("reduce_partials");
   return 0;
+}
+
+static int reduce_to(const float* part, int nparts, int nvals, float* out, float scale, bool accumulate,
+                     hipStream_t s) {
+  return reduce_to2(part, nparts, nvals, out, nvals, nullptr, scale, accumulate, s);
 }
 
 int launch_smear_fwd(const int* ids, const uint16_t* wte, const uint16_t* sw, const uint16_t* slam, float* x,
@@ -428,12 +471,7 @@ int launch_smear_bwd(const int* ids, const uint16_t* wte, const uint16_t* sw, co
   GS_LAUNCH_CHECK("smear_bwd");
   if (!slam) return 0;
   // part rows: [d lam, d w_0 .. d w_23]; d lam and d w are separate parameter slots
-  int rc = reduce_to(part, kFeatBlocks, kSmearCh + 1, part + (long long)kFeatBlocks * (kSmearCh + 1), 1.f, false, s);
-  if (rc) return rc;
-  const float* tot = part + (long long)kFeatBlocks * (kSmearCh + 1);
-  rc = reduce_to(tot, 1, 1, dlam, 1.f, accumulate, s);
-  if (rc) return rc;
-  return reduce_to(tot + 1, 1, kSmearCh, dw, 1.f, accumulate, s);
+  return reduce_to2(part, kFeatBlocks, kSmearCh + 1, dlam, 1, dw, 1.f, accumulate, s);
 }
 
 int launch_mix_rmsnorm_fwd(float* x, const float* y, const uint16_t* pa, const uint16_t* pb, float bsign,
@@ -493,14 +531,8 @@ int launch_resid_bwd(float* g, uint16_t* g_bf, const uint16_t* xin, const float*
   hipLaunchKernelGGL(resid_bwd_kernel, dim3(kFeatBlocks), dim3(256), 0, s, g, g_bf, xin, x0, g0, (int)g0_first, pa, pb,
                      n / 4, part);
   GS_LAUNCH_CHECK("resid_bwd");
-  // part rows: [g . x_in, g . x0]
-  hipLaunchKernelGGL(reduce_partials_kernel, dim3(1), dim3(256), 0, s, part, kFeatBlocks, 2,
-                     part + (long long)kFeatBlocks * 2, 1.f, 0.f);
-  GS_LAUNCH_CHECK("reduce_partials");
-  const float* tot = part + (long long)kFeatBlocks * 2;
-  int rc = reduce_to(tot, 1, 1, da, 1.f, accumulate, s);
-  if (rc) return rc;
-  return reduce_to(tot + 1, 1, 1, db, 1.f, accumulate, s);
+  // part rows: [g . x_in, g . x0] into the two scalars' slots
+  return reduce_to2(part, kFeatBlocks, 2, da, 1, db, 1.f, accumulate, s);
 }
 
 int launch_backout_bwd(const float* g, const float* xm, float* gcopy, long long n, float* part, float* dlam,
