@@ -1156,12 +1156,23 @@ struct MuonWS {
   size_t partial, Xb0, Xb1, Ab, Bb, gpart, nm_part, nm_scale, total;
 };
 
-// k-splits of the Gram products X^T X (a few output tiles, long K)
-inline int gram_splits(int count, int rows, int cols) {
+// The Gram product A = X^T X of a Newton-Schulz iteration: k-split count and
+// whether only the tiles on and above the diagonal are computed (then
+// mirrored).  Symmetric when the batch holds more 128 x 128 tiles than the
+// chip has CUs, or when K is split: the split multiplies the workgroups, so
+// halving the tiles lets about twice as many splits share a grid (one
+// 1664 x 6656 matrix: 91 tiles x 6 splits instead of 169 x 4).
+struct GramPlan {
+  int splits, sym;
+};
+inline GramPlan gram_plan(int count, int rows, int cols) {
   const int lrow = std::max(rows, cols), sm = std::min(rows, cols);
-  const long long tiles = (long long)count * ((sm + 127) / 128) * ((sm + 127) / 128);
-  if (tiles >= 512) return 1;
-  return (int)std::max<long long>(1, std::min<long long>(std::max(1, lrow / 1024), (512 + tiles - 1) / tiles));
+  const long long t = (sm + 127) / 128;
+  const long long full = (long long)count * t * t, upper = (long long)count * t * (t + 1) / 2;
+  if (full >= 512 || lrow / 1024 <= 1) return {1, full > 256 ? 1 : 0};
+  const long long tiles = full > 256 ? full : upper;  // the symmetric grid when the split applies
+  const int splits = (int)std::max<long long>(1, std::min<long long>(lrow / 1024, (512 + tiles - 1) / tiles));
+  return {splits, (splits > 1 || full > 256) ? 1 : 0};
 }
 
 MuonWS muon_layout(int count, int rows, int cols) {
@@ -1175,7 +1186,7 @@ MuonWS muon_layout(int count, int rows, int cols) {
   m.Xb1 = take(n * 2);
   m.Ab = take((size_t)count * sm * sm * 2);
   m.Bb = take((size_t)count * sm * sm * 2);
-  const int gs_ = gram_splits(count, rows, cols);
+  const int gs_ = gram_plan(count, rows, cols).splits;
   m.gpart = take(gs_ > 1 ? (size_t)gs_ * count * sm * sm * 4 : 4);
   m.nm_part = take((size_t)normuon_part_floats(count, rows, cols) * 4);
   m.nm_scale = take((size_t)count * std::max(rows, cols) * 4);
@@ -1238,21 +1249,24 @@ int muon_impl(float* Wt, uint16_t* W_bf16, const float* Gm, float* M, float* O_o
   { ProfScope ps_(P_MUON_ELEMWISE, s); TRY(launch_ns_init(src, partial, kFrobBlocks, nullptr, Xb[0], count, rows, cols, 1e-7f, s)); }
 
   const long long sX = (long long)lrow * sm, sA = (long long)sm * sm;
-  const int gram_split = gram_splits(count, rows, cols);
+  const GramPlan gplan = gram_plan(count, rows, cols);
+  const int gram_split = gplan.splits;
   float* gpart = at<float>(ws, m.gpart);
   int cur = 0;
   // A = X^T X and B = b A + c A A are symmetric: when the batch holds more
   // 128 x 128 tiles than the chip has CUs, both products compute only the
   // tiles on and above the diagonal, and their bf16 outputs, which the next
   // product reads in full, are mirrored (with fewer tiles all of them run in
-  // one wave anyway, and the mirror would only add time).  A is kept in bf16
+  // one wave anyway, and the mirror would only add time; the Gram product
+  // also when its K is split, see gram_plan).  A is kept in bf16
   // only, like the iteration's other operands: the polynomial's epilogue
   // reads the same bf16 A its product reads (the b A term then carries one
   // bf16 rounding, as B itself does when it is stored).
   const long long t128 = (sm + 127) / 128;
-  const int sym = (long long)count * t128 * t128 > 256 ? 1 : 0;
+  const int sym = (long long)count * t128 * t128 > 256 ? 1 : 0;  // the polynomial product
+  const int gsym = gplan.sym;
   GemmArgs ga;
-  ga.M = sm; ga.N = sm; ga.K = lrow; ga.batch = count; ga.sym = sym;
+  ga.M = sm; ga.N = sm; ga.K = lrow; ga.batch = count; ga.sym = gsym;
   ga.lda = sm; ga.sA = sX; ga.a_kcontig = 0;
   ga.ldb = sm; ga.sB = sX; ga.b_kcontig = 0;
   ga.C = Ab; ga.ldc = sm; ga.sC = sA;
@@ -1278,7 +1292,7 @@ int muon_impl(float* Wt, uint16_t* W_bf16, const float* Gm, float* M, float* O_o
         TRY(gemm_bf16(a, EPI_F32, s));
         TRY(launch_splitk_reduce(gpart, gram_split, sA * count, nullptr, Ab, sA * count, 0.f, s));
       }
-      if (sym) TRY(launch_sym_mirror(Ab, sm, sm, sA, count, s));
+      if (gsym) TRY(launch_sym_mirror(Ab, sm, sm, sA, count, s));
     }
     {
       ProfScope ps_(P_NS_POLY, s);
