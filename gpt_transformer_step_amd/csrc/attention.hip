@@ -518,7 +518,12 @@ attn_bwd_kv8_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
   const int n_it = G * nq;  // (query head, query tile) pairs; block-uniform
 
   auto hq_of = [&](int it) { return GEN ? hk * G + it / nq : hk; };
-  auto qt_of = [&](int it) { return GEN ? qt_first + it % nq : qt_first + it; };
+  // query tiles from the last one down: every workgroup of a (sequence, head)
+  // starts on the same tile, so blocks dispatched together read each Q / dO
+  // tile at about the same time (one L2 fill serves them all); walking up
+  // from its own diagonal, block kb would reach tile t at a different time
+  // from every other block
+  auto qt_of = [&](int it) { return GEN ? qt_end - 1 - it % nq : qt_end - 1 - it; };
   // the K8_LOADS direct loads of tile it (clamped to the last tile) into
   // stage st: Q and dO (two 16-byte chunks per thread each) and the
   // statistics (one per thread of lanes 0 .. PER - 1, below)
