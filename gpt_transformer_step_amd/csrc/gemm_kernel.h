@@ -452,6 +452,28 @@ __device__ __forceinline__ void epi8(const GemmArgs& p, int bi, int m, int n, co
   }
 }
 
+// 16-bit outputs already converted (8 consecutive columns n .. n+7 of row m
+// as one 16-byte word): store, and the amax of the stored values
+template <int EPI>
+__device__ __forceinline__ void st16(const GemmArgs& p, int bi, int m, int n, uint4 w, float& amx) {
+  uint16_t* C = reinterpret_cast<uint16_t*>(p.C) + (long long)bi * p.sC + (long long)m * p.ldc + n;
+  const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+  if (n + 7 < p.N) {
+    st_nt(C, w);
+    if (EPI != EPI_F16 && p.amax) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) amx = fmaxf(amx, fmaxf(fabsf(lo_bf(ww[j])), fabsf(hi_bf(ww[j]))));
+    }
+  } else {
+    for (int j = 0; j < 8; ++j)
+      if (n + j < p.N) {
+        const uint16_t b = (uint16_t)(ww[j >> 1] >> (16 * (j & 1)));
+        C[j] = b;
+        if (EPI != EPI_F16 && p.amax) amx = fmaxf(amx, fabsf(bf2f(b)));
+      }
+  }
+}
+
 // ---------------------------------------------------------------------------
 // K loop: double-buffered LDS stages, fragments double-buffered in registers,
 // and (for interior tiles, GUARD = false) an explicit interleave of MFMAs with
@@ -1013,6 +1035,9 @@ __global__ void __launch_bounds__((Cfg<BM, BN>::NT), 1) gemm_kernel(GemmArgs p) 
                          SE == EPI_NS_POLY;
     constexpr bool AUX8 = SE == EPI_DRELU2 || SE == EPI_NS_POLY;  // bf16 aux read per output
     constexpr int CH2 = CH / 2, NIT8 = 32 * CH2 / 64;
+    // 16-bit outputs staged as such (below)
+    constexpr bool PRE16 = SE == EPI_BF16 || SE == EPI_RELU2 || SE == EPI_QKV || SE == EPI_F16;
+    constexpr int ROWB16 = WN * 2;
     const bool w8 = W8E && (p.ldc % 8 == 0) && (!AUX8 || p.ldaux % 8 == 0);
     // (the ReLU^2-derivative epilogue always takes the 8-column path: its
     // launches keep C and the saved activation 16-byte aligned, and the 4-column
@@ -1067,6 +1092,56 @@ __global__ void __launch_bounds__((Cfg<BM, BN>::NT), 1) gemm_kernel(GemmArgs p) 
         fetch_c(i);
       }
       qkv_rows(i);
+      if (PRE16 && w8) {
+        if constexpr (PRE16) {
+          // Outputs whose epilogue is elementwise on the accumulator are
+          // converted before staging: 16-bit rows of 2 WN bytes (16-byte
+          // chunks of 8 columns XOR-swizzled by row), half the LDS bytes of
+          // fp32 staging, and each lane reads back a finished 16-byte store.
+          // Same arithmetic as the fp32-staged path (scale, ReLU^2, one
+          // rounding), so the same bits.
+#pragma unroll
+          for (int j = 0; j < TN; ++j)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+              float o[4];
+#pragma unroll
+              for (int r = 0; r < 4; ++r) {
+                o[r] = acc[i][j][4 * g + r] * alpha_st;
+                if constexpr (SE == EPI_RELU2) {
+                  const float t = fmaxf(o[r], 0.f);
+                  o[r] = t * t;
+                }
+              }
+              uint2 w;
+              if constexpr (SE == EPI_F16) {
+                typedef _Float16 h4_t __attribute__((ext_vector_type(4)));
+                const h4_t h = {(_Float16)o[0], (_Float16)o[1], (_Float16)o[2], (_Float16)o[3]};
+                w = __builtin_bit_cast(uint2, h);
+              } else {
+                w = make_uint2(pack_bf2(o[0], o[1]), pack_bf2(o[2], o[3]));
+              }
+              const int c8 = (j * 32 + 8 * g) >> 3;
+              *reinterpret_cast<uint2*>(wbuf + lr * ROWB16 + ((c8 ^ (lr & (CH2 - 1))) << 4) + 8 * lh) = w;
+            }
+          __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+          __builtin_amdgcn_wave_barrier();
+          __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+          for (int it = 0; it < NIT8; ++it) {
+            const int q = it * 64 + lane;
+            const int rr = q / CH2, cc = q % CH2;
+            const uint4 w = *reinterpret_cast<const uint4*>(wbuf + rr * ROWB16 + ((cc ^ (rr & (CH2 - 1))) << 4));
+            const int m = m0 + wm * WM + i * 32 + rr;
+            const int n = n0 + wn * WN + cc * 8;
+            if (m < p.M && n < p.N) st16<SE>(p, bi, m, n, w, amx);
+          }
+          __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+          __builtin_amdgcn_wave_barrier();
+          __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        }
+        continue;
+      }
 #pragma unroll
       for (int j = 0; j < TN; ++j)
 #pragma unroll
